@@ -1,0 +1,237 @@
+/*
+ * kvq.h - C ABI of libkvq: quantize-on-append into a paged INT-b KV cache and
+ * fused quantized decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * Conventions (all entry points):
+ *  - Every function returns kvq_status. KVQ_OK is 0. On failure nothing is
+ *    launched and nothing is written, and kvq_last_error() returns a message
+ *    for the calling thread (valid until the next kvq call on that thread).
+ *  - No C++ exception crosses this boundary.
+ *  - "device" pointers are HIP device memory owned by the caller; the library
+ *    never allocates, frees or retains device memory.
+ *  - Device work is asynchronous on the caller's hipStream_t (0 = the null
+ *    stream) with no implicit synchronisation. A launch failure is reported as
+ *    KVQ_ERR_DEVICE.
+ *  - Host functions are synchronous and need no GPU.
+ *  - Functions keep no global mutable state; concurrent calls that write
+ *    different buffers are safe.
+ *  - Inputs must be finite; results on NaN or Inf inputs are unspecified.
+ *
+ * Sources for what is computed (page titles as published on gist.science):
+ *  [RQ]  "RateQuant" technical summary (paper 2605.06675), Methodology.
+ *  [MKV] "Quantize What Counts: More for Keys, Less for Values" (2502.15075).
+ *  [LQ]  "LogQuant: Log-Distributed 2-Bit Quantization of KV Cache with
+ *        Superior Accuracy Preservation" (2503.19950), technical summary.
+ *  [SAW] "SAW-INT4: System-Aware 4-Bit KV-Cache Quantization for Real-World
+ *        LLM Serving" (2604.19157).
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_ABI_VERSION 1
+#define KVQ_MAX_KV_HEADS 64
+#define KVQ_BLOCK_TOKENS 16
+
+typedef enum kvq_status {
+  KVQ_OK = 0,
+  KVQ_ERR_ARG = 1,         /* a null pointer, a bad size or an inconsistent argument */
+  KVQ_ERR_UNSUPPORTED = 2, /* a valid request outside what is built (e.g. head_dim 96) */
+  KVQ_ERR_BUDGET = 3,      /* bit budget infeasible or not spent exactly */
+  KVQ_ERR_WORKSPACE = 4,   /* workspace smaller than kvq_decode_workspace_bytes */
+  KVQ_ERR_DEVICE = 5,      /* a HIP call or kernel launch failed */
+  KVQ_ERR_CAPACITY = 6     /* the page free list ran out */
+} kvq_status;
+
+typedef enum kvq_dtype {
+  KVQ_F32 = 0,
+  KVQ_BF16 = 1
+} kvq_dtype;
+
+typedef struct hipStream_t_opaque* kvq_stream; /* a hipStream_t */
+
+/*
+ * Cache geometry of one pool (one layer, or one precision segment of a layer).
+ *
+ * A pool is an array of blocks of block_bytes each; a block holds 16
+ * consecutive tokens of one sequence for every KV head. Inside a block the K
+ * areas of heads 0..Hkv-1 come first, then the V areas. One head's area is
+ *     codes[16][head_dim * b / 8]  then  meta[16] { float scale; float min; }
+ * where code j of a row occupies bits [j*b, j*b+b) of the row's little-endian
+ * bit-stream. For b = 16 the area is bf16[16][head_dim] of the rotated row
+ * (round half to even) and has no meta. Per-head b may differ between heads
+ * and between K and V [RQ: stage 3, K/V decoupling; MKV: more bits for keys];
+ * uniform blocks follow [SAW: section 1, PagedAttention].
+ */
+typedef struct kvq_layout {
+  /* inputs */
+  int32_t num_kv_heads; /* Hkv, 1..KVQ_MAX_KV_HEADS */
+  int32_t group;        /* G query heads per KV head (q-head g reads KV head g / G), 1..4 */
+  int32_t head_dim;     /* d, 64 or 128 */
+  int32_t had_block;    /* n, Hadamard block: power of two, 1 <= n <= d (1 = no rotation) */
+  int32_t block_tokens; /* must be KVQ_BLOCK_TOKENS */
+  int32_t bits_k[KVQ_MAX_KV_HEADS]; /* each in {2, 3, 4, 8, 16} */
+  int32_t bits_v[KVQ_MAX_KV_HEADS];
+  /* outputs of kvq_layout_init */
+  int64_t k_off[KVQ_MAX_KV_HEADS]; /* byte offset of head h's K area in a block */
+  int64_t v_off[KVQ_MAX_KV_HEADS];
+  int64_t block_bytes;
+} kvq_layout;
+
+/* One precision segment of the cache, read by decode attention. All segments
+ * passed together must share num_kv_heads, group, head_dim and had_block.
+ * The attended set is the union of every segment's first seq_lens[b] tokens;
+ * token order does not matter [LQ: Methodology 4, A.V = A_P.V_P]. */
+typedef struct kvq_segment {
+  const kvq_layout* layout;  /* host */
+  const void* pool;          /* device, pool_blocks * layout->block_bytes bytes */
+  int64_t pool_blocks;
+  const int32_t* block_table;/* device, [batch][table_stride] physical block ids */
+  int32_t table_stride;
+  const int32_t* seq_lens;   /* device, [batch] tokens held by this segment */
+  int32_t max_len;           /* host upper bound on seq_lens[] (sizes the grid) */
+} kvq_segment;
+
+int kvq_abi_version(void);
+const char* kvq_status_str(kvq_status s);
+const char* kvq_last_error(void);
+
+/*
+ * Host. Fill k_off, v_off and block_bytes from the inputs of *L.
+ * Errors: KVQ_ERR_ARG for a null L, block_tokens != 16, num_kv_heads or group
+ * out of range, a bit width outside {2,3,4,8,16}, had_block not a power of
+ * two or not dividing head_dim; KVQ_ERR_UNSUPPORTED for head_dim not 64/128.
+ */
+kvq_status kvq_layout_init(kvq_layout* L);
+
+/*
+ * Host. Greedy marginal-gain integer bit allocation [RQ: Methodology 1 and 3].
+ * Minimises sum_i w[i] * D(b_i), D(b) = alpha * beta^-b, subject to
+ * sum_i b_i = budget_bits, each b_i taken from ladder[0..n_ladder).
+ * Every head starts at the smallest ladder width; each round gives one more
+ * ladder step to the head with the largest weighted distortion drop per bit,
+ * w_i (D(b) - D(b+)) / (b+ - b), among steps that fit the remaining budget
+ * (ties: lowest index), until the budget is spent or no step fits.
+ * In:  n >= 1 heads, w[n] > 0 (host), alpha > 0, beta > 1, ladder of
+ *      1..16 distinct positive widths (any order), budget_bits.
+ * Out: bits_out[n] (host), *leftover_out = unspent bits (may be null).
+ * Errors: KVQ_ERR_ARG for bad arguments; KVQ_ERR_BUDGET if budget_bits is below
+ * n*min(ladder) or above n*max(ladder) (nothing written), or if bits are left
+ * over (the allocation found is still written).
+ */
+kvq_status kvq_plan_bits(int32_t n, const float* w, double alpha, double beta,
+                         const int32_t* ladder, int32_t n_ladder, int64_t budget_bits,
+                         int32_t* bits_out, int64_t* leftover_out);
+
+/*
+ * Host. Precision class of each of `total` tokens (position 0 = oldest) for a
+ * log-spaced long-context schedule [LQ: Methodology 2]: 0 = the newest
+ * `window` tokens (kept in bf16); 1 = the log-spaced subset; 2 = the rest.
+ * With r the distance behind the window, span k covers
+ * r in [(2^k - 1) window, (2^(k+1) - 1) window) and keeps every 2^k-th token
+ * from the span's start in class 1.
+ * Out: cls_out[total] (host). Errors: KVQ_ERR_ARG for total < 0, window < 1
+ * or a null cls_out with total > 0.
+ */
+kvq_status kvq_logquant_classes(int32_t total, int32_t window, int8_t* cls_out);
+
+/*
+ * Host. Deterministic page allocation. For seq = 0..batch-1 in order, and
+ * within a sequence for logical blocks ceil(old_len/16) .. ceil(new_len/16)-1
+ * in order, set block_table[seq * table_stride + lb] = free_list[(*cursor)++].
+ * All pointers are host. new_len[s] >= old_len[s] >= 0 and
+ * ceil(new_len[s]/16) <= table_stride are required (KVQ_ERR_ARG).
+ * KVQ_ERR_CAPACITY if the free list runs out (the table and cursor are then
+ * left as they were before the call).
+ */
+kvq_status kvq_page_alloc(const int32_t* free_list, int32_t n_free, int32_t* cursor,
+                          int32_t batch, const int32_t* old_len, const int32_t* new_len,
+                          int32_t* block_table, int32_t table_stride);
+
+/*
+ * Device, async. Quantize-on-append [SAW: sections 2-3; RQ: stage 3].
+ * For every sequence b < batch, new token i < n_new and KV head h, the row
+ * x = k[b][i][h][:] (resp. v) is rotated, x' = blockdiag(H_n) x with H_n the
+ * orthonormal Sylvester Hadamard matrix, then quantized token-wise in fp32:
+ * mn = min x', mx = max x', s = (mx - mn) / (2^b - 1),
+ * code = round_half_even((x' - mn) * (2^b - 1) / (mx - mn)) (s = 0 and codes 0
+ * for a constant row), packed, and stored with {s, mn} at position
+ * p = start_pos[b] + i: block block_table[b * table_stride + p / 16], slot p % 16.
+ * For b = 16 the rotated row is stored as bf16.
+ * In:  k, v device [batch][n_new][Hkv][head_dim] of in_dtype; start_pos device
+ *      [batch]; block_table device. Every block the new tokens touch must be
+ *      mapped; a row whose block id is outside [0, pool_blocks) is skipped.
+ * Out: pool (device) rows and meta of the new tokens only.
+ * Errors: KVQ_ERR_ARG (null pointers, batch < 0, n_new < 0, bad stride),
+ * KVQ_ERR_DEVICE.
+ */
+kvq_status kvq_quantize_append(const kvq_layout* L, void* pool, int64_t pool_blocks,
+                               const int32_t* block_table, int32_t table_stride,
+                               int32_t batch, const int32_t* start_pos, int32_t n_new,
+                               const void* k, const void* v, kvq_dtype in_dtype,
+                               kvq_stream stream);
+
+/*
+ * Device, async. Read back n tokens [pos0, pos0 + n) of sequence `seq`:
+ * x_hat' = code * s + mn in fp32 (a rounded product then a rounded sum), or the
+ * bf16 value for b = 16. With rotated = 0 the original basis blockdiag(H_n)^T
+ * x_hat' is returned instead (fp32 fast Walsh-Hadamard transform).
+ * Out: k_out, v_out device float [n][Hkv][head_dim].
+ * Errors: KVQ_ERR_ARG (null pointers, n < 0, pos0 < 0, seq < 0), KVQ_ERR_DEVICE.
+ * Rows whose block id is outside [0, pool_blocks) are written as zeros.
+ */
+kvq_status kvq_dequant(const kvq_layout* L, const void* pool, int64_t pool_blocks,
+                       const int32_t* block_table, int32_t table_stride, int32_t seq,
+                       int32_t pos0, int32_t n, int32_t rotated,
+                       float* k_out, float* v_out, kvq_stream stream);
+
+/*
+ * Host. Bytes of device workspace kvq_decode_attn needs for these segments
+ * and batch size (split-K partials: max, sum and o' per query head and split).
+ */
+kvq_status kvq_decode_workspace_bytes(const kvq_segment* segs, int32_t n_segs,
+                                      int32_t batch, size_t* bytes);
+
+/*
+ * Device, async. Fused quantized decode attention, one query per q-head:
+ *   o[b][g] = softmax(q[b][g] . K_hat^T / sqrt(d)) V_hat
+ * over the union of the segments' tokens of KV head g / G, with K_hat, V_hat
+ * the dequantized cache in the original basis. Computed in the rotated basis:
+ * q' = R q, scores against the stored rotated keys, o' = sum_t p_t v_hat'_t,
+ * o = R^T o' (one inverse rotation per output row) [SAW: section 3]. Split-K
+ * over pages with an online-softmax merge; fp32 accumulation.
+ * A sequence with no tokens in any segment gets a zero output row.
+ * In:  q device [batch][Hkv*G][head_dim] of q_dtype.
+ * Out: out device float [batch][Hkv*G][head_dim].
+ * ws: device workspace of at least kvq_decode_workspace_bytes bytes (its
+ * contents on entry do not matter).
+ * Errors: KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE, KVQ_ERR_DEVICE.
+ */
+kvq_status kvq_decode_attn(const kvq_segment* segs, int32_t n_segs, int32_t batch,
+                           const void* q, kvq_dtype q_dtype, float* out,
+                           void* ws, size_t ws_bytes, kvq_stream stream);
+
+/*
+ * The two launches kvq_decode_attn makes, exported so a profiler or caller can
+ * time them apart: kvq_decode_partial writes the split partials into ws;
+ * kvq_decode_merge combines them and writes out. Same arguments and errors as
+ * kvq_decode_attn; calling them in this order on one stream equals one
+ * kvq_decode_attn call.
+ */
+kvq_status kvq_decode_partial(const kvq_segment* segs, int32_t n_segs, int32_t batch,
+                              const void* q, kvq_dtype q_dtype,
+                              void* ws, size_t ws_bytes, kvq_stream stream);
+kvq_status kvq_decode_merge(const kvq_segment* segs, int32_t n_segs, int32_t batch,
+                            float* out, void* ws, size_t ws_bytes, kvq_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -9,7 +9,8 @@ Everything here is the plain definition of what the method computes, written
 for a reader to check against the source pages by eye:
 
 * Rotation: block-diagonal Hadamard rotation of each head row, applied as an
-  explicit matrix product in float64 and then rounded to float32.
+  explicit +-1 matrix product in float64, one 1/sqrt(n) scaling, then rounded
+  to float32.
   Source: "SAW-INT4: System-Aware 4-Bit KV-Cache Quantization for Real-World
   LLM Serving" (gist.science/ar/paper/2604.19157), section 2 ("shuffle before
   you shrink": block-diagonal Hadamard rotation spreads outliers).
@@ -53,13 +54,9 @@ META_BYTES = 8  # float32 scale + float32 minimum per (token, head) row
 # Rotation (SAW-INT4 page, section 2)
 # ---------------------------------------------------------------------------
 
-def hadamard_matrix(n):
-    """Orthonormal Hadamard matrix of order n in Sylvester (natural) order.
-
-    H[i][j] = (-1)^popcount(i & j) / sqrt(n). The pages say only
-    "block-diagonal Hadamard"; this reading takes the Sylvester matrix with no
-    random sign flips, normalised so that H^T H = I.
-    """
+def hadamard_pm1(n):
+    """Sylvester Hadamard matrix of order n with entries +-1, natural order:
+    H[i][j] = (-1)^popcount(i & j)."""
     if n < 1 or n & (n - 1):
         raise ValueError("Hadamard order must be a power of two")
     idx = np.arange(n)
@@ -67,21 +64,34 @@ def hadamard_matrix(n):
     both = idx[:, None] & idx[None, :]
     for bit in range(max(1, n.bit_length())):
         parity ^= (both >> bit) & 1
-    return np.where(parity == 0, 1.0, -1.0) / math.sqrt(n)
+    return np.where(parity == 0, 1.0, -1.0)
+
+
+def hadamard_matrix(n):
+    """Orthonormal Hadamard matrix H_n / sqrt(n) in Sylvester (natural) order.
+
+    The pages say only "block-diagonal Hadamard"; this reading takes the
+    Sylvester matrix with no random sign flips, normalised so that H^T H = I.
+    """
+    return hadamard_pm1(n) / math.sqrt(n)
 
 
 def rotate(x, n):
-    """x' = blockdiag(H_n, ..., H_n) x over the last axis, fp64, rounded to fp32.
+    """x' = blockdiag(H_n, ..., H_n) x / sqrt(n) over the last axis, rounded to fp32.
 
-    Blocks are contiguous channel ranges [k*n, (k+1)*n).
+    Blocks are contiguous channel ranges [k*n, (k+1)*n). The +-1 matrix product
+    is taken in fp64 (exact for bf16 or fp32 inputs of moderate dynamic range),
+    then scaled once by 1/sqrt(n) in fp64, then rounded to fp32: the value of the
+    orthonormal rotation up to that last rounding.
     """
     x = np.asarray(x, dtype=np.float64)
     d = x.shape[-1]
     if d % n:
         raise ValueError("head_dim must be a multiple of the Hadamard block")
-    h = hadamard_matrix(n)
+    h = hadamard_pm1(n)
     blocks = x.reshape(x.shape[:-1] + (d // n, n))
     y = np.matmul(blocks, h.T)  # y_k = H x_k for each block k
+    y = y * (1.0 / math.sqrt(n))
     return y.reshape(x.shape).astype(np.float32)
 
 
@@ -89,9 +99,9 @@ def unrotate(y, n):
     """R^T y over the last axis in fp64 (returns fp64)."""
     y = np.asarray(y, dtype=np.float64)
     d = y.shape[-1]
-    h = hadamard_matrix(n)
+    h = hadamard_pm1(n)
     blocks = y.reshape(y.shape[:-1] + (d // n, n))
-    x = np.matmul(blocks, h)  # x_k = H^T y_k
+    x = np.matmul(blocks, h) * (1.0 / math.sqrt(n))  # x_k = H^T y_k / sqrt(n)
     return x.reshape(y.shape)
 
 

@@ -1,0 +1,760 @@
+// Fused quantized decode attention over the paged INT-b KV cache.
+//
+// What is computed: o = softmax(q K^T / sqrt(d)) V for one query per q-head,
+// over the dequantized cache. The cache stores rotated rows (x' = R x, R the
+// block-diagonal Hadamard matrix), so the query is rotated once (q' = R q),
+// scores are taken against the stored keys directly, and the output is
+// un-rotated once per head (o = R^T o'), as the SAW-INT4 summary page
+// (gist.science/ar/paper/2604.19157), section 3, describes: rotation and
+// quantization are folded into reading the cache, with no separate pass.
+// Tokens may sit in any order and in several precision segments
+// (LogQuant summary page, 2503.19950, Methodology section 4: A.V = A_P.V_P).
+//
+// Work decomposition (split-K / flash-decoding): one wave per (sequence, KV
+// head, split of pages). A split walks its pages four at a time (64 tokens):
+//  * QK on the matrix cores: v_mfma_f32_16x16x32_f16 with A = the G query rows
+//    of this KV head (hi and lo fp16 halves of q', each its own MFMA, so the
+//    product carries ~22 bits of q) and B = the page's key codes, which the
+//    lanes turn into exact fp16 numbers 1024 + sigma*c with one v_and_or_b32
+//    per pair (the constant 1024*sum(q) is removed afterwards, exactly).
+//  * The four pages' score tiles are packed into one dense set of four
+//    registers (lane = token, register = query head) with
+//    v_permlane16_swap / v_permlane32_swap.
+//  * Online softmax in log2 units on that dense layout; the weights
+//    w = p * scale are split into fp16 hi/lo halves and transposed through
+//    LDS into the A operand of the PV product.
+//  * PV on the matrix cores: v_mfma_f32_16x16x32_f16, A = weights (hi rows
+//    0..G-1, lo rows 4..4+G-1), B = value codes centred and made exact in
+//    fp16, 32 tokens per instruction. The min term sum_t p_t (mn_t + 2^(b-1) s_t)
+//    is accumulated per head on the vector ALU and added at the end.
+// Each split writes (running max, sum of p, o') to the workspace; a second
+// kernel merges the splits of all segments and applies R^T.
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+#include <cmath>
+
+namespace kvq {
+
+namespace {
+
+constexpr uint32_t kBias = 0x64006400u;  // fp16 pair (1024, 1024)
+
+__device__ __forceinline__ float4_t mfma_f16(u32x4_t a, u32x4_t b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
+                                                __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ float4_t mfma_bf16(u32x4_t a, u32x4_t b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+template <bool BF16>
+__device__ __forceinline__ float4_t mfma(u32x4_t a, u32x4_t b, float4_t c) {
+  if constexpr (BF16) return mfma_bf16(a, b, c);
+  else return mfma_f16(a, b, c);
+}
+
+template <int S>
+__device__ __forceinline__ uint32_t shl_signed(uint32_t w) {
+  if constexpr (S >= 0) return w << S;
+  else return w >> (-S);
+}
+
+// ---------------------------------------------------------------------------
+// Key formats. A lane (token t = lane % 16, quarter g4 = lane / 16) holds the
+// quarter [g4*D/4, (g4+1)*D/4) of token t's stored row; chunk c of the QK
+// product takes 8 of those channels as the lane's 8 K-slots. channel(c, e) is
+// the channel (relative to the quarter) in K-slot e of chunk c; sigma is the
+// power of two each code is scaled by inside its fp16 number 1024 + sigma*c.
+// ---------------------------------------------------------------------------
+template <int KB, int D> struct KFmt;
+
+template <int D> struct KFmt<4, D> {
+  static constexpr int kWords = D / 32;  // quarter = D/8 bytes
+  static constexpr float sigma = 16.f;
+  static constexpr bool bf16 = false;
+  __device__ static int channel(int c, int e) {
+    constexpr int rel[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+    return 8 * c + rel[e];
+  }
+  __device__ static u32x4_t unpack(const uint32_t (&w)[kWords], int c) {
+    const uint32_t x = w[c];
+    u32x4_t r;
+    r[0] = and_or(x << 4, 0x00f000f0u, kBias);
+    r[1] = and_or(x, 0x00f000f0u, kBias);
+    r[2] = and_or(x >> 4, 0x00f000f0u, kBias);
+    r[3] = and_or(x >> 8, 0x00f000f0u, kBias);
+    return r;
+  }
+};
+
+template <int D> struct KFmt<2, D> {
+  static constexpr int kWords = D / 64;  // quarter = D/16 bytes
+  static constexpr float sigma = 256.f;
+  static constexpr bool bf16 = false;
+  __device__ static int channel(int c, int e) {
+    const int m = c >> 1, k = 4 * (c & 1) + (e >> 1);
+    return 16 * m + ((e & 1) ? 8 : 0) + k;
+  }
+  template <int K>
+  __device__ static uint32_t pair(uint32_t x) { return and_or(shl_signed<8 - 2 * K>(x), 0x03000300u, kBias); }
+  __device__ static u32x4_t unpack(const uint32_t (&w)[kWords], int c) {
+    const uint32_t x = w[c >> 1];
+    u32x4_t r;
+    if (c & 1) { r[0] = pair<4>(x); r[1] = pair<5>(x); r[2] = pair<6>(x); r[3] = pair<7>(x); }
+    else       { r[0] = pair<0>(x); r[1] = pair<1>(x); r[2] = pair<2>(x); r[3] = pair<3>(x); }
+    return r;
+  }
+};
+
+template <int D> struct KFmt<8, D> {
+  static constexpr int kWords = D / 16;  // quarter = D/4 bytes
+  static constexpr float sigma = 1.f;
+  static constexpr bool bf16 = false;
+  __device__ static int channel(int c, int e) {
+    constexpr int rel[8] = {0, 2, 1, 3, 4, 6, 5, 7};
+    return 8 * c + rel[e];
+  }
+  __device__ static u32x4_t unpack(const uint32_t (&w)[kWords], int c) {
+    const uint32_t x0 = w[2 * c], x1 = w[2 * c + 1];
+    u32x4_t r;
+    r[0] = and_or(x0, 0x00ff00ffu, kBias);
+    r[1] = and_or(x0 >> 8, 0x00ff00ffu, kBias);
+    r[2] = and_or(x1, 0x00ff00ffu, kBias);
+    r[3] = and_or(x1 >> 8, 0x00ff00ffu, kBias);
+    return r;
+  }
+};
+
+template <int D> struct KFmt<3, D> {
+  static constexpr int kWords = (3 * D / 32 + 3) / 4;  // quarter = 3D/32 bytes (12 or 6)
+  static constexpr float sigma = 128.f;
+  static constexpr bool bf16 = false;
+  __device__ static int channel(int c, int e) { return 8 * c + e; }
+  template <int K>
+  __device__ static uint32_t code(const uint32_t (&w)[kWords]) {
+    constexpr int bit = 3 * K, i = bit / 32, sh = bit % 32;
+    if constexpr (sh <= 29) return (w[i] >> sh) & 7u;
+    else return ((w[i] >> sh) | (w[i + 1] << (32 - sh))) & 7u;
+  }
+  template <int C>
+  __device__ static u32x4_t unpack_c(const uint32_t (&w)[kWords]) {
+    u32x4_t r;
+    r[0] = (((code<8 * C + 1>(w) << 16) | code<8 * C + 0>(w)) << 7) | kBias;
+    r[1] = (((code<8 * C + 3>(w) << 16) | code<8 * C + 2>(w)) << 7) | kBias;
+    r[2] = (((code<8 * C + 5>(w) << 16) | code<8 * C + 4>(w)) << 7) | kBias;
+    r[3] = (((code<8 * C + 7>(w) << 16) | code<8 * C + 6>(w)) << 7) | kBias;
+    return r;
+  }
+  __device__ static u32x4_t unpack(const uint32_t (&w)[kWords], int c) {
+    if constexpr (D == 128) {
+      switch (c) {
+        case 0: return unpack_c<0>(w);
+        case 1: return unpack_c<1>(w);
+        case 2: return unpack_c<2>(w);
+        default: return unpack_c<3>(w);
+      }
+    } else {
+      return c == 0 ? unpack_c<0>(w) : unpack_c<1>(w);
+    }
+  }
+};
+
+template <int D> struct KFmt<16, D> {
+  static constexpr int kWords = D / 8;  // quarter = D/2 bytes of bf16
+  static constexpr float sigma = 1.f;
+  static constexpr bool bf16 = true;
+  __device__ static int channel(int c, int e) { return 8 * c + e; }
+  __device__ static u32x4_t unpack(const uint32_t (&w)[kWords], int c) {
+    u32x4_t r;
+    r[0] = w[4 * c]; r[1] = w[4 * c + 1]; r[2] = w[4 * c + 2]; r[3] = w[4 * c + 3];
+    return r;
+  }
+};
+
+// Load the lane's quarter row of key codes (kWords dwords).
+template <int KB, int D>
+__device__ __forceinline__ void load_kquarter(const uint8_t* p, uint32_t (&w)[KFmt<KB, D>::kWords]) {
+  constexpr int kW = KFmt<KB, D>::kWords;
+  if constexpr (KB == 3 && D == 64) {  // 6 bytes, 2-byte aligned
+    const uint16_t* s = reinterpret_cast<const uint16_t*>(p);
+    w[0] = s[0] | (static_cast<uint32_t>(s[1]) << 16);
+    w[1] = s[2];
+  } else if constexpr (kW == 1) {
+    w[0] = *reinterpret_cast<const uint32_t*>(p);
+  } else if constexpr (kW == 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    w[0] = v.x; w[1] = v.y;
+  } else if constexpr (kW == 3) {
+    const uint32_t* s = reinterpret_cast<const uint32_t*>(p);
+    w[0] = s[0]; w[1] = s[1]; w[2] = s[2];
+  } else {
+#pragma unroll
+    for (int j = 0; j < kW; j += 4) {
+      const uint4 v = *reinterpret_cast<const uint4*>(p + 4 * j);
+      w[j] = v.x; w[j + 1] = v.y; w[j + 2] = v.z; w[j + 3] = v.w;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Value formats. A lane (column n = lane % 16, token group g4 = lane / 16)
+// owns the channels [n*D/16, (n+1)*D/16) of 8 tokens; chunk c of the PV
+// product is output channel n*D/16 + c. Each fp16 pair holds two tokens'
+// centred codes sigma_c * (code - 2^(b-1)), exact.
+// ---------------------------------------------------------------------------
+template <int VB, int D> struct VFmt;
+
+// Bytes each lane reads from one token row, and where.
+template <int VB, int D>
+__device__ __forceinline__ int v_lane_offset(int n) {
+  constexpr int bits_per_lane = VB * D / 16;
+  if constexpr (VB == 3) return ((bits_per_lane * n) / 32) * 4;  // dword holding the first bit
+  else if constexpr (bits_per_lane >= 32) return n * bits_per_lane / 8;
+  else return ((bits_per_lane * n) / 32) * 4;  // sub-dword ranges: load the containing dword
+}
+
+template <int VB, int D> struct VRaw {
+  static constexpr int bits_per_lane = VB * D / 16;
+  static constexpr int kWords = VB == 3 ? 2 : (bits_per_lane >= 32 ? bits_per_lane / 32 : 1);
+};
+
+template <int VB, int D>
+__device__ __forceinline__ void load_vtoken(const uint8_t* p, uint32_t* w) {
+  constexpr int kW = VRaw<VB, D>::kWords;
+  if constexpr (VB == 3) {  // two dwords at a 4-byte aligned offset
+    const uint32_t* s = reinterpret_cast<const uint32_t*>(p);
+    w[0] = s[0];
+    w[1] = s[1];
+  } else if constexpr (kW == 1) {
+    w[0] = *reinterpret_cast<const uint32_t*>(p);
+  } else if constexpr (kW == 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    w[0] = v.x; w[1] = v.y;
+  } else {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  }
+}
+
+// Per token pair (t0 in the low fp16, t1 in the high fp16), value of chunk c.
+template <int VB, int D> struct VFmt {
+  static constexpr int kW = VRaw<VB, D>::kWords;
+  static constexpr bool bf16 = VB == 16;
+  static constexpr int kChunks = D / 16;
+  // Bring the lane's field of each token into the low 16 bits (per half) of a
+  // combined word, or for 3-bit into a 24-bit aligned value per token.
+  __device__ static float sigma(int c) {
+    if constexpr (VB == 4) return (c & 1) ? 16.f : 1.f;
+    else if constexpr (VB == 2) return D == 128 ? static_cast<float>(1 << (2 * (c < 5 ? c : c - 5)))
+                                                 : static_cast<float>(1 << (2 * c));
+    else if constexpr (VB == 3) return 128.f;
+    else return 1.f;
+  }
+};
+
+// Produce the B operand (4 dwords = 8 tokens) of value chunk c for one lane.
+// raw[e][*] are the 8 tokens' words; n is the lane's column.
+template <int VB, int D>
+__device__ __forceinline__ u32x4_t v_operand(const uint32_t (&raw)[8][VRaw<VB, D>::kWords], int n, int c) {
+  u32x4_t r;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const uint32_t* a = raw[2 * v];
+    const uint32_t* b = raw[2 * v + 1];
+    uint32_t out;
+    if constexpr (VB == 4) {
+      // channels [n*D/16, ...): D=128: the whole dword n; D=64: half (n & 1) of dword n/2
+      uint32_t sel;
+      if constexpr (D == 128) sel = c < 4 ? 0x05040100u : 0x07060302u;
+      else sel = (n & 1) ? 0x07060302u : 0x05040100u;
+      uint32_t x = perm_b32(b[0], a[0], sel);
+      const int cc = D == 128 ? (c & 3) : c;
+      if (cc >= 2) x >>= 8;
+      const uint32_t mask = (cc & 1) ? 0x00f000f0u : 0x000f000fu;
+      const float sg = (cc & 1) ? 16.f : 1.f;
+      out = and_or(x, mask, kBias);
+      const _Float16 off = static_cast<_Float16>(-(1024.f + 8.f * sg));
+      out = pk_add_h(out, half_bits(off) * 0x10001u);
+    } else if constexpr (VB == 2) {
+      uint32_t x;
+      int cc;
+      if constexpr (D == 128) {
+        x = perm_b32(b[0], a[0], (n & 1) ? 0x07060302u : 0x05040100u);
+        cc = c;
+        if (c >= 5) { x >>= 10; cc = c - 5; }
+      } else {
+        const uint32_t k = n & 3;
+        x = perm_b32(b[0], a[0], 0x0c000c00u | ((4 + k) << 16) | k);
+        cc = c;
+      }
+      out = and_or(x, 0x00030003u << (2 * cc), kBias);
+      const float sg = static_cast<float>(1 << (2 * cc));
+      const _Float16 off = static_cast<_Float16>(-(1024.f + 2.f * sg));
+      out = pk_add_h(out, half_bits(off) * 0x10001u);
+    } else if constexpr (VB == 8) {
+      const int word = D == 128 ? (c >> 2) : 0;
+      const uint32_t k = c & 3;
+      const uint32_t x = perm_b32(b[word], a[word], 0x0c000c00u | ((4 + k) << 16) | k);
+      out = x | kBias;
+      const _Float16 off = static_cast<_Float16>(-(1024.f + 128.f));
+      out = pk_add_h(out, half_bits(off) * 0x10001u);
+    } else if constexpr (VB == 3) {
+      constexpr int bpl = 3 * D / 16;  // 24 or 12 bits per lane
+      const uint32_t sh = (bpl * n) & 31;
+      const uint32_t wa = __builtin_amdgcn_alignbit(a[1], a[0], sh);
+      const uint32_t wb = __builtin_amdgcn_alignbit(b[1], b[0], sh);
+      const uint32_t ca = (wa >> (3 * c)) & 7u, cb = (wb >> (3 * c)) & 7u;
+      out = (((cb << 16) | ca) << 7) | kBias;
+      const _Float16 off = static_cast<_Float16>(-(1024.f + 4.f * 128.f));
+      out = pk_add_h(out, half_bits(off) * 0x10001u);
+    } else {  // bf16 values: channel n*D/16 + c is half (c & 1) of word c/2
+      const int word = c >> 1;
+      out = perm_b32(b[word], a[word], (c & 1) ? 0x07060302u : 0x05040100u);
+    }
+    r[v] = out;
+  }
+  return r;
+}
+
+template <int D>
+__device__ __forceinline__ int v_channel(int n, int c) { return n * (D / 16) + c; }
+
+// ---------------------------------------------------------------------------
+// The partial kernel.
+// ---------------------------------------------------------------------------
+template <int KB, int VB, int D>
+__global__ __launch_bounds__(64) void decode_partial_kernel(DecodeArgs a, float qscale) {
+  using KF = KFmt<KB, D>;
+  using VF = VFmt<VB, D>;
+  constexpr int NCK = D / 32;               // QK chunks (32 channels each)
+  constexpr int NCV = D / 16;               // PV chunks (16 output channels each)
+  constexpr int RBK = D * KB / 8;           // bytes per stored key row
+  constexpr int RBV = D * VB / 8;
+  constexpr int QBYTES = RBK / 4;           // a lane's quarter of a key row
+  constexpr int KW = KF::kWords;
+  constexpr int VW = VRaw<VB, D>::kWords;
+  constexpr bool KMETA = KB != 16, VMETA = VB != 16;
+  constexpr float NEG_INF = -__builtin_huge_valf();
+
+  __shared__ float qs[4][D];
+  __shared__ __attribute__((aligned(16))) uint16_t wt[2][4][64];
+  __shared__ __attribute__((aligned(16))) uint16_t wzero[8];
+
+  const int lane = threadIdx.x;
+  const int split = blockIdx.x;
+  const int hidx = blockIdx.y;
+  const int b = blockIdx.z;
+  const int h = a.heads[hidx];
+  const int G = a.group;
+  const int hq = a.hkv * G;
+  const int64_t koff = a.k_off[hidx], voff = a.v_off[hidx];
+  const int seq_len = a.seq_lens[b];
+  const int pages = min((seq_len + kBlockTokens - 1) / kBlockTokens, a.table_stride);
+  const int p0 = split * a.pages_per_split;
+  const int p1 = min(p0 + a.pages_per_split, pages);
+  const int slot = a.slot_base + split;
+
+  auto write_empty = [&]() {
+    for (int r = 0; r < G; ++r) {
+      const int64_t bg = static_cast<int64_t>(b) * hq + h * G + r;
+      float* po = a.part_o + (bg * a.total_slots + slot) * D;
+      for (int j = lane; j < D; j += 64) po[j] = 0.f;
+      if (lane == 0) {
+        a.part_ml[(bg * a.total_slots + slot) * 2] = NEG_INF;
+        a.part_ml[(bg * a.total_slots + slot) * 2 + 1] = 0.f;
+      }
+    }
+  };
+  if (p0 >= p1) { write_empty(); return; }
+
+  // ---- q' = R q for the G query heads of this KV head (LDS butterflies) ----
+  for (int e = lane; e < 4 * D; e += 64) {
+    const int r = e / D, ch = e % D;
+    float v = 0.f;
+    if (r < G) {
+      const int64_t qi = (static_cast<int64_t>(b) * hq + h * G + r) * D + ch;
+      v = a.q_bf16 ? bf16lo_to_f(static_cast<const uint16_t*>(a.q)[qi])
+                   : static_cast<const float*>(a.q)[qi];
+    }
+    qs[r][ch] = v;
+  }
+  if (lane < 8) wzero[lane] = 0;
+  __syncthreads();
+  for (int st = 1; st < a.had_block; st <<= 1) {
+    for (int pi = lane; pi < 2 * D; pi += 64) {
+      const int r = pi / (D / 2), jj = pi % (D / 2);
+      const int j = (jj / st) * 2 * st + (jj % st);
+      const float u = qs[r][j], v = qs[r][j + st];
+      qs[r][j] = u + v;
+      qs[r][j + st] = u - v;
+    }
+    __syncthreads();
+  }
+
+  // ---- QK A operands: row r = lane % 16 (query head), K-slots of quarter g4 ----
+  const int row = lane & 15;
+  const int g4 = lane >> 4;
+  float amax = 0.f;
+#pragma unroll
+  for (int c = 0; c < NCK; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float v = row < G ? qs[row][g4 * (D / 4) + KF::channel(c, e)] * qscale / KF::sigma : 0.f;
+      amax = fmaxf(amax, fabsf(v));
+    }
+  amax = wave_max(amax);
+  // Power-of-two scale keeping the fp16 halves away from subnormals.
+  float qsc = 1.f;
+  if (!KF::bf16 && amax > 0.f) {
+    int ex;
+    frexpf(amax, &ex);
+    qsc = ldexpf(1.f, 10 - ex);
+  }
+  u32x4_t ahi[NCK], alo[NCK];
+  double q1 = 0.0;  // sum of the A values actually used (bias correction)
+#pragma unroll
+  for (int c = 0; c < NCK; ++c) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      uint32_t hp = 0, lp = 0;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int e = 2 * v + half;
+        const float x = row < G ? qs[row][g4 * (D / 4) + KF::channel(c, e)] * qscale / KF::sigma * qsc : 0.f;
+        uint32_t hb, lb;
+        float hv, lv;
+        if constexpr (KF::bf16) {
+          hb = f_to_bf16_rne(x); hv = bf16lo_to_f(hb);
+          lb = f_to_bf16_rne(x - hv); lv = bf16lo_to_f(lb);
+        } else {
+          const _Float16 hh = static_cast<_Float16>(x);
+          hv = static_cast<float>(hh);
+          const _Float16 ll = static_cast<_Float16>(x - hv);
+          lv = static_cast<float>(ll);
+          hb = half_bits(hh); lb = half_bits(ll);
+        }
+        q1 += static_cast<double>(hv) + static_cast<double>(lv);
+        hp |= hb << (16 * half);
+        lp |= lb << (16 * half);
+      }
+      ahi[c][v] = hp;
+      alo[c][v] = lp;
+    }
+  }
+  // Reduce q1 over the four quarters (lanes row, row+16, row+32, row+48).
+  {
+    float q1f_hi = static_cast<float>(q1);
+    float q1f_lo = static_cast<float>(q1 - static_cast<double>(q1f_hi));
+    double t = q1;
+    t += static_cast<double>(shfl_xor(q1f_hi, 16)) + static_cast<double>(shfl_xor(q1f_lo, 16));
+    q1f_hi = static_cast<float>(t);
+    q1f_lo = static_cast<float>(t - static_cast<double>(q1f_hi));
+    t += static_cast<double>(shfl_xor(q1f_hi, 32)) + static_cast<double>(shfl_xor(q1f_lo, 32));
+    q1 = t;
+  }
+  // Per query head constants, broadcast from lane i (row i):
+  //   bias_i = 1024 * Q1_i (scaled units), q2_i = sum_j q~_ij (log2 units).
+  float biasq[4], q2[4];
+  const float inv_qsc = 1.f / qsc;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float q1i = __shfl(static_cast<float>(q1), i, 64);
+    biasq[i] = KF::bf16 ? 0.f : 1024.f * q1i;
+    q2[i] = q1i * KF::sigma * inv_qsc;
+  }
+
+  // ---- main loop over groups of four pages ----
+  float4_t acc[NCV];
+#pragma unroll
+  for (int c = 0; c < NCV; ++c) acc[c] = float4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+  float l_part[4] = {0.f, 0.f, 0.f, 0.f};
+  float mn_part[4] = {0.f, 0.f, 0.f, 0.f};
+
+  const int pl = lane >> 4;      // page of this lane in the packed (token) layout
+  const int tslot = lane & 15;   // token slot of this lane in that page
+  const int vcol = lane & 15;    // PV column (value channels) of this lane
+  const int vgrp = lane >> 4;    // PV token group of this lane
+  const uint8_t* pool = a.pool;
+  const int32_t* trow = a.table + static_cast<int64_t>(b) * a.table_stride;
+
+  for (int grp = p0; grp < p1; grp += 4) {
+    int64_t boff[4];
+    bool pv[4];
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      const int page = grp + pp;
+      int64_t blk = -1;
+      if (page < p1) blk = trow[page];
+      pv[pp] = blk >= 0 && blk < a.pool_blocks;
+      boff[pp] = pv[pp] ? blk * a.block_bytes : 0;
+    }
+    // -- loads: key quarters, metadata (token layout), value words --
+    uint32_t kraw[4][KW];
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      if (pv[pp]) {
+        load_kquarter<KB, D>(pool + boff[pp] + koff + tslot * RBK + g4 * QBYTES, kraw[pp]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < KW; ++j) kraw[pp][j] = 0;
+      }
+    }
+    const int64_t my_boff = pl == 0 ? boff[0] : pl == 1 ? boff[1] : pl == 2 ? boff[2] : boff[3];
+    const bool my_pv = pl == 0 ? pv[0] : pl == 1 ? pv[1] : pl == 2 ? pv[2] : pv[3];
+    const int tok = (grp + pl) * kBlockTokens + tslot;
+    const bool valid = my_pv && tok < seq_len;
+    float ks = 1.f, kmn = 0.f, vs = 1.f, vmn = 0.f;
+    if (valid) {
+      if constexpr (KMETA) {
+        const float2 mk = *reinterpret_cast<const float2*>(pool + my_boff + koff + kBlockTokens * RBK + tslot * kMetaBytes);
+        ks = mk.x; kmn = mk.y;
+      }
+      if constexpr (VMETA) {
+        const float2 mv = *reinterpret_cast<const float2*>(pool + my_boff + voff + kBlockTokens * RBV + tslot * kMetaBytes);
+        vs = mv.x; vmn = mv.y;
+      }
+    }
+    uint32_t vraw[2][8][VW];
+#pragma unroll
+    for (int pp2 = 0; pp2 < 2; ++pp2) {
+      const int pg = 2 * pp2 + (vgrp >> 1);
+      const int64_t vb = pg == 0 ? boff[0] : pg == 1 ? boff[1] : pg == 2 ? boff[2] : boff[3];
+      const bool vok = pg == 0 ? pv[0] : pg == 1 ? pv[1] : pg == 2 ? pv[2] : pv[3];
+      const uint8_t* base = pool + vb + voff + (8 * (vgrp & 1)) * RBV + v_lane_offset<VB, D>(vcol);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        bool ok = vok;
+        if constexpr (VB == 16) ok = ok && ((grp + pg) * kBlockTokens + 8 * (vgrp & 1) + e) < seq_len;
+        if (ok) {
+          load_vtoken<VB, D>(base + e * RBV, vraw[pp2][e]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < VW; ++j) vraw[pp2][e][j] = 0;
+        }
+      }
+    }
+
+    // -- QK: one 16x16 tile per page, rows = query heads, columns = tokens --
+    float4_t cq[4];
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      cq[pp] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NCK; ++c) {
+        const u32x4_t bk = KF::unpack(kraw[pp], c);
+        cq[pp] = mfma<KF::bf16>(ahi[c], bk, cq[pp]);
+        cq[pp] = mfma<KF::bf16>(alo[c], bk, cq[pp]);
+      }
+    }
+    // -- pack the four tiles: lane = token of the group, register i = head i --
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const auto r01 = __builtin_amdgcn_permlane16_swap(f_bits(cq[0][i]), f_bits(cq[1][i]), false, false);
+      const auto r23 = __builtin_amdgcn_permlane16_swap(f_bits(cq[2][i]), f_bits(cq[3][i]), false, false);
+      const auto r = __builtin_amdgcn_permlane32_swap(r01[0], r23[0], false, false);
+      sc[i] = bits_f(r[0]);
+    }
+
+    // -- online softmax (log2 units) --
+    const float ks_q = ks * inv_qsc;
+    const float vmid = VMETA ? vmn + static_cast<float>(1 << (VB - 1)) * vs : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i >= G) break;
+      float z;
+      if constexpr (KMETA) z = fmaf(ks_q, sc[i], fmaf(-ks_q, biasq[i], kmn * q2[i]));
+      else z = sc[i];
+      z = valid ? z : NEG_INF;
+      const float gm = wave_max(z);
+      if (gm > m_run[i]) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run[i] - gm);
+#pragma unroll
+        for (int c = 0; c < NCV; ++c) acc[c][i] *= alpha;
+        l_part[i] *= alpha;
+        mn_part[i] *= alpha;
+        m_run[i] = gm;
+      }
+      const float p = valid ? __builtin_amdgcn_exp2f(z - m_run[i]) : 0.f;
+      l_part[i] += p;
+      float w = p;
+      if constexpr (VMETA) {
+        w = p * vs;
+        mn_part[i] += valid ? p * vmid : 0.f;
+      }
+      uint32_t hb, lb;
+      if constexpr (VF::bf16) {
+        hb = f_to_bf16_rne(w);
+        lb = f_to_bf16_rne(w - bf16lo_to_f(hb));
+      } else {
+        const _Float16 hh = static_cast<_Float16>(w);
+        hb = half_bits(hh);
+        lb = half_bits(static_cast<_Float16>(w - static_cast<float>(hh)));
+      }
+      wt[0][i][lane] = static_cast<uint16_t>(hb);
+      wt[1][i][lane] = static_cast<uint16_t>(lb);
+    }
+    __syncthreads();
+
+    // -- PV: two 32-token steps --
+#pragma unroll
+    for (int pp2 = 0; pp2 < 2; ++pp2) {
+      const uint16_t* asrc;
+      if (row < 4 && row < G) asrc = &wt[0][row][32 * pp2 + 8 * vgrp];
+      else if (row >= 4 && row < 4 + G) asrc = &wt[1][row - 4][32 * pp2 + 8 * vgrp];
+      else asrc = wzero;
+      const uint4 av = *reinterpret_cast<const uint4*>(asrc);
+      const u32x4_t aw = u32x4_t{av.x, av.y, av.z, av.w};
+#pragma unroll
+      for (int c = 0; c < NCV; ++c) {
+        const u32x4_t bv = v_operand<VB, D>(vraw[pp2], vcol, c);
+        acc[c] = mfma<VF::bf16>(aw, bv, acc[c]);
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: combine hi/lo rows, add the min term, write the partials ----
+  float lsum[4], mnsum[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    lsum[i] = wave_sum(l_part[i]);
+    mnsum[i] = wave_sum(mn_part[i]);
+  }
+  float o[NCV][4];
+#pragma unroll
+  for (int c = 0; c < NCV; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t x = f_bits(acc[c][i]);
+      const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+      o[c][i] = (bits_f(r[0]) + bits_f(r[1])) / VF::sigma(c) + mnsum[i];
+    }
+  if (lane < 16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i >= G) break;
+      const int64_t bg = static_cast<int64_t>(b) * hq + h * G + i;
+      float* po = a.part_o + (bg * a.total_slots + slot) * D + v_channel<D>(vcol, 0);
+      if constexpr (NCV == 8) {
+        reinterpret_cast<float4*>(po)[0] = make_float4(o[0][i], o[1][i], o[2][i], o[3][i]);
+        reinterpret_cast<float4*>(po)[1] = make_float4(o[4][i], o[5][i], o[6][i], o[7][i]);
+      } else {
+        reinterpret_cast<float4*>(po)[0] = make_float4(o[0][i], o[1][i], o[2][i], o[3][i]);
+      }
+      if (lane == 0) {
+        float* ml = a.part_ml + (bg * a.total_slots + slot) * 2;
+        ml[0] = m_run[i];
+        ml[1] = lsum[i];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge of the split partials (all segments) and the inverse rotation.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(64) void decode_merge_kernel(MergeArgs a, float rs_n) {
+  constexpr int CPL = D / 64;  // channels per lane: [CPL*lane, CPL*lane + CPL)
+  constexpr float NEG_INF = -__builtin_huge_valf();
+  const int lane = threadIdx.x;
+  const int64_t bg = blockIdx.x;
+  const float* ml = a.part_ml + bg * a.total_slots * 2;
+  const float* po = a.part_o + bg * a.total_slots * D;
+  float mx = NEG_INF;
+  for (int s = 0; s < a.total_slots; ++s) mx = fmaxf(mx, ml[2 * s]);
+  float x[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) x[j] = 0.f;
+  if (mx != NEG_INF) {
+    float l = 0.f;
+    for (int s = 0; s < a.total_slots; ++s) {
+      const float ms = ml[2 * s];
+      if (ms == NEG_INF) continue;
+      const float wgt = __builtin_amdgcn_exp2f(ms - mx);
+      l = fmaf(wgt, ml[2 * s + 1], l);
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) x[j] = fmaf(wgt, po[static_cast<int64_t>(s) * D + CPL * lane + j], x[j]);
+    }
+    const float inv = 1.f / l;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) x[j] *= inv;
+  }
+  // o = R^T o' (H symmetric): butterflies in-lane for stride < CPL, else across lanes.
+  if constexpr (CPL == 2) {
+    if (a.had_block >= 2) {
+      const float u = x[0], v = x[1];
+      x[0] = u + v;
+      x[1] = u - v;
+    }
+  }
+  for (int m = 1; m * CPL < a.had_block; m <<= 1) {
+    const bool upper = (lane & m) != 0;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const float y = shfl_xor(x[j], m);
+      x[j] = upper ? (y - x[j]) : (x[j] + y);
+    }
+  }
+  float* out = a.out + bg * D + CPL * lane;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) out[j] = x[j] * rs_n;
+}
+
+template <int KB, int VB, int D>
+hipError_t launch_partial_t(const DecodeArgs& a, int n_splits, int batch, float qscale, hipStream_t s) {
+  dim3 grid(n_splits, a.n_heads, batch);
+  hipLaunchKernelGGL((decode_partial_kernel<KB, VB, D>), grid, dim3(64), 0, s, a, qscale);
+  return hipGetLastError();
+}
+
+template <int KB, int D>
+hipError_t dispatch_v(const DecodeArgs& a, int vbits, int n_splits, int batch, float qs, hipStream_t s) {
+  switch (vbits) {
+    case 2: return launch_partial_t<KB, 2, D>(a, n_splits, batch, qs, s);
+    case 3: return launch_partial_t<KB, 3, D>(a, n_splits, batch, qs, s);
+    case 4: return launch_partial_t<KB, 4, D>(a, n_splits, batch, qs, s);
+    case 8: return launch_partial_t<KB, 8, D>(a, n_splits, batch, qs, s);
+    case 16: return launch_partial_t<KB, 16, D>(a, n_splits, batch, qs, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int D>
+hipError_t dispatch_k(const DecodeArgs& a, int kbits, int vbits, int n_splits, int batch, float qs, hipStream_t s) {
+  switch (kbits) {
+    case 2: return dispatch_v<2, D>(a, vbits, n_splits, batch, qs, s);
+    case 3: return dispatch_v<3, D>(a, vbits, n_splits, batch, qs, s);
+    case 4: return dispatch_v<4, D>(a, vbits, n_splits, batch, qs, s);
+    case 8: return dispatch_v<8, D>(a, vbits, n_splits, batch, qs, s);
+    case 16: return dispatch_v<16, D>(a, vbits, n_splits, batch, qs, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_partial(const DecodeArgs& a, int kbits, int vbits, int d, int n_splits,
+                                 int batch, hipStream_t s) {
+  if (n_splits == 0 || batch == 0 || a.n_heads == 0) return hipSuccess;
+  // q~ = (R q) * log2(e) / sqrt(d), with R's 1/sqrt(n) folded in.
+  const float qscale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(a.had_block) * d));
+  if (d == 128) return dispatch_k<128>(a, kbits, vbits, n_splits, batch, qscale, s);
+  if (d == 64) return dispatch_k<64>(a, kbits, vbits, n_splits, batch, qscale, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_merge(const MergeArgs& a, hipStream_t s) {
+  if (a.batch * a.hq == 0) return hipSuccess;
+  const float rs = static_cast<float>(1.0 / std::sqrt(static_cast<double>(a.had_block)));
+  dim3 grid(a.batch * a.hq);
+  if (a.d == 128) hipLaunchKernelGGL((decode_merge_kernel<128>), grid, dim3(64), 0, s, a, rs);
+  else if (a.d == 64) hipLaunchKernelGGL((decode_merge_kernel<64>), grid, dim3(64), 0, s, a, rs);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace kvq

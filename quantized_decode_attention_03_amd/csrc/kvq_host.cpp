@@ -1,0 +1,482 @@
+// libkvq host side: argument checks, layout, bit planning, page allocation,
+// split planning and kernel dispatch behind the C ABI in include/kvq.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kvq.h"
+#include "kvq_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kvq_status fail(kvq_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+kvq_status ok() {
+  g_last_error.clear();
+  return KVQ_OK;
+}
+
+kvq_status device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(KVQ_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+bool valid_bits(int b) { return b == 2 || b == 3 || b == 4 || b == 8 || b == 16; }
+
+int64_t row_bytes(int d, int b) { return static_cast<int64_t>(d) * b / 8; }
+int64_t area_bytes(int d, int b) {
+  return KVQ_BLOCK_TOKENS * row_bytes(d, b) + (b == 16 ? 0 : KVQ_BLOCK_TOKENS * 8);
+}
+
+// Checks the inputs of a layout and that its outputs match them.
+kvq_status check_layout(const kvq_layout* L, const char* who) {
+  if (!L) return fail(KVQ_ERR_ARG, "%s: null layout", who);
+  if (L->block_tokens != KVQ_BLOCK_TOKENS) return fail(KVQ_ERR_ARG, "%s: block_tokens must be 16", who);
+  if (L->num_kv_heads < 1 || L->num_kv_heads > KVQ_MAX_KV_HEADS)
+    return fail(KVQ_ERR_ARG, "%s: num_kv_heads %d out of [1, %d]", who, L->num_kv_heads, KVQ_MAX_KV_HEADS);
+  if (L->group < 1 || L->group > 4) return fail(KVQ_ERR_ARG, "%s: group %d out of [1, 4]", who, L->group);
+  if (L->head_dim != 64 && L->head_dim != 128)
+    return fail(KVQ_ERR_UNSUPPORTED, "%s: head_dim %d (built: 64, 128)", who, L->head_dim);
+  if (!is_pow2(L->had_block) || L->had_block > L->head_dim)
+    return fail(KVQ_ERR_ARG, "%s: had_block %d must be a power of two in [1, head_dim]", who, L->had_block);
+  for (int h = 0; h < L->num_kv_heads; ++h) {
+    if (!valid_bits(L->bits_k[h]) || !valid_bits(L->bits_v[h]))
+      return fail(KVQ_ERR_ARG, "%s: head %d bits (%d, %d) not in {2,3,4,8,16}", who, h, L->bits_k[h], L->bits_v[h]);
+  }
+  return KVQ_OK;
+}
+
+kvq_status check_layout_ready(const kvq_layout* L, const char* who) {
+  kvq_status s = check_layout(L, who);
+  if (s != KVQ_OK) return s;
+  kvq_layout tmp = *L;
+  if (kvq_layout_init(&tmp) != KVQ_OK || tmp.block_bytes != L->block_bytes ||
+      std::memcmp(tmp.k_off, L->k_off, sizeof(tmp.k_off)) != 0 ||
+      std::memcmp(tmp.v_off, L->v_off, sizeof(tmp.v_off)) != 0)
+    return fail(KVQ_ERR_ARG, "%s: layout outputs stale; call kvq_layout_init", who);
+  return KVQ_OK;
+}
+
+// Split plan of one segment: pages per split (a multiple of 4) and split count.
+struct SplitPlan {
+  int pages_per_split;
+  int n_splits;
+};
+
+SplitPlan plan_splits(const kvq_segment& s, int batch) {
+  const int pages = (std::max(s.max_len, 0) + KVQ_BLOCK_TOKENS - 1) / KVQ_BLOCK_TOKENS;
+  SplitPlan p{4, 0};
+  if (pages == 0 || batch == 0) return p;
+  int pps = 0;
+  if (const char* env = std::getenv("KVQ_SPLIT_PAGES")) pps = std::atoi(env);
+  if (pps <= 0) {
+    // Enough waves to fill 256 CUs several times over, but at least 16 pages
+    // (4 groups) per wave so the prologue and the partial write amortise.
+    const int64_t units = static_cast<int64_t>(batch) * s.layout->num_kv_heads;
+    const int64_t target_waves = 4096;
+    const int64_t want_splits = std::max<int64_t>(1, (target_waves + units - 1) / units);
+    pps = static_cast<int>((pages + want_splits - 1) / want_splits);
+    pps = std::max(pps, 16);
+  }
+  pps = (pps + 3) / 4 * 4;
+  p.pages_per_split = pps;
+  p.n_splits = (pages + pps - 1) / pps;
+  return p;
+}
+
+kvq_status check_segments(const kvq_segment* segs, int n_segs, int batch, const char* who) {
+  if (!segs || n_segs < 1) return fail(KVQ_ERR_ARG, "%s: need at least one segment", who);
+  if (batch < 0) return fail(KVQ_ERR_ARG, "%s: batch %d < 0", who, batch);
+  for (int i = 0; i < n_segs; ++i) {
+    const kvq_segment& s = segs[i];
+    kvq_status st = check_layout_ready(s.layout, who);
+    if (st != KVQ_OK) return st;
+    const kvq_layout& L0 = *segs[0].layout;
+    const kvq_layout& L = *s.layout;
+    if (L.num_kv_heads != L0.num_kv_heads || L.group != L0.group || L.head_dim != L0.head_dim ||
+        L.had_block != L0.had_block)
+      return fail(KVQ_ERR_ARG, "%s: segment %d geometry differs from segment 0", who, i);
+    if (s.max_len < 0) return fail(KVQ_ERR_ARG, "%s: segment %d max_len < 0", who, i);
+    if (s.max_len > 0 && batch > 0) {
+      if (!s.pool || !s.block_table || !s.seq_lens) return fail(KVQ_ERR_ARG, "%s: segment %d null pointer", who, i);
+      if (s.pool_blocks < 1) return fail(KVQ_ERR_ARG, "%s: segment %d pool_blocks < 1", who, i);
+      const int pages = (s.max_len + KVQ_BLOCK_TOKENS - 1) / KVQ_BLOCK_TOKENS;
+      if (s.table_stride < pages)
+        return fail(KVQ_ERR_ARG, "%s: segment %d table_stride %d < ceil(max_len/16) = %d", who, i, s.table_stride, pages);
+    } else if (!s.seq_lens && batch > 0) {
+      return fail(KVQ_ERR_ARG, "%s: segment %d null seq_lens", who, i);
+    }
+  }
+  return KVQ_OK;
+}
+
+int total_slots(const kvq_segment* segs, int n_segs, int batch, std::vector<SplitPlan>* plans) {
+  int total = 0;
+  for (int i = 0; i < n_segs; ++i) {
+    SplitPlan p = plan_splits(segs[i], batch);
+    if (plans) plans->push_back(p);
+    total += p.n_splits;
+  }
+  return total;
+}
+
+size_t workspace_bytes(int batch, int hq, int d, int slots) {
+  if (slots == 0) slots = 1;
+  return static_cast<size_t>(batch) * hq * slots * (static_cast<size_t>(d) + 2) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvq_abi_version(void) { return KVQ_ABI_VERSION; }
+
+const char* kvq_status_str(kvq_status s) {
+  switch (s) {
+    case KVQ_OK: return "KVQ_OK";
+    case KVQ_ERR_ARG: return "KVQ_ERR_ARG";
+    case KVQ_ERR_UNSUPPORTED: return "KVQ_ERR_UNSUPPORTED";
+    case KVQ_ERR_BUDGET: return "KVQ_ERR_BUDGET";
+    case KVQ_ERR_WORKSPACE: return "KVQ_ERR_WORKSPACE";
+    case KVQ_ERR_DEVICE: return "KVQ_ERR_DEVICE";
+    case KVQ_ERR_CAPACITY: return "KVQ_ERR_CAPACITY";
+  }
+  return "KVQ_ERR_UNKNOWN";
+}
+
+const char* kvq_last_error(void) { return g_last_error.c_str(); }
+
+kvq_status kvq_layout_init(kvq_layout* L) {
+  kvq_status s = check_layout(L, "kvq_layout_init");
+  if (s != KVQ_OK) return s;
+  int64_t off = 0;
+  std::memset(L->k_off, 0, sizeof(L->k_off));
+  std::memset(L->v_off, 0, sizeof(L->v_off));
+  for (int h = 0; h < L->num_kv_heads; ++h) {
+    L->k_off[h] = off;
+    off += area_bytes(L->head_dim, L->bits_k[h]);
+  }
+  for (int h = 0; h < L->num_kv_heads; ++h) {
+    L->v_off[h] = off;
+    off += area_bytes(L->head_dim, L->bits_v[h]);
+  }
+  L->block_bytes = off;
+  return ok();
+}
+
+kvq_status kvq_plan_bits(int32_t n, const float* w, double alpha, double beta, const int32_t* ladder,
+                         int32_t n_ladder, int64_t budget_bits, int32_t* bits_out, int64_t* leftover_out) {
+  if (n < 1 || !w || !ladder || !bits_out) return fail(KVQ_ERR_ARG, "kvq_plan_bits: null pointer or n < 1");
+  if (n_ladder < 1 || n_ladder > 16) return fail(KVQ_ERR_ARG, "kvq_plan_bits: n_ladder %d out of [1, 16]", n_ladder);
+  if (!(alpha > 0.0) || !(beta > 1.0) || !std::isfinite(alpha) || !std::isfinite(beta))
+    return fail(KVQ_ERR_ARG, "kvq_plan_bits: need alpha > 0 and beta > 1");
+  std::vector<int> lad(ladder, ladder + n_ladder);
+  std::sort(lad.begin(), lad.end());
+  for (int i = 0; i < n_ladder; ++i) {
+    if (lad[i] < 1) return fail(KVQ_ERR_ARG, "kvq_plan_bits: ladder widths must be positive");
+    if (i && lad[i] == lad[i - 1]) return fail(KVQ_ERR_ARG, "kvq_plan_bits: ladder widths must be distinct");
+  }
+  for (int i = 0; i < n; ++i)
+    if (!(w[i] > 0.f) || !std::isfinite(w[i])) return fail(KVQ_ERR_ARG, "kvq_plan_bits: w[%d] must be positive", i);
+  const int64_t lo = static_cast<int64_t>(n) * lad.front(), hi = static_cast<int64_t>(n) * lad.back();
+  if (budget_bits < lo || budget_bits > hi)
+    return fail(KVQ_ERR_BUDGET, "kvq_plan_bits: budget %lld outside [%lld, %lld]", static_cast<long long>(budget_bits),
+                static_cast<long long>(lo), static_cast<long long>(hi));
+  // D(b) at every ladder rung, in double.
+  std::vector<double> dist(n_ladder);
+  for (int k = 0; k < n_ladder; ++k) dist[k] = alpha * std::pow(beta, -static_cast<double>(lad[k]));
+  std::vector<int> level(n, 0);
+  int64_t remaining = budget_bits - lo;
+  while (remaining > 0) {
+    int best = -1;
+    double best_gain = -1.0;
+    for (int i = 0; i < n; ++i) {
+      const int lv = level[i];
+      if (lv + 1 >= n_ladder) continue;
+      const int step = lad[lv + 1] - lad[lv];
+      if (step > remaining) continue;
+      const double gain = static_cast<double>(w[i]) * (dist[lv] - dist[lv + 1]) / step;
+      if (gain > best_gain) {
+        best = i;
+        best_gain = gain;
+      }
+    }
+    if (best < 0) break;
+    remaining -= lad[level[best] + 1] - lad[level[best]];
+    ++level[best];
+  }
+  for (int i = 0; i < n; ++i) bits_out[i] = lad[level[i]];
+  if (leftover_out) *leftover_out = remaining;
+  if (remaining != 0)
+    return fail(KVQ_ERR_BUDGET, "kvq_plan_bits: %lld bits could not be placed on the ladder",
+                static_cast<long long>(remaining));
+  return ok();
+}
+
+kvq_status kvq_logquant_classes(int32_t total, int32_t window, int8_t* cls_out) {
+  if (total < 0 || window < 1) return fail(KVQ_ERR_ARG, "kvq_logquant_classes: total < 0 or window < 1");
+  if (total > 0 && !cls_out) return fail(KVQ_ERR_ARG, "kvq_logquant_classes: null output");
+  for (int32_t pos = 0; pos < total; ++pos) {
+    const int64_t dist = static_cast<int64_t>(total) - 1 - pos;
+    if (dist < window) {
+      cls_out[pos] = 0;
+      continue;
+    }
+    const int64_t r = dist - window;
+    // span k: (2^k - 1) W <= r < (2^(k+1) - 1) W, i.e. 2^k <= r/W + 1 < 2^(k+1)
+    const int64_t q = r / window + 1;
+    int k = 63 - __builtin_clzll(static_cast<unsigned long long>(q));
+    const int64_t start = ((int64_t{1} << k) - 1) * window;
+    cls_out[pos] = ((r - start) & ((int64_t{1} << k) - 1)) == 0 ? 1 : 2;
+  }
+  return ok();
+}
+
+kvq_status kvq_page_alloc(const int32_t* free_list, int32_t n_free, int32_t* cursor, int32_t batch,
+                          const int32_t* old_len, const int32_t* new_len, int32_t* block_table,
+                          int32_t table_stride) {
+  if (!cursor || batch < 0 || n_free < 0) return fail(KVQ_ERR_ARG, "kvq_page_alloc: bad arguments");
+  if (batch > 0 && (!old_len || !new_len || !block_table)) return fail(KVQ_ERR_ARG, "kvq_page_alloc: null pointer");
+  if (n_free > 0 && !free_list) return fail(KVQ_ERR_ARG, "kvq_page_alloc: null free list");
+  if (*cursor < 0 || *cursor > n_free) return fail(KVQ_ERR_ARG, "kvq_page_alloc: cursor out of range");
+  int64_t need = 0;
+  for (int s = 0; s < batch; ++s) {
+    if (old_len[s] < 0 || new_len[s] < old_len[s])
+      return fail(KVQ_ERR_ARG, "kvq_page_alloc: seq %d needs 0 <= old_len <= new_len", s);
+    const int have = (old_len[s] + KVQ_BLOCK_TOKENS - 1) / KVQ_BLOCK_TOKENS;
+    const int want = (new_len[s] + KVQ_BLOCK_TOKENS - 1) / KVQ_BLOCK_TOKENS;
+    if (want > table_stride)
+      return fail(KVQ_ERR_ARG, "kvq_page_alloc: seq %d needs %d blocks > table_stride %d", s, want, table_stride);
+    need += want - have;
+  }
+  if (need > n_free - *cursor)
+    return fail(KVQ_ERR_CAPACITY, "kvq_page_alloc: need %lld blocks, %d free", static_cast<long long>(need),
+                n_free - *cursor);
+  for (int s = 0; s < batch; ++s) {
+    const int have = (old_len[s] + KVQ_BLOCK_TOKENS - 1) / KVQ_BLOCK_TOKENS;
+    const int want = (new_len[s] + KVQ_BLOCK_TOKENS - 1) / KVQ_BLOCK_TOKENS;
+    for (int lb = have; lb < want; ++lb)
+      block_table[static_cast<int64_t>(s) * table_stride + lb] = free_list[(*cursor)++];
+  }
+  return ok();
+}
+
+kvq_status kvq_quantize_append(const kvq_layout* L, void* pool, int64_t pool_blocks, const int32_t* block_table,
+                               int32_t table_stride, int32_t batch, const int32_t* start_pos, int32_t n_new,
+                               const void* k, const void* v, kvq_dtype in_dtype, kvq_stream stream) {
+  kvq_status st = check_layout_ready(L, "kvq_quantize_append");
+  if (st != KVQ_OK) return st;
+  if (batch < 0 || n_new < 0) return fail(KVQ_ERR_ARG, "kvq_quantize_append: batch/n_new < 0");
+  if (in_dtype != KVQ_F32 && in_dtype != KVQ_BF16) return fail(KVQ_ERR_ARG, "kvq_quantize_append: bad dtype");
+  if (batch == 0 || n_new == 0) return ok();
+  if (!pool || !block_table || !start_pos || !k || !v) return fail(KVQ_ERR_ARG, "kvq_quantize_append: null pointer");
+  if (pool_blocks < 1 || table_stride < 1) return fail(KVQ_ERR_ARG, "kvq_quantize_append: empty pool or table");
+  if (static_cast<int64_t>(batch) * n_new > (int64_t{1} << 31) / 8)
+    return fail(KVQ_ERR_ARG, "kvq_quantize_append: too many rows in one call");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  for (int half = 0; half < 2; ++half) {
+    const int32_t* bits = half ? L->bits_v : L->bits_k;
+    const int64_t* offs = half ? L->v_off : L->k_off;
+    bool done[KVQ_MAX_KV_HEADS] = {};
+    for (int h0 = 0; h0 < L->num_kv_heads; ++h0) {
+      if (done[h0]) continue;
+      kvq::AppendArgs a{};
+      a.pool = static_cast<uint8_t*>(pool);
+      a.pool_blocks = pool_blocks;
+      a.block_bytes = L->block_bytes;
+      a.table = block_table;
+      a.table_stride = table_stride;
+      a.start_pos = start_pos;
+      a.src = half ? v : k;
+      a.src_bf16 = in_dtype == KVQ_BF16;
+      a.batch = batch;
+      a.n_new = n_new;
+      a.hkv = L->num_kv_heads;
+      a.d = L->head_dim;
+      a.had_block = L->had_block;
+      a.bits = bits[h0];
+      for (int h = h0; h < L->num_kv_heads; ++h) {
+        if (!done[h] && bits[h] == bits[h0]) {
+          a.heads[a.n_heads] = h;
+          a.area_off[a.n_heads] = offs[h];
+          ++a.n_heads;
+          done[h] = true;
+        }
+      }
+      hipError_t e = kvq::launch_append(a, 0, s);
+      if (e != hipSuccess) return device_status(e, "kvq_quantize_append launch");
+    }
+  }
+  return ok();
+}
+
+kvq_status kvq_dequant(const kvq_layout* L, const void* pool, int64_t pool_blocks, const int32_t* block_table,
+                       int32_t table_stride, int32_t seq, int32_t pos0, int32_t n, int32_t rotated, float* k_out,
+                       float* v_out, kvq_stream stream) {
+  kvq_status st = check_layout_ready(L, "kvq_dequant");
+  if (st != KVQ_OK) return st;
+  if (n < 0 || pos0 < 0 || seq < 0) return fail(KVQ_ERR_ARG, "kvq_dequant: negative seq, pos0 or n");
+  if (n == 0) return ok();
+  if (!pool || !block_table || !k_out || !v_out) return fail(KVQ_ERR_ARG, "kvq_dequant: null pointer");
+  if (pool_blocks < 1) return fail(KVQ_ERR_ARG, "kvq_dequant: empty pool");
+  const int64_t last_page = (static_cast<int64_t>(pos0) + n - 1) / KVQ_BLOCK_TOKENS;
+  if (last_page >= table_stride)
+    return fail(KVQ_ERR_ARG, "kvq_dequant: tokens [%d, %d) exceed the table row (%d blocks)", pos0, pos0 + n,
+                table_stride);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  for (int half = 0; half < 2; ++half) {
+    const int32_t* bits = half ? L->bits_v : L->bits_k;
+    const int64_t* offs = half ? L->v_off : L->k_off;
+    bool done[KVQ_MAX_KV_HEADS] = {};
+    for (int h0 = 0; h0 < L->num_kv_heads; ++h0) {
+      if (done[h0]) continue;
+      kvq::DequantArgs a{};
+      a.pool = static_cast<const uint8_t*>(pool);
+      a.pool_blocks = pool_blocks;
+      a.block_bytes = L->block_bytes;
+      a.table_row = block_table + static_cast<int64_t>(seq) * table_stride;
+      a.pos0 = pos0;
+      a.n = n;
+      a.hkv = L->num_kv_heads;
+      a.d = L->head_dim;
+      a.had_block = L->had_block;
+      a.rotated = rotated != 0;
+      a.bits = bits[h0];
+      a.out = half ? v_out : k_out;
+      for (int h = h0; h < L->num_kv_heads; ++h) {
+        if (!done[h] && bits[h] == bits[h0]) {
+          a.heads[a.n_heads] = h;
+          a.area_off[a.n_heads] = offs[h];
+          ++a.n_heads;
+          done[h] = true;
+        }
+      }
+      hipError_t e = kvq::launch_dequant(a, s);
+      if (e != hipSuccess) return device_status(e, "kvq_dequant launch");
+    }
+  }
+  return ok();
+}
+
+kvq_status kvq_decode_workspace_bytes(const kvq_segment* segs, int32_t n_segs, int32_t batch, size_t* bytes) {
+  if (!bytes) return fail(KVQ_ERR_ARG, "kvq_decode_workspace_bytes: null output");
+  kvq_status st = check_segments(segs, n_segs, batch, "kvq_decode_workspace_bytes");
+  if (st != KVQ_OK) return st;
+  const kvq_layout& L = *segs[0].layout;
+  *bytes = workspace_bytes(batch, L.num_kv_heads * L.group, L.head_dim, total_slots(segs, n_segs, batch, nullptr));
+  return ok();
+}
+
+kvq_status kvq_decode_partial(const kvq_segment* segs, int32_t n_segs, int32_t batch, const void* q,
+                              kvq_dtype q_dtype, void* ws, size_t ws_bytes, kvq_stream stream) {
+  kvq_status st = check_segments(segs, n_segs, batch, "kvq_decode_partial");
+  if (st != KVQ_OK) return st;
+  if (q_dtype != KVQ_F32 && q_dtype != KVQ_BF16) return fail(KVQ_ERR_ARG, "kvq_decode_partial: bad q dtype");
+  if (batch == 0) return ok();
+  if (!q || !ws) return fail(KVQ_ERR_ARG, "kvq_decode_partial: null q or workspace");
+  const kvq_layout& L0 = *segs[0].layout;
+  const int hq = L0.num_kv_heads * L0.group;
+  std::vector<SplitPlan> plans;
+  const int slots = total_slots(segs, n_segs, batch, &plans);
+  const size_t need = workspace_bytes(batch, hq, L0.head_dim, slots);
+  if (ws_bytes < need)
+    return fail(KVQ_ERR_WORKSPACE, "kvq_decode_partial: workspace %zu < %zu bytes", ws_bytes, need);
+  float* part_o = static_cast<float*>(ws);
+  float* part_ml = part_o + static_cast<size_t>(batch) * hq * std::max(slots, 1) * L0.head_dim;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int slot_base = 0;
+  for (int i = 0; i < n_segs; ++i) {
+    const kvq_segment& sg = segs[i];
+    const kvq_layout& L = *sg.layout;
+    const SplitPlan& p = plans[i];
+    if (p.n_splits > 0) {
+      bool done[KVQ_MAX_KV_HEADS] = {};
+      for (int h0 = 0; h0 < L.num_kv_heads; ++h0) {
+        if (done[h0]) continue;
+        kvq::DecodeArgs a{};
+        a.pool = static_cast<const uint8_t*>(sg.pool);
+        a.pool_blocks = sg.pool_blocks;
+        a.block_bytes = L.block_bytes;
+        a.table = sg.block_table;
+        a.table_stride = sg.table_stride;
+        a.seq_lens = sg.seq_lens;
+        a.q = q;
+        a.q_bf16 = q_dtype == KVQ_BF16;
+        a.hkv = L.num_kv_heads;
+        a.group = L.group;
+        a.had_block = L.had_block;
+        a.pages_per_split = p.pages_per_split;
+        a.slot_base = slot_base;
+        a.total_slots = slots;
+        a.part_o = part_o;
+        a.part_ml = part_ml;
+        for (int h = h0; h < L.num_kv_heads; ++h) {
+          if (!done[h] && L.bits_k[h] == L.bits_k[h0] && L.bits_v[h] == L.bits_v[h0]) {
+            a.heads[a.n_heads] = h;
+            a.k_off[a.n_heads] = L.k_off[h];
+            a.v_off[a.n_heads] = L.v_off[h];
+            ++a.n_heads;
+            done[h] = true;
+          }
+        }
+        hipError_t e = kvq::launch_decode_partial(a, L.bits_k[h0], L.bits_v[h0], L.head_dim, p.n_splits, batch, s);
+        if (e != hipSuccess) return device_status(e, "kvq_decode_partial launch");
+      }
+    }
+    slot_base += p.n_splits;
+  }
+  return ok();
+}
+
+kvq_status kvq_decode_merge(const kvq_segment* segs, int32_t n_segs, int32_t batch, float* out, void* ws,
+                            size_t ws_bytes, kvq_stream stream) {
+  kvq_status st = check_segments(segs, n_segs, batch, "kvq_decode_merge");
+  if (st != KVQ_OK) return st;
+  if (batch == 0) return ok();
+  if (!out || !ws) return fail(KVQ_ERR_ARG, "kvq_decode_merge: null output or workspace");
+  const kvq_layout& L0 = *segs[0].layout;
+  const int hq = L0.num_kv_heads * L0.group;
+  const int slots = total_slots(segs, n_segs, batch, nullptr);
+  const size_t need = workspace_bytes(batch, hq, L0.head_dim, slots);
+  if (ws_bytes < need) return fail(KVQ_ERR_WORKSPACE, "kvq_decode_merge: workspace %zu < %zu bytes", ws_bytes, need);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // With no split at all the merge kernel still runs and writes zero rows
+  // (no memset node, so the call stays safe to capture in a graph).
+  kvq::MergeArgs a{};
+  a.part_o = static_cast<const float*>(ws);
+  a.part_ml = a.part_o + static_cast<size_t>(batch) * hq * slots * L0.head_dim;
+  a.batch = batch;
+  a.hq = hq;
+  a.d = L0.head_dim;
+  a.had_block = L0.had_block;
+  a.total_slots = slots;
+  a.out = out;
+  return device_status(kvq::launch_decode_merge(a, s), "kvq_decode_merge launch");
+}
+
+kvq_status kvq_decode_attn(const kvq_segment* segs, int32_t n_segs, int32_t batch, const void* q, kvq_dtype q_dtype,
+                           float* out, void* ws, size_t ws_bytes, kvq_stream stream) {
+  kvq_status st = kvq_decode_partial(segs, n_segs, batch, q, q_dtype, ws, ws_bytes, stream);
+  if (st != KVQ_OK) return st;
+  return kvq_decode_merge(segs, n_segs, batch, out, ws, ws_bytes, stream);
+}
+
+}  // extern "C"

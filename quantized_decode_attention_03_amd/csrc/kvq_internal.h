@@ -1,0 +1,78 @@
+// Internal interface between the libkvq host code and its kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq.h"
+
+namespace kvq {
+
+// One append launch: every row of one KV half (K or V) for a set of heads
+// that share a bit width.
+struct AppendArgs {
+  uint8_t* pool;
+  int64_t pool_blocks;
+  int64_t block_bytes;
+  const int32_t* table;
+  int32_t table_stride;
+  const int32_t* start_pos;
+  const void* src;      // [batch][n_new][hkv][d]
+  int32_t src_bf16;
+  int32_t batch, n_new, hkv, d, had_block;
+  int32_t n_heads;      // heads in this launch
+  int32_t bits;         // shared bit width of these heads
+  int32_t heads[KVQ_MAX_KV_HEADS];
+  int64_t area_off[KVQ_MAX_KV_HEADS];  // byte offset of each listed head's area in a block
+};
+
+struct DequantArgs {
+  const uint8_t* pool;
+  int64_t pool_blocks;
+  int64_t block_bytes;
+  const int32_t* table_row;  // this sequence's table row
+  int32_t pos0, n, hkv, d, had_block, rotated;
+  int32_t n_heads, bits;
+  int32_t heads[KVQ_MAX_KV_HEADS];
+  int64_t area_off[KVQ_MAX_KV_HEADS];
+  float* out;  // [n][hkv][d]
+};
+
+// One partial-decode launch: one segment, the heads of that segment whose
+// (K bits, V bits) pair is (kbits, vbits).
+struct DecodeArgs {
+  const uint8_t* pool;
+  int64_t pool_blocks;
+  int64_t block_bytes;
+  const int32_t* table;
+  int32_t table_stride;
+  const int32_t* seq_lens;
+  const void* q;       // [batch][hkv*group][d]
+  int32_t q_bf16;
+  int32_t hkv, group, had_block;
+  int32_t pages_per_split;
+  int32_t slot_base;   // first split slot of this segment
+  int32_t total_slots; // split slots over all segments
+  int32_t n_heads;
+  int32_t heads[KVQ_MAX_KV_HEADS];
+  int64_t k_off[KVQ_MAX_KV_HEADS];
+  int64_t v_off[KVQ_MAX_KV_HEADS];
+  float* part_o;       // [batch][hq][total_slots][d]
+  float* part_ml;      // [batch][hq][total_slots][2]  (running max in log2 units, sum)
+};
+
+struct MergeArgs {
+  const float* part_o;
+  const float* part_ml;
+  int32_t batch, hq, d, had_block, total_slots;
+  float* out;  // [batch][hq][d]
+};
+
+// Launchers return hipSuccess or the launch error; they never synchronise.
+hipError_t launch_append(const AppendArgs& a, int n_splits_rows, hipStream_t s);
+hipError_t launch_dequant(const DequantArgs& a, hipStream_t s);
+hipError_t launch_decode_partial(const DecodeArgs& a, int kbits, int vbits, int d, int n_splits,
+                                 int batch, hipStream_t s);
+hipError_t launch_decode_merge(const MergeArgs& a, hipStream_t s);
+
+}  // namespace kvq

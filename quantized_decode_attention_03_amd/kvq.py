@@ -1,0 +1,309 @@
+"""Python binding of libkvq: the C ABI in include/kvq.h, one function per entry point.
+
+Argument marshalling only. Device buffers are torch tensors (device memory and
+streams come from torch); every step of the hot path runs in libkvq's HIP
+kernels. There is no fallback: if libkvq.so is missing or a call fails, an
+exception is raised.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkvq.so")
+
+KVQ_ABI_VERSION = 1
+KVQ_MAX_KV_HEADS = 64
+KVQ_BLOCK_TOKENS = 16
+
+KVQ_OK, KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_BUDGET, KVQ_ERR_WORKSPACE, KVQ_ERR_DEVICE, KVQ_ERR_CAPACITY = range(7)
+KVQ_F32, KVQ_BF16 = 0, 1
+
+EXPORTED = [
+    "kvq_abi_version", "kvq_status_str", "kvq_last_error", "kvq_layout_init", "kvq_plan_bits",
+    "kvq_logquant_classes", "kvq_page_alloc", "kvq_quantize_append", "kvq_dequant",
+    "kvq_decode_workspace_bytes", "kvq_decode_attn", "kvq_decode_partial", "kvq_decode_merge",
+]
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+class KvqLayout(ctypes.Structure):
+    _fields_ = [
+        ("num_kv_heads", ctypes.c_int32),
+        ("group", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("had_block", ctypes.c_int32),
+        ("block_tokens", ctypes.c_int32),
+        ("bits_k", ctypes.c_int32 * KVQ_MAX_KV_HEADS),
+        ("bits_v", ctypes.c_int32 * KVQ_MAX_KV_HEADS),
+        ("k_off", ctypes.c_int64 * KVQ_MAX_KV_HEADS),
+        ("v_off", ctypes.c_int64 * KVQ_MAX_KV_HEADS),
+        ("block_bytes", ctypes.c_int64),
+    ]
+
+
+class KvqSegment(ctypes.Structure):
+    _fields_ = [
+        ("layout", ctypes.POINTER(KvqLayout)),
+        ("pool", ctypes.c_void_p),
+        ("pool_blocks", ctypes.c_int64),
+        ("block_table", ctypes.c_void_p),
+        ("table_stride", ctypes.c_int32),
+        ("seq_lens", ctypes.c_void_p),
+        ("max_len", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """Load libkvq.so (built in-tree by `python -m quantized_decode_attention_03_amd.build`)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libkvq.so not found at {LIB_PATH}; build it with "
+                          "`python -m quantized_decode_attention_03_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    i32, i64, vp, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+    L.kvq_abi_version.restype = ctypes.c_int
+    L.kvq_status_str.restype = ctypes.c_char_p
+    L.kvq_status_str.argtypes = [ctypes.c_int]
+    L.kvq_last_error.restype = ctypes.c_char_p
+    L.kvq_layout_init.argtypes = [ctypes.POINTER(KvqLayout)]
+    L.kvq_plan_bits.argtypes = [i32, vp, ctypes.c_double, ctypes.c_double, vp, i32, i64, vp, vp]
+    L.kvq_logquant_classes.argtypes = [i32, i32, vp]
+    L.kvq_page_alloc.argtypes = [vp, i32, vp, i32, vp, vp, vp, i32]
+    L.kvq_quantize_append.argtypes = [ctypes.POINTER(KvqLayout), vp, i64, vp, i32, i32, vp, i32, vp, vp,
+                                      ctypes.c_int, vp]
+    L.kvq_dequant.argtypes = [ctypes.POINTER(KvqLayout), vp, i64, vp, i32, i32, i32, i32, i32, vp, vp, vp]
+    L.kvq_decode_workspace_bytes.argtypes = [ctypes.POINTER(KvqSegment), i32, i32, ctypes.POINTER(sz)]
+    L.kvq_decode_attn.argtypes = [ctypes.POINTER(KvqSegment), i32, i32, vp, ctypes.c_int, vp, vp, sz, vp]
+    L.kvq_decode_partial.argtypes = [ctypes.POINTER(KvqSegment), i32, i32, vp, ctypes.c_int, vp, sz, vp]
+    L.kvq_decode_merge.argtypes = [ctypes.POINTER(KvqSegment), i32, i32, vp, vp, sz, vp]
+    for name in EXPORTED:
+        if name not in ("kvq_abi_version", "kvq_status_str", "kvq_last_error"):
+            getattr(L, name).restype = ctypes.c_int
+    if L.kvq_abi_version() != KVQ_ABI_VERSION:
+        raise ImportError("libkvq ABI version mismatch; rebuild the library")
+    _lib = L
+    return L
+
+
+def _check(status, what):
+    if status != KVQ_OK:
+        msg = lib().kvq_last_error().decode()
+        raise KvqError(status, f"{what}: {msg or lib().kvq_status_str(status).decode()}")
+
+
+def _np_ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev_ptr(t, dtypes, what):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{what} must be a GPU tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{what} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+# ---------------------------------------------------------------------------
+# Host entry points
+# ---------------------------------------------------------------------------
+
+def kvq_abi_version():
+    return lib().kvq_abi_version()
+
+
+def kvq_status_str(status):
+    return lib().kvq_status_str(status).decode()
+
+
+def kvq_last_error():
+    return lib().kvq_last_error().decode()
+
+
+def kvq_layout_init(num_kv_heads, group, head_dim, had_block, bits_k, bits_v):
+    """Return an initialised KvqLayout (bits_k / bits_v: one width per KV head)."""
+    L = KvqLayout()
+    L.num_kv_heads, L.group, L.head_dim, L.had_block = num_kv_heads, group, head_dim, had_block
+    L.block_tokens = KVQ_BLOCK_TOKENS
+    bits_k, bits_v = list(bits_k), list(bits_v)
+    if len(bits_k) != num_kv_heads or len(bits_v) != num_kv_heads:
+        raise ValueError("bits_k and bits_v need one entry per KV head")
+    for h in range(num_kv_heads):
+        L.bits_k[h], L.bits_v[h] = int(bits_k[h]), int(bits_v[h])
+    _check(lib().kvq_layout_init(ctypes.byref(L)), "kvq_layout_init")
+    return L
+
+
+def kvq_plan_bits(w, alpha, beta, ladder, budget_bits, allow_leftover=False):
+    """Greedy per-head bit allocation. Returns (bits int32 array, leftover)."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    ladder = np.ascontiguousarray(ladder, dtype=np.int32)
+    out = np.zeros(w.shape[0], dtype=np.int32)
+    left = ctypes.c_int64(0)
+    st = lib().kvq_plan_bits(int(w.shape[0]), _np_ptr(w), float(alpha), float(beta), _np_ptr(ladder),
+                             int(ladder.shape[0]), int(budget_bits), _np_ptr(out), ctypes.byref(left))
+    if not (allow_leftover and st == KVQ_ERR_BUDGET and left.value != 0):
+        _check(st, "kvq_plan_bits")
+    return out, left.value
+
+
+def kvq_logquant_classes(total, window):
+    out = np.zeros(total, dtype=np.int8)
+    _check(lib().kvq_logquant_classes(int(total), int(window), _np_ptr(out)), "kvq_logquant_classes")
+    return out
+
+
+def kvq_page_alloc(free_list, cursor, old_len, new_len, block_table):
+    """Fill block_table (host int32 [batch, stride], in place); returns the new cursor."""
+    free_list = np.ascontiguousarray(free_list, dtype=np.int32)
+    old_len = np.ascontiguousarray(old_len, dtype=np.int32)
+    new_len = np.ascontiguousarray(new_len, dtype=np.int32)
+    if block_table.dtype != np.int32 or not block_table.flags["C_CONTIGUOUS"] or block_table.ndim != 2:
+        raise ValueError("block_table must be a C-contiguous int32 [batch, stride] array")
+    cur = ctypes.c_int32(int(cursor))
+    _check(lib().kvq_page_alloc(_np_ptr(free_list), int(free_list.shape[0]), ctypes.byref(cur),
+                                int(old_len.shape[0]), _np_ptr(old_len), _np_ptr(new_len),
+                                _np_ptr(block_table), int(block_table.shape[1])), "kvq_page_alloc")
+    return cur.value
+
+
+def kvq_decode_workspace_bytes(segments, batch):
+    segs = _segments(segments)
+    n = ctypes.c_size_t(0)
+    _check(lib().kvq_decode_workspace_bytes(segs, len(segments), int(batch), ctypes.byref(n)),
+           "kvq_decode_workspace_bytes")
+    return n.value
+
+
+# ---------------------------------------------------------------------------
+# Device entry points
+# ---------------------------------------------------------------------------
+
+def kvq_quantize_append(layout, pool, block_table, start_pos, k, v, stream=None):
+    """Quantize k, v ([batch, n_new, Hkv, d], fp32 or bf16) into the pool at start_pos."""
+    import torch
+    dt = KVQ_BF16 if k.dtype == torch.bfloat16 else KVQ_F32
+    if v.dtype != k.dtype or tuple(v.shape) != tuple(k.shape) or k.dim() != 4:
+        raise ValueError("k and v must share shape [batch, n_new, Hkv, d] and dtype")
+    if k.shape[2] != layout.num_kv_heads or k.shape[3] != layout.head_dim:
+        raise ValueError("k does not match the layout's heads / head_dim")
+    if block_table.dim() != 2 or start_pos.shape[0] != k.shape[0] or block_table.shape[0] < k.shape[0]:
+        raise ValueError("block_table must be [batch, stride] and start_pos [batch]")
+    if pool.dim() != 2 or pool.shape[1] != layout.block_bytes:
+        raise ValueError("pool must be uint8 [n_blocks, block_bytes]")
+    st = lib().kvq_quantize_append(
+        ctypes.byref(layout), _dev_ptr(pool, (torch.uint8,), "pool"), int(pool.shape[0]),
+        _dev_ptr(block_table, (torch.int32,), "block_table"), int(block_table.shape[1]), int(k.shape[0]),
+        _dev_ptr(start_pos, (torch.int32,), "start_pos"), int(k.shape[1]),
+        _dev_ptr(k, (torch.float32, torch.bfloat16), "k"), _dev_ptr(v, (torch.float32, torch.bfloat16), "v"),
+        dt, _stream(stream))
+    _check(st, "kvq_quantize_append")
+
+
+def kvq_dequant(layout, pool, block_table, seq, pos0, n, rotated=True, k_out=None, v_out=None, stream=None):
+    """Read tokens [pos0, pos0+n) of sequence `seq` back to fp32 [n, Hkv, d] (K and V)."""
+    import torch
+    shape = (n, layout.num_kv_heads, layout.head_dim)
+    if k_out is None:
+        k_out = torch.empty(shape, dtype=torch.float32, device=pool.device)
+    if v_out is None:
+        v_out = torch.empty(shape, dtype=torch.float32, device=pool.device)
+    if tuple(k_out.shape) != shape or tuple(v_out.shape) != shape:
+        raise ValueError("outputs must be [n, Hkv, d]")
+    st = lib().kvq_dequant(
+        ctypes.byref(layout), _dev_ptr(pool, (torch.uint8,), "pool"), int(pool.shape[0]),
+        _dev_ptr(block_table, (torch.int32,), "block_table"), int(block_table.shape[1]), int(seq), int(pos0),
+        int(n), int(bool(rotated)), _dev_ptr(k_out, (torch.float32,), "k_out"),
+        _dev_ptr(v_out, (torch.float32,), "v_out"), _stream(stream))
+    _check(st, "kvq_dequant")
+    return k_out, v_out
+
+
+class Segment:
+    """One precision segment: layout + pool + block table + per-sequence lengths."""
+
+    def __init__(self, layout, pool, block_table, seq_lens, max_len):
+        self.layout, self.pool, self.block_table, self.seq_lens = layout, pool, block_table, seq_lens
+        self.max_len = int(max_len)
+
+
+def _segments(segments):
+    import torch
+    arr = (KvqSegment * len(segments))()
+    for i, s in enumerate(segments):
+        arr[i].layout = ctypes.pointer(s.layout)
+        arr[i].pool = _dev_ptr(s.pool, (torch.uint8,), "pool")
+        arr[i].pool_blocks = int(s.pool.shape[0])
+        arr[i].block_table = _dev_ptr(s.block_table, (torch.int32,), "block_table")
+        arr[i].table_stride = int(s.block_table.shape[1])
+        arr[i].seq_lens = _dev_ptr(s.seq_lens, (torch.int32,), "seq_lens")
+        arr[i].max_len = s.max_len
+    return arr
+
+
+def _decode_common(segments, q, ws):
+    import torch
+    batch = int(q.shape[0])
+    need = kvq_decode_workspace_bytes(segments, batch)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError("workspace too small")
+    return batch, ws
+
+
+def kvq_decode_attn(segments, q, out=None, ws=None, stream=None):
+    """Decode attention for q [batch, Hq, d] (fp32 or bf16); returns fp32 [batch, Hq, d]."""
+    import torch
+    batch, ws = _decode_common(segments, q, ws)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    dt = KVQ_BF16 if q.dtype == torch.bfloat16 else KVQ_F32
+    segs = _segments(segments)
+    st = lib().kvq_decode_attn(segs, len(segments), batch, _dev_ptr(q, (torch.float32, torch.bfloat16), "q"), dt,
+                               _dev_ptr(out, (torch.float32,), "out"), _dev_ptr(ws, (torch.uint8,), "ws"),
+                               ws.numel(), _stream(stream))
+    _check(st, "kvq_decode_attn")
+    return out
+
+
+def kvq_decode_partial(segments, q, ws, stream=None):
+    import torch
+    batch = int(q.shape[0])
+    dt = KVQ_BF16 if q.dtype == torch.bfloat16 else KVQ_F32
+    st = lib().kvq_decode_partial(_segments(segments), len(segments), batch,
+                                  _dev_ptr(q, (torch.float32, torch.bfloat16), "q"), dt,
+                                  _dev_ptr(ws, (torch.uint8,), "ws"), ws.numel(), _stream(stream))
+    _check(st, "kvq_decode_partial")
+
+
+def kvq_decode_merge(segments, batch, out, ws, stream=None):
+    import torch
+    st = lib().kvq_decode_merge(_segments(segments), len(segments), int(batch),
+                                _dev_ptr(out, (torch.float32,), "out"), _dev_ptr(ws, (torch.uint8,), "ws"),
+                                ws.numel(), _stream(stream))
+    _check(st, "kvq_decode_merge")

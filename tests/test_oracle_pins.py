@@ -64,6 +64,24 @@ def test_rotate_preserves_norm_and_inverts():
         assert np.abs(back - x).max() < 1e-5
 
 
+def test_rotate_equals_the_orthonormal_matrix_product():
+    # The +-1 product plus one scaling is the same map as multiplying by the
+    # orthonormal matrix, up to fp64 rounding before the final fp32 rounding.
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((200, 128))
+    for n in (2, 32, 128):
+        h = O.hadamard_matrix(n)
+        ref = (x.reshape(200, 128 // n, n) @ h.T).reshape(200, 128)
+        y = O.rotate(x, n).astype(np.float64)
+        assert np.all(np.abs(y - ref) <= np.spacing(np.abs(ref).astype(np.float32)) * 0.5 + 1e-14)
+
+
+def test_rotate_gives_exact_zero_for_cancelling_inputs():
+    # (1, 1) rotated with n = 2 is (sqrt(2), 0): the second entry is exactly 0.
+    y = O.rotate(np.array([1.0, 1.0], dtype=np.float32), 2)
+    assert y[1] == 0.0 and y[0] == np.float32(math.sqrt(2))
+
+
 def test_rotate_is_block_diagonal():
     # A vector living in one block stays in that block.
     x = np.zeros(128, dtype=np.float32)
