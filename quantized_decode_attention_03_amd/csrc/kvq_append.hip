@@ -19,6 +19,11 @@
 
 #include <cmath>
 
+// Every multiply and add here rounds on its own (no fused multiply-add): the
+// stored codes and the dequantized values are defined by separately rounded
+// fp32 operations, e.g. x_hat = c * s + mn is a rounded product then a rounded sum.
+#pragma clang fp contract(off)
+
 namespace kvq {
 
 namespace {
@@ -101,7 +106,7 @@ template <int BITS>
 __device__ __forceinline__ void quantize_store8(const float (&x)[8], float mn, float inv, uint8_t* dst) {
   float u[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) u[j] = __fmul_rn(__fsub_rn(x[j], mn), inv);
+  for (int j = 0; j < 8; ++j) u[j] = (x[j] - mn) * inv;
   // v_cvt_pk_u8_f32 rounds half to even and saturates to [0, 255]; u lies in
   // [0, 2^b - 1 + 2^-22 (2^b - 1)], so the code is already in range.
   if constexpr (BITS == 8) {
@@ -198,11 +203,11 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a, double r
       mx = fmaxf(mx, shfl_xor(mx, m));
     }
     const float qmax = static_cast<float>((1 << BITS) - 1);
-    const float rng = __fsub_rn(mx, mn);
+    const float rng = mx - mn;
     float s = 0.f, inv = 0.f;
     if (rng > 0.f) {
-      s = __fdiv_rn(rng, qmax);
-      inv = __fdiv_rn(qmax, rng);
+      s = rng / qmax;  // IEEE division (correctly rounded)
+      inv = qmax / rng;
     }
     if (store) {
       quantize_store8<BITS>(x, mn, inv, base + slot * RB + lane * BITS);
@@ -240,7 +245,7 @@ __device__ __forceinline__ void load_row8(const uint8_t* rowp, const uint8_t* me
       uint32_t code;
       if constexpr (BITS == 8) code = ((j < 4 ? lo : hi) >> (8 * (j & 3))) & 0xffu;
       else code = (lo >> (BITS * j)) & ((1u << BITS) - 1u);
-      x[j] = __fadd_rn(__fmul_rn(static_cast<float>(code), meta.x), meta.y);
+      x[j] = static_cast<float>(code) * meta.x + meta.y;  // two roundings (contraction is off)
     }
   }
 }
@@ -270,7 +275,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(DequantArgs a, float 
   if (!a.rotated) {
     fwht8(x, lane, a.had_block);  // H is symmetric: R^T applies the same butterflies
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = __fmul_rn(x[j], rs_n);
+    for (int j = 0; j < 8; ++j) x[j] = x[j] * rs_n;
   }
   if (active) {
     float4* o = reinterpret_cast<float4*>(a.out + (static_cast<size_t>(t) * a.hkv + h) * D + lane * 8);

@@ -163,3 +163,10 @@ def max_rel_err(out, ref):
 
 
 ATTN_TOL = 2e-3
+
+
+def rel(a, b):
+    """max |a - b| / max |b| over whole arrays."""
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.abs(a - b).max() / max(1e-30, np.abs(b).max()))
