@@ -38,7 +38,8 @@ namespace kvq {
 
 namespace {
 
-constexpr uint32_t kBias = 0x64006400u;  // fp16 pair (1024, 1024)
+// fp16 pair (1024, 1024), held in a VGPR so (x & mask) | bias is one v_and_or_b32
+__device__ __forceinline__ uint32_t kbias() { return vconst(0x64006400u); }
 
 __device__ __forceinline__ float4_t mfma_f16(u32x4_t a, u32x4_t b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
@@ -80,10 +81,10 @@ template <int D> struct KFmt<4, D> {
   __device__ static u32x4_t unpack(const uint32_t (&w)[kWords], int c) {
     const uint32_t x = w[c];
     u32x4_t r;
-    r[0] = and_or(x << 4, 0x00f000f0u, kBias);
-    r[1] = and_or(x, 0x00f000f0u, kBias);
-    r[2] = and_or(x >> 4, 0x00f000f0u, kBias);
-    r[3] = and_or(x >> 8, 0x00f000f0u, kBias);
+    r[0] = and_or(x << 4, 0x00f000f0u, kbias());
+    r[1] = and_or(x, 0x00f000f0u, kbias());
+    r[2] = and_or(x >> 4, 0x00f000f0u, kbias());
+    r[3] = and_or(x >> 8, 0x00f000f0u, kbias());
     return r;
   }
 };
@@ -97,7 +98,7 @@ template <int D> struct KFmt<2, D> {
     return 16 * m + ((e & 1) ? 8 : 0) + k;
   }
   template <int K>
-  __device__ static uint32_t pair(uint32_t x) { return and_or(shl_signed<8 - 2 * K>(x), 0x03000300u, kBias); }
+  __device__ static uint32_t pair(uint32_t x) { return and_or(shl_signed<8 - 2 * K>(x), 0x03000300u, kbias()); }
   __device__ static u32x4_t unpack(const uint32_t (&w)[kWords], int c) {
     const uint32_t x = w[c >> 1];
     u32x4_t r;
@@ -118,10 +119,10 @@ template <int D> struct KFmt<8, D> {
   __device__ static u32x4_t unpack(const uint32_t (&w)[kWords], int c) {
     const uint32_t x0 = w[2 * c], x1 = w[2 * c + 1];
     u32x4_t r;
-    r[0] = and_or(x0, 0x00ff00ffu, kBias);
-    r[1] = and_or(x0 >> 8, 0x00ff00ffu, kBias);
-    r[2] = and_or(x1, 0x00ff00ffu, kBias);
-    r[3] = and_or(x1 >> 8, 0x00ff00ffu, kBias);
+    r[0] = and_or(x0, 0x00ff00ffu, kbias());
+    r[1] = and_or(x0 >> 8, 0x00ff00ffu, kbias());
+    r[2] = and_or(x1, 0x00ff00ffu, kbias());
+    r[3] = and_or(x1 >> 8, 0x00ff00ffu, kbias());
     return r;
   }
 };
@@ -140,10 +141,10 @@ template <int D> struct KFmt<3, D> {
   template <int C>
   __device__ static u32x4_t unpack_c(const uint32_t (&w)[kWords]) {
     u32x4_t r;
-    r[0] = (((code<8 * C + 1>(w) << 16) | code<8 * C + 0>(w)) << 7) | kBias;
-    r[1] = (((code<8 * C + 3>(w) << 16) | code<8 * C + 2>(w)) << 7) | kBias;
-    r[2] = (((code<8 * C + 5>(w) << 16) | code<8 * C + 4>(w)) << 7) | kBias;
-    r[3] = (((code<8 * C + 7>(w) << 16) | code<8 * C + 6>(w)) << 7) | kBias;
+    r[0] = (((code<8 * C + 1>(w) << 16) | code<8 * C + 0>(w)) << 7) | kbias();
+    r[1] = (((code<8 * C + 3>(w) << 16) | code<8 * C + 2>(w)) << 7) | kbias();
+    r[2] = (((code<8 * C + 5>(w) << 16) | code<8 * C + 4>(w)) << 7) | kbias();
+    r[3] = (((code<8 * C + 7>(w) << 16) | code<8 * C + 6>(w)) << 7) | kbias();
     return r;
   }
   __device__ static u32x4_t unpack(const uint32_t (&w)[kWords], int c) {
@@ -273,7 +274,7 @@ __device__ __forceinline__ u32x4_t v_operand(const uint32_t (&raw)[8][VRaw<VB, D
       if (cc >= 2) x >>= 8;
       const uint32_t mask = (cc & 1) ? 0x00f000f0u : 0x000f000fu;
       const float sg = (cc & 1) ? 16.f : 1.f;
-      out = and_or(x, mask, kBias);
+      out = and_or(x, mask, kbias());
       const _Float16 off = static_cast<_Float16>(-(1024.f + 8.f * sg));
       out = pk_add_h(out, half_bits(off) * 0x10001u);
     } else if constexpr (VB == 2) {
@@ -288,7 +289,7 @@ __device__ __forceinline__ u32x4_t v_operand(const uint32_t (&raw)[8][VRaw<VB, D
         x = perm_b32(b[0], a[0], 0x0c000c00u | ((4 + k) << 16) | k);
         cc = c;
       }
-      out = and_or(x, 0x00030003u << (2 * cc), kBias);
+      out = and_or(x, 0x00030003u << (2 * cc), kbias());
       const float sg = static_cast<float>(1 << (2 * cc));
       const _Float16 off = static_cast<_Float16>(-(1024.f + 2.f * sg));
       out = pk_add_h(out, half_bits(off) * 0x10001u);
@@ -296,7 +297,7 @@ __device__ __forceinline__ u32x4_t v_operand(const uint32_t (&raw)[8][VRaw<VB, D
       const int word = D == 128 ? (c >> 2) : 0;
       const uint32_t k = c & 3;
       const uint32_t x = perm_b32(b[word], a[word], 0x0c000c00u | ((4 + k) << 16) | k);
-      out = x | kBias;
+      out = x | kbias();
       const _Float16 off = static_cast<_Float16>(-(1024.f + 128.f));
       out = pk_add_h(out, half_bits(off) * 0x10001u);
     } else if constexpr (VB == 3) {
@@ -305,7 +306,7 @@ __device__ __forceinline__ u32x4_t v_operand(const uint32_t (&raw)[8][VRaw<VB, D
       const uint32_t wa = __builtin_amdgcn_alignbit(a[1], a[0], sh);
       const uint32_t wb = __builtin_amdgcn_alignbit(b[1], b[0], sh);
       const uint32_t ca = (wa >> (3 * c)) & 7u, cb = (wb >> (3 * c)) & 7u;
-      out = (((cb << 16) | ca) << 7) | kBias;
+      out = (((cb << 16) | ca) << 7) | kbias();
       const _Float16 off = static_cast<_Float16>(-(1024.f + 4.f * 128.f));
       out = pk_add_h(out, half_bits(off) * 0x10001u);
     } else {  // bf16 values: channel n*D/16 + c is half (c & 1) of word c/2
@@ -323,18 +324,191 @@ __device__ __forceinline__ int v_channel(int n, int c) { return n * (D / 16) + c
 // ---------------------------------------------------------------------------
 // The partial kernel.
 // ---------------------------------------------------------------------------
+
+// Raw data of one group (four pages) for one lane, loaded before it is used so
+// the next group's loads are in flight while the current group is computed.
+template <int KB, int VB, int D>
+struct GroupRaw {
+  uint32_t k[4][KFmt<KB, D>::kWords];         // key quarter rows, one per page
+  uint32_t v[2][8][VRaw<VB, D>::kWords];       // value words, 8 tokens per page pair
+  float ks, kmn, vs, vmn;                      // metadata of this lane's token
+  bool valid;                                  // this lane's token is a cached token
+  uint32_t vmask;                              // bit 8*pp2+e: value token e of pair pp2 is cached
+};
+
+// Running max of the scores may grow by up to this much (log2 units) before the
+// accumulators are rescaled, so weights stay below 2^4 between rescales.
+constexpr float kRescaleSlack = 4.f;
+
+// Every load is issued unconditionally (pages past the split or unmapped read
+// block 0 and are masked afterwards), so the number of loads in flight is
+// static and the wait before a group's compute leaves the next group's loads
+// outstanding.
+template <int KB, int VB, int D>
+__device__ __forceinline__ void load_group(const DecodeArgs& a, const uint8_t* pool, const int32_t* trow, int grp,
+                                           int p1, int seq_len, int64_t koff, int64_t voff, int lane,
+                                           GroupRaw<KB, VB, D>& g) {
+  constexpr int RBK = D * KB / 8, RBV = D * VB / 8, QBYTES = RBK / 4;
+  const int tslot = lane & 15, g4 = lane >> 4;
+  int64_t boff[4];
+  bool pv[4];
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp) {
+    const int page = grp + pp;
+    const int64_t blk = trow[min(page, p1 - 1)];
+    pv[pp] = page < p1 && blk >= 0 && blk < a.pool_blocks;
+    boff[pp] = pv[pp] ? blk * a.block_bytes : 0;
+  }
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp)
+    load_kquarter<KB, D>(pool + boff[pp] + koff + tslot * RBK + g4 * QBYTES, g.k[pp]);
+  // token layout: lane = (page g4, slot tslot)
+  const int64_t my_boff = g4 == 0 ? boff[0] : g4 == 1 ? boff[1] : g4 == 2 ? boff[2] : boff[3];
+  const bool my_pv = g4 == 0 ? pv[0] : g4 == 1 ? pv[1] : g4 == 2 ? pv[2] : pv[3];
+  g.valid = my_pv && (grp + g4) * kBlockTokens + tslot < seq_len;
+  g.ks = 1.f; g.kmn = 0.f; g.vs = 1.f; g.vmn = 0.f;
+  if constexpr (KB != 16) {
+    const float2 mk = *reinterpret_cast<const float2*>(pool + my_boff + koff + kBlockTokens * RBK + tslot * kMetaBytes);
+    g.ks = mk.x; g.kmn = mk.y;
+  }
+  if constexpr (VB != 16) {
+    const float2 mv = *reinterpret_cast<const float2*>(pool + my_boff + voff + kBlockTokens * RBV + tslot * kMetaBytes);
+    g.vs = mv.x; g.vmn = mv.y;
+  }
+  // value layout: lane = (column n = tslot, token group g4) over page pairs
+  g.vmask = 0;
+#pragma unroll
+  for (int pp2 = 0; pp2 < 2; ++pp2) {
+    const int pg = 2 * pp2 + (g4 >> 1);
+    const int64_t vb = pg == 0 ? boff[0] : pg == 1 ? boff[1] : pg == 2 ? boff[2] : boff[3];
+    const bool vok = pg == 0 ? pv[0] : pg == 1 ? pv[1] : pg == 2 ? pv[2] : pv[3];
+    const uint8_t* base = pool + vb + voff + (8 * (g4 & 1)) * RBV + v_lane_offset<VB, D>(tslot);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      load_vtoken<VB, D>(base + e * RBV, g.v[pp2][e]);
+      const bool ok = vok && ((grp + pg) * kBlockTokens + 8 * (g4 & 1) + e) < seq_len;
+      g.vmask |= static_cast<uint32_t>(ok) << (8 * pp2 + e);
+    }
+  }
+}
+
+template <int KB, int VB, int D>
+struct SplitState {
+  float4_t acc[D / 16];  // PV accumulators (rows: hi heads 0..3 | lo heads 0..3 | zero)
+  float m_run[4];        // reference max per query head (log2 units)
+  float l_part[4];       // per-lane partial sum of p
+  float mn_part[4];      // per-lane partial sum of p * (mn + 2^(b-1) s)
+};
+
+template <int KB, int VB, int D>
+__device__ __forceinline__ void compute_group(GroupRaw<KB, VB, D>& g, const u32x4_t (&ahi)[D / 32],
+                                              const u32x4_t (&alo)[D / 32], const float (&biasq)[4],
+                                              const float (&q2)[4], float inv_qsc, int G, int lane,
+                                              uint16_t (*wt)[4][64], const uint16_t* wzero,
+                                              SplitState<KB, VB, D>& st) {
+  using KF = KFmt<KB, D>;
+  using VF = VFmt<VB, D>;
+  constexpr int NCK = D / 32, NCV = D / 16;
+  constexpr bool KMETA = KB != 16, VMETA = VB != 16;
+  constexpr float NEG_INF = -__builtin_huge_valf();
+  const int row = lane & 15, g4 = lane >> 4;
+
+  // QK: one 16x16 tile per page (rows = query heads, columns = tokens)
+  float4_t cq[4];
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp) {
+    cq[pp] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NCK; ++c) {
+      const u32x4_t bk = KF::unpack(g.k[pp], c);
+      cq[pp] = mfma<KF::bf16>(ahi[c], bk, cq[pp]);
+      cq[pp] = mfma<KF::bf16>(alo[c], bk, cq[pp]);
+    }
+  }
+  // pack the four tiles: lane = token of the group, register i = head i
+  float sc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const auto r01 = __builtin_amdgcn_permlane16_swap(f_bits(cq[0][i]), f_bits(cq[1][i]), false, false);
+    const auto r23 = __builtin_amdgcn_permlane16_swap(f_bits(cq[2][i]), f_bits(cq[3][i]), false, false);
+    const auto r = __builtin_amdgcn_permlane32_swap(r01[0], r23[0], false, false);
+    sc[i] = bits_f(r[0]);
+  }
+
+  // online softmax (log2 units) with a lazily raised reference max
+  const float ks_q = g.ks * inv_qsc;
+  const float vmid = VMETA ? g.vmn + static_cast<float>(1 << (VB - 1)) * g.vs : 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (i >= G) break;
+    float z;
+    if constexpr (KMETA) z = fmaf(ks_q, sc[i], fmaf(-ks_q, biasq[i], g.kmn * q2[i]));
+    else z = sc[i];
+    z = g.valid ? z : NEG_INF;
+    const float gm = wave_max_scalar(z);
+    if (gm > st.m_run[i] + kRescaleSlack) {
+      const float alpha = __builtin_amdgcn_exp2f(st.m_run[i] - gm);
+#pragma unroll
+      for (int c = 0; c < NCV; ++c) st.acc[c][i] *= alpha;
+      st.l_part[i] *= alpha;
+      st.mn_part[i] *= alpha;
+      st.m_run[i] = gm;
+    }
+    const float p = g.valid ? __builtin_amdgcn_exp2f(z - st.m_run[i]) : 0.f;
+    st.l_part[i] += p;
+    float w = p;
+    if constexpr (VMETA) {
+      w = g.valid ? p * g.vs : 0.f;
+      st.mn_part[i] = fmaf(p, g.valid ? vmid : 0.f, st.mn_part[i]);
+    }
+    uint32_t hb, lb;
+    if constexpr (VF::bf16) {
+      hb = f_to_bf16_rne(w);
+      lb = f_to_bf16_rne(w - bf16lo_to_f(hb));
+    } else {
+      const _Float16 hh = static_cast<_Float16>(w);
+      hb = half_bits(hh);
+      lb = half_bits(static_cast<_Float16>(w - static_cast<float>(hh)));
+    }
+    wt[0][i][lane] = static_cast<uint16_t>(hb);
+    wt[1][i][lane] = static_cast<uint16_t>(lb);
+  }
+  __syncthreads();
+
+  // PV: two 32-token steps
+#pragma unroll
+  for (int pp2 = 0; pp2 < 2; ++pp2) {
+    const uint16_t* asrc;
+    if (row < 4 && row < G) asrc = &wt[0][row][32 * pp2 + 8 * g4];
+    else if (row >= 4 && row < 4 + G) asrc = &wt[1][row - 4][32 * pp2 + 8 * g4];
+    else asrc = wzero;
+    const uint4 av = *reinterpret_cast<const uint4*>(asrc);
+    const u32x4_t aw = u32x4_t{av.x, av.y, av.z, av.w};
+    if constexpr (VB == 16) {
+      if ((g.vmask >> (8 * pp2) & 0xffu) != 0xffu) {  // a masked token in this pair: clear its words
+        auto& vv = g.v[pp2];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+#pragma unroll
+          for (int j = 0; j < VRaw<VB, D>::kWords; ++j)
+            vv[e][j] = (g.vmask >> (8 * pp2 + e) & 1u) ? vv[e][j] : 0u;
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < NCV; ++c) {
+      const u32x4_t bv = v_operand<VB, D>(g.v[pp2], row, c);
+      st.acc[c] = mfma<VF::bf16>(aw, bv, st.acc[c]);
+    }
+  }
+  __syncthreads();
+}
+
 template <int KB, int VB, int D>
 __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeArgs a, float qscale) {
   using KF = KFmt<KB, D>;
   using VF = VFmt<VB, D>;
   constexpr int NCK = D / 32;               // QK chunks (32 channels each)
   constexpr int NCV = D / 16;               // PV chunks (16 output channels each)
-  constexpr int RBK = D * KB / 8;           // bytes per stored key row
-  constexpr int RBV = D * VB / 8;
-  constexpr int QBYTES = RBK / 4;           // a lane's quarter of a key row
-  constexpr int KW = KF::kWords;
-  constexpr int VW = VRaw<VB, D>::kWords;
-  constexpr bool KMETA = KB != 16, VMETA = VB != 16;
   constexpr float NEG_INF = -__builtin_huge_valf();
 
   __shared__ float qs[4][D];
@@ -355,7 +529,7 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeArgs a, float 
   const int p1 = min(p0 + a.pages_per_split, pages);
   const int slot = a.slot_base + split;
 
-  auto write_empty = [&]() {
+  if (p0 >= p1) {
     for (int r = 0; r < G; ++r) {
       const int64_t bg = static_cast<int64_t>(b) * hq + h * G + r;
       float* po = a.part_o + (bg * a.total_slots + slot) * D;
@@ -365,8 +539,14 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeArgs a, float 
         a.part_ml[(bg * a.total_slots + slot) * 2 + 1] = 0.f;
       }
     }
-  };
-  if (p0 >= p1) { write_empty(); return; }
+    return;
+  }
+
+  const uint8_t* pool = a.pool;
+  const int32_t* trow = a.table + static_cast<int64_t>(b) * a.table_stride;
+  // first group's loads go out before the query is prepared
+  GroupRaw<KB, VB, D> ga, gb;
+  load_group<KB, VB, D>(a, pool, trow, p0, p1, seq_len, koff, voff, lane, ga);
 
   // ---- q' = R q for the G query heads of this KV head (LDS butterflies) ----
   for (int e = lane; e < 4 * D; e += 64) {
@@ -403,7 +583,7 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeArgs a, float 
       const float v = row < G ? qs[row][g4 * (D / 4) + KF::channel(c, e)] * qscale / KF::sigma : 0.f;
       amax = fmaxf(amax, fabsf(v));
     }
-  amax = wave_max(amax);
+  amax = wave_max_scalar(amax);
   // Power-of-two scale keeping the fp16 halves away from subnormals.
   float qsc = 1.f;
   if (!KF::bf16 && amax > 0.f) {
@@ -412,7 +592,7 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeArgs a, float 
     qsc = ldexpf(1.f, 10 - ex);
   }
   u32x4_t ahi[NCK], alo[NCK];
-  double q1 = 0.0;  // sum of the A values actually used (bias correction)
+  double q1 = 0.0;  // this lane's share of the sum of the A values used (bias correction)
 #pragma unroll
   for (int c = 0; c < NCK; ++c) {
 #pragma unroll
@@ -442,193 +622,51 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeArgs a, float 
       alo[c][v] = lp;
     }
   }
-  // Reduce q1 over the four quarters (lanes row, row+16, row+32, row+48).
-  {
-    float q1f_hi = static_cast<float>(q1);
-    float q1f_lo = static_cast<float>(q1 - static_cast<double>(q1f_hi));
-    double t = q1;
-    t += static_cast<double>(shfl_xor(q1f_hi, 16)) + static_cast<double>(shfl_xor(q1f_lo, 16));
-    q1f_hi = static_cast<float>(t);
-    q1f_lo = static_cast<float>(t - static_cast<double>(q1f_hi));
-    t += static_cast<double>(shfl_xor(q1f_hi, 32)) + static_cast<double>(shfl_xor(q1f_lo, 32));
-    q1 = t;
-  }
+  // Sum over the four quarters (lanes row, row+16, row+32, row+48), in fp64.
+  q1 += __shfl_xor(q1, 16, 64);
+  q1 += __shfl_xor(q1, 32, 64);
+  const float q1t = static_cast<float>(q1);
   // Per query head constants, broadcast from lane i (row i):
-  //   bias_i = 1024 * Q1_i (scaled units), q2_i = sum_j q~_ij (log2 units).
+  //   biasq_i = 1024 * Q1_i (scaled units), q2_i = sum_j q~_ij (log2 units).
   float biasq[4], q2[4];
   const float inv_qsc = 1.f / qsc;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float q1i = __shfl(static_cast<float>(q1), i, 64);
+    const float q1i = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, q1t), i));
     biasq[i] = KF::bf16 ? 0.f : 1024.f * q1i;
     q2[i] = q1i * KF::sigma * inv_qsc;
   }
 
-  // ---- main loop over groups of four pages ----
-  float4_t acc[NCV];
+  // ---- main loop: two groups per trip, loads of the next group in flight ----
+  SplitState<KB, VB, D> st;
 #pragma unroll
-  for (int c = 0; c < NCV; ++c) acc[c] = float4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
-  float l_part[4] = {0.f, 0.f, 0.f, 0.f};
-  float mn_part[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < NCV; ++c) st.acc[c] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { st.m_run[i] = NEG_INF; st.l_part[i] = 0.f; st.mn_part[i] = 0.f; }
 
-  const int pl = lane >> 4;      // page of this lane in the packed (token) layout
-  const int tslot = lane & 15;   // token slot of this lane in that page
-  const int vcol = lane & 15;    // PV column (value channels) of this lane
-  const int vgrp = lane >> 4;    // PV token group of this lane
-  const uint8_t* pool = a.pool;
-  const int32_t* trow = a.table + static_cast<int64_t>(b) * a.table_stride;
-
-  for (int grp = p0; grp < p1; grp += 4) {
-    int64_t boff[4];
-    bool pv[4];
-#pragma unroll
-    for (int pp = 0; pp < 4; ++pp) {
-      const int page = grp + pp;
-      int64_t blk = -1;
-      if (page < p1) blk = trow[page];
-      pv[pp] = blk >= 0 && blk < a.pool_blocks;
-      boff[pp] = pv[pp] ? blk * a.block_bytes : 0;
-    }
-    // -- loads: key quarters, metadata (token layout), value words --
-    uint32_t kraw[4][KW];
-#pragma unroll
-    for (int pp = 0; pp < 4; ++pp) {
-      if (pv[pp]) {
-        load_kquarter<KB, D>(pool + boff[pp] + koff + tslot * RBK + g4 * QBYTES, kraw[pp]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < KW; ++j) kraw[pp][j] = 0;
-      }
-    }
-    const int64_t my_boff = pl == 0 ? boff[0] : pl == 1 ? boff[1] : pl == 2 ? boff[2] : boff[3];
-    const bool my_pv = pl == 0 ? pv[0] : pl == 1 ? pv[1] : pl == 2 ? pv[2] : pv[3];
-    const int tok = (grp + pl) * kBlockTokens + tslot;
-    const bool valid = my_pv && tok < seq_len;
-    float ks = 1.f, kmn = 0.f, vs = 1.f, vmn = 0.f;
-    if (valid) {
-      if constexpr (KMETA) {
-        const float2 mk = *reinterpret_cast<const float2*>(pool + my_boff + koff + kBlockTokens * RBK + tslot * kMetaBytes);
-        ks = mk.x; kmn = mk.y;
-      }
-      if constexpr (VMETA) {
-        const float2 mv = *reinterpret_cast<const float2*>(pool + my_boff + voff + kBlockTokens * RBV + tslot * kMetaBytes);
-        vs = mv.x; vmn = mv.y;
-      }
-    }
-    uint32_t vraw[2][8][VW];
-#pragma unroll
-    for (int pp2 = 0; pp2 < 2; ++pp2) {
-      const int pg = 2 * pp2 + (vgrp >> 1);
-      const int64_t vb = pg == 0 ? boff[0] : pg == 1 ? boff[1] : pg == 2 ? boff[2] : boff[3];
-      const bool vok = pg == 0 ? pv[0] : pg == 1 ? pv[1] : pg == 2 ? pv[2] : pv[3];
-      const uint8_t* base = pool + vb + voff + (8 * (vgrp & 1)) * RBV + v_lane_offset<VB, D>(vcol);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        bool ok = vok;
-        if constexpr (VB == 16) ok = ok && ((grp + pg) * kBlockTokens + 8 * (vgrp & 1) + e) < seq_len;
-        if (ok) {
-          load_vtoken<VB, D>(base + e * RBV, vraw[pp2][e]);
-        } else {
-#pragma unroll
-          for (int j = 0; j < VW; ++j) vraw[pp2][e][j] = 0;
-        }
-      }
-    }
-
-    // -- QK: one 16x16 tile per page, rows = query heads, columns = tokens --
-    float4_t cq[4];
-#pragma unroll
-    for (int pp = 0; pp < 4; ++pp) {
-      cq[pp] = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < NCK; ++c) {
-        const u32x4_t bk = KF::unpack(kraw[pp], c);
-        cq[pp] = mfma<KF::bf16>(ahi[c], bk, cq[pp]);
-        cq[pp] = mfma<KF::bf16>(alo[c], bk, cq[pp]);
-      }
-    }
-    // -- pack the four tiles: lane = token of the group, register i = head i --
-    float sc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const auto r01 = __builtin_amdgcn_permlane16_swap(f_bits(cq[0][i]), f_bits(cq[1][i]), false, false);
-      const auto r23 = __builtin_amdgcn_permlane16_swap(f_bits(cq[2][i]), f_bits(cq[3][i]), false, false);
-      const auto r = __builtin_amdgcn_permlane32_swap(r01[0], r23[0], false, false);
-      sc[i] = bits_f(r[0]);
-    }
-
-    // -- online softmax (log2 units) --
-    const float ks_q = ks * inv_qsc;
-    const float vmid = VMETA ? vmn + static_cast<float>(1 << (VB - 1)) * vs : 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (i >= G) break;
-      float z;
-      if constexpr (KMETA) z = fmaf(ks_q, sc[i], fmaf(-ks_q, biasq[i], kmn * q2[i]));
-      else z = sc[i];
-      z = valid ? z : NEG_INF;
-      const float gm = wave_max(z);
-      if (gm > m_run[i]) {
-        const float alpha = __builtin_amdgcn_exp2f(m_run[i] - gm);
-#pragma unroll
-        for (int c = 0; c < NCV; ++c) acc[c][i] *= alpha;
-        l_part[i] *= alpha;
-        mn_part[i] *= alpha;
-        m_run[i] = gm;
-      }
-      const float p = valid ? __builtin_amdgcn_exp2f(z - m_run[i]) : 0.f;
-      l_part[i] += p;
-      float w = p;
-      if constexpr (VMETA) {
-        w = p * vs;
-        mn_part[i] += valid ? p * vmid : 0.f;
-      }
-      uint32_t hb, lb;
-      if constexpr (VF::bf16) {
-        hb = f_to_bf16_rne(w);
-        lb = f_to_bf16_rne(w - bf16lo_to_f(hb));
-      } else {
-        const _Float16 hh = static_cast<_Float16>(w);
-        hb = half_bits(hh);
-        lb = half_bits(static_cast<_Float16>(w - static_cast<float>(hh)));
-      }
-      wt[0][i][lane] = static_cast<uint16_t>(hb);
-      wt[1][i][lane] = static_cast<uint16_t>(lb);
-    }
-    __syncthreads();
-
-    // -- PV: two 32-token steps --
-#pragma unroll
-    for (int pp2 = 0; pp2 < 2; ++pp2) {
-      const uint16_t* asrc;
-      if (row < 4 && row < G) asrc = &wt[0][row][32 * pp2 + 8 * vgrp];
-      else if (row >= 4 && row < 4 + G) asrc = &wt[1][row - 4][32 * pp2 + 8 * vgrp];
-      else asrc = wzero;
-      const uint4 av = *reinterpret_cast<const uint4*>(asrc);
-      const u32x4_t aw = u32x4_t{av.x, av.y, av.z, av.w};
-#pragma unroll
-      for (int c = 0; c < NCV; ++c) {
-        const u32x4_t bv = v_operand<VB, D>(vraw[pp2], vcol, c);
-        acc[c] = mfma<VF::bf16>(aw, bv, acc[c]);
-      }
-    }
-    __syncthreads();
+  for (int grp = p0; grp < p1;) {
+    load_group<KB, VB, D>(a, pool, trow, grp + 4, p1, seq_len, koff, voff, lane, gb);
+    compute_group<KB, VB, D>(ga, ahi, alo, biasq, q2, inv_qsc, G, lane, wt, wzero, st);
+    grp += 4;
+    if (grp >= p1) break;
+    load_group<KB, VB, D>(a, pool, trow, grp + 4, p1, seq_len, koff, voff, lane, ga);
+    compute_group<KB, VB, D>(gb, ahi, alo, biasq, q2, inv_qsc, G, lane, wt, wzero, st);
+    grp += 4;
   }
 
   // ---- epilogue: combine hi/lo rows, add the min term, write the partials ----
   float lsum[4], mnsum[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    lsum[i] = wave_sum(l_part[i]);
-    mnsum[i] = wave_sum(mn_part[i]);
+    lsum[i] = wave_sum_scalar(st.l_part[i]);
+    mnsum[i] = wave_sum_scalar(st.mn_part[i]);
   }
   float o[NCV][4];
 #pragma unroll
   for (int c = 0; c < NCV; ++c)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t x = f_bits(acc[c][i]);
+      const uint32_t x = f_bits(st.acc[c][i]);
       const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
       o[c][i] = (bits_f(r[0]) + bits_f(r[1])) / VF::sigma(c) + mnsum[i];
     }
@@ -637,7 +675,7 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeArgs a, float 
     for (int i = 0; i < 4; ++i) {
       if (i >= G) break;
       const int64_t bg = static_cast<int64_t>(b) * hq + h * G + i;
-      float* po = a.part_o + (bg * a.total_slots + slot) * D + v_channel<D>(vcol, 0);
+      float* po = a.part_o + (bg * a.total_slots + slot) * D + v_channel<D>(lane, 0);
       if constexpr (NCV == 8) {
         reinterpret_cast<float4*>(po)[0] = make_float4(o[0][i], o[1][i], o[2][i], o[3][i]);
         reinterpret_cast<float4*>(po)[1] = make_float4(o[4][i], o[5][i], o[6][i], o[7][i]);
@@ -646,7 +684,7 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeArgs a, float 
       }
       if (lane == 0) {
         float* ml = a.part_ml + (bg * a.total_slots + slot) * 2;
-        ml[0] = m_run[i];
+        ml[0] = st.m_run[i];
         ml[1] = lsum[i];
       }
     }

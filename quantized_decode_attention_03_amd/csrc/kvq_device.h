@@ -65,3 +65,51 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 }  // namespace kvq
+
+namespace kvq {
+
+// ---------------------------------------------------------------------------
+// DPP wave reductions (gfx9 row_shr / row_bcast patterns): the result lands in
+// lane 63 and is read into a scalar. Each step is one VALU op with a DPP
+// source, with no LDS round trip.
+// ---------------------------------------------------------------------------
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ float dpp_or(float old, float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old), __builtin_bit_cast(int, v),
+                                                               CTRL, ROWMASK, 0xf, false));
+}
+
+__device__ __forceinline__ float wave_max_scalar(float x) {
+  const float ninf = -__builtin_huge_valf();
+  x = fmaxf(x, dpp_or<kDppRowShr1, 0xf>(ninf, x));
+  x = fmaxf(x, dpp_or<kDppRowShr2, 0xf>(ninf, x));
+  x = fmaxf(x, dpp_or<kDppRowShr4, 0xf>(ninf, x));
+  x = fmaxf(x, dpp_or<kDppRowShr8, 0xf>(ninf, x));
+  x = fmaxf(x, dpp_or<kDppRowBcast15, 0xa>(ninf, x));
+  x = fmaxf(x, dpp_or<kDppRowBcast31, 0xc>(ninf, x));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+
+__device__ __forceinline__ float wave_sum_scalar(float x) {
+  x += dpp_or<kDppRowShr1, 0xf>(0.f, x);
+  x += dpp_or<kDppRowShr2, 0xf>(0.f, x);
+  x += dpp_or<kDppRowShr4, 0xf>(0.f, x);
+  x += dpp_or<kDppRowShr8, 0xf>(0.f, x);
+  x += dpp_or<kDppRowBcast15, 0xa>(0.f, x);
+  x += dpp_or<kDppRowBcast31, 0xc>(0.f, x);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+
+// A constant materialised in a VGPR: lets v_and_or_b32 / v_perm_b32 take it
+// as their vector operand (gfx9 VOP3 encodings take no literal constants and
+// at most one scalar operand).
+__device__ __forceinline__ uint32_t vconst(uint32_t c) {
+  uint32_t r;
+  asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(c));
+  return r;
+}
+
+}  // namespace kvq

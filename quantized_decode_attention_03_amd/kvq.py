@@ -307,3 +307,46 @@ def kvq_decode_merge(segments, batch, out, ws, stream=None):
                                 _dev_ptr(out, (torch.float32,), "out"), _dev_ptr(ws, (torch.uint8,), "ws"),
                                 ws.numel(), _stream(stream))
     _check(st, "kvq_decode_merge")
+
+
+# ---------------------------------------------------------------------------
+# Pre-marshalled calls: pack the ctypes arguments of an entry point once and
+# invoke it many times (the per-layer loop of a decode step). Marshalling only.
+# ---------------------------------------------------------------------------
+
+class PreparedCall:
+    def __init__(self, fn, args, what, keep):
+        self._fn, self._args, self._what, self._keep = fn, args, what, keep
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != KVQ_OK:
+            _check(st, self._what)
+
+
+def prepare_quantize_append(layout, pool, block_table, start_pos, k, v, stream=None):
+    import torch
+    dt = KVQ_BF16 if k.dtype == torch.bfloat16 else KVQ_F32
+    args = (ctypes.byref(layout), _dev_ptr(pool, (torch.uint8,), "pool"), int(pool.shape[0]),
+            _dev_ptr(block_table, (torch.int32,), "block_table"), int(block_table.shape[1]), int(k.shape[0]),
+            _dev_ptr(start_pos, (torch.int32,), "start_pos"), int(k.shape[1]),
+            _dev_ptr(k, (torch.float32, torch.bfloat16), "k"), _dev_ptr(v, (torch.float32, torch.bfloat16), "v"),
+            dt, _stream(stream))
+    return PreparedCall(lib().kvq_quantize_append, args, "kvq_quantize_append", (layout, pool, block_table, start_pos, k, v))
+
+
+def prepare_decode_partial(segments, q, ws, stream=None):
+    import torch
+    segs = _segments(segments)
+    dt = KVQ_BF16 if q.dtype == torch.bfloat16 else KVQ_F32
+    args = (segs, len(segments), int(q.shape[0]), _dev_ptr(q, (torch.float32, torch.bfloat16), "q"), dt,
+            _dev_ptr(ws, (torch.uint8,), "ws"), ws.numel(), _stream(stream))
+    return PreparedCall(lib().kvq_decode_partial, args, "kvq_decode_partial", (segments, q, ws))
+
+
+def prepare_decode_merge(segments, batch, out, ws, stream=None):
+    import torch
+    segs = _segments(segments)
+    args = (segs, len(segments), int(batch), _dev_ptr(out, (torch.float32,), "out"),
+            _dev_ptr(ws, (torch.uint8,), "ws"), ws.numel(), _stream(stream))
+    return PreparedCall(lib().kvq_decode_merge, args, "kvq_decode_merge", (segments, out, ws))
