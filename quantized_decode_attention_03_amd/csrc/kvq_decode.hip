@@ -38,8 +38,6 @@ namespace kvq {
 
 namespace {
 
-// fp16 pair (1024, 1024), held in a VGPR so (x & mask) | bias is one v_and_or_b32
-__device__ __forceinline__ uint32_t kbias() { return vconst(0x64006400u); }
 
 __device__ __forceinline__ float4_t mfma_f16(u32x4_t a, u32x4_t b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
@@ -72,65 +70,67 @@ template <int KB, int D> struct KFmt;
 
 template <int D> struct KFmt<4, D> {
   static constexpr int kWords = D / 32;  // quarter = D/8 bytes
-  static constexpr float sigma = 16.f;
   static constexpr bool bf16 = false;
+  // nibbles 0 and 2 sit at bits 0-3 of their half (sigma 1), nibbles 1 and 3 at
+  // bits 4-7 (sigma 16); both reach their place with at most one shift
+  __device__ static float sigma(int /*c*/, int e) { return (e & 2) ? 16.f : 1.f; }
   __device__ static int channel(int c, int e) {
     constexpr int rel[8] = {0, 4, 1, 5, 2, 6, 3, 7};
     return 8 * c + rel[e];
   }
-  __device__ static u32x4_t unpack(const uint32_t (&w)[kWords], int c) {
-    const uint32_t x = w[c];
+  __device__ static u32x4_t unpack(const uint32_t (&w)[kWords], int c, uint32_t bias) {
+    const uint32_t x = w[c], x8 = x >> 8;
     u32x4_t r;
-    r[0] = and_or(x << 4, 0x00f000f0u, kbias());
-    r[1] = and_or(x, 0x00f000f0u, kbias());
-    r[2] = and_or(x >> 4, 0x00f000f0u, kbias());
-    r[3] = and_or(x >> 8, 0x00f000f0u, kbias());
+    r[0] = and_or(x, 0x000f000fu, bias);
+    r[1] = and_or(x, 0x00f000f0u, bias);
+    r[2] = and_or(x8, 0x000f000fu, bias);
+    r[3] = and_or(x8, 0x00f000f0u, bias);
     return r;
   }
 };
 
 template <int D> struct KFmt<2, D> {
   static constexpr int kWords = D / 64;  // quarter = D/16 bytes
-  static constexpr float sigma = 256.f;
   static constexpr bool bf16 = false;
+  __device__ static float sigma(int, int) { return 256.f; }
   __device__ static int channel(int c, int e) {
     const int m = c >> 1, k = 4 * (c & 1) + (e >> 1);
     return 16 * m + ((e & 1) ? 8 : 0) + k;
   }
   template <int K>
-  __device__ static uint32_t pair(uint32_t x) { return and_or(shl_signed<8 - 2 * K>(x), 0x03000300u, kbias()); }
-  __device__ static u32x4_t unpack(const uint32_t (&w)[kWords], int c) {
+  __device__ static uint32_t pair(uint32_t x, uint32_t b) { return and_or(shl_signed<8 - 2 * K>(x), 0x03000300u, b); }
+  __device__ static u32x4_t unpack(const uint32_t (&w)[kWords], int c, uint32_t b) {
     const uint32_t x = w[c >> 1];
     u32x4_t r;
-    if (c & 1) { r[0] = pair<4>(x); r[1] = pair<5>(x); r[2] = pair<6>(x); r[3] = pair<7>(x); }
-    else       { r[0] = pair<0>(x); r[1] = pair<1>(x); r[2] = pair<2>(x); r[3] = pair<3>(x); }
+    if (c & 1) { r[0] = pair<4>(x, b); r[1] = pair<5>(x, b); r[2] = pair<6>(x, b); r[3] = pair<7>(x, b); }
+    else       { r[0] = pair<0>(x, b); r[1] = pair<1>(x, b); r[2] = pair<2>(x, b); r[3] = pair<3>(x, b); }
     return r;
   }
 };
 
 template <int D> struct KFmt<8, D> {
   static constexpr int kWords = D / 16;  // quarter = D/4 bytes
-  static constexpr float sigma = 1.f;
   static constexpr bool bf16 = false;
+  __device__ static float sigma(int, int) { return 1.f; }
   __device__ static int channel(int c, int e) {
     constexpr int rel[8] = {0, 2, 1, 3, 4, 6, 5, 7};
     return 8 * c + rel[e];
   }
-  __device__ static u32x4_t unpack(const uint32_t (&w)[kWords], int c) {
+  __device__ static u32x4_t unpack(const uint32_t (&w)[kWords], int c, uint32_t b) {
     const uint32_t x0 = w[2 * c], x1 = w[2 * c + 1];
     u32x4_t r;
-    r[0] = and_or(x0, 0x00ff00ffu, kbias());
-    r[1] = and_or(x0 >> 8, 0x00ff00ffu, kbias());
-    r[2] = and_or(x1, 0x00ff00ffu, kbias());
-    r[3] = and_or(x1 >> 8, 0x00ff00ffu, kbias());
+    r[0] = and_or(x0, 0x00ff00ffu, b);
+    r[1] = and_or(x0 >> 8, 0x00ff00ffu, b);
+    r[2] = and_or(x1, 0x00ff00ffu, b);
+    r[3] = and_or(x1 >> 8, 0x00ff00ffu, b);
     return r;
   }
 };
 
 template <int D> struct KFmt<3, D> {
   static constexpr int kWords = (3 * D / 32 + 3) / 4;  // quarter = 3D/32 bytes (12 or 6)
-  static constexpr float sigma = 128.f;
   static constexpr bool bf16 = false;
+  __device__ static float sigma(int, int) { return 128.f; }
   __device__ static int channel(int c, int e) { return 8 * c + e; }
   template <int K>
   __device__ static uint32_t code(const uint32_t (&w)[kWords]) {
@@ -139,34 +139,34 @@ template <int D> struct KFmt<3, D> {
     else return ((w[i] >> sh) | (w[i + 1] << (32 - sh))) & 7u;
   }
   template <int C>
-  __device__ static u32x4_t unpack_c(const uint32_t (&w)[kWords]) {
+  __device__ static u32x4_t unpack_c(const uint32_t (&w)[kWords], uint32_t b) {
     u32x4_t r;
-    r[0] = (((code<8 * C + 1>(w) << 16) | code<8 * C + 0>(w)) << 7) | kbias();
-    r[1] = (((code<8 * C + 3>(w) << 16) | code<8 * C + 2>(w)) << 7) | kbias();
-    r[2] = (((code<8 * C + 5>(w) << 16) | code<8 * C + 4>(w)) << 7) | kbias();
-    r[3] = (((code<8 * C + 7>(w) << 16) | code<8 * C + 6>(w)) << 7) | kbias();
+    r[0] = (((code<8 * C + 1>(w) << 16) | code<8 * C + 0>(w)) << 7) | b;
+    r[1] = (((code<8 * C + 3>(w) << 16) | code<8 * C + 2>(w)) << 7) | b;
+    r[2] = (((code<8 * C + 5>(w) << 16) | code<8 * C + 4>(w)) << 7) | b;
+    r[3] = (((code<8 * C + 7>(w) << 16) | code<8 * C + 6>(w)) << 7) | b;
     return r;
   }
-  __device__ static u32x4_t unpack(const uint32_t (&w)[kWords], int c) {
+  __device__ static u32x4_t unpack(const uint32_t (&w)[kWords], int c, uint32_t b) {
     if constexpr (D == 128) {
       switch (c) {
-        case 0: return unpack_c<0>(w);
-        case 1: return unpack_c<1>(w);
-        case 2: return unpack_c<2>(w);
-        default: return unpack_c<3>(w);
+        case 0: return unpack_c<0>(w, b);
+        case 1: return unpack_c<1>(w, b);
+        case 2: return unpack_c<2>(w, b);
+        default: return unpack_c<3>(w, b);
       }
     } else {
-      return c == 0 ? unpack_c<0>(w) : unpack_c<1>(w);
+      return c == 0 ? unpack_c<0>(w, b) : unpack_c<1>(w, b);
     }
   }
 };
 
 template <int D> struct KFmt<16, D> {
   static constexpr int kWords = D / 8;  // quarter = D/2 bytes of bf16
-  static constexpr float sigma = 1.f;
   static constexpr bool bf16 = true;
+  __device__ static float sigma(int, int) { return 1.f; }
   __device__ static int channel(int c, int e) { return 8 * c + e; }
-  __device__ static u32x4_t unpack(const uint32_t (&w)[kWords], int c) {
+  __device__ static u32x4_t unpack(const uint32_t (&w)[kWords], int c, uint32_t) {
     u32x4_t r;
     r[0] = w[4 * c]; r[1] = w[4 * c + 1]; r[2] = w[4 * c + 2]; r[3] = w[4 * c + 3];
     return r;
@@ -257,7 +257,8 @@ template <int VB, int D> struct VFmt {
 // Produce the B operand (4 dwords = 8 tokens) of value chunk c for one lane.
 // raw[e][*] are the 8 tokens' words; n is the lane's column.
 template <int VB, int D>
-__device__ __forceinline__ u32x4_t v_operand(const uint32_t (&raw)[8][VRaw<VB, D>::kWords], int n, int c) {
+__device__ __forceinline__ u32x4_t v_operand(const uint32_t (&raw)[8][VRaw<VB, D>::kWords], int n, int c,
+                                             uint32_t bias) {
   u32x4_t r;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
@@ -274,7 +275,7 @@ __device__ __forceinline__ u32x4_t v_operand(const uint32_t (&raw)[8][VRaw<VB, D
       if (cc >= 2) x >>= 8;
       const uint32_t mask = (cc & 1) ? 0x00f000f0u : 0x000f000fu;
       const float sg = (cc & 1) ? 16.f : 1.f;
-      out = and_or(x, mask, kbias());
+      out = and_or(x, mask, bias);
       const _Float16 off = static_cast<_Float16>(-(1024.f + 8.f * sg));
       out = pk_add_h(out, half_bits(off) * 0x10001u);
     } else if constexpr (VB == 2) {
@@ -289,7 +290,7 @@ __device__ __forceinline__ u32x4_t v_operand(const uint32_t (&raw)[8][VRaw<VB, D
         x = perm_b32(b[0], a[0], 0x0c000c00u | ((4 + k) << 16) | k);
         cc = c;
       }
-      out = and_or(x, 0x00030003u << (2 * cc), kbias());
+      out = and_or(x, 0x00030003u << (2 * cc), bias);
       const float sg = static_cast<float>(1 << (2 * cc));
       const _Float16 off = static_cast<_Float16>(-(1024.f + 2.f * sg));
       out = pk_add_h(out, half_bits(off) * 0x10001u);
@@ -297,7 +298,7 @@ __device__ __forceinline__ u32x4_t v_operand(const uint32_t (&raw)[8][VRaw<VB, D
       const int word = D == 128 ? (c >> 2) : 0;
       const uint32_t k = c & 3;
       const uint32_t x = perm_b32(b[word], a[word], 0x0c000c00u | ((4 + k) << 16) | k);
-      out = x | kbias();
+      out = x | bias;
       const _Float16 off = static_cast<_Float16>(-(1024.f + 128.f));
       out = pk_add_h(out, half_bits(off) * 0x10001u);
     } else if constexpr (VB == 3) {
@@ -306,7 +307,7 @@ __device__ __forceinline__ u32x4_t v_operand(const uint32_t (&raw)[8][VRaw<VB, D
       const uint32_t wa = __builtin_amdgcn_alignbit(a[1], a[0], sh);
       const uint32_t wb = __builtin_amdgcn_alignbit(b[1], b[0], sh);
       const uint32_t ca = (wa >> (3 * c)) & 7u, cb = (wb >> (3 * c)) & 7u;
-      out = (((cb << 16) | ca) << 7) | kbias();
+      out = (((cb << 16) | ca) << 7) | bias;
       const _Float16 off = static_cast<_Float16>(-(1024.f + 4.f * 128.f));
       out = pk_add_h(out, half_bits(off) * 0x10001u);
     } else {  // bf16 values: channel n*D/16 + c is half (c & 1) of word c/2
@@ -343,7 +344,8 @@ constexpr float kRescaleSlack = 4.f;
 // Every load is issued unconditionally (pages past the split or unmapped read
 // block 0 and are masked afterwards), so the number of loads in flight is
 // static and the wait before a group's compute leaves the next group's loads
-// outstanding.
+// outstanding. Each load instruction reads one page, so its base address is
+// wave-uniform and the per-lane part is a loop-invariant offset.
 template <int KB, int VB, int D>
 __device__ __forceinline__ void load_group(const DecodeArgs& a, const uint8_t* pool, const int32_t* trow, int grp,
                                            int p1, int seq_len, int64_t koff, int64_t voff, int lane,
@@ -351,46 +353,59 @@ __device__ __forceinline__ void load_group(const DecodeArgs& a, const uint8_t* p
   constexpr int RBK = D * KB / 8, RBV = D * VB / 8, QBYTES = RBK / 4;
   const int tslot = lane & 15, g4 = lane >> 4;
   int64_t boff[4];
-  bool pv[4];
+  uint32_t pv = 0;  // bit pp: page grp + pp is mapped
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp) {
     const int page = grp + pp;
     const int64_t blk = trow[min(page, p1 - 1)];
-    pv[pp] = page < p1 && blk >= 0 && blk < a.pool_blocks;
-    boff[pp] = pv[pp] ? blk * a.block_bytes : 0;
+    const bool ok = page < p1 && blk >= 0 && blk < a.pool_blocks;
+    pv |= static_cast<uint32_t>(ok) << pp;
+    boff[pp] = ok ? blk * a.block_bytes : 0;
   }
+  const int kl = tslot * RBK + g4 * QBYTES;  // lane offsets (loop invariant)
+  const int vl = 4 * g4 * RBV + v_lane_offset<VB, D>(tslot);
+  const int ml = tslot * kMetaBytes;
 #pragma unroll
-  for (int pp = 0; pp < 4; ++pp)
-    load_kquarter<KB, D>(pool + boff[pp] + koff + tslot * RBK + g4 * QBYTES, g.k[pp]);
-  // token layout: lane = (page g4, slot tslot)
-  const int64_t my_boff = g4 == 0 ? boff[0] : g4 == 1 ? boff[1] : g4 == 2 ? boff[2] : boff[3];
-  const bool my_pv = g4 == 0 ? pv[0] : g4 == 1 ? pv[1] : g4 == 2 ? pv[2] : pv[3];
-  g.valid = my_pv && (grp + g4) * kBlockTokens + tslot < seq_len;
+  for (int pp = 0; pp < 4; ++pp) load_kquarter<KB, D>(pool + boff[pp] + koff + kl, g.k[pp]);
+  // token layout: lane = (page g4, slot tslot); each page's metadata by its 16 lanes
+  g.valid = ((pv >> g4) & 1u) && (grp + g4) * kBlockTokens + tslot < seq_len;
+  // (all lanes active: a load under a divergent branch would make the compiler
+  // wait for every outstanding load, including the prefetch)
+  const int64_t my_boff = (g4 & 2) ? ((g4 & 1) ? boff[3] : boff[2]) : ((g4 & 1) ? boff[1] : boff[0]);
+  const uint8_t* mbase = pool + my_boff + ml;
   g.ks = 1.f; g.kmn = 0.f; g.vs = 1.f; g.vmn = 0.f;
   if constexpr (KB != 16) {
-    const float2 mk = *reinterpret_cast<const float2*>(pool + my_boff + koff + kBlockTokens * RBK + tslot * kMetaBytes);
+    const float2 mk = *reinterpret_cast<const float2*>(mbase + koff + kBlockTokens * RBK);
     g.ks = mk.x; g.kmn = mk.y;
   }
   if constexpr (VB != 16) {
-    const float2 mv = *reinterpret_cast<const float2*>(pool + my_boff + voff + kBlockTokens * RBV + tslot * kMetaBytes);
+    const float2 mv = *reinterpret_cast<const float2*>(mbase + voff + kBlockTokens * RBV);
     g.vs = mv.x; g.vmn = mv.y;
   }
-  // value layout: lane = (column n = tslot, token group g4) over page pairs
+  // value layout: lane = (column n = tslot, K-slot group g4); K-slot e of a page
+  // pair is slot 4*g4 + (e & 3) of page 2*pp2 + (e >> 2)
   g.vmask = 0;
 #pragma unroll
   for (int pp2 = 0; pp2 < 2; ++pp2) {
-    const int pg = 2 * pp2 + (g4 >> 1);
-    const int64_t vb = pg == 0 ? boff[0] : pg == 1 ? boff[1] : pg == 2 ? boff[2] : boff[3];
-    const bool vok = pg == 0 ? pv[0] : pg == 1 ? pv[1] : pg == 2 ? pv[2] : pv[3];
-    const uint8_t* base = pool + vb + voff + (8 * (g4 & 1)) * RBV + v_lane_offset<VB, D>(tslot);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      load_vtoken<VB, D>(base + e * RBV, g.v[pp2][e]);
-      const bool ok = vok && ((grp + pg) * kBlockTokens + 8 * (g4 & 1) + e) < seq_len;
+      const int pg = 2 * pp2 + (e >> 2);
+      load_vtoken<VB, D>(pool + boff[pg] + voff + (e & 3) * RBV + vl, g.v[pp2][e]);
+      const bool ok = ((pv >> pg) & 1u) && (grp + pg) * kBlockTokens + 4 * g4 + (e & 3) < seq_len;
       g.vmask |= static_cast<uint32_t>(ok) << (8 * pp2 + e);
     }
   }
 }
+
+// Waves per SIMD each instance is compiled for: its working set (three group
+// buffers in flight) fits 256 registers at head_dim 128, 168 for most
+// head_dim 64 formats; bf16 segments take a whole SIMD.
+template <int KB, int VB, int D>
+struct PartialWaves {
+  static constexpr int value =
+      D == 64 ? ((VB == 3 || VB == 16 || KB == 3 || KB == 8 || KB == 16) ? 2 : 3)
+              : (VB == 16 || KB == 16 || KB == 8) ? 1 : 2;
+};
 
 template <int KB, int VB, int D>
 struct SplitState {
@@ -401,9 +416,8 @@ struct SplitState {
 };
 
 template <int KB, int VB, int D>
-__device__ __forceinline__ void compute_group(GroupRaw<KB, VB, D>& g, const u32x4_t (&ahi)[D / 32],
-                                              const u32x4_t (&alo)[D / 32], const float (&biasq)[4],
-                                              const float (&q2)[4], float inv_qsc, int G, int lane,
+__device__ __forceinline__ void compute_group(GroupRaw<KB, VB, D>& g, const uint4 (*qa)[2][64], const float (&biasq)[4],
+                                              const float (&q2)[4], float inv_qsc, int G, int lane, uint32_t bias,
                                               uint16_t (*wt)[4][64], const uint16_t* wzero,
                                               SplitState<KB, VB, D>& st) {
   using KF = KFmt<KB, D>;
@@ -413,53 +427,68 @@ __device__ __forceinline__ void compute_group(GroupRaw<KB, VB, D>& g, const u32x
   constexpr float NEG_INF = -__builtin_huge_valf();
   const int row = lane & 15, g4 = lane >> 4;
 
-  // QK: one 16x16 tile per page (rows = query heads, columns = tokens)
+  // QK: one 16x16 tile per page (rows = query heads, columns = tokens). The
+  // query fragments come from LDS once per chunk and feed all four pages.
   float4_t cq[4];
 #pragma unroll
-  for (int pp = 0; pp < 4; ++pp) {
-    cq[pp] = float4_t{0.f, 0.f, 0.f, 0.f};
+  for (int pp = 0; pp < 4; ++pp) cq[pp] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < NCK; ++c) {
-      const u32x4_t bk = KF::unpack(g.k[pp], c);
-      cq[pp] = mfma<KF::bf16>(ahi[c], bk, cq[pp]);
-      cq[pp] = mfma<KF::bf16>(alo[c], bk, cq[pp]);
+  for (int c = 0; c < NCK; ++c) {
+    const uint4 h4 = qa[c][0][lane], l4 = qa[c][1][lane];
+    const u32x4_t ah = u32x4_t{h4.x, h4.y, h4.z, h4.w}, al = u32x4_t{l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      const u32x4_t bk = KF::unpack(g.k[pp], c, bias);
+      cq[pp] = mfma<KF::bf16>(ah, bk, cq[pp]);
+      cq[pp] = mfma<KF::bf16>(al, bk, cq[pp]);
     }
   }
   // pack the four tiles: lane = token of the group, register i = head i
-  float sc[4];
+  float z[4];
+  const float ks_q = g.ks * inv_qsc;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const auto r01 = __builtin_amdgcn_permlane16_swap(f_bits(cq[0][i]), f_bits(cq[1][i]), false, false);
     const auto r23 = __builtin_amdgcn_permlane16_swap(f_bits(cq[2][i]), f_bits(cq[3][i]), false, false);
     const auto r = __builtin_amdgcn_permlane32_swap(r01[0], r23[0], false, false);
-    sc[i] = bits_f(r[0]);
+    const float sc = bits_f(r[0]);
+    float zi;
+    if constexpr (KMETA) zi = fmaf(ks_q, sc, fmaf(-ks_q, biasq[i], g.kmn * q2[i]));
+    else zi = sc;
+    z[i] = (g.valid && i < G) ? zi : NEG_INF;
   }
 
-  // online softmax (log2 units) with a lazily raised reference max
-  const float ks_q = g.ks * inv_qsc;
-  const float vmid = VMETA ? g.vmn + static_cast<float>(1 << (VB - 1)) * g.vs : 0.f;
+  // online softmax (log2 units): the reference max is raised (and the
+  // accumulators rescaled) only when a score exceeds it by more than the slack
+  bool over = false;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) over = over || z[i] > st.m_run[i] + kRescaleSlack;
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(over) != 0, 0)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i >= G) break;
+      const float gm = wave_max_scalar(z[i]);
+      if (gm > st.m_run[i] + kRescaleSlack) {
+        const float alpha = __builtin_amdgcn_exp2f(st.m_run[i] - gm);
+#pragma unroll
+        for (int c = 0; c < NCV; ++c) st.acc[c][i] *= alpha;
+        st.l_part[i] *= alpha;
+        st.mn_part[i] *= alpha;
+        st.m_run[i] = gm;
+      }
+    }
+  }
+  const float vs_eff = VMETA ? (g.valid ? g.vs : 0.f) : 1.f;
+  const float vmid_eff = VMETA ? (g.valid ? g.vmn + static_cast<float>(1 << (VB - 1)) * g.vs : 0.f) : 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if (i >= G) break;
-    float z;
-    if constexpr (KMETA) z = fmaf(ks_q, sc[i], fmaf(-ks_q, biasq[i], g.kmn * q2[i]));
-    else z = sc[i];
-    z = g.valid ? z : NEG_INF;
-    const float gm = wave_max_scalar(z);
-    if (gm > st.m_run[i] + kRescaleSlack) {
-      const float alpha = __builtin_amdgcn_exp2f(st.m_run[i] - gm);
-#pragma unroll
-      for (int c = 0; c < NCV; ++c) st.acc[c][i] *= alpha;
-      st.l_part[i] *= alpha;
-      st.mn_part[i] *= alpha;
-      st.m_run[i] = gm;
-    }
-    const float p = g.valid ? __builtin_amdgcn_exp2f(z - st.m_run[i]) : 0.f;
+    const float p = __builtin_amdgcn_exp2f(z[i] - st.m_run[i]);  // masked: exp2(-inf) = 0
     st.l_part[i] += p;
     float w = p;
     if constexpr (VMETA) {
-      w = g.valid ? p * g.vs : 0.f;
-      st.mn_part[i] = fmaf(p, g.valid ? vmid : 0.f, st.mn_part[i]);
+      w = p * vs_eff;
+      st.mn_part[i] = fmaf(p, vmid_eff, st.mn_part[i]);
     }
     uint32_t hb, lb;
     if constexpr (VF::bf16) {
@@ -475,15 +504,18 @@ __device__ __forceinline__ void compute_group(GroupRaw<KB, VB, D>& g, const u32x
   }
   __syncthreads();
 
-  // PV: two 32-token steps
+  // PV: two 32-token steps; K-slot e of lane group g4 is token 4*g4 + (e & 3) of
+  // the step's page e >> 2
 #pragma unroll
   for (int pp2 = 0; pp2 < 2; ++pp2) {
     const uint16_t* asrc;
-    if (row < 4 && row < G) asrc = &wt[0][row][32 * pp2 + 8 * g4];
-    else if (row >= 4 && row < 4 + G) asrc = &wt[1][row - 4][32 * pp2 + 8 * g4];
-    else asrc = wzero;
-    const uint4 av = *reinterpret_cast<const uint4*>(asrc);
-    const u32x4_t aw = u32x4_t{av.x, av.y, av.z, av.w};
+    int step = 16;
+    if (row < 4 && row < G) asrc = &wt[0][row][32 * pp2 + 4 * g4];
+    else if (row >= 4 && row < 4 + G) asrc = &wt[1][row - 4][32 * pp2 + 4 * g4];
+    else { asrc = wzero; step = 0; }
+    const uint2 a0 = *reinterpret_cast<const uint2*>(asrc);
+    const uint2 a1 = *reinterpret_cast<const uint2*>(asrc + step);
+    const u32x4_t aw = u32x4_t{a0.x, a0.y, a1.x, a1.y};
     if constexpr (VB == 16) {
       if ((g.vmask >> (8 * pp2) & 0xffu) != 0xffu) {  // a masked token in this pair: clear its words
         auto& vv = g.v[pp2];
@@ -496,7 +528,7 @@ __device__ __forceinline__ void compute_group(GroupRaw<KB, VB, D>& g, const u32x
     }
 #pragma unroll
     for (int c = 0; c < NCV; ++c) {
-      const u32x4_t bv = v_operand<VB, D>(g.v[pp2], row, c);
+      const u32x4_t bv = v_operand<VB, D>(g.v[pp2], row, c, bias);
       st.acc[c] = mfma<VF::bf16>(aw, bv, st.acc[c]);
     }
   }
@@ -504,7 +536,9 @@ __device__ __forceinline__ void compute_group(GroupRaw<KB, VB, D>& g, const u32x
 }
 
 template <int KB, int VB, int D>
-__global__ __launch_bounds__(64) void decode_partial_kernel(DecodeArgs a, float qscale) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PartialWaves<KB, VB, D>::value,
+                                                                    PartialWaves<KB, VB, D>::value)))
+void decode_partial_kernel(DecodeArgs a, float qscale) {
   using KF = KFmt<KB, D>;
   using VF = VFmt<VB, D>;
   constexpr int NCK = D / 32;               // QK chunks (32 channels each)
@@ -512,6 +546,7 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeArgs a, float 
   constexpr float NEG_INF = -__builtin_huge_valf();
 
   __shared__ float qs[4][D];
+  __shared__ uint4 qa[NCK][2][64];   // QK A fragments (hi, lo) in lane order
   __shared__ __attribute__((aligned(16))) uint16_t wt[2][4][64];
   __shared__ __attribute__((aligned(16))) uint16_t wzero[8];
 
@@ -544,9 +579,10 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeArgs a, float 
 
   const uint8_t* pool = a.pool;
   const int32_t* trow = a.table + static_cast<int64_t>(b) * a.table_stride;
-  // first group's loads go out before the query is prepared
-  GroupRaw<KB, VB, D> ga, gb;
+  // the first two groups' loads go out before the query is prepared
+  GroupRaw<KB, VB, D> ga, gb, gc;
   load_group<KB, VB, D>(a, pool, trow, p0, p1, seq_len, koff, voff, lane, ga);
+  load_group<KB, VB, D>(a, pool, trow, p0 + 4, p1, seq_len, koff, voff, lane, gb);
 
   // ---- q' = R q for the G query heads of this KV head (LDS butterflies) ----
   for (int e = lane; e < 4 * D; e += 64) {
@@ -580,7 +616,7 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeArgs a, float 
   for (int c = 0; c < NCK; ++c)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float v = row < G ? qs[row][g4 * (D / 4) + KF::channel(c, e)] * qscale / KF::sigma : 0.f;
+      const float v = row < G ? qs[row][g4 * (D / 4) + KF::channel(c, e)] * qscale / KF::sigma(c, e) : 0.f;
       amax = fmaxf(amax, fabsf(v));
     }
   amax = wave_max_scalar(amax);
@@ -591,8 +627,8 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeArgs a, float 
     frexpf(amax, &ex);
     qsc = ldexpf(1.f, 10 - ex);
   }
-  u32x4_t ahi[NCK], alo[NCK];
   double q1 = 0.0;  // this lane's share of the sum of the A values used (bias correction)
+  double q2l = 0.0; // and of sum_j q~_j (the min term)
 #pragma unroll
   for (int c = 0; c < NCK; ++c) {
 #pragma unroll
@@ -601,7 +637,8 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeArgs a, float 
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int e = 2 * v + half;
-        const float x = row < G ? qs[row][g4 * (D / 4) + KF::channel(c, e)] * qscale / KF::sigma * qsc : 0.f;
+        const float qt = row < G ? qs[row][g4 * (D / 4) + KF::channel(c, e)] * qscale : 0.f;
+        const float x = qt / KF::sigma(c, e) * qsc;
         uint32_t hb, lb;
         float hv, lv;
         if constexpr (KF::bf16) {
@@ -615,42 +652,54 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeArgs a, float 
           hb = half_bits(hh); lb = half_bits(ll);
         }
         q1 += static_cast<double>(hv) + static_cast<double>(lv);
+        q2l += static_cast<double>(qt);
         hp |= hb << (16 * half);
         lp |= lb << (16 * half);
       }
-      ahi[c][v] = hp;
-      alo[c][v] = lp;
+      reinterpret_cast<uint32_t*>(&qa[c][0][lane])[v] = hp;
+      reinterpret_cast<uint32_t*>(&qa[c][1][lane])[v] = lp;
     }
   }
   // Sum over the four quarters (lanes row, row+16, row+32, row+48), in fp64.
   q1 += __shfl_xor(q1, 16, 64);
   q1 += __shfl_xor(q1, 32, 64);
-  const float q1t = static_cast<float>(q1);
+  q2l += __shfl_xor(q2l, 16, 64);
+  q2l += __shfl_xor(q2l, 32, 64);
   // Per query head constants, broadcast from lane i (row i):
   //   biasq_i = 1024 * Q1_i (scaled units), q2_i = sum_j q~_ij (log2 units).
   float biasq[4], q2[4];
   const float inv_qsc = 1.f / qsc;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float q1i = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, q1t), i));
+    const float q1i = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, static_cast<float>(q1)), i));
     biasq[i] = KF::bf16 ? 0.f : 1024.f * q1i;
-    q2[i] = q1i * KF::sigma * inv_qsc;
+    q2[i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, static_cast<float>(q2l)), i));
   }
+  const uint32_t bias = vconst(0x64006400u);  // fp16 pair (1024, 1024)
+
+  __syncthreads();  // the A fragments are read by the same wave; order LDS writes before reads
 
   // ---- main loop: two groups per trip, loads of the next group in flight ----
   SplitState<KB, VB, D> st;
 #pragma unroll
   for (int c = 0; c < NCV; ++c) st.acc[c] = float4_t{0.f, 0.f, 0.f, 0.f};
+  // A finite floor (not -inf) for the reference max: exp2(z - m) stays 0 for
+  // masked tokens (z = -inf) before any token was seen.
 #pragma unroll
-  for (int i = 0; i < 4; ++i) { st.m_run[i] = NEG_INF; st.l_part[i] = 0.f; st.mn_part[i] = 0.f; }
+  for (int i = 0; i < 4; ++i) { st.m_run[i] = -1e30f; st.l_part[i] = 0.f; st.mn_part[i] = 0.f; }
 
+  // three rotating buffers: while group g is computed, g+1 and g+2 are in flight
   for (int grp = p0; grp < p1;) {
-    load_group<KB, VB, D>(a, pool, trow, grp + 4, p1, seq_len, koff, voff, lane, gb);
-    compute_group<KB, VB, D>(ga, ahi, alo, biasq, q2, inv_qsc, G, lane, wt, wzero, st);
+    load_group<KB, VB, D>(a, pool, trow, grp + 8, p1, seq_len, koff, voff, lane, gc);
+    compute_group<KB, VB, D>(ga, qa, biasq, q2, inv_qsc, G, lane, bias, wt, wzero, st);
     grp += 4;
     if (grp >= p1) break;
-    load_group<KB, VB, D>(a, pool, trow, grp + 4, p1, seq_len, koff, voff, lane, ga);
-    compute_group<KB, VB, D>(gb, ahi, alo, biasq, q2, inv_qsc, G, lane, wt, wzero, st);
+    load_group<KB, VB, D>(a, pool, trow, grp + 8, p1, seq_len, koff, voff, lane, ga);
+    compute_group<KB, VB, D>(gb, qa, biasq, q2, inv_qsc, G, lane, bias, wt, wzero, st);
+    grp += 4;
+    if (grp >= p1) break;
+    load_group<KB, VB, D>(a, pool, trow, grp + 8, p1, seq_len, koff, voff, lane, gb);
+    compute_group<KB, VB, D>(gc, qa, biasq, q2, inv_qsc, G, lane, bias, wt, wzero, st);
     grp += 4;
   }
 
@@ -684,7 +733,7 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeArgs a, float 
       }
       if (lane == 0) {
         float* ml = a.part_ml + (bg * a.total_slots + slot) * 2;
-        ml[0] = st.m_run[i];
+        ml[0] = lsum[i] > 0.f ? st.m_run[i] : NEG_INF;
         ml[1] = lsum[i];
       }
     }
@@ -698,26 +747,51 @@ template <int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(MergeArgs a, float rs_n) {
   constexpr int CPL = D / 64;  // channels per lane: [CPL*lane, CPL*lane + CPL)
   constexpr float NEG_INF = -__builtin_huge_valf();
+  __shared__ float wsh[256];   // split weights 2^(m_s - M) of the current chunk of splits
   const int lane = threadIdx.x;
   const int64_t bg = blockIdx.x;
-  const float* ml = a.part_ml + bg * a.total_slots * 2;
-  const float* po = a.part_o + bg * a.total_slots * D;
+  const int S = a.total_slots;
+  const float* ml = a.part_ml + bg * S * 2;
+  const float* po = a.part_o + bg * S * D;
+
+  // global max over splits: lanes own splits
   float mx = NEG_INF;
-  for (int s = 0; s < a.total_slots; ++s) mx = fmaxf(mx, ml[2 * s]);
+  for (int s = lane; s < S; s += 64) mx = fmaxf(mx, ml[2 * s]);
+  mx = wave_max_scalar(mx);
+
   float x[CPL];
 #pragma unroll
   for (int j = 0; j < CPL; ++j) x[j] = 0.f;
   if (mx != NEG_INF) {
-    float l = 0.f;
-    for (int s = 0; s < a.total_slots; ++s) {
-      const float ms = ml[2 * s];
-      if (ms == NEG_INF) continue;
-      const float wgt = __builtin_amdgcn_exp2f(ms - mx);
-      l = fmaf(wgt, ml[2 * s + 1], l);
+    float lpart = 0.f;
+    for (int s0 = 0; s0 < S; s0 += 256) {
+      const int n = min(256, S - s0);
+      __syncthreads();
+      for (int s = lane; s < n; s += 64) {
+        const float ms = ml[2 * (s0 + s)];
+        const float w = ms == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(ms - mx);
+        wsh[s] = w;
+        lpart = fmaf(w, ml[2 * (s0 + s) + 1], lpart);
+      }
+      __syncthreads();
+      const float* pc = po + static_cast<int64_t>(s0) * D + CPL * lane;
+      int s = 0;
+      for (; s + 8 <= n; s += 8) {
+        float v[8][CPL];
 #pragma unroll
-      for (int j = 0; j < CPL; ++j) x[j] = fmaf(wgt, po[static_cast<int64_t>(s) * D + CPL * lane + j], x[j]);
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int j = 0; j < CPL; ++j) v[u][j] = pc[static_cast<int64_t>(s + u) * D + j];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int j = 0; j < CPL; ++j) x[j] = fmaf(wsh[s + u], v[u][j], x[j]);
+      }
+      for (; s < n; ++s)
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) x[j] = fmaf(wsh[s], pc[static_cast<int64_t>(s) * D + j], x[j]);
     }
-    const float inv = 1.f / l;
+    const float inv = 1.f / wave_sum_scalar(lpart);
 #pragma unroll
     for (int j = 0; j < CPL; ++j) x[j] *= inv;
   }
@@ -738,8 +812,11 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(MergeArgs a, float rs_
     }
   }
   float* out = a.out + bg * D + CPL * lane;
-#pragma unroll
-  for (int j = 0; j < CPL; ++j) out[j] = x[j] * rs_n;
+  if constexpr (CPL == 2) {
+    *reinterpret_cast<float2*>(out) = make_float2(x[0] * rs_n, x[1] * rs_n);
+  } else {
+    out[0] = x[0] * rs_n;
+  }
 }
 
 template <int KB, int VB, int D>
@@ -773,7 +850,33 @@ hipError_t dispatch_k(const DecodeArgs& a, int kbits, int vbits, int n_splits, i
   }
 }
 
+template <int KB, int D>
+int waves_v(int vbits) {
+  switch (vbits) {
+    case 2: return PartialWaves<KB, 2, D>::value;
+    case 3: return PartialWaves<KB, 3, D>::value;
+    case 4: return PartialWaves<KB, 4, D>::value;
+    case 8: return PartialWaves<KB, 8, D>::value;
+    default: return PartialWaves<KB, 16, D>::value;
+  }
+}
+
+template <int D>
+int waves_k(int kbits, int vbits) {
+  switch (kbits) {
+    case 2: return waves_v<2, D>(vbits);
+    case 3: return waves_v<3, D>(vbits);
+    case 4: return waves_v<4, D>(vbits);
+    case 8: return waves_v<8, D>(vbits);
+    default: return waves_v<16, D>(vbits);
+  }
+}
+
 }  // namespace
+
+int decode_partial_waves_per_simd(int kbits, int vbits, int d) {
+  return d == 64 ? waves_k<64>(kbits, vbits) : waves_k<128>(kbits, vbits);
+}
 
 hipError_t launch_decode_partial(const DecodeArgs& a, int kbits, int vbits, int d, int n_splits,
                                  int batch, hipStream_t s) {

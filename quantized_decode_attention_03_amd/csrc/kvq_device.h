@@ -82,24 +82,30 @@ __device__ __forceinline__ float dpp_or(float old, float v) {
                                                                CTRL, ROWMASK, 0xf, false));
 }
 
+// old == src for max: lanes with no DPP source keep their own value, which lets
+// the compiler fold each step into one v_max_f32 with a DPP operand.
 __device__ __forceinline__ float wave_max_scalar(float x) {
-  const float ninf = -__builtin_huge_valf();
-  x = fmaxf(x, dpp_or<kDppRowShr1, 0xf>(ninf, x));
-  x = fmaxf(x, dpp_or<kDppRowShr2, 0xf>(ninf, x));
-  x = fmaxf(x, dpp_or<kDppRowShr4, 0xf>(ninf, x));
-  x = fmaxf(x, dpp_or<kDppRowShr8, 0xf>(ninf, x));
-  x = fmaxf(x, dpp_or<kDppRowBcast15, 0xa>(ninf, x));
-  x = fmaxf(x, dpp_or<kDppRowBcast31, 0xc>(ninf, x));
+  x = fmaxf(x, dpp_or<kDppRowShr1, 0xf>(x, x));
+  x = fmaxf(x, dpp_or<kDppRowShr2, 0xf>(x, x));
+  x = fmaxf(x, dpp_or<kDppRowShr4, 0xf>(x, x));
+  x = fmaxf(x, dpp_or<kDppRowShr8, 0xf>(x, x));
+  x = fmaxf(x, dpp_or<kDppRowBcast15, 0xa>(x, x));
+  x = fmaxf(x, dpp_or<kDppRowBcast31, 0xc>(x, x));
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
 }
 
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ float dpp_zero(float v) {  // lanes with no source read 0
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWMASK, 0xf, true));
+}
+
 __device__ __forceinline__ float wave_sum_scalar(float x) {
-  x += dpp_or<kDppRowShr1, 0xf>(0.f, x);
-  x += dpp_or<kDppRowShr2, 0xf>(0.f, x);
-  x += dpp_or<kDppRowShr4, 0xf>(0.f, x);
-  x += dpp_or<kDppRowShr8, 0xf>(0.f, x);
-  x += dpp_or<kDppRowBcast15, 0xa>(0.f, x);
-  x += dpp_or<kDppRowBcast31, 0xc>(0.f, x);
+  x += dpp_zero<kDppRowShr1, 0xf>(x);
+  x += dpp_zero<kDppRowShr2, 0xf>(x);
+  x += dpp_zero<kDppRowShr4, 0xf>(x);
+  x += dpp_zero<kDppRowShr8, 0xf>(x);
+  x += dpp_zero<kDppRowBcast15, 0xa>(x);
+  x += dpp_zero<kDppRowBcast31, 0xc>(x);
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
 }
 

@@ -81,6 +81,21 @@ struct SplitPlan {
   int n_splits;
 };
 
+// Compute units of the current device (0 if no device is visible), read once.
+int device_cus() {
+  static const int cus = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    return n;
+  }();
+  return cus;
+}
+
+// Splits sized so one resident round of waves covers the segment: as many
+// splits per (sequence, KV head) as the GPU holds waves of this kernel at
+// once, balanced, each a multiple of four pages (one group) and at least two
+// groups so the per-split prologue and partial write amortise.
 SplitPlan plan_splits(const kvq_segment& s, int batch) {
   const int pages = (std::max(s.max_len, 0) + KVQ_BLOCK_TOKENS - 1) / KVQ_BLOCK_TOKENS;
   SplitPlan p{4, 0};
@@ -88,13 +103,16 @@ SplitPlan plan_splits(const kvq_segment& s, int batch) {
   int pps = 0;
   if (const char* env = std::getenv("KVQ_SPLIT_PAGES")) pps = std::atoi(env);
   if (pps <= 0) {
-    // Enough waves to fill 256 CUs several times over, but at least 16 pages
-    // (4 groups) per wave so the prologue and the partial write amortise.
-    const int64_t units = static_cast<int64_t>(batch) * s.layout->num_kv_heads;
-    const int64_t target_waves = 4096;
-    const int64_t want_splits = std::max<int64_t>(1, (target_waves + units - 1) / units);
+    const kvq_layout& L = *s.layout;
+    int waves = 3;
+    for (int h = 0; h < L.num_kv_heads; ++h)
+      waves = std::min(waves, kvq::decode_partial_waves_per_simd(L.bits_k[h], L.bits_v[h], L.head_dim));
+    const int cus = device_cus() > 0 ? device_cus() : 256;
+    const int64_t capacity = static_cast<int64_t>(waves) * 4 * cus;
+    const int64_t units = static_cast<int64_t>(batch) * L.num_kv_heads;
+    const int64_t want_splits = std::max<int64_t>(1, capacity / units);
     pps = static_cast<int>((pages + want_splits - 1) / want_splits);
-    pps = std::max(pps, 16);
+    pps = std::max(pps, 8);
   }
   pps = (pps + 3) / 4 * 4;
   p.pages_per_split = pps;

@@ -75,4 +75,7 @@ hipError_t launch_decode_partial(const DecodeArgs& a, int kbits, int vbits, int 
                                  int batch, hipStream_t s);
 hipError_t launch_decode_merge(const MergeArgs& a, hipStream_t s);
 
+// Waves per SIMD the partial kernel for (kbits, vbits, d) is compiled to hold.
+int decode_partial_waves_per_simd(int kbits, int vbits, int d);
+
 }  // namespace kvq
