@@ -579,21 +579,38 @@ void decode_partial_kernel(DecodeArgs a, float qscale) {
 
   const uint8_t* pool = a.pool;
   const int32_t* trow = a.table + static_cast<int64_t>(b) * a.table_stride;
-  // the first two groups' loads go out before the query is prepared
+  // The query loads go out first (straight-line, no lane-dependent branch),
+  // then the first two groups' loads, so that preparing the query waits only
+  // for the query.
+  constexpr int QPL = 4 * D / 64;  // query values per lane (4 head rows)
+  // Both element types are read as 16-bit halves (upper half at byte esz - 2,
+  // lower half at byte 0; for bf16 both read the element itself), so the loads
+  // are the same instructions whatever the type.
+  uint32_t qhi[QPL], qlo[QPL];
+  {
+    const int64_t qrow0 = static_cast<int64_t>(b) * hq + h * G;
+    const int esz = a.q_bf16 ? 2 : 4;
+    const uint8_t* qp = static_cast<const uint8_t*>(a.q);
+#pragma unroll
+    for (int k = 0; k < QPL; ++k) {
+      const int e = lane + 64 * k, r = min(e / D, G - 1);
+      const uint8_t* el = qp + ((qrow0 + r) * D + e % D) * esz;
+      qhi[k] = *reinterpret_cast<const uint16_t*>(el + esz - 2);
+      qlo[k] = *reinterpret_cast<const uint16_t*>(el);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep the query loads ahead of the group loads
   GroupRaw<KB, VB, D> ga, gb, gc;
   load_group<KB, VB, D>(a, pool, trow, p0, p1, seq_len, koff, voff, lane, ga);
   load_group<KB, VB, D>(a, pool, trow, p0 + 4, p1, seq_len, koff, voff, lane, gb);
+  __builtin_amdgcn_sched_barrier(0);
 
   // ---- q' = R q for the G query heads of this KV head (LDS butterflies) ----
-  for (int e = lane; e < 4 * D; e += 64) {
-    const int r = e / D, ch = e % D;
-    float v = 0.f;
-    if (r < G) {
-      const int64_t qi = (static_cast<int64_t>(b) * hq + h * G + r) * D + ch;
-      v = a.q_bf16 ? bf16lo_to_f(static_cast<const uint16_t*>(a.q)[qi])
-                   : static_cast<const float*>(a.q)[qi];
-    }
-    qs[r][ch] = v;
+#pragma unroll
+  for (int k = 0; k < QPL; ++k) {
+    const int e = lane + 64 * k, r = e / D;
+    const float qf = bits_f(qhi[k] << 16 | (a.q_bf16 ? 0u : qlo[k]));
+    qs[r][e % D] = r < G ? qf : 0.f;
   }
   if (lane < 8) wzero[lane] = 0;
   __syncthreads();
@@ -688,20 +705,24 @@ void decode_partial_kernel(DecodeArgs a, float qscale) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) { st.m_run[i] = -1e30f; st.l_part[i] = 0.f; st.mn_part[i] = 0.f; }
 
-  // three rotating buffers: while group g is computed, g+1 and g+2 are in flight
-  for (int grp = p0; grp < p1;) {
+  // Three rotating buffers: while group g is computed, g+1 and g+2 are in
+  // flight. The loop runs whole trips of three groups and has a single exit at
+  // its bottom, so the loads in flight at the back edge are the same at every
+  // trip; the last one or two groups (already loaded) are computed after it.
+  const int n_groups = (p1 - p0 + 3) / 4;
+  int grp = p0;
+  for (int trip = n_groups / 3; trip > 0; --trip) {
     load_group<KB, VB, D>(a, pool, trow, grp + 8, p1, seq_len, koff, voff, lane, gc);
     compute_group<KB, VB, D>(ga, qa, biasq, q2, inv_qsc, G, lane, bias, wt, wzero, st);
-    grp += 4;
-    if (grp >= p1) break;
-    load_group<KB, VB, D>(a, pool, trow, grp + 8, p1, seq_len, koff, voff, lane, ga);
+    load_group<KB, VB, D>(a, pool, trow, grp + 12, p1, seq_len, koff, voff, lane, ga);
     compute_group<KB, VB, D>(gb, qa, biasq, q2, inv_qsc, G, lane, bias, wt, wzero, st);
-    grp += 4;
-    if (grp >= p1) break;
-    load_group<KB, VB, D>(a, pool, trow, grp + 8, p1, seq_len, koff, voff, lane, gb);
+    load_group<KB, VB, D>(a, pool, trow, grp + 16, p1, seq_len, koff, voff, lane, gb);
     compute_group<KB, VB, D>(gc, qa, biasq, q2, inv_qsc, G, lane, bias, wt, wzero, st);
-    grp += 4;
+    grp += 12;
   }
+  const int rest = n_groups % 3;
+  if (rest >= 1) compute_group<KB, VB, D>(ga, qa, biasq, q2, inv_qsc, G, lane, bias, wt, wzero, st);
+  if (rest >= 2) compute_group<KB, VB, D>(gb, qa, biasq, q2, inv_qsc, G, lane, bias, wt, wzero, st);
 
   // ---- epilogue: combine hi/lo rows, add the min term, write the partials ----
   float lsum[4], mnsum[4];
