@@ -119,7 +119,7 @@ def main():
         layers.append({"pool": pool, "table": table, "seg": seg, "q": q, "new_k": new_k, "new_v": new_v})
     torch.cuda.synchronize()
 
-    ws = torch.empty(kvq.kvq_decode_workspace_bytes(layers[0]["seg"], B), dtype=torch.uint8, device=dev)
+    ws = kvq.decode_workspace(layers[0]["seg"], B, dev)
     out = torch.empty((B, HKV * G, D), dtype=torch.float32, device=dev)
     calls = []
     for ly in layers:

@@ -193,10 +193,21 @@ kvq_status kvq_dequant(const kvq_layout* L, const void* pool, int64_t pool_block
 
 /*
  * Host. Bytes of device workspace kvq_decode_attn needs for these segments
- * and batch size (split-K partials: max, sum and o' per query head and split).
+ * and batch size: the split-K partials (max, sum and o' per query head and
+ * split) and two work-sharing counters per (segment, sequence, KV head).
  */
 kvq_status kvq_decode_workspace_bytes(const kvq_segment* segs, int32_t n_segs,
                                       int32_t batch, size_t* bytes);
+
+/*
+ * Device, async. Zeroes a decode workspace (ws_bytes bytes, a multiple of 4,
+ * 4-byte aligned). Required once on a new workspace before its first decode
+ * call, and again after a decode call that failed on the device; every
+ * completed decode call leaves the counters zero, so a workspace is reused
+ * without it. Launches a kernel (no memset), so it may be graph-captured.
+ * Errors: KVQ_ERR_ARG (null or misaligned), KVQ_ERR_DEVICE.
+ */
+kvq_status kvq_decode_workspace_init(void* ws, size_t ws_bytes, kvq_stream stream);
 
 /*
  * Device, async. Fused quantized decode attention, one query per q-head:
@@ -209,8 +220,10 @@ kvq_status kvq_decode_workspace_bytes(const kvq_segment* segs, int32_t n_segs,
  * A sequence with no tokens in any segment gets a zero output row.
  * In:  q device [batch][Hkv*G][head_dim] of q_dtype.
  * Out: out device float [batch][Hkv*G][head_dim].
- * ws: device workspace of at least kvq_decode_workspace_bytes bytes (its
- * contents on entry do not matter).
+ * ws: device workspace of at least kvq_decode_workspace_bytes bytes, zeroed
+ * once by kvq_decode_workspace_init before its first use. The waves of one
+ * (sequence, KV head) share its pages through counters in ws, so two calls
+ * in flight at once must not share a workspace.
  * Errors: KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE, KVQ_ERR_DEVICE.
  */
 kvq_status kvq_decode_attn(const kvq_segment* segs, int32_t n_segs, int32_t batch,

@@ -21,6 +21,11 @@ LIB = os.path.join(PKG, "libkvq.so")
 
 SOURCES = ["kvq_host.cpp", "kvq_append.hip", "kvq_decode.hip"]
 
+# The decode kernel's work-sharing fetch is one lane's atomic whose result is
+# read a whole page group later; the compiler's atomic rewrite (a wave
+# reduction around the atomic) would read it at once and stall on it.
+SOURCE_FLAGS = {"kvq_decode.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
+
 # Packed FP32 instructions stay off in all device code.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -35,7 +40,8 @@ def hipcc():
 
 def _compile(src):
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + HIP_FLAGS + ["-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = ([hipcc()] + HIP_FLAGS + SOURCE_FLAGS.get(src, []) +
+           ["-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj])
     if src.endswith(".cpp"):
         cmd.insert(1, "-x")
         cmd.insert(2, "hip")

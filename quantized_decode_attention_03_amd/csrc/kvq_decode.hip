@@ -24,14 +24,19 @@
 //    w = p * scale are split into fp16 hi/lo halves and transposed through
 //    LDS into the A operand of the PV product.
 //  * PV on the matrix cores: v_mfma_f32_16x16x32_f16, A = weights (hi rows
-//    0..G-1, lo rows 4..4+G-1), B = value codes centred and made exact in
-//    fp16, 32 tokens per instruction. The min term sum_t p_t (mn_t + 2^(b-1) s_t)
-//    is accumulated per head on the vector ALU and added at the end.
+//    0..G-1, lo rows 4..4+G-1), B = value codes as exact fp16 numbers
+//    1024 + sigma*c (one v_and_or_b32 per pair), centred exactly by one
+//    packed fp16 add, 32 tokens per instruction. (Leaving the offset in and
+//    removing it with a second MFMA against a constant costs the same time and
+//    loses precision: the matrix core rounds sums carrying 1024 * sum(w).) The
+//    min term sum_t p_t (mn_t + 2^(b-1) s_t) is accumulated per head on the
+//    vector ALU and added at the end.
 // Each split writes (running max, sum of p, o') to the workspace; a second
 // kernel merges the splits of all segments and applies R^T.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
+#include <algorithm>
 #include <cmath>
 
 namespace kvq {
@@ -252,6 +257,18 @@ template <int VB, int D> struct VFmt {
     else if constexpr (VB == 3) return 128.f;
     else return 1.f;
   }
+  // Centring: one packed fp16 add of -(1024 + 2^(b-1) sigma_c) per pair turns
+  // 1024 + sigma_c c into the exact centred value sigma_c (c - 2^(b-1)), so
+  // the accumulator carries sigma_c * sum_t w_t (c_t - 2^(b-1)) and no offset.
+  // Chunks with equal sigma share one constant (a class).
+  __device__ static constexpr int cls(int c) {
+    return VB == 4 ? (c & 1) : VB == 2 ? (D == 128 ? (c < 5 ? c : c - 5) : c) : 0;
+  }
+  static constexpr uint32_t center_bits(int k) {  // fp16 pair of -(1024 + 2^(b-1) sigma)
+    const int sg = VB == 4 ? (k ? 16 : 1) : VB == 2 ? (1 << (2 * k)) : VB == 3 ? 128 : 1;
+    const uint32_t h = 0xe400u | static_cast<uint32_t>((1 << (VB - 1)) * sg);
+    return h | (h << 16);
+  }
 };
 
 // Produce the B operand (4 dwords = 8 tokens) of value chunk c for one lane.
@@ -274,10 +291,8 @@ __device__ __forceinline__ u32x4_t v_operand(const uint32_t (&raw)[8][VRaw<VB, D
       const int cc = D == 128 ? (c & 3) : c;
       if (cc >= 2) x >>= 8;
       const uint32_t mask = (cc & 1) ? 0x00f000f0u : 0x000f000fu;
-      const float sg = (cc & 1) ? 16.f : 1.f;
       out = and_or(x, mask, bias);
-      const _Float16 off = static_cast<_Float16>(-(1024.f + 8.f * sg));
-      out = pk_add_h(out, half_bits(off) * 0x10001u);
+      out = pk_add_h(out, VFmt<VB, D>::center_bits(VFmt<VB, D>::cls(c)));
     } else if constexpr (VB == 2) {
       uint32_t x;
       int cc;
@@ -291,16 +306,13 @@ __device__ __forceinline__ u32x4_t v_operand(const uint32_t (&raw)[8][VRaw<VB, D
         cc = c;
       }
       out = and_or(x, 0x00030003u << (2 * cc), bias);
-      const float sg = static_cast<float>(1 << (2 * cc));
-      const _Float16 off = static_cast<_Float16>(-(1024.f + 2.f * sg));
-      out = pk_add_h(out, half_bits(off) * 0x10001u);
+      out = pk_add_h(out, VFmt<VB, D>::center_bits(VFmt<VB, D>::cls(c)));
     } else if constexpr (VB == 8) {
       const int word = D == 128 ? (c >> 2) : 0;
       const uint32_t k = c & 3;
       const uint32_t x = perm_b32(b[word], a[word], 0x0c000c00u | ((4 + k) << 16) | k);
       out = x | bias;
-      const _Float16 off = static_cast<_Float16>(-(1024.f + 128.f));
-      out = pk_add_h(out, half_bits(off) * 0x10001u);
+      out = pk_add_h(out, VFmt<VB, D>::center_bits(0));
     } else if constexpr (VB == 3) {
       constexpr int bpl = 3 * D / 16;  // 24 or 12 bits per lane
       const uint32_t sh = (bpl * n) & 31;
@@ -308,8 +320,7 @@ __device__ __forceinline__ u32x4_t v_operand(const uint32_t (&raw)[8][VRaw<VB, D
       const uint32_t wb = __builtin_amdgcn_alignbit(b[1], b[0], sh);
       const uint32_t ca = (wa >> (3 * c)) & 7u, cb = (wb >> (3 * c)) & 7u;
       out = (((cb << 16) | ca) << 7) | bias;
-      const _Float16 off = static_cast<_Float16>(-(1024.f + 4.f * 128.f));
-      out = pk_add_h(out, half_bits(off) * 0x10001u);
+      out = pk_add_h(out, VFmt<VB, D>::center_bits(0));
     } else {  // bf16 values: channel n*D/16 + c is half (c & 1) of word c/2
       const int word = c >> 1;
       out = perm_b32(b[word], a[word], (c & 1) ? 0x07060302u : 0x05040100u);
@@ -335,6 +346,7 @@ struct GroupRaw {
   float ks, kmn, vs, vmn;                      // metadata of this lane's token
   bool valid;                                  // this lane's token is a cached token
   uint32_t vmask;                              // bit 8*pp2+e: value token e of pair pp2 is cached
+  int gid;                                     // group index in the unit (>= unit groups: none)
 };
 
 // Running max of the scores may grow by up to this much (log2 units) before the
@@ -346,6 +358,14 @@ constexpr float kRescaleSlack = 4.f;
 // static and the wait before a group's compute leaves the next group's loads
 // outstanding. Each load instruction reads one page, so its base address is
 // wave-uniform and the per-lane part is a loop-invariant offset.
+constexpr int kXcds = 8;  // accelerator dies of the chip; workgroups go round-robin over them
+#ifndef KVQ_TUNE_STATIC_EIGHTHS
+#define KVQ_TUNE_STATIC_EIGHTHS 2
+#endif
+// Share of a unit's groups dealt out in fixed order before the shared tail
+// (measured: 2/8 beats 0, 4/8 and 6/8 at the 32k Llama-shaped decode).
+constexpr int kStaticEighths = KVQ_TUNE_STATIC_EIGHTHS;
+
 template <int KB, int VB, int D>
 __device__ __forceinline__ void load_group(const DecodeArgs& a, const uint8_t* pool, const int32_t* trow, int grp,
                                            int p1, int seq_len, int64_t koff, int64_t voff, int lane,
@@ -354,11 +374,13 @@ __device__ __forceinline__ void load_group(const DecodeArgs& a, const uint8_t* p
   const int tslot = lane & 15, g4 = lane >> 4;
   int64_t boff[4];
   uint32_t pv = 0;  // bit pp: page grp + pp is mapped
+  // (32-bit compare: table entries are int32; a negative entry wraps above any bound)
+  const uint32_t nblk = a.pool_blocks > 0x7fffffff ? 0x80000000u : static_cast<uint32_t>(a.pool_blocks);
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp) {
     const int page = grp + pp;
-    const int64_t blk = trow[min(page, p1 - 1)];
-    const bool ok = page < p1 && blk >= 0 && blk < a.pool_blocks;
+    const int32_t blk = trow[max(min(page, p1 - 1), 0)];
+    const bool ok = page < p1 && static_cast<uint32_t>(blk) < nblk;
     pv |= static_cast<uint32_t>(ok) << pp;
     boff[pp] = ok ? blk * a.block_bytes : 0;
   }
@@ -397,14 +419,29 @@ __device__ __forceinline__ void load_group(const DecodeArgs& a, const uint8_t* p
   }
 }
 
-// Waves per SIMD each instance is compiled for: its working set (three group
-// buffers in flight) fits 256 registers at head_dim 128, 168 for most
-// head_dim 64 formats; bf16 segments take a whole SIMD.
+// Group buffers in flight while one is computed (prefetch depth) and waves
+// per SIMD each instance is compiled for.
+#ifndef KVQ_TUNE_DEPTH
+#define KVQ_TUNE_DEPTH 2
+#endif
+#ifndef KVQ_TUNE_WAVES128
+#define KVQ_TUNE_WAVES128 2
+#endif
+template <int KB, int VB, int D>
+struct PrefetchDepth {
+  static constexpr int value = KVQ_TUNE_DEPTH;
+};
+
+// The wide formats (8- and 16-bit keys, bf16 values, and the 3/8-bit values
+// beside 4-bit keys at head_dim 128, 16-bit keys beside 3- or 16-bit values at
+// head_dim 64) need more than half the register file: one wave per SIMD. The
+// choice is checked by compiling every instance and requiring zero spills.
 template <int KB, int VB, int D>
 struct PartialWaves {
-  static constexpr int value =
-      D == 64 ? ((VB == 3 || VB == 16 || KB == 3 || KB == 8 || KB == 16) ? 2 : 3)
-              : (VB == 16 || KB == 16 || KB == 8) ? 1 : 2;
+  static constexpr bool wide =
+      D == 128 ? (VB == 16 || KB == 16 || KB == 8 || (KB == 4 && (VB == 3 || VB == 8)))
+               : (KB == 16 && (VB == 3 || VB == 16));
+  static constexpr int value = wide ? 1 : (D == 128 ? KVQ_TUNE_WAVES128 : 2);
 };
 
 template <int KB, int VB, int D>
@@ -416,10 +453,10 @@ struct SplitState {
 };
 
 template <int KB, int VB, int D>
-__device__ __forceinline__ void compute_group(GroupRaw<KB, VB, D>& g, const uint4 (*qa)[2][64], const float (&biasq)[4],
-                                              const float (&q2)[4], float inv_qsc, int G, int lane, uint32_t bias,
-                                              uint16_t (*wt)[4][64], const uint16_t* wzero,
-                                              SplitState<KB, VB, D>& st) {
+__device__ __forceinline__ void compute_group(GroupRaw<KB, VB, D>& g, const u32x4_t (&qf)[D / 32][2],
+                                              const float (&biasq)[4], const float (&q2)[4], float inv_qsc, int G,
+                                              int lane, uint32_t bias, uint16_t (*wt)[4][64],
+                                              const uint16_t* wzero, SplitState<KB, VB, D>& st) {
   using KF = KFmt<KB, D>;
   using VF = VFmt<VB, D>;
   constexpr int NCK = D / 32, NCV = D / 16;
@@ -427,15 +464,14 @@ __device__ __forceinline__ void compute_group(GroupRaw<KB, VB, D>& g, const uint
   constexpr float NEG_INF = -__builtin_huge_valf();
   const int row = lane & 15, g4 = lane >> 4;
 
-  // QK: one 16x16 tile per page (rows = query heads, columns = tokens). The
-  // query fragments come from LDS once per chunk and feed all four pages.
+  // QK: one 16x16 tile per page (rows = query heads, columns = tokens). Each
+  // chunk's query fragments (hi, lo) feed all four pages.
   float4_t cq[4];
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp) cq[pp] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < NCK; ++c) {
-    const uint4 h4 = qa[c][0][lane], l4 = qa[c][1][lane];
-    const u32x4_t ah = u32x4_t{h4.x, h4.y, h4.z, h4.w}, al = u32x4_t{l4.x, l4.y, l4.z, l4.w};
+    const u32x4_t ah = qf[c][0], al = qf[c][1];
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) {
       const u32x4_t bk = KF::unpack(g.k[pp], c, bias);
@@ -465,8 +501,7 @@ __device__ __forceinline__ void compute_group(GroupRaw<KB, VB, D>& g, const uint
   for (int i = 0; i < 4; ++i) over = over || z[i] > st.m_run[i] + kRescaleSlack;
   if (__builtin_expect(__builtin_amdgcn_ballot_w64(over) != 0, 0)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (i >= G) break;
+    for (int i = 0; i < 4; ++i) {  // (heads i >= G have z = -inf: never raised)
       const float gm = wave_max_scalar(z[i]);
       if (gm > st.m_run[i] + kRescaleSlack) {
         const float alpha = __builtin_amdgcn_exp2f(st.m_run[i] - gm);
@@ -481,8 +516,7 @@ __device__ __forceinline__ void compute_group(GroupRaw<KB, VB, D>& g, const uint
   const float vs_eff = VMETA ? (g.valid ? g.vs : 0.f) : 1.f;
   const float vmid_eff = VMETA ? (g.valid ? g.vmn + static_cast<float>(1 << (VB - 1)) * g.vs : 0.f) : 0.f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (i >= G) break;
+  for (int i = 0; i < 4; ++i) {  // all four rows, branch-free: heads i >= G get p = 0
     const float p = __builtin_amdgcn_exp2f(z[i] - st.m_run[i]);  // masked: exp2(-inf) = 0
     st.l_part[i] += p;
     float w = p;
@@ -538,7 +572,10 @@ __device__ __forceinline__ void compute_group(GroupRaw<KB, VB, D>& g, const uint
 template <int KB, int VB, int D>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PartialWaves<KB, VB, D>::value,
                                                                     PartialWaves<KB, VB, D>::value)))
-void decode_partial_kernel(DecodeArgs a, float qscale) {
+void decode_partial_kernel(DecodeArgs a, const int32_t* __restrict__ table, uint32_t* __restrict__ steal,
+                           float qscale) {
+  // (table and counters as separate restrict arguments: the counters' atomics
+  // cannot alias the block table, so its entries stay scalar loads)
   using KF = KFmt<KB, D>;
   using VF = VFmt<VB, D>;
   constexpr int NCK = D / 32;               // QK chunks (32 channels each)
@@ -551,34 +588,44 @@ void decode_partial_kernel(DecodeArgs a, float qscale) {
   __shared__ __attribute__((aligned(16))) uint16_t wzero[8];
 
   const int lane = threadIdx.x;
-  const int split = blockIdx.x;
-  const int hidx = blockIdx.y;
-  const int b = blockIdx.z;
+  // One-dimensional grid of U units x W splits (W a multiple of the XCD
+  // count). Workgroup L runs on XCD x = L % 8 as that XCD's m-th workgroup,
+  // m = L / 8, and serves unit m % U as its split x + 8 * (m / U). So every
+  // unit has waves on all eight XCDs and from early and late in each XCD's
+  // dispatch order (of two waves on a SIMD the first dispatched is issued
+  // first); sharing the tail then evens the units out.
+  const int U = a.n_heads * a.batch;
+  const int m = static_cast<int>(blockIdx.x) / kXcds;
+  const int unit = m % U;
+  const int split = static_cast<int>(blockIdx.x) % kXcds + kXcds * (m / U);
+  const int hidx = unit % a.n_heads;
+  const int b = unit / a.n_heads;
   const int h = a.heads[hidx];
   const int G = a.group;
   const int hq = a.hkv * G;
   const int64_t koff = a.k_off[hidx], voff = a.v_off[hidx];
   const int seq_len = a.seq_lens[b];
   const int pages = min((seq_len + kBlockTokens - 1) / kBlockTokens, a.table_stride);
-  const int p0 = split * a.pages_per_split;
-  const int p1 = min(p0 + a.pages_per_split, pages);
   const int slot = a.slot_base + split;
 
-  if (p0 >= p1) {
-    for (int r = 0; r < G; ++r) {
-      const int64_t bg = static_cast<int64_t>(b) * hq + h * G + r;
-      float* po = a.part_o + (bg * a.total_slots + slot) * D;
-      for (int j = lane; j < D; j += 64) po[j] = 0.f;
-      if (lane == 0) {
-        a.part_ml[(bg * a.total_slots + slot) * 2] = NEG_INF;
-        a.part_ml[(bg * a.total_slots + slot) * 2 + 1] = 0.f;
-      }
-    }
-    return;
-  }
-
+  // Work sharing inside the unit (sequence b, KV head h), whose W waves each
+  // write one partial. The unit's NG groups of four pages: wave w first takes
+  // the SG groups [w*SG, (w+1)*SG) (a quarter of the unit, in order), then
+  // groups of the shared tail [W*SG, NG), one at a time, from a counter in the
+  // workspace. Wave speeds differ by tens of percent (the older of two waves
+  // on a SIMD is issued first; some dies run slower); fast waves take more of
+  // the tail, so the unit's waves finish within about a group of each other.
+  // The last wave of the unit to finish resets the counters to zero.
+  // Without sharing (deterministic order) wave w takes [w*SG, (w+1)*SG) with
+  // SG = ceil(NG / W) and there is no tail.
+  const int W = static_cast<int>(gridDim.x) / U;
+  const int NG = (pages + 3) / 4;
+  const int SG = a.share_tail ? (NG * kStaticEighths / 8) / W : (NG + W - 1) / W;
+  const int pool0 = min(SG * W, NG);
+  const uint32_t pool_groups = static_cast<uint32_t>(NG - pool0);
+  uint32_t* const ctr = steal + 2 * (static_cast<int64_t>(b) * a.hkv + h);
   const uint8_t* pool = a.pool;
-  const int32_t* trow = a.table + static_cast<int64_t>(b) * a.table_stride;
+  const int32_t* trow = table + static_cast<int64_t>(b) * a.table_stride;
   // The query loads go out first (straight-line, no lane-dependent branch),
   // then the first two groups' loads, so that preparing the query waits only
   // for the query.
@@ -600,9 +647,42 @@ void decode_partial_kernel(DecodeArgs a, float qscale) {
     }
   }
   __builtin_amdgcn_sched_barrier(0);  // keep the query loads ahead of the group loads
-  GroupRaw<KB, VB, D> ga, gb, gc;
-  load_group<KB, VB, D>(a, pool, trow, p0, p1, seq_len, koff, voff, lane, ga);
-  load_group<KB, VB, D>(a, pool, trow, p0 + 4, p1, seq_len, koff, voff, lane, gb);
+  constexpr int DEPTH = PrefetchDepth<KB, VB, D>::value;
+  constexpr int NB = DEPTH + 1;  // group buffers
+  GroupRaw<KB, VB, D> gbuf[NB];
+  // The wave's groups in order ("positions"): its static groups, then tail
+  // groups. A tail fetch is issued one position ahead of its use (when the
+  // previous position is loaded), so its latency hides behind a group.
+  int lpos = 0;                          // next position to load
+  uint32_t inflight = 0;                 // lane 0: the outstanding tail fetch
+  bool exhausted = pool_groups == 0;     // the tail is used up: no further fetches
+  auto fetch = [&]() {
+    uint32_t v = 0;
+    if (lane == 0) v = atomicAdd(ctr, 1u);
+    inflight = v;
+  };
+  if (SG == 0 && !exhausted) fetch();
+  auto load_next = [&](GroupRaw<KB, VB, D>& g) {
+    int gid = NG;
+    if (lpos < SG) {
+      gid = min(split * SG + lpos, NG);
+      if (lpos == SG - 1 && !exhausted) fetch();
+    } else if (!exhausted) {
+      const uint32_t idx = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(inflight)));
+      if (idx < pool_groups) {
+        gid = pool0 + static_cast<int>(idx);
+        fetch();
+      } else {
+        exhausted = true;
+      }
+    }
+    ++lpos;
+    gid = __builtin_amdgcn_readfirstlane(gid);  // wave-uniform: page addresses stay scalar
+    g.gid = gid;
+    load_group<KB, VB, D>(a, pool, trow, 4 * gid, pages, seq_len, koff, voff, lane, g);
+  };
+#pragma unroll
+  for (int j = 0; j < DEPTH; ++j) load_next(gbuf[j]);
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- q' = R q for the G query heads of this KV head (LDS butterflies) ----
@@ -705,24 +785,55 @@ void decode_partial_kernel(DecodeArgs a, float qscale) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) { st.m_run[i] = -1e30f; st.l_part[i] = 0.f; st.mn_part[i] = 0.f; }
 
-  // Three rotating buffers: while group g is computed, g+1 and g+2 are in
-  // flight. The loop runs whole trips of three groups and has a single exit at
-  // its bottom, so the loads in flight at the back edge are the same at every
-  // trip; the last one or two groups (already loaded) are computed after it.
-  const int n_groups = (p1 - p0 + 3) / 4;
-  int grp = p0;
-  for (int trip = n_groups / 3; trip > 0; --trip) {
-    load_group<KB, VB, D>(a, pool, trow, grp + 8, p1, seq_len, koff, voff, lane, gc);
-    compute_group<KB, VB, D>(ga, qa, biasq, q2, inv_qsc, G, lane, bias, wt, wzero, st);
-    load_group<KB, VB, D>(a, pool, trow, grp + 12, p1, seq_len, koff, voff, lane, ga);
-    compute_group<KB, VB, D>(gb, qa, biasq, q2, inv_qsc, G, lane, bias, wt, wzero, st);
-    load_group<KB, VB, D>(a, pool, trow, grp + 16, p1, seq_len, koff, voff, lane, gb);
-    compute_group<KB, VB, D>(gc, qa, biasq, q2, inv_qsc, G, lane, bias, wt, wzero, st);
-    grp += 12;
+  // Query fragments: held in registers when the register budget allows, else
+  // re-read from LDS before each group. The estimate counts the three group
+  // buffers, the fragments and the PV accumulators against the 256
+  // architectural registers, leaving room for the rest of the loop.
+  constexpr int GROUP_WORDS = 4 * KF::kWords + 16 * VRaw<VB, D>::kWords + 4;
+  constexpr bool QF_REGS = 3 * GROUP_WORDS + 8 * NCK + 4 * NCV <= 180;
+  u32x4_t qreg[NCK][2];
+  if constexpr (QF_REGS) {
+#pragma unroll
+    for (int c = 0; c < NCK; ++c)
+#pragma unroll
+      for (int l = 0; l < 2; ++l) {
+        const uint4 v = qa[c][l][lane];
+        qreg[c][l] = u32x4_t{v.x, v.y, v.z, v.w};
+      }
   }
-  const int rest = n_groups % 3;
-  if (rest >= 1) compute_group<KB, VB, D>(ga, qa, biasq, q2, inv_qsc, G, lane, bias, wt, wzero, st);
-  if (rest >= 2) compute_group<KB, VB, D>(gb, qa, biasq, q2, inv_qsc, G, lane, bias, wt, wzero, st);
+  auto compute = [&](GroupRaw<KB, VB, D>& g) {
+    if constexpr (QF_REGS) {
+      compute_group<KB, VB, D>(g, qreg, biasq, q2, inv_qsc, G, lane, bias, wt, wzero, st);
+    } else {
+      u32x4_t qf[NCK][2];
+#pragma unroll
+      for (int c = 0; c < NCK; ++c)
+#pragma unroll
+        for (int l = 0; l < 2; ++l) {
+          const uint4 v = qa[c][l][lane];
+          qf[c][l] = u32x4_t{v.x, v.y, v.z, v.w};
+        }
+      compute_group<KB, VB, D>(g, qf, biasq, q2, inv_qsc, G, lane, bias, wt, wzero, st);
+    }
+  };
+
+  // Rotating group buffers: while position i is computed, positions
+  // i+1 .. i+DEPTH are in flight. Each trip covers NB positions, unrolled so
+  // that every buffer index is static; positions past the wave's last group
+  // are skipped (loads of such positions read masked pages). The loop has a
+  // single exit at its bottom, taken when the next trip's first position has
+  // no group, so the loads in flight at the back edge are the same at every
+  // trip.
+  if (gbuf[0].gid < NG) {
+    for (;;) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        load_next(gbuf[(j + DEPTH) % NB]);
+        if (gbuf[j].gid < NG) compute(gbuf[j]);
+      }
+      if (gbuf[0].gid >= NG) break;
+    }
+  }
 
   // ---- epilogue: combine hi/lo rows, add the min term, write the partials ----
   float lsum[4], mnsum[4];
@@ -757,6 +868,15 @@ void decode_partial_kernel(DecodeArgs a, float qscale) {
         ml[0] = lsum[i] > 0.f ? st.m_run[i] : NEG_INF;
         ml[1] = lsum[i];
       }
+    }
+  }
+  // Every tail fetch of this wave has returned (the last one found the tail
+  // used up). The wave that completes the unit resets both counters.
+  if (pool_groups != 0 && lane == 0) {
+    const uint32_t done = atomicAdd(ctr + 1, 1u);
+    if (done == static_cast<uint32_t>(W - 1)) {
+      atomicExch(ctr, 0u);
+      atomicExch(ctr + 1, 0u);
     }
   }
 }
@@ -842,8 +962,9 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(MergeArgs a, float rs_
 
 template <int KB, int VB, int D>
 hipError_t launch_partial_t(const DecodeArgs& a, int n_splits, int batch, float qscale, hipStream_t s) {
-  dim3 grid(n_splits, a.n_heads, batch);
-  hipLaunchKernelGGL((decode_partial_kernel<KB, VB, D>), grid, dim3(64), 0, s, a, qscale);
+  if (a.batch != batch || n_splits % kXcds != 0) return hipErrorInvalidValue;
+  dim3 grid(static_cast<unsigned>(n_splits) * a.n_heads * batch);
+  hipLaunchKernelGGL((decode_partial_kernel<KB, VB, D>), grid, dim3(64), 0, s, a, a.table, a.steal, qscale);
   return hipGetLastError();
 }
 
@@ -916,6 +1037,19 @@ hipError_t launch_decode_merge(const MergeArgs& a, hipStream_t s) {
   if (a.d == 128) hipLaunchKernelGGL((decode_merge_kernel<128>), grid, dim3(64), 0, s, a, rs);
   else if (a.d == 64) hipLaunchKernelGGL((decode_merge_kernel<64>), grid, dim3(64), 0, s, a, rs);
   else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+
+namespace {
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, size_t n) {
+  for (size_t i = blockIdx.x * 256ull + threadIdx.x; i < n; i += 256ull * gridDim.x) p[i] = 0u;
+}
+}  // namespace
+
+hipError_t launch_zero_words(uint32_t* p, size_t n_words, hipStream_t s) {
+  const size_t blocks = std::min<size_t>((n_words + 255) / 256, 4096);
+  hipLaunchKernelGGL(zero_words_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p, n_words);
   return hipGetLastError();
 }
 

@@ -75,7 +75,18 @@ kvq_status check_layout_ready(const kvq_layout* L, const char* who) {
   return KVQ_OK;
 }
 
-// Split plan of one segment: pages per split (a multiple of 4) and split count.
+// KVQ_DECODE_DETERMINISTIC=1 fixes which wave computes which pages, so the
+// result is bitwise reproducible; by default three quarters of each unit's
+// pages go to whichever of its waves is free first (faster, last-bit
+// differences between runs).
+bool deterministic_order() {
+  const char* env = std::getenv("KVQ_DECODE_DETERMINISTIC");
+  return env && env[0] && env[0] != '0';
+}
+
+// Split plan of one segment: nominal pages per split (a multiple of 4) and
+// the number of waves (splits) per (sequence, KV head). The kernel shares a
+// unit's pages among its waves itself; the nominal size only sets the count.
 struct SplitPlan {
   int pages_per_split;
   int n_splits;
@@ -116,7 +127,9 @@ SplitPlan plan_splits(const kvq_segment& s, int batch) {
   }
   pps = (pps + 3) / 4 * 4;
   p.pages_per_split = pps;
-  p.n_splits = (pages + pps - 1) / pps;
+  // a multiple of the eight XCDs: the kernel spreads each unit's waves evenly
+  // over them
+  p.n_splits = ((pages + pps - 1) / pps + 7) / 8 * 8;
   return p;
 }
 
@@ -156,9 +169,15 @@ int total_slots(const kvq_segment* segs, int n_segs, int batch, std::vector<Spli
   return total;
 }
 
-size_t workspace_bytes(int batch, int hq, int d, int slots) {
+// Workspace: partial o' [batch][hq][slots][d], partial (max, sum)
+// [batch][hq][slots][2], then the work-sharing counters
+// [n_segs][batch][hkv][2] (uint32, zero between calls).
+size_t partials_bytes(int batch, int hq, int d, int slots) {
   if (slots == 0) slots = 1;
   return static_cast<size_t>(batch) * hq * slots * (static_cast<size_t>(d) + 2) * sizeof(float);
+}
+size_t workspace_bytes(int batch, int hq, int hkv, int d, int slots, int n_segs) {
+  return partials_bytes(batch, hq, d, slots) + static_cast<size_t>(n_segs) * batch * hkv * 2 * sizeof(uint32_t);
 }
 
 }  // namespace
@@ -399,8 +418,19 @@ kvq_status kvq_decode_workspace_bytes(const kvq_segment* segs, int32_t n_segs, i
   kvq_status st = check_segments(segs, n_segs, batch, "kvq_decode_workspace_bytes");
   if (st != KVQ_OK) return st;
   const kvq_layout& L = *segs[0].layout;
-  *bytes = workspace_bytes(batch, L.num_kv_heads * L.group, L.head_dim, total_slots(segs, n_segs, batch, nullptr));
+  *bytes = workspace_bytes(batch, L.num_kv_heads * L.group, L.num_kv_heads, L.head_dim,
+                           total_slots(segs, n_segs, batch, nullptr), n_segs);
   return ok();
+}
+
+kvq_status kvq_decode_workspace_init(void* ws, size_t ws_bytes, kvq_stream stream) {
+  if (ws_bytes == 0) return ok();
+  if (!ws) return fail(KVQ_ERR_ARG, "kvq_decode_workspace_init: null workspace");
+  if (ws_bytes % 4 != 0 || reinterpret_cast<uintptr_t>(ws) % 4 != 0)
+    return fail(KVQ_ERR_ARG, "kvq_decode_workspace_init: workspace not 4-byte aligned and sized");
+  return device_status(kvq::launch_zero_words(static_cast<uint32_t*>(ws), ws_bytes / 4,
+                                              reinterpret_cast<hipStream_t>(stream)),
+                       "kvq_decode_workspace_init launch");
 }
 
 kvq_status kvq_decode_partial(const kvq_segment* segs, int32_t n_segs, int32_t batch, const void* q,
@@ -414,11 +444,13 @@ kvq_status kvq_decode_partial(const kvq_segment* segs, int32_t n_segs, int32_t b
   const int hq = L0.num_kv_heads * L0.group;
   std::vector<SplitPlan> plans;
   const int slots = total_slots(segs, n_segs, batch, &plans);
-  const size_t need = workspace_bytes(batch, hq, L0.head_dim, slots);
+  const size_t need = workspace_bytes(batch, hq, L0.num_kv_heads, L0.head_dim, slots, n_segs);
   if (ws_bytes < need)
     return fail(KVQ_ERR_WORKSPACE, "kvq_decode_partial: workspace %zu < %zu bytes", ws_bytes, need);
   float* part_o = static_cast<float*>(ws);
   float* part_ml = part_o + static_cast<size_t>(batch) * hq * std::max(slots, 1) * L0.head_dim;
+  uint32_t* steal = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) +
+                                                partials_bytes(batch, hq, L0.head_dim, slots));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   int slot_base = 0;
   for (int i = 0; i < n_segs; ++i) {
@@ -441,7 +473,9 @@ kvq_status kvq_decode_partial(const kvq_segment* segs, int32_t n_segs, int32_t b
         a.hkv = L.num_kv_heads;
         a.group = L.group;
         a.had_block = L.had_block;
-        a.pages_per_split = p.pages_per_split;
+        a.batch = batch;
+        a.steal = steal + static_cast<size_t>(i) * batch * L.num_kv_heads * 2;
+        a.share_tail = deterministic_order() ? 0 : 1;
         a.slot_base = slot_base;
         a.total_slots = slots;
         a.part_o = part_o;
@@ -473,14 +507,14 @@ kvq_status kvq_decode_merge(const kvq_segment* segs, int32_t n_segs, int32_t bat
   const kvq_layout& L0 = *segs[0].layout;
   const int hq = L0.num_kv_heads * L0.group;
   const int slots = total_slots(segs, n_segs, batch, nullptr);
-  const size_t need = workspace_bytes(batch, hq, L0.head_dim, slots);
+  const size_t need = workspace_bytes(batch, hq, L0.num_kv_heads, L0.head_dim, slots, n_segs);
   if (ws_bytes < need) return fail(KVQ_ERR_WORKSPACE, "kvq_decode_merge: workspace %zu < %zu bytes", ws_bytes, need);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   // With no split at all the merge kernel still runs and writes zero rows
   // (no memset node, so the call stays safe to capture in a graph).
   kvq::MergeArgs a{};
   a.part_o = static_cast<const float*>(ws);
-  a.part_ml = a.part_o + static_cast<size_t>(batch) * hq * slots * L0.head_dim;
+  a.part_ml = a.part_o + static_cast<size_t>(batch) * hq * std::max(slots, 1) * L0.head_dim;
   a.batch = batch;
   a.hq = hq;
   a.d = L0.head_dim;

@@ -50,9 +50,11 @@ struct DecodeArgs {
   const void* q;       // [batch][hkv*group][d]
   int32_t q_bf16;
   int32_t hkv, group, had_block;
-  int32_t pages_per_split;
+  int32_t batch;       // sequences (the grid covers batch x n_heads units)
   int32_t slot_base;   // first split slot of this segment
   int32_t total_slots; // split slots over all segments
+  uint32_t* steal;     // [batch][hkv][2] work-sharing counters of this segment (zero between calls)
+  int32_t share_tail;  // 1: most of each unit's groups go to whichever wave is free; 0: fixed order
   int32_t n_heads;
   int32_t heads[KVQ_MAX_KV_HEADS];
   int64_t k_off[KVQ_MAX_KV_HEADS];
@@ -74,6 +76,7 @@ hipError_t launch_dequant(const DequantArgs& a, hipStream_t s);
 hipError_t launch_decode_partial(const DecodeArgs& a, int kbits, int vbits, int d, int n_splits,
                                  int batch, hipStream_t s);
 hipError_t launch_decode_merge(const MergeArgs& a, hipStream_t s);
+hipError_t launch_zero_words(uint32_t* p, size_t n_words, hipStream_t s);
 
 // Waves per SIMD the partial kernel for (kbits, vbits, d) is compiled to hold.
 int decode_partial_waves_per_simd(int kbits, int vbits, int d);

@@ -24,7 +24,8 @@ KVQ_F32, KVQ_BF16 = 0, 1
 EXPORTED = [
     "kvq_abi_version", "kvq_status_str", "kvq_last_error", "kvq_layout_init", "kvq_plan_bits",
     "kvq_logquant_classes", "kvq_page_alloc", "kvq_quantize_append", "kvq_dequant",
-    "kvq_decode_workspace_bytes", "kvq_decode_attn", "kvq_decode_partial", "kvq_decode_merge",
+    "kvq_decode_workspace_bytes", "kvq_decode_workspace_init", "kvq_decode_attn", "kvq_decode_partial",
+    "kvq_decode_merge",
 ]
 
 
@@ -86,6 +87,7 @@ def lib():
                                       ctypes.c_int, vp]
     L.kvq_dequant.argtypes = [ctypes.POINTER(KvqLayout), vp, i64, vp, i32, i32, i32, i32, i32, vp, vp, vp]
     L.kvq_decode_workspace_bytes.argtypes = [ctypes.POINTER(KvqSegment), i32, i32, ctypes.POINTER(sz)]
+    L.kvq_decode_workspace_init.argtypes = [vp, sz, vp]
     L.kvq_decode_attn.argtypes = [ctypes.POINTER(KvqSegment), i32, i32, vp, ctypes.c_int, vp, vp, sz, vp]
     L.kvq_decode_partial.argtypes = [ctypes.POINTER(KvqSegment), i32, i32, vp, ctypes.c_int, vp, sz, vp]
     L.kvq_decode_merge.argtypes = [ctypes.POINTER(KvqSegment), i32, i32, vp, vp, sz, vp]
@@ -265,12 +267,26 @@ def _segments(segments):
     return arr
 
 
-def _decode_common(segments, q, ws):
+def kvq_decode_workspace_init(ws, stream=None):
+    """Zero a decode workspace (uint8 device tensor) on the stream; needed once before first use."""
     import torch
+    _check(lib().kvq_decode_workspace_init(_dev_ptr(ws, (torch.uint8,), "ws"), ws.numel(), _stream(stream)),
+           "kvq_decode_workspace_init")
+
+
+def decode_workspace(segments, batch, device, stream=None):
+    """Allocate a decode workspace for these segments and batch, initialised for use."""
+    import torch
+    ws = torch.empty(kvq_decode_workspace_bytes(segments, batch), dtype=torch.uint8, device=device)
+    kvq_decode_workspace_init(ws, stream)
+    return ws
+
+
+def _decode_common(segments, q, ws):
     batch = int(q.shape[0])
     need = kvq_decode_workspace_bytes(segments, batch)
     if ws is None:
-        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws = decode_workspace(segments, batch, q.device)
     if ws.numel() * ws.element_size() < need:
         raise ValueError("workspace too small")
     return batch, ws

@@ -264,7 +264,9 @@ def test_decode_three_precision_segments():
 # Invariants of the HIP path itself
 # ---------------------------------------------------------------------------
 
-def test_decode_invariant_to_page_placement_bitwise():
+def test_decode_invariant_to_page_placement_bitwise(monkeypatch):
+    # fixed page-to-wave order: the result is a function of the cached rows only
+    monkeypatch.setenv("KVQ_DECODE_DETERMINISTIC", "1")
     lens = [333, 1000]
     L, lay, cache, ref, table, k, v = build_case(128, 128, 4, [4, 4], [4, 4], lens, seed=31)
     # same data, different physical blocks (a different free-list permutation)
@@ -314,14 +316,43 @@ def test_decode_zero_query_gives_mean_value():
         assert T.rel(o[0, g], mean[g // 4]) < 1e-5
 
 
-def test_decode_partial_then_merge_equals_one_call():
+def test_decode_partial_then_merge_equals_one_call(monkeypatch):
+    monkeypatch.setenv("KVQ_DECODE_DETERMINISTIC", "1")
     lens = [700, 90]
     L, lay, cache, ref, table, k, v = build_case(64, 64, 4, [4, 4], [2, 2], lens, seed=39)
     q = torch.randn((2, 8, 64), device=T.DEV).bfloat16()
     seg = [cache.segment(lens)]
     o1 = kvq.kvq_decode_attn(seg, q)
-    ws = torch.empty(kvq.kvq_decode_workspace_bytes(seg, 2), dtype=torch.uint8, device=T.DEV)
+    ws = kvq.decode_workspace(seg, 2, T.DEV)
     o2 = torch.empty_like(o1)
     kvq.kvq_decode_partial(seg, q, ws)
     kvq.kvq_decode_merge(seg, 2, o2, ws)
     assert torch.equal(o1, o2)
+
+
+def test_decode_work_sharing_matches_fixed_order_and_oracle(monkeypatch):
+    # Many waves per (sequence, KV head) so the shared tail is exercised, with
+    # ragged lengths (one sequence shorter than a split) and repeated calls on
+    # one workspace (the counters must come back to zero after every call).
+    lens = [3000, 37, 1601]
+    L, lay, cache, ref, table, k, v = build_case(128, 128, 4, [4, 4], [4, 4], lens, seed=41)
+    q = torch.from_numpy(synth.bf16_round(np.random.default_rng(42).standard_normal((3, 8, 128)).astype(np.float32))).to(T.DEV).bfloat16()
+    expect = O.decode_attention([(lay, ref, table, np.array(lens))], q.float().cpu().numpy().astype(np.float64))
+    seg = [cache.segment(lens)]
+    ws = kvq.decode_workspace(seg, 3, T.DEV)
+    monkeypatch.setenv("KVQ_SPLIT_PAGES", "8")
+    outs = []
+    for _ in range(3):
+        o = torch.empty((3, 8, 128), dtype=torch.float32, device=T.DEV)
+        kvq.kvq_decode_partial(seg, q, ws)
+        kvq.kvq_decode_merge(seg, 3, o, ws)
+        outs.append(o.cpu().numpy())
+    monkeypatch.setenv("KVQ_DECODE_DETERMINISTIC", "1")
+    fixed = kvq.kvq_decode_attn(seg, q).cpu().numpy()
+    for o in outs:
+        assert T.max_rel_err(o, expect) <= T.ATTN_TOL
+        assert T.rel(o, fixed) < 1e-5
+    # the counters (the workspace's last words) are zero again
+    n_cnt = 3 * 2 * 2
+    tail = ws[-4 * n_cnt:].view(torch.int32).cpu().numpy()
+    assert np.all(tail == 0)

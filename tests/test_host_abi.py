@@ -153,6 +153,13 @@ def test_decode_argument_checks_need_no_device():
     n = ctypes.c_size_t(0)
     assert lib.kvq_decode_workspace_bytes(segs, 1, 16, ctypes.byref(n)) == kvq.KVQ_OK
     assert n.value > 16 * 32 * 130 * 4
+    # partials for every split slot, then two counters per (sequence, KV head)
+    assert (n.value - 16 * 8 * 2 * 4) % (16 * 32 * 130 * 4) == 0
+    # workspace initialisation: null or misaligned
+    assert lib.kvq_decode_workspace_init(None, 64, None) == kvq.KVQ_ERR_ARG
+    assert lib.kvq_decode_workspace_init(ctypes.c_void_p(0x4002), 64, None) == kvq.KVQ_ERR_ARG
+    assert lib.kvq_decode_workspace_init(ctypes.c_void_p(0x4000), 62, None) == kvq.KVQ_ERR_ARG
+    assert lib.kvq_decode_workspace_init(None, 0, None) == kvq.KVQ_OK
     # workspace too small
     st = lib.kvq_decode_attn(segs, 1, 16, ctypes.c_void_p(0x4000), kvq.KVQ_BF16, ctypes.c_void_p(0x5000),
                              ctypes.c_void_p(0x6000), 16, None)
