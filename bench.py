@@ -15,18 +15,35 @@ resident in HBM when timing starts.
 Prints one JSON line. `roofline` is for the dominant kernel (the split-K
 partial decode kernel): algorithmic bytes per launch over its average
 duration from HIP events recorded around each launch on the launch stream.
-`cpu_baseline` times the CPU oracle on a bounded sample of the same step.
+`roofline.traffic` is the kernel's measured HBM bytes per launch from two
+rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE), each scaled by what the same
+counter reads for a 1 GiB device copy; it is read from the committed summary
+under profiles/ and reported only while the kernel source still has the hash
+recorded there (else null). `cpu_baseline` times the CPU oracle on a bounded
+sample of the same step.
+
+    python bench.py [--steps K] [--warmup W] [--layers L] [--cpu-units U]
+    python bench.py --summarize-pmc FETCH_CSV WRITE_CSV   # writes the traffic summary to stdout
+    python bench.py --summarize-trace KERNEL_TRACE_CSV    # per-kernel durations of a kernel trace
 """
 
 import argparse
+import csv
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+DECODE_SRC = os.path.join(ROOT, "quantized_decode_attention_03_amd", "csrc", "kvq_decode.hip")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_partial_k4v4_d128_b16_ctx32k_traffic.md")
+PARTIAL_KERNEL = "decode_partial_kernel<4, 4, 128>"
+COPY_BYTES = 1 << 30
 
 B, T, HKV, G, D, HAD = 16, 32768, 8, 4, 128, 128
 BITS_K, BITS_V = 4, 4
@@ -35,6 +52,79 @@ SEED_BASE = 2000
 
 WORKLOAD = ("llama3-8b-shaped decode: 32 layers, batch 16, ctx 32768, 8 kv heads x 4 q heads, "
             "head_dim 128, K4/V4 token-wise INT4, hadamard 128, 16-token pages, permuted page table")
+
+
+def source_hash():
+    with open(DECODE_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """Bytes per launch of the partial kernel from the committed counter summary, if current."""
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            text = f.read()
+    except OSError:
+        return None
+    fields = dict(line.split(": ", 1) for line in text.splitlines() if line.startswith("- ") and ": " in line)
+    if fields.get("- kernel source sha256/16") != source_hash():
+        return None
+    return int(fields["- traffic bytes per launch"])
+
+
+def _pmc_rows(path, counter):
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def summarize_pmc(fetch_csv, write_csv):
+    """Traffic summary from a FETCH_SIZE pass and a WRITE_SIZE pass (KiB per dispatch)."""
+    out = []
+    factors, per_launch = {}, {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _pmc_rows(path, counter)
+        copy = max(v for k, v in rows if "copyBuffer" in k or "copy" in k.lower())
+        factors[counter] = COPY_BYTES / (copy * 1024.0)
+        part = [v for k, v in rows if PARTIAL_KERNEL in k]
+        per_launch[counter] = float(np.mean(part)) * 1024.0 * factors[counter]
+        out.append(f"- {counter} of the 1 GiB copy (KiB): {copy:.0f}")
+        out.append(f"- {counter} scale factor: {factors[counter]:.4f}")
+        out.append(f"- {counter} partial-kernel launches: {len(part)}, mean KiB {np.mean(part):.0f}, "
+                   f"scaled bytes {per_launch[counter]:.0f}")
+    traffic = per_launch["FETCH_SIZE"] + per_launch["WRITE_SIZE"]
+    out.append(f"- kernel source sha256/16: {source_hash()}")
+    out.append(f"- algorithmic bytes per launch: {bytes_per_layer()}")
+    out.append(f"- traffic bytes per launch: {traffic:.0f}")
+    out.append(f"- traffic / algorithmic: {traffic / bytes_per_layer():.4f}")
+    return "\n".join(out) + "\n"
+
+
+def summarize_trace(trace_csv):
+    """Per-kernel durations of the library's kernels from a rocprofv3 kernel trace.
+
+    Launches are grouped by kernel and grid size, so the prefill appends (one
+    token per lane group, 32768 tokens) and the per-step appends (one token)
+    are told apart.
+    """
+    groups = {}
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"]
+            if "kvq::" not in name:
+                continue
+            m = re.search(r"(\w+_kernel(<[^>]*>)?)", name)
+            short = m.group(1) if m else name
+            key = (short, int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]))
+            groups.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    out = ["| kernel | grid threads | launches | mean us | min us | max us |", "|---|---|---|---|---|---|"]
+    for (short, grid), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        d = np.asarray(d) / 1e3
+        out.append(f"| {short} | {grid} | {len(d)} | {d.mean():.2f} | {d.min():.2f} | {d.max():.2f} |")
+    return "\n".join(out) + "\n"
 
 
 def bytes_per_layer():
@@ -80,10 +170,20 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=LAYERS)
-    ap.add_argument("--cpu-units", type=int, default=16, help="oracle units timed for cpu_baseline (0: skip)")
+    ap.add_argument("--cpu-units", type=int, default=48, help="oracle units timed for cpu_baseline (0: skip)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run one 1 GiB device copy (for scaling HBM counters)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print the traffic summary of two counter passes and exit")
+    ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
+                    help="print per-kernel durations from a rocprofv3 kernel trace and exit")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        sys.stdout.write(summarize_pmc(*args.summarize_pmc))
+        return
+    if args.summarize_trace:
+        sys.stdout.write(summarize_trace(args.summarize_trace))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(this build runs on a single MI355X)", file=sys.stderr)
@@ -159,7 +259,7 @@ def main():
     step_bytes = layer_bytes * args.layers
 
     if args.copy_calib:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
@@ -184,7 +284,7 @@ def main():
         "config": {"workload": WORKLOAD, "layers": args.layers, "batch": B, "ctx": T, "kv_heads": HKV,
                    "q_per_kv": G, "head_dim": D, "bits_k": BITS_K, "bits_v": BITS_V, "had_block": HAD},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "kernel": "decode_partial_kernel<4,4,128>", "avg_us": round(part_us, 3),
                      "bytes_per_launch": layer_bytes},
         "step_hbm_gbs": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
