@@ -1,0 +1,192 @@
+"""Parity at the full sizes of the five workloads, on sampled outputs.
+
+Each test fills the whole cache on the GPU through the C ABI and decodes it
+in the launch configuration the benchmark times (default split planner, work
+sharing on). The oracle then rebuilds, from the same input tensors, the cache
+of a few sampled (sequence, KV head) units (a one-head layout with that
+head's bits) and computes their attention. Compared:
+- the GPU output rows of those units against the oracle (max relative error
+  per output vector at most 2e-3);
+- a sample of stored code rows and metadata of those units against the
+  oracle's rows (identical except codes off by one at rounding ties, at a
+  rate of at most 1e-5).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import kvq_oracle as O
+from quantized_decode_attention_03_amd import kvq, synth
+from tests import kvq_testlib as T
+
+pytestmark = pytest.mark.gpu
+
+TIE_RATE = 1e-5
+ROW_SAMPLE = 512
+
+
+def device_rows(pool, block_bytes, table_np, seq, positions, area_off, d, bits):
+    """Stored bytes (and meta) of the given tokens of one head area, gathered on the device."""
+    rb = d * bits // 8
+    pos = np.asarray(positions)
+    blk = torch.from_numpy(table_np[seq, pos // 16].astype(np.int64)).to(pool.device)
+    slot = torch.from_numpy(pos % 16).to(pool.device)
+    cols = area_off + slot[:, None] * rb + torch.arange(rb, device=pool.device)[None, :]
+    rows = pool[blk[:, None], cols].cpu().numpy()
+    meta = None
+    if bits != 16:
+        mcols = area_off + 16 * rb + slot[:, None] * 8 + torch.arange(8, device=pool.device)[None, :]
+        meta = pool[blk[:, None], mcols].cpu().numpy().copy().view(np.float32).reshape(-1, 2)
+    return rows, meta
+
+
+def oracle_unit(k_rows, v_rows, q_rows, bk, bv, n):
+    """The oracle's cache and attention for one (sequence, KV head) unit.
+
+    k_rows, v_rows: [T, d] float32 (bf16 values); q_rows: [G, d]."""
+    t, d = k_rows.shape
+    g = q_rows.shape[0]
+    lay = O.Layout(1, g, d, n, [bk], [bv])
+    pages = -(-t // 16)
+    table = np.arange(pages, dtype=np.int32)[None]
+    pool = np.zeros((pages, lay.block_bytes), np.uint8)
+    O.quantize_append(lay, pool, table, np.array([0]), k_rows[None, :, None, :], v_rows[None, :, None, :])
+    return lay, pool, table
+
+
+def check_unit_rows(L, gpu_pool, gpu_table, b, h, lay, ref_pool, ref_table, k_rows, v_rows, positions, stats):
+    d, n = L.head_dim, L.had_block
+    for x, bits, goff, roff in ((k_rows, L.bits_k[h], L.k_off[h], lay.k_off[0]),
+                                (v_rows, L.bits_v[h], L.v_off[h], lay.v_off[0])):
+        g_rows, g_meta = device_rows(gpu_pool, L.block_bytes, gpu_table, b, positions, goff, d, bits)
+        r_rows, r_meta = T.gather_rows(ref_pool, lay.block_bytes, ref_table, 0, positions, roff, d, bits)
+        T.compare_rows(g_rows, g_meta, r_rows, r_meta, O.rotate(x[positions], n), bits, d, stats)
+
+
+def full_cache(L, batch, tokens, k, v, seed):
+    """Pool and permuted page table for `batch` sequences of `tokens`, filled in one append."""
+    pages = -(-tokens // 16)
+    n_blocks = batch * pages
+    table = np.full((batch, pages), -1, np.int32)
+    kvq.kvq_page_alloc(synth.free_list(n_blocks, seed), 0, np.zeros(batch, np.int32),
+                       np.full(batch, tokens, np.int32), table)
+    pool = torch.empty((n_blocks, L.block_bytes), dtype=torch.uint8, device=T.DEV)
+    table_t = torch.from_numpy(table).to(T.DEV)
+    kvq.kvq_quantize_append(L, pool, table_t, torch.zeros(batch, dtype=torch.int32, device=T.DEV), k, v)
+    return pool, table, table_t
+
+
+def decode_units(L, pool, table_t, batch, tokens, q):
+    lens = torch.full((batch,), tokens, dtype=torch.int32, device=T.DEV)
+    return kvq.kvq_decode_attn([kvq.Segment(L, pool, table_t, lens, tokens)], q).cpu().numpy()
+
+
+def run_units(L, pool, table, out, k, v, q, units, seed):
+    """Oracle comparison for the sampled units; returns the code statistics."""
+    g, n = L.group, L.had_block
+    rng = np.random.default_rng(seed)
+    stats = T.CodeStats()
+    tokens = k.shape[1]
+    for b, h in units:
+        k_rows = k[b, :, h].float().cpu().numpy()
+        v_rows = v[b, :, h].float().cpu().numpy()
+        q_rows = q[b, h * g:(h + 1) * g].float().cpu().numpy()
+        lay, ref_pool, ref_table = oracle_unit(k_rows, v_rows, q_rows, L.bits_k[h], L.bits_v[h], n)
+        expect = O.decode_attention([(lay, ref_pool, ref_table, np.array([tokens]))],
+                                    q_rows[None].astype(np.float64))[0]
+        err = T.max_rel_err(out[b, h * g:(h + 1) * g], expect)
+        assert err <= T.ATTN_TOL, f"unit (b={b}, h={h}): max relative error {err:.3e}"
+        positions = np.sort(rng.choice(tokens, size=min(ROW_SAMPLE, tokens), replace=False))
+        check_unit_rows(L, pool, table, b, h, lay, ref_pool, ref_table, k_rows, v_rows, positions, stats)
+    assert stats.rate <= TIE_RATE
+    return stats
+
+
+def test_llama_32k_decode_full_size():
+    """Batch 16, 32768 tokens, 8 KV heads x 4, head_dim 128, K4/V4, Hadamard 128 (one layer)."""
+    batch, tokens, hkv, group, d = 16, 32768, 8, 4, 128
+    L = kvq.kvq_layout_init(hkv, group, d, 128, [4] * hkv, [4] * hkv)
+    k, v, q = synth.llama_layer_torch(2000, batch, tokens, hkv, group, d, device=T.DEV)
+    pool, table, table_t = full_cache(L, batch, tokens, k, v, seed=2000)
+    out = decode_units(L, pool, table_t, batch, tokens, q)
+    assert np.all(np.isfinite(out))
+    run_units(L, pool, table, out, k, v, q, [(0, 0), (7, 3), (15, 7), (9, 5)], seed=1)
+
+
+def test_mixed_precision_32k_decode_full_size():
+    """Batch 8, 32768 tokens, per-head bits from kvq_plan_bits (average 3, ladder {2,3,4,8})."""
+    batch, tokens, hkv, group, d, layers = 8, 32768, 8, 4, 128, 32
+    ladder = [2, 3, 4, 8]
+    w_k = synth.sensitivities(layers, hkv, seed=3).ravel()
+    w_v = synth.sensitivities(layers, hkv, seed=33).ravel()
+    budget = 3 * layers * hkv
+    bits_k = kvq.kvq_plan_bits(w_k, 1.0, 3.6, ladder, budget)[0].reshape(layers, hkv)
+    bits_v = kvq.kvq_plan_bits(w_v, 1.0, 5.3, ladder, budget)[0].reshape(layers, hkv)
+    ref_k, left_k = O.plan_bits_greedy(w_k.astype(np.float32), 1.0, 3.6, ladder, budget)
+    assert left_k == 0 and np.array_equal(bits_k.ravel(), np.asarray(ref_k))
+    # the layer with the most distinct (K, V) bit pairs
+    pairs = [len({(int(a), int(c)) for a, c in zip(bits_k[l], bits_v[l])}) for l in range(layers)]
+    layer = int(np.argmax(pairs))
+    bk, bv = [int(x) for x in bits_k[layer]], [int(x) for x in bits_v[layer]]
+    L = kvq.kvq_layout_init(hkv, group, d, 128, bk, bv)
+    k, v, q = synth.llama_layer_torch(3000 + layer, batch, tokens, hkv, group, d, device=T.DEV)
+    pool, table, table_t = full_cache(L, batch, tokens, k, v, seed=3000 + layer)
+    out = decode_units(L, pool, table_t, batch, tokens, q)
+    assert np.all(np.isfinite(out))
+    # one unit per distinct bit pair, spread over the batch
+    seen, units = set(), []
+    for h in range(hkv):
+        if (bk[h], bv[h]) not in seen:
+            seen.add((bk[h], bv[h]))
+            units.append((len(units) % batch, h))
+    run_units(L, pool, table, out, k, v, q, units, seed=2)
+
+
+def test_long_context_131k_three_segments_full_size():
+    """Batch 1, 131072 tokens, Hadamard 32: bf16 window of 128, log-spaced 4-bit subset, 2-bit rest."""
+    tokens, window, hkv, group, d = 131072, 128, 8, 4, 128
+    cls = kvq.kvq_logquant_classes(tokens, window)
+    assert np.array_equal(cls.astype(np.int32), O.logquant_precision_map(tokens, window))
+    counts = [int((cls == c).sum()) for c in range(3)]
+    assert counts == [128, 1280, 129664]
+    k, v, q = synth.llama_layer_torch(4, 1, tokens, hkv, group, d, device=T.DEV)
+    segs, keep = [], []
+    for c, bits in ((0, 16), (1, 4), (2, 2)):
+        idx = torch.from_numpy(np.flatnonzero(cls == c)).to(T.DEV)
+        L = kvq.kvq_layout_init(hkv, group, d, 32, [bits] * hkv, [bits] * hkv)
+        kk = k[:, idx].contiguous()
+        vv = v[:, idx].contiguous()
+        pool, table, table_t = full_cache(L, 1, counts[c], kk, vv, seed=40 + c)
+        lens = torch.full((1,), counts[c], dtype=torch.int32, device=T.DEV)
+        segs.append(kvq.Segment(L, pool, table_t, lens, counts[c]))
+        keep.append((L, pool, table, kk, vv))
+    out = kvq.kvq_decode_attn(segs, q).cpu().numpy()
+    assert np.all(np.isfinite(out))
+    for h in (0, 5):
+        q_rows = q[0, h * group:(h + 1) * group].float().cpu().numpy()
+        ref_segs = []
+        stats = T.CodeStats()
+        for c, (L, pool, table, kk, vv) in enumerate(keep):
+            k_rows = kk[0, :, h].float().cpu().numpy()
+            v_rows = vv[0, :, h].float().cpu().numpy()
+            lay, ref_pool, ref_table = oracle_unit(k_rows, v_rows, q_rows, L.bits_k[h], L.bits_v[h], 32)
+            ref_segs.append((lay, ref_pool, ref_table, np.array([counts[c]])))
+            positions = np.sort(np.random.default_rng(c).choice(counts[c], size=min(ROW_SAMPLE, counts[c]),
+                                                                replace=False))
+            check_unit_rows(L, pool, table, 0, h, lay, ref_pool, ref_table, k_rows, v_rows, positions, stats)
+        expect = O.decode_attention(ref_segs, q_rows[None].astype(np.float64))[0]
+        err = T.max_rel_err(out[0, h * group:(h + 1) * group], expect)
+        assert err <= T.ATTN_TOL, f"head {h}: max relative error {err:.3e}"
+        assert stats.rate <= TIE_RATE
+
+
+def test_bulk_append_16k_then_decode_full_size():
+    """Batch 4, 16384 new tokens in one append, K4/V2, Hadamard 128, then one decode over them."""
+    batch, tokens, hkv, group, d = 4, 16384, 8, 4, 128
+    L = kvq.kvq_layout_init(hkv, group, d, 128, [4] * hkv, [2] * hkv)
+    k, v, q = synth.llama_layer_torch(5, batch, tokens, hkv, group, d, device=T.DEV)
+    pool, table, table_t = full_cache(L, batch, tokens, k, v, seed=5)
+    out = decode_units(L, pool, table_t, batch, tokens, q)
+    assert np.all(np.isfinite(out))
+    run_units(L, pool, table, out, k, v, q, [(0, 0), (3, 6), (1, 3)], seed=3)
