@@ -16,7 +16,8 @@
 //    of this KV head (hi and lo fp16 halves of q', each its own MFMA, so the
 //    product carries ~22 bits of q) and B = the page's key codes, which the
 //    lanes turn into exact fp16 numbers 1024 + sigma*c with one v_and_or_b32
-//    per pair (the constant 1024*sum(q) is removed afterwards, exactly).
+//    per pair; 4-bit keys are centred to sigma*(c - 8) by one packed add, for
+//    the other widths the constant 1024*sum(q) is removed afterwards.
 //  * The four pages' score tiles are packed into one dense set of four
 //    registers (lane = token, register = query head) with
 //    v_permlane16_swap / v_permlane32_swap.
@@ -70,26 +71,34 @@ __device__ __forceinline__ uint32_t shl_signed(uint32_t w) {
 // product takes 8 of those channels as the lane's 8 K-slots. channel(c, e) is
 // the channel (relative to the quarter) in K-slot e of chunk c; sigma is the
 // power of two each code is scaled by inside its fp16 number 1024 + sigma*c.
+// base is the constant part of the B value (1024, or -kCentre*sigma for a
+// centred format), whose product with the query is removed per head.
 // ---------------------------------------------------------------------------
 template <int KB, int D> struct KFmt;
 
 template <int D> struct KFmt<4, D> {
   static constexpr int kWords = D / 32;  // quarter = D/8 bytes
   static constexpr bool bf16 = false;
+  // Centred: one packed add turns 1024 + sigma*c into sigma*(c - 8), so the
+  // products carry no 1024 offset (at sigma 1 that offset would be about 136x
+  // the signal and the matrix core's fp32 sums would lose ~7 bits to it).
+  static constexpr float kCentre = 8.f;
   // nibbles 0 and 2 sit at bits 0-3 of their half (sigma 1), nibbles 1 and 3 at
   // bits 4-7 (sigma 16); both reach their place with at most one shift
   __device__ static float sigma(int /*c*/, int e) { return (e & 2) ? 16.f : 1.f; }
+  __device__ static float base(int c, int e) { return -kCentre * sigma(c, e); }
   __device__ static int channel(int c, int e) {
     constexpr int rel[8] = {0, 4, 1, 5, 2, 6, 3, 7};
     return 8 * c + rel[e];
   }
   __device__ static u32x4_t unpack(const uint32_t (&w)[kWords], int c, uint32_t bias) {
     const uint32_t x = w[c], x8 = x >> 8;
+    constexpr uint32_t c1 = 0xe408e408u, c16 = 0xe480e480u;  // fp16 pairs -(1024 + 8), -(1024 + 128)
     u32x4_t r;
-    r[0] = and_or(x, 0x000f000fu, bias);
-    r[1] = and_or(x, 0x00f000f0u, bias);
-    r[2] = and_or(x8, 0x000f000fu, bias);
-    r[3] = and_or(x8, 0x00f000f0u, bias);
+    r[0] = pk_add_h(and_or(x, 0x000f000fu, bias), c1);
+    r[1] = pk_add_h(and_or(x, 0x00f000f0u, bias), c16);
+    r[2] = pk_add_h(and_or(x8, 0x000f000fu, bias), c1);
+    r[3] = pk_add_h(and_or(x8, 0x00f000f0u, bias), c16);
     return r;
   }
 };
@@ -98,6 +107,8 @@ template <int D> struct KFmt<2, D> {
   static constexpr int kWords = D / 64;  // quarter = D/16 bytes
   static constexpr bool bf16 = false;
   __device__ static float sigma(int, int) { return 256.f; }
+  static constexpr float kCentre = 0.f;
+  __device__ static float base(int, int) { return 1024.f; }
   __device__ static int channel(int c, int e) {
     const int m = c >> 1, k = 4 * (c & 1) + (e >> 1);
     return 16 * m + ((e & 1) ? 8 : 0) + k;
@@ -117,6 +128,8 @@ template <int D> struct KFmt<8, D> {
   static constexpr int kWords = D / 16;  // quarter = D/4 bytes
   static constexpr bool bf16 = false;
   __device__ static float sigma(int, int) { return 1.f; }
+  static constexpr float kCentre = 0.f;
+  __device__ static float base(int, int) { return 1024.f; }
   __device__ static int channel(int c, int e) {
     constexpr int rel[8] = {0, 2, 1, 3, 4, 6, 5, 7};
     return 8 * c + rel[e];
@@ -136,6 +149,8 @@ template <int D> struct KFmt<3, D> {
   static constexpr int kWords = (3 * D / 32 + 3) / 4;  // quarter = 3D/32 bytes (12 or 6)
   static constexpr bool bf16 = false;
   __device__ static float sigma(int, int) { return 128.f; }
+  static constexpr float kCentre = 0.f;
+  __device__ static float base(int, int) { return 1024.f; }
   __device__ static int channel(int c, int e) { return 8 * c + e; }
   template <int K>
   __device__ static uint32_t code(const uint32_t (&w)[kWords]) {
@@ -170,6 +185,8 @@ template <int D> struct KFmt<16, D> {
   static constexpr int kWords = D / 8;  // quarter = D/2 bytes of bf16
   static constexpr bool bf16 = true;
   __device__ static float sigma(int, int) { return 1.f; }
+  static constexpr float kCentre = 0.f;
+  __device__ static float base(int, int) { return 0.f; }
   __device__ static int channel(int c, int e) { return 8 * c + e; }
   __device__ static u32x4_t unpack(const uint32_t (&w)[kWords], int c, uint32_t) {
     u32x4_t r;
@@ -482,6 +499,8 @@ __device__ __forceinline__ void compute_group(GroupRaw<KB, VB, D>& g, const u32x
   // pack the four tiles: lane = token of the group, register i = head i
   float z[4];
   const float ks_q = g.ks * inv_qsc;
+  // centred codes: s*sum q(c - m) + (mn + m*s)*sum q, the centre term per token
+  const float kmid = KF::kCentre != 0.f ? fmaf(KF::kCentre, g.ks, g.kmn) : g.kmn;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const auto r01 = __builtin_amdgcn_permlane16_swap(f_bits(cq[0][i]), f_bits(cq[1][i]), false, false);
@@ -489,7 +508,8 @@ __device__ __forceinline__ void compute_group(GroupRaw<KB, VB, D>& g, const u32x
     const auto r = __builtin_amdgcn_permlane32_swap(r01[0], r23[0], false, false);
     const float sc = bits_f(r[0]);
     float zi;
-    if constexpr (KMETA) zi = fmaf(ks_q, sc, fmaf(-ks_q, biasq[i], g.kmn * q2[i]));
+    if constexpr (KMETA && KF::kCentre != 0.f) zi = fmaf(ks_q, sc, kmid * q2[i]);
+    else if constexpr (KMETA) zi = fmaf(ks_q, sc, fmaf(-ks_q, biasq[i], g.kmn * q2[i]));
     else zi = sc;
     z[i] = (g.valid && i < G) ? zi : NEG_INF;
   }
@@ -724,7 +744,7 @@ void decode_partial_kernel(DecodeArgs a, const int32_t* __restrict__ table, uint
     frexpf(amax, &ex);
     qsc = ldexpf(1.f, 10 - ex);
   }
-  double q1 = 0.0;  // this lane's share of the sum of the A values used (bias correction)
+  double q1 = 0.0;  // this lane's share of sum A * (base + centre*sigma): the offset to remove
   double q2l = 0.0; // and of sum_j q~_j (the min term)
 #pragma unroll
   for (int c = 0; c < NCK; ++c) {
@@ -748,7 +768,8 @@ void decode_partial_kernel(DecodeArgs a, const int32_t* __restrict__ table, uint
           lv = static_cast<float>(ll);
           hb = half_bits(hh); lb = half_bits(ll);
         }
-        q1 += static_cast<double>(hv) + static_cast<double>(lv);
+        q1 += (static_cast<double>(hv) + static_cast<double>(lv)) *
+              static_cast<double>(KF::base(c, e) + KF::kCentre * KF::sigma(c, e));
         q2l += static_cast<double>(qt);
         hp |= hb << (16 * half);
         lp |= lb << (16 * half);
@@ -763,13 +784,14 @@ void decode_partial_kernel(DecodeArgs a, const int32_t* __restrict__ table, uint
   q2l += __shfl_xor(q2l, 16, 64);
   q2l += __shfl_xor(q2l, 32, 64);
   // Per query head constants, broadcast from lane i (row i):
-  //   biasq_i = 1024 * Q1_i (scaled units), q2_i = sum_j q~_ij (log2 units).
+  //   biasq_i = sum A * (base + centre*sigma) (scaled units; 1024 * sum A for the
+  //   uncentred formats, 0 for centred ones), q2_i = sum_j q~_ij (log2 units).
   float biasq[4], q2[4];
   const float inv_qsc = 1.f / qsc;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float q1i = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, static_cast<float>(q1)), i));
-    biasq[i] = KF::bf16 ? 0.f : 1024.f * q1i;
+    biasq[i] = q1i;
     q2[i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, static_cast<float>(q2l)), i));
   }
   const uint32_t bias = vconst(0x64006400u);  // fp16 pair (1024, 1024)
