@@ -7,13 +7,10 @@
 // write). Bits per head can differ between K and V and between heads, as in
 // the RateQuant summary page (2605.06675), Methodology stage 3.
 //
-// Layout of work: a row is one (sequence, token, head) vector of head_dim
-// values; d/8 consecutive lanes hold one row, 8 channels per lane
-// ([8L, 8L+8) on lane L of the row). The Walsh-Hadamard butterflies run in
-// registers for strides 1, 2, 4 and across lanes (xor shuffles) for strides
-// 8 .. n/2. Row min/max reduce across the same lanes. Each lane then packs its
-// 8 codes into b bytes, so a row's codes leave as one coalesced run of d*b/8
-// bytes; lane 0 writes the row's {scale, min}.
+// Layout of work (append): four lanes per row, each with d/4 contiguous
+// channels (see append_rows). Dequantize (a read-back path, not the hot one):
+// d/8 lanes per row, 8 channels per lane, butterflies across lanes by xor
+// shuffles.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -57,58 +54,91 @@ __device__ __forceinline__ void fwht8(float (&x)[8], int lane_in_row, int n) {
   }
 }
 
-// The same transform in fp64 for the write path. MI355X issues fp64 adds at
-// the fp32 (non-packed) lane rate, and the sums of bf16 or fp32 inputs here are
-// exact or nearly so in fp64, so rounding the result to fp32 reproduces the
-// rotation's value (an explicit fp64 matrix product rounded to fp32) instead of
-// accumulating fp32 rounding over log2(n) stages of cancellation.
-__device__ __forceinline__ void fwht8_f64(double (&x)[8], int lane_in_row, int n) {
+// ---------------------------------------------------------------------------
+// Quantize-on-append. A row is one (sequence, token, head) vector of D values;
+// four consecutive lanes hold it, lane m taking the contiguous channels
+// [m*CPR, (m+1)*CPR), CPR = D/4. So a lane reads 2*CPR (bf16) or 4*CPR (fp32)
+// contiguous bytes and writes its CPR*b/8 code bytes contiguously, and 16
+// consecutive tokens of one head (one page) leave a wave as one run of codes.
+// The Walsh-Hadamard butterflies of stride < CPR run in registers, the (at
+// most two) strides CPR and 2*CPR between the four lanes through DPP quad
+// permutations. The butterflies run in fp64: MI355X issues fp64 adds at the
+// fp32 (non-packed) lane rate, and the +-1 sums of bf16 or fp32 inputs are
+// exact in fp64, so scaling by 1/sqrt(n) and rounding to fp32 reproduces the
+// rotation's value (an exact matrix product, one rounding).
+// ---------------------------------------------------------------------------
+
+constexpr int kDppXor1 = 0xb1;  // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4e;  // quad_perm [2, 3, 0, 1]
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const int lo = __builtin_amdgcn_mov_dpp(static_cast<int>(u), CTRL, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_mov_dpp(static_cast<int>(u >> 32), CTRL, 0xf, 0xf, false);
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) |
+                                        static_cast<uint32_t>(lo));
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+
+template <int CPR, int MAXST>
+__device__ __forceinline__ void butterflies_in_lane(double (&x)[CPR]) {
 #pragma unroll
-  for (int st = 1; st < 8; st <<= 1) {
-    if (st < n) {
+  for (int st = 1; st < MAXST; st <<= 1) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (!(j & st)) {
-          const double u = x[j], v = x[j | st];
-          x[j] = u + v;
-          x[j | st] = u - v;
+    for (int j = 0; j < CPR; ++j) {
+      if (!(j & st)) {
+        const double u = x[j], v = x[j | st];
+        x[j] = u + v;
+        x[j | st] = u - v;
+      }
+    }
+  }
+}
+
+template <int CPR>
+__device__ __forceinline__ void fwht_row_f64(double (&x)[CPR], int m, int n) {
+  // blocks at least a lane wide (the common case) take every in-lane stride
+  if (n >= CPR) {
+    butterflies_in_lane<CPR, CPR>(x);
+  } else {
+#pragma unroll
+    for (int st = 1; st < CPR; st <<= 1) {
+      if (st < n) {
+#pragma unroll
+        for (int j = 0; j < CPR; ++j) {
+          if (!(j & st)) {
+            const double u = x[j], v = x[j | st];
+            x[j] = u + v;
+            x[j | st] = u - v;
+          }
         }
       }
     }
   }
-  for (int m = 1; m * 8 < n; m <<= 1) {
-    const double sgn = (lane_in_row & m) ? -1.0 : 1.0;  // lower: x + y, upper: y - x
+  // lower lane of a pair keeps x + y, upper keeps y - x: fma(+-1, x, y) rounds
+  // once, exactly like the add or subtract
+  if (CPR < n) {
+    const double sgn = (m & 1) ? -1.0 : 1.0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const double y = __shfl_xor(x[j], m, 64);
-      x[j] = fma(sgn, x[j], y);
-    }
+    for (int j = 0; j < CPR; ++j) x[j] = fma(sgn, x[j], dpp_f64<kDppXor1>(x[j]));
+  }
+  if (2 * CPR < n) {
+    const double sgn = (m & 2) ? -1.0 : 1.0;
+#pragma unroll
+    for (int j = 0; j < CPR; ++j) x[j] = fma(sgn, x[j], dpp_f64<kDppXor2>(x[j]));
   }
 }
 
-__device__ __forceinline__ void load8(const void* src, bool bf16, size_t elem, float (&x)[8]) {
-  if (bf16) {
-    const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + elem);
-    x[0] = bf16lo_to_f(w.x); x[1] = bf16hi_to_f(w.x);
-    x[2] = bf16lo_to_f(w.y); x[3] = bf16hi_to_f(w.y);
-    x[4] = bf16lo_to_f(w.z); x[5] = bf16hi_to_f(w.z);
-    x[6] = bf16lo_to_f(w.w); x[7] = bf16hi_to_f(w.w);
-  } else {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(src) + elem);
-    const float4 a = p[0], b = p[1];
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-  }
-}
-
-// Quantize 8 values with (mn, inv) and store this lane's BITS bytes.
+// Codes of 8 consecutive values (already scaled to code units u) packed
+// little-endian: BITS=4 -> one word, 2 -> 16 bits, 8 -> two words, 3 -> 24 bits.
+// v_cvt_pk_u8_f32 rounds half to even and saturates to [0, 255]; u lies in
+// [0, 2^b - 1 + 2^-22 (2^b - 1)], so every code is already in range.
 template <int BITS>
-__device__ __forceinline__ void quantize_store8(const float (&x)[8], float mn, float inv, uint8_t* dst) {
-  float u[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) u[j] = (x[j] - mn) * inv;
-  // v_cvt_pk_u8_f32 rounds half to even and saturates to [0, 255]; u lies in
-  // [0, 2^b - 1 + 2^-22 (2^b - 1)], so the code is already in range.
+__device__ __forceinline__ uint64_t pack8(const float* u) {
   if constexpr (BITS == 8) {
     uint32_t w0 = 0, w1 = 0;
 #pragma unroll
@@ -116,63 +146,75 @@ __device__ __forceinline__ void quantize_store8(const float (&x)[8], float mn, f
       w0 = __builtin_amdgcn_cvt_pk_u8_f32(u[j], j, w0);
       w1 = __builtin_amdgcn_cvt_pk_u8_f32(u[4 + j], j, w1);
     }
-    *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
-  } else if constexpr (BITS == 4) {
+    return w0 | (static_cast<uint64_t>(w1) << 32);
+  } else if constexpr (BITS == 4 || BITS == 2) {
     uint32_t ev = 0, od = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       ev = __builtin_amdgcn_cvt_pk_u8_f32(u[2 * j], j, ev);
       od = __builtin_amdgcn_cvt_pk_u8_f32(u[2 * j + 1], j, od);
     }
-    *reinterpret_cast<uint32_t*>(dst) = ev | (od << 4);
-  } else if constexpr (BITS == 2) {
-    uint32_t ev = 0, od = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      ev = __builtin_amdgcn_cvt_pk_u8_f32(u[2 * j], j, ev);
-      od = __builtin_amdgcn_cvt_pk_u8_f32(u[2 * j + 1], j, od);
-    }
-    const uint32_t t = ev | (od << 2);              // byte m: c[2m] | c[2m+1] << 2
+    if constexpr (BITS == 4) return ev | (od << 4);
+    const uint32_t t = ev | (od << 2);              // byte k: c[2k] | c[2k+1] << 2
     const uint32_t v = (t | (t >> 4)) & 0x00ff00ffu; // byte 0: c0..c3, byte 2: c4..c7
-    *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>((v & 0xffu) | ((v >> 8) & 0xff00u));
-  } else {  // BITS == 3: 24 bits per lane, byte stores (lane offsets are 3-byte aligned)
+    return (v & 0xffu) | ((v >> 8) & 0xff00u);
+  } else {  // BITS == 3
     uint32_t w = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) w |= static_cast<uint32_t>(__builtin_rintf(u[j])) << (3 * j);
-    dst[0] = static_cast<uint8_t>(w);
-    dst[1] = static_cast<uint8_t>(w >> 8);
-    dst[2] = static_cast<uint8_t>(w >> 16);
+    return w;
   }
 }
 
 template <int BITS, int D>
-__global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a, double rs_n) {
-  constexpr int LPR = D / 8;             // lanes per row
+__device__ __forceinline__ void append_rows(const AppendArgs& a, int half, double rs_n) {
+  constexpr int LPR = 4, CPR = D / LPR;  // lanes per row, channels per lane
   constexpr int RPB = kThreads / LPR;    // rows per workgroup
   constexpr int RB = D * BITS / 8;       // bytes per stored row
   const int tid = threadIdx.x;
-  const int lane = tid % LPR;
+  const int m = tid & (LPR - 1);
   const int row = blockIdx.x * RPB + tid / LPR;
   const int h = a.heads[blockIdx.y];
-  const int64_t area = a.area_off[blockIdx.y];
+  const int64_t area = a.area_off[half][blockIdx.y];
   const int total = a.batch * a.n_new;
   const bool active = row < total;
   const int r = active ? row : 0;
   const int b = r / a.n_new;
   const int i = r - b * a.n_new;
 
-  float x[8];
-  const size_t elem = (static_cast<size_t>(r) * a.hkv + h) * D + lane * 8;
-  load8(a.src, a.src_bf16 != 0, elem, x);
-
-  double xd[8];
+  // ---- load this lane's CPR channels ----
+  float x[CPR];
+  const size_t elem = (static_cast<size_t>(r) * a.hkv + h) * D + m * CPR;
+  if (a.src_bf16) {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.src[half]) + elem);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) xd[j] = static_cast<double>(x[j]);
-  fwht8_f64(xd, lane, a.had_block);
+    for (int k = 0; k < CPR / 8; ++k) {
+      const uint4 w = p[k];
+      x[8 * k + 0] = bf16lo_to_f(w.x); x[8 * k + 1] = bf16hi_to_f(w.x);
+      x[8 * k + 2] = bf16lo_to_f(w.y); x[8 * k + 3] = bf16hi_to_f(w.y);
+      x[8 * k + 4] = bf16lo_to_f(w.z); x[8 * k + 5] = bf16hi_to_f(w.z);
+      x[8 * k + 6] = bf16lo_to_f(w.w); x[8 * k + 7] = bf16hi_to_f(w.w);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.src[half]) + elem);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) x[j] = static_cast<float>(xd[j] * rs_n);
+    for (int k = 0; k < CPR / 4; ++k) {
+      const float4 w = p[k];
+      x[4 * k + 0] = w.x; x[4 * k + 1] = w.y; x[4 * k + 2] = w.z; x[4 * k + 3] = w.w;
+    }
+  }
 
-  // Destination of this row; rows whose page is unmapped are skipped.
+  // ---- rotate ----
+  {
+    double xd[CPR];
+#pragma unroll
+    for (int j = 0; j < CPR; ++j) xd[j] = static_cast<double>(x[j]);
+    fwht_row_f64<CPR>(xd, m, a.had_block);
+#pragma unroll
+    for (int j = 0; j < CPR; ++j) x[j] = static_cast<float>(xd[j] * rs_n);
+  }
+
+  // ---- destination; rows whose page is unmapped are skipped ----
   const int p = a.start_pos[b] + i;
   const int page = p / kBlockTokens;
   bool store = active && p >= 0 && page < a.table_stride;
@@ -182,26 +224,29 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a, double r
     store = blk >= 0 && blk < a.pool_blocks;
   }
   const int slot = p - page * kBlockTokens;
-  uint8_t* base = store ? a.pool + blk * a.block_bytes + area : nullptr;
+  uint8_t* dst = store ? a.pool + blk * a.block_bytes + area + slot * RB + m * (CPR * BITS / 8) : nullptr;
 
   if constexpr (BITS == 16) {
     if (store) {
-      uint4 w;
-      w.x = f_to_bf16_rne(x[0]) | (f_to_bf16_rne(x[1]) << 16);
-      w.y = f_to_bf16_rne(x[2]) | (f_to_bf16_rne(x[3]) << 16);
-      w.z = f_to_bf16_rne(x[4]) | (f_to_bf16_rne(x[5]) << 16);
-      w.w = f_to_bf16_rne(x[6]) | (f_to_bf16_rne(x[7]) << 16);
-      *reinterpret_cast<uint4*>(base + slot * RB + lane * 16) = w;
+#pragma unroll
+      for (int k = 0; k < CPR / 8; ++k) {
+        uint4 w;
+        w.x = f_to_bf16_rne(x[8 * k + 0]) | (f_to_bf16_rne(x[8 * k + 1]) << 16);
+        w.y = f_to_bf16_rne(x[8 * k + 2]) | (f_to_bf16_rne(x[8 * k + 3]) << 16);
+        w.z = f_to_bf16_rne(x[8 * k + 4]) | (f_to_bf16_rne(x[8 * k + 5]) << 16);
+        w.w = f_to_bf16_rne(x[8 * k + 6]) | (f_to_bf16_rne(x[8 * k + 7]) << 16);
+        reinterpret_cast<uint4*>(dst)[k] = w;
+      }
     }
   } else {
+    // ---- row min / max: this lane's values, then the row's four lanes ----
     float mn = x[0], mx = x[0];
 #pragma unroll
-    for (int j = 1; j < 8; ++j) { mn = fminf(mn, x[j]); mx = fmaxf(mx, x[j]); }
-#pragma unroll
-    for (int m = 1; m < LPR; m <<= 1) {
-      mn = fminf(mn, shfl_xor(mn, m));
-      mx = fmaxf(mx, shfl_xor(mx, m));
-    }
+    for (int j = 1; j < CPR; ++j) { mn = fminf(mn, x[j]); mx = fmaxf(mx, x[j]); }
+    mn = fminf(mn, dpp_f32<kDppXor1>(mn));
+    mx = fmaxf(mx, dpp_f32<kDppXor1>(mx));
+    mn = fminf(mn, dpp_f32<kDppXor2>(mn));
+    mx = fmaxf(mx, dpp_f32<kDppXor2>(mx));
     const float qmax = static_cast<float>((1 << BITS) - 1);
     const float rng = mx - mn;
     float s = 0.f, inv = 0.f;
@@ -209,12 +254,58 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a, double r
       s = rng / qmax;  // IEEE division (correctly rounded)
       inv = qmax / rng;
     }
+    // ---- quantize and pack this lane's CPR codes ----
+    float u[CPR];
+#pragma unroll
+    for (int j = 0; j < CPR; ++j) u[j] = (x[j] - mn) * inv;
+    uint64_t g[CPR / 8];
+#pragma unroll
+    for (int k = 0; k < CPR / 8; ++k) g[k] = pack8<BITS>(u + 8 * k);
     if (store) {
-      quantize_store8<BITS>(x, mn, inv, base + slot * RB + lane * BITS);
-      if (lane == 0)
-        *reinterpret_cast<float2*>(base + kBlockTokens * RB + slot * kMetaBytes) = make_float2(s, mn);
+      if constexpr (BITS == 4) {
+        if constexpr (CPR == 32)
+          *reinterpret_cast<uint4*>(dst) = make_uint4(static_cast<uint32_t>(g[0]), static_cast<uint32_t>(g[1]),
+                                                      static_cast<uint32_t>(g[2]), static_cast<uint32_t>(g[3]));
+        else
+          *reinterpret_cast<uint2*>(dst) = make_uint2(static_cast<uint32_t>(g[0]), static_cast<uint32_t>(g[1]));
+      } else if constexpr (BITS == 2) {
+        if constexpr (CPR == 32)
+          *reinterpret_cast<uint2*>(dst) = make_uint2(static_cast<uint32_t>(g[0] | (g[1] << 16)),
+                                                      static_cast<uint32_t>(g[2] | (g[3] << 16)));
+        else
+          *reinterpret_cast<uint32_t*>(dst) = static_cast<uint32_t>(g[0] | (g[1] << 16));
+      } else if constexpr (BITS == 8) {
+#pragma unroll
+        for (int k = 0; k < CPR / 16; ++k)
+          reinterpret_cast<uint4*>(dst)[k] =
+              make_uint4(static_cast<uint32_t>(g[2 * k]), static_cast<uint32_t>(g[2 * k] >> 32),
+                         static_cast<uint32_t>(g[2 * k + 1]), static_cast<uint32_t>(g[2 * k + 1] >> 32));
+      } else {  // BITS == 3: 24 bits per group of 8
+        if constexpr (CPR == 32) {  // 12 bytes at a 4-byte aligned offset
+          uint32_t* w = reinterpret_cast<uint32_t*>(dst);
+          w[0] = static_cast<uint32_t>(g[0] | (g[1] << 24));
+          w[1] = static_cast<uint32_t>((g[1] >> 8) | (g[2] << 16));
+          w[2] = static_cast<uint32_t>((g[2] >> 16) | (g[3] << 8));
+        } else {  // 6 bytes at a 2-byte aligned offset
+          uint16_t* w = reinterpret_cast<uint16_t*>(dst);
+          w[0] = static_cast<uint16_t>(g[0]);
+          w[1] = static_cast<uint16_t>((g[0] >> 16) | (g[1] << 8));
+          w[2] = static_cast<uint16_t>(g[1] >> 8);
+        }
+      }
+      if (m == 0)
+        *reinterpret_cast<float2*>(a.pool + blk * a.block_bytes + area + kBlockTokens * RB + slot * kMetaBytes) =
+            make_float2(s, mn);
     }
   }
+}
+
+// K rows (blockIdx.z == 0) at BK bits and V rows (blockIdx.z == 1) at BV bits
+// of the listed heads, in one launch.
+template <int BK, int BV, int D>
+__global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a, double rs_n) {
+  if (blockIdx.z == 0) append_rows<BK, D>(a, 0, rs_n);
+  else append_rows<BV, D>(a, 1, rs_n);
 }
 
 // Read this lane's 8 stored values of one row back to fp32 (rotated basis).
@@ -284,12 +375,12 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(DequantArgs a, float 
   }
 }
 
-template <int BITS, int D>
+template <int BK, int BV, int D>
 hipError_t launch_append_t(const AppendArgs& a, double rs, hipStream_t s) {
-  constexpr int RPB = kThreads / (D / 8);
+  constexpr int RPB = kThreads / 4;
   const int rows = a.batch * a.n_new;
-  dim3 grid((rows + RPB - 1) / RPB, a.n_heads);
-  hipLaunchKernelGGL((append_kernel<BITS, D>), grid, dim3(kThreads), 0, s, a, rs);
+  dim3 grid((rows + RPB - 1) / RPB, a.n_heads, 2);
+  hipLaunchKernelGGL((append_kernel<BK, BV, D>), grid, dim3(kThreads), 0, s, a, rs);
   return hipGetLastError();
 }
 
@@ -315,12 +406,24 @@ float rsqrt_exact(int n) { return static_cast<float>(1.0 / std::sqrt(static_cast
     default: return hipErrorInvalidValue;                                         \
   }
 
-hipError_t launch_append(const AppendArgs& a, int /*unused*/, hipStream_t s) {
+template <int BK>
+hipError_t launch_append_k(const AppendArgs& a, double rs, hipStream_t s) {
+#define KVQ_APPEND_CALL(B_, D_) launch_append_t<BK, B_, D_>(a, rs, s)
+  KVQ_BITS_SWITCH(a.bits[1], a.d, KVQ_APPEND_CALL)
+#undef KVQ_APPEND_CALL
+}
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
   if (a.batch * a.n_new == 0 || a.n_heads == 0) return hipSuccess;
   const double rs = 1.0 / std::sqrt(static_cast<double>(a.had_block));
-#define KVQ_APPEND_CALL(B_, D_) launch_append_t<B_, D_>(a, rs, s)
-  KVQ_BITS_SWITCH(a.bits, a.d, KVQ_APPEND_CALL)
-#undef KVQ_APPEND_CALL
+  switch (a.bits[0]) {
+    case 2: return launch_append_k<2>(a, rs, s);
+    case 3: return launch_append_k<3>(a, rs, s);
+    case 4: return launch_append_k<4>(a, rs, s);
+    case 8: return launch_append_k<8>(a, rs, s);
+    case 16: return launch_append_k<16>(a, rs, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t s) {

@@ -329,38 +329,38 @@ kvq_status kvq_quantize_append(const kvq_layout* L, void* pool, int64_t pool_blo
   if (static_cast<int64_t>(batch) * n_new > (int64_t{1} << 31) / 8)
     return fail(KVQ_ERR_ARG, "kvq_quantize_append: too many rows in one call");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  for (int half = 0; half < 2; ++half) {
-    const int32_t* bits = half ? L->bits_v : L->bits_k;
-    const int64_t* offs = half ? L->v_off : L->k_off;
-    bool done[KVQ_MAX_KV_HEADS] = {};
-    for (int h0 = 0; h0 < L->num_kv_heads; ++h0) {
-      if (done[h0]) continue;
-      kvq::AppendArgs a{};
-      a.pool = static_cast<uint8_t*>(pool);
-      a.pool_blocks = pool_blocks;
-      a.block_bytes = L->block_bytes;
-      a.table = block_table;
-      a.table_stride = table_stride;
-      a.start_pos = start_pos;
-      a.src = half ? v : k;
-      a.src_bf16 = in_dtype == KVQ_BF16;
-      a.batch = batch;
-      a.n_new = n_new;
-      a.hkv = L->num_kv_heads;
-      a.d = L->head_dim;
-      a.had_block = L->had_block;
-      a.bits = bits[h0];
-      for (int h = h0; h < L->num_kv_heads; ++h) {
-        if (!done[h] && bits[h] == bits[h0]) {
-          a.heads[a.n_heads] = h;
-          a.area_off[a.n_heads] = offs[h];
-          ++a.n_heads;
-          done[h] = true;
-        }
+  // one launch per distinct (K bits, V bits) pair, K and V rows together
+  bool done[KVQ_MAX_KV_HEADS] = {};
+  for (int h0 = 0; h0 < L->num_kv_heads; ++h0) {
+    if (done[h0]) continue;
+    kvq::AppendArgs a{};
+    a.pool = static_cast<uint8_t*>(pool);
+    a.pool_blocks = pool_blocks;
+    a.block_bytes = L->block_bytes;
+    a.table = block_table;
+    a.table_stride = table_stride;
+    a.start_pos = start_pos;
+    a.src[0] = k;
+    a.src[1] = v;
+    a.src_bf16 = in_dtype == KVQ_BF16;
+    a.batch = batch;
+    a.n_new = n_new;
+    a.hkv = L->num_kv_heads;
+    a.d = L->head_dim;
+    a.had_block = L->had_block;
+    a.bits[0] = L->bits_k[h0];
+    a.bits[1] = L->bits_v[h0];
+    for (int h = h0; h < L->num_kv_heads; ++h) {
+      if (!done[h] && L->bits_k[h] == L->bits_k[h0] && L->bits_v[h] == L->bits_v[h0]) {
+        a.heads[a.n_heads] = h;
+        a.area_off[0][a.n_heads] = L->k_off[h];
+        a.area_off[1][a.n_heads] = L->v_off[h];
+        ++a.n_heads;
+        done[h] = true;
       }
-      hipError_t e = kvq::launch_append(a, 0, s);
-      if (e != hipSuccess) return device_status(e, "kvq_quantize_append launch");
     }
+    hipError_t e = kvq::launch_append(a, s);
+    if (e != hipSuccess) return device_status(e, "kvq_quantize_append launch");
   }
   return ok();
 }

@@ -8,8 +8,8 @@
 
 namespace kvq {
 
-// One append launch: every row of one KV half (K or V) for a set of heads
-// that share a bit width.
+// One append launch: the K and V rows of a set of heads that share their
+// (K bits, V bits) pair.
 struct AppendArgs {
   uint8_t* pool;
   int64_t pool_blocks;
@@ -17,13 +17,13 @@ struct AppendArgs {
   const int32_t* table;
   int32_t table_stride;
   const int32_t* start_pos;
-  const void* src;      // [batch][n_new][hkv][d]
+  const void* src[2];   // K, V: [batch][n_new][hkv][d]
   int32_t src_bf16;
   int32_t batch, n_new, hkv, d, had_block;
   int32_t n_heads;      // heads in this launch
-  int32_t bits;         // shared bit width of these heads
+  int32_t bits[2];      // K bits, V bits of these heads
   int32_t heads[KVQ_MAX_KV_HEADS];
-  int64_t area_off[KVQ_MAX_KV_HEADS];  // byte offset of each listed head's area in a block
+  int64_t area_off[2][KVQ_MAX_KV_HEADS];  // byte offset of each listed head's K / V area in a block
 };
 
 struct DequantArgs {
@@ -71,7 +71,7 @@ struct MergeArgs {
 };
 
 // Launchers return hipSuccess or the launch error; they never synchronise.
-hipError_t launch_append(const AppendArgs& a, int n_splits_rows, hipStream_t s);
+hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t s);
 hipError_t launch_decode_partial(const DecodeArgs& a, int kbits, int vbits, int d, int n_splits,
                                  int batch, hipStream_t s);
