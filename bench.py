@@ -164,12 +164,303 @@ def cpu_baseline(units, seed=77):
                       f"to the full step ({B * HKV * LAYERS} units)"}
 
 
+def decode_bytes(batch, tokens, bits_k, bits_v, d=D):
+    """Algorithmic bytes the partial kernels read for one layer of one segment: codes + metadata
+    (none at 16 bits) per token and head, the page table, and q (bf16)."""
+    per_tok = sum(d * bk // 8 + (8 if bk != 16 else 0) + d * bv // 8 + (8 if bv != 16 else 0)
+                  for bk, bv in zip(bits_k, bits_v))
+    return batch * tokens * per_tok + batch * (-(-tokens // 16)) * 4
+
+
+def make_pool(kvq, torch, dev, L, batch, tokens, seed):
+    pages = -(-tokens // 16)
+    n_blocks = batch * pages
+    table_np = np.full((batch, pages), -1, np.int32)
+    kvq.kvq_page_alloc(synth_mod().free_list(n_blocks, seed), 0, np.zeros(batch, np.int32),
+                       np.full(batch, tokens, np.int32), table_np)
+    return (torch.empty((n_blocks, L.block_bytes), dtype=torch.uint8, device=dev),
+            torch.from_numpy(table_np).to(dev))
+
+
+def synth_mod():
+    from quantized_decode_attention_03_amd import synth
+    return synth
+
+
+def build_decode_layers(args, kvq, torch, dev):
+    """Per layer: segments (layout, pool, table, lens, tokens), q, the new token's K/V and the
+    segment it is appended to; plus the config and the algorithmic bytes per layer."""
+    synth = synth_mod()
+    layers = []
+    if args.workload == "mixed32k":
+        batch, tokens = 8, 32768
+        w_k = synth.sensitivities(LAYERS, HKV, seed=3).ravel()
+        w_v = synth.sensitivities(LAYERS, HKV, seed=33).ravel()
+        budget = 3 * LAYERS * HKV
+        bk_all = kvq.kvq_plan_bits(w_k, 1.0, 3.6, [2, 3, 4, 8], budget)[0].reshape(LAYERS, HKV)
+        bv_all = kvq.kvq_plan_bits(w_v, 1.0, 5.3, [2, 3, 4, 8], budget)[0].reshape(LAYERS, HKV)
+        total_bytes = 0
+        for l in range(args.layers):
+            bk, bv = [int(x) for x in bk_all[l]], [int(x) for x in bv_all[l]]
+            L = kvq.kvq_layout_init(HKV, G, D, HAD, bk, bv)
+            pool, table = make_pool(kvq, torch, dev, L, batch, tokens, 3000 + l)
+            k, v, q = synth.llama_layer_torch(3000 + l, batch, tokens, HKV, G, D, device=dev)
+            kvq.kvq_quantize_append(L, pool, table, torch.zeros(batch, dtype=torch.int32, device=dev), k, v)
+            lens = torch.full((batch,), tokens, dtype=torch.int32, device=dev)
+            layers.append({"segs": [(L, pool, table, lens, tokens)], "q": q, "app": 0,
+                           "new_k": k[:, -1:].contiguous(), "new_v": v[:, -1:].contiguous(),
+                           "pos": tokens - 1})
+            total_bytes += decode_bytes(batch, tokens, bk, bv)
+            del k, v
+        config = {"workload": "mixed-precision decode: 32 layers, batch 8, ctx 32768, 8 kv heads x 4 q heads, "
+                              "head_dim 128, per-head K/V bits from kvq_plan_bits (ladder {2,3,4,8}, average 3, "
+                              "beta_K 3.6, beta_V 5.3), hadamard 128",
+                  "layers": args.layers, "batch": batch, "ctx": tokens}
+        return layers, config, batch, total_bytes / args.layers, "decode_partial_kernel (per (K,V) bit pair)"
+    if args.workload == "long131k":
+        batch, tokens, window = 1, 131072, 128
+        cls = kvq.kvq_logquant_classes(tokens, window)
+        idx_all = [torch.from_numpy(np.flatnonzero(cls == c)).to(dev) for c in range(3)]
+        counts = [int(i.numel()) for i in idx_all]
+        total_bytes = 0
+        for l in range(args.layers):
+            k, v, q = synth.llama_layer_torch(4000 + l, batch, tokens, HKV, G, D, device=dev)
+            segs = []
+            for c, bits in enumerate((16, 4, 2)):
+                L = kvq.kvq_layout_init(HKV, G, D, 32, [bits] * HKV, [bits] * HKV)
+                pool, table = make_pool(kvq, torch, dev, L, batch, counts[c], 40 + c + 10 * l)
+                kvq.kvq_quantize_append(L, pool, table, torch.zeros(batch, dtype=torch.int32, device=dev),
+                                        k[:, idx_all[c]].contiguous(), v[:, idx_all[c]].contiguous())
+                segs.append((L, pool, table, torch.full((batch,), counts[c], dtype=torch.int32, device=dev),
+                             counts[c]))
+                total_bytes += decode_bytes(batch, counts[c], [bits] * HKV, [bits] * HKV)
+            # the new token goes into the bf16 window (its last slot is rewritten each step)
+            layers.append({"segs": segs, "q": q, "app": 0, "new_k": k[:, -1:].contiguous(),
+                           "new_v": v[:, -1:].contiguous(), "pos": counts[0] - 1})
+            del k, v
+        config = {"workload": "long-context decode: batch 1, ctx 131072, 8 kv heads x 4 q heads, head_dim 128, "
+                              "hadamard 32; segments: bf16 window 128, log-spaced 4-bit subset 1280, 2-bit 129664; "
+                              "layers back to back (each layer's cache evicted from the MALL by the others)",
+                  "layers": args.layers, "batch": batch, "ctx": tokens}
+        return layers, config, batch, total_bytes / args.layers, "decode_partial_kernel (3 segments)"
+    # default: Llama-3-8B-shaped 32k decode
+    batch, tokens = B, T
+    L = kvq.kvq_layout_init(HKV, G, D, HAD, [BITS_K] * HKV, [BITS_V] * HKV)
+    for l in range(args.layers):
+        seed = SEED_BASE + l
+        pool, table = make_pool(kvq, torch, dev, L, batch, tokens, seed)
+        k, v, q = synth.llama_layer_torch(seed, batch, tokens, HKV, G, D, device=dev)
+        kvq.kvq_quantize_append(L, pool, table, torch.zeros(batch, dtype=torch.int32, device=dev), k, v)
+        lens = torch.full((batch,), tokens, dtype=torch.int32, device=dev)
+        layers.append({"segs": [(L, pool, table, lens, tokens)], "q": q, "app": 0,
+                       "new_k": k[:, T - 1:T].contiguous(), "new_v": v[:, T - 1:T].contiguous(), "pos": T - 1})
+        del k, v
+    config = {"workload": WORKLOAD, "layers": args.layers, "batch": B, "ctx": T, "kv_heads": HKV,
+              "q_per_kv": G, "head_dim": D, "bits_k": BITS_K, "bits_v": BITS_V, "had_block": HAD}
+    return layers, config, batch, bytes_per_layer(), "decode_partial_kernel<4,4,128>"
+
+
+def run_decode(args, torch, dev, kvq):
+    """One step = per layer: append the new token, partial decode, merge."""
+    layers, config, batch, layer_bytes, kernel = build_decode_layers(args, kvq, torch, dev)
+    torch.cuda.synchronize()
+    seg_objs = [[kvq.Segment(L, pool, table, lens, n) for (L, pool, table, lens, n) in ly["segs"]] for ly in layers]
+    # one workspace for every layer: the largest any layer needs (split counts follow the bit widths)
+    ws_bytes = max(kvq.kvq_decode_workspace_bytes(sg, batch) for sg in seg_objs)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    kvq.kvq_decode_workspace_init(ws)
+    out = torch.empty((batch, HKV * G, D), dtype=torch.float32, device=dev)
+    calls = []
+    for ly, segs in zip(layers, seg_objs):
+        L, pool, table, _, _ = ly["segs"][ly["app"]]
+        start = torch.full((batch,), ly["pos"], dtype=torch.int32, device=dev)
+        calls.append((kvq.prepare_quantize_append(L, pool, table, start, ly["new_k"], ly["new_v"]),
+                      kvq.prepare_decode_partial(segs, ly["q"], ws),
+                      kvq.prepare_decode_merge(segs, batch, out, ws)))
+
+    n_ev = args.layers * args.steps
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+
+    def step(record=None):
+        for i, (app, part, merge) in enumerate(calls):
+            app()
+            if record is not None:
+                ev_a[record + i].record()
+            part()
+            if record is not None:
+                ev_b[record + i].record()
+            merge()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # eager timed steps: per-launch events around every partial call
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(record=s * args.layers)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    eager_elapsed = elapsed
+    if args.graph:
+        # the same K steps captured once as one HIP graph and replayed: the
+        # step rate comes from the replay (events cannot be graph nodes here,
+        # so the kernel's duration stays the eager pass's)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for s in range(args.steps):
+                step()
+        graph.replay()  # first replay (uploads the graph)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        graph.replay()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+
+    part_ms = [a.elapsed_time(b) for a, b in zip(ev_a, ev_b)]
+    part_us = 1e3 * float(np.mean(part_ms))
+    ms_per_step = 1e3 * elapsed / args.steps
+    achieved = layer_bytes / (part_us * 1e-6) / 1e9
+    extra = {}
+    if args.graph:
+        config = dict(config, launch="hip graph of the timed steps")
+        extra["eager_tokens_per_s"] = round(batch * args.steps / eager_elapsed, 2)
+    return {**extra,
+        "value": round(batch * args.steps / elapsed, 2),
+        "unit": "tokens/s",
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "config": config,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic() if args.workload == "llama32k" else None,
+                     "kernel": kernel, "avg_us": round(part_us, 3), "bytes_per_launch": int(layer_bytes)},
+        "step_hbm_gbs": round(layer_bytes * args.layers / (ms_per_step * 1e-3) / 1e9, 1),
+    }
+
+
+def run_bulk_append(args, torch, dev, kvq):
+    """One step = per layer: quantize-append 16384 new bf16 tokens of 4 sequences (K4/V2); then one decode
+    step over the 16384 cached tokens is timed separately."""
+    synth = synth_mod()
+    batch, tokens = 4, 16384
+    L = kvq.kvq_layout_init(HKV, G, D, HAD, [4] * HKV, [2] * HKV)
+    layers = []
+    for l in range(args.layers):
+        pool, table = make_pool(kvq, torch, dev, L, batch, tokens, 5000 + l)
+        k, v, q = synth.llama_layer_torch(5000 + l, batch, tokens, HKV, G, D, device=dev)
+        layers.append((pool, table, k, v, q))
+    zeros = torch.zeros(batch, dtype=torch.int32, device=dev)
+    calls = [kvq.prepare_quantize_append(L, pool, table, zeros, k, v) for (pool, table, k, v, q) in layers]
+    rows = batch * tokens * HKV
+    app_bytes = 2 * rows * D * 2 + rows * (D * 4 // 8 + 8) + rows * (D * 2 // 8 + 8)
+    for _ in range(args.warmup):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        for c in calls:
+            c()
+    e1.record()
+    torch.cuda.synchronize()
+    app_us = e0.elapsed_time(e1) * 1e3 / (args.steps * args.layers)
+    # one decode step over the whole cache
+    lens = torch.full((batch,), tokens, dtype=torch.int32, device=dev)
+    segs = [[kvq.Segment(L, pool, table, lens, tokens)] for (pool, table, k, v, q) in layers]
+    ws = kvq.decode_workspace(segs[0], batch, dev)
+    out = torch.empty((batch, HKV * G, D), dtype=torch.float32, device=dev)
+    dcalls = [(kvq.prepare_decode_partial(sg, ly[4], ws), kvq.prepare_decode_merge(sg, batch, out, ws))
+              for sg, ly in zip(segs, layers)]
+    for p, m in dcalls:
+        p(); m()
+    torch.cuda.synchronize()
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    d0.record()
+    for _ in range(args.steps):
+        for p, m in dcalls:
+            p(); m()
+    d1.record()
+    torch.cuda.synchronize()
+    dec_us = d0.elapsed_time(d1) * 1e3 / (args.steps * args.layers)
+    achieved = app_bytes / (app_us * 1e-6) / 1e9
+    return {
+        "metric": "quantized-KV bulk append: GB/s (bf16 read + packed write), then one decode step",
+        "value": round(achieved, 1),
+        "unit": "GB/s",
+        "ms_per_step": round(app_us * args.layers / 1e3, 4),
+        "higher_is_better": True,
+        "config": {"workload": "prefill-time bulk quantize-append: 32 layers, batch 4, 16384 new tokens per "
+                               "sequence, 8 kv heads, head_dim 128, bf16 inputs, K4/V2, hadamard 128, then one "
+                               "decode step (x4 q heads) over the 16384 cached tokens",
+                   "layers": args.layers, "batch": batch, "new_tokens": tokens},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "append_kernel<4,2,128>", "avg_us": round(app_us, 3), "bytes_per_launch": app_bytes},
+        "decode_after": {"us_per_layer": round(dec_us, 3),
+                         "gb_s": round(decode_bytes(batch, tokens, [4] * HKV, [2] * HKV) / (dec_us * 1e-6) / 1e9, 1)},
+    }
+
+
+def run_tiny(args, torch, dev, kvq):
+    """The 1024-token tiny layer: append all tokens, then decode; latency per decode call."""
+    synth = synth_mod()
+    k, v, q = synth.tiny_layer(seed=1)
+    L = kvq.kvq_layout_init(4, 4, 64, 64, [4] * 4, [2] * 4)
+    pool, table = make_pool(kvq, torch, dev, L, 1, 1024, 1)
+    kvq.kvq_quantize_append(L, pool, table, torch.zeros(1, dtype=torch.int32, device=dev),
+                            torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev))
+    lens = torch.full((1,), 1024, dtype=torch.int32, device=dev)
+    seg = [kvq.Segment(L, pool, table, lens, 1024)]
+    qt = torch.from_numpy(q).to(dev)
+    ws = kvq.decode_workspace(seg, 1, dev)
+    out = torch.empty((1, 16, 64), dtype=torch.float32, device=dev)
+    p, m = kvq.prepare_decode_partial(seg, qt, ws), kvq.prepare_decode_merge(seg, 1, out, ws)
+    for _ in range(max(args.warmup, 3)):
+        p(); m()
+    torch.cuda.synchronize()
+    n = max(args.steps, 1) * 10
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        p(); m()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / n
+    nbytes = decode_bytes(1, 1024, [4] * 4, [2] * 4, d=64)
+    return {
+        "metric": "tiny-layer decode latency (launch-bound)",
+        "value": round(us, 3),
+        "unit": "us",
+        "ms_per_step": round(us / 1e3, 6),
+        "higher_is_better": False,
+        "config": {"workload": "tiny layer: batch 1, 1024 tokens, 4 kv heads x 4 q heads, head_dim 64, "
+                               "hadamard 64, K4/V2, fp32 inputs", "layers": 1, "batch": 1, "ctx": 1024},
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / (us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 5), "traffic": None,
+                     "kernel": "decode_partial_kernel<4,2,64> + decode_merge_kernel<64>", "avg_us": round(us, 3),
+                     "bytes_per_launch": nbytes},
+    }
+
+
+WORKLOADS = ("llama32k", "mixed32k", "long131k", "bulk16k", "tiny")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=LAYERS)
+    ap.add_argument("--workload", choices=WORKLOADS, default="llama32k",
+                    help="llama32k (default, the headline): batch 16, 32k decode, K4/V4; mixed32k: per-head "
+                         "bits from the planner; long131k: batch 1, three precision segments; bulk16k: "
+                         "prefill append; tiny: the 1024-token layer")
+    ap.add_argument("--graph", action=argparse.BooleanOptionalAction, default=True,
+                    help="decode workloads: after the eager timed steps (which give the partial kernel's "
+                         "per-launch times), capture the same steps as one HIP graph and take the step rate "
+                         "from its replay (default on)")
     ap.add_argument("--cpu-units", type=int, default=48, help="oracle units timed for cpu_baseline (0: skip)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run one 1 GiB device copy (for scaling HBM counters)")
@@ -191,72 +482,16 @@ def main():
 
     import torch
 
-    from quantized_decode_attention_03_amd import kvq, synth
+    from quantized_decode_attention_03_amd import kvq
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    L = kvq.kvq_layout_init(HKV, G, D, HAD, [BITS_K] * HKV, [BITS_V] * HKV)
-    pages = T // 16
-    n_blocks = B * pages
-    start = torch.full((B,), T - 1, dtype=torch.int32, device=dev)
-    zeros = torch.zeros((B,), dtype=torch.int32, device=dev)
-    lens = torch.full((B,), T, dtype=torch.int32, device=dev)
-
-    layers = []
-    for l in range(args.layers):
-        seed = SEED_BASE + l
-        free = synth.free_list(n_blocks, seed)
-        table_np = np.full((B, pages), -1, np.int32)
-        kvq.kvq_page_alloc(free, 0, np.zeros(B, np.int32), np.full(B, T, np.int32), table_np)
-        table = torch.from_numpy(table_np).to(dev)
-        pool = torch.empty((n_blocks, L.block_bytes), dtype=torch.uint8, device=dev)
-        k, v, q = synth.llama_layer_torch(seed, B, T, HKV, G, D, device=dev)
-        kvq.kvq_quantize_append(L, pool, table, zeros, k, v)      # prefill all T positions
-        new_k = k[:, T - 1:T].contiguous()
-        new_v = v[:, T - 1:T].contiguous()
-        del k, v
-        seg = [kvq.Segment(L, pool, table, lens, T)]
-        layers.append({"pool": pool, "table": table, "seg": seg, "q": q, "new_k": new_k, "new_v": new_v})
-    torch.cuda.synchronize()
-
-    ws = kvq.decode_workspace(layers[0]["seg"], B, dev)
-    out = torch.empty((B, HKV * G, D), dtype=torch.float32, device=dev)
-    calls = []
-    for ly in layers:
-        calls.append((kvq.prepare_quantize_append(L, ly["pool"], ly["table"], start, ly["new_k"], ly["new_v"]),
-                      kvq.prepare_decode_partial(ly["seg"], ly["q"], ws),
-                      kvq.prepare_decode_merge(ly["seg"], B, out, ws)))
-
-    n_ev = args.layers * args.steps
-    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
-    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
-
-    def step(record=None):
-        for i, (app, part, merge) in enumerate(calls):
-            app()
-            if record is not None:
-                ev_a[record + i].record()
-            part()
-            if record is not None:
-                ev_b[record + i].record()
-            merge()
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(record=s * args.layers)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-
-    part_ms = [a.elapsed_time(b) for a, b in zip(ev_a, ev_b)]
-    part_us = 1e3 * float(np.mean(part_ms))
-    ms_per_step = 1e3 * elapsed / args.steps
-    tokens_per_s = B * args.steps / elapsed
-    layer_bytes = bytes_per_layer()
-    achieved = layer_bytes / (part_us * 1e-6) / 1e9
-    step_bytes = layer_bytes * args.layers
+    if args.workload == "bulk16k":
+        res = run_bulk_append(args, torch, dev, kvq)
+    elif args.workload == "tiny":
+        res = run_tiny(args, torch, dev, kvq)
+    else:
+        res = run_decode(args, torch, dev, kvq)
 
     if args.copy_calib:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
@@ -265,31 +500,27 @@ def main():
         torch.cuda.synchronize()
 
     cpu = None
-    if args.cpu_units > 0:
+    if args.cpu_units > 0 and args.workload == "llama32k":
         cpu = cpu_baseline(args.cpu_units)
 
     line = {
-        "metric": "quantized-KV decode attention: tokens/s and HBM GB/s (% of peak) at 32k ctx",
-        "value": round(tokens_per_s, 2),
-        "unit": "tokens/s",
+        "metric": res.pop("metric", "quantized-KV decode attention: tokens/s and HBM GB/s (% of peak) at 32k ctx"),
+        "value": res.pop("value"),
+        "unit": res.pop("unit"),
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True,
+        "ms_per_step": res.pop("ms_per_step"),
+        "higher_is_better": res.pop("higher_is_better"),
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD, "layers": args.layers, "batch": B, "ctx": T, "kv_heads": HKV,
-                   "q_per_kv": G, "head_dim": D, "bits_k": BITS_K, "bits_v": BITS_V, "had_block": HAD},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "kernel": "decode_partial_kernel<4,4,128>", "avg_us": round(part_us, 3),
-                     "bytes_per_launch": layer_bytes},
-        "step_hbm_gbs": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
-        "cpu_baseline": cpu,
+        "config": res.pop("config"),
+        "roofline": res.pop("roofline"),
     }
+    line.update(res)
+    line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 
 

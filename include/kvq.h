@@ -204,7 +204,10 @@ kvq_status kvq_decode_workspace_bytes(const kvq_segment* segs, int32_t n_segs,
  * 4-byte aligned). Required once on a new workspace before its first decode
  * call, and again after a decode call that failed on the device; every
  * completed decode call leaves the counters zero, so a workspace is reused
- * without it. Launches a kernel (no memset), so it may be graph-captured.
+ * without it. Launches a kernel (no memset). It also creates, once per
+ * device, the side streams that a decode call with several launches (several
+ * segments or per-head bit pairs) runs them on concurrently; so call it
+ * outside graph capture, before capturing decode calls.
  * Errors: KVQ_ERR_ARG (null or misaligned), KVQ_ERR_DEVICE.
  */
 kvq_status kvq_decode_workspace_init(void* ws, size_t ws_bytes, kvq_stream stream);
@@ -223,7 +226,10 @@ kvq_status kvq_decode_workspace_init(void* ws, size_t ws_bytes, kvq_stream strea
  * ws: device workspace of at least kvq_decode_workspace_bytes bytes, zeroed
  * once by kvq_decode_workspace_init before its first use. The waves of one
  * (sequence, KV head) share its pages through counters in ws, so two calls
- * in flight at once must not share a workspace.
+ * in flight at once must not share a workspace. When the call makes several
+ * launches (several segments or per-head bit pairs), they run concurrently
+ * on library side streams forked from and joined back to `stream` with
+ * events; graph capture of the call records the same dependencies.
  * Errors: KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE, KVQ_ERR_DEVICE.
  */
 kvq_status kvq_decode_attn(const kvq_segment* segs, int32_t n_segs, int32_t batch,

@@ -629,21 +629,31 @@ void decode_partial_kernel(DecodeArgs a, const int32_t* __restrict__ table, uint
   const int slot = a.slot_base + split;
 
   // Work sharing inside the unit (sequence b, KV head h), whose W waves each
-  // write one partial. The unit's NG groups of four pages: wave w first takes
-  // the SG groups [w*SG, (w+1)*SG) (a quarter of the unit, in order), then
-  // groups of the shared tail [W*SG, NG), one at a time, from a counter in the
+  // write one partial. The unit's page groups (four pages each) are divided
+  // into W/8 contiguous ranges, one per sharing group of eight waves: wave
+  // split = x + 8r (x its XCD, r its dispatch round) joins group (r - x) mod
+  // (W/8), so a group mixes all eight XCDs and early and late waves. In its
+  // group's range of NG groups a wave first takes the SG groups
+  // [i*SG, (i+1)*SG) (a quarter of the range, in order; i = x), then groups of
+  // the shared tail [8*SG, NG), one at a time, from the group's counter in the
   // workspace. Wave speeds differ by tens of percent (the older of two waves
   // on a SIMD is issued first; some dies run slower); fast waves take more of
-  // the tail, so the unit's waves finish within about a group of each other.
-  // The last wave of the unit to finish resets the counters to zero.
-  // Without sharing (deterministic order) wave w takes [w*SG, (w+1)*SG) with
-  // SG = ceil(NG / W) and there is no tail.
+  // the tail, so a group's waves finish within about a page group of each
+  // other. Eight waves per counter keep the atomics on one address few. The
+  // last wave of a group to finish resets its counters to zero. Without
+  // sharing (deterministic order) wave i takes [i*SG, (i+1)*SG) with
+  // SG = ceil(NG / 8) and there is no tail.
   const int W = static_cast<int>(gridDim.x) / U;
-  const int NG = (pages + 3) / 4;
-  const int SG = a.share_tail ? (NG * kStaticEighths / 8) / W : (NG + W - 1) / W;
-  const int pool0 = min(SG * W, NG);
+  const int S = W / kXcds;
+  const int wx = split % kXcds, wr = split / kXcds;
+  const int sgrp = ((wr - wx) % S + S) % S;
+  const int NGU = (pages + 3) / 4;
+  const int g_lo = static_cast<int>((static_cast<int64_t>(NGU) * sgrp) / S);
+  const int NG = static_cast<int>((static_cast<int64_t>(NGU) * (sgrp + 1)) / S) - g_lo;
+  const int SG = a.share_tail ? (NG * kStaticEighths / 8) / kXcds : (NG + kXcds - 1) / kXcds;
+  const int pool0 = min(SG * kXcds, NG);
   const uint32_t pool_groups = static_cast<uint32_t>(NG - pool0);
-  uint32_t* const ctr = steal + 2 * (static_cast<int64_t>(b) * a.hkv + h);
+  uint32_t* const ctr = steal + 2 * ((static_cast<int64_t>(b) * a.hkv + h) * S + sgrp);
   const uint8_t* pool = a.pool;
   const int32_t* trow = table + static_cast<int64_t>(b) * a.table_stride;
   // The query loads go out first (straight-line, no lane-dependent branch),
@@ -685,7 +695,7 @@ void decode_partial_kernel(DecodeArgs a, const int32_t* __restrict__ table, uint
   auto load_next = [&](GroupRaw<KB, VB, D>& g) {
     int gid = NG;
     if (lpos < SG) {
-      gid = min(split * SG + lpos, NG);
+      gid = min(wx * SG + lpos, NG);
       if (lpos == SG - 1 && !exhausted) fetch();
     } else if (!exhausted) {
       const uint32_t idx = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(inflight)));
@@ -699,7 +709,7 @@ void decode_partial_kernel(DecodeArgs a, const int32_t* __restrict__ table, uint
     ++lpos;
     gid = __builtin_amdgcn_readfirstlane(gid);  // wave-uniform: page addresses stay scalar
     g.gid = gid;
-    load_group<KB, VB, D>(a, pool, trow, 4 * gid, pages, seq_len, koff, voff, lane, g);
+    load_group<KB, VB, D>(a, pool, trow, 4 * (g_lo + gid), pages, seq_len, koff, voff, lane, g);
   };
 #pragma unroll
   for (int j = 0; j < DEPTH; ++j) load_next(gbuf[j]);
@@ -893,10 +903,10 @@ void decode_partial_kernel(DecodeArgs a, const int32_t* __restrict__ table, uint
     }
   }
   // Every tail fetch of this wave has returned (the last one found the tail
-  // used up). The wave that completes the unit resets both counters.
+  // used up). The wave that completes its sharing group resets both counters.
   if (pool_groups != 0 && lane == 0) {
     const uint32_t done = atomicAdd(ctr + 1, 1u);
-    if (done == static_cast<uint32_t>(W - 1)) {
+    if (done == static_cast<uint32_t>(kXcds - 1)) {
       atomicExch(ctr, 0u);
       atomicExch(ctr + 1, 0u);
     }
@@ -906,55 +916,77 @@ void decode_partial_kernel(DecodeArgs a, const int32_t* __restrict__ table, uint
 // ---------------------------------------------------------------------------
 // Merge of the split partials (all segments) and the inverse rotation.
 // ---------------------------------------------------------------------------
+// One workgroup of four waves per (sequence, query head): the waves share the
+// split slots (wave w takes slots s = w mod 4), so a long list of slots (batch
+// 1 at long context has hundreds) is read with four waves' loads in flight.
 template <int D>
-__global__ __launch_bounds__(64) void decode_merge_kernel(MergeArgs a, float rs_n) {
+__global__ __launch_bounds__(256) void decode_merge_kernel(MergeArgs a, float rs_n) {
   constexpr int CPL = D / 64;  // channels per lane: [CPL*lane, CPL*lane + CPL)
+  constexpr int NW = 4;        // waves
+  constexpr int CHUNK = 1024;  // slots whose weights sit in LDS at a time
   constexpr float NEG_INF = -__builtin_huge_valf();
-  __shared__ float wsh[256];   // split weights 2^(m_s - M) of the current chunk of splits
-  const int lane = threadIdx.x;
+  __shared__ float wsh[CHUNK];   // split weights 2^(m_s - M) of the current chunk
+  __shared__ float red[NW][D];   // per-wave channel sums
+  __shared__ float scal[NW][2];  // per-wave max, then per-wave sum of weights * l
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t bg = blockIdx.x;
   const int S = a.total_slots;
   const float* ml = a.part_ml + bg * S * 2;
   const float* po = a.part_o + bg * S * D;
 
-  // global max over splits: lanes own splits
+  // global max over splits
   float mx = NEG_INF;
-  for (int s = lane; s < S; s += 64) mx = fmaxf(mx, ml[2 * s]);
+  for (int s = tid; s < S; s += 64 * NW) mx = fmaxf(mx, ml[2 * s]);
   mx = wave_max_scalar(mx);
+  if (lane == 0) scal[w][0] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(scal[0][0], scal[1][0]), fmaxf(scal[2][0], scal[3][0]));
 
   float x[CPL];
 #pragma unroll
   for (int j = 0; j < CPL; ++j) x[j] = 0.f;
+  float lpart = 0.f;
   if (mx != NEG_INF) {
-    float lpart = 0.f;
-    for (int s0 = 0; s0 < S; s0 += 256) {
-      const int n = min(256, S - s0);
+    for (int s0 = 0; s0 < S; s0 += CHUNK) {
+      const int n = min(CHUNK, S - s0);
       __syncthreads();
-      for (int s = lane; s < n; s += 64) {
+      for (int s = tid; s < n; s += 64 * NW) {
         const float ms = ml[2 * (s0 + s)];
-        const float w = ms == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(ms - mx);
-        wsh[s] = w;
-        lpart = fmaf(w, ml[2 * (s0 + s) + 1], lpart);
+        const float wt = ms == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(ms - mx);
+        wsh[s] = wt;
+        lpart = fmaf(wt, ml[2 * (s0 + s) + 1], lpart);
       }
       __syncthreads();
       const float* pc = po + static_cast<int64_t>(s0) * D + CPL * lane;
-      int s = 0;
-      for (; s + 8 <= n; s += 8) {
+      int s = w;
+      for (; s + 7 * NW < n; s += 8 * NW) {
         float v[8][CPL];
 #pragma unroll
         for (int u = 0; u < 8; ++u)
 #pragma unroll
-          for (int j = 0; j < CPL; ++j) v[u][j] = pc[static_cast<int64_t>(s + u) * D + j];
+          for (int j = 0; j < CPL; ++j) v[u][j] = pc[static_cast<int64_t>(s + u * NW) * D + j];
 #pragma unroll
         for (int u = 0; u < 8; ++u)
 #pragma unroll
-          for (int j = 0; j < CPL; ++j) x[j] = fmaf(wsh[s + u], v[u][j], x[j]);
+          for (int j = 0; j < CPL; ++j) x[j] = fmaf(wsh[s + u * NW], v[u][j], x[j]);
       }
-      for (; s < n; ++s)
+      for (; s < n; s += NW)
 #pragma unroll
         for (int j = 0; j < CPL; ++j) x[j] = fmaf(wsh[s], pc[static_cast<int64_t>(s) * D + j], x[j]);
     }
-    const float inv = 1.f / wave_sum_scalar(lpart);
+  }
+  // combine the four waves
+  lpart = wave_sum_scalar(lpart);
+  if (lane == 0) scal[w][1] = lpart;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) red[w][CPL * lane + j] = x[j];
+  __syncthreads();
+  if (w != 0) return;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) x[j] = (red[0][CPL * lane + j] + red[1][CPL * lane + j]) +
+                                       (red[2][CPL * lane + j] + red[3][CPL * lane + j]);
+  if (mx != NEG_INF) {
+    const float inv = 1.f / ((scal[0][1] + scal[1][1]) + (scal[2][1] + scal[3][1]));
 #pragma unroll
     for (int j = 0; j < CPL; ++j) x[j] *= inv;
   }
@@ -1056,8 +1088,8 @@ hipError_t launch_decode_merge(const MergeArgs& a, hipStream_t s) {
   if (a.batch * a.hq == 0) return hipSuccess;
   const float rs = static_cast<float>(1.0 / std::sqrt(static_cast<double>(a.had_block)));
   dim3 grid(a.batch * a.hq);
-  if (a.d == 128) hipLaunchKernelGGL((decode_merge_kernel<128>), grid, dim3(64), 0, s, a, rs);
-  else if (a.d == 64) hipLaunchKernelGGL((decode_merge_kernel<64>), grid, dim3(64), 0, s, a, rs);
+  if (a.d == 128) hipLaunchKernelGGL((decode_merge_kernel<128>), grid, dim3(256), 0, s, a, rs);
+  else if (a.d == 64) hipLaunchKernelGGL((decode_merge_kernel<64>), grid, dim3(256), 0, s, a, rs);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -36,6 +37,44 @@ kvq_status ok() {
 kvq_status device_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
   return fail(KVQ_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Side streams for calls that make several partial-decode launches (one per
+// segment and per (K bits, V bits) head group): the launches are independent,
+// so they run concurrently, forked from and joined back to the caller's
+// stream with events (a pattern graph capture also follows). Created once per
+// device, default priority; one enqueue at a time (the events are shared).
+constexpr int kSideStreams = 4;
+struct SideStreams {
+  bool ready = false;
+  hipStream_t s[kSideStreams];
+  hipEvent_t fork;
+  hipEvent_t join[kSideStreams];
+};
+std::mutex g_side_mutex;
+SideStreams g_side[64];
+
+// Creating streams is not allowed while the caller's stream is being captured
+// into a graph: kvq_decode_workspace_init creates them ahead of any capture.
+hipError_t side_streams(SideStreams** out, hipStream_t caller) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  SideStreams& ss = g_side[dev];
+  if (!ss.ready) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (caller && hipStreamIsCapturing(caller, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone)
+      return hipErrorStreamCaptureUnsupported;
+    for (int i = 0; i < kSideStreams; ++i) {
+      if ((e = hipStreamCreateWithFlags(&ss.s[i], hipStreamNonBlocking)) != hipSuccess) return e;
+      if ((e = hipEventCreateWithFlags(&ss.join[i], hipEventDisableTiming)) != hipSuccess) return e;
+    }
+    if ((e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming)) != hipSuccess) return e;
+    ss.ready = true;
+  }
+  *out = &ss;
+  return hipSuccess;
 }
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
@@ -170,14 +209,16 @@ int total_slots(const kvq_segment* segs, int n_segs, int batch, std::vector<Spli
 }
 
 // Workspace: partial o' [batch][hq][slots][d], partial (max, sum)
-// [batch][hq][slots][2], then the work-sharing counters
-// [n_segs][batch][hkv][2] (uint32, zero between calls).
+// [batch][hq][slots][2], then the work-sharing counters: for each segment
+// [batch][hkv][splits / 8][2] (uint32, zero between calls); slots is the sum
+// of the segments' splits, so the counters take slots / 8 * batch * hkv * 2
+// words in all.
 size_t partials_bytes(int batch, int hq, int d, int slots) {
   if (slots == 0) slots = 1;
   return static_cast<size_t>(batch) * hq * slots * (static_cast<size_t>(d) + 2) * sizeof(float);
 }
-size_t workspace_bytes(int batch, int hq, int hkv, int d, int slots, int n_segs) {
-  return partials_bytes(batch, hq, d, slots) + static_cast<size_t>(n_segs) * batch * hkv * 2 * sizeof(uint32_t);
+size_t workspace_bytes(int batch, int hq, int hkv, int d, int slots) {
+  return partials_bytes(batch, hq, d, slots) + static_cast<size_t>(slots / 8) * batch * hkv * 2 * sizeof(uint32_t);
 }
 
 }  // namespace
@@ -419,7 +460,7 @@ kvq_status kvq_decode_workspace_bytes(const kvq_segment* segs, int32_t n_segs, i
   if (st != KVQ_OK) return st;
   const kvq_layout& L = *segs[0].layout;
   *bytes = workspace_bytes(batch, L.num_kv_heads * L.group, L.num_kv_heads, L.head_dim,
-                           total_slots(segs, n_segs, batch, nullptr), n_segs);
+                           total_slots(segs, n_segs, batch, nullptr));
   return ok();
 }
 
@@ -428,6 +469,12 @@ kvq_status kvq_decode_workspace_init(void* ws, size_t ws_bytes, kvq_stream strea
   if (!ws) return fail(KVQ_ERR_ARG, "kvq_decode_workspace_init: null workspace");
   if (ws_bytes % 4 != 0 || reinterpret_cast<uintptr_t>(ws) % 4 != 0)
     return fail(KVQ_ERR_ARG, "kvq_decode_workspace_init: workspace not 4-byte aligned and sized");
+  {
+    std::lock_guard<std::mutex> lock(g_side_mutex);
+    SideStreams* ss = nullptr;
+    hipError_t e = side_streams(&ss, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return device_status(e, "kvq_decode_workspace_init side streams");
+  }
   return device_status(kvq::launch_zero_words(static_cast<uint32_t*>(ws), ws_bytes / 4,
                                               reinterpret_cast<hipStream_t>(stream)),
                        "kvq_decode_workspace_init launch");
@@ -444,7 +491,7 @@ kvq_status kvq_decode_partial(const kvq_segment* segs, int32_t n_segs, int32_t b
   const int hq = L0.num_kv_heads * L0.group;
   std::vector<SplitPlan> plans;
   const int slots = total_slots(segs, n_segs, batch, &plans);
-  const size_t need = workspace_bytes(batch, hq, L0.num_kv_heads, L0.head_dim, slots, n_segs);
+  const size_t need = workspace_bytes(batch, hq, L0.num_kv_heads, L0.head_dim, slots);
   if (ws_bytes < need)
     return fail(KVQ_ERR_WORKSPACE, "kvq_decode_partial: workspace %zu < %zu bytes", ws_bytes, need);
   float* part_o = static_cast<float*>(ws);
@@ -452,6 +499,11 @@ kvq_status kvq_decode_partial(const kvq_segment* segs, int32_t n_segs, int32_t b
   uint32_t* steal = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) +
                                                 partials_bytes(batch, hq, L0.head_dim, slots));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  struct Launch {
+    kvq::DecodeArgs a;
+    int kbits, vbits, d, n_splits;
+  };
+  std::vector<Launch> launches;
   int slot_base = 0;
   for (int i = 0; i < n_segs; ++i) {
     const kvq_segment& sg = segs[i];
@@ -474,7 +526,7 @@ kvq_status kvq_decode_partial(const kvq_segment* segs, int32_t n_segs, int32_t b
         a.group = L.group;
         a.had_block = L.had_block;
         a.batch = batch;
-        a.steal = steal + static_cast<size_t>(i) * batch * L.num_kv_heads * 2;
+        a.steal = steal + static_cast<size_t>(slot_base / 8) * batch * L.num_kv_heads * 2;
         a.share_tail = deterministic_order() ? 0 : 1;
         a.slot_base = slot_base;
         a.total_slots = slots;
@@ -489,11 +541,36 @@ kvq_status kvq_decode_partial(const kvq_segment* segs, int32_t n_segs, int32_t b
             done[h] = true;
           }
         }
-        hipError_t e = kvq::launch_decode_partial(a, L.bits_k[h0], L.bits_v[h0], L.head_dim, p.n_splits, batch, s);
-        if (e != hipSuccess) return device_status(e, "kvq_decode_partial launch");
+        launches.push_back({a, L.bits_k[h0], L.bits_v[h0], L.head_dim, p.n_splits});
       }
     }
     slot_base += p.n_splits;
+  }
+  if (launches.size() == 1) {
+    const Launch& l = launches[0];
+    return device_status(kvq::launch_decode_partial(l.a, l.kbits, l.vbits, l.d, l.n_splits, batch, s),
+                         "kvq_decode_partial launch");
+  }
+  // several launches: the first on the caller's stream, the others on side
+  // streams forked from it, all joined back before the call returns
+  std::lock_guard<std::mutex> lock(g_side_mutex);
+  SideStreams* ss = nullptr;
+  hipError_t e = side_streams(&ss, s);
+  if (e != hipSuccess)
+    return device_status(e, "kvq_decode_partial side streams (call kvq_decode_workspace_init before capturing)");
+  const int n_side = std::min<int>(kSideStreams, static_cast<int>(launches.size()) - 1);
+  if ((e = hipEventRecord(ss->fork, s)) != hipSuccess) return device_status(e, "kvq_decode_partial fork");
+  for (int i = 0; i < n_side; ++i)
+    if ((e = hipStreamWaitEvent(ss->s[i], ss->fork, 0)) != hipSuccess) return device_status(e, "kvq_decode_partial fork");
+  for (size_t j = 0; j < launches.size(); ++j) {
+    const Launch& l = launches[j];
+    hipStream_t st = j == 0 ? s : ss->s[(j - 1) % n_side];
+    if ((e = kvq::launch_decode_partial(l.a, l.kbits, l.vbits, l.d, l.n_splits, batch, st)) != hipSuccess)
+      return device_status(e, "kvq_decode_partial launch");
+  }
+  for (int i = 0; i < n_side; ++i) {
+    if ((e = hipEventRecord(ss->join[i], ss->s[i])) != hipSuccess) return device_status(e, "kvq_decode_partial join");
+    if ((e = hipStreamWaitEvent(s, ss->join[i], 0)) != hipSuccess) return device_status(e, "kvq_decode_partial join");
   }
   return ok();
 }
@@ -507,7 +584,7 @@ kvq_status kvq_decode_merge(const kvq_segment* segs, int32_t n_segs, int32_t bat
   const kvq_layout& L0 = *segs[0].layout;
   const int hq = L0.num_kv_heads * L0.group;
   const int slots = total_slots(segs, n_segs, batch, nullptr);
-  const size_t need = workspace_bytes(batch, hq, L0.num_kv_heads, L0.head_dim, slots, n_segs);
+  const size_t need = workspace_bytes(batch, hq, L0.num_kv_heads, L0.head_dim, slots);
   if (ws_bytes < need) return fail(KVQ_ERR_WORKSPACE, "kvq_decode_merge: workspace %zu < %zu bytes", ws_bytes, need);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   // With no split at all the merge kernel still runs and writes zero rows

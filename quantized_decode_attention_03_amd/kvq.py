@@ -331,11 +331,17 @@ def kvq_decode_merge(segments, batch, out, ws, stream=None):
 # ---------------------------------------------------------------------------
 
 class PreparedCall:
-    def __init__(self, fn, args, what, keep):
+    """A call with its arguments marshalled once. The stream is the last argument; if none was
+    given, torch's current stream is taken at each call (so a call prepared outside graph capture
+    launches on the capture stream inside it)."""
+
+    def __init__(self, fn, args, what, keep, follow_stream):
         self._fn, self._args, self._what, self._keep = fn, args, what, keep
+        self._follow = follow_stream
 
     def __call__(self):
-        st = self._fn(*self._args)
+        args = self._args[:-1] + (_stream(None),) if self._follow else self._args
+        st = self._fn(*args)
         if st != KVQ_OK:
             _check(st, self._what)
 
@@ -348,7 +354,8 @@ def prepare_quantize_append(layout, pool, block_table, start_pos, k, v, stream=N
             _dev_ptr(start_pos, (torch.int32,), "start_pos"), int(k.shape[1]),
             _dev_ptr(k, (torch.float32, torch.bfloat16), "k"), _dev_ptr(v, (torch.float32, torch.bfloat16), "v"),
             dt, _stream(stream))
-    return PreparedCall(lib().kvq_quantize_append, args, "kvq_quantize_append", (layout, pool, block_table, start_pos, k, v))
+    return PreparedCall(lib().kvq_quantize_append, args, "kvq_quantize_append",
+                        (layout, pool, block_table, start_pos, k, v), stream is None)
 
 
 def prepare_decode_partial(segments, q, ws, stream=None):
@@ -357,7 +364,7 @@ def prepare_decode_partial(segments, q, ws, stream=None):
     dt = KVQ_BF16 if q.dtype == torch.bfloat16 else KVQ_F32
     args = (segs, len(segments), int(q.shape[0]), _dev_ptr(q, (torch.float32, torch.bfloat16), "q"), dt,
             _dev_ptr(ws, (torch.uint8,), "ws"), ws.numel(), _stream(stream))
-    return PreparedCall(lib().kvq_decode_partial, args, "kvq_decode_partial", (segments, q, ws))
+    return PreparedCall(lib().kvq_decode_partial, args, "kvq_decode_partial", (segments, q, ws), stream is None)
 
 
 def prepare_decode_merge(segments, batch, out, ws, stream=None):
@@ -365,4 +372,4 @@ def prepare_decode_merge(segments, batch, out, ws, stream=None):
     segs = _segments(segments)
     args = (segs, len(segments), int(batch), _dev_ptr(out, (torch.float32,), "out"),
             _dev_ptr(ws, (torch.uint8,), "ws"), ws.numel(), _stream(stream))
-    return PreparedCall(lib().kvq_decode_merge, args, "kvq_decode_merge", (segments, out, ws))
+    return PreparedCall(lib().kvq_decode_merge, args, "kvq_decode_merge", (segments, out, ws), stream is None)

@@ -352,7 +352,55 @@ def test_decode_work_sharing_matches_fixed_order_and_oracle(monkeypatch):
     for o in outs:
         assert T.max_rel_err(o, expect) <= T.ATTN_TOL
         assert T.rel(o, fixed) < 1e-5
-    # the counters (the workspace's last words) are zero again
-    n_cnt = 3 * 2 * 2
+    # the counters (the workspace's last words: two per sequence, KV head and
+    # group of eight splits) are zero again
+    slots = ws.numel() // (3 * 8 * 130 * 4 + 3 * 2 * 2 * 4 // 8)
+    n_cnt = (slots // 8) * 3 * 2 * 2
     tail = ws[-4 * n_cnt:].view(torch.int32).cpu().numpy()
-    assert np.all(tail == 0)
+    assert slots % 8 == 0 and np.all(tail == 0)
+
+
+@pytest.mark.parametrize("deterministic", [True, False])
+def test_decode_step_in_hip_graph_matches_eager(monkeypatch, deterministic):
+    # append one token + partial + merge captured as one graph, over two
+    # segments of different precision (so the partial call forks onto side
+    # streams inside the capture). Replayed three times with eager work and a
+    # synchronisation between replays; every replay must match the eager step.
+    if deterministic:
+        monkeypatch.setenv("KVQ_DECODE_DETERMINISTIC", "1")
+    lens = [300, 1500]
+    L1, lay1, c1, r1, t1, k1, v1 = build_case(128, 128, 4, [4, 4], [4, 4], lens, seed=51)
+    L2, lay2, c2, r2, t2, k2, v2 = build_case(128, 128, 4, [2, 8], [2, 3], lens, seed=52, stride_extra=1)
+    q = torch.from_numpy(synth.bf16_round(np.random.default_rng(53).standard_normal((2, 8, 128)).astype(np.float32))).to(T.DEV).bfloat16()
+    new_lens = [n + 1 for n in lens]
+    segs = [c1.segment(lens), c2.segment(new_lens)]
+    nk = torch.from_numpy(synth.bf16_round(np.random.default_rng(54).standard_normal((2, 1, 2, 128)).astype(np.float32))).to(T.DEV).bfloat16()
+    start = torch.as_tensor(np.asarray(lens, np.int32), device=T.DEV)
+    ws = kvq.decode_workspace(segs, 2, T.DEV)
+    out = torch.empty((2, 8, 128), dtype=torch.float32, device=T.DEV)
+    app = kvq.prepare_quantize_append(L2, c2.pool, c2.table, start, nk, nk)
+    part = kvq.prepare_decode_partial(segs, q, ws)
+    merge = kvq.prepare_decode_merge(segs, 2, out, ws)
+
+    def step():
+        app()
+        part()
+        merge()
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(3):
+        out.zero_()
+        other = kvq.kvq_decode_attn(segs, q)  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        if deterministic:
+            assert torch.equal(out, eager) and torch.equal(other, eager)
+        else:
+            assert T.rel(out.cpu().numpy(), eager.cpu().numpy()) < 1e-5
+            assert T.rel(other.cpu().numpy(), eager.cpu().numpy()) < 1e-5

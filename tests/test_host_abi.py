@@ -153,8 +153,9 @@ def test_decode_argument_checks_need_no_device():
     n = ctypes.c_size_t(0)
     assert lib.kvq_decode_workspace_bytes(segs, 1, 16, ctypes.byref(n)) == kvq.KVQ_OK
     assert n.value > 16 * 32 * 130 * 4
-    # partials for every split slot, then two counters per (sequence, KV head)
-    assert (n.value - 16 * 8 * 2 * 4) % (16 * 32 * 130 * 4) == 0
+    # partials for every split slot, then two counters per (sequence, KV head, group of 8 splits)
+    per_slot = 16 * 32 * 130 * 4 + 16 * 8 * 2 * 4 // 8
+    assert n.value % per_slot == 0 and (n.value // per_slot) % 8 == 0
     # workspace initialisation: null or misaligned
     assert lib.kvq_decode_workspace_init(None, 64, None) == kvq.KVQ_ERR_ARG
     assert lib.kvq_decode_workspace_init(ctypes.c_void_p(0x4002), 64, None) == kvq.KVQ_ERR_ARG
