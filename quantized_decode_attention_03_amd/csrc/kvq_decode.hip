@@ -384,8 +384,8 @@ constexpr int kXcds = 8;  // accelerator dies of the chip; workgroups go round-r
 constexpr int kStaticEighths = KVQ_TUNE_STATIC_EIGHTHS;
 
 template <int KB, int VB, int D>
-__device__ __forceinline__ void load_group(const DecodeArgs& a, const uint8_t* pool, const int32_t* trow, int grp,
-                                           int p1, int seq_len, int64_t koff, int64_t voff, int lane,
+__device__ __forceinline__ void load_group(const DecodeArgs& a, const uint8_t* pool, const int32_t (&blks)[4],
+                                           int grp, int p1, int seq_len, int64_t koff, int64_t voff, int lane,
                                            GroupRaw<KB, VB, D>& g) {
   constexpr int RBK = D * KB / 8, RBV = D * VB / 8, QBYTES = RBK / 4;
   const int tslot = lane & 15, g4 = lane >> 4;
@@ -396,13 +396,13 @@ __device__ __forceinline__ void load_group(const DecodeArgs& a, const uint8_t* p
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp) {
     const int page = grp + pp;
-    const int32_t blk = trow[max(min(page, p1 - 1), 0)];
+    const int32_t blk = blks[pp];
     const bool ok = page < p1 && static_cast<uint32_t>(blk) < nblk;
     pv |= static_cast<uint32_t>(ok) << pp;
     boff[pp] = ok ? blk * a.block_bytes : 0;
   }
   const int kl = tslot * RBK + g4 * QBYTES;  // lane offsets (loop invariant)
-  const int vl = 4 * g4 * RBV + v_lane_offset<VB, D>(tslot);
+  const int vl = g4 * RBV + v_lane_offset<VB, D>(tslot);
   const int ml = tslot * kMetaBytes;
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp) load_kquarter<KB, D>(pool + boff[pp] + koff + kl, g.k[pp]);
@@ -422,15 +422,17 @@ __device__ __forceinline__ void load_group(const DecodeArgs& a, const uint8_t* p
     g.vs = mv.x; g.vmn = mv.y;
   }
   // value layout: lane = (column n = tslot, K-slot group g4); K-slot e of a page
-  // pair is slot 4*g4 + (e & 3) of page 2*pp2 + (e >> 2)
+  // pair is slot 4*(e & 3) + g4 of page 2*pp2 + (e >> 2). One load instruction
+  // (fixed e) then reads four consecutive token rows, whole cache lines that no
+  // other load of the group touches.
   g.vmask = 0;
 #pragma unroll
   for (int pp2 = 0; pp2 < 2; ++pp2) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int pg = 2 * pp2 + (e >> 2);
-      load_vtoken<VB, D>(pool + boff[pg] + voff + (e & 3) * RBV + vl, g.v[pp2][e]);
-      const bool ok = ((pv >> pg) & 1u) && (grp + pg) * kBlockTokens + 4 * g4 + (e & 3) < seq_len;
+      load_vtoken<VB, D>(pool + boff[pg] + voff + 4 * (e & 3) * RBV + vl, g.v[pp2][e]);
+      const bool ok = ((pv >> pg) & 1u) && (grp + pg) * kBlockTokens + 4 * (e & 3) + g4 < seq_len;
       g.vmask |= static_cast<uint32_t>(ok) << (8 * pp2 + e);
     }
   }
@@ -443,6 +445,9 @@ __device__ __forceinline__ void load_group(const DecodeArgs& a, const uint8_t* p
 #endif
 #ifndef KVQ_TUNE_WAVES128
 #define KVQ_TUNE_WAVES128 2
+#endif
+#ifndef KVQ_TUNE_QF_REGS
+#define KVQ_TUNE_QF_REGS 1
 #endif
 template <int KB, int VB, int D>
 struct PrefetchDepth {
@@ -533,6 +538,11 @@ __device__ __forceinline__ void compute_group(GroupRaw<KB, VB, D>& g, const u32x
       }
     }
   }
+  // This lane's token (page lane / 16, slot s = lane % 16) is K-slot (s / 4) of
+  // lane group s % 4 in the PV step: its weight goes to row position
+  // 16 * page + 4 * (s % 4) + s / 4, so each lane group reads its K-slots
+  // contiguously.
+  const int wpos = (lane & 0x30) | ((lane & 3) << 2) | ((lane >> 2) & 3);
   const float vs_eff = VMETA ? (g.valid ? g.vs : 0.f) : 1.f;
   const float vmid_eff = VMETA ? (g.valid ? g.vmn + static_cast<float>(1 << (VB - 1)) * g.vs : 0.f) : 0.f;
 #pragma unroll
@@ -553,12 +563,12 @@ __device__ __forceinline__ void compute_group(GroupRaw<KB, VB, D>& g, const u32x
       hb = half_bits(hh);
       lb = half_bits(static_cast<_Float16>(w - static_cast<float>(hh)));
     }
-    wt[0][i][lane] = static_cast<uint16_t>(hb);
-    wt[1][i][lane] = static_cast<uint16_t>(lb);
+    wt[0][i][wpos] = static_cast<uint16_t>(hb);
+    wt[1][i][wpos] = static_cast<uint16_t>(lb);
   }
   __syncthreads();
 
-  // PV: two 32-token steps; K-slot e of lane group g4 is token 4*g4 + (e & 3) of
+  // PV: two 32-token steps; K-slot e of lane group g4 is token 4*(e & 3) + g4 of
   // the step's page e >> 2
 #pragma unroll
   for (int pp2 = 0; pp2 < 2; ++pp2) {
@@ -681,35 +691,51 @@ void decode_partial_kernel(DecodeArgs a, const int32_t* __restrict__ table, uint
   constexpr int NB = DEPTH + 1;  // group buffers
   GroupRaw<KB, VB, D> gbuf[NB];
   // The wave's groups in order ("positions"): its static groups, then tail
-  // groups. A tail fetch is issued one position ahead of its use (when the
-  // previous position is loaded), so its latency hides behind a group.
-  int lpos = 0;                          // next position to load
+  // groups. Position q is resolved (its group known and its four block-table
+  // entries requested) one position before its pages are loaded, and the tail
+  // fetch that names it is issued one position before that, so neither the
+  // counter nor the table is waited for when the loads go out. Everything is
+  // a vector-memory access issued in program order, so each wait leaves the
+  // later loads outstanding: per load_next, the table entries of this position
+  // are read from registers, then the tail fetch, the table entries of the
+  // next position and the pages of this position go out.
+  int rpos = 0;                          // next position to resolve
   uint32_t inflight = 0;                 // lane 0: the outstanding tail fetch
   bool exhausted = pool_groups == 0;     // the tail is used up: no further fetches
+  int next_gid = NG;                     // group of the resolved position (>= NG: none)
+  int32_t next_tab = 0;                  // lane i < 4: table entry of its page i
   auto fetch = [&]() {
     uint32_t v = 0;
     if (lane == 0) v = atomicAdd(ctr, 1u);
     inflight = v;
   };
-  if (SG == 0 && !exhausted) fetch();
-  auto load_next = [&](GroupRaw<KB, VB, D>& g) {
+  auto resolve = [&]() {
     int gid = NG;
-    if (lpos < SG) {
-      gid = min(wx * SG + lpos, NG);
-      if (lpos == SG - 1 && !exhausted) fetch();
+    if (rpos < SG) {
+      gid = min(wx * SG + rpos, NG);
     } else if (!exhausted) {
       const uint32_t idx = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(inflight)));
-      if (idx < pool_groups) {
-        gid = pool0 + static_cast<int>(idx);
-        fetch();
-      } else {
-        exhausted = true;
-      }
+      if (idx < pool_groups) gid = pool0 + static_cast<int>(idx);
+      else exhausted = true;
     }
-    ++lpos;
-    gid = __builtin_amdgcn_readfirstlane(gid);  // wave-uniform: page addresses stay scalar
+    // the position after this one is a tail position: fetch its group now
+    if (rpos + 1 >= SG && !exhausted) fetch();
+    ++rpos;
+    next_gid = __builtin_amdgcn_readfirstlane(gid);  // wave-uniform: page addresses stay scalar
+    // (unconditional, clamped into the sequence's row like the page loads)
+    const int page = 4 * (g_lo + min(next_gid, NG)) + (lane & 3);
+    next_tab = trow[max(min(page, pages - 1), 0)];
+  };
+  if (SG == 0 && !exhausted) fetch();
+  resolve();
+  auto load_next = [&](GroupRaw<KB, VB, D>& g) {
+    const int gid = next_gid;
+    int32_t blks[4];
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) blks[pp] = __builtin_amdgcn_readlane(next_tab, pp);
+    resolve();
     g.gid = gid;
-    load_group<KB, VB, D>(a, pool, trow, 4 * (g_lo + gid), pages, seq_len, koff, voff, lane, g);
+    load_group<KB, VB, D>(a, pool, blks, 4 * (g_lo + gid), pages, seq_len, koff, voff, lane, g);
   };
 #pragma unroll
   for (int j = 0; j < DEPTH; ++j) load_next(gbuf[j]);
@@ -822,7 +848,7 @@ void decode_partial_kernel(DecodeArgs a, const int32_t* __restrict__ table, uint
   // buffers, the fragments and the PV accumulators against the 256
   // architectural registers, leaving room for the rest of the loop.
   constexpr int GROUP_WORDS = 4 * KF::kWords + 16 * VRaw<VB, D>::kWords + 4;
-  constexpr bool QF_REGS = 3 * GROUP_WORDS + 8 * NCK + 4 * NCV <= 180;
+  constexpr bool QF_REGS = KVQ_TUNE_QF_REGS && (DEPTH + 1) * GROUP_WORDS + 8 * NCK + 4 * NCV <= 180;
   u32x4_t qreg[NCK][2];
   if constexpr (QF_REGS) {
 #pragma unroll
