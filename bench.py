@@ -243,9 +243,11 @@ def build_decode_layers(args, kvq, torch, dev):
                               "layers back to back (each layer's cache evicted from the MALL by the others)",
                   "layers": args.layers, "batch": batch, "ctx": tokens}
         return layers, config, batch, total_bytes / args.layers, "decode_partial_kernel (3 segments)"
-    # default: Llama-3-8B-shaped 32k decode
+    # default: Llama-3-8B-shaped 32k decode (bf16_32k: the same shape with 16-bit rows, the unquantized
+    # baseline the 4-bit cache is compared with)
     batch, tokens = B, T
-    L = kvq.kvq_layout_init(HKV, G, D, HAD, [BITS_K] * HKV, [BITS_V] * HKV)
+    bk, bv = (16, 16) if args.workload == "bf16_32k" else (BITS_K, BITS_V)
+    L = kvq.kvq_layout_init(HKV, G, D, HAD, [bk] * HKV, [bv] * HKV)
     for l in range(args.layers):
         seed = SEED_BASE + l
         pool, table = make_pool(kvq, torch, dev, L, batch, tokens, seed)
@@ -255,6 +257,13 @@ def build_decode_layers(args, kvq, torch, dev):
         layers.append({"segs": [(L, pool, table, lens, tokens)], "q": q, "app": 0,
                        "new_k": k[:, T - 1:T].contiguous(), "new_v": v[:, T - 1:T].contiguous(), "pos": T - 1})
         del k, v
+    if args.workload == "bf16_32k":
+        args.dtype = "bf16"
+        config = {"workload": "bf16 paged decode baseline: " + WORKLOAD.replace("K4/V4 token-wise INT4", "bf16 K/V rows (rotated, no metadata)"),
+                  "layers": args.layers, "batch": B, "ctx": T, "kv_heads": HKV, "q_per_kv": G, "head_dim": D,
+                  "bits_k": 16, "bits_v": 16, "had_block": HAD}
+        return (layers, config, batch, decode_bytes(B, T, [16] * HKV, [16] * HKV) + B * HKV * G * D * 2,
+                "decode_partial_kernel<16,16,128>")
     config = {"workload": WORKLOAD, "layers": args.layers, "batch": B, "ctx": T, "kv_heads": HKV,
               "q_per_kv": G, "head_dim": D, "bits_k": BITS_K, "bits_v": BITS_V, "had_block": HAD}
     return layers, config, batch, bytes_per_layer(), "decode_partial_kernel<4,4,128>"
@@ -325,6 +334,8 @@ def run_decode(args, torch, dev, kvq):
     if args.graph:
         config = dict(config, launch="hip graph of the timed steps")
         extra["eager_tokens_per_s"] = round(batch * args.steps / eager_elapsed, 2)
+    if getattr(args, "dtype", None):
+        extra["dtype"] = args.dtype
     return {**extra,
         "value": round(batch * args.steps / elapsed, 2),
         "unit": "tokens/s",
@@ -403,6 +414,52 @@ def run_bulk_append(args, torch, dev, kvq):
     }
 
 
+def run_calib(args, torch, dev, kvq):
+    """Distortion calibration of the key quantizer: mean squared error at widths 2..6 over the K rows of a
+    16-sequence x 2048-token calibration batch, every layer and KV head pooled (one kvq_quant_mse call),
+    then the fit of alpha, beta."""
+    synth = synth_mod()
+    seqs, tokens = 16, 2048
+    ks = []
+    for l in range(args.layers):
+        k, _, _ = synth.llama_layer_torch(6000 + l, seqs, tokens, HKV, G, D, device=dev)
+        ks.append(k.reshape(-1, D))
+        del _
+    x = torch.cat(ks)
+    del ks
+    widths = [2, 3, 4, 5, 6]
+    out = torch.empty(len(widths), dtype=torch.float64, device=dev)
+    for _ in range(args.warmup):
+        kvq.kvq_quant_mse(x, HAD, widths, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        kvq.kvq_quant_mse(x, HAD, widths, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    alpha, beta, r2 = kvq.kvq_fit_distortion(widths, out.cpu().numpy())
+    rows = int(x.shape[0])
+    nbytes = rows * D * 2
+    achieved = nbytes / (us * 1e-6) / 1e9
+    return {
+        "metric": "distortion calibration: rows/s through rotate + quantize at 5 widths (kvq_quant_mse)",
+        "value": round(rows / (us * 1e-6), 1),
+        "unit": "rows/s",
+        "ms_per_step": round(us / 1e3, 4),
+        "higher_is_better": True,
+        "dtype": "f64",
+        "config": {"workload": f"key-quantizer calibration: {args.layers} layers x 8 kv heads x 16 sequences x "
+                               f"2048 tokens = {rows} bf16 rows of 128, hadamard 128, widths 2..6",
+                   "layers": args.layers, "rows": rows},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "quant_mse_kernel<128>", "avg_us": round(us, 3), "bytes_per_launch": nbytes},
+        "fit": {"alpha": alpha, "beta": beta, "r2": r2},
+    }
+
+
 def run_tiny(args, torch, dev, kvq):
     """The 1024-token tiny layer: append all tokens, then decode; latency per decode call."""
     synth = synth_mod()
@@ -444,7 +501,7 @@ def run_tiny(args, torch, dev, kvq):
     }
 
 
-WORKLOADS = ("llama32k", "mixed32k", "long131k", "bulk16k", "tiny")
+WORKLOADS = ("llama32k", "mixed32k", "long131k", "bulk16k", "tiny", "bf16_32k", "calib")
 
 
 def main():
@@ -456,7 +513,9 @@ def main():
     ap.add_argument("--workload", choices=WORKLOADS, default="llama32k",
                     help="llama32k (default, the headline): batch 16, 32k decode, K4/V4; mixed32k: per-head "
                          "bits from the planner; long131k: batch 1, three precision segments; bulk16k: "
-                         "prefill append; tiny: the 1024-token layer")
+                         "prefill append; tiny: the 1024-token layer; bf16_32k: the llama32k shape with "
+                         "16-bit rows (the unquantized baseline); calib: kvq_quant_mse over a key "
+                         "calibration set")
     ap.add_argument("--graph", action=argparse.BooleanOptionalAction, default=True,
                     help="decode workloads: after the eager timed steps (which give the partial kernel's "
                          "per-launch times), capture the same steps as one HIP graph and take the step rate "
@@ -490,6 +549,8 @@ def main():
         res = run_bulk_append(args, torch, dev, kvq)
     elif args.workload == "tiny":
         res = run_tiny(args, torch, dev, kvq)
+    elif args.workload == "calib":
+        res = run_calib(args, torch, dev, kvq)
     else:
         res = run_decode(args, torch, dev, kvq)
 
@@ -514,7 +575,7 @@ def main():
         "higher_is_better": res.pop("higher_is_better"),
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": res.pop("dtype", "f16"),
         "data": "synthetic",
         "config": res.pop("config"),
         "roofline": res.pop("roofline"),

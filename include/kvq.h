@@ -130,6 +130,49 @@ kvq_status kvq_plan_bits(int32_t n, const float* w, double alpha, double beta,
                          int32_t* bits_out, int64_t* leftover_out);
 
 /*
+ * Host. Least-squares fit of the distortion model D(b) = alpha * beta^-b to
+ * measured mean squared errors, as ln mse = ln alpha - b ln beta [RQ:
+ * Methodology 1 (the model) and 3 ("distortion calibration": the model is
+ * fitted per quantizer, not assumed); Pipeline step 2 (fit at 5 widths)].
+ * In:  n >= 2 points (host): widths[n] (not all equal), mse[n] > 0 finite.
+ * Out: *alpha_out, *beta_out; *r2_out = coefficient of determination of the
+ *      log-linear fit (may be null; 1 when every ln mse is equal).
+ * Errors: KVQ_ERR_ARG (nothing written).
+ */
+kvq_status kvq_fit_distortion(int32_t n, const int32_t* widths, const double* mse,
+                              double* alpha_out, double* beta_out, double* r2_out);
+
+/*
+ * Host. Ratio of the arithmetic to the geometric mean of the head
+ * sensitivities w[n] > 0: the factor by which the optimal per-head
+ * allocation lowers the weighted distortion against a uniform one, in the
+ * continuous model [RQ: Methodology 1 (AM/GM bound); Significance (the ratio
+ * as a predictor of when mixed precision pays)]. Computed in fp64.
+ * Errors: KVQ_ERR_ARG (n < 1, null pointers, a w[i] not positive).
+ */
+kvq_status kvq_amgm_ratio(int32_t n, const float* w, double* ratio_out);
+
+/*
+ * Device, async. Calibration measurement for kvq_fit_distortion: the mean
+ * squared error of this library's quantizer on `rows` rows of head_dim values
+ * at each of the n_widths widths [RQ: Methodology 3, distortion calibration].
+ * Each row x is rotated, x' = blockdiag(H_n) x, and quantized exactly as in
+ * kvq_quantize_append (fp32 {s, mn}, round half to even), at every width b:
+ * mse[w] = sum over rows and channels of (code * s + mn - x')^2 / (rows *
+ * head_dim), the errors squared and summed in fp64. Since the rotation is
+ * orthonormal this is also the error in the original basis (up to rounding).
+ * In:  x device [rows][head_dim] of dtype; widths host [n_widths], each in
+ *      1..8, 1 <= n_widths <= 8; had_block a power of two <= head_dim.
+ * Out: mse_out device double [n_widths]. The sums are combined with fp64
+ *      atomics, so the last bits may vary from call to call.
+ * Errors: KVQ_ERR_ARG (null pointers, rows < 1, bad widths or had_block),
+ * KVQ_ERR_UNSUPPORTED (head_dim not 64/128), KVQ_ERR_DEVICE.
+ */
+kvq_status kvq_quant_mse(const void* x, kvq_dtype dtype, int64_t rows, int32_t head_dim,
+                         int32_t had_block, const int32_t* widths, int32_t n_widths,
+                         double* mse_out, kvq_stream stream);
+
+/*
  * Host. Precision class of each of `total` tokens (position 0 = oldest) for a
  * log-spaced long-context schedule [LQ: Methodology 2]: 0 = the newest
  * `window` tokens (kept in bf16); 1 = the log-spaced subset; 2 = the rest.

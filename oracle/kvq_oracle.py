@@ -445,6 +445,28 @@ def amgm_ratio(w):
     return w.mean() / math.exp(np.log(w).mean())
 
 
+def quant_mse(x, n, widths):
+    """Mean squared quantization error of this quantizer at each width.
+
+    RateQuant page, Methodology 3 ("distortion calibration": the distortion
+    curve alpha * beta^-b is fitted per quantizer from measured errors) and
+    the pipeline's step 2 (errors at five widths). The quantizer is the one
+    this cache stores: each row of x ([..., d]) is rotated (rotate), quantized
+    token-wise (quantize_rows) and dequantized (dequantize_rows), all in
+    float32; the error of each element against the rotated value is taken in
+    float64 (exact for two float32 values), squared, and averaged over every
+    element. Returns one float per width.
+    """
+    xr = rotate(np.asarray(x, dtype=np.float32), n)
+    ref = xr.astype(np.float64)
+    out = []
+    for b in widths:
+        codes, s, mn = quantize_rows(xr, b)
+        err = dequantize_rows(codes, s, mn).astype(np.float64) - ref
+        out.append(float((err * err).sum() / err.size))
+    return out
+
+
 def fit_distortion(bits, mse):
     """Least-squares fit of ln MSE = ln alpha - b ln beta; returns (alpha, beta, r2)."""
     b = np.asarray(bits, dtype=np.float64)

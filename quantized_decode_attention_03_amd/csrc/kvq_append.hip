@@ -308,6 +308,110 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a, double r
   else append_rows<BV, D>(a, 1, rs_n);
 }
 
+// ---------------------------------------------------------------------------
+// Distortion calibration (RateQuant summary page, Methodology, "distortion
+// calibration" and pipeline step 2: the distortion model alpha * beta^-b is
+// fitted per quantizer from its measured mean squared error at a few widths).
+// Each row goes through exactly the append path's rotation and quantizer, at
+// every listed width b: x_hat = code * s + mn, and the error x_hat - x' of
+// each element is squared and summed in fp64 (the difference of two fp32
+// values and its square are exact there). Rows are spread over a fixed grid;
+// each workgroup adds its sums to out[] with one fp64 atomic per width.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void quant_mse_kernel(QuantMseArgs a, double rs_n) {
+  constexpr int LPR = 4, CPR = D / LPR, RPB = kThreads / LPR;
+  constexpr int NW = kMaxCalibWidths;
+  const int tid = threadIdx.x;
+  const int m = tid & (LPR - 1);
+  double acc[NW];
+#pragma unroll
+  for (int w = 0; w < NW; ++w) acc[w] = 0.0;
+  // every lane runs the same trips (the quad butterflies need whole rows)
+  for (int64_t base = static_cast<int64_t>(blockIdx.x) * RPB; base < a.rows;
+       base += static_cast<int64_t>(gridDim.x) * RPB) {
+    const int64_t row = base + tid / LPR;
+    const bool active = row < a.rows;
+    const int64_t r = active ? row : 0;
+    float x[CPR];
+    const size_t elem = static_cast<size_t>(r) * D + m * CPR;
+    if (a.x_bf16) {
+      const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + elem);
+#pragma unroll
+      for (int k = 0; k < CPR / 8; ++k) {
+        const uint4 w = p[k];
+        x[8 * k + 0] = bf16lo_to_f(w.x); x[8 * k + 1] = bf16hi_to_f(w.x);
+        x[8 * k + 2] = bf16lo_to_f(w.y); x[8 * k + 3] = bf16hi_to_f(w.y);
+        x[8 * k + 4] = bf16lo_to_f(w.z); x[8 * k + 5] = bf16hi_to_f(w.z);
+        x[8 * k + 6] = bf16lo_to_f(w.w); x[8 * k + 7] = bf16hi_to_f(w.w);
+      }
+    } else {
+      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + elem);
+#pragma unroll
+      for (int k = 0; k < CPR / 4; ++k) {
+        const float4 w = p[k];
+        x[4 * k + 0] = w.x; x[4 * k + 1] = w.y; x[4 * k + 2] = w.z; x[4 * k + 3] = w.w;
+      }
+    }
+    {
+      double xd[CPR];
+#pragma unroll
+      for (int j = 0; j < CPR; ++j) xd[j] = static_cast<double>(x[j]);
+      fwht_row_f64<CPR>(xd, m, a.had_block);
+#pragma unroll
+      for (int j = 0; j < CPR; ++j) x[j] = static_cast<float>(xd[j] * rs_n);
+    }
+    float mn = x[0], mx = x[0];
+#pragma unroll
+    for (int j = 1; j < CPR; ++j) { mn = fminf(mn, x[j]); mx = fmaxf(mx, x[j]); }
+    mn = fminf(mn, dpp_f32<kDppXor1>(mn));
+    mx = fmaxf(mx, dpp_f32<kDppXor1>(mx));
+    mn = fminf(mn, dpp_f32<kDppXor2>(mn));
+    mx = fmaxf(mx, dpp_f32<kDppXor2>(mx));
+    const float rng = mx - mn;
+    if (!active) continue;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      if (w >= a.n_widths) break;
+      const float qmax = static_cast<float>((1 << a.widths[w]) - 1);
+      float s = 0.f, inv = 0.f;
+      if (rng > 0.f) {
+        s = rng / qmax;
+        inv = qmax / rng;
+      }
+      double sum = 0.0;
+#pragma unroll
+      for (int j = 0; j < CPR; ++j) {
+        const float c = fminf(fmaxf(__builtin_rintf((x[j] - mn) * inv), 0.f), qmax);
+        const float xh = c * s + mn;  // a rounded product, then a rounded sum
+        const double e = static_cast<double>(xh) - static_cast<double>(x[j]);
+        sum += e * e;
+      }
+      acc[w] += sum;
+    }
+  }
+  // workgroup sums: the wave by xor shuffles, then the four waves through LDS
+  __shared__ double part[kThreads / 64][NW];
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    double v = acc[w];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    if ((tid & 63) == 0) part[tid >> 6][w] = v;
+  }
+  __syncthreads();
+  if (tid < a.n_widths) {
+    double v = 0.0;
+#pragma unroll
+    for (int k = 0; k < kThreads / 64; ++k) v += part[k][tid];
+    atomicAdd(a.out + tid, v);
+  }
+}
+
+__global__ void quant_mse_finish_kernel(double* out, int n, double count) {
+  if (static_cast<int>(threadIdx.x) < n) out[threadIdx.x] = out[threadIdx.x] / count;
+}
+
 // Read this lane's 8 stored values of one row back to fp32 (rotated basis).
 template <int BITS>
 __device__ __forceinline__ void load_row8(const uint8_t* rowp, const uint8_t* metap, int lane, float (&x)[8]) {
@@ -424,6 +528,23 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
     case 16: return launch_append_k<16>(a, rs, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_quant_mse(const QuantMseArgs& a, hipStream_t s) {
+  hipError_t e = launch_zero_words(reinterpret_cast<uint32_t*>(a.out), 2 * static_cast<size_t>(a.n_widths), s);
+  if (e != hipSuccess) return e;
+  constexpr int RPB = kThreads / 4;
+  const int64_t want = (a.rows + RPB - 1) / RPB;
+  const int blocks = static_cast<int>(want < 512 ? want : 512);
+  const double rs = 1.0 / std::sqrt(static_cast<double>(a.had_block));
+  if (a.d == 64) hipLaunchKernelGGL(quant_mse_kernel<64>, dim3(blocks), dim3(kThreads), 0, s, a, rs);
+  else if (a.d == 128) hipLaunchKernelGGL(quant_mse_kernel<128>, dim3(blocks), dim3(kThreads), 0, s, a, rs);
+  else return hipErrorInvalidValue;
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(quant_mse_finish_kernel, dim3(1), dim3(64), 0, s, a.out, a.n_widths,
+                     static_cast<double>(a.rows) * a.d);
+  return hipGetLastError();
 }
 
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t s) {

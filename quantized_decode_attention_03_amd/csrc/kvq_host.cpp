@@ -309,6 +309,78 @@ kvq_status kvq_plan_bits(int32_t n, const float* w, double alpha, double beta, c
   return ok();
 }
 
+kvq_status kvq_fit_distortion(int32_t n, const int32_t* widths, const double* mse, double* alpha_out,
+                              double* beta_out, double* r2_out) {
+  if (n < 2 || !widths || !mse || !alpha_out || !beta_out)
+    return fail(KVQ_ERR_ARG, "kvq_fit_distortion: null pointer or n < 2");
+  double mb = 0.0, my = 0.0;
+  for (int i = 0; i < n; ++i) {
+    if (!(mse[i] > 0.0) || !std::isfinite(mse[i]))
+      return fail(KVQ_ERR_ARG, "kvq_fit_distortion: mse[%d] must be positive and finite", i);
+    mb += widths[i];
+    my += std::log(mse[i]);
+  }
+  mb /= n;
+  my /= n;
+  // least squares of y = ln mse on b: slope = S_by / S_bb, intercept = my - slope * mb
+  double sbb = 0.0, sby = 0.0, syy = 0.0;
+  for (int i = 0; i < n; ++i) {
+    const double db = widths[i] - mb, dy = std::log(mse[i]) - my;
+    sbb += db * db;
+    sby += db * dy;
+    syy += dy * dy;
+  }
+  if (!(sbb > 0.0)) return fail(KVQ_ERR_ARG, "kvq_fit_distortion: the widths must not all be equal");
+  const double slope = sby / sbb, icpt = my - slope * mb;
+  double ssr = 0.0;
+  for (int i = 0; i < n; ++i) {
+    const double e = std::log(mse[i]) - (icpt + slope * widths[i]);
+    ssr += e * e;
+  }
+  *alpha_out = std::exp(icpt);
+  *beta_out = std::exp(-slope);
+  if (r2_out) *r2_out = syy > 0.0 ? 1.0 - ssr / syy : 1.0;
+  return ok();
+}
+
+kvq_status kvq_amgm_ratio(int32_t n, const float* w, double* ratio_out) {
+  if (n < 1 || !w || !ratio_out) return fail(KVQ_ERR_ARG, "kvq_amgm_ratio: null pointer or n < 1");
+  double am = 0.0, lg = 0.0;
+  for (int i = 0; i < n; ++i) {
+    if (!(w[i] > 0.f) || !std::isfinite(w[i])) return fail(KVQ_ERR_ARG, "kvq_amgm_ratio: w[%d] must be positive", i);
+    am += w[i];
+    lg += std::log(static_cast<double>(w[i]));
+  }
+  *ratio_out = (am / n) / std::exp(lg / n);
+  return ok();
+}
+
+kvq_status kvq_quant_mse(const void* x, kvq_dtype dtype, int64_t rows, int32_t head_dim, int32_t had_block,
+                         const int32_t* widths, int32_t n_widths, double* mse_out, kvq_stream stream) {
+  if (!x || !widths || !mse_out) return fail(KVQ_ERR_ARG, "kvq_quant_mse: null pointer");
+  if (rows < 1) return fail(KVQ_ERR_ARG, "kvq_quant_mse: rows %lld < 1", static_cast<long long>(rows));
+  if (dtype != KVQ_F32 && dtype != KVQ_BF16) return fail(KVQ_ERR_ARG, "kvq_quant_mse: bad dtype %d", dtype);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(KVQ_ERR_UNSUPPORTED, "kvq_quant_mse: head_dim %d (built: 64, 128)", head_dim);
+  if (had_block < 1 || had_block > head_dim || (had_block & (had_block - 1)))
+    return fail(KVQ_ERR_ARG, "kvq_quant_mse: had_block %d must be a power of two in [1, head_dim]", had_block);
+  if (n_widths < 1 || n_widths > kvq::kMaxCalibWidths)
+    return fail(KVQ_ERR_ARG, "kvq_quant_mse: n_widths %d out of [1, %d]", n_widths, kvq::kMaxCalibWidths);
+  kvq::QuantMseArgs a{};
+  for (int i = 0; i < n_widths; ++i) {
+    if (widths[i] < 1 || widths[i] > 8) return fail(KVQ_ERR_ARG, "kvq_quant_mse: width %d out of [1, 8]", widths[i]);
+    a.widths[i] = widths[i];
+  }
+  a.x = x;
+  a.x_bf16 = dtype == KVQ_BF16;
+  a.rows = rows;
+  a.d = head_dim;
+  a.had_block = had_block;
+  a.n_widths = n_widths;
+  a.out = mse_out;
+  return device_status(kvq::launch_quant_mse(a, reinterpret_cast<hipStream_t>(stream)), "kvq_quant_mse");
+}
+
 kvq_status kvq_logquant_classes(int32_t total, int32_t window, int8_t* cls_out) {
   if (total < 0 || window < 1) return fail(KVQ_ERR_ARG, "kvq_logquant_classes: total < 0 or window < 1");
   if (total > 0 && !cls_out) return fail(KVQ_ERR_ARG, "kvq_logquant_classes: null output");

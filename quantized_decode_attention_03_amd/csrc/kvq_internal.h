@@ -63,6 +63,19 @@ struct DecodeArgs {
   float* part_ml;      // [batch][hq][total_slots][2]  (running max in log2 units, sum)
 };
 
+// Distortion calibration: rows [rows][d] of fp32 or bf16, rotated and
+// quantized at each listed width; squared errors summed into out[w].
+constexpr int kMaxCalibWidths = 8;
+struct QuantMseArgs {
+  const void* x;
+  int32_t x_bf16;
+  int64_t rows;
+  int32_t d, had_block;
+  int32_t n_widths;
+  int32_t widths[kMaxCalibWidths];
+  double* out;  // [n_widths]
+};
+
 struct MergeArgs {
   const float* part_o;
   const float* part_ml;
@@ -77,6 +90,8 @@ hipError_t launch_decode_partial(const DecodeArgs& a, int kbits, int vbits, int 
                                  int batch, hipStream_t s);
 hipError_t launch_decode_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_zero_words(uint32_t* p, size_t n_words, hipStream_t s);
+// Zeroes out[], accumulates the squared errors, then divides by rows * d.
+hipError_t launch_quant_mse(const QuantMseArgs& a, hipStream_t s);
 
 // Waves per SIMD the partial kernel for (kbits, vbits, d) is compiled to hold.
 int decode_partial_waves_per_simd(int kbits, int vbits, int d);

@@ -25,7 +25,7 @@ EXPORTED = [
     "kvq_abi_version", "kvq_status_str", "kvq_last_error", "kvq_layout_init", "kvq_plan_bits",
     "kvq_logquant_classes", "kvq_page_alloc", "kvq_quantize_append", "kvq_dequant",
     "kvq_decode_workspace_bytes", "kvq_decode_workspace_init", "kvq_decode_attn", "kvq_decode_partial",
-    "kvq_decode_merge",
+    "kvq_decode_merge", "kvq_fit_distortion", "kvq_amgm_ratio", "kvq_quant_mse",
 ]
 
 
@@ -82,6 +82,9 @@ def lib():
     L.kvq_layout_init.argtypes = [ctypes.POINTER(KvqLayout)]
     L.kvq_plan_bits.argtypes = [i32, vp, ctypes.c_double, ctypes.c_double, vp, i32, i64, vp, vp]
     L.kvq_logquant_classes.argtypes = [i32, i32, vp]
+    L.kvq_fit_distortion.argtypes = [i32, vp, vp, vp, vp, vp]
+    L.kvq_amgm_ratio.argtypes = [i32, vp, vp]
+    L.kvq_quant_mse.argtypes = [vp, ctypes.c_int, i64, i32, i32, vp, i32, vp, vp]
     L.kvq_page_alloc.argtypes = [vp, i32, vp, i32, vp, vp, vp, i32]
     L.kvq_quantize_append.argtypes = [ctypes.POINTER(KvqLayout), vp, i64, vp, i32, i32, vp, i32, vp, vp,
                                       ctypes.c_int, vp]
@@ -173,6 +176,26 @@ def kvq_plan_bits(w, alpha, beta, ladder, budget_bits, allow_leftover=False):
     return out, left.value
 
 
+def kvq_fit_distortion(widths, mse):
+    """Fit D(b) = alpha * beta^-b to measured MSEs; returns (alpha, beta, r2)."""
+    widths = np.ascontiguousarray(widths, dtype=np.int32)
+    mse = np.ascontiguousarray(mse, dtype=np.float64)
+    if widths.shape != mse.shape or widths.ndim != 1:
+        raise ValueError("widths and mse must be 1-D of equal length")
+    out = np.zeros(3, dtype=np.float64)
+    _check(lib().kvq_fit_distortion(int(widths.shape[0]), _np_ptr(widths), _np_ptr(mse), _np_ptr(out[0:]),
+                                    _np_ptr(out[1:]), _np_ptr(out[2:])), "kvq_fit_distortion")
+    return float(out[0]), float(out[1]), float(out[2])
+
+
+def kvq_amgm_ratio(w):
+    """Arithmetic over geometric mean of the sensitivities w."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    r = ctypes.c_double(0.0)
+    _check(lib().kvq_amgm_ratio(int(w.shape[0]), _np_ptr(w), ctypes.byref(r)), "kvq_amgm_ratio")
+    return r.value
+
+
 def kvq_logquant_classes(total, window):
     out = np.zeros(total, dtype=np.int8)
     _check(lib().kvq_logquant_classes(int(total), int(window), _np_ptr(out)), "kvq_logquant_classes")
@@ -243,6 +266,25 @@ def kvq_dequant(layout, pool, block_table, seq, pos0, n, rotated=True, k_out=Non
         _dev_ptr(v_out, (torch.float32,), "v_out"), _stream(stream))
     _check(st, "kvq_dequant")
     return k_out, v_out
+
+
+def kvq_quant_mse(x, had_block, widths, out=None, stream=None):
+    """Mean squared quantization error of the rows of x ([..., d], fp32 or bf16, on the GPU) at each width;
+    returns a float64 GPU tensor [len(widths)]."""
+    import torch
+    widths = np.ascontiguousarray(widths, dtype=np.int32)
+    d = int(x.shape[-1])
+    rows = x.numel() // d if d else 0
+    if out is None:
+        out = torch.empty(int(widths.shape[0]), dtype=torch.float64, device=x.device)
+    if tuple(out.shape) != (int(widths.shape[0]),):
+        raise ValueError("out must be [len(widths)]")
+    dt = KVQ_BF16 if x.dtype == torch.bfloat16 else KVQ_F32
+    st = lib().kvq_quant_mse(_dev_ptr(x, (torch.float32, torch.bfloat16), "x"), dt, int(rows), d, int(had_block),
+                             _np_ptr(widths), int(widths.shape[0]), _dev_ptr(out, (torch.float64,), "out"),
+                             _stream(stream))
+    _check(st, "kvq_quant_mse")
+    return out
 
 
 class Segment:

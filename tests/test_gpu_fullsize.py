@@ -1,4 +1,4 @@
-"""Parity at the full sizes of the five workloads, on sampled outputs.
+"""Parity at the full sizes of the five workloads and the bf16 baseline, on sampled outputs.
 
 Each test fills the whole cache on the GPU through the C ABI and decodes it
 in the launch configuration the benchmark times (default split planner, work
@@ -112,6 +112,17 @@ def test_llama_32k_decode_full_size():
     out = decode_units(L, pool, table_t, batch, tokens, q)
     assert np.all(np.isfinite(out))
     run_units(L, pool, table, out, k, v, q, [(0, 0), (7, 3), (15, 7), (9, 5)], seed=1)
+
+
+def test_bf16_32k_baseline_decode_full_size():
+    """The unquantized baseline at the 32k shape: bf16 rows (rotated, no metadata), batch 16, one layer."""
+    batch, tokens, hkv, group, d = 16, 32768, 8, 4, 128
+    L = kvq.kvq_layout_init(hkv, group, d, 128, [16] * hkv, [16] * hkv)
+    k, v, q = synth.llama_layer_torch(2001, batch, tokens, hkv, group, d, device=T.DEV)
+    pool, table, table_t = full_cache(L, batch, tokens, k, v, seed=2001)
+    out = decode_units(L, pool, table_t, batch, tokens, q)
+    assert np.all(np.isfinite(out))
+    run_units(L, pool, table, out, k, v, q, [(0, 1), (11, 4), (15, 7)], seed=4)
 
 
 def test_mixed_precision_32k_decode_full_size():

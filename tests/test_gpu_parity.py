@@ -404,3 +404,49 @@ def test_decode_step_in_hip_graph_matches_eager(monkeypatch, deterministic):
         else:
             assert T.rel(out.cpu().numpy(), eager.cpu().numpy()) < 1e-5
             assert T.rel(other.cpu().numpy(), eager.cpu().numpy()) < 1e-5
+
+
+# ---------------------------------------------------------------------------
+# Distortion calibration (RateQuant page, Methodology 3): kvq_quant_mse
+# ---------------------------------------------------------------------------
+
+def calib_rows(rows, d, seed, in_bf16):
+    """Key-like rows: per-channel offsets and scales, a few x15 outlier channels, one constant row."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, d)).astype(np.float32) * rng.uniform(0.5, 2.0, d).astype(np.float32)
+    x += rng.standard_normal(d).astype(np.float32)
+    x[:, rng.choice(d, 4, replace=False)] *= 15
+    x[rows // 2] = 1.25
+    return synth.bf16_round(x) if in_bf16 else x
+
+
+@pytest.mark.parametrize("rows,d,n,in_bf16", [
+    (3000, 64, 64, False),     # 47 workgroups, a ragged last one
+    (3001, 128, 128, True),
+    (777, 128, 32, True),      # block-diagonal rotation
+    (500, 64, 1, False),       # no rotation
+    (40000, 128, 128, True),   # more rows than one pass of the grid
+])
+def test_quant_mse_matches_oracle(rows, d, n, in_bf16):
+    x = calib_rows(rows, d, seed=rows + d + n, in_bf16=in_bf16)
+    widths = [1, 2, 3, 4, 5, 6, 8]
+    xt = torch.from_numpy(x).to(T.DEV)
+    if in_bf16:
+        xt = xt.to(torch.bfloat16)
+    got = kvq.kvq_quant_mse(xt, n, widths).cpu().numpy()
+    expect = np.array(O.quant_mse(x, n, widths))
+    # same codes up to ties (where both roundings err by s/2); only the fp64 summation order differs
+    np.testing.assert_allclose(got, expect, rtol=1e-9, atol=0)
+
+
+def test_quant_mse_fit_gives_a_geometric_curve():
+    # Gaussian rows stay iid Gaussian under the rotation: ln MSE is linear in b, and the fitted
+    # beta falls in the range the RateQuant page reports (3.6 to 5.3)
+    rng = np.random.default_rng(8)
+    x = torch.from_numpy(rng.standard_normal((20000, 128)).astype(np.float32)).to(T.DEV)
+    widths = [2, 3, 4, 5, 6]
+    mse = kvq.kvq_quant_mse(x, 128, widths).cpu().numpy()
+    alpha, beta, r2 = kvq.kvq_fit_distortion(widths, mse)
+    assert r2 >= 0.99 and 3.6 <= beta <= 5.3
+    ea, eb, er2 = O.fit_distortion(widths, O.quant_mse(x.cpu().numpy(), 128, widths))
+    assert abs(beta / eb - 1) < 1e-9 and abs(alpha / ea - 1) < 1e-9

@@ -198,3 +198,72 @@ def test_append_and_dequant_argument_checks_need_no_device():
     assert st == kvq.KVQ_ERR_ARG
     st = lib.kvq_dequant(ctypes.byref(L), p, 4, p, 2, 0, 0, 0, 1, p, p, None)
     assert st == kvq.KVQ_OK
+
+
+# ---------------------------------------------------------------------------
+# Distortion calibration host functions (RateQuant page, Methodology 1 and 3)
+# ---------------------------------------------------------------------------
+
+def test_fit_distortion_matches_oracle():
+    rng = np.random.default_rng(41)
+    for _ in range(20):
+        widths = np.array([2, 3, 4, 5, 6], np.int32)
+        mse = 0.3 * 4.1 ** (-widths.astype(float)) * np.exp(0.05 * rng.standard_normal(5))
+        a, b, r2 = kvq.kvq_fit_distortion(widths, mse)
+        ea, eb, er2 = O.fit_distortion(widths, mse)
+        assert abs(a / ea - 1) < 1e-12 and abs(b / eb - 1) < 1e-12 and abs(r2 - er2) < 1e-12
+    a, b, r2 = kvq.kvq_fit_distortion([1, 4, 8], 2.5 * 3.7 ** -np.array([1.0, 4.0, 8.0]))
+    assert abs(a - 2.5) < 1e-12 and abs(b - 3.7) < 1e-12 and r2 > 1 - 1e-12
+
+
+def test_fit_distortion_errors():
+    for widths, mse in (([2], [0.1]), ([3, 3], [0.1, 0.2]), ([2, 3], [0.1, 0.0]), ([2, 3], [0.1, np.inf])):
+        with pytest.raises(kvq.KvqError) as e:
+            kvq.kvq_fit_distortion(widths, mse)
+        assert e.value.status == kvq.KVQ_ERR_ARG
+
+
+def test_amgm_ratio_matches_oracle():
+    w = synth.sensitivities(32, 8, seed=3).ravel().astype(np.float32)
+    assert abs(kvq.kvq_amgm_ratio(w) / O.amgm_ratio(w) - 1) < 1e-12
+    assert kvq.kvq_amgm_ratio(np.full(7, 2.5, np.float32)) == pytest.approx(1.0, abs=1e-15)
+    with pytest.raises(kvq.KvqError):
+        kvq.kvq_amgm_ratio(np.array([1.0, 0.0], np.float32))
+
+
+def test_planning_with_a_mismatched_beta_costs_distortion():
+    # RateQuant's mismatch failure mode in miniature: allocating with another
+    # quantizer's beta never beats allocating with the fitted one, under the
+    # fitted model; on these sensitivities it is strictly worse.
+    w = synth.sensitivities(32, 8, seed=33).ravel().astype(np.float32)
+    budget = 3 * w.shape[0]
+    ladder = [2, 3, 4, 8]
+    true_beta = 5.3
+    worse = 0
+    for wrong in (1.5, 2.0, 3.6, 8.0, 16.0):
+        good, _ = kvq.kvq_plan_bits(w, 1.0, true_beta, ladder, budget)
+        bad, _ = kvq.kvq_plan_bits(w, 1.0, wrong, ladder, budget)
+        cost = lambda bits: float(np.sum(w.astype(np.float64) * O.distortion(bits.astype(np.float64), 1.0, true_beta)))
+        assert cost(good) <= cost(bad) * (1 + 1e-12)
+        worse += cost(good) < cost(bad) * (1 - 1e-6)
+    assert worse >= 3
+
+
+def test_quant_mse_argument_checks_need_no_device():
+    lib = kvq.lib()
+    p = ctypes.c_void_p(0x1000)
+    widths = np.array([2, 3, 4], np.int32)
+    wp = widths.ctypes.data_as(ctypes.c_void_p)
+    st = lib.kvq_quant_mse(None, kvq.KVQ_F32, 10, 64, 64, wp, 3, p, None)
+    assert st == kvq.KVQ_ERR_ARG
+    st = lib.kvq_quant_mse(p, kvq.KVQ_F32, 0, 64, 64, wp, 3, p, None)
+    assert st == kvq.KVQ_ERR_ARG
+    st = lib.kvq_quant_mse(p, kvq.KVQ_F32, 10, 96, 32, wp, 3, p, None)
+    assert st == kvq.KVQ_ERR_UNSUPPORTED
+    st = lib.kvq_quant_mse(p, kvq.KVQ_F32, 10, 64, 48, wp, 3, p, None)
+    assert st == kvq.KVQ_ERR_ARG
+    st = lib.kvq_quant_mse(p, kvq.KVQ_F32, 10, 64, 64, wp, 9, p, None)
+    assert st == kvq.KVQ_ERR_ARG
+    bad = np.array([2, 9], np.int32)
+    st = lib.kvq_quant_mse(p, kvq.KVQ_F32, 10, 64, 64, bad.ctypes.data_as(ctypes.c_void_p), 2, p, None)
+    assert st == kvq.KVQ_ERR_ARG

@@ -447,10 +447,7 @@ def test_mse_decays_geometrically_on_gaussian_rows():
     rng = np.random.default_rng(20)
     x = O.rotate(rng.standard_normal((4000, 128)).astype(np.float32), 128)
     bits = [2, 3, 4, 5, 6]
-    mse = []
-    for b in bits:
-        codes, s, mn = O.quantize_rows(x, b)
-        mse.append(float(((O.dequantize_rows(codes, s, mn) - x) ** 2).mean()))
+    mse = O.quant_mse(x, 1, bits)  # x is already rotated: n = 1 leaves it as it is
     alpha, beta, r2 = O.fit_distortion(bits, mse)
     assert r2 >= 0.99 and 3.6 <= beta <= 5.3
     # uniform-quantizer closed form MSE ~ E[(mx-mn)^2] / (12 (2^b-1)^2), b >= 3
@@ -459,6 +456,48 @@ def test_mse_decays_geometrically_on_gaussian_rows():
         if b >= 3:
             pred = float((rng2 ** 2).mean()) / (12 * (2 ** b - 1) ** 2)
             assert abs(m / pred - 1) < 0.10
+
+
+def test_quant_mse_hand_examples():
+    # [0, 1, 2, 3] at 1 bit: s = 3, codes 0, 0, 1, 1, errors 0, 1, 1, 0
+    assert O.quant_mse([[0, 1, 2, 3]], 1, [1, 2]) == [0.5, 0.0]
+    # a constant row dequantizes to its minimum exactly and adds no error, but counts in the mean
+    assert O.quant_mse([[0, 1, 2, 3], [5, 5, 5, 5]], 1, [1]) == [0.25]
+    # with rotation (n = 2): [3, 1, 0, 0] -> [2 sqrt2, sqrt2, 0, 0]; at 1 bit the middle value is a
+    # tie (u = 0.5) that rounds to the even code 0, so the only error is sqrt2 on one of 4 elements
+    (m,) = O.quant_mse([[3, 1, 0, 0]], 2, [1])
+    assert abs(m - 0.5) < 1e-6
+
+
+def test_quant_mse_equals_nearest_grid_point_error():
+    # brute force: the error of each element is its distance to the nearest of the row's 2^b grid
+    # points k*s + mn (computed in float32 like the dequantizer)
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((300, 8)).astype(np.float32) * 3
+    xr = O.rotate(x, 8).astype(np.float32)
+    for b in (1, 2, 3, 5, 8):
+        q = 2 ** b - 1
+        mn = xr.min(1)
+        s = ((xr.max(1) - mn) / np.float32(q)).astype(np.float32)
+        k = np.arange(q + 1, dtype=np.float32)
+        grid = (k[None, :] * s[:, None]).astype(np.float32) + mn[:, None]
+        d2 = (grid[:, None, :].astype(np.float64) - xr[:, :, None].astype(np.float64)) ** 2
+        brute = float(d2.min(axis=2).mean())
+        (m,) = O.quant_mse(x, 8, [b])
+        assert abs(m - brute) <= 1e-6 * brute
+
+
+def test_quant_mse_is_the_error_in_the_original_basis_too():
+    rng = np.random.default_rng(32)
+    x = rng.standard_normal((200, 64)).astype(np.float32)
+    for n in (4, 64):
+        xr = O.rotate(x, n)
+        for b in (2, 4):
+            codes, s, mn = O.quantize_rows(xr, b)
+            back = O.unrotate(O.dequantize_rows(codes, s, mn), n)
+            orig = float(((back - x.astype(np.float64)) ** 2).mean())
+            (m,) = O.quant_mse(x, n, [b])
+            assert abs(m - orig) <= 1e-5 * orig
 
 
 # ---------------------------------------------------------------------------
