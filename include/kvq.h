@@ -185,6 +185,87 @@ kvq_status kvq_quant_mse(const void* x, kvq_dtype dtype, int64_t rows, int32_t h
 kvq_status kvq_logquant_classes(int32_t total, int32_t window, int8_t* cls_out);
 
 /*
+ * LogQuant's dynamic schedule [LQ: Methodology 2, "dynamic adjustment"]: the
+ * cache grows one token at a time and keeps three segments per sequence, the
+ * newest `window` tokens in a window segment (a ring: position p in slot
+ * p mod window), a middle-precision segment holding the log-spaced kept
+ * tokens and a low-precision segment holding the rest. A token at position p
+ * behind the window lies in span k (as in kvq_logquant_classes) and is kept
+ * when p + 1 is a multiple of 2^k, so as it ages into older spans it can only
+ * lose precision, and each span still keeps `window` tokens. At a length that
+ * is a multiple of 2^K (K the oldest span present) the classes equal
+ * kvq_logquant_classes. Appending token T moves token T - window out of the
+ * window into the middle segment and demotes at most one middle token,
+ * T - 2^k window with k = 1 + (number of trailing zero bits of T + 1), to the
+ * low segment; that token's middle slot is reused for the arriving one.
+ */
+typedef struct kvq_lq_state {
+  int32_t total;     /* tokens appended so far */
+  int32_t window;    /* window size W >= 1 */
+  int32_t n_mid;     /* tokens in the middle segment (slots 0 .. n_mid-1) */
+  int32_t n_low;     /* tokens in the low segment (slots 0 .. n_low-1) */
+  int32_t* mid_pos;  /* host [cap_mid]: the position each middle slot holds */
+  int32_t cap_mid;
+} kvq_lq_state;
+
+typedef struct kvq_lq_move {
+  int32_t win_slot;    /* window slot of the token leaving the window, -1: none */
+  int32_t mid_slot;    /* middle slot it is stored into */
+  int32_t demote_slot; /* middle slot of the token moving to the low segment, -1: none */
+  int32_t low_slot;    /* low slot it is stored into */
+  int32_t new_slot;    /* window slot that receives the appended token */
+} kvq_lq_move;
+
+/*
+ * Host. Classes (0 window, 1 middle, 2 low) of `total` tokens under the
+ * dynamic schedule above. Out: cls_out[total] (host).
+ * Errors: KVQ_ERR_ARG for total < 0, window < 1 or a null cls_out (total > 0).
+ */
+kvq_status kvq_logquant_dynamic_classes(int32_t total, int32_t window, int8_t* cls_out);
+
+/*
+ * Host. State of a sequence whose first `total` tokens are already stored by
+ * class (prefill): middle slots hold the class-1 positions in ascending
+ * order, n_low = the class-2 count. st->mid_pos and st->cap_mid must be set;
+ * the other fields are written.
+ * Errors: KVQ_ERR_ARG (bad sizes, null pointers), KVQ_ERR_CAPACITY (more
+ * middle tokens than cap_mid).
+ */
+kvq_status kvq_logquant_init(int32_t total, int32_t window, kvq_lq_state* st);
+
+/*
+ * Host. Plan the append of one token to each of `batch` sequences and
+ * advance their states: moves_out[b] says which stored rows move (for
+ * kvq_logquant_requant) and where the new token goes (for
+ * kvq_quantize_append into the window segment, start_pos = new_slot).
+ * Errors: KVQ_ERR_ARG (null pointers, a state whose mid_pos does not hold the
+ * token to demote); KVQ_ERR_CAPACITY (the middle segment needs a slot beyond
+ * cap_mid). On an error no state is changed.
+ */
+kvq_status kvq_logquant_advance(int32_t batch, kvq_lq_state* states, kvq_lq_move* moves_out);
+
+/*
+ * Device, async. Apply the row moves of one kvq_logquant_advance step
+ * [LQ: Methodology 2]. For every sequence b and KV head: the window row in
+ * slot win_slot is stored into middle slot mid_slot, and the middle row in
+ * demote_slot into low slot low_slot, each re-encoded at the destination
+ * head's bits from the values the source holds (bf16, or code * s + mn):
+ * token-wise min/max quantization in fp32, round half to even, exactly as
+ * kvq_quantize_append quantizes a rotated row. Every source row is read
+ * before any destination row is written, so a demoted token's slot may
+ * receive the arriving one in the same call. Run it before appending the new
+ * token, whose window slot is the exiting token's.
+ * In:  three segments (window, middle, low) of one geometry (heads, head_dim,
+ *      had_block); their block tables must map every slot named;
+ *      moves host [batch]. seq_lens and max_len of the segments are unused.
+ * Errors: KVQ_ERR_ARG (null pointers, geometry mismatch, a slot outside a
+ * table row), KVQ_ERR_DEVICE.
+ */
+kvq_status kvq_logquant_requant(const kvq_segment* window, const kvq_segment* mid,
+                                const kvq_segment* low, int32_t batch,
+                                const kvq_lq_move* moves, kvq_stream stream);
+
+/*
  * Host. Deterministic page allocation. For seq = 0..batch-1 in order, and
  * within a sequence for logical blocks ceil(old_len/16) .. ceil(new_len/16)-1
  * in order, set block_table[seq * table_stride + lb] = free_list[(*cursor)++].

@@ -509,3 +509,52 @@ def logquant_precision_map(total, window):
         if (r - start) % (1 << k) == 0:
             cls[pos] = 1
     return cls
+
+
+def logquant_dynamic_map(total, window):
+    """Precision class of each of `total` tokens when the cache grows one token
+    at a time (LogQuant technical summary, Methodology 2, "dynamic adjustment":
+    as tokens arrive, the older windows are thinned by half, keeping tokens at
+    regular intervals, so a kept token only ever loses precision).
+
+    Same window and spans as logquant_precision_map. In span k a token at
+    position p is kept (class 1) when (p + 1) is a multiple of 2^k: every
+    2^k-th token, counted on absolute positions. As the context grows a token
+    moves into older spans, where the condition only gets stricter, so its
+    class never returns to a higher precision. Span k (2^k W tokens) still
+    keeps W of them. When `total` is a multiple of 2^K, K the oldest span
+    present, this picks the same tokens as logquant_precision_map (there p is
+    kept when p = total - 1 modulo 2^k, which is -1 modulo 2^k).
+    """
+    cls = np.full(total, 2, dtype=np.int32)
+    for pos in range(total):
+        dist = total - 1 - pos
+        if dist < window:
+            cls[pos] = 0
+            continue
+        r = dist - window
+        k = 0
+        while r >= ((1 << (k + 1)) - 1) * window:
+            k += 1
+        if (pos + 1) % (1 << k) == 0:
+            cls[pos] = 1
+    return cls
+
+
+def logquant_transitions(total, window):
+    """Class changes when token `total` is appended to a cache of `total`
+    tokens: [(position, old class, new class)] over the existing positions,
+    read off the two dynamic maps (the new token itself enters class 0)."""
+    before = logquant_dynamic_map(total, window)
+    after = logquant_dynamic_map(total + 1, window)[:total]
+    changed = np.flatnonzero(before != after)
+    return [(int(p), int(before[p]), int(after[p])) for p in changed]
+
+
+def requantize_row(x_hat, b):
+    """Re-encode a stored row at b bits (LogQuant Methodology 2: a token that
+    leaves the window, or the kept subset, is stored again at the lower
+    precision). The source is what the cache holds, already in the rotated
+    basis: the bf16 window row, or the dequantized middle-precision row. It is
+    quantized token-wise exactly like a new row (quantize_rows)."""
+    return quantize_rows(np.asarray(x_hat, dtype=np.float32), b)

@@ -412,6 +412,148 @@ __global__ void quant_mse_finish_kernel(double* out, int n, double count) {
   if (static_cast<int>(threadIdx.x) < n) out[threadIdx.x] = out[threadIdx.x] / count;
 }
 
+// ---------------------------------------------------------------------------
+// LogQuant row moves (LogQuant summary page, Methodology 2, dynamic
+// adjustment): a token leaving the bf16 window is stored again at the middle
+// precision, and a middle token leaving the log-spaced subset at the low
+// precision. Workgroup (sequence, KV head), one wave per row: waves 0/1 move
+// the K/V window row to the middle segment, waves 2/3 the K/V middle row to
+// the low segment. Each source row is turned back into the values it holds
+// (bf16, or code * s + mn), then quantized like a new row: token-wise min and
+// max in fp32, s = (max - min) / (2^b - 1), codes rounded half to even. All
+// four rows are read before any is written (the arriving token may take the
+// demoted token's middle slot).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int64_t area_bytes(int d, int b) {
+  return static_cast<int64_t>(kBlockTokens) * (d * b / 8) + (b == 16 ? 0 : kBlockTokens * kMetaBytes);
+}
+
+// Byte offset of head h's K (half 0) or V (half 1) area: the K areas of all
+// heads come first, then the V areas.
+__device__ __forceinline__ int64_t area_offset(const RequantSeg& sg, int hkv, int d, int half, int h) {
+  int64_t off = 0;
+  for (int i = 0; i < hkv; ++i) {
+    if (half == 1) off += area_bytes(d, sg.bits[0][i]);
+    else if (i < h) off += area_bytes(d, sg.bits[0][i]);
+  }
+  if (half == 1)
+    for (int i = 0; i < h; ++i) off += area_bytes(d, sg.bits[1][i]);
+  return off;
+}
+
+// The row of slot `slot` of sequence `seq` in segment sg (null if unmapped).
+__device__ __forceinline__ uint8_t* seg_row(const RequantSeg& sg, int seq, int slot, int64_t area, int rb,
+                                           uint8_t** meta) {
+  const int page = slot / kBlockTokens;
+  if (page >= sg.table_stride) return nullptr;
+  const int64_t blk = sg.table[static_cast<int64_t>(seq) * sg.table_stride + page];
+  if (blk < 0 || blk >= sg.pool_blocks) return nullptr;
+  uint8_t* base = sg.pool + blk * sg.block_bytes + area;
+  const int t = slot - page * kBlockTokens;
+  *meta = base + kBlockTokens * rb + t * kMetaBytes;
+  return base + t * rb;
+}
+
+__device__ __forceinline__ float wave_min_f(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fminf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_max_f(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void requant_kernel(RequantArgs a) {
+  constexpr int CPL = D / 64;  // channels per lane
+  __shared__ uint8_t codes[4][D];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int si = blockIdx.x, h = blockIdx.y, seq = a.seq0 + si;
+  const int half = wave & 1;
+  const bool demote = wave >= 2;
+  const RequantSeg& src = a.seg[demote ? 1 : 0];
+  const RequantSeg& dst = a.seg[demote ? 2 : 1];
+  const int src_slot = a.moves[si][demote ? 2 : 0], dst_slot = a.moves[si][demote ? 3 : 1];
+  const int bs = src.bits[half][h], bd = dst.bits[half][h];
+  const int rbs = D * bs / 8, rbd = D * bd / 8;
+  uint8_t *smeta = nullptr, *dmeta = nullptr;
+  const uint8_t* srow = nullptr;
+  uint8_t* drow = nullptr;
+  if (src_slot >= 0 && dst_slot >= 0) {
+    srow = seg_row(src, seq, src_slot, area_offset(src, a.hkv, D, half, h), rbs, &smeta);
+    drow = seg_row(dst, seq, dst_slot, area_offset(dst, a.hkv, D, half, h), rbd, &dmeta);
+  }
+  const bool active = srow != nullptr && drow != nullptr;  // wave-uniform
+
+  // ---- the values the source row holds ----
+  float x[CPL];
+  if (active) {
+    if (bs == 16) {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c)
+        x[c] = bf16lo_to_f(reinterpret_cast<const uint16_t*>(srow)[lane * CPL + c]);
+    } else {
+      const float2 m = *reinterpret_cast<const float2*>(smeta);
+      const uint32_t mask = (1u << bs) - 1u;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const int o = (lane * CPL + c) * bs;
+        const int byte = o >> 3;
+        uint32_t v = srow[byte];
+        if (byte + 1 < rbs) v |= static_cast<uint32_t>(srow[byte + 1]) << 8;
+        const uint32_t code = (v >> (o & 7)) & mask;
+        x[c] = static_cast<float>(code) * m.x + m.y;  // a rounded product, then a rounded sum
+      }
+    }
+  }
+  __syncthreads();  // every source row has been read
+
+  // ---- quantize at the destination bits ----
+  float s = 0.f, mn = 0.f;
+  if (active) {
+    if (bd == 16) {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c)
+        reinterpret_cast<uint16_t*>(drow)[lane * CPL + c] = static_cast<uint16_t>(f_to_bf16_rne(x[c]));
+    } else {
+      float lmn = x[0], lmx = x[0];
+#pragma unroll
+      for (int c = 1; c < CPL; ++c) { lmn = fminf(lmn, x[c]); lmx = fmaxf(lmx, x[c]); }
+      mn = wave_min_f(lmn);
+      const float mx = wave_max_f(lmx);
+      const float qmax = static_cast<float>((1 << bd) - 1);
+      const float rng = mx - mn;
+      float inv = 0.f;
+      if (rng > 0.f) {
+        s = rng / qmax;
+        inv = qmax / rng;
+      }
+#pragma unroll
+      for (int c = 0; c < CPL; ++c)
+        codes[wave][lane * CPL + c] =
+            static_cast<uint8_t>(fminf(fmaxf(__builtin_rintf((x[c] - mn) * inv), 0.f), qmax));
+    }
+  }
+  __syncthreads();
+  // ---- pack the codes as the row's little-endian bit-stream and store ----
+  if (active && bd != 16) {
+    const int n_words = rbd / 4;
+    if (lane < n_words) {
+      const int w0 = 32 * lane;
+      uint64_t acc = 0;
+      for (int j = w0 / bd; j < D && j * bd < w0 + 32; ++j) {
+        const int o = j * bd - w0;
+        const uint64_t c = codes[wave][j];
+        acc |= o >= 0 ? (c << o) : (c >> (-o));
+      }
+      reinterpret_cast<uint32_t*>(drow)[lane] = static_cast<uint32_t>(acc);
+    }
+    if (lane == 0) *reinterpret_cast<float2*>(dmeta) = make_float2(s, mn);
+  }
+}
+
 // Read this lane's 8 stored values of one row back to fp32 (rotated basis).
 template <int BITS>
 __device__ __forceinline__ void load_row8(const uint8_t* rowp, const uint8_t* metap, int lane, float (&x)[8]) {
@@ -544,6 +686,15 @@ hipError_t launch_quant_mse(const QuantMseArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(quant_mse_finish_kernel, dim3(1), dim3(64), 0, s, a.out, a.n_widths,
                      static_cast<double>(a.rows) * a.d);
+  return hipGetLastError();
+}
+
+hipError_t launch_requant(const RequantArgs& a, int n_seqs, hipStream_t s) {
+  if (n_seqs <= 0 || a.hkv <= 0) return hipSuccess;
+  const dim3 grid(n_seqs, a.hkv);
+  if (a.d == 64) hipLaunchKernelGGL(requant_kernel<64>, grid, dim3(256), 0, s, a);
+  else if (a.d == 128) hipLaunchKernelGGL(requant_kernel<128>, grid, dim3(256), 0, s, a);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -379,6 +380,160 @@ kvq_status kvq_quant_mse(const void* x, kvq_dtype dtype, int64_t rows, int32_t h
   a.n_widths = n_widths;
   a.out = mse_out;
   return device_status(kvq::launch_quant_mse(a, reinterpret_cast<hipStream_t>(stream)), "kvq_quant_mse");
+}
+
+}  // extern "C"
+
+namespace {
+
+// Class (0 window, 1 middle, 2 low) of position pos at length total under the
+// dynamic schedule: span k of the distance r behind the window holds
+// 2^k <= r / W + 1 < 2^(k+1); a token there is kept when 2^k divides pos + 1.
+int lq_dynamic_class(int64_t pos, int64_t total, int64_t window) {
+  const int64_t dist = total - 1 - pos;
+  if (dist < window) return 0;
+  const uint64_t q = static_cast<uint64_t>((dist - window) / window + 1);
+  const int k = 63 - __builtin_clzll(q);
+  return ((pos + 1) & ((int64_t{1} << k) - 1)) == 0 ? 1 : 2;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_logquant_dynamic_classes(int32_t total, int32_t window, int8_t* cls_out) {
+  if (total < 0 || window < 1) return fail(KVQ_ERR_ARG, "kvq_logquant_dynamic_classes: total < 0 or window < 1");
+  if (total > 0 && !cls_out) return fail(KVQ_ERR_ARG, "kvq_logquant_dynamic_classes: null output");
+  for (int32_t p = 0; p < total; ++p) cls_out[p] = static_cast<int8_t>(lq_dynamic_class(p, total, window));
+  return ok();
+}
+
+kvq_status kvq_logquant_init(int32_t total, int32_t window, kvq_lq_state* st) {
+  if (!st || total < 0 || window < 1 || st->cap_mid < 0 || (st->cap_mid > 0 && !st->mid_pos))
+    return fail(KVQ_ERR_ARG, "kvq_logquant_init: null state, total < 0, window < 1 or bad mid_pos");
+  int32_t n_mid = 0, n_low = 0;
+  for (int32_t p = 0; p < total; ++p) {
+    const int c = lq_dynamic_class(p, total, window);
+    n_mid += c == 1;
+    n_low += c == 2;
+  }
+  if (n_mid > st->cap_mid)
+    return fail(KVQ_ERR_CAPACITY, "kvq_logquant_init: %d middle tokens exceed cap_mid %d", n_mid, st->cap_mid);
+  int32_t slot = 0;
+  for (int32_t p = 0; p < total; ++p)
+    if (lq_dynamic_class(p, total, window) == 1) st->mid_pos[slot++] = p;
+  st->total = total;
+  st->window = window;
+  st->n_mid = n_mid;
+  st->n_low = n_low;
+  return ok();
+}
+
+kvq_status kvq_logquant_advance(int32_t batch, kvq_lq_state* states, kvq_lq_move* moves_out) {
+  if (batch < 0 || (batch > 0 && (!states || !moves_out)))
+    return fail(KVQ_ERR_ARG, "kvq_logquant_advance: batch < 0 or null pointers");
+  // plan every sequence first, so that an error leaves every state unchanged
+  std::vector<kvq_lq_move> plan(batch);
+  for (int32_t b = 0; b < batch; ++b) {
+    const kvq_lq_state& st = states[b];
+    if (st.window < 1 || st.total < 0 || st.total == INT32_MAX || st.n_mid < 0 || st.n_low < 0 ||
+        st.n_mid > st.cap_mid || (st.cap_mid > 0 && !st.mid_pos))
+      return fail(KVQ_ERR_ARG, "kvq_logquant_advance: sequence %d has an invalid state", b);
+    const int64_t t = st.total, w = st.window;
+    kvq_lq_move m{-1, -1, -1, -1, static_cast<int32_t>(t % w)};
+    if (t >= w) {
+      const int32_t e = static_cast<int32_t>(t - w);
+      m.win_slot = static_cast<int32_t>(e % w);
+      // the token crossing into span k = 1 + tz(t + 1) drops out of the kept set there
+      const int k = 1 + __builtin_ctzll(static_cast<uint64_t>(t + 1));
+      const int64_t d = k < 62 ? t - (int64_t{1} << k) * w : -1;
+      if (d >= 0) {
+        int32_t s = -1;
+        for (int32_t i = 0; i < st.n_mid; ++i)
+          if (st.mid_pos[i] == d) { s = i; break; }
+        if (s < 0)
+          return fail(KVQ_ERR_ARG, "kvq_logquant_advance: sequence %d: position %lld is not in the middle segment",
+                      b, static_cast<long long>(d));
+        m.demote_slot = s;
+        m.low_slot = st.n_low;
+        m.mid_slot = s;
+      } else {
+        if (st.n_mid >= st.cap_mid)
+          return fail(KVQ_ERR_CAPACITY, "kvq_logquant_advance: sequence %d: middle segment full (%d slots)", b,
+                      st.cap_mid);
+        m.mid_slot = st.n_mid;
+      }
+    }
+    plan[b] = m;
+  }
+  for (int32_t b = 0; b < batch; ++b) {
+    kvq_lq_state& st = states[b];
+    const kvq_lq_move& m = plan[b];
+    if (m.win_slot >= 0) {
+      st.mid_pos[m.mid_slot] = st.total - st.window;
+      if (m.demote_slot >= 0) ++st.n_low;
+      else ++st.n_mid;
+    }
+    ++st.total;
+    moves_out[b] = m;
+  }
+  return ok();
+}
+
+kvq_status kvq_logquant_requant(const kvq_segment* window, const kvq_segment* mid, const kvq_segment* low,
+                                int32_t batch, const kvq_lq_move* moves, kvq_stream stream) {
+  const char* who = "kvq_logquant_requant";
+  if (!window || !mid || !low || batch < 0 || (batch > 0 && !moves))
+    return fail(KVQ_ERR_ARG, "%s: null pointers or batch < 0", who);
+  const kvq_segment* segs[3] = {window, mid, low};
+  kvq::RequantArgs a{};
+  for (int i = 0; i < 3; ++i) {
+    kvq_status st = check_layout_ready(segs[i]->layout, who);
+    if (st != KVQ_OK) return st;
+    const kvq_layout& L = *segs[i]->layout;
+    const kvq_layout& L0 = *window->layout;
+    if (L.num_kv_heads != L0.num_kv_heads || L.head_dim != L0.head_dim || L.had_block != L0.had_block)
+      return fail(KVQ_ERR_ARG, "%s: segment %d geometry differs from the window's", who, i);
+    if (!segs[i]->pool || !segs[i]->block_table || segs[i]->pool_blocks < 1 || segs[i]->table_stride < 1)
+      return fail(KVQ_ERR_ARG, "%s: segment %d needs a pool and a block table", who, i);
+    kvq::RequantSeg& sg = a.seg[i];
+    sg.pool = static_cast<uint8_t*>(const_cast<void*>(segs[i]->pool));
+    sg.pool_blocks = segs[i]->pool_blocks;
+    sg.block_bytes = L.block_bytes;
+    sg.table = segs[i]->block_table;
+    sg.table_stride = segs[i]->table_stride;
+    for (int h = 0; h < L.num_kv_heads; ++h) {
+      sg.bits[0][h] = static_cast<uint8_t>(L.bits_k[h]);
+      sg.bits[1][h] = static_cast<uint8_t>(L.bits_v[h]);
+    }
+  }
+  a.hkv = window->layout->num_kv_heads;
+  a.d = window->layout->head_dim;
+  for (int32_t b = 0; b < batch; ++b) {
+    const kvq_lq_move& m = moves[b];
+    const int32_t slots[4] = {m.win_slot, m.mid_slot, m.demote_slot, m.low_slot};
+    const int seg_of[4] = {0, 1, 1, 2};
+    for (int j = 0; j < 4; ++j)
+      if (slots[j] >= static_cast<int64_t>(segs[seg_of[j]]->table_stride) * KVQ_BLOCK_TOKENS)
+        return fail(KVQ_ERR_ARG, "%s: sequence %d slot %d outside the table row", who, b, slots[j]);
+    if ((m.win_slot >= 0) != (m.mid_slot >= 0) || (m.demote_slot >= 0) != (m.low_slot >= 0))
+      return fail(KVQ_ERR_ARG, "%s: sequence %d has a half-specified move", who, b);
+  }
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  for (int32_t b0 = 0; b0 < batch; b0 += kvq::kRequantMaxSeqs) {
+    const int n = std::min(batch - b0, kvq::kRequantMaxSeqs);
+    a.seq0 = b0;
+    for (int i = 0; i < n; ++i) {
+      const kvq_lq_move& m = moves[b0 + i];
+      a.moves[i][0] = m.win_slot;
+      a.moves[i][1] = m.mid_slot;
+      a.moves[i][2] = m.demote_slot;
+      a.moves[i][3] = m.low_slot;
+    }
+    const hipError_t e = kvq::launch_requant(a, n, s);
+    if (e != hipSuccess) return device_status(e, who);
+  }
+  return ok();
 }
 
 kvq_status kvq_logquant_classes(int32_t total, int32_t window, int8_t* cls_out) {

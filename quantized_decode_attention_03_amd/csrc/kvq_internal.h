@@ -76,6 +76,25 @@ struct QuantMseArgs {
   double* out;  // [n_widths]
 };
 
+// LogQuant row moves: per sequence, window row -> middle row and middle row
+// -> low row, re-encoded at the destination bits. Segment 0 window, 1
+// middle, 2 low; area offsets are recomputed in the kernel from the bits.
+constexpr int kRequantMaxSeqs = 64;
+struct RequantSeg {
+  uint8_t* pool;
+  int64_t pool_blocks;
+  int64_t block_bytes;
+  const int32_t* table;
+  int32_t table_stride;
+  uint8_t bits[2][KVQ_MAX_KV_HEADS];  // K, V bits per head
+};
+struct RequantArgs {
+  RequantSeg seg[3];
+  int32_t hkv, d;
+  int32_t seq0;                        // sequence index of moves[0]
+  int32_t moves[kRequantMaxSeqs][4];   // win_slot, mid_slot, demote_slot, low_slot
+};
+
 struct MergeArgs {
   const float* part_o;
   const float* part_ml;
@@ -92,6 +111,7 @@ hipError_t launch_decode_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_zero_words(uint32_t* p, size_t n_words, hipStream_t s);
 // Zeroes out[], accumulates the squared errors, then divides by rows * d.
 hipError_t launch_quant_mse(const QuantMseArgs& a, hipStream_t s);
+hipError_t launch_requant(const RequantArgs& a, int n_seqs, hipStream_t s);
 
 // Waves per SIMD the partial kernel for (kbits, vbits, d) is compiled to hold.
 int decode_partial_waves_per_simd(int kbits, int vbits, int d);

@@ -26,6 +26,7 @@ EXPORTED = [
     "kvq_logquant_classes", "kvq_page_alloc", "kvq_quantize_append", "kvq_dequant",
     "kvq_decode_workspace_bytes", "kvq_decode_workspace_init", "kvq_decode_attn", "kvq_decode_partial",
     "kvq_decode_merge", "kvq_fit_distortion", "kvq_amgm_ratio", "kvq_quant_mse",
+    "kvq_logquant_dynamic_classes", "kvq_logquant_init", "kvq_logquant_advance", "kvq_logquant_requant",
 ]
 
 
@@ -62,6 +63,21 @@ class KvqSegment(ctypes.Structure):
     ]
 
 
+class KvqLqState(ctypes.Structure):
+    _fields_ = [
+        ("total", ctypes.c_int32),
+        ("window", ctypes.c_int32),
+        ("n_mid", ctypes.c_int32),
+        ("n_low", ctypes.c_int32),
+        ("mid_pos", ctypes.POINTER(ctypes.c_int32)),
+        ("cap_mid", ctypes.c_int32),
+    ]
+
+
+class KvqLqMove(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int32) for name in ("win_slot", "mid_slot", "demote_slot", "low_slot", "new_slot")]
+
+
 _lib = None
 
 
@@ -85,6 +101,11 @@ def lib():
     L.kvq_fit_distortion.argtypes = [i32, vp, vp, vp, vp, vp]
     L.kvq_amgm_ratio.argtypes = [i32, vp, vp]
     L.kvq_quant_mse.argtypes = [vp, ctypes.c_int, i64, i32, i32, vp, i32, vp, vp]
+    L.kvq_logquant_dynamic_classes.argtypes = [i32, i32, vp]
+    L.kvq_logquant_init.argtypes = [i32, i32, ctypes.POINTER(KvqLqState)]
+    L.kvq_logquant_advance.argtypes = [i32, ctypes.POINTER(KvqLqState), ctypes.POINTER(KvqLqMove)]
+    L.kvq_logquant_requant.argtypes = [ctypes.POINTER(KvqSegment), ctypes.POINTER(KvqSegment),
+                                       ctypes.POINTER(KvqSegment), i32, ctypes.POINTER(KvqLqMove), vp]
     L.kvq_page_alloc.argtypes = [vp, i32, vp, i32, vp, vp, vp, i32]
     L.kvq_quantize_append.argtypes = [ctypes.POINTER(KvqLayout), vp, i64, vp, i32, i32, vp, i32, vp, vp,
                                       ctypes.c_int, vp]
@@ -202,6 +223,43 @@ def kvq_logquant_classes(total, window):
     return out
 
 
+def kvq_logquant_dynamic_classes(total, window):
+    out = np.zeros(total, dtype=np.int8)
+    _check(lib().kvq_logquant_dynamic_classes(int(total), int(window), _np_ptr(out)),
+           "kvq_logquant_dynamic_classes")
+    return out
+
+
+class LogQuantStates:
+    """Per-sequence states of the dynamic schedule (host memory owned here, handed to the C ABI)."""
+
+    def __init__(self, batch, window, cap_mid):
+        self.batch, self.window = int(batch), int(window)
+        self.mid_pos = np.zeros((self.batch, int(cap_mid)), dtype=np.int32)
+        self.states = (KvqLqState * self.batch)()
+        for b in range(self.batch):
+            st = self.states[b]
+            st.window, st.cap_mid = self.window, int(cap_mid)
+            st.mid_pos = self.mid_pos[b].ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        self.moves = (KvqLqMove * max(self.batch, 1))()
+
+    def init(self, b, total):
+        """Sequence b holds its first `total` tokens stored by class."""
+        _check(lib().kvq_logquant_init(int(total), self.window, ctypes.byref(self.states[b])), "kvq_logquant_init")
+
+    def advance(self):
+        """Plan the append of one token to every sequence; returns the moves (ctypes array, also kept)."""
+        _check(lib().kvq_logquant_advance(self.batch, self.states, self.moves), "kvq_logquant_advance")
+        return self.moves
+
+    def field(self, name):
+        return np.array([getattr(self.states[b], name) for b in range(self.batch)], dtype=np.int64)
+
+    def move_array(self):
+        return np.array([[getattr(self.moves[b], f) for f, _ in KvqLqMove._fields_] for b in range(self.batch)],
+                        dtype=np.int64)
+
+
 def kvq_page_alloc(free_list, cursor, old_len, new_len, block_table):
     """Fill block_table (host int32 [batch, stride], in place); returns the new cursor."""
     free_list = np.ascontiguousarray(free_list, dtype=np.int32)
@@ -285,6 +343,14 @@ def kvq_quant_mse(x, had_block, widths, out=None, stream=None):
                              _stream(stream))
     _check(st, "kvq_quant_mse")
     return out
+
+
+def kvq_logquant_requant(window, mid, low, batch, moves, stream=None):
+    """Apply one step's row moves (window -> middle, middle -> low) for `batch` sequences."""
+    segs = _segments([window, mid, low])
+    st = lib().kvq_logquant_requant(ctypes.byref(segs[0]), ctypes.byref(segs[1]), ctypes.byref(segs[2]),
+                                    int(batch), moves, _stream(stream))
+    _check(st, "kvq_logquant_requant")
 
 
 class Segment:

@@ -267,3 +267,69 @@ def test_quant_mse_argument_checks_need_no_device():
     bad = np.array([2, 9], np.int32)
     st = lib.kvq_quant_mse(p, kvq.KVQ_F32, 10, 64, 64, bad.ctypes.data_as(ctypes.c_void_p), 2, p, None)
     assert st == kvq.KVQ_ERR_ARG
+
+
+# ---------------------------------------------------------------------------
+# LogQuant dynamic schedule (LogQuant page, Methodology 2, dynamic adjustment)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("total,window", [(0, 4), (1, 1), (9, 2), (300, 16), (4095, 16), (5000, 128)])
+def test_logquant_dynamic_classes_match_oracle(total, window):
+    got = kvq.kvq_logquant_dynamic_classes(total, window)
+    assert np.array_equal(got.astype(np.int32), O.logquant_dynamic_map(total, window))
+
+
+@pytest.mark.parametrize("start,window", [(0, 4), (37, 4), (512, 16), (130, 1)])
+def test_logquant_advance_tracks_the_oracle_classes(start, window):
+    batch = 2
+    st = kvq.LogQuantStates(batch, window, cap_mid=4096)
+    for b in range(batch):
+        st.init(b, start + b)
+    for step in range(700):
+        totals = st.field("total")
+        before = [st.mid_pos[b, :st.states[b].n_mid].copy() for b in range(batch)]
+        st.advance()
+        moves = st.move_array()
+        for b in range(batch):
+            t = int(totals[b])
+            win_slot, mid_slot, demote_slot, low_slot, new_slot = moves[b].tolist()
+            assert new_slot == t % window
+            trans = O.logquant_transitions(t, window)
+            exits = [p for p, a, c in trans if (a, c) == (0, 1)]
+            demos = [p for p, a, c in trans if (a, c) == (1, 2)]
+            if exits:
+                assert win_slot == exits[0] % window and st.mid_pos[b, mid_slot] == exits[0]
+            else:
+                assert win_slot == -1 and mid_slot == -1
+            if demos:
+                assert before[b][demote_slot] == demos[0] and mid_slot == demote_slot
+            else:
+                assert demote_slot == -1 and low_slot == -1
+            cls = O.logquant_dynamic_map(t + 1, window)
+            n_mid = st.states[b].n_mid
+            assert sorted(st.mid_pos[b, :n_mid].tolist()) == np.flatnonzero(cls == 1).tolist()
+            assert st.states[b].n_low == int((cls == 2).sum()) and st.states[b].total == t + 1
+
+
+def test_logquant_init_and_advance_capacity_and_consistency_errors():
+    st = kvq.LogQuantStates(1, 2, cap_mid=3)
+    with pytest.raises(kvq.KvqError) as e:
+        st.init(0, 8)  # four middle tokens
+    assert e.value.status == kvq.KVQ_ERR_CAPACITY
+    st.init(0, 6)  # classes at 6 tokens: [2, 1, 1, 1, 0, 0], three middle tokens
+    assert st.states[0].n_mid == 3 and st.mid_pos[0, :3].tolist() == [1, 2, 3]
+    # token 6: token 4 leaves the window into the slot of token 2, which drops to the low segment
+    st.advance()
+    assert st.states[0].n_mid == 3 and sorted(st.mid_pos[0, :3].tolist()) == [1, 3, 4]
+    # token 7: no demotion (7 + 1 = 8 reaches no span yet), so a fourth middle slot is needed
+    with pytest.raises(kvq.KvqError) as e:
+        st.advance()
+    assert e.value.status == kvq.KVQ_ERR_CAPACITY and st.states[0].total == 7
+    # corrupt the middle slots: the token to demote is no longer there
+    st2 = kvq.LogQuantStates(1, 2, cap_mid=8)
+    st2.init(0, 8)
+    st2.mid_pos[0, :] = -5
+    with pytest.raises(kvq.KvqError) as e:
+        st2.advance()
+    assert e.value.status == kvq.KVQ_ERR_ARG
+    assert st2.states[0].total == 8

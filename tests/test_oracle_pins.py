@@ -517,3 +517,59 @@ def test_logquant_map_tiles_a_power_of_two_context():
         total = (2 ** m) * 128
         cls = O.logquant_precision_map(total, 128)
         assert (cls == 0).sum() == 128 and (cls == 1).sum() == m * 128
+
+
+def test_logquant_dynamic_map_hand_example():
+    # W = 2. At 8 tokens: window = positions 6, 7; span 0 (r = 0, 1) = positions 5, 4, all kept;
+    # span 1 (r = 2..5) = positions 3..0, kept when p + 1 is even: 3 and 1.
+    assert O.logquant_dynamic_map(8, 2).tolist() == [2, 1, 2, 1, 1, 1, 0, 0]
+    # One more token: 6 leaves the window into span 0 (kept); 4 moves into span 1 and, p + 1 = 5
+    # being odd, drops to the lowest class.
+    assert O.logquant_dynamic_map(9, 2).tolist() == [2, 1, 2, 1, 2, 1, 1, 0, 0]
+    assert O.logquant_transitions(8, 2) == [(4, 1, 2), (6, 0, 1)]
+
+
+def test_logquant_dynamic_map_equals_the_static_map_on_aligned_lengths():
+    # both keep W tokens per span; their anchorings agree when the length is a multiple of 2^K
+    for total, window in ((4096, 16), (131072, 128), (64, 4), (1024, 1)):
+        assert np.array_equal(O.logquant_dynamic_map(total, window), O.logquant_precision_map(total, window))
+    # and differ in general
+    assert not np.array_equal(O.logquant_dynamic_map(4095, 16), O.logquant_precision_map(4095, 16))
+
+
+def test_logquant_dynamic_steps_only_lower_precision_one_exit_one_demotion():
+    window = 8
+    prev = O.logquant_dynamic_map(0, window)
+    for total in range(0, 1200):
+        cur = O.logquant_dynamic_map(total + 1, window)
+        old = cur[:total]
+        assert np.all(old >= prev)  # classes only move towards lower precision
+        moves = [(p, int(prev[p]), int(old[p])) for p in np.flatnonzero(old != prev)]
+        exits = [m for m in moves if m[1:] == (0, 1)]
+        demotions = [m for m in moves if m[1:] == (1, 2)]
+        assert len(exits) == (1 if total >= window else 0) and len(exits) + len(demotions) == len(moves)
+        assert len(demotions) <= 1
+        if exits:
+            assert exits[0][0] == total - window
+        prev = cur
+    # spans fully inside the context keep exactly W tokens each
+    total = 8 * 1024 + 5
+    cls = O.logquant_dynamic_map(total, window)
+    r = total - 1 - np.arange(total) - window
+    for k in range(10):
+        lo, hi = ((1 << k) - 1) * window, ((1 << (k + 1)) - 1) * window
+        inside = (r >= lo) & (r < hi)
+        if hi <= r.max() + 1:
+            assert int((cls[inside] == 1).sum()) == window
+
+
+def test_requantize_row_is_the_plain_quantizer_on_the_stored_values():
+    rng = np.random.default_rng(51)
+    x = O.rotate(rng.standard_normal((40, 64)).astype(np.float32), 64)
+    codes4, s4, mn4 = O.quantize_rows(x, 4)
+    x4 = O.dequantize_rows(codes4, s4, mn4)
+    codes2, s2, mn2 = O.requantize_row(x4, 2)
+    # the re-encoded row's range is the 4-bit row's range, and its error against the 4-bit values
+    # is within half a 2-bit step
+    assert np.array_equal(mn2, x4.min(1)) and np.all(np.abs(O.dequantize_rows(codes2, s2, mn2) - x4)
+                                                     <= s2[:, None] / 2 * (1 + 1e-6) + 1e-7)
