@@ -460,6 +460,96 @@ def run_calib(args, torch, dev, kvq):
     }
 
 
+def run_long_dynamic(args, torch, dev, kvq):
+    """The 131k long-context decode grown token by token with LogQuant's dynamic adjustment: per step the
+    host plans the class changes once (kvq_logquant_advance, shared by every layer), then per layer the
+    moved rows are re-encoded (kvq_logquant_requant), the new token goes into the bf16 window ring, and the
+    three segments are decoded (partials + merge). Eager: the plan is made on the host every step."""
+    synth = synth_mod()
+    batch, tokens, window = 1, 131072, 128
+    extra = args.steps + args.warmup + 16
+    cls = kvq.kvq_logquant_dynamic_classes(tokens, window)
+    idx_all = [torch.from_numpy(np.flatnonzero(cls == c)).to(dev) for c in range(3)]
+    counts = [int(i.numel()) for i in idx_all]
+    caps = [window, counts[1] + extra, counts[2] + extra]
+    lens = [torch.full((batch,), counts[c], dtype=torch.int32, device=dev) for c in range(3)]
+    layers = []
+    total_bytes = 0
+    for l in range(args.layers):
+        k, v, q = synth.llama_layer_torch(4000 + l, batch, tokens + extra, HKV, G, D, device=dev)
+        segs = []
+        for c, bits in enumerate((16, 4, 2)):
+            L = kvq.kvq_layout_init(HKV, G, D, 32, [bits] * HKV, [bits] * HKV)
+            pool, table = make_pool(kvq, torch, dev, L, batch, caps[c], 40 + c + 10 * l)
+            # positions ascend within each class; the window's 128 positions fill ring slots p mod 128 = 0..127
+            kvq.kvq_quantize_append(L, pool, table, torch.zeros(batch, dtype=torch.int32, device=dev),
+                                    k[:, idx_all[c]].contiguous(), v[:, idx_all[c]].contiguous())
+            segs.append(kvq.Segment(L, pool, table, lens[c], caps[c]))
+            total_bytes += decode_bytes(batch, counts[c], [bits] * HKV, [bits] * HKV)
+        layers.append({"segs": segs, "q": q, "new_k": k[:, tokens:].contiguous(), "new_v": v[:, tokens:].contiguous()})
+        del k, v
+    st = kvq.LogQuantStates(batch, window, cap_mid=caps[1])
+    st.init(0, tokens)
+    ws = kvq.decode_workspace(layers[0]["segs"], batch, dev)
+    out = torch.empty((batch, HKV * G, D), dtype=torch.float32, device=dev)
+    prepared = [(kvq.prepare_decode_partial(ly["segs"], ly["q"], ws), kvq.prepare_decode_merge(ly["segs"], batch, out, ws))
+                for ly in layers]
+    n_ev = args.layers * args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(3)]
+
+    def step(i, record=None):
+        moves = st.advance()
+        mv = st.move_array()
+        # (fill kernels take the value as an argument, so no host buffer is shared between steps)
+        for c, n_c in enumerate((window, st.states[0].n_mid, st.states[0].n_low)):
+            lens[c].fill_(int(n_c))
+        start = torch.full((batch,), int(mv[0, 4]), dtype=torch.int32, device=dev)
+        for li, (ly, (part, merge)) in enumerate(zip(layers, prepared)):
+            if record is not None:
+                ev[0][record + li].record()
+            kvq.kvq_logquant_requant(ly["segs"][0], ly["segs"][1], ly["segs"][2], batch, moves)
+            w = ly["segs"][0]
+            kvq.kvq_quantize_append(w.layout, w.pool, w.block_table, start, ly["new_k"][:, i:i + 1],
+                                    ly["new_v"][:, i:i + 1])
+            if record is not None:
+                ev[1][record + li].record()
+            part()
+            if record is not None:
+                ev[2][record + li].record()
+            merge()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s_ in range(args.steps):
+        step(args.warmup + s_, record=s_ * args.layers)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    upd_us = 1e3 * float(np.mean([a.elapsed_time(b) for a, b in zip(ev[0], ev[1])]))
+    part_us = 1e3 * float(np.mean([a.elapsed_time(b) for a, b in zip(ev[1], ev[2])]))
+    layer_bytes = total_bytes / args.layers
+    achieved = layer_bytes / (part_us * 1e-6) / 1e9
+    return {
+        "value": round(batch * args.steps / elapsed, 2),
+        "unit": "tokens/s",
+        "ms_per_step": round(1e3 * elapsed / args.steps, 4),
+        "higher_is_better": True,
+        "config": {"workload": "long-context decode with LogQuant's dynamic adjustment: batch 1, ctx 131072 "
+                               "growing one token per step, 8 kv heads x 4 q heads, head_dim 128, hadamard 32; "
+                               "segments: bf16 window ring 128, log-spaced 4-bit subset, 2-bit rest; per layer "
+                               "per step: requant of the moved rows, append, partials, merge (eager)",
+                   "layers": args.layers, "batch": batch, "ctx": tokens},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode_partial_kernel (3 segments)", "avg_us": round(part_us, 3),
+                     "bytes_per_launch": int(layer_bytes)},
+        "update_us_per_layer": round(upd_us, 3),
+        "final_state": {"total": int(st.states[0].total), "n_mid": int(st.states[0].n_mid),
+                        "n_low": int(st.states[0].n_low)},
+    }
+
+
 def run_tiny(args, torch, dev, kvq):
     """The 1024-token tiny layer: append all tokens, then decode; latency per decode call."""
     synth = synth_mod()
@@ -501,7 +591,7 @@ def run_tiny(args, torch, dev, kvq):
     }
 
 
-WORKLOADS = ("llama32k", "mixed32k", "long131k", "bulk16k", "tiny", "bf16_32k", "calib")
+WORKLOADS = ("llama32k", "mixed32k", "long131k", "bulk16k", "tiny", "bf16_32k", "calib", "long131k_dyn")
 
 
 def main():
@@ -515,7 +605,8 @@ def main():
                          "bits from the planner; long131k: batch 1, three precision segments; bulk16k: "
                          "prefill append; tiny: the 1024-token layer; bf16_32k: the llama32k shape with "
                          "16-bit rows (the unquantized baseline); calib: kvq_quant_mse over a key "
-                         "calibration set")
+                         "calibration set; long131k_dyn: long131k grown one token per step with LogQuant's "
+                         "dynamic adjustment")
     ap.add_argument("--graph", action=argparse.BooleanOptionalAction, default=True,
                     help="decode workloads: after the eager timed steps (which give the partial kernel's "
                          "per-launch times), capture the same steps as one HIP graph and take the step rate "
@@ -551,6 +642,8 @@ def main():
         res = run_tiny(args, torch, dev, kvq)
     elif args.workload == "calib":
         res = run_calib(args, torch, dev, kvq)
+    elif args.workload == "long131k_dyn":
+        res = run_long_dynamic(args, torch, dev, kvq)
     else:
         res = run_decode(args, torch, dev, kvq)
 
