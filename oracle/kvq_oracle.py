@@ -134,8 +134,52 @@ def quantize_rows(xr, b):
     return codes, s, mn.astype(np.float32)
 
 
+def float16_down(x):
+    """The largest float16 value <= x (float32 input, within the float16 range)."""
+    x = np.asarray(x, dtype=np.float32)
+    h = x.astype(np.float16)  # round half to even
+    with np.errstate(over="ignore"):  # (the unused branch of the largest values)
+        return np.where(h.astype(np.float32) > x, np.nextafter(h, np.float16(-np.inf)), h).astype(np.float16)
+
+
+def float16_up(x):
+    """The smallest float16 value >= x."""
+    x = np.asarray(x, dtype=np.float32)
+    h = x.astype(np.float16)
+    with np.errstate(over="ignore"):
+        return np.where(h.astype(np.float32) < x, np.nextafter(h, np.float16(np.inf)), h).astype(np.float16)
+
+
+def quantize_rows_fp16_meta(xr, b):
+    """quantize_rows with the scale and minimum stored as float16.
+
+    The float16 pair has to bound the row for the codes to fit: the minimum
+    is rounded down, mn = fp16_down(min x), and the scale up,
+    s = fp16_up((max x - mn) / (2^b - 1)) (both operations in float32, so the
+    bound holds up to their rounding, and the clamp absorbs the rest). Then
+    inv = 1 / s and c = clamp(round_half_even((x - mn) * inv), 0, 2^b - 1),
+    in float32. A row with max x == mn gets s = 0 and codes 0. Values must lie
+    within the float16 range. Returns (codes, s, mn) with s, mn float16.
+    """
+    xr = np.asarray(xr, dtype=np.float32)
+    qmax = np.float32(2 ** b - 1)
+    mn = float16_down(xr.min(axis=-1))
+    rng = (xr.max(axis=-1) - mn.astype(np.float32)).astype(np.float32)
+    nonconst = rng > 0
+    s = np.where(nonconst, float16_up((np.where(nonconst, rng, np.float32(1)) / qmax).astype(np.float32)),
+                 np.float16(0)).astype(np.float16)
+    s32 = s.astype(np.float32)
+    inv = np.where(nonconst, np.float32(1) / np.where(nonconst, s32, np.float32(1)), np.float32(0)).astype(np.float32)
+    u = ((xr - mn.astype(np.float32)[..., None]).astype(np.float32) * inv[..., None]).astype(np.float32)
+    codes = np.clip(np.rint(u), 0, qmax).astype(np.uint8)
+    return codes, s, mn
+
+
 def dequantize_rows(codes, s, mn):
-    """x_hat = c * s + mn in float32 (a rounded product, then a rounded sum)."""
+    """x_hat = c * s + mn in float32 (a rounded product, then a rounded sum);
+    float16 metadata is widened to float32 (exactly) first."""
+    s = np.asarray(s).astype(np.float32)
+    mn = np.asarray(mn).astype(np.float32)
     prod = (codes.astype(np.float32) * s[..., None]).astype(np.float32)
     return (prod + mn[..., None]).astype(np.float32)
 
@@ -187,16 +231,17 @@ def row_bytes(d, b):
     return d * b // 8
 
 
-def segment_bytes(d, b):
-    """One head's K (or V) area in a block: 16 rows, then 16 metadata pairs.
+def segment_bytes(d, b, meta_bytes=META_BYTES):
+    """One head's K (or V) area in a block: 16 rows, then 16 metadata pairs
+    (meta_bytes each: 8 for a float32 pair, 4 for a float16 pair).
 
     b = 16 rows are stored as bf16 of the rotated row and carry no metadata.
     """
-    meta = 0 if b == 16 else BLOCK_TOKENS * META_BYTES
+    meta = 0 if b == 16 else BLOCK_TOKENS * meta_bytes
     return BLOCK_TOKENS * row_bytes(d, b) + meta
 
 
-def block_layout(num_kv_heads, d, bits_k, bits_v):
+def block_layout(num_kv_heads, d, bits_k, bits_v, meta_bytes=META_BYTES):
     """Byte offsets of every head's K and V area inside a block.
 
     Order: K head 0, K head 1, ..., then V head 0, V head 1, ...
@@ -206,17 +251,19 @@ def block_layout(num_kv_heads, d, bits_k, bits_v):
     k_off, v_off = [], []
     for h in range(num_kv_heads):
         k_off.append(off)
-        off += segment_bytes(d, bits_k[h])
+        off += segment_bytes(d, bits_k[h], meta_bytes)
     for h in range(num_kv_heads):
         v_off.append(off)
-        off += segment_bytes(d, bits_v[h])
+        off += segment_bytes(d, bits_v[h], meta_bytes)
     return k_off, v_off, off
 
 
 class Layout:
     """The cache geometry of one pool: heads, head_dim, Hadamard block, bits."""
 
-    def __init__(self, num_kv_heads, group, head_dim, had_block, bits_k, bits_v):
+    def __init__(self, num_kv_heads, group, head_dim, had_block, bits_k, bits_v, meta_fp16=False):
+        self.meta_fp16 = bool(meta_fp16)
+        self.meta_bytes = 4 if self.meta_fp16 else META_BYTES
         self.hkv = int(num_kv_heads)
         self.group = int(group)
         self.d = int(head_dim)
@@ -224,7 +271,7 @@ class Layout:
         self.bits_k = [int(b) for b in bits_k]
         self.bits_v = [int(b) for b in bits_v]
         self.k_off, self.v_off, self.block_bytes = block_layout(
-            self.hkv, self.d, self.bits_k, self.bits_v)
+            self.hkv, self.d, self.bits_k, self.bits_v, self.meta_bytes)
 
 
 # ---------------------------------------------------------------------------
@@ -254,16 +301,16 @@ def page_alloc(free_list, cursor, old_len, new_len, table):
 # Quantize-on-append into the paged pool
 # ---------------------------------------------------------------------------
 
-def encode_rows(x, n, b):
+def encode_rows(x, n, b, meta_fp16=False):
     """Rotate then quantize rows of x ([..., d]); returns (row bytes, s, mn).
 
     For b = 16 the stored row is the rotated row rounded to bf16 and s, mn are
-    None.
+    None. With meta_fp16 the float16-metadata quantizer is used.
     """
     xr = rotate(x, n)
     if b == 16:
         return float32_to_bf16_bits(xr).view(np.uint8).reshape(xr.shape[:-1] + (-1,)), None, None
-    codes, s, mn = quantize_rows(xr, b)
+    codes, s, mn = quantize_rows_fp16_meta(xr, b) if meta_fp16 else quantize_rows(xr, b)
     return pack_codes(codes, b), s, mn
 
 
@@ -280,7 +327,7 @@ def quantize_append(layout, pool, table, start_pos, k, v):
         for h in range(hkv):
             b = bits[h]
             rb = row_bytes(d, b)
-            rows, s, mn = encode_rows(x[:, :, h, :], layout.n, b)
+            rows, s, mn = encode_rows(x[:, :, h, :], layout.n, b, layout.meta_fp16)
             for seq in range(batch):
                 for i in range(n_new):
                     pos = int(start_pos[seq]) + i
@@ -289,9 +336,10 @@ def quantize_append(layout, pool, table, start_pos, k, v):
                     base = offs[h]
                     pool[blk, base + slot * rb: base + (slot + 1) * rb] = rows[seq, i]
                     if b != 16:
-                        mbase = base + BLOCK_TOKENS * rb + slot * META_BYTES
-                        meta = np.array([s[seq, i], mn[seq, i]], dtype=np.float32)
-                        pool[blk, mbase: mbase + META_BYTES] = meta.view(np.uint8)
+                        mb = layout.meta_bytes
+                        mbase = base + BLOCK_TOKENS * rb + slot * mb
+                        meta = np.array([s[seq, i], mn[seq, i]], dtype=np.float16 if layout.meta_fp16 else np.float32)
+                        pool[blk, mbase: mbase + mb] = meta.view(np.uint8)
 
 
 def read_rows(layout, pool, table_row, pos0, n, h, which):
@@ -308,8 +356,10 @@ def read_rows(layout, pool, table_row, pos0, n, h, which):
     if bits == 16:
         return bf16_bits_to_float32(raw.view(np.uint16).reshape(n, d))
     codes = unpack_codes(raw, bits, d)
-    mcols = base + BLOCK_TOKENS * rb + slot[:, None] * META_BYTES + np.arange(META_BYTES)[None, :]
-    meta = pool[blk[:, None], mcols].copy().view(np.float32).reshape(n, 2)
+    mb = layout.meta_bytes
+    mcols = base + BLOCK_TOKENS * rb + slot[:, None] * mb + np.arange(mb)[None, :]
+    meta = pool[blk[:, None], mcols].copy().view(np.float16 if layout.meta_fp16 else np.float32)
+    meta = meta.astype(np.float32).reshape(n, 2)
     return dequantize_rows(codes, meta[:, 0], meta[:, 1])
 
 
@@ -551,10 +601,12 @@ def logquant_transitions(total, window):
     return [(int(p), int(before[p]), int(after[p])) for p in changed]
 
 
-def requantize_row(x_hat, b):
+def requantize_row(x_hat, b, meta_fp16=False):
     """Re-encode a stored row at b bits (LogQuant Methodology 2: a token that
     leaves the window, or the kept subset, is stored again at the lower
     precision). The source is what the cache holds, already in the rotated
     basis: the bf16 window row, or the dequantized middle-precision row. It is
-    quantized token-wise exactly like a new row (quantize_rows)."""
-    return quantize_rows(np.asarray(x_hat, dtype=np.float32), b)
+    quantized token-wise exactly like a new row (quantize_rows, or
+    quantize_rows_fp16_meta for a destination with float16 metadata)."""
+    x_hat = np.asarray(x_hat, dtype=np.float32)
+    return quantize_rows_fp16_meta(x_hat, b) if meta_fp16 else quantize_rows(x_hat, b)

@@ -573,3 +573,75 @@ def test_requantize_row_is_the_plain_quantizer_on_the_stored_values():
     # is within half a 2-bit step
     assert np.array_equal(mn2, x4.min(1)) and np.all(np.abs(O.dequantize_rows(codes2, s2, mn2) - x4)
                                                      <= s2[:, None] / 2 * (1 + 1e-6) + 1e-7)
+
+
+# ---------------------------------------------------------------------------
+# Float16 metadata (the fp16 {s, mn} variant of the quantizer)
+# ---------------------------------------------------------------------------
+
+def test_float16_directed_rounding():
+    rng = np.random.default_rng(61)
+    x = (rng.standard_normal(20000) * np.exp(rng.uniform(-8, 8, 20000))).astype(np.float32)
+    x = x[np.abs(x) < 60000]
+    lo, hi = O.float16_down(x), O.float16_up(x)
+    assert np.all(lo.astype(np.float32) <= x) and np.all(hi.astype(np.float32) >= x)
+    # adjacent float16 values (or equal when x is one)
+    exact = lo.astype(np.float32) == x
+    assert np.all(hi[exact] == lo[exact])
+    assert np.all(np.nextafter(lo[~exact], np.float16(np.inf)) == hi[~exact])
+    for v in (0.0, 1.0, -2.5, 65504.0, 2.0 ** -24):
+        assert O.float16_down(np.float32(v)) == O.float16_up(np.float32(v)) == np.float16(v)
+
+
+def test_fp16_meta_hand_example():
+    # [0.1, 0.2, 0.3, 0.4] at 2 bits: mn rounds down to the float16 just below 0.1 (1638/16384),
+    # (0.4 - mn) / 3 = 0.1000081... rounds up to the next float16 above 0.1 (1639/16384);
+    # then (x - mn) / s = 0, 1.0, 2.0, 3.0 up to float32 rounding: codes 0, 1, 2, 3.
+    codes, s, mn = O.quantize_rows_fp16_meta(np.array([[0.1, 0.2, 0.3, 0.4]], np.float32), 2)
+    assert float(mn[0]) == 1638 / 16384 and float(s[0]) == 1639 / 16384
+    assert codes.tolist() == [[0, 1, 2, 3]]
+
+
+@pytest.mark.parametrize("b", [2, 3, 4, 8])
+def test_fp16_meta_bounds_and_error(b):
+    rng = np.random.default_rng(62 + b)
+    x = O.rotate((rng.standard_normal((3000, 64)) * rng.uniform(0.01, 30, (3000, 1))).astype(np.float32), 64)
+    codes, s, mn = O.quantize_rows_fp16_meta(x, b)
+    q = 2 ** b - 1
+    s64, mn64 = s.astype(np.float64), mn.astype(np.float64)
+    # the pair bounds the row up to the float32 rounding of (max - mn) / (2^b - 1)
+    assert np.all(mn64 <= x.min(1)) and np.all(s64 * q >= (x.max(1) - mn64) * (1 - 2.0 ** -22))
+    assert codes.max() <= q
+    err = np.abs(O.dequantize_rows(codes, s, mn).astype(np.float64) - x)
+    assert np.all(err <= s64[:, None] / 2 * (1 + 1e-5) + 1e-6 * np.abs(x).max())
+
+
+def test_fp16_meta_codes_are_the_nearest_grid_points():
+    rng = np.random.default_rng(63)
+    x = O.rotate(rng.standard_normal((400, 8)).astype(np.float32) * 4, 8).astype(np.float32)
+    for b in (2, 3, 4):
+        codes, s, mn = O.quantize_rows_fp16_meta(x, b)
+        k = np.arange(2 ** b, dtype=np.float32)
+        grid = (k[None, :] * s.astype(np.float32)[:, None]).astype(np.float32) + mn.astype(np.float32)[:, None]
+        d = np.abs(grid[:, None, :].astype(np.float64) - x[:, :, None])
+        best = d.min(axis=2)
+        mine = np.take_along_axis(d, codes[:, :, None].astype(np.int64), axis=2)[:, :, 0]
+        assert np.all(mine <= best + 1e-6 * (1 + np.abs(x)))
+
+
+def test_fp16_meta_layout_and_round_trip():
+    lay = O.Layout(2, 4, 64, 64, [4, 2], [3, 8], meta_fp16=True)
+    assert lay.meta_bytes == 4
+    assert lay.block_bytes == 16 * (32 + 4) + 16 * (16 + 4) + 16 * (24 + 4) + 16 * (64 + 4)
+    rng = np.random.default_rng(64)
+    k = rng.standard_normal((1, 20, 2, 64)).astype(np.float32)
+    v = rng.standard_normal((1, 20, 2, 64)).astype(np.float32)
+    table = np.array([[3, 0]], np.int32)
+    pool = np.zeros((4, lay.block_bytes), np.uint8)
+    O.quantize_append(lay, pool, table, np.array([0]), k, v)
+    dk, dv = O.dequant(lay, pool, table[0], 0, 20, rotated=True)
+    for h, (bk, bv) in enumerate(((4, 3), (2, 8))):
+        ck, sk, mk = O.quantize_rows_fp16_meta(O.rotate(k[0, :, h], 64), bk)
+        assert np.array_equal(dk[:, h], O.dequantize_rows(ck, sk, mk))
+        cv, sv, mv = O.quantize_rows_fp16_meta(O.rotate(v[0, :, h], 64), bv)
+        assert np.array_equal(dv[:, h], O.dequantize_rows(cv, sv, mv))
