@@ -164,10 +164,10 @@ def cpu_baseline(units, seed=77):
                       f"to the full step ({B * HKV * LAYERS} units)"}
 
 
-def decode_bytes(batch, tokens, bits_k, bits_v, d=D):
+def decode_bytes(batch, tokens, bits_k, bits_v, d=D, meta=8):
     """Algorithmic bytes the partial kernels read for one layer of one segment: codes + metadata
-    (none at 16 bits) per token and head, the page table, and q (bf16)."""
-    per_tok = sum(d * bk // 8 + (8 if bk != 16 else 0) + d * bv // 8 + (8 if bv != 16 else 0)
+    (`meta` bytes per row, none at 16 bits) per token and head, and the page table."""
+    per_tok = sum(d * bk // 8 + (meta if bk != 16 else 0) + d * bv // 8 + (meta if bv != 16 else 0)
                   for bk, bv in zip(bits_k, bits_v))
     return batch * tokens * per_tok + batch * (-(-tokens // 16)) * 4
 
@@ -247,7 +247,8 @@ def build_decode_layers(args, kvq, torch, dev):
     # baseline the 4-bit cache is compared with)
     batch, tokens = B, T
     bk, bv = (16, 16) if args.workload == "bf16_32k" else (BITS_K, BITS_V)
-    L = kvq.kvq_layout_init(HKV, G, D, HAD, [bk] * HKV, [bv] * HKV)
+    m16 = args.workload == "llama32k_m16"
+    L = kvq.kvq_layout_init(HKV, G, D, HAD, [bk] * HKV, [bv] * HKV, meta_fp16=m16)
     for l in range(args.layers):
         seed = SEED_BASE + l
         pool, table = make_pool(kvq, torch, dev, L, batch, tokens, seed)
@@ -257,6 +258,12 @@ def build_decode_layers(args, kvq, torch, dev):
         layers.append({"segs": [(L, pool, table, lens, tokens)], "q": q, "app": 0,
                        "new_k": k[:, T - 1:T].contiguous(), "new_v": v[:, T - 1:T].contiguous(), "pos": T - 1})
         del k, v
+    if m16:
+        config = {"workload": WORKLOAD.replace("K4/V4 token-wise INT4", "K4/V4 token-wise INT4 with float16 {s, mn}"),
+                  "layers": args.layers, "batch": B, "ctx": T, "kv_heads": HKV, "q_per_kv": G, "head_dim": D,
+                  "bits_k": BITS_K, "bits_v": BITS_V, "had_block": HAD, "meta": "fp16"}
+        return (layers, config, batch, decode_bytes(B, T, [BITS_K] * HKV, [BITS_V] * HKV, meta=4) + B * HKV * G * D * 2,
+                "decode_partial_kernel<4,4,128,fp16 meta>")
     if args.workload == "bf16_32k":
         args.dtype = "bf16"
         config = {"workload": "bf16 paged decode baseline: " + WORKLOAD.replace("K4/V4 token-wise INT4", "bf16 K/V rows (rotated, no metadata)"),
@@ -591,7 +598,8 @@ def run_tiny(args, torch, dev, kvq):
     }
 
 
-WORKLOADS = ("llama32k", "mixed32k", "long131k", "bulk16k", "tiny", "bf16_32k", "calib", "long131k_dyn")
+WORKLOADS = ("llama32k", "mixed32k", "long131k", "bulk16k", "tiny", "bf16_32k", "calib", "long131k_dyn",
+             "llama32k_m16")
 
 
 def main():
@@ -606,7 +614,7 @@ def main():
                          "prefill append; tiny: the 1024-token layer; bf16_32k: the llama32k shape with "
                          "16-bit rows (the unquantized baseline); calib: kvq_quant_mse over a key "
                          "calibration set; long131k_dyn: long131k grown one token per step with LogQuant's "
-                         "dynamic adjustment")
+                         "dynamic adjustment; llama32k_m16: llama32k with float16 metadata")
     ap.add_argument("--graph", action=argparse.BooleanOptionalAction, default=True,
                     help="decode workloads: after the eager timed steps (which give the partial kernel's "
                          "per-launch times), capture the same steps as one HIP graph and take the step rate "

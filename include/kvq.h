@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 1
+#define KVQ_ABI_VERSION 2
 #define KVQ_MAX_KV_HEADS 64
 #define KVQ_BLOCK_TOKENS 16
 
@@ -65,7 +65,11 @@ typedef struct hipStream_t_opaque* kvq_stream; /* a hipStream_t */
  *     codes[16][head_dim * b / 8]  then  meta[16] { float scale; float min; }
  * where code j of a row occupies bits [j*b, j*b+b) of the row's little-endian
  * bit-stream. For b = 16 the area is bf16[16][head_dim] of the rotated row
- * (round half to even) and has no meta. Per-head b may differ between heads
+ * (round half to even) and has no meta. With meta_fp16 = 1 the meta pairs are
+ * { _Float16 scale; _Float16 min; } (4 bytes): the minimum is rounded down
+ * and the scale up to float16 before the codes are computed from them, so
+ * the codes still fit and the error stays within half a step (the rotated
+ * values must lie within the float16 range). Per-head b may differ between heads
  * and between K and V [RQ: stage 3, K/V decoupling; MKV: more bits for keys];
  * uniform blocks follow [SAW: section 1, PagedAttention].
  */
@@ -76,6 +80,7 @@ typedef struct kvq_layout {
   int32_t head_dim;     /* d, 64 or 128 */
   int32_t had_block;    /* n, Hadamard block: power of two, 1 <= n <= d (1 = no rotation) */
   int32_t block_tokens; /* must be KVQ_BLOCK_TOKENS */
+  int32_t meta_fp16;    /* 0: float32 {s, mn} (8 B per row), 1: float16 {s, mn} (4 B per row) */
   int32_t bits_k[KVQ_MAX_KV_HEADS]; /* each in {2, 3, 4, 8, 16} */
   int32_t bits_v[KVQ_MAX_KV_HEADS];
   /* outputs of kvq_layout_init */
@@ -104,8 +109,8 @@ const char* kvq_last_error(void);
 
 /*
  * Host. Fill k_off, v_off and block_bytes from the inputs of *L.
- * Errors: KVQ_ERR_ARG for a null L, block_tokens != 16, num_kv_heads or group
- * out of range, a bit width outside {2,3,4,8,16}, had_block not a power of
+ * Errors: KVQ_ERR_ARG for a null L, block_tokens != 16, meta_fp16 not 0 or 1,
+ * num_kv_heads or group out of range, a bit width outside {2,3,4,8,16}, had_block not a power of
  * two or not dividing head_dim; KVQ_ERR_UNSUPPORTED for head_dim not 64/128.
  */
 kvq_status kvq_layout_init(kvq_layout* L);

@@ -248,11 +248,27 @@ __device__ __forceinline__ void append_rows(const AppendArgs& a, int half, doubl
     mn = fminf(mn, dpp_f32<kDppXor2>(mn));
     mx = fmaxf(mx, dpp_f32<kDppXor2>(mx));
     const float qmax = static_cast<float>((1 << BITS) - 1);
-    const float rng = mx - mn;
     float s = 0.f, inv = 0.f;
-    if (rng > 0.f) {
-      s = rng / qmax;  // IEEE division (correctly rounded)
-      inv = qmax / rng;
+    uint32_t meta_h = 0;  // float16 pair (s low, mn high)
+    if (a.meta16) {
+      // float16 metadata: the minimum rounded down and the scale up, so the
+      // pair still bounds the row; the codes are taken against them
+      const uint32_t mnh = f16_down(mn);
+      mn = f16_to_f(mnh);
+      const float rng = mx - mn;
+      uint32_t sh = 0;
+      if (rng > 0.f) {
+        sh = f16_up(rng / qmax);
+        s = f16_to_f(sh);
+        inv = 1.f / s;
+      }
+      meta_h = sh | (mnh << 16);
+    } else {
+      const float rng = mx - mn;
+      if (rng > 0.f) {
+        s = rng / qmax;  // IEEE division (correctly rounded)
+        inv = qmax / rng;
+      }
     }
     // ---- quantize and pack this lane's CPR codes ----
     float u[CPR];
@@ -293,9 +309,11 @@ __device__ __forceinline__ void append_rows(const AppendArgs& a, int half, doubl
           w[2] = static_cast<uint16_t>(g[1] >> 8);
         }
       }
-      if (m == 0)
-        *reinterpret_cast<float2*>(a.pool + blk * a.block_bytes + area + kBlockTokens * RB + slot * kMetaBytes) =
-            make_float2(s, mn);
+      if (m == 0) {
+        uint8_t* meta = a.pool + blk * a.block_bytes + area + kBlockTokens * RB;
+        if (a.meta16) *reinterpret_cast<uint32_t*>(meta + slot * 4) = meta_h;
+        else *reinterpret_cast<float2*>(meta + slot * kMetaBytes) = make_float2(s, mn);
+      }
     }
   }
 }
@@ -424,8 +442,8 @@ __global__ void quant_mse_finish_kernel(double* out, int n, double count) {
 // four rows are read before any is written (the arriving token may take the
 // demoted token's middle slot).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int64_t area_bytes(int d, int b) {
-  return static_cast<int64_t>(kBlockTokens) * (d * b / 8) + (b == 16 ? 0 : kBlockTokens * kMetaBytes);
+__device__ __forceinline__ int64_t area_bytes(int d, int b, int meta16) {
+  return static_cast<int64_t>(kBlockTokens) * (d * b / 8) + (b == 16 ? 0 : kBlockTokens * (meta16 ? 4 : kMetaBytes));
 }
 
 // Byte offset of head h's K (half 0) or V (half 1) area: the K areas of all
@@ -433,11 +451,11 @@ __device__ __forceinline__ int64_t area_bytes(int d, int b) {
 __device__ __forceinline__ int64_t area_offset(const RequantSeg& sg, int hkv, int d, int half, int h) {
   int64_t off = 0;
   for (int i = 0; i < hkv; ++i) {
-    if (half == 1) off += area_bytes(d, sg.bits[0][i]);
-    else if (i < h) off += area_bytes(d, sg.bits[0][i]);
+    if (half == 1) off += area_bytes(d, sg.bits[0][i], sg.meta16);
+    else if (i < h) off += area_bytes(d, sg.bits[0][i], sg.meta16);
   }
   if (half == 1)
-    for (int i = 0; i < h; ++i) off += area_bytes(d, sg.bits[1][i]);
+    for (int i = 0; i < h; ++i) off += area_bytes(d, sg.bits[1][i], sg.meta16);
   return off;
 }
 
@@ -450,7 +468,7 @@ __device__ __forceinline__ uint8_t* seg_row(const RequantSeg& sg, int seq, int s
   if (blk < 0 || blk >= sg.pool_blocks) return nullptr;
   uint8_t* base = sg.pool + blk * sg.block_bytes + area;
   const int t = slot - page * kBlockTokens;
-  *meta = base + kBlockTokens * rb + t * kMetaBytes;
+  *meta = base + kBlockTokens * rb + t * (sg.meta16 ? 4 : kMetaBytes);
   return base + t * rb;
 }
 
@@ -495,7 +513,13 @@ __global__ __launch_bounds__(256) void requant_kernel(RequantArgs a) {
       for (int c = 0; c < CPL; ++c)
         x[c] = bf16lo_to_f(reinterpret_cast<const uint16_t*>(srow)[lane * CPL + c]);
     } else {
-      const float2 m = *reinterpret_cast<const float2*>(smeta);
+      float2 m;
+      if (src.meta16) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(smeta);
+        m = make_float2(f16_to_f(w & 0xffffu), f16_to_f(w >> 16));
+      } else {
+        m = *reinterpret_cast<const float2*>(smeta);
+      }
       const uint32_t mask = (1u << bs) - 1u;
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
@@ -512,6 +536,7 @@ __global__ __launch_bounds__(256) void requant_kernel(RequantArgs a) {
 
   // ---- quantize at the destination bits ----
   float s = 0.f, mn = 0.f;
+  uint32_t meta_h = 0;
   if (active) {
     if (bd == 16) {
 #pragma unroll
@@ -524,11 +549,24 @@ __global__ __launch_bounds__(256) void requant_kernel(RequantArgs a) {
       mn = wave_min_f(lmn);
       const float mx = wave_max_f(lmx);
       const float qmax = static_cast<float>((1 << bd) - 1);
-      const float rng = mx - mn;
       float inv = 0.f;
-      if (rng > 0.f) {
-        s = rng / qmax;
-        inv = qmax / rng;
+      if (dst.meta16) {  // float16 metadata: minimum down, scale up (as in the append kernel)
+        const uint32_t mnh = f16_down(mn);
+        mn = f16_to_f(mnh);
+        const float rng = mx - mn;
+        uint32_t sh = 0;
+        if (rng > 0.f) {
+          sh = f16_up(rng / qmax);
+          s = f16_to_f(sh);
+          inv = 1.f / s;
+        }
+        meta_h = sh | (mnh << 16);
+      } else {
+        const float rng = mx - mn;
+        if (rng > 0.f) {
+          s = rng / qmax;
+          inv = qmax / rng;
+        }
       }
 #pragma unroll
       for (int c = 0; c < CPL; ++c)
@@ -550,13 +588,17 @@ __global__ __launch_bounds__(256) void requant_kernel(RequantArgs a) {
       }
       reinterpret_cast<uint32_t*>(drow)[lane] = static_cast<uint32_t>(acc);
     }
-    if (lane == 0) *reinterpret_cast<float2*>(dmeta) = make_float2(s, mn);
+    if (lane == 0) {
+      if (dst.meta16) *reinterpret_cast<uint32_t*>(dmeta) = meta_h;
+      else *reinterpret_cast<float2*>(dmeta) = make_float2(s, mn);
+    }
   }
 }
 
 // Read this lane's 8 stored values of one row back to fp32 (rotated basis).
 template <int BITS>
-__device__ __forceinline__ void load_row8(const uint8_t* rowp, const uint8_t* metap, int lane, float (&x)[8]) {
+__device__ __forceinline__ void load_row8(const uint8_t* rowp, const uint8_t* metap, bool meta16, int lane,
+                                          float (&x)[8]) {
   if constexpr (BITS == 16) {
     const uint4 w = *reinterpret_cast<const uint4*>(rowp + lane * 16);
     x[0] = bf16lo_to_f(w.x); x[1] = bf16hi_to_f(w.x);
@@ -576,7 +618,13 @@ __device__ __forceinline__ void load_row8(const uint8_t* rowp, const uint8_t* me
     } else {
       lo = c[0] | (static_cast<uint32_t>(c[1]) << 8) | (static_cast<uint32_t>(c[2]) << 16);
     }
-    const float2 meta = *reinterpret_cast<const float2*>(metap);
+    float2 meta;
+    if (meta16) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(metap);
+      meta = make_float2(f16_to_f(w & 0xffffu), f16_to_f(w >> 16));
+    } else {
+      meta = *reinterpret_cast<const float2*>(metap);
+    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       uint32_t code;
@@ -607,7 +655,8 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(DequantArgs a, float 
   float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (ok) {
     const uint8_t* base = a.pool + blk * a.block_bytes + area;
-    load_row8<BITS>(base + slot * RB, base + kBlockTokens * RB + slot * kMetaBytes, lane, x);
+    load_row8<BITS>(base + slot * RB, base + kBlockTokens * RB + slot * (a.meta16 ? 4 : kMetaBytes), a.meta16 != 0,
+                    lane, x);
   }
   if (!a.rotated) {
     fwht8(x, lane, a.had_block);  // H is symmetric: R^T applies the same butterflies

@@ -383,7 +383,7 @@ constexpr int kXcds = 8;  // accelerator dies of the chip; workgroups go round-r
 // (measured: 2/8 beats 0, 4/8 and 6/8 at the 32k Llama-shaped decode).
 constexpr int kStaticEighths = KVQ_TUNE_STATIC_EIGHTHS;
 
-template <int KB, int VB, int D>
+template <int KB, int VB, int D, bool M16>
 __device__ __forceinline__ void load_group(const DecodeArgs& a, const uint8_t* pool, const int32_t (&blks)[4],
                                            int grp, int p1, int seq_len, int64_t koff, int64_t voff, int lane,
                                            GroupRaw<KB, VB, D>& g) {
@@ -403,7 +403,8 @@ __device__ __forceinline__ void load_group(const DecodeArgs& a, const uint8_t* p
   }
   const int kl = tslot * RBK + g4 * QBYTES;  // lane offsets (loop invariant)
   const int vl = g4 * RBV + v_lane_offset<VB, D>(tslot);
-  const int ml = tslot * kMetaBytes;
+  constexpr int MB = M16 ? 4 : kMetaBytes;  // metadata bytes per row
+  const int ml = tslot * MB;
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp) load_kquarter<KB, D>(pool + boff[pp] + koff + kl, g.k[pp]);
   // token layout: lane = (page g4, slot tslot); each page's metadata by its 16 lanes
@@ -414,12 +415,22 @@ __device__ __forceinline__ void load_group(const DecodeArgs& a, const uint8_t* p
   const uint8_t* mbase = pool + my_boff + ml;
   g.ks = 1.f; g.kmn = 0.f; g.vs = 1.f; g.vmn = 0.f;
   if constexpr (KB != 16) {
-    const float2 mk = *reinterpret_cast<const float2*>(mbase + koff + kBlockTokens * RBK);
-    g.ks = mk.x; g.kmn = mk.y;
+    if constexpr (M16) {
+      const uint32_t mk = *reinterpret_cast<const uint32_t*>(mbase + koff + kBlockTokens * RBK);
+      g.ks = f16_to_f(mk & 0xffffu); g.kmn = f16_to_f(mk >> 16);
+    } else {
+      const float2 mk = *reinterpret_cast<const float2*>(mbase + koff + kBlockTokens * RBK);
+      g.ks = mk.x; g.kmn = mk.y;
+    }
   }
   if constexpr (VB != 16) {
-    const float2 mv = *reinterpret_cast<const float2*>(mbase + voff + kBlockTokens * RBV);
-    g.vs = mv.x; g.vmn = mv.y;
+    if constexpr (M16) {
+      const uint32_t mv = *reinterpret_cast<const uint32_t*>(mbase + voff + kBlockTokens * RBV);
+      g.vs = f16_to_f(mv & 0xffffu); g.vmn = f16_to_f(mv >> 16);
+    } else {
+      const float2 mv = *reinterpret_cast<const float2*>(mbase + voff + kBlockTokens * RBV);
+      g.vs = mv.x; g.vmn = mv.y;
+    }
   }
   // value layout: lane = (column n = tslot, K-slot group g4); K-slot e of a page
   // pair is slot 4*(e & 3) + g4 of page 2*pp2 + (e >> 2). One load instruction
@@ -455,14 +466,15 @@ struct PrefetchDepth {
 };
 
 // The wide formats (8- and 16-bit keys, bf16 values, and the 3/8-bit values
-// beside 4-bit keys at head_dim 128, 16-bit keys beside 3- or 16-bit values at
-// head_dim 64) need more than half the register file: one wave per SIMD. The
-// choice is checked by compiling every instance and requiring zero spills.
+// beside 4-bit keys at head_dim 128; 16-bit keys beside 3- or 16-bit values and
+// 8-bit keys beside bf16 values at head_dim 64) need more than half the
+// register file: one wave per SIMD. The choice is checked by compiling every
+// instance and requiring zero spills.
 template <int KB, int VB, int D>
 struct PartialWaves {
   static constexpr bool wide =
       D == 128 ? (VB == 16 || KB == 16 || KB == 8 || (KB == 4 && (VB == 3 || VB == 8)))
-               : (KB == 16 && (VB == 3 || VB == 16));
+               : ((KB == 16 && (VB == 3 || VB == 16)) || (KB == 8 && VB == 16));
   static constexpr int value = wide ? 1 : (D == 128 ? KVQ_TUNE_WAVES128 : 2);
 };
 
@@ -599,7 +611,7 @@ __device__ __forceinline__ void compute_group(GroupRaw<KB, VB, D>& g, const u32x
   __syncthreads();
 }
 
-template <int KB, int VB, int D>
+template <int KB, int VB, int D, bool M16>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PartialWaves<KB, VB, D>::value,
                                                                     PartialWaves<KB, VB, D>::value)))
 void decode_partial_kernel(DecodeArgs a, const int32_t* __restrict__ table, uint32_t* __restrict__ steal,
@@ -735,7 +747,7 @@ void decode_partial_kernel(DecodeArgs a, const int32_t* __restrict__ table, uint
     for (int pp = 0; pp < 4; ++pp) blks[pp] = __builtin_amdgcn_readlane(next_tab, pp);
     resolve();
     g.gid = gid;
-    load_group<KB, VB, D>(a, pool, blks, 4 * (g_lo + gid), pages, seq_len, koff, voff, lane, g);
+    load_group<KB, VB, D, M16>(a, pool, blks, 4 * (g_lo + gid), pages, seq_len, koff, voff, lane, g);
   };
 #pragma unroll
   for (int j = 0; j < DEPTH; ++j) load_next(gbuf[j]);
@@ -1040,22 +1052,31 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeArgs a, float rs
   }
 }
 
-template <int KB, int VB, int D>
+template <int KB, int VB, int D, bool M16>
 hipError_t launch_partial_t(const DecodeArgs& a, int n_splits, int batch, float qscale, hipStream_t s) {
   if (a.batch != batch || n_splits % kXcds != 0) return hipErrorInvalidValue;
   dim3 grid(static_cast<unsigned>(n_splits) * a.n_heads * batch);
-  hipLaunchKernelGGL((decode_partial_kernel<KB, VB, D>), grid, dim3(64), 0, s, a, a.table, a.steal, qscale);
+  hipLaunchKernelGGL((decode_partial_kernel<KB, VB, D, M16>), grid, dim3(64), 0, s, a, a.table, a.steal, qscale);
   return hipGetLastError();
+}
+
+// Formats whose rows carry metadata get a float16-metadata instance too.
+template <int KB, int VB, int D>
+hipError_t launch_partial_m(const DecodeArgs& a, int n_splits, int batch, float qs, hipStream_t s) {
+  if constexpr (KB != 16 || VB != 16) {
+    if (a.meta16) return launch_partial_t<KB, VB, D, true>(a, n_splits, batch, qs, s);
+  }
+  return launch_partial_t<KB, VB, D, false>(a, n_splits, batch, qs, s);
 }
 
 template <int KB, int D>
 hipError_t dispatch_v(const DecodeArgs& a, int vbits, int n_splits, int batch, float qs, hipStream_t s) {
   switch (vbits) {
-    case 2: return launch_partial_t<KB, 2, D>(a, n_splits, batch, qs, s);
-    case 3: return launch_partial_t<KB, 3, D>(a, n_splits, batch, qs, s);
-    case 4: return launch_partial_t<KB, 4, D>(a, n_splits, batch, qs, s);
-    case 8: return launch_partial_t<KB, 8, D>(a, n_splits, batch, qs, s);
-    case 16: return launch_partial_t<KB, 16, D>(a, n_splits, batch, qs, s);
+    case 2: return launch_partial_m<KB, 2, D>(a, n_splits, batch, qs, s);
+    case 3: return launch_partial_m<KB, 3, D>(a, n_splits, batch, qs, s);
+    case 4: return launch_partial_m<KB, 4, D>(a, n_splits, batch, qs, s);
+    case 8: return launch_partial_m<KB, 8, D>(a, n_splits, batch, qs, s);
+    case 16: return launch_partial_m<KB, 16, D>(a, n_splits, batch, qs, s);
     default: return hipErrorInvalidValue;
   }
 }

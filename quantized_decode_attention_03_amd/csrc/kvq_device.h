@@ -52,6 +52,23 @@ __device__ __forceinline__ uint32_t pk_add_h(uint32_t a, uint32_t c) {
 
 __device__ __forceinline__ uint32_t half_bits(_Float16 h) { return __builtin_bit_cast(uint16_t, h); }
 
+// float16 metadata: widening, and rounding down / up to a float16 value (the
+// conversion rounds half to even; a result on the wrong side of x steps to
+// the neighbouring float16, -0 and +0 stepping to the smallest subnormals).
+__device__ __forceinline__ float f16_to_f(uint32_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
+}
+__device__ __forceinline__ uint32_t f16_down(float x) {
+  const uint32_t h = half_bits(static_cast<_Float16>(x));
+  if (!(f16_to_f(h) > x)) return h;
+  return (h & 0x7fffu) == 0 ? 0x8001u : ((h & 0x8000u) ? h + 1 : h - 1);
+}
+__device__ __forceinline__ uint32_t f16_up(float x) {
+  const uint32_t h = half_bits(static_cast<_Float16>(x));
+  if (!(f16_to_f(h) < x)) return h;
+  return (h & 0x7fffu) == 0 ? 0x0001u : ((h & 0x8000u) ? h - 1 : h + 1);
+}
+
 // Wave-wide reductions (64 lanes) returning the result in every lane.
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

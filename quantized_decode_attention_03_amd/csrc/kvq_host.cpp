@@ -82,14 +82,15 @@ bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 bool valid_bits(int b) { return b == 2 || b == 3 || b == 4 || b == 8 || b == 16; }
 
 int64_t row_bytes(int d, int b) { return static_cast<int64_t>(d) * b / 8; }
-int64_t area_bytes(int d, int b) {
-  return KVQ_BLOCK_TOKENS * row_bytes(d, b) + (b == 16 ? 0 : KVQ_BLOCK_TOKENS * 8);
+int64_t area_bytes(int d, int b, int meta_fp16) {
+  return KVQ_BLOCK_TOKENS * row_bytes(d, b) + (b == 16 ? 0 : KVQ_BLOCK_TOKENS * (meta_fp16 ? 4 : 8));
 }
 
 // Checks the inputs of a layout and that its outputs match them.
 kvq_status check_layout(const kvq_layout* L, const char* who) {
   if (!L) return fail(KVQ_ERR_ARG, "%s: null layout", who);
   if (L->block_tokens != KVQ_BLOCK_TOKENS) return fail(KVQ_ERR_ARG, "%s: block_tokens must be 16", who);
+  if (L->meta_fp16 != 0 && L->meta_fp16 != 1) return fail(KVQ_ERR_ARG, "%s: meta_fp16 must be 0 or 1", who);
   if (L->num_kv_heads < 1 || L->num_kv_heads > KVQ_MAX_KV_HEADS)
     return fail(KVQ_ERR_ARG, "%s: num_kv_heads %d out of [1, %d]", who, L->num_kv_heads, KVQ_MAX_KV_HEADS);
   if (L->group < 1 || L->group > 4) return fail(KVQ_ERR_ARG, "%s: group %d out of [1, 4]", who, L->group);
@@ -251,11 +252,11 @@ kvq_status kvq_layout_init(kvq_layout* L) {
   std::memset(L->v_off, 0, sizeof(L->v_off));
   for (int h = 0; h < L->num_kv_heads; ++h) {
     L->k_off[h] = off;
-    off += area_bytes(L->head_dim, L->bits_k[h]);
+    off += area_bytes(L->head_dim, L->bits_k[h], L->meta_fp16);
   }
   for (int h = 0; h < L->num_kv_heads; ++h) {
     L->v_off[h] = off;
-    off += area_bytes(L->head_dim, L->bits_v[h]);
+    off += area_bytes(L->head_dim, L->bits_v[h], L->meta_fp16);
   }
   L->block_bytes = off;
   return ok();
@@ -502,6 +503,7 @@ kvq_status kvq_logquant_requant(const kvq_segment* window, const kvq_segment* mi
     sg.block_bytes = L.block_bytes;
     sg.table = segs[i]->block_table;
     sg.table_stride = segs[i]->table_stride;
+    sg.meta16 = L.meta_fp16;
     for (int h = 0; h < L.num_kv_heads; ++h) {
       sg.bits[0][h] = static_cast<uint8_t>(L.bits_k[h]);
       sg.bits[1][h] = static_cast<uint8_t>(L.bits_v[h]);
@@ -611,6 +613,7 @@ kvq_status kvq_quantize_append(const kvq_layout* L, void* pool, int64_t pool_blo
     a.src[0] = k;
     a.src[1] = v;
     a.src_bf16 = in_dtype == KVQ_BF16;
+    a.meta16 = L->meta_fp16;
     a.batch = batch;
     a.n_new = n_new;
     a.hkv = L->num_kv_heads;
@@ -664,6 +667,7 @@ kvq_status kvq_dequant(const kvq_layout* L, const void* pool, int64_t pool_block
       a.d = L->head_dim;
       a.had_block = L->had_block;
       a.rotated = rotated != 0;
+      a.meta16 = L->meta_fp16;
       a.bits = bits[h0];
       a.out = half ? v_out : k_out;
       for (int h = h0; h < L->num_kv_heads; ++h) {
@@ -749,6 +753,7 @@ kvq_status kvq_decode_partial(const kvq_segment* segs, int32_t n_segs, int32_t b
         a.seq_lens = sg.seq_lens;
         a.q = q;
         a.q_bf16 = q_dtype == KVQ_BF16;
+        a.meta16 = L.meta_fp16;
         a.hkv = L.num_kv_heads;
         a.group = L.group;
         a.had_block = L.had_block;

@@ -19,6 +19,7 @@ struct AppendArgs {
   const int32_t* start_pos;
   const void* src[2];   // K, V: [batch][n_new][hkv][d]
   int32_t src_bf16;
+  int32_t meta16;       // 1: float16 {s, mn} (4 bytes per row)
   int32_t batch, n_new, hkv, d, had_block;
   int32_t n_heads;      // heads in this launch
   int32_t bits[2];      // K bits, V bits of these heads
@@ -32,6 +33,7 @@ struct DequantArgs {
   int64_t block_bytes;
   const int32_t* table_row;  // this sequence's table row
   int32_t pos0, n, hkv, d, had_block, rotated;
+  int32_t meta16;
   int32_t n_heads, bits;
   int32_t heads[KVQ_MAX_KV_HEADS];
   int64_t area_off[KVQ_MAX_KV_HEADS];
@@ -49,6 +51,7 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   const void* q;       // [batch][hkv*group][d]
   int32_t q_bf16;
+  int32_t meta16;      // 1: float16 {s, mn} (4 bytes per row)
   int32_t hkv, group, had_block;
   int32_t batch;       // sequences (the grid covers batch x n_heads units)
   int32_t slot_base;   // first split slot of this segment
@@ -86,6 +89,7 @@ struct RequantSeg {
   int64_t block_bytes;
   const int32_t* table;
   int32_t table_stride;
+  int32_t meta16;
   uint8_t bits[2][KVQ_MAX_KV_HEADS];  // K, V bits per head
 };
 struct RequantArgs {

@@ -14,7 +14,7 @@ import numpy as np
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkvq.so")
 
-KVQ_ABI_VERSION = 1
+KVQ_ABI_VERSION = 2
 KVQ_MAX_KV_HEADS = 64
 KVQ_BLOCK_TOKENS = 16
 
@@ -43,6 +43,7 @@ class KvqLayout(ctypes.Structure):
         ("head_dim", ctypes.c_int32),
         ("had_block", ctypes.c_int32),
         ("block_tokens", ctypes.c_int32),
+        ("meta_fp16", ctypes.c_int32),
         ("bits_k", ctypes.c_int32 * KVQ_MAX_KV_HEADS),
         ("bits_v", ctypes.c_int32 * KVQ_MAX_KV_HEADS),
         ("k_off", ctypes.c_int64 * KVQ_MAX_KV_HEADS),
@@ -170,11 +171,13 @@ def kvq_last_error():
     return lib().kvq_last_error().decode()
 
 
-def kvq_layout_init(num_kv_heads, group, head_dim, had_block, bits_k, bits_v):
-    """Return an initialised KvqLayout (bits_k / bits_v: one width per KV head)."""
+def kvq_layout_init(num_kv_heads, group, head_dim, had_block, bits_k, bits_v, meta_fp16=False):
+    """Return an initialised KvqLayout (bits_k / bits_v: one width per KV head; meta_fp16: 4-byte
+    float16 {s, mn} per row instead of 8-byte float32)."""
     L = KvqLayout()
     L.num_kv_heads, L.group, L.head_dim, L.had_block = num_kv_heads, group, head_dim, had_block
     L.block_tokens = KVQ_BLOCK_TOKENS
+    L.meta_fp16 = int(bool(meta_fp16))
     bits_k, bits_v = list(bits_k), list(bits_v)
     if len(bits_k) != num_kv_heads or len(bits_v) != num_kv_heads:
         raise ValueError("bits_k and bits_v need one entry per KV head")

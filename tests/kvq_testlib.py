@@ -49,7 +49,7 @@ class GpuCache:
 def oracle_layout(L, heads=None):
     heads = list(range(L.num_kv_heads)) if heads is None else list(heads)
     return O.Layout(len(heads), L.group, L.head_dim, L.had_block,
-                    [L.bits_k[h] for h in heads], [L.bits_v[h] for h in heads])
+                    [L.bits_k[h] for h in heads], [L.bits_v[h] for h in heads], meta_fp16=bool(L.meta_fp16))
 
 
 def oracle_cache(lay, table_np, start, k, v, n_blocks):
@@ -62,8 +62,8 @@ def oracle_cache(lay, table_np, start, k, v, n_blocks):
 # Row-level comparison of stored codes and metadata
 # ---------------------------------------------------------------------------
 
-def gather_rows(pool_np, block_bytes, table_np, seq, positions, area_off, d, bits):
-    """Bytes of stored rows (codes or bf16) and their meta for tokens `positions`."""
+def gather_rows(pool_np, block_bytes, table_np, seq, positions, area_off, d, bits, meta_fp16=False):
+    """Bytes of stored rows (codes or bf16) and their meta (as float32) for tokens `positions`."""
     rb = d * bits // 8
     pos = np.asarray(positions)
     blk = table_np[seq, pos // 16].astype(np.int64)
@@ -72,8 +72,10 @@ def gather_rows(pool_np, block_bytes, table_np, seq, positions, area_off, d, bit
     rows = pool_np[blk[:, None], cols]
     meta = None
     if bits != 16:
-        mcols = area_off + 16 * rb + slot[:, None] * 8 + np.arange(8)[None, :]
-        meta = pool_np[blk[:, None], mcols].copy().view(np.float32).reshape(-1, 2)
+        mb = 4 if meta_fp16 else 8
+        mcols = area_off + 16 * rb + slot[:, None] * mb + np.arange(mb)[None, :]
+        meta = pool_np[blk[:, None], mcols].copy().view(np.float16 if meta_fp16 else np.float32)
+        meta = meta.astype(np.float32).reshape(-1, 2)
     return rows, meta
 
 
@@ -103,7 +105,7 @@ class CodeStats:
         return self.mismatch / max(1, self.codes)
 
 
-def compare_rows(gpu_rows, gpu_meta, ref_rows, ref_meta, x_rot, bits, d, stats):
+def compare_rows(gpu_rows, gpu_meta, ref_rows, ref_meta, x_rot, bits, d, stats, meta_fp16=False):
     """Bit-exact rows except codes off by one at near ties (or in rows whose
     min/max moved by a few ulps). x_rot is the oracle's rotated fp32 rows."""
     stats.rows += gpu_rows.shape[0]
@@ -138,9 +140,14 @@ def compare_rows(gpu_rows, gpu_meta, ref_rows, ref_meta, x_rot, bits, d, stats):
     r, j = np.nonzero(diff)
     xr = np.asarray(x_rot, np.float32)
     mn = xr[r].min(axis=1)
-    rng = (xr[r].max(axis=1) - mn).astype(np.float32)
     qmax = np.float32(2 ** bits - 1)
-    inv = (qmax / rng).astype(np.float32)
+    if meta_fp16:  # the float16-metadata quantizer's own grid
+        mn = O.float16_down(mn).astype(np.float32)
+        rng = (xr[r].max(axis=1) - mn).astype(np.float32)
+        inv = (np.float32(1) / O.float16_up((rng / qmax).astype(np.float32)).astype(np.float32)).astype(np.float32)
+    else:
+        rng = (xr[r].max(axis=1) - mn).astype(np.float32)
+        inv = (qmax / rng).astype(np.float32)
     x = xr[r, j]
     u = ((x - mn).astype(np.float32) * inv).astype(np.float64)
     frac = np.abs(u - np.floor(u) - 0.5)

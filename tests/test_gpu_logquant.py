@@ -26,8 +26,9 @@ pytestmark = pytest.mark.gpu
 class OracleTokens:
     """The oracle's stored representation of every token of one sequence, per (head, half)."""
 
-    def __init__(self, hkv, d, n, bits):
+    def __init__(self, hkv, d, n, bits, m16):
         self.hkv, self.d, self.n, self.bits = hkv, d, n, bits  # bits[cls][half][h]
+        self.m16 = m16  # float16 metadata in the middle and low segments
         self.rep = {}  # (pos, h, half) -> (bits, codes, s, mn, values, source values)
 
     def store(self, pos, cls, x_rows):
@@ -50,7 +51,10 @@ class OracleTokens:
         if b == 16:
             bits16 = O.float32_to_bf16_bits(src)
             return (16, bits16, None, None, O.bf16_bits_to_float32(bits16), src)
-        codes, s, mn = O.requantize_row(src, b) if requant else O.quantize_rows(src, b)
+        if requant:
+            codes, s, mn = O.requantize_row(src, b, meta_fp16=self.m16)
+        else:
+            codes, s, mn = O.quantize_rows_fp16_meta(src, b) if self.m16 else O.quantize_rows(src, b)
         return (b, codes, s, mn, O.dequantize_rows(codes, s, mn), src)
 
     def values(self, positions, h, half):
@@ -60,7 +64,8 @@ class OracleTokens:
 def gpu_rows(pool_np, L, table_np, seq, slots, h, half):
     area = (L.k_off if half == 0 else L.v_off)[h]
     bits = (L.bits_k if half == 0 else L.bits_v)[h]
-    return T.gather_rows(pool_np, L.block_bytes, table_np, seq, np.asarray(slots), area, L.head_dim, bits)
+    return T.gather_rows(pool_np, L.block_bytes, table_np, seq, np.asarray(slots), area, L.head_dim, bits,
+                         bool(L.meta_fp16))
 
 
 def oracle_rows(tok, positions, h, half):
@@ -70,15 +75,17 @@ def oracle_rows(tok, positions, h, half):
     if b == 16:
         return np.concatenate([r[1] for r in reps]).view(np.uint8).reshape(len(reps), -1), None, src, 16
     rows = O.pack_codes(np.concatenate([r[1] for r in reps]), b)
-    meta = np.stack([np.concatenate([r[2] for r in reps]), np.concatenate([r[3] for r in reps])], 1)
-    return rows, meta.astype(np.float32), src, b
+    meta = np.stack([np.concatenate([r[2] for r in reps]).astype(np.float32),
+                     np.concatenate([r[3] for r in reps]).astype(np.float32)], 1)
+    return rows, meta, src, b
 
 
-@pytest.mark.parametrize("d,n,window,starts,steps,mid_bits,low_bits", [
-    (64, 64, 16, [300, 77], 150, ([4, 8], [4, 3]), ([2, 2], [2, 3])),
-    (128, 32, 8, [129, 1], 200, ([4, 4], [4, 4]), ([2, 2], [2, 2])),
+@pytest.mark.parametrize("d,n,window,starts,steps,mid_bits,low_bits,m16", [
+    (64, 64, 16, [300, 77], 150, ([4, 8], [4, 3]), ([2, 2], [2, 3]), False),
+    (128, 32, 8, [129, 1], 200, ([4, 4], [4, 4]), ([2, 2], [2, 2]), False),
+    (128, 128, 16, [200, 33], 120, ([4, 4], [4, 4]), ([2, 3], [2, 2]), True),
 ])
-def test_logquant_dynamic_steps_match_oracle(d, n, window, starts, steps, mid_bits, low_bits):
+def test_logquant_dynamic_steps_match_oracle(d, n, window, starts, steps, mid_bits, low_bits, m16):
     hkv, group, batch = 2, 2, len(starts)
     rng = np.random.default_rng(d + window)
     final = [t + steps for t in starts]
@@ -89,8 +96,8 @@ def test_logquant_dynamic_steps_match_oracle(d, n, window, starts, steps, mid_bi
     q = rng.standard_normal((batch, hkv * group, d)).astype(np.float32)
 
     L = [kvq.kvq_layout_init(hkv, group, d, n, [16] * hkv, [16] * hkv),
-         kvq.kvq_layout_init(hkv, group, d, n, mid_bits[0], mid_bits[1]),
-         kvq.kvq_layout_init(hkv, group, d, n, low_bits[0], low_bits[1])]
+         kvq.kvq_layout_init(hkv, group, d, n, mid_bits[0], mid_bits[1], meta_fp16=m16),
+         kvq.kvq_layout_init(hkv, group, d, n, low_bits[0], low_bits[1], meta_fp16=m16)]
     cap = [window, 256, total_max]
     tables, caches = [], []
     for c in range(3):
@@ -99,7 +106,7 @@ def test_logquant_dynamic_steps_match_oracle(d, n, window, starts, steps, mid_bi
         caches.append(T.GpuCache(L[c], n_blocks, tables[c]))
 
     bits = [[[16] * hkv] * 2, [list(mid_bits[0]), list(mid_bits[1])], [list(low_bits[0]), list(low_bits[1])]]
-    toks = [OracleTokens(hkv, d, n, bits) for _ in range(batch)]
+    toks = [OracleTokens(hkv, d, n, bits, m16) for _ in range(batch)]
     st = kvq.LogQuantStates(batch, window, cap_mid=cap[1])
     low_pos = []
     dev = T.DEV
@@ -169,7 +176,7 @@ def test_logquant_dynamic_steps_match_oracle(d, n, window, starts, steps, mid_bi
                 for half in range(2):
                     g, gm = gpu_rows(pools[c], L[c], tables[c], b, held[c], h, half)
                     r, rm, src, bb = oracle_rows(toks[b], positions[c], h, half)
-                    T.compare_rows(g, gm, r, rm, src, bb, d, stats)
+                    T.compare_rows(g, gm, r, rm, src, bb, d, stats, m16 and c > 0)
     assert stats.rate <= 1e-5
 
     # ---- decode over the three segments ----

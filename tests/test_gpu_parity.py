@@ -22,7 +22,8 @@ pytestmark = pytest.mark.gpu
 TIE_RATE = 1e-5
 
 
-def build_case(d, n, group, bits_k, bits_v, lens, seed, in_bf16=True, chunks=None, stride_extra=0, offsets=None):
+def build_case(d, n, group, bits_k, bits_v, lens, seed, in_bf16=True, chunks=None, stride_extra=0, offsets=None,
+               meta_fp16=False):
     """Append max(lens) tokens to every sequence (in `chunks` appends), sequence
     b starting at position offsets[b], on both sides. Decode then reads only
     lens[b] tokens, so tokens past a sequence's length sit in its last page."""
@@ -36,7 +37,7 @@ def build_case(d, n, group, bits_k, bits_v, lens, seed, in_bf16=True, chunks=Non
     v = rng.standard_normal((batch, tmax, hkv, d)).astype(np.float32)
     if in_bf16:
         k, v = synth.bf16_round(k), synth.bf16_round(v)
-    L = kvq.kvq_layout_init(hkv, group, d, n, bits_k, bits_v)
+    L = kvq.kvq_layout_init(hkv, group, d, n, bits_k, bits_v, meta_fp16=meta_fp16)
     ends = (offsets + tmax).tolist()
     n_blocks = sum(-(-t // 16) for t in ends) + 5
     pages = max(-(-t // 16) for t in ends)
@@ -72,10 +73,11 @@ def compare_cache(L, lay, cache, ref_pool, table, k, v, offsets=None, stats=None
         pos = offsets[b] + np.arange(tmax)
         for h in range(L.num_kv_heads):
             for x, bits, off in ((k, L.bits_k[h], L.k_off[h]), (v, L.bits_v[h], L.v_off[h])):
-                g_rows, g_meta = T.gather_rows(gpu_pool, L.block_bytes, table, b, pos, off, d, bits)
-                r_rows, r_meta = T.gather_rows(ref_pool, L.block_bytes, table, b, pos, off, d, bits)
+                m16 = bool(L.meta_fp16)
+                g_rows, g_meta = T.gather_rows(gpu_pool, L.block_bytes, table, b, pos, off, d, bits, m16)
+                r_rows, r_meta = T.gather_rows(ref_pool, L.block_bytes, table, b, pos, off, d, bits, m16)
                 x_rot = O.rotate(x[b, :, h, :], n)
-                T.compare_rows(g_rows, g_meta, r_rows, r_meta, x_rot, bits, d, stats)
+                T.compare_rows(g_rows, g_meta, r_rows, r_meta, x_rot, bits, d, stats, m16)
     return stats
 
 
@@ -221,6 +223,51 @@ def test_decode_formats_ragged_lengths(d, n, g, bk, bv):
     q = synth.bf16_round(rng.standard_normal((len(lens), len(bk) * g, d)).astype(np.float32))
     out, expect = decode_both(L, lay, cache, ref, table, lens, q)
     assert np.all(out[5] == 0)  # the empty sequence
+    assert T.max_rel_err(out, expect) <= T.ATTN_TOL
+
+
+# float16 metadata: the same formats with 4-byte {s, mn} (minimum rounded down, scale up)
+@pytest.mark.parametrize("d,n,bk,bv", [f for f in FORMATS if 16 not in f[2] + f[3]] + [(128, 32, [2, 16], [3, 2])])
+@pytest.mark.parametrize("in_bf16", [True, False])
+def test_append_fp16_meta(d, n, bk, bv, in_bf16):
+    lens = [37, 1, 53]
+    offsets = [0, 5, 13]
+    L, lay, cache, ref, table, k, v = build_case(d, n, 2, bk, bv, lens, seed=8, in_bf16=in_bf16,
+                                                 chunks=[5, 13, 40], offsets=offsets, meta_fp16=True)
+    assert L.meta_fp16 == 1 and lay.meta_bytes == 4
+    stats = compare_cache(L, lay, cache, ref, table, k, v, offsets=offsets)
+    assert stats.rate <= TIE_RATE, stats.rate
+
+
+@pytest.mark.parametrize("d,n,bk,bv", [(64, 64, [4, 4], [2, 2]), (128, 32, [2, 16], [3, 2]), (128, 128, [8, 3], [4, 8])])
+def test_dequant_fp16_meta(d, n, bk, bv):
+    lens = [45, 29]
+    L, lay, cache, ref, table, k, v = build_case(d, n, 1, bk, bv, lens, seed=12, chunks=[20, 25], meta_fp16=True)
+    gpu_pool = cache.pool.cpu().numpy()
+    for b, t in enumerate(lens):
+        gk, gv = [x.cpu().numpy() for x in kvq.kvq_dequant(L, cache.pool, cache.table, b, 0, t, rotated=True)]
+        rk, rv = O.dequant(lay, ref, table[b], 0, t, rotated=True)
+        pos = np.arange(t)
+        for h in range(L.num_kv_heads):
+            for g, r, bits, off in ((gk, rk, bk[h], L.k_off[h]), (gv, rv, bv[h], L.v_off[h])):
+                g_rows, g_meta = T.gather_rows(gpu_pool, L.block_bytes, table, b, pos, off, d, bits, True)
+                r_rows, r_meta = T.gather_rows(ref, L.block_bytes, table, b, pos, off, d, bits, True)
+                same = np.all(g_rows == r_rows, axis=1)
+                if g_meta is not None:
+                    same &= np.all(g_meta == r_meta, axis=1)
+                assert same.mean() > 0.9
+                assert np.array_equal(g[same, h], r[same, h])
+
+
+@pytest.mark.parametrize("d,n,g,bk,bv", [f for f in DECODE_FORMATS if 16 not in f[3] + f[4]] +
+                         [(128, 64, 1, [16, 4], [8, 3])])
+def test_decode_fp16_meta(d, n, g, bk, bv):
+    lens = [1, 15, 17, 1000, 64, 0, 300]
+    L, lay, cache, ref, table, k, v = build_case(d, n, g, bk, bv, lens, seed=25, chunks=[7, 500, 600], meta_fp16=True)
+    rng = np.random.default_rng(26)
+    q = synth.bf16_round(rng.standard_normal((len(lens), len(bk) * g, d)).astype(np.float32))
+    out, expect = decode_both(L, lay, cache, ref, table, lens, q)
+    assert np.all(out[5] == 0)
     assert T.max_rel_err(out, expect) <= T.ATTN_TOL
 
 

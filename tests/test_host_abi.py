@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     for name in sorted(declared):
         assert hasattr(lib, name), name
     assert declared == set(kvq.EXPORTED)
-    assert kvq.kvq_abi_version() == 1
+    assert kvq.kvq_abi_version() == 2
     assert kvq.kvq_status_str(kvq.KVQ_ERR_BUDGET) == "KVQ_ERR_BUDGET"
 
 
@@ -36,10 +36,11 @@ def test_library_exports_every_declared_symbol():
     (8, 128, 32, [2, 3, 4, 8, 16, 2, 3, 4], [8, 4, 3, 2, 16, 16, 2, 8]),
 ])
 def test_layout_matches_oracle(hkv, d, n, bk, bv):
-    L = kvq.kvq_layout_init(hkv, 4, d, n, bk, bv)
-    k_off, v_off, total = O.block_layout(hkv, d, bk, bv)
-    assert L.block_bytes == total
-    assert list(L.k_off[:hkv]) == k_off and list(L.v_off[:hkv]) == v_off
+    for m16 in (False, True):
+        L = kvq.kvq_layout_init(hkv, 4, d, n, bk, bv, meta_fp16=m16)
+        k_off, v_off, total = O.block_layout(hkv, d, bk, bv, 4 if m16 else 8)
+        assert L.block_bytes == total
+        assert list(L.k_off[:hkv]) == k_off and list(L.v_off[:hkv]) == v_off
 
 
 def test_layout_rejects_bad_arguments():
