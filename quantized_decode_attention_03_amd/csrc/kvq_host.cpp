@@ -155,14 +155,17 @@ SplitPlan plan_splits(const kvq_segment& s, int batch) {
   int pps = 0;
   if (const char* env = std::getenv("KVQ_SPLIT_PAGES")) pps = std::atoi(env);
   if (pps <= 0) {
+    // One resident round: a head whose format runs w waves per SIMD takes 1/w
+    // of a SIMD per wave, so the splits per unit are the SIMDs of the device
+    // over batch * sum_h 1/w_h (heads of different formats share the round).
     const kvq_layout& L = *s.layout;
-    int waves = 3;
+    double simd_share = 0.0;
     for (int h = 0; h < L.num_kv_heads; ++h)
-      waves = std::min(waves, kvq::decode_partial_waves_per_simd(L.bits_k[h], L.bits_v[h], L.head_dim));
+      simd_share += 1.0 / kvq::decode_partial_waves_per_simd(L.bits_k[h], L.bits_v[h], L.head_dim);
     const int cus = device_cus() > 0 ? device_cus() : 256;
-    const int64_t capacity = static_cast<int64_t>(waves) * 4 * cus;
-    const int64_t units = static_cast<int64_t>(batch) * L.num_kv_heads;
-    const int64_t want_splits = std::max<int64_t>(1, capacity / units);
+    // (rounded down to whole rounds of the eight XCDs, so the round is not overfilled)
+    const int64_t fit = static_cast<int64_t>(4.0 * cus / (static_cast<double>(batch) * simd_share));
+    const int64_t want_splits = std::max<int64_t>(1, fit >= 8 ? fit / 8 * 8 : fit);
     pps = static_cast<int>((pages + want_splits - 1) / want_splits);
     pps = std::max(pps, 8);
   }
