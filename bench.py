@@ -42,7 +42,7 @@ HBM_PEAK_GBS = 8000.0
 ROOT = os.path.dirname(os.path.abspath(__file__))
 DECODE_SRC = os.path.join(ROOT, "quantized_decode_attention_03_amd", "csrc", "kvq_decode.hip")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_partial_k4v4_d128_b16_ctx32k_traffic.md")
-PARTIAL_KERNEL = "decode_partial_kernel<4, 4, 128>"
+PARTIAL_KERNEL = "decode_partial_kernel<4, 4, 128, false>"
 COPY_BYTES = 1 << 30
 
 B, T, HKV, G, D, HAD = 16, 32768, 8, 4, 128, 128
