@@ -954,13 +954,13 @@ void decode_partial_kernel(DecodeArgs a, const int32_t* __restrict__ table, uint
 // ---------------------------------------------------------------------------
 // Merge of the split partials (all segments) and the inverse rotation.
 // ---------------------------------------------------------------------------
-// One workgroup of four waves per (sequence, query head): the waves share the
-// split slots (wave w takes slots s = w mod 4), so a long list of slots (batch
-// 1 at long context has hundreds) is read with four waves' loads in flight.
-template <int D>
-__global__ __launch_bounds__(256) void decode_merge_kernel(MergeArgs a, float rs_n) {
+// One workgroup of NW waves per (sequence, query head): the waves share the
+// split slots (wave w takes slots s = w mod NW), so a long list of slots
+// (batch 1 at long context has hundreds) is read with NW waves' loads in
+// flight; each wave's loop is bound by load latency, not bandwidth.
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_merge_kernel(MergeArgs a, float rs_n) {
   constexpr int CPL = D / 64;  // channels per lane: [CPL*lane, CPL*lane + CPL)
-  constexpr int NW = 4;        // waves
   constexpr int CHUNK = 1024;  // slots whose weights sit in LDS at a time
   constexpr float NEG_INF = -__builtin_huge_valf();
   __shared__ float wsh[CHUNK];   // split weights 2^(m_s - M) of the current chunk
@@ -978,7 +978,9 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeArgs a, float rs
   mx = wave_max_scalar(mx);
   if (lane == 0) scal[w][0] = mx;
   __syncthreads();
-  mx = fmaxf(fmaxf(scal[0][0], scal[1][0]), fmaxf(scal[2][0], scal[3][0]));
+  mx = scal[0][0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) mx = fmaxf(mx, scal[i][0]);
 
   float x[CPL];
 #pragma unroll
@@ -1021,10 +1023,17 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeArgs a, float rs
   __syncthreads();
   if (w != 0) return;
 #pragma unroll
-  for (int j = 0; j < CPL; ++j) x[j] = (red[0][CPL * lane + j] + red[1][CPL * lane + j]) +
-                                       (red[2][CPL * lane + j] + red[3][CPL * lane + j]);
+  for (int j = 0; j < CPL; ++j) {
+    float t = red[0][CPL * lane + j];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) t += red[i][CPL * lane + j];
+    x[j] = t;
+  }
   if (mx != NEG_INF) {
-    const float inv = 1.f / ((scal[0][1] + scal[1][1]) + (scal[2][1] + scal[3][1]));
+    float lsum = scal[0][1];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) lsum += scal[i][1];
+    const float inv = 1.f / lsum;
 #pragma unroll
     for (int j = 0; j < CPL; ++j) x[j] *= inv;
   }
@@ -1135,8 +1144,13 @@ hipError_t launch_decode_merge(const MergeArgs& a, hipStream_t s) {
   if (a.batch * a.hq == 0) return hipSuccess;
   const float rs = static_cast<float>(1.0 / std::sqrt(static_cast<double>(a.had_block)));
   dim3 grid(a.batch * a.hq);
-  if (a.d == 128) hipLaunchKernelGGL((decode_merge_kernel<128>), grid, dim3(256), 0, s, a, rs);
-  else if (a.d == 64) hipLaunchKernelGGL((decode_merge_kernel<64>), grid, dim3(256), 0, s, a, rs);
+  // long slot lists (batch 1 at long context) get sixteen waves, so the
+  // latency-bound loop runs a few trips per wave
+  const bool many = a.total_slots >= 128;
+  if (a.d == 128 && many) hipLaunchKernelGGL((decode_merge_kernel<128, 16>), grid, dim3(1024), 0, s, a, rs);
+  else if (a.d == 128) hipLaunchKernelGGL((decode_merge_kernel<128, 4>), grid, dim3(256), 0, s, a, rs);
+  else if (a.d == 64 && many) hipLaunchKernelGGL((decode_merge_kernel<64, 16>), grid, dim3(1024), 0, s, a, rs);
+  else if (a.d == 64) hipLaunchKernelGGL((decode_merge_kernel<64, 4>), grid, dim3(256), 0, s, a, rs);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -340,6 +340,17 @@ def test_decode_split_count_invariance(monkeypatch):
         assert T.rel(o.cpu().numpy(), base.cpu().numpy()) < 1e-5
 
 
+def test_decode_long_slot_list_merge(monkeypatch):
+    # 4-page splits over 8192 tokens: 256 split slots per query head, the merge's sixteen-wave path
+    monkeypatch.setenv("KVQ_SPLIT_PAGES", "4")
+    lens = [8192, 3000]
+    L, lay, cache, ref, table, k, v = build_case(128, 128, 4, [4, 2], [4, 3], lens, seed=37, chunks=[4096, 4096])
+    assert kvq.kvq_decode_workspace_bytes([cache.segment(lens)], 2) > 2 * 8 * 128 * 130 * 4
+    q = synth.bf16_round(np.random.default_rng(38).standard_normal((2, 8, 128)).astype(np.float32))
+    out, expect = decode_both(L, lay, cache, ref, table, lens, q)
+    assert T.max_rel_err(out, expect) <= T.ATTN_TOL
+
+
 def test_decode_single_token_returns_dequantized_value():
     lens = [1, 1, 1]
     L, lay, cache, ref, table, k, v = build_case(128, 128, 4, [4, 4], [3, 8], lens, seed=35)
