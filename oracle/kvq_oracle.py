@@ -175,6 +175,29 @@ def quantize_rows_fp16_meta(xr, b):
     return codes, s, mn
 
 
+def quantize_cols(xr, b):
+    """Per-channel quantization of one group of rows (xr [tokens, d], float32):
+    the KIVI-style key granularity that the RateQuant page names (Methodology 3,
+    per-channel symmetric keys in KIVI) and the LogQuant page uses (Methodology
+    5, key-per-channel). Here the group is the 16 tokens of a page and the
+    scale is asymmetric, as for rows: per channel c over the group's tokens,
+    mn_c = min, mx_c = max, s_c = (mx_c - mn_c) / (2^b - 1),
+    inv_c = (2^b - 1) / (mx_c - mn_c), code = clamp(rne((x - mn_c) * inv_c)),
+    all in float32; a constant channel gets s_c = 0 and codes 0.
+    Returns (codes [tokens, d] uint8, s [d], mn [d]).
+    """
+    xr = np.asarray(xr, dtype=np.float32)
+    qmax = np.float32(2 ** b - 1)
+    mn = xr.min(axis=0)
+    rng = (xr.max(axis=0) - mn).astype(np.float32)
+    nonconst = rng > 0
+    safe = np.where(nonconst, rng, np.float32(1))
+    s = np.where(nonconst, safe / qmax, np.float32(0)).astype(np.float32)
+    inv = np.where(nonconst, qmax / safe, np.float32(0)).astype(np.float32)
+    u = ((xr - mn[None, :]).astype(np.float32) * inv[None, :]).astype(np.float32)
+    return np.clip(np.rint(u), 0, qmax).astype(np.uint8), s, mn.astype(np.float32)
+
+
 def dequantize_rows(codes, s, mn):
     """x_hat = c * s + mn in float32 (a rounded product, then a rounded sum);
     float16 metadata is widened to float32 (exactly) first."""
@@ -241,7 +264,15 @@ def segment_bytes(d, b, meta_bytes=META_BYTES):
     return BLOCK_TOKENS * row_bytes(d, b) + meta
 
 
-def block_layout(num_kv_heads, d, bits_k, bits_v, meta_bytes=META_BYTES):
+def key_area_bytes(d, b, meta_bytes=META_BYTES, key_per_channel=False):
+    """A head's K area: per-token metadata as segment_bytes, or with per-channel
+    keys 16 code rows then one float32 {s, mn} pair per channel (d pairs)."""
+    if key_per_channel and b != 16:
+        return BLOCK_TOKENS * row_bytes(d, b) + d * META_BYTES
+    return segment_bytes(d, b, meta_bytes)
+
+
+def block_layout(num_kv_heads, d, bits_k, bits_v, meta_bytes=META_BYTES, key_per_channel=False):
     """Byte offsets of every head's K and V area inside a block.
 
     Order: K head 0, K head 1, ..., then V head 0, V head 1, ...
@@ -251,7 +282,7 @@ def block_layout(num_kv_heads, d, bits_k, bits_v, meta_bytes=META_BYTES):
     k_off, v_off = [], []
     for h in range(num_kv_heads):
         k_off.append(off)
-        off += segment_bytes(d, bits_k[h], meta_bytes)
+        off += key_area_bytes(d, bits_k[h], meta_bytes, key_per_channel)
     for h in range(num_kv_heads):
         v_off.append(off)
         off += segment_bytes(d, bits_v[h], meta_bytes)
@@ -261,8 +292,12 @@ def block_layout(num_kv_heads, d, bits_k, bits_v, meta_bytes=META_BYTES):
 class Layout:
     """The cache geometry of one pool: heads, head_dim, Hadamard block, bits."""
 
-    def __init__(self, num_kv_heads, group, head_dim, had_block, bits_k, bits_v, meta_fp16=False):
+    def __init__(self, num_kv_heads, group, head_dim, had_block, bits_k, bits_v, meta_fp16=False,
+                 key_per_channel=False):
         self.meta_fp16 = bool(meta_fp16)
+        self.key_per_channel = bool(key_per_channel)
+        if self.meta_fp16 and self.key_per_channel:
+            raise ValueError("per-channel keys keep float32 metadata")
         self.meta_bytes = 4 if self.meta_fp16 else META_BYTES
         self.hkv = int(num_kv_heads)
         self.group = int(group)
@@ -271,7 +306,7 @@ class Layout:
         self.bits_k = [int(b) for b in bits_k]
         self.bits_v = [int(b) for b in bits_v]
         self.k_off, self.v_off, self.block_bytes = block_layout(
-            self.hkv, self.d, self.bits_k, self.bits_v, self.meta_bytes)
+            self.hkv, self.d, self.bits_k, self.bits_v, self.meta_bytes, self.key_per_channel)
 
 
 # ---------------------------------------------------------------------------
@@ -322,10 +357,14 @@ def quantize_append(layout, pool, table, start_pos, k, v):
     k = np.asarray(k, dtype=np.float32)
     v = np.asarray(v, dtype=np.float32)
     batch, n_new, hkv, d = k.shape
+    if layout.key_per_channel:
+        _append_keys_per_channel(layout, pool, table, start_pos, k)
     for which, x, bits, offs in (("k", k, layout.bits_k, layout.k_off),
                                  ("v", v, layout.bits_v, layout.v_off)):
         for h in range(hkv):
             b = bits[h]
+            if which == "k" and layout.key_per_channel and b != 16:
+                continue  # written per page above
             rb = row_bytes(d, b)
             rows, s, mn = encode_rows(x[:, :, h, :], layout.n, b, layout.meta_fp16)
             for seq in range(batch):
@@ -342,6 +381,30 @@ def quantize_append(layout, pool, table, start_pos, k, v):
                         pool[blk, mbase: mbase + mb] = meta.view(np.uint8)
 
 
+def _append_keys_per_channel(layout, pool, table, start_pos, k):
+    """Per-channel keys: each page of 16 new tokens is one quantization group,
+    so appends must cover whole pages (start and count multiples of 16)."""
+    batch, n_new, hkv, d = k.shape
+    if n_new % BLOCK_TOKENS:
+        raise ValueError("per-channel keys are appended in whole pages")
+    for h in range(hkv):
+        b = layout.bits_k[h]
+        if b == 16:
+            continue
+        rb = row_bytes(d, b)
+        base = layout.k_off[h]
+        xr = rotate(k[:, :, h, :], layout.n)
+        for seq in range(batch):
+            if int(start_pos[seq]) % BLOCK_TOKENS:
+                raise ValueError("per-channel keys are appended in whole pages")
+            for i0 in range(0, n_new, BLOCK_TOKENS):
+                codes, s, mn = quantize_cols(xr[seq, i0:i0 + BLOCK_TOKENS], b)
+                blk = int(table[seq, (int(start_pos[seq]) + i0) // BLOCK_TOKENS])
+                pool[blk, base: base + BLOCK_TOKENS * rb] = pack_codes(codes, b).reshape(-1)
+                meta = np.stack([s, mn], axis=1).astype(np.float32)  # [d][{s, mn}]
+                pool[blk, base + BLOCK_TOKENS * rb: base + BLOCK_TOKENS * rb + d * META_BYTES] = meta.view(np.uint8).reshape(-1)
+
+
 def read_rows(layout, pool, table_row, pos0, n, h, which):
     """Return the rotated, dequantized fp32 rows [n, d] of one head (K or V)."""
     d = layout.d
@@ -356,6 +419,11 @@ def read_rows(layout, pool, table_row, pos0, n, h, which):
     if bits == 16:
         return bf16_bits_to_float32(raw.view(np.uint16).reshape(n, d))
     codes = unpack_codes(raw, bits, d)
+    if which == "k" and layout.key_per_channel:
+        mcols = base + BLOCK_TOKENS * rb + np.arange(d * META_BYTES)
+        meta = pool[blk[:, None], mcols[None, :]].copy().view(np.float32).reshape(n, d, 2)
+        prod = (codes.astype(np.float32) * meta[:, :, 0]).astype(np.float32)
+        return (prod + meta[:, :, 1]).astype(np.float32)
     mb = layout.meta_bytes
     mcols = base + BLOCK_TOKENS * rb + slot[:, None] * mb + np.arange(mb)[None, :]
     meta = pool[blk[:, None], mcols].copy().view(np.float16 if layout.meta_fp16 else np.float32)

@@ -645,3 +645,60 @@ def test_fp16_meta_layout_and_round_trip():
         assert np.array_equal(dk[:, h], O.dequantize_rows(ck, sk, mk))
         cv, sv, mv = O.quantize_rows_fp16_meta(O.rotate(v[0, :, h], 64), bv)
         assert np.array_equal(dv[:, h], O.dequantize_rows(cv, sv, mv))
+
+
+# ---------------------------------------------------------------------------
+# Per-channel keys (KIVI-style grouping: one page of 16 tokens per channel)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("b", [2, 3, 4, 8])
+def test_quantize_cols_is_the_row_quantizer_on_channels(b):
+    rng = np.random.default_rng(70 + b)
+    x = (rng.standard_normal((16, 64)) * rng.uniform(0.1, 20, 64)).astype(np.float32)
+    x[:, 5] = 2.5  # a constant channel
+    codes, s, mn = O.quantize_cols(x, b)
+    rc, rs, rmn = O.quantize_rows(x.T.copy(), b)
+    assert np.array_equal(codes, rc.T) and np.array_equal(s, rs) and np.array_equal(mn, rmn)
+    assert s[5] == 0 and np.all(codes[:, 5] == 0) and mn[5] == np.float32(2.5)
+    xh = (codes.astype(np.float32) * s[None, :]).astype(np.float32) + mn[None, :]
+    assert np.all(np.abs(xh - x) <= s[None, :] / 2 * (1 + 1e-6) + 1e-6 * np.abs(x).max(0))
+
+
+def test_quantize_cols_hand_example():
+    # channel 0 holds 0..15, channel 1 is constant 7: at 2 bits s_0 = 5, codes round (t / 5)
+    x = np.stack([np.arange(16, dtype=np.float32), np.full(16, 7, np.float32)], axis=1)
+    codes, s, mn = O.quantize_cols(x, 2)
+    assert s.tolist() == [5.0, 0.0] and mn.tolist() == [0.0, 7.0]
+    # t / 5 = 0.5 and 2.5 are ties that round to the even codes 0 and 2; 7.5 (t = 12.5) does not occur
+    assert codes[:, 0].tolist() == [0, 0, 0, 1, 1, 1, 1, 1, 2, 2, 2, 2, 2, 3, 3, 3]
+    assert np.all(codes[:, 1] == 0)
+
+
+def test_per_channel_key_layout_round_trip_and_attention():
+    lay = O.Layout(2, 2, 64, 16, [4, 2], [4, 3], key_per_channel=True)
+    assert lay.block_bytes == (16 * 32 + 64 * 8) + (16 * 16 + 64 * 8) + (16 * 32 + 16 * 8) + (16 * 24 + 16 * 8)
+    rng = np.random.default_rng(71)
+    k = rng.standard_normal((1, 48, 2, 64)).astype(np.float32) * 3
+    v = rng.standard_normal((1, 48, 2, 64)).astype(np.float32)
+    table = np.array([[2, 0, 3]], np.int32)
+    pool = np.zeros((4, lay.block_bytes), np.uint8)
+    O.quantize_append(lay, pool, table, np.array([0]), k, v)
+    dk, dv = O.dequant(lay, pool, table[0], 0, 48, rotated=True)
+    for h, b in enumerate((4, 2)):
+        xr = O.rotate(k[0, :, h], 16)
+        for p in range(3):
+            codes, s, mn = O.quantize_cols(xr[16 * p:16 * p + 16], b)
+            want = (codes.astype(np.float32) * s[None, :]).astype(np.float32) + mn[None, :]
+            assert np.array_equal(dk[16 * p:16 * p + 16, h], want)
+    # values stay per token
+    cv, sv, mv = O.quantize_rows(O.rotate(v[0, :, 1], 16), 3)
+    assert np.array_equal(dv[:, 1], O.dequantize_rows(cv, sv, mv))
+    # attention over the per-channel cache equals plain attention over its dequantized keys and values
+    q = rng.standard_normal((1, 4, 64))
+    got = O.decode_attention([(lay, pool, table, np.array([48]))], q)
+    for g in range(4):
+        h = g // 2
+        o = O.attention_plain(O.rotate(q[0, g:g + 1], 16)[0], dk[:, h], dv[:, h])
+        assert np.allclose(got[0, g], O.unrotate(o[None], 16)[0], rtol=1e-6, atol=1e-7)  # float32 output
+    with pytest.raises(ValueError):
+        O.quantize_append(lay, pool, table, np.array([0]), k[:, :20], v[:, :20])
