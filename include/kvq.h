@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 2
+#define KVQ_ABI_VERSION 3
 #define KVQ_MAX_KV_HEADS 64
 #define KVQ_BLOCK_TOKENS 16
 
@@ -69,7 +69,12 @@ typedef struct hipStream_t_opaque* kvq_stream; /* a hipStream_t */
  * { _Float16 scale; _Float16 min; } (4 bytes): the minimum is rounded down
  * and the scale up to float16 before the codes are computed from them, so
  * the codes still fit and the error stays within half a step (the rotated
- * values must lie within the float16 range). Per-head b may differ between heads
+ * values must lie within the float16 range). With key_per_channel = 1 (and
+ * float32 metadata) a K area with b < 16 instead holds codes[16][head_dim*b/8]
+ * then kmeta[head_dim] { float scale; float min; }: each channel of the
+ * rotated keys is quantized over the block's 16 tokens (the KIVI/Quanto key
+ * granularity [RQ: stage 3, KIVI's per-channel keys; LQ: Methodology 5]); V
+ * areas stay per token. Per-head b may differ between heads
  * and between K and V [RQ: stage 3, K/V decoupling; MKV: more bits for keys];
  * uniform blocks follow [SAW: section 1, PagedAttention].
  */
@@ -81,6 +86,7 @@ typedef struct kvq_layout {
   int32_t had_block;    /* n, Hadamard block: power of two, 1 <= n <= d (1 = no rotation) */
   int32_t block_tokens; /* must be KVQ_BLOCK_TOKENS */
   int32_t meta_fp16;    /* 0: float32 {s, mn} (8 B per row), 1: float16 {s, mn} (4 B per row) */
+  int32_t key_per_channel; /* 0: keys per token; 1: keys per channel over each block (needs meta_fp16 = 0) */
   int32_t bits_k[KVQ_MAX_KV_HEADS]; /* each in {2, 3, 4, 8, 16} */
   int32_t bits_v[KVQ_MAX_KV_HEADS];
   /* outputs of kvq_layout_init */
@@ -109,9 +115,10 @@ const char* kvq_last_error(void);
 
 /*
  * Host. Fill k_off, v_off and block_bytes from the inputs of *L.
- * Errors: KVQ_ERR_ARG for a null L, block_tokens != 16, meta_fp16 not 0 or 1,
+ * Errors: KVQ_ERR_ARG for a null L, block_tokens != 16, meta_fp16 or key_per_channel not 0 or 1,
  * num_kv_heads or group out of range, a bit width outside {2,3,4,8,16}, had_block not a power of
- * two or not dividing head_dim; KVQ_ERR_UNSUPPORTED for head_dim not 64/128.
+ * two or not dividing head_dim; KVQ_ERR_UNSUPPORTED for head_dim not 64/128
+ * or for key_per_channel together with meta_fp16.
  */
 kvq_status kvq_layout_init(kvq_layout* L);
 
@@ -264,7 +271,8 @@ kvq_status kvq_logquant_advance(int32_t batch, kvq_lq_state* states, kvq_lq_move
  *      had_block); their block tables must map every slot named;
  *      moves host [batch]. seq_lens and max_len of the segments are unused.
  * Errors: KVQ_ERR_ARG (null pointers, geometry mismatch, a slot outside a
- * table row), KVQ_ERR_DEVICE.
+ * table row), KVQ_ERR_UNSUPPORTED (a segment with per-channel keys),
+ * KVQ_ERR_DEVICE.
  */
 kvq_status kvq_logquant_requant(const kvq_segment* window, const kvq_segment* mid,
                                 const kvq_segment* low, int32_t batch,
@@ -292,7 +300,11 @@ kvq_status kvq_page_alloc(const int32_t* free_list, int32_t n_free, int32_t* cur
  * code = round_half_even((x' - mn) * (2^b - 1) / (mx - mn)) (s = 0 and codes 0
  * for a constant row), packed, and stored with {s, mn} at position
  * p = start_pos[b] + i: block block_table[b * table_stride + p / 16], slot p % 16.
- * For b = 16 the rotated row is stored as bf16.
+ * For b = 16 the rotated row is stored as bf16. With key_per_channel the keys
+ * of each block are quantized together, per channel over its 16 tokens (same
+ * formulas along the token axis), so such appends write whole blocks: n_new
+ * and every start_pos[b] must be multiples of 16 (n_new is checked; the keys
+ * of a sequence whose start_pos is not are not written).
  * In:  k, v device [batch][n_new][Hkv][head_dim] of in_dtype; start_pos device
  *      [batch]; block_table device. Every block the new tokens touch must be
  *      mapped; a row whose block id is outside [0, pool_blocks) is skipped.

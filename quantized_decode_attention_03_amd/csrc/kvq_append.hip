@@ -322,8 +322,98 @@ __device__ __forceinline__ void append_rows(const AppendArgs& a, int half, doubl
 // of the listed heads, in one launch.
 template <int BK, int BV, int D>
 __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a, double rs_n) {
-  if (blockIdx.z == 0) append_rows<BK, D>(a, 0, rs_n);
-  else append_rows<BV, D>(a, 1, rs_n);
+  if (blockIdx.z == 0) {
+    if (BK == 16 || !a.key_per_channel) append_rows<BK, D>(a, 0, rs_n);  // else append_kc_kernel
+  } else {
+    append_rows<BV, D>(a, 1, rs_n);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Per-channel keys (the KIVI/Quanto key granularity named by the RateQuant
+// summary, Methodology 3, and the LogQuant summary, Methodology 5): the 16
+// keys of a block are rotated like any row, then every channel is quantized
+// over the block's tokens with the row formulas along the token axis
+// (fp32 min and max, s = (max - min) / (2^b - 1), codes rounded half to
+// even). One wave per (block, head); lane l holds channels
+// [l*D/64, (l+1)*D/64) of all 16 rows, so the channel statistics stay in the
+// lane and the rotation's butterflies of stride >= D/64 cross lanes by xor
+// shuffles (fp64, exact like the row path). Codes go through LDS and are
+// packed as each row's bit-stream.
+// ---------------------------------------------------------------------------
+template <int BITS, int D>
+__global__ __launch_bounds__(64) void append_kc_kernel(AppendArgs a, double rs_n) {
+  constexpr int CPL = D / 64;
+  constexpr int RB = D * BITS / 8;
+  constexpr int WPR = RB / 4;  // 32-bit words per row
+  __shared__ uint8_t codes[kBlockTokens][D];
+  const int lane = threadIdx.x;
+  const int blocks_per_seq = a.n_new / kBlockTokens;
+  const int b = static_cast<int>(blockIdx.x) / blocks_per_seq;
+  const int bi = static_cast<int>(blockIdx.x) % blocks_per_seq;
+  const int h = a.heads[blockIdx.y];
+  const int64_t area = a.area_off[0][blockIdx.y];
+  const int start = a.start_pos[b];
+  const int p0 = start + bi * kBlockTokens;
+  const int page = p0 / kBlockTokens;
+  // whole, mapped blocks only (the condition is the same for the whole wave)
+  if (start < 0 || start % kBlockTokens != 0 || page >= a.table_stride) return;
+  const int64_t blk = a.table[static_cast<int64_t>(b) * a.table_stride + page];
+  if (blk < 0 || blk >= a.pool_blocks) return;
+  uint8_t* base = a.pool + blk * a.block_bytes + area;
+
+  float x[kBlockTokens][CPL];
+#pragma unroll
+  for (int t = 0; t < kBlockTokens; ++t) {
+    const size_t elem = ((static_cast<size_t>(b) * a.n_new + bi * kBlockTokens + t) * a.hkv + h) * D + lane * CPL;
+    double xd[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+      xd[c] = a.src_bf16 ? static_cast<double>(bf16lo_to_f(static_cast<const uint16_t*>(a.src[0])[elem + c]))
+                         : static_cast<double>(static_cast<const float*>(a.src[0])[elem + c]);
+    if constexpr (CPL == 2) {
+      if (a.had_block >= 2) {
+        const double u = xd[0], v = xd[1];
+        xd[0] = u + v;
+        xd[1] = u - v;
+      }
+    }
+    for (int m = 1; m * CPL < a.had_block; m <<= 1) {
+      const double sgn = (lane & m) ? -1.0 : 1.0;  // lower lane x + y, upper lane y - x
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) xd[c] = fma(sgn, xd[c], __shfl_xor(xd[c], m, 64));
+    }
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) x[t][c] = static_cast<float>(xd[c] * rs_n);
+  }
+  const float qmax = static_cast<float>((1 << BITS) - 1);
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    float mn = x[0][c], mx = x[0][c];
+#pragma unroll
+    for (int t = 1; t < kBlockTokens; ++t) { mn = fminf(mn, x[t][c]); mx = fmaxf(mx, x[t][c]); }
+    const float rng = mx - mn;
+    float s = 0.f, inv = 0.f;
+    if (rng > 0.f) {
+      s = rng / qmax;
+      inv = qmax / rng;
+    }
+#pragma unroll
+    for (int t = 0; t < kBlockTokens; ++t)
+      codes[t][lane * CPL + c] = static_cast<uint8_t>(fminf(fmaxf(__builtin_rintf((x[t][c] - mn) * inv), 0.f), qmax));
+    *reinterpret_cast<float2*>(base + kBlockTokens * RB + (lane * CPL + c) * kMetaBytes) = make_float2(s, mn);
+  }
+  __syncthreads();
+  for (int wi = lane; wi < kBlockTokens * WPR; wi += 64) {
+    const int t = wi / WPR, w0 = 32 * (wi % WPR);
+    uint64_t acc = 0;
+    for (int j = w0 / BITS; j < D && j * BITS < w0 + 32; ++j) {
+      const int o = j * BITS - w0;
+      const uint64_t c = codes[t][j];
+      acc |= o >= 0 ? (c << o) : (c >> (-o));
+    }
+    reinterpret_cast<uint32_t*>(base + t * RB)[wi % WPR] = static_cast<uint32_t>(acc);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -596,8 +686,9 @@ __global__ __launch_bounds__(256) void requant_kernel(RequantArgs a) {
 }
 
 // Read this lane's 8 stored values of one row back to fp32 (rotated basis).
+// metap: the row's {s, mn}, or with kc the first of the area's per-channel pairs.
 template <int BITS>
-__device__ __forceinline__ void load_row8(const uint8_t* rowp, const uint8_t* metap, bool meta16, int lane,
+__device__ __forceinline__ void load_row8(const uint8_t* rowp, const uint8_t* metap, bool meta16, bool kc, int lane,
                                           float (&x)[8]) {
   if constexpr (BITS == 16) {
     const uint4 w = *reinterpret_cast<const uint4*>(rowp + lane * 16);
@@ -618,8 +709,9 @@ __device__ __forceinline__ void load_row8(const uint8_t* rowp, const uint8_t* me
     } else {
       lo = c[0] | (static_cast<uint32_t>(c[1]) << 8) | (static_cast<uint32_t>(c[2]) << 16);
     }
-    float2 meta;
-    if (meta16) {
+    float2 meta = make_float2(0.f, 0.f);
+    if (kc) {
+    } else if (meta16) {
       const uint32_t w = *reinterpret_cast<const uint32_t*>(metap);
       meta = make_float2(f16_to_f(w & 0xffffu), f16_to_f(w >> 16));
     } else {
@@ -630,6 +722,7 @@ __device__ __forceinline__ void load_row8(const uint8_t* rowp, const uint8_t* me
       uint32_t code;
       if constexpr (BITS == 8) code = ((j < 4 ? lo : hi) >> (8 * (j & 3))) & 0xffu;
       else code = (lo >> (BITS * j)) & ((1u << BITS) - 1u);
+      if (kc) meta = reinterpret_cast<const float2*>(metap)[lane * 8 + j];  // channel lane*8 + j
       x[j] = static_cast<float>(code) * meta.x + meta.y;  // two roundings (contraction is off)
     }
   }
@@ -655,8 +748,8 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(DequantArgs a, float 
   float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (ok) {
     const uint8_t* base = a.pool + blk * a.block_bytes + area;
-    load_row8<BITS>(base + slot * RB, base + kBlockTokens * RB + slot * (a.meta16 ? 4 : kMetaBytes), a.meta16 != 0,
-                    lane, x);
+    const uint8_t* metap = base + kBlockTokens * RB + (a.kc ? 0 : slot * (a.meta16 ? 4 : kMetaBytes));
+    load_row8<BITS>(base + slot * RB, metap, a.meta16 != 0, a.kc != 0, lane, x);
   }
   if (!a.rotated) {
     fwht8(x, lane, a.had_block);  // H is symmetric: R^T applies the same butterflies
@@ -745,6 +838,30 @@ hipError_t launch_requant(const RequantArgs& a, int n_seqs, hipStream_t s) {
   else if (a.d == 128) hipLaunchKernelGGL(requant_kernel<128>, grid, dim3(256), 0, s, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+template <int BITS, int D>
+hipError_t launch_append_kc_t(const AppendArgs& a, double rs, hipStream_t s) {
+  const dim3 grid(a.batch * (a.n_new / kBlockTokens), a.n_heads);
+  hipLaunchKernelGGL((append_kc_kernel<BITS, D>), grid, dim3(64), 0, s, a, rs);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_kc(const AppendArgs& a, hipStream_t s) {
+  if (a.batch * a.n_new == 0 || a.n_heads == 0) return hipSuccess;
+  if (a.n_new % kBlockTokens != 0) return hipErrorInvalidValue;
+  const double rs = 1.0 / std::sqrt(static_cast<double>(a.had_block));
+  switch (a.bits[0] * 1000 + a.d) {
+    case 2064: return launch_append_kc_t<2, 64>(a, rs, s);
+    case 2128: return launch_append_kc_t<2, 128>(a, rs, s);
+    case 3064: return launch_append_kc_t<3, 64>(a, rs, s);
+    case 3128: return launch_append_kc_t<3, 128>(a, rs, s);
+    case 4064: return launch_append_kc_t<4, 64>(a, rs, s);
+    case 4128: return launch_append_kc_t<4, 128>(a, rs, s);
+    case 8064: return launch_append_kc_t<8, 64>(a, rs, s);
+    case 8128: return launch_append_kc_t<8, 128>(a, rs, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t s) {

@@ -1061,6 +1061,211 @@ __global__ __launch_bounds__(64 * NW) void decode_merge_kernel(MergeArgs a, floa
   }
 }
 
+// ---------------------------------------------------------------------------
+// Decode over per-channel keys (the KIVI/Quanto key granularity of the
+// RateQuant summary, Methodology 3, and the LogQuant summary, Methodology 5).
+// A key's dequantized value is code * s_c + mn_c with a {s, mn} pair per
+// channel and block, so the scale cannot be folded into one offset per token
+// as in the row layout; this kernel dequantizes and multiplies on the VALU in
+// fp32. One wave per (sequence, KV head, split), each split a contiguous run
+// of blocks. Scores: lane = (token t = lane % 16, channel quarter lane / 16),
+// summed over the quarters by xor shuffles. Online softmax in log2 units as
+// in the MFMA kernel, same partial format, so the same merge follows. Values
+// (per token): lane l owns channels [l*D/64, (l+1)*D/64) and accumulates
+// p_t * v_hat_t over the block's tokens.
+// ---------------------------------------------------------------------------
+// Code j of a little-endian bit-stream held in words w (B bits per code),
+// the stream starting at bit `off` of w[0].
+template <int B, int NW>
+__device__ __forceinline__ uint32_t stream_code(const uint32_t (&w)[NW], int j, int off) {
+  const int bit = off + j * B, wi = bit >> 5, sh = bit & 31;
+  const uint64_t two = static_cast<uint64_t>(w[wi]) | (static_cast<uint64_t>(w[wi + 1]) << 32);
+  return static_cast<uint32_t>(two >> sh) & ((1u << B) - 1u);
+}
+
+template <int KB, int VB, int D>
+__global__ __launch_bounds__(64) void decode_kc_kernel(DecodeArgs a, const int32_t* __restrict__ table,
+                                                       float qscale, int n_splits) {
+  constexpr int RBK = D * KB / 8, RBV = D * VB / 8;
+  constexpr int CPQ = D / 4;             // key channels per quarter (scores)
+  constexpr int NWQ = (31 + CPQ * KB) / 32 + 1;  // aligned words a quarter row can span
+  constexpr int CPL = D / 64;            // value channels per lane
+  constexpr float NEG_INF = -__builtin_huge_valf();
+  __shared__ float qs[4][D];
+  const int lane = threadIdx.x;
+  const int split = static_cast<int>(blockIdx.x) % n_splits;
+  const int unit = static_cast<int>(blockIdx.x) / n_splits;
+  const int hidx = unit % a.n_heads, b = unit / a.n_heads;
+  const int h = a.heads[hidx], G = a.group, hq = a.hkv * G;
+  const int seq_len = a.seq_lens[b];
+  const int pages = min((seq_len + kBlockTokens - 1) / kBlockTokens, a.table_stride);
+  const int pps = (pages + n_splits - 1) / n_splits;
+  const int p_lo = min(split * pps, pages), p_hi = min(p_lo + pps, pages);
+  const int32_t* trow = table + static_cast<int64_t>(b) * a.table_stride;
+
+  // ---- q~ = (R q) * log2(e) / sqrt(d) (R's 1/sqrt(n) folded into qscale) ----
+  {
+    const int64_t qrow0 = static_cast<int64_t>(b) * hq + h * G;
+    for (int e = lane; e < 4 * D; e += 64) {
+      const int r = e / D, c = e % D;
+      float v = 0.f;
+      if (r < G) {
+        const int64_t idx = (qrow0 + r) * D + c;
+        v = a.q_bf16 ? bf16lo_to_f(static_cast<const uint16_t*>(a.q)[idx]) : static_cast<const float*>(a.q)[idx];
+      }
+      qs[r][c] = v;
+    }
+    __syncthreads();
+    for (int st = 1; st < a.had_block; st <<= 1) {
+      for (int pi = lane; pi < 2 * D; pi += 64) {
+        const int r = pi / (D / 2), jj = pi % (D / 2);
+        const int j = (jj / st) * 2 * st + (jj % st);
+        const float u = qs[r][j], v = qs[r][j + st];
+        qs[r][j] = u + v;
+        qs[r][j + st] = u - v;
+      }
+      __syncthreads();
+    }
+    for (int e = lane; e < 4 * D; e += 64) qs[e / D][e % D] *= qscale;
+    __syncthreads();
+  }
+
+  const int t = lane & 15, qq = lane >> 4;
+  const int64_t koff = a.k_off[hidx], voff = a.v_off[hidx];
+  float m_run[4], l_part[4], o[4][CPL];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m_run[i] = -1e30f;
+    l_part[i] = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) o[i][c] = 0.f;
+  }
+  const uint32_t nblk = a.pool_blocks > 0x7fffffff ? 0x80000000u : static_cast<uint32_t>(a.pool_blocks);
+  for (int page = p_lo; page < p_hi; ++page) {
+    const int32_t blk = trow[page];
+    if (static_cast<uint32_t>(blk) >= nblk) continue;  // unmapped block: no tokens
+    const uint8_t* kb = a.pool + blk * a.block_bytes + koff;
+    const uint8_t* vb = a.pool + blk * a.block_bytes + voff;
+    const int tok0 = page * kBlockTokens;
+
+    // ---- scores of the block's 16 tokens ----
+    // this lane's quarter of its token's code row, from the aligned word that
+    // holds its first bit (rows are whole words; the guard word past a row's
+    // end stays inside the area: the channel metadata follows the codes)
+    const int qbit = qq * CPQ * KB;
+    const uint32_t* kwp = reinterpret_cast<const uint32_t*>(kb + t * RBK) + (qbit >> 5);
+    uint32_t kw[NWQ + 1];
+#pragma unroll
+    for (int i = 0; i < NWQ; ++i) kw[i] = kwp[i];
+    kw[NWQ] = 0u;
+    const float2* kmeta = reinterpret_cast<const float2*>(kb + kBlockTokens * RBK);
+    float z[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+    for (int cl = 0; cl < CPQ; ++cl) {
+      const int c = qq * CPQ + cl;
+      const float2 m = kmeta[c];
+      const float kh = static_cast<float>(stream_code<KB>(kw, cl, qbit & 31)) * m.x + m.y;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z[i] = fmaf(qs[i][c], kh, z[i]);
+    }
+    const bool valid = tok0 + t < seq_len;
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      z[i] += __shfl_xor(z[i], 16, 64);
+      z[i] += __shfl_xor(z[i], 32, 64);
+      z[i] = valid ? z[i] : NEG_INF;
+      const float gm = wave_max_scalar(z[i]);
+      if (gm > m_run[i]) {  // wave-uniform
+        const float alpha = __builtin_amdgcn_exp2f(m_run[i] - gm);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) o[i][c] *= alpha;
+        l_part[i] *= alpha;
+        m_run[i] = gm;
+      }
+      p[i] = __builtin_amdgcn_exp2f(z[i] - m_run[i]);
+      if (qq == 0) l_part[i] += p[i];
+    }
+
+    // ---- values: o += p_t * v_hat_t over the block's valid tokens ----
+    const int nvalid = min(kBlockTokens, seq_len - tok0);
+    for (int tt = 0; tt < nvalid; ++tt) {
+      const uint8_t* vrow = vb + tt * RBV;
+      float vh[CPL];
+      if constexpr (VB == 16) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) vh[c] = bf16lo_to_f(reinterpret_cast<const uint16_t*>(vrow)[lane * CPL + c]);
+      } else {
+        const float2 vm = reinterpret_cast<const float2*>(vb + kBlockTokens * RBV)[tt];
+        const int bit = lane * CPL * VB;
+        uint32_t vw[2];
+        vw[0] = reinterpret_cast<const uint32_t*>(vrow)[bit >> 5];
+        vw[1] = ((bit >> 5) + 1) * 4 < RBV ? reinterpret_cast<const uint32_t*>(vrow)[(bit >> 5) + 1] : 0u;
+        const uint64_t two = static_cast<uint64_t>(vw[0]) | (static_cast<uint64_t>(vw[1]) << 32);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          const uint32_t code = static_cast<uint32_t>(two >> ((bit & 31) + c * VB)) & ((1u << VB) - 1u);
+          vh[c] = static_cast<float>(code) * vm.x + vm.y;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pt = __shfl(p[i], tt, 64);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) o[i][c] = fmaf(pt, vh[c], o[i][c]);
+      }
+    }
+  }
+
+  // ---- partials (the MFMA kernel's format) ----
+  const int slot = a.slot_base + split;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (i >= G) break;
+    const float lsum = wave_sum_scalar(l_part[i]);
+    const int64_t bg = static_cast<int64_t>(b) * hq + h * G + i;
+    float* po = a.part_o + (bg * a.total_slots + slot) * D + lane * CPL;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) po[c] = o[i][c];
+    if (lane == 0) {
+      float* ml = a.part_ml + (bg * a.total_slots + slot) * 2;
+      ml[0] = lsum > 0.f ? m_run[i] : NEG_INF;
+      ml[1] = lsum;
+    }
+  }
+}
+
+template <int KB, int VB, int D>
+hipError_t launch_kc_t(const DecodeArgs& a, int n_splits, int batch, float qscale, hipStream_t s) {
+  if (a.batch != batch) return hipErrorInvalidValue;
+  dim3 grid(static_cast<unsigned>(n_splits) * a.n_heads * batch);
+  hipLaunchKernelGGL((decode_kc_kernel<KB, VB, D>), grid, dim3(64), 0, s, a, a.table, qscale, n_splits);
+  return hipGetLastError();
+}
+
+template <int KB, int D>
+hipError_t dispatch_kc_v(const DecodeArgs& a, int vbits, int n_splits, int batch, float qs, hipStream_t s) {
+  switch (vbits) {
+    case 2: return launch_kc_t<KB, 2, D>(a, n_splits, batch, qs, s);
+    case 3: return launch_kc_t<KB, 3, D>(a, n_splits, batch, qs, s);
+    case 4: return launch_kc_t<KB, 4, D>(a, n_splits, batch, qs, s);
+    case 8: return launch_kc_t<KB, 8, D>(a, n_splits, batch, qs, s);
+    case 16: return launch_kc_t<KB, 16, D>(a, n_splits, batch, qs, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int D>
+hipError_t dispatch_kc(const DecodeArgs& a, int kbits, int vbits, int n_splits, int batch, float qs, hipStream_t s) {
+  switch (kbits) {
+    case 2: return dispatch_kc_v<2, D>(a, vbits, n_splits, batch, qs, s);
+    case 3: return dispatch_kc_v<3, D>(a, vbits, n_splits, batch, qs, s);
+    case 4: return dispatch_kc_v<4, D>(a, vbits, n_splits, batch, qs, s);
+    case 8: return dispatch_kc_v<8, D>(a, vbits, n_splits, batch, qs, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <int KB, int VB, int D, bool M16>
 hipError_t launch_partial_t(const DecodeArgs& a, int n_splits, int batch, float qscale, hipStream_t s) {
   if (a.batch != batch || n_splits % kXcds != 0) return hipErrorInvalidValue;
@@ -1135,6 +1340,11 @@ hipError_t launch_decode_partial(const DecodeArgs& a, int kbits, int vbits, int 
   if (n_splits == 0 || batch == 0 || a.n_heads == 0) return hipSuccess;
   // q~ = (R q) * log2(e) / sqrt(d), with R's 1/sqrt(n) folded in.
   const float qscale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(a.had_block) * d));
+  if (a.kc && kbits != 16) {
+    if (d == 128) return dispatch_kc<128>(a, kbits, vbits, n_splits, batch, qscale, s);
+    if (d == 64) return dispatch_kc<64>(a, kbits, vbits, n_splits, batch, qscale, s);
+    return hipErrorInvalidValue;
+  }
   if (d == 128) return dispatch_k<128>(a, kbits, vbits, n_splits, batch, qscale, s);
   if (d == 64) return dispatch_k<64>(a, kbits, vbits, n_splits, batch, qscale, s);
   return hipErrorInvalidValue;

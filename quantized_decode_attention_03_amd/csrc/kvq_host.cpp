@@ -85,12 +85,21 @@ int64_t row_bytes(int d, int b) { return static_cast<int64_t>(d) * b / 8; }
 int64_t area_bytes(int d, int b, int meta_fp16) {
   return KVQ_BLOCK_TOKENS * row_bytes(d, b) + (b == 16 ? 0 : KVQ_BLOCK_TOKENS * (meta_fp16 ? 4 : 8));
 }
+// A K area with per-channel metadata: 16 code rows, then {s, mn} per channel.
+int64_t key_area_bytes(int d, int b, int meta_fp16, int per_channel) {
+  if (per_channel && b != 16) return KVQ_BLOCK_TOKENS * row_bytes(d, b) + static_cast<int64_t>(d) * 8;
+  return area_bytes(d, b, meta_fp16);
+}
 
 // Checks the inputs of a layout and that its outputs match them.
 kvq_status check_layout(const kvq_layout* L, const char* who) {
   if (!L) return fail(KVQ_ERR_ARG, "%s: null layout", who);
   if (L->block_tokens != KVQ_BLOCK_TOKENS) return fail(KVQ_ERR_ARG, "%s: block_tokens must be 16", who);
   if (L->meta_fp16 != 0 && L->meta_fp16 != 1) return fail(KVQ_ERR_ARG, "%s: meta_fp16 must be 0 or 1", who);
+  if (L->key_per_channel != 0 && L->key_per_channel != 1)
+    return fail(KVQ_ERR_ARG, "%s: key_per_channel must be 0 or 1", who);
+  if (L->key_per_channel && L->meta_fp16)
+    return fail(KVQ_ERR_UNSUPPORTED, "%s: per-channel keys keep float32 metadata", who);
   if (L->num_kv_heads < 1 || L->num_kv_heads > KVQ_MAX_KV_HEADS)
     return fail(KVQ_ERR_ARG, "%s: num_kv_heads %d out of [1, %d]", who, L->num_kv_heads, KVQ_MAX_KV_HEADS);
   if (L->group < 1 || L->group > 4) return fail(KVQ_ERR_ARG, "%s: group %d out of [1, 4]", who, L->group);
@@ -255,7 +264,7 @@ kvq_status kvq_layout_init(kvq_layout* L) {
   std::memset(L->v_off, 0, sizeof(L->v_off));
   for (int h = 0; h < L->num_kv_heads; ++h) {
     L->k_off[h] = off;
-    off += area_bytes(L->head_dim, L->bits_k[h], L->meta_fp16);
+    off += key_area_bytes(L->head_dim, L->bits_k[h], L->meta_fp16, L->key_per_channel);
   }
   for (int h = 0; h < L->num_kv_heads; ++h) {
     L->v_off[h] = off;
@@ -498,6 +507,8 @@ kvq_status kvq_logquant_requant(const kvq_segment* window, const kvq_segment* mi
     const kvq_layout& L0 = *window->layout;
     if (L.num_kv_heads != L0.num_kv_heads || L.head_dim != L0.head_dim || L.had_block != L0.had_block)
       return fail(KVQ_ERR_ARG, "%s: segment %d geometry differs from the window's", who, i);
+    if (L.key_per_channel)
+      return fail(KVQ_ERR_UNSUPPORTED, "%s: segment %d has per-channel keys (moved rows are per token)", who, i);
     if (!segs[i]->pool || !segs[i]->block_table || segs[i]->pool_blocks < 1 || segs[i]->table_stride < 1)
       return fail(KVQ_ERR_ARG, "%s: segment %d needs a pool and a block table", who, i);
     kvq::RequantSeg& sg = a.seg[i];
@@ -601,6 +612,8 @@ kvq_status kvq_quantize_append(const kvq_layout* L, void* pool, int64_t pool_blo
   if (pool_blocks < 1 || table_stride < 1) return fail(KVQ_ERR_ARG, "kvq_quantize_append: empty pool or table");
   if (static_cast<int64_t>(batch) * n_new > (int64_t{1} << 31) / 8)
     return fail(KVQ_ERR_ARG, "kvq_quantize_append: too many rows in one call");
+  if (L->key_per_channel && n_new % KVQ_BLOCK_TOKENS != 0)
+    return fail(KVQ_ERR_ARG, "kvq_quantize_append: per-channel keys are appended in whole blocks (n_new %d)", n_new);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   // one launch per distinct (K bits, V bits) pair, K and V rows together
   bool done[KVQ_MAX_KV_HEADS] = {};
@@ -617,6 +630,7 @@ kvq_status kvq_quantize_append(const kvq_layout* L, void* pool, int64_t pool_blo
     a.src[1] = v;
     a.src_bf16 = in_dtype == KVQ_BF16;
     a.meta16 = L->meta_fp16;
+    a.key_per_channel = L->key_per_channel;
     a.batch = batch;
     a.n_new = n_new;
     a.hkv = L->num_kv_heads;
@@ -635,6 +649,10 @@ kvq_status kvq_quantize_append(const kvq_layout* L, void* pool, int64_t pool_blo
     }
     hipError_t e = kvq::launch_append(a, s);
     if (e != hipSuccess) return device_status(e, "kvq_quantize_append launch");
+    if (L->key_per_channel && a.bits[0] != 16) {
+      e = kvq::launch_append_kc(a, s);
+      if (e != hipSuccess) return device_status(e, "kvq_quantize_append launch (per-channel keys)");
+    }
   }
   return ok();
 }
@@ -672,6 +690,7 @@ kvq_status kvq_dequant(const kvq_layout* L, const void* pool, int64_t pool_block
       a.rotated = rotated != 0;
       a.meta16 = L->meta_fp16;
       a.bits = bits[h0];
+      a.kc = half == 0 && L->key_per_channel && bits[h0] != 16;
       a.out = half ? v_out : k_out;
       for (int h = h0; h < L->num_kv_heads; ++h) {
         if (!done[h] && bits[h] == bits[h0]) {
@@ -757,6 +776,7 @@ kvq_status kvq_decode_partial(const kvq_segment* segs, int32_t n_segs, int32_t b
         a.q = q;
         a.q_bf16 = q_dtype == KVQ_BF16;
         a.meta16 = L.meta_fp16;
+        a.kc = L.key_per_channel;
         a.hkv = L.num_kv_heads;
         a.group = L.group;
         a.had_block = L.had_block;

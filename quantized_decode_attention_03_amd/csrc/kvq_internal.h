@@ -20,6 +20,7 @@ struct AppendArgs {
   const void* src[2];   // K, V: [batch][n_new][hkv][d]
   int32_t src_bf16;
   int32_t meta16;       // 1: float16 {s, mn} (4 bytes per row)
+  int32_t key_per_channel;  // 1: keys are written per block by append_kc_kernel, not per row
   int32_t batch, n_new, hkv, d, had_block;
   int32_t n_heads;      // heads in this launch
   int32_t bits[2];      // K bits, V bits of these heads
@@ -34,6 +35,7 @@ struct DequantArgs {
   const int32_t* table_row;  // this sequence's table row
   int32_t pos0, n, hkv, d, had_block, rotated;
   int32_t meta16;
+  int32_t kc;  // rows of a per-channel key area (metadata per channel)
   int32_t n_heads, bits;
   int32_t heads[KVQ_MAX_KV_HEADS];
   int64_t area_off[KVQ_MAX_KV_HEADS];
@@ -52,6 +54,7 @@ struct DecodeArgs {
   const void* q;       // [batch][hkv*group][d]
   int32_t q_bf16;
   int32_t meta16;      // 1: float16 {s, mn} (4 bytes per row)
+  int32_t kc;          // 1: keys quantized per channel over each block (decode_kc_kernel)
   int32_t hkv, group, had_block;
   int32_t batch;       // sequences (the grid covers batch x n_heads units)
   int32_t slot_base;   // first split slot of this segment
@@ -108,6 +111,8 @@ struct MergeArgs {
 
 // Launchers return hipSuccess or the launch error; they never synchronise.
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+// Per-channel keys of whole blocks (a.bits[0] < 16, n_new a multiple of 16).
+hipError_t launch_append_kc(const AppendArgs& a, hipStream_t s);
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t s);
 hipError_t launch_decode_partial(const DecodeArgs& a, int kbits, int vbits, int d, int n_splits,
                                  int batch, hipStream_t s);

@@ -14,7 +14,7 @@ import numpy as np
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkvq.so")
 
-KVQ_ABI_VERSION = 2
+KVQ_ABI_VERSION = 3
 KVQ_MAX_KV_HEADS = 64
 KVQ_BLOCK_TOKENS = 16
 
@@ -44,6 +44,7 @@ class KvqLayout(ctypes.Structure):
         ("had_block", ctypes.c_int32),
         ("block_tokens", ctypes.c_int32),
         ("meta_fp16", ctypes.c_int32),
+        ("key_per_channel", ctypes.c_int32),
         ("bits_k", ctypes.c_int32 * KVQ_MAX_KV_HEADS),
         ("bits_v", ctypes.c_int32 * KVQ_MAX_KV_HEADS),
         ("k_off", ctypes.c_int64 * KVQ_MAX_KV_HEADS),
@@ -171,13 +172,16 @@ def kvq_last_error():
     return lib().kvq_last_error().decode()
 
 
-def kvq_layout_init(num_kv_heads, group, head_dim, had_block, bits_k, bits_v, meta_fp16=False):
+def kvq_layout_init(num_kv_heads, group, head_dim, had_block, bits_k, bits_v, meta_fp16=False,
+                    key_per_channel=False):
     """Return an initialised KvqLayout (bits_k / bits_v: one width per KV head; meta_fp16: 4-byte
-    float16 {s, mn} per row instead of 8-byte float32)."""
+    float16 {s, mn} per row instead of 8-byte float32; key_per_channel: keys quantized per channel over
+    each 16-token block)."""
     L = KvqLayout()
     L.num_kv_heads, L.group, L.head_dim, L.had_block = num_kv_heads, group, head_dim, had_block
     L.block_tokens = KVQ_BLOCK_TOKENS
     L.meta_fp16 = int(bool(meta_fp16))
+    L.key_per_channel = int(bool(key_per_channel))
     bits_k, bits_v = list(bits_k), list(bits_v)
     if len(bits_k) != num_kv_heads or len(bits_v) != num_kv_heads:
         raise ValueError("bits_k and bits_v need one entry per KV head")

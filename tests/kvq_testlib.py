@@ -49,7 +49,8 @@ class GpuCache:
 def oracle_layout(L, heads=None):
     heads = list(range(L.num_kv_heads)) if heads is None else list(heads)
     return O.Layout(len(heads), L.group, L.head_dim, L.had_block,
-                    [L.bits_k[h] for h in heads], [L.bits_v[h] for h in heads], meta_fp16=bool(L.meta_fp16))
+                    [L.bits_k[h] for h in heads], [L.bits_v[h] for h in heads], meta_fp16=bool(L.meta_fp16),
+                    key_per_channel=bool(L.key_per_channel))
 
 
 def oracle_cache(lay, table_np, start, k, v, n_blocks):

@@ -508,3 +508,116 @@ def test_quant_mse_fit_gives_a_geometric_curve():
     assert r2 >= 0.99 and 3.6 <= beta <= 5.3
     ea, eb, er2 = O.fit_distortion(widths, O.quant_mse(x.cpu().numpy(), 128, widths))
     assert abs(beta / eb - 1) < 1e-9 and abs(alpha / ea - 1) < 1e-9
+
+
+# ---------------------------------------------------------------------------
+# Per-channel keys (keys quantized per channel over each 16-token block)
+# ---------------------------------------------------------------------------
+
+def compare_kc_keys(L, lay, cache, ref, table, k, lens):
+    """Key code rows and per-channel metadata of every block, GPU against oracle: identical except codes
+    one step apart at rounding ties of the oracle's own per-channel arithmetic."""
+    gpu = cache.pool.cpu().numpy()
+    d, n = L.head_dim, L.had_block
+    mismatch = total = 0
+    for b, t in enumerate(lens):
+        for h in range(L.num_kv_heads):
+            bits = L.bits_k[h]
+            rb = d * bits // 8
+            off = L.k_off[h]
+            xr = O.rotate(k[b, :t, h, :], n)
+            for p in range(t // 16):
+                blk = table[b, p]
+                area_g, area_r = gpu[blk, off:off + 16 * rb + d * 8], ref[blk, off:off + 16 * rb + d * 8]
+                mg = area_g[16 * rb:].copy().view(np.float32).reshape(d, 2)
+                mr = area_r[16 * rb:].copy().view(np.float32).reshape(d, 2)
+                assert np.array_equal(mg, mr), "per-channel metadata differs"
+                cg = T.decode_codes(area_g[:16 * rb].reshape(16, rb), bits, d)
+                cr = T.decode_codes(area_r[:16 * rb].reshape(16, rb), bits, d)
+                total += cg.size
+                diff = cg != cr
+                if diff.any():
+                    assert np.abs(cg.astype(int) - cr)[diff].max() == 1
+                    r_, c_ = np.nonzero(diff)
+                    x = xr[16 * p:16 * p + 16]
+                    inv = (np.float32(2 ** bits - 1) / (x.max(0) - x.min(0))).astype(np.float32)
+                    u = ((x[r_, c_] - x.min(0)[c_]).astype(np.float32) * inv[c_]).astype(np.float64)
+                    assert np.all(np.abs(u - np.floor(u) - 0.5) < 1e-3), "code mismatch away from a tie"
+                    mismatch += int(diff.sum())
+    assert mismatch <= TIE_RATE * max(total, 1) + 1
+
+
+KC_FORMATS = [
+    (128, 128, 4, [4, 4], [4, 4]),
+    (128, 32, 2, [2, 8], [2, 16]),
+    (64, 64, 4, [3, 4], [3, 8]),
+    (64, 1, 2, [8, 2], [4, 2]),
+]
+
+
+@pytest.mark.parametrize("d,n,g,bk,bv", KC_FORMATS)
+def test_per_channel_keys_append_dequant_decode(d, n, g, bk, bv):
+    stored = [320, 320, 320]         # whole blocks
+    lens = [64, 9, 301]              # decode reads fewer tokens than are stored
+    hkv = len(bk)
+    rng = np.random.default_rng(d + n)
+    k = rng.standard_normal((3, 320, hkv, d)).astype(np.float32) * rng.uniform(0.5, 3.0, (1, 1, hkv, d)).astype(np.float32)
+    k += rng.standard_normal((1, 1, hkv, d)).astype(np.float32) * 2
+    v = rng.standard_normal((3, 320, hkv, d)).astype(np.float32)
+    k, v = synth.bf16_round(k), synth.bf16_round(v)
+    L = kvq.kvq_layout_init(hkv, g, d, n, bk, bv, key_per_channel=True)
+    n_blocks = sum(s // 16 for s in stored) + 3
+    table = T.alloc_tables(3, stored, n_blocks, seed=90, stride=20)
+    cache = T.GpuCache(L, n_blocks, table)
+    lay = T.oracle_layout(L)
+    assert lay.key_per_channel and lay.block_bytes == L.block_bytes
+    ref = np.zeros((n_blocks, lay.block_bytes), np.uint8)
+    for c0, cn in ((0, 16), (16, 304)):   # two appends of whole blocks
+        kt = torch.from_numpy(np.ascontiguousarray(k[:, c0:c0 + cn])).to(T.DEV).bfloat16()
+        vt = torch.from_numpy(np.ascontiguousarray(v[:, c0:c0 + cn])).to(T.DEV).bfloat16()
+        cache.append(kt, vt, [c0] * 3)
+        O.quantize_append(lay, ref, table, np.array([c0] * 3), k[:, c0:c0 + cn], v[:, c0:c0 + cn])
+    compare_kc_keys(L, lay, cache, ref, table, k, stored)
+    stats = T.CodeStats()
+    gpu_pool = cache.pool.cpu().numpy()
+    for b in range(3):
+        pos = np.arange(320)
+        for h in range(hkv):
+            g_rows, g_meta = T.gather_rows(gpu_pool, L.block_bytes, table, b, pos, L.v_off[h], d, bv[h])
+            r_rows, r_meta = T.gather_rows(ref, L.block_bytes, table, b, pos, L.v_off[h], d, bv[h])
+            T.compare_rows(g_rows, g_meta, r_rows, r_meta, O.rotate(v[b, :, h, :], n), bv[h], d, stats)
+    assert stats.rate <= TIE_RATE
+    # dequant: identical stored keys give identical rows
+    gk, gv = [x.cpu().numpy() for x in kvq.kvq_dequant(L, cache.pool, cache.table, 2, 0, 320, rotated=True)]
+    rk, rv = O.dequant(lay, ref, table[2], 0, 320, rotated=True)
+    assert np.mean(gk == rk) > 0.999 and np.max(np.abs(gk - rk)) <= np.abs(rk).max() * 0.2
+    # decode over the per-channel cache
+    q = synth.bf16_round(rng.standard_normal((3, hkv * g, d)).astype(np.float32))
+    out, expect = decode_both(L, lay, cache, ref, table, lens, q)
+    assert T.max_rel_err(out, expect) <= T.ATTN_TOL
+
+
+def test_per_channel_keys_with_a_bf16_residual_segment():
+    # the KIVI arrangement: whole blocks quantized per channel, the newest tokens in bf16
+    hkv, g, d, n = 2, 4, 128, 128
+    rng = np.random.default_rng(95)
+    k = synth.bf16_round(rng.standard_normal((2, 200, hkv, d)).astype(np.float32) * 2)
+    v = synth.bf16_round(rng.standard_normal((2, 200, hkv, d)).astype(np.float32))
+    q = synth.bf16_round(rng.standard_normal((2, hkv * g, d)).astype(np.float32))
+    segs, ref_segs, keep = [], [], []
+    for kc, lo, hi, bits in ((True, 0, 192, 4), (False, 192, 200, 16)):
+        L = kvq.kvq_layout_init(hkv, g, d, n, [bits] * hkv, [bits] * hkv, key_per_channel=kc)
+        cnt = hi - lo
+        nb = 2 * (-(-cnt // 16)) + 1
+        table = T.alloc_tables(2, [cnt, cnt], nb, seed=96 + lo)
+        cache = T.GpuCache(L, nb, table)
+        kk, vv = np.ascontiguousarray(k[:, lo:hi]), np.ascontiguousarray(v[:, lo:hi])
+        cache.append(torch.from_numpy(kk).to(T.DEV).bfloat16(), torch.from_numpy(vv).to(T.DEV).bfloat16(), [0, 0])
+        lay = T.oracle_layout(L)
+        ref = T.oracle_cache(lay, table, [0, 0], kk, vv, nb)
+        segs.append(cache.segment([cnt, cnt]))
+        ref_segs.append((lay, ref, table, np.array([cnt, cnt])))
+        keep.append(cache)
+    out = kvq.kvq_decode_attn(segs, torch.from_numpy(q).to(T.DEV).bfloat16()).cpu().numpy()
+    expect = O.decode_attention(ref_segs, q.astype(np.float64))
+    assert T.max_rel_err(out, expect) <= T.ATTN_TOL

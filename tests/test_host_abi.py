@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     for name in sorted(declared):
         assert hasattr(lib, name), name
     assert declared == set(kvq.EXPORTED)
-    assert kvq.kvq_abi_version() == 2
+    assert kvq.kvq_abi_version() == 3
     assert kvq.kvq_status_str(kvq.KVQ_ERR_BUDGET) == "KVQ_ERR_BUDGET"
 
 
@@ -36,11 +36,22 @@ def test_library_exports_every_declared_symbol():
     (8, 128, 32, [2, 3, 4, 8, 16, 2, 3, 4], [8, 4, 3, 2, 16, 16, 2, 8]),
 ])
 def test_layout_matches_oracle(hkv, d, n, bk, bv):
-    for m16 in (False, True):
-        L = kvq.kvq_layout_init(hkv, 4, d, n, bk, bv, meta_fp16=m16)
-        k_off, v_off, total = O.block_layout(hkv, d, bk, bv, 4 if m16 else 8)
+    for m16, kc in ((False, False), (True, False), (False, True)):
+        L = kvq.kvq_layout_init(hkv, 4, d, n, bk, bv, meta_fp16=m16, key_per_channel=kc)
+        k_off, v_off, total = O.block_layout(hkv, d, bk, bv, 4 if m16 else 8, kc)
         assert L.block_bytes == total
         assert list(L.k_off[:hkv]) == k_off and list(L.v_off[:hkv]) == v_off
+
+
+def test_per_channel_key_layout_rules():
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_layout_init(2, 4, 64, 64, [4, 4], [4, 4], meta_fp16=True, key_per_channel=True)
+    assert e.value.status == kvq.KVQ_ERR_UNSUPPORTED
+    # appends of per-channel keys come in whole blocks
+    L = kvq.kvq_layout_init(2, 4, 64, 64, [4, 4], [4, 4], key_per_channel=True)
+    p = ctypes.c_void_p(0x1000)
+    st = kvq.lib().kvq_quantize_append(ctypes.byref(L), p, 4, p, 4, 1, p, 20, p, p, kvq.KVQ_F32, None)
+    assert st == kvq.KVQ_ERR_ARG
 
 
 def test_layout_rejects_bad_arguments():
