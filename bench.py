@@ -248,7 +248,8 @@ def build_decode_layers(args, kvq, torch, dev):
     batch, tokens = B, T
     bk, bv = (16, 16) if args.workload == "bf16_32k" else (BITS_K, BITS_V)
     m16 = args.workload == "llama32k_m16"
-    L = kvq.kvq_layout_init(HKV, G, D, HAD, [bk] * HKV, [bv] * HKV, meta_fp16=m16)
+    kc = args.workload == "kivi32k"
+    L = kvq.kvq_layout_init(HKV, G, D, HAD, [bk] * HKV, [bv] * HKV, meta_fp16=m16, key_per_channel=kc)
     for l in range(args.layers):
         seed = SEED_BASE + l
         pool, table = make_pool(kvq, torch, dev, L, batch, tokens, seed)
@@ -256,8 +257,24 @@ def build_decode_layers(args, kvq, torch, dev):
         kvq.kvq_quantize_append(L, pool, table, torch.zeros(batch, dtype=torch.int32, device=dev), k, v)
         lens = torch.full((batch,), tokens, dtype=torch.int32, device=dev)
         layers.append({"segs": [(L, pool, table, lens, tokens)], "q": q, "app": 0,
-                       "new_k": k[:, T - 1:T].contiguous(), "new_v": v[:, T - 1:T].contiguous(), "pos": T - 1})
+                       "new_k": k[:, T - 1:T].contiguous(), "new_v": v[:, T - 1:T].contiguous(), "pos": T - 1,
+                       "new_k_block": k[:, T - 16:T].contiguous() if kc else None,
+                       "new_v_block": v[:, T - 16:T].contiguous() if kc else None})
         del k, v
+    if kc:
+        # per-channel keys cannot take single tokens: the step's new token is written as the block that
+        # holds it (its 16 tokens re-quantized), the cost a KIVI-style cache pays when a block completes
+        for ly in layers:
+            ly["new_k"] = ly["new_k_block"]
+            ly["new_v"] = ly["new_v_block"]
+            ly["pos"] = T - 16
+        config = {"workload": WORKLOAD.replace("K4/V4 token-wise INT4", "K4 per channel over each 16-token block, "
+                                               "V4 per token"),
+                  "layers": args.layers, "batch": B, "ctx": T, "kv_heads": HKV, "q_per_kv": G, "head_dim": D,
+                  "bits_k": BITS_K, "bits_v": BITS_V, "had_block": HAD, "keys": "per channel"}
+        per_tok = D * BITS_K // 8 + D * 8 // 16 + D * BITS_V // 8 + 8
+        return (layers, config, batch, B * HKV * T * per_tok + B * (T // 16) * 4 + B * HKV * G * D * 2,
+                "decode_kc_kernel<4,4,128>")
     if m16:
         config = {"workload": WORKLOAD.replace("K4/V4 token-wise INT4", "K4/V4 token-wise INT4 with float16 {s, mn}"),
                   "layers": args.layers, "batch": B, "ctx": T, "kv_heads": HKV, "q_per_kv": G, "head_dim": D,
@@ -599,7 +616,7 @@ def run_tiny(args, torch, dev, kvq):
 
 
 WORKLOADS = ("llama32k", "mixed32k", "long131k", "bulk16k", "tiny", "bf16_32k", "calib", "long131k_dyn",
-             "llama32k_m16")
+             "llama32k_m16", "kivi32k")
 
 
 def main():
@@ -614,7 +631,8 @@ def main():
                          "prefill append; tiny: the 1024-token layer; bf16_32k: the llama32k shape with "
                          "16-bit rows (the unquantized baseline); calib: kvq_quant_mse over a key "
                          "calibration set; long131k_dyn: long131k grown one token per step with LogQuant's "
-                         "dynamic adjustment; llama32k_m16: llama32k with float16 metadata")
+                         "dynamic adjustment; llama32k_m16: llama32k with float16 metadata; kivi32k: llama32k "
+                         "with keys quantized per channel over each block")
     ap.add_argument("--graph", action=argparse.BooleanOptionalAction, default=True,
                     help="decode workloads: after the eager timed steps (which give the partial kernel's "
                          "per-launch times), capture the same steps as one HIP graph and take the step rate "

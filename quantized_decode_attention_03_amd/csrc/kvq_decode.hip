@@ -1083,15 +1083,65 @@ __device__ __forceinline__ uint32_t stream_code(const uint32_t (&w)[NW], int j, 
   return static_cast<uint32_t>(two >> sh) & ((1u << B) - 1u);
 }
 
+// Blocks in flight while one is computed: each wave holds a few KB of loads in
+// flight, and enough of them keep the memory system busy despite the short
+// compute per block.
+constexpr int kKcDepth = 4;
+
+// One block's data for one lane, loaded a block ahead of its use.
+template <int KB, int VB, int D>
+struct KcBlock {
+  static constexpr int CPQ = D / 4;
+  static constexpr int NWQ = (31 + CPQ * KB) / 32 + 1;            // aligned words a quarter row can span
+  static constexpr int CPL = D / 64;
+  static constexpr int VW = (32 % (CPL * VB) == 0 || VB == 16) ? 1 : 2;  // words per value token (3-bit straddles)
+  float4 kmeta;            // the block's key channel pairs {s, mn} of channels 2 * lane, 2 * lane + 1
+  uint32_t kw[NWQ + 1];    // key codes of this lane's (token, quarter)
+  uint32_t vw[16][VW];     // per token: the word(s) holding this lane's value channels
+  float2 vmeta;            // lane < 16: {s, mn} of value token `lane`
+  int ok;                  // the block is mapped
+};
+
+// Loads of block `page` of the split [p_lo, p_hi); a position past p_hi loads
+// block 0 and is marked empty, so every position issues the same loads.
+template <int KB, int VB, int D>
+__device__ __forceinline__ void kc_load(const DecodeArgs& a, const int32_t* trow, int page, int p_hi, uint32_t nblk,
+                                        int lane, int64_t koff, int64_t voff, KcBlock<KB, VB, D>& g) {
+  using KBL = KcBlock<KB, VB, D>;
+  constexpr int RBK = D * KB / 8, RBV = D * VB / 8;
+  const int32_t blk = page < p_hi ? trow[page] : -1;
+  g.ok = static_cast<uint32_t>(blk) < nblk;
+  // (an unmapped block reads block 0 and is skipped, so the loads are the same every time)
+  const uint8_t* base = a.pool + (g.ok ? blk : 0) * a.block_bytes;
+  const uint8_t* kb = base + koff;
+  const uint8_t* vb = base + voff;
+  const int t = lane & 15, qq = lane >> 4;
+  g.kmeta = lane < D / 2 ? reinterpret_cast<const float4*>(kb + kBlockTokens * RBK)[lane] : make_float4(0, 0, 0, 0);
+  const uint32_t* kwp = reinterpret_cast<const uint32_t*>(kb + t * RBK) + ((qq * KBL::CPQ * KB) >> 5);
+#pragma unroll
+  for (int i = 0; i < KBL::NWQ; ++i) g.kw[i] = kwp[i];
+  g.kw[KBL::NWQ] = 0u;
+  const int bit = lane * KBL::CPL * VB;
+#pragma unroll
+  for (int tt = 0; tt < 16; ++tt) {
+    const uint32_t* row = reinterpret_cast<const uint32_t*>(vb + tt * RBV);
+    g.vw[tt][0] = row[bit >> 5];
+    if constexpr (KBL::VW == 2) g.vw[tt][1] = ((bit >> 5) + 1) * 4 < RBV ? row[(bit >> 5) + 1] : 0u;
+  }
+  g.vmeta = (VB != 16 && lane < 16) ? reinterpret_cast<const float2*>(vb + kBlockTokens * RBV)[lane]
+                                    : make_float2(1.f, 0.f);
+}
+
 template <int KB, int VB, int D>
 __global__ __launch_bounds__(64) void decode_kc_kernel(DecodeArgs a, const int32_t* __restrict__ table,
                                                        float qscale, int n_splits) {
-  constexpr int RBK = D * KB / 8, RBV = D * VB / 8;
-  constexpr int CPQ = D / 4;             // key channels per quarter (scores)
-  constexpr int NWQ = (31 + CPQ * KB) / 32 + 1;  // aligned words a quarter row can span
-  constexpr int CPL = D / 64;            // value channels per lane
+  using KBL = KcBlock<KB, VB, D>;
+  constexpr int CPQ = KBL::CPQ, CPL = KBL::CPL;
   constexpr float NEG_INF = -__builtin_huge_valf();
-  __shared__ float qs[4][D];
+  __shared__ float4 qt[D];                 // q~ of the four query rows, channel-major
+  __shared__ float qs[4][D];               // (rotation workspace)
+  __shared__ __attribute__((aligned(16))) float2 kms[D];  // the current block's key channel metadata
+  __shared__ float2 vms[16];               // the current block's value metadata
   const int lane = threadIdx.x;
   const int split = static_cast<int>(blockIdx.x) % n_splits;
   const int unit = static_cast<int>(blockIdx.x) / n_splits;
@@ -1102,6 +1152,13 @@ __global__ __launch_bounds__(64) void decode_kc_kernel(DecodeArgs a, const int32
   const int pps = (pages + n_splits - 1) / n_splits;
   const int p_lo = min(split * pps, pages), p_hi = min(p_lo + pps, pages);
   const int32_t* trow = table + static_cast<int64_t>(b) * a.table_stride;
+  const uint32_t nblk = a.pool_blocks > 0x7fffffff ? 0x80000000u : static_cast<uint32_t>(a.pool_blocks);
+  const int64_t koff = a.k_off[hidx], voff = a.v_off[hidx];
+
+  constexpr int NB = kKcDepth + 1;
+  KBL gb[NB];
+#pragma unroll
+  for (int j = 0; j < kKcDepth; ++j) kc_load<KB, VB, D>(a, trow, p_lo + j, p_hi, nblk, lane, koff, voff, gb[j]);
 
   // ---- q~ = (R q) * log2(e) / sqrt(d) (R's 1/sqrt(n) folded into qscale) ----
   {
@@ -1126,12 +1183,12 @@ __global__ __launch_bounds__(64) void decode_kc_kernel(DecodeArgs a, const int32
       }
       __syncthreads();
     }
-    for (int e = lane; e < 4 * D; e += 64) qs[e / D][e % D] *= qscale;
+    for (int c = lane; c < D; c += 64)
+      qt[c] = make_float4(qs[0][c] * qscale, qs[1][c] * qscale, qs[2][c] * qscale, qs[3][c] * qscale);
     __syncthreads();
   }
 
   const int t = lane & 15, qq = lane >> 4;
-  const int64_t koff = a.k_off[hidx], voff = a.v_off[hidx];
   float m_run[4], l_part[4], o[4][CPL];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -1140,33 +1197,46 @@ __global__ __launch_bounds__(64) void decode_kc_kernel(DecodeArgs a, const int32
 #pragma unroll
     for (int c = 0; c < CPL; ++c) o[i][c] = 0.f;
   }
-  const uint32_t nblk = a.pool_blocks > 0x7fffffff ? 0x80000000u : static_cast<uint32_t>(a.pool_blocks);
-  for (int page = p_lo; page < p_hi; ++page) {
-    const int32_t blk = trow[page];
-    if (static_cast<uint32_t>(blk) >= nblk) continue;  // unmapped block: no tokens
-    const uint8_t* kb = a.pool + blk * a.block_bytes + koff;
-    const uint8_t* vb = a.pool + blk * a.block_bytes + voff;
+  auto compute = [&](KBL& g, int page) {
+    if (!g.ok) return;
     const int tok0 = page * kBlockTokens;
-
+    __syncthreads();  // the previous block's metadata has been read
+    if (lane < D / 2) reinterpret_cast<float4*>(kms)[lane] = g.kmeta;
+    if (lane < 16) vms[lane] = g.vmeta;
+    __syncthreads();
     // ---- scores of the block's 16 tokens ----
-    // this lane's quarter of its token's code row, from the aligned word that
-    // holds its first bit (rows are whole words; the guard word past a row's
-    // end stays inside the area: the channel metadata follows the codes)
-    const int qbit = qq * CPQ * KB;
-    const uint32_t* kwp = reinterpret_cast<const uint32_t*>(kb + t * RBK) + (qbit >> 5);
-    uint32_t kw[NWQ + 1];
+    // (the quarter starts at bit 0 of its first word except at head_dim 64 with
+    // 3-bit keys, where odd quarters start at bit 16: shift the words once, so
+    // every code below sits at a compile-time bit position and the words stay
+    // in registers)
+    uint32_t kw[KBL::NWQ + 1];
+    if constexpr ((CPQ * KB) % 32 == 0) {
 #pragma unroll
-    for (int i = 0; i < NWQ; ++i) kw[i] = kwp[i];
-    kw[NWQ] = 0u;
-    const float2* kmeta = reinterpret_cast<const float2*>(kb + kBlockTokens * RBK);
+      for (int i = 0; i <= KBL::NWQ; ++i) kw[i] = g.kw[i];
+    } else {
+      const int off = (qq * CPQ * KB) & 31;  // 0 or 16
+#pragma unroll
+      for (int i = 0; i < KBL::NWQ; ++i) kw[i] = off ? (g.kw[i] >> 16) | (g.kw[i + 1] << 16) : g.kw[i];
+      kw[KBL::NWQ] = 0u;
+    }
     float z[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-    for (int cl = 0; cl < CPQ; ++cl) {
-      const int c = qq * CPQ + cl;
-      const float2 m = kmeta[c];
-      const float kh = static_cast<float>(stream_code<KB>(kw, cl, qbit & 31)) * m.x + m.y;
+    // word by word (codes that start in word wi), so every register index is static
+    constexpr int NWORDS = (CPQ * KB + 31) / 32;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) z[i] = fmaf(qs[i][c], kh, z[i]);
+    for (int wi = 0; wi < NWORDS; ++wi) {
+      const uint64_t two = static_cast<uint64_t>(kw[wi]) | (static_cast<uint64_t>(kw[wi + 1]) << 32);
+#pragma unroll
+      for (int cl = (32 * wi + KB - 1) / KB; cl < CPQ && cl * KB < 32 * (wi + 1); ++cl) {
+        const int c = qq * CPQ + cl;
+        const float2 m = kms[c];
+        const uint32_t code = static_cast<uint32_t>(two >> (cl * KB - 32 * wi)) & ((1u << KB) - 1u);
+        const float kh = static_cast<float>(code) * m.x + m.y;
+        const float4 qv = qt[c];
+        z[0] = fmaf(qv.x, kh, z[0]);
+        z[1] = fmaf(qv.y, kh, z[1]);
+        z[2] = fmaf(qv.z, kh, z[2]);
+        z[3] = fmaf(qv.w, kh, z[3]);
+      }
     }
     const bool valid = tok0 + t < seq_len;
     float p[4];
@@ -1186,34 +1256,41 @@ __global__ __launch_bounds__(64) void decode_kc_kernel(DecodeArgs a, const int32
       p[i] = __builtin_amdgcn_exp2f(z[i] - m_run[i]);
       if (qq == 0) l_part[i] += p[i];
     }
-
-    // ---- values: o += p_t * v_hat_t over the block's valid tokens ----
+    // ---- values ----
     const int nvalid = min(kBlockTokens, seq_len - tok0);
-    for (int tt = 0; tt < nvalid; ++tt) {
-      const uint8_t* vrow = vb + tt * RBV;
-      float vh[CPL];
-      if constexpr (VB == 16) {
+    const int bit = (lane * CPL * VB) & 31;
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) vh[c] = bf16lo_to_f(reinterpret_cast<const uint16_t*>(vrow)[lane * CPL + c]);
-      } else {
-        const float2 vm = reinterpret_cast<const float2*>(vb + kBlockTokens * RBV)[tt];
-        const int bit = lane * CPL * VB;
-        uint32_t vw[2];
-        vw[0] = reinterpret_cast<const uint32_t*>(vrow)[bit >> 5];
-        vw[1] = ((bit >> 5) + 1) * 4 < RBV ? reinterpret_cast<const uint32_t*>(vrow)[(bit >> 5) + 1] : 0u;
-        const uint64_t two = static_cast<uint64_t>(vw[0]) | (static_cast<uint64_t>(vw[1]) << 32);
+    for (int tt = 0; tt < 16; ++tt) {
+      if (tt < nvalid) {  // wave-uniform
+        float vh[CPL];
+        if constexpr (VB == 16) {
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-          const uint32_t code = static_cast<uint32_t>(two >> ((bit & 31) + c * VB)) & ((1u << VB) - 1u);
-          vh[c] = static_cast<float>(code) * vm.x + vm.y;
+          for (int c = 0; c < CPL; ++c) vh[c] = bf16lo_to_f(g.vw[tt][0] >> (16 * ((lane * CPL + c) & 1)));
+        } else {
+          uint64_t two = g.vw[tt][0];
+          if constexpr (KBL::VW == 2) two |= static_cast<uint64_t>(g.vw[tt][1]) << 32;
+          const float2 vm = vms[tt];
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) {
+            const uint32_t code = static_cast<uint32_t>(two >> (bit + c * VB)) & ((1u << VB) - 1u);
+            vh[c] = static_cast<float>(code) * vm.x + vm.y;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p[i]), tt));
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) o[i][c] = fmaf(pt, vh[c], o[i][c]);
         }
       }
+    }
+  };
+  // rotating block buffers (static indices: one trip covers NB positions)
+  for (int base = p_lo; base < p_hi; base += NB) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pt = __shfl(p[i], tt, 64);
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) o[i][c] = fmaf(pt, vh[c], o[i][c]);
-      }
+    for (int j = 0; j < NB; ++j) {
+      kc_load<KB, VB, D>(a, trow, base + j + kKcDepth, p_hi, nblk, lane, koff, voff, gb[(j + kKcDepth) % NB]);
+      if (base + j < p_hi) compute(gb[j], base + j);
     }
   }
 
