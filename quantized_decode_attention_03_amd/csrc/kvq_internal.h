@@ -117,6 +117,9 @@ hipError_t launch_dequant(const DequantArgs& a, hipStream_t s);
 hipError_t launch_decode_partial(const DecodeArgs& a, int kbits, int vbits, int d, int n_splits,
                                  int batch, hipStream_t s);
 hipError_t launch_decode_merge(const MergeArgs& a, hipStream_t s);
+// Per-channel keys (a.kc, kbits < 16): called by launch_decode_partial.
+hipError_t launch_decode_kc(const DecodeArgs& a, int kbits, int vbits, int d, int n_splits, int batch, float qscale,
+                            hipStream_t s);
 hipError_t launch_zero_words(uint32_t* p, size_t n_words, hipStream_t s);
 // Zeroes out[], accumulates the squared errors, then divides by rows * d.
 hipError_t launch_quant_mse(const QuantMseArgs& a, hipStream_t s);
