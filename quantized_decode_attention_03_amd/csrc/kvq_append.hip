@@ -319,13 +319,30 @@ __device__ __forceinline__ void append_rows(const AppendArgs& a, int half, doubl
 }
 
 // K rows (blockIdx.z == 0) at BK bits and V rows (blockIdx.z == 1) at BV bits
-// of the listed heads, in one launch.
+// of the listed heads, in one launch. BK = BV = 0: each workgroup takes its
+// head's widths from the arguments (a uniform branch), so heads of different
+// widths still share one launch; that instance is held to 168 registers (three
+// waves per SIMD, like the fixed-width instances).
 template <int BK, int BV, int D>
-__global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a, double rs_n) {
-  if (blockIdx.z == 0) {
-    if (BK == 16 || !a.key_per_channel) append_rows<BK, D>(a, 0, rs_n);  // else append_kc_kernel
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BK == 0 ? 3 : 1)))
+void append_kernel(AppendArgs a, double rs_n) {
+  const int half = static_cast<int>(blockIdx.z);
+  if constexpr (BK != 0) {
+    if (half == 0) {
+      if (BK == 16 || !a.key_per_channel) append_rows<BK, D>(a, 0, rs_n);  // else append_kc_kernel
+    } else {
+      append_rows<BV, D>(a, 1, rs_n);
+    }
   } else {
-    append_rows<BV, D>(a, 1, rs_n);
+    const int bits = a.head_bits[half][blockIdx.y];
+    if (half == 0 && bits != 16 && a.key_per_channel) return;  // keys written by append_kc_kernel
+    switch (bits) {
+      case 2: append_rows<2, D>(a, half, rs_n); break;
+      case 3: append_rows<3, D>(a, half, rs_n); break;
+      case 4: append_rows<4, D>(a, half, rs_n); break;
+      case 8: append_rows<8, D>(a, half, rs_n); break;
+      default: append_rows<16, D>(a, half, rs_n); break;  // the host sends 2, 3, 4, 8 or 16
+    }
   }
 }
 
@@ -797,20 +814,31 @@ float rsqrt_exact(int n) { return static_cast<float>(1.0 / std::sqrt(static_cast
 template <int BK>
 hipError_t launch_append_k(const AppendArgs& a, double rs, hipStream_t s) {
 #define KVQ_APPEND_CALL(B_, D_) launch_append_t<BK, B_, D_>(a, rs, s)
-  KVQ_BITS_SWITCH(a.bits[1], a.d, KVQ_APPEND_CALL)
+  KVQ_BITS_SWITCH(a.head_bits[1][0], a.d, KVQ_APPEND_CALL)
 #undef KVQ_APPEND_CALL
 }
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
   if (a.batch * a.n_new == 0 || a.n_heads == 0) return hipSuccess;
+  bool uniform = true;
+  for (int half = 0; half < 2; ++half)
+    for (int i = 0; i < a.n_heads; ++i) {
+      const int b = a.head_bits[half][i];
+      if (b != 2 && b != 3 && b != 4 && b != 8 && b != 16) return hipErrorInvalidValue;
+      uniform = uniform && b == a.head_bits[half][0];
+    }
   const double rs = 1.0 / std::sqrt(static_cast<double>(a.had_block));
-  switch (a.bits[0]) {
+  if (!uniform) {
+    if (a.d == 64) return launch_append_t<0, 0, 64>(a, rs, s);
+    if (a.d == 128) return launch_append_t<0, 0, 128>(a, rs, s);
+    return hipErrorInvalidValue;
+  }
+  switch (a.head_bits[0][0]) {
     case 2: return launch_append_k<2>(a, rs, s);
     case 3: return launch_append_k<3>(a, rs, s);
     case 4: return launch_append_k<4>(a, rs, s);
     case 8: return launch_append_k<8>(a, rs, s);
-    case 16: return launch_append_k<16>(a, rs, s);
-    default: return hipErrorInvalidValue;
+    default: return launch_append_k<16>(a, rs, s);
   }
 }
 

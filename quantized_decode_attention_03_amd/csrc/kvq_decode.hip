@@ -232,23 +232,24 @@ template <int VB, int D> struct VFmt;
 template <int VB, int D>
 __device__ __forceinline__ int v_lane_offset(int n) {
   constexpr int bits_per_lane = VB * D / 16;
-  if constexpr (VB == 3) return ((bits_per_lane * n) / 32) * 4;  // dword holding the first bit
+  if constexpr (VB == 3) return (bits_per_lane * n) / 8;  // byte holding the first bit (an unaligned dword load)
   else if constexpr (bits_per_lane >= 32) return n * bits_per_lane / 8;
   else return ((bits_per_lane * n) / 32) * 4;  // sub-dword ranges: load the containing dword
 }
 
 template <int VB, int D> struct VRaw {
   static constexpr int bits_per_lane = VB * D / 16;
-  static constexpr int kWords = VB == 3 ? 2 : (bits_per_lane >= 32 ? bits_per_lane / 32 : 1);
+  static constexpr int kWords = bits_per_lane >= 32 ? bits_per_lane / 32 : 1;
 };
 
 template <int VB, int D>
 __device__ __forceinline__ void load_vtoken(const uint8_t* p, uint32_t* w) {
   constexpr int kW = VRaw<VB, D>::kWords;
-  if constexpr (VB == 3) {  // two dwords at a 4-byte aligned offset
-    const uint32_t* s = reinterpret_cast<const uint32_t*>(p);
-    w[0] = s[0];
-    w[1] = s[1];
+  if constexpr (VB == 3) {
+    // 24 (or 12) bits from a byte offset: one dword load at that byte (the
+    // target reads unaligned dwords from global memory); the dword's last
+    // byte belongs to the next lane or row, still inside the area
+    __builtin_memcpy(&w[0], p, 4);
   } else if constexpr (kW == 1) {
     w[0] = *reinterpret_cast<const uint32_t*>(p);
   } else if constexpr (kW == 2) {
@@ -332,9 +333,9 @@ __device__ __forceinline__ u32x4_t v_operand(const uint32_t (&raw)[8][VRaw<VB, D
       out = pk_add_h(out, VFmt<VB, D>::center_bits(0));
     } else if constexpr (VB == 3) {
       constexpr int bpl = 3 * D / 16;  // 24 or 12 bits per lane
-      const uint32_t sh = (bpl * n) & 31;
-      const uint32_t wa = __builtin_amdgcn_alignbit(a[1], a[0], sh);
-      const uint32_t wb = __builtin_amdgcn_alignbit(b[1], b[0], sh);
+      const uint32_t sh = (bpl * n) & 7;  // the lane's first bit within the loaded byte
+      const uint32_t wa = a[0] >> sh;
+      const uint32_t wb = b[0] >> sh;
       const uint32_t ca = (wa >> (3 * c)) & 7u, cb = (wb >> (3 * c)) & 7u;
       out = (((cb << 16) | ca) << 7) | bias;
       out = pk_add_h(out, VFmt<VB, D>::center_bits(0));
@@ -465,7 +466,7 @@ struct PrefetchDepth {
   static constexpr int value = KVQ_TUNE_DEPTH;
 };
 
-// The wide formats (8- and 16-bit keys, bf16 values, and the 3/8-bit values
+// The wide formats (8- and 16-bit keys, bf16 values, and the 8-bit values
 // beside 4-bit keys at head_dim 128; 16-bit keys beside 3- or 16-bit values and
 // 8-bit keys beside bf16 values at head_dim 64) need more than half the
 // register file: one wave per SIMD. The choice is checked by compiling every
@@ -473,7 +474,7 @@ struct PrefetchDepth {
 template <int KB, int VB, int D>
 struct PartialWaves {
   static constexpr bool wide =
-      D == 128 ? (VB == 16 || KB == 16 || KB == 8 || (KB == 4 && (VB == 3 || VB == 8)))
+      D == 128 ? (VB == 16 || KB == 16 || KB == 8 || (KB == 4 && VB == 8))
                : ((KB == 16 && (VB == 3 || VB == 16)) || (KB == 8 && VB == 16));
   static constexpr int value = wide ? 1 : (D == 128 ? KVQ_TUNE_WAVES128 : 2);
 };
@@ -611,23 +612,32 @@ __device__ __forceinline__ void compute_group(GroupRaw<KB, VB, D>& g, const u32x
   __syncthreads();
 }
 
+// The wave's LDS: the rotated queries, the QK A fragments and the PV weight
+// staging. They depend on head_dim only, so one allocation serves every format
+// of a multi-format launch.
+template <int D>
+struct PartialLds {
+  float qs[4][D];
+  uint4 qa[D / 32][2][64];  // QK A fragments (hi, lo) in lane order
+  __attribute__((aligned(16))) uint16_t wt[2][4][64];
+  __attribute__((aligned(16))) uint16_t wzero[8];
+};
+
+// One split of one (sequence, KV head) unit in format (KB, VB): the body of the
+// partial kernels, inlined into each of them.
 template <int KB, int VB, int D, bool M16>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PartialWaves<KB, VB, D>::value,
-                                                                    PartialWaves<KB, VB, D>::value)))
-void decode_partial_kernel(DecodeArgs a, const int32_t* __restrict__ table, uint32_t* __restrict__ steal,
-                           float qscale) {
-  // (table and counters as separate restrict arguments: the counters' atomics
-  // cannot alias the block table, so its entries stay scalar loads)
+__device__ __forceinline__ void partial_split(const DecodeArgs& a, const int32_t* __restrict__ table,
+                                              uint32_t* __restrict__ steal, float qscale, PartialLds<D>& lds) {
   using KF = KFmt<KB, D>;
   using VF = VFmt<VB, D>;
   constexpr int NCK = D / 32;               // QK chunks (32 channels each)
   constexpr int NCV = D / 16;               // PV chunks (16 output channels each)
   constexpr float NEG_INF = -__builtin_huge_valf();
 
-  __shared__ float qs[4][D];
-  __shared__ uint4 qa[NCK][2][64];   // QK A fragments (hi, lo) in lane order
-  __shared__ __attribute__((aligned(16))) uint16_t wt[2][4][64];
-  __shared__ __attribute__((aligned(16))) uint16_t wzero[8];
+  auto& qs = lds.qs;
+  auto& qa = lds.qa;
+  auto& wt = lds.wt;
+  auto& wzero = lds.wzero;
 
   const int lane = threadIdx.x;
   // One-dimensional grid of U units x W splits (W a multiple of the XCD
@@ -951,6 +961,43 @@ void decode_partial_kernel(DecodeArgs a, const int32_t* __restrict__ table, uint
   }
 }
 
+template <int KB, int VB, int D, bool M16>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PartialWaves<KB, VB, D>::value,
+                                                                    PartialWaves<KB, VB, D>::value)))
+void decode_partial_kernel(DecodeArgs a, const int32_t* __restrict__ table, uint32_t* __restrict__ steal,
+                           float qscale) {
+  // (table and counters as separate restrict arguments: the counters' atomics
+  // cannot alias the block table, so its entries stay scalar loads)
+  __shared__ PartialLds<D> lds;
+  partial_split<KB, VB, D, M16>(a, table, steal, qscale, lds);
+}
+
+// Heads of several formats in one launch (a segment whose per-head widths
+// differ): each wave runs the body of its head's (key, value) width pair.
+// Covers the pairs of 2-, 3- and 4-bit codes, which all run two waves per
+// SIMD. One launch fills the device in one dispatch; launches per format on
+// concurrent streams start one after another, tens of microseconds apart.
+template <int D, bool M16>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void decode_partial_mixed_kernel(DecodeArgs a, const int32_t* __restrict__ table, uint32_t* __restrict__ steal,
+                                 float qscale) {
+  __shared__ PartialLds<D> lds;
+  const int unit = (static_cast<int>(blockIdx.x) / kXcds) % (a.n_heads * a.batch);
+  const int pair = __builtin_amdgcn_readfirstlane(a.pair[unit % a.n_heads]);
+  switch (pair) {
+    case 0x22: partial_split<2, 2, D, M16>(a, table, steal, qscale, lds); break;
+    case 0x23: partial_split<2, 3, D, M16>(a, table, steal, qscale, lds); break;
+    case 0x24: partial_split<2, 4, D, M16>(a, table, steal, qscale, lds); break;
+    case 0x32: partial_split<3, 2, D, M16>(a, table, steal, qscale, lds); break;
+    case 0x33: partial_split<3, 3, D, M16>(a, table, steal, qscale, lds); break;
+    case 0x34: partial_split<3, 4, D, M16>(a, table, steal, qscale, lds); break;
+    case 0x42: partial_split<4, 2, D, M16>(a, table, steal, qscale, lds); break;
+    case 0x43: partial_split<4, 3, D, M16>(a, table, steal, qscale, lds); break;
+    case 0x44: partial_split<4, 4, D, M16>(a, table, steal, qscale, lds); break;
+    default: break;  // the host sends only these pairs
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Merge of the split partials (all segments) and the inverse rotation.
 // ---------------------------------------------------------------------------
@@ -1113,6 +1160,14 @@ int waves_v(int vbits) {
   }
 }
 
+template <int D, bool M16>
+hipError_t launch_mixed_t(const DecodeArgs& a, int n_splits, int batch, float qscale, hipStream_t s) {
+  if (a.batch != batch || n_splits % kXcds != 0) return hipErrorInvalidValue;
+  dim3 grid(static_cast<unsigned>(n_splits) * a.n_heads * batch);
+  hipLaunchKernelGGL((decode_partial_mixed_kernel<D, M16>), grid, dim3(64), 0, s, a, a.table, a.steal, qscale);
+  return hipGetLastError();
+}
+
 template <int D>
 int waves_k(int kbits, int vbits) {
   switch (kbits) {
@@ -1139,6 +1194,22 @@ hipError_t launch_decode_partial(const DecodeArgs& a, int kbits, int vbits, int 
   if (d == 128) return dispatch_k<128>(a, kbits, vbits, n_splits, batch, qscale, s);
   if (d == 64) return dispatch_k<64>(a, kbits, vbits, n_splits, batch, qscale, s);
   return hipErrorInvalidValue;
+}
+
+bool decode_partial_mixable(int kbits, int vbits, int d) {
+  return (d == 64 || d == 128) && kbits >= 2 && kbits <= 4 && vbits >= 2 && vbits <= 4;
+}
+
+hipError_t launch_decode_partial_mixed(const DecodeArgs& a, int d, int n_splits, int batch, hipStream_t s) {
+  if (n_splits == 0 || batch == 0 || a.n_heads == 0) return hipSuccess;
+  if (a.kc) return hipErrorInvalidValue;
+  for (int i = 0; i < a.n_heads; ++i)
+    if (!decode_partial_mixable(a.pair[i] >> 4, a.pair[i] & 15, d)) return hipErrorInvalidValue;
+  const float qscale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(a.had_block) * d));
+  if (d == 128) return a.meta16 ? launch_mixed_t<128, true>(a, n_splits, batch, qscale, s)
+                                : launch_mixed_t<128, false>(a, n_splits, batch, qscale, s);
+  return a.meta16 ? launch_mixed_t<64, true>(a, n_splits, batch, qscale, s)
+                  : launch_mixed_t<64, false>(a, n_splits, batch, qscale, s);
 }
 
 hipError_t launch_decode_merge(const MergeArgs& a, hipStream_t s) {

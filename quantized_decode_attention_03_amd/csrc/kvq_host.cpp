@@ -134,6 +134,15 @@ bool deterministic_order() {
   return env && env[0] && env[0] != '0';
 }
 
+// KVQ_MIXED_LAUNCH=0: one partial launch per (key, value) width pair of a
+// segment, on concurrent streams. By default the heads whose pairs use 2-, 3-
+// or 4-bit codes share one launch of the multi-format kernel when the segment
+// has several such pairs (same results: each head runs the same code).
+bool mixed_launch_enabled() {
+  const char* env = std::getenv("KVQ_MIXED_LAUNCH");
+  return !(env && env[0] == '0');
+}
+
 // Split plan of one segment: nominal pages per split (a multiple of 4) and
 // the number of waves (splits) per (sequence, KV head). The kernel shares a
 // unit's pages among its waves itself; the nominal size only sets the count.
@@ -615,42 +624,52 @@ kvq_status kvq_quantize_append(const kvq_layout* L, void* pool, int64_t pool_blo
   if (L->key_per_channel && n_new % KVQ_BLOCK_TOKENS != 0)
     return fail(KVQ_ERR_ARG, "kvq_quantize_append: per-channel keys are appended in whole blocks (n_new %d)", n_new);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  // one launch per distinct (K bits, V bits) pair, K and V rows together
-  bool done[KVQ_MAX_KV_HEADS] = {};
-  for (int h0 = 0; h0 < L->num_kv_heads; ++h0) {
-    if (done[h0]) continue;
-    kvq::AppendArgs a{};
-    a.pool = static_cast<uint8_t*>(pool);
-    a.pool_blocks = pool_blocks;
-    a.block_bytes = L->block_bytes;
-    a.table = block_table;
-    a.table_stride = table_stride;
-    a.start_pos = start_pos;
-    a.src[0] = k;
-    a.src[1] = v;
-    a.src_bf16 = in_dtype == KVQ_BF16;
-    a.meta16 = L->meta_fp16;
-    a.key_per_channel = L->key_per_channel;
-    a.batch = batch;
-    a.n_new = n_new;
-    a.hkv = L->num_kv_heads;
-    a.d = L->head_dim;
-    a.had_block = L->had_block;
-    a.bits[0] = L->bits_k[h0];
-    a.bits[1] = L->bits_v[h0];
-    for (int h = h0; h < L->num_kv_heads; ++h) {
-      if (!done[h] && L->bits_k[h] == L->bits_k[h0] && L->bits_v[h] == L->bits_v[h0]) {
-        a.heads[a.n_heads] = h;
-        a.area_off[0][a.n_heads] = L->k_off[h];
-        a.area_off[1][a.n_heads] = L->v_off[h];
-        ++a.n_heads;
-        done[h] = true;
+  // Token-wise rows of every head in one launch (each workgroup takes its
+  // head's widths); per-channel keys then in one launch per key width.
+  kvq::AppendArgs a{};
+  a.pool = static_cast<uint8_t*>(pool);
+  a.pool_blocks = pool_blocks;
+  a.block_bytes = L->block_bytes;
+  a.table = block_table;
+  a.table_stride = table_stride;
+  a.start_pos = start_pos;
+  a.src[0] = k;
+  a.src[1] = v;
+  a.src_bf16 = in_dtype == KVQ_BF16;
+  a.meta16 = L->meta_fp16;
+  a.key_per_channel = L->key_per_channel;
+  a.batch = batch;
+  a.n_new = n_new;
+  a.hkv = L->num_kv_heads;
+  a.d = L->head_dim;
+  a.had_block = L->had_block;
+  a.n_heads = L->num_kv_heads;
+  for (int h = 0; h < L->num_kv_heads; ++h) {
+    a.heads[h] = h;
+    a.area_off[0][h] = L->k_off[h];
+    a.area_off[1][h] = L->v_off[h];
+    a.head_bits[0][h] = static_cast<uint8_t>(L->bits_k[h]);
+    a.head_bits[1][h] = static_cast<uint8_t>(L->bits_v[h]);
+  }
+  hipError_t e = kvq::launch_append(a, s);
+  if (e != hipSuccess) return device_status(e, "kvq_quantize_append launch");
+  if (L->key_per_channel) {
+    bool done[KVQ_MAX_KV_HEADS] = {};
+    for (int h0 = 0; h0 < L->num_kv_heads; ++h0) {
+      if (done[h0] || L->bits_k[h0] == 16) continue;
+      kvq::AppendArgs ak = a;
+      ak.n_heads = 0;
+      ak.bits[0] = L->bits_k[h0];
+      for (int h = h0; h < L->num_kv_heads; ++h) {
+        if (!done[h] && L->bits_k[h] == L->bits_k[h0]) {
+          ak.heads[ak.n_heads] = h;
+          ak.area_off[0][ak.n_heads] = L->k_off[h];
+          ak.area_off[1][ak.n_heads] = L->v_off[h];
+          ++ak.n_heads;
+          done[h] = true;
+        }
       }
-    }
-    hipError_t e = kvq::launch_append(a, s);
-    if (e != hipSuccess) return device_status(e, "kvq_quantize_append launch");
-    if (L->key_per_channel && a.bits[0] != 16) {
-      e = kvq::launch_append_kc(a, s);
+      e = kvq::launch_append_kc(ak, s);
       if (e != hipSuccess) return device_status(e, "kvq_quantize_append launch (per-channel keys)");
     }
   }
@@ -755,17 +774,34 @@ kvq_status kvq_decode_partial(const kvq_segment* segs, int32_t n_segs, int32_t b
   struct Launch {
     kvq::DecodeArgs a;
     int kbits, vbits, d, n_splits;
+    bool mixed;
+    int64_t bytes;  // code bytes the launch reads per sequence (orders the launches)
   };
   std::vector<Launch> launches;
   int slot_base = 0;
+  const bool allow_mixed = mixed_launch_enabled();
   for (int i = 0; i < n_segs; ++i) {
     const kvq_segment& sg = segs[i];
     const kvq_layout& L = *sg.layout;
     const SplitPlan& p = plans[i];
     if (p.n_splits > 0) {
       bool done[KVQ_MAX_KV_HEADS] = {};
+      // Heads of two or more mixable formats go into one multi-format launch;
+      // the rest get one launch per format.
+      bool mixable[KVQ_MAX_KV_HEADS] = {};
+      int first_pair = -1;
+      bool several = false;
+      for (int h = 0; h < L.num_kv_heads; ++h) {
+        mixable[h] = allow_mixed && !L.key_per_channel &&
+                     kvq::decode_partial_mixable(L.bits_k[h], L.bits_v[h], L.head_dim);
+        if (!mixable[h]) continue;
+        const int pr = L.bits_k[h] << 4 | L.bits_v[h];
+        if (first_pair < 0) first_pair = pr;
+        else if (pr != first_pair) several = true;
+      }
       for (int h0 = 0; h0 < L.num_kv_heads; ++h0) {
         if (done[h0]) continue;
+        const bool mixed = several && mixable[h0];
         kvq::DecodeArgs a{};
         a.pool = static_cast<const uint8_t*>(sg.pool);
         a.pool_blocks = sg.pool_blocks;
@@ -788,26 +824,36 @@ kvq_status kvq_decode_partial(const kvq_segment* segs, int32_t n_segs, int32_t b
         a.part_o = part_o;
         a.part_ml = part_ml;
         for (int h = h0; h < L.num_kv_heads; ++h) {
-          if (!done[h] && L.bits_k[h] == L.bits_k[h0] && L.bits_v[h] == L.bits_v[h0]) {
+          const bool same = mixed ? mixable[h] : L.bits_k[h] == L.bits_k[h0] && L.bits_v[h] == L.bits_v[h0];
+          if (!done[h] && same) {
             a.heads[a.n_heads] = h;
             a.k_off[a.n_heads] = L.k_off[h];
             a.v_off[a.n_heads] = L.v_off[h];
+            a.pair[a.n_heads] = static_cast<uint8_t>(L.bits_k[h] << 4 | L.bits_v[h]);
             ++a.n_heads;
             done[h] = true;
           }
         }
-        launches.push_back({a, L.bits_k[h0], L.bits_v[h0], L.head_dim, p.n_splits});
+        int64_t row_bits = 0;
+        for (int j = 0; j < a.n_heads; ++j) row_bits += L.bits_k[a.heads[j]] + L.bits_v[a.heads[j]];
+        launches.push_back({a, L.bits_k[h0], L.bits_v[h0], L.head_dim, p.n_splits, mixed,
+                            row_bits * L.head_dim / 8 * std::max(sg.max_len, 0)});
       }
     }
     slot_base += p.n_splits;
   }
-  if (launches.size() == 1) {
-    const Launch& l = launches[0];
-    return device_status(kvq::launch_decode_partial(l.a, l.kbits, l.vbits, l.d, l.n_splits, batch, s),
-                         "kvq_decode_partial launch");
-  }
-  // several launches: the first on the caller's stream, the others on side
-  // streams forked from it, all joined back before the call returns
+  auto launch = [&](const Launch& l, hipStream_t st) {
+    return l.mixed ? kvq::launch_decode_partial_mixed(l.a, l.d, l.n_splits, batch, st)
+                   : kvq::launch_decode_partial(l.a, l.kbits, l.vbits, l.d, l.n_splits, batch, st);
+  };
+  if (launches.size() == 1) return device_status(launch(launches[0], s), "kvq_decode_partial launch");
+  // Several launches (segments, and width groups that cannot share a launch)
+  // run concurrently: the largest on the caller's stream, which starts it
+  // first, the others on side streams forked from it and joined back before
+  // the call returns. (One after another on one stream is slower: the small
+  // launches of a short segment are latency-bound and then add up.)
+  std::stable_sort(launches.begin(), launches.end(),
+                   [](const Launch& x, const Launch& y) { return x.bytes > y.bytes; });
   std::lock_guard<std::mutex> lock(g_side_mutex);
   SideStreams* ss = nullptr;
   hipError_t e = side_streams(&ss, s);
@@ -818,10 +864,8 @@ kvq_status kvq_decode_partial(const kvq_segment* segs, int32_t n_segs, int32_t b
   for (int i = 0; i < n_side; ++i)
     if ((e = hipStreamWaitEvent(ss->s[i], ss->fork, 0)) != hipSuccess) return device_status(e, "kvq_decode_partial fork");
   for (size_t j = 0; j < launches.size(); ++j) {
-    const Launch& l = launches[j];
     hipStream_t st = j == 0 ? s : ss->s[(j - 1) % n_side];
-    if ((e = kvq::launch_decode_partial(l.a, l.kbits, l.vbits, l.d, l.n_splits, batch, st)) != hipSuccess)
-      return device_status(e, "kvq_decode_partial launch");
+    if ((e = launch(launches[j], st)) != hipSuccess) return device_status(e, "kvq_decode_partial launch");
   }
   for (int i = 0; i < n_side; ++i) {
     if ((e = hipEventRecord(ss->join[i], ss->s[i])) != hipSuccess) return device_status(e, "kvq_decode_partial join");

@@ -23,9 +23,10 @@ struct AppendArgs {
   int32_t key_per_channel;  // 1: keys are written per block by append_kc_kernel, not per row
   int32_t batch, n_new, hkv, d, had_block;
   int32_t n_heads;      // heads in this launch
-  int32_t bits[2];      // K bits, V bits of these heads
+  int32_t bits[2];      // append_kc_kernel: the key bits of the listed heads
   int32_t heads[KVQ_MAX_KV_HEADS];
   int64_t area_off[2][KVQ_MAX_KV_HEADS];  // byte offset of each listed head's K / V area in a block
+  uint8_t head_bits[2][KVQ_MAX_KV_HEADS];  // append_kernel: K / V bits of each listed head
 };
 
 struct DequantArgs {
@@ -65,6 +66,7 @@ struct DecodeArgs {
   int32_t heads[KVQ_MAX_KV_HEADS];
   int64_t k_off[KVQ_MAX_KV_HEADS];
   int64_t v_off[KVQ_MAX_KV_HEADS];
+  uint8_t pair[KVQ_MAX_KV_HEADS];  // (key bits << 4) | value bits per listed head (multi-format launch)
   float* part_o;       // [batch][hq][total_slots][d]
   float* part_ml;      // [batch][hq][total_slots][2]  (running max in log2 units, sum)
 };
@@ -127,5 +129,11 @@ hipError_t launch_requant(const RequantArgs& a, int n_seqs, hipStream_t s);
 
 // Waves per SIMD the partial kernel for (kbits, vbits, d) is compiled to hold.
 int decode_partial_waves_per_simd(int kbits, int vbits, int d);
+// Whether heads of this format can share a multi-format launch (2-, 3- and
+// 4-bit keys and values, head_dim 64 or 128, per-token keys).
+bool decode_partial_mixable(int kbits, int vbits, int d);
+// One launch over heads of several formats: a.pair[i] names head i's widths,
+// every pair mixable. Same grid, partials and counters as launch_decode_partial.
+hipError_t launch_decode_partial_mixed(const DecodeArgs& a, int d, int n_splits, int batch, hipStream_t s);
 
 }  // namespace kvq

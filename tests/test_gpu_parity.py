@@ -271,6 +271,35 @@ def test_decode_fp16_meta(d, n, g, bk, bv):
     assert T.max_rel_err(out, expect) <= T.ATTN_TOL
 
 
+# one segment holding every (key, value) pair of 2-, 3- and 4-bit codes, which
+# share the multi-format launch, and an 8-bit-key head launched on its own
+MIX_BK = [2, 2, 2, 3, 3, 3, 4, 4, 4, 8]
+MIX_BV = [2, 3, 4, 2, 3, 4, 2, 3, 4, 4]
+
+
+@pytest.mark.parametrize("d,n,m16", [(128, 128, False), (64, 32, False), (128, 64, True), (64, 64, True)])
+def test_decode_multi_format_launch(monkeypatch, d, n, m16):
+    lens = [1, 300, 1000, 0, 77]
+    L, lay, cache, ref, table, k, v = build_case(d, n, 2, MIX_BK, MIX_BV, lens, seed=41, chunks=[500, 600],
+                                                 meta_fp16=m16)
+    rng = np.random.default_rng(42)
+    q = synth.bf16_round(rng.standard_normal((len(lens), len(MIX_BK) * 2, d)).astype(np.float32))
+    # fixed order: each head runs the same code in either launch, so the results are identical
+    monkeypatch.setenv("KVQ_DECODE_DETERMINISTIC", "1")
+    out, expect = decode_both(L, lay, cache, ref, table, lens, q)
+    assert np.all(out[3] == 0)
+    assert T.max_rel_err(out, expect) <= T.ATTN_TOL
+    monkeypatch.setenv("KVQ_MIXED_LAUNCH", "0")
+    qt = torch.from_numpy(q).to(T.DEV).to(torch.bfloat16)
+    per_format = kvq.kvq_decode_attn([cache.segment(lens)], qt).cpu().numpy()
+    assert np.array_equal(out, per_format)
+    # shared tail (default order): within the tolerance
+    monkeypatch.delenv("KVQ_MIXED_LAUNCH")
+    monkeypatch.delenv("KVQ_DECODE_DETERMINISTIC")
+    shared = kvq.kvq_decode_attn([cache.segment(lens)], qt).cpu().numpy()
+    assert T.max_rel_err(shared, expect) <= T.ATTN_TOL
+
+
 def test_decode_fp32_query_and_inputs():
     lens = [200, 77]
     L, lay, cache, ref, table, k, v = build_case(128, 128, 4, [4, 4], [2, 2], lens, seed=23, in_bf16=False)
