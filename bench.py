@@ -274,7 +274,7 @@ def build_decode_layers(args, kvq, torch, dev):
                   "bits_k": BITS_K, "bits_v": BITS_V, "had_block": HAD, "keys": "per channel"}
         per_tok = D * BITS_K // 8 + D * 8 // 16 + D * BITS_V // 8 + 8
         return (layers, config, batch, B * HKV * T * per_tok + B * (T // 16) * 4 + B * HKV * G * D * 2,
-                "decode_kc_kernel<4,4,128>")
+                "decode_partial_kc_kernel<4,4,128>")
     if m16:
         config = {"workload": WORKLOAD.replace("K4/V4 token-wise INT4", "K4/V4 token-wise INT4 with float16 {s, mn}"),
                   "layers": args.layers, "batch": B, "ctx": T, "kv_heads": HKV, "q_per_kv": G, "head_dim": D,

@@ -362,6 +362,7 @@ struct GroupRaw {
   uint32_t k[4][KFmt<KB, D>::kWords];         // key quarter rows, one per page
   uint32_t v[2][8][VRaw<VB, D>::kWords];       // value words, 8 tokens per page pair
   float ks, kmn, vs, vmn;                      // metadata of this lane's token
+  float4 kcm[4];                               // per-channel keys: {s, mn} of this lane's two channels, per page
   bool valid;                                  // this lane's token is a cached token
   uint32_t vmask;                              // bit 8*pp2+e: value token e of pair pp2 is cached
   int gid;                                     // group index in the unit (>= unit groups: none)
@@ -384,10 +385,10 @@ constexpr int kXcds = 8;  // accelerator dies of the chip; workgroups go round-r
 // (measured: 2/8 beats 0, 4/8 and 6/8 at the 32k Llama-shaped decode).
 constexpr int kStaticEighths = KVQ_TUNE_STATIC_EIGHTHS;
 
-template <int KB, int VB, int D, bool M16>
+template <int KB, int VB, int D, bool M16, bool KC>
 __device__ __forceinline__ void load_group(const DecodeArgs& a, const uint8_t* pool, const int32_t (&blks)[4],
                                            int grp, int p1, int seq_len, int64_t koff, int64_t voff, int lane,
-                                           GroupRaw<KB, VB, D>& g) {
+                                           int kc0, int kc1, GroupRaw<KB, VB, D>& g) {
   constexpr int RBK = D * KB / 8, RBV = D * VB / 8, QBYTES = RBK / 4;
   const int tslot = lane & 15, g4 = lane >> 4;
   int64_t boff[4];
@@ -416,7 +417,17 @@ __device__ __forceinline__ void load_group(const DecodeArgs& a, const uint8_t* p
   const uint8_t* mbase = pool + my_boff + ml;
   g.ks = 1.f; g.kmn = 0.f; g.vs = 1.f; g.vmn = 0.f;
   if constexpr (KB != 16) {
-    if constexpr (M16) {
+    if constexpr (KC) {
+      // per-channel keys: each page's {s, mn} pairs of the lane's two fragment
+      // channels (byte offsets kc0, kc1 in the page's channel metadata)
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        const uint8_t* km = pool + boff[pp] + koff + kBlockTokens * RBK;
+        const float2 m0 = *reinterpret_cast<const float2*>(km + kc0);
+        const float2 m1 = *reinterpret_cast<const float2*>(km + kc1);
+        g.kcm[pp] = make_float4(m0.x, m0.y, m1.x, m1.y);
+      }
+    } else if constexpr (M16) {
       const uint32_t mk = *reinterpret_cast<const uint32_t*>(mbase + koff + kBlockTokens * RBK);
       g.ks = f16_to_f(mk & 0xffffu); g.kmn = f16_to_f(mk >> 16);
     } else {
@@ -487,11 +498,25 @@ struct SplitState {
   float mn_part[4];      // per-lane partial sum of p * (mn + 2^(b-1) s)
 };
 
-template <int KB, int VB, int D>
+// Per-channel keys: the lane's share of building each page's query fragments.
+// A key is s_i c_i + mn_i with a pair per channel and page, so the QK A operand
+// is q~ scaled per channel, rebuilt per page: lane (quarter g4, w = lane % 16)
+// owns word w % 4 of chunk w / 4, i.e. two channels of its quarter, for all
+// four query rows, and its share of the page constant sum_i q~_i (mn_i - s_i
+// base_i / sigma_i).
+struct KcLane {
+  float qk[4][2];  // q~ of the four query rows at the two channels (0 for rows >= group)
+  float isig[2];   // 1 / sigma of the channels' fp16 code values
+  float bsig[2];   // base / sigma: the constant part of a code value, in code units
+  int word;        // u32 index of the word in the hi fragment area (row 0); -1: no word (head_dim 64)
+};
+
+template <int KB, int VB, int D, bool KC>
 __device__ __forceinline__ void compute_group(GroupRaw<KB, VB, D>& g, const u32x4_t (&qf)[D / 32][2],
                                               const float (&biasq)[4], const float (&q2)[4], float inv_qsc, int G,
                                               int lane, uint32_t bias, uint16_t (*wt)[4][64],
-                                              const uint16_t* wzero, SplitState<KB, VB, D>& st) {
+                                              const uint16_t* wzero, SplitState<KB, VB, D>& st,
+                                              const KcLane& kl, uint4 (*qa)[2][64]) {
   using KF = KFmt<KB, D>;
   using VF = VFmt<VB, D>;
   constexpr int NCK = D / 32, NCV = D / 16;
@@ -504,14 +529,67 @@ __device__ __forceinline__ void compute_group(GroupRaw<KB, VB, D>& g, const u32x
   float4_t cq[4];
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp) cq[pp] = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int c = 0; c < NCK; ++c) {
-    const u32x4_t ah = qf[c][0], al = qf[c][1];
+  if constexpr (KC) {
+    // Per page: A = q~ s / sigma at a power-of-two page scale (fp16 hi/lo in the
+    // LDS fragment area, rows >= 4 kept zero), B = the codes as in the row
+    // layout; score = sum / scale + the page constant of each query row.
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) {
-      const u32x4_t bk = KF::unpack(g.k[pp], c, bias);
-      cq[pp] = mfma<KF::bf16>(ah, bk, cq[pp]);
-      cq[pp] = mfma<KF::bf16>(al, bk, cq[pp]);
+      const float4 m = g.kcm[pp];
+      const float f0 = m.x * kl.isig[0], f1 = m.z * kl.isig[1];
+      const float n0 = fmaf(-m.x, kl.bsig[0], m.y), n1 = fmaf(-m.z, kl.bsig[1], m.w);
+      float x[4][2], cp[4], amax = 0.f;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        x[h][0] = kl.qk[h][0] * f0;
+        x[h][1] = kl.qk[h][1] * f1;
+        amax = fmaxf(amax, fmaxf(fabsf(x[h][0]), fabsf(x[h][1])));
+        cp[h] = fmaf(kl.qk[h][0], n0, kl.qk[h][1] * n1);
+      }
+      amax = wave_max_scalar(amax);
+      float psc = 1.f;
+      if (amax > 0.f) {
+        int ex;
+        frexpf(amax, &ex);
+        psc = ldexpf(1.f, 10 - ex);
+      }
+      if (kl.word >= 0) {
+        uint32_t* qw = reinterpret_cast<uint32_t*>(&qa[0][0][0]);
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const float y0 = x[h][0] * psc, y1 = x[h][1] * psc;
+          const _Float16 h0 = static_cast<_Float16>(y0), h1 = static_cast<_Float16>(y1);
+          const _Float16 l0 = static_cast<_Float16>(y0 - static_cast<float>(h0));
+          const _Float16 l1 = static_cast<_Float16>(y1 - static_cast<float>(h1));
+          qw[kl.word + 4 * h] = half_bits(h0) | (half_bits(h1) << 16);
+          qw[kl.word + 4 * h + 256] = half_bits(l0) | (half_bits(l1) << 16);
+        }
+      }
+      float cst[4];
+      wave_sum4(cp, cst);
+      __syncthreads();  // the fragment words are written before they are read
+      const float ipsc = 1.f / psc;
+#pragma unroll
+      for (int c = 0; c < NCK; ++c) {
+        const uint4 vh = qa[c][0][lane], vl = qa[c][1][lane];
+        const u32x4_t bk = KF::unpack(g.k[pp], c, bias);
+        cq[pp] = mfma<KF::bf16>(u32x4_t{vh.x, vh.y, vh.z, vh.w}, bk, cq[pp]);
+        cq[pp] = mfma<KF::bf16>(u32x4_t{vl.x, vl.y, vl.z, vl.w}, bk, cq[pp]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cq[pp][i] = fmaf(cq[pp][i], ipsc, cst[i]);
+      __syncthreads();  // and read before the next page writes them
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < NCK; ++c) {
+      const u32x4_t ah = qf[c][0], al = qf[c][1];
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        const u32x4_t bk = KF::unpack(g.k[pp], c, bias);
+        cq[pp] = mfma<KF::bf16>(ah, bk, cq[pp]);
+        cq[pp] = mfma<KF::bf16>(al, bk, cq[pp]);
+      }
     }
   }
   // pack the four tiles: lane = token of the group, register i = head i
@@ -526,7 +604,8 @@ __device__ __forceinline__ void compute_group(GroupRaw<KB, VB, D>& g, const u32x
     const auto r = __builtin_amdgcn_permlane32_swap(r01[0], r23[0], false, false);
     const float sc = bits_f(r[0]);
     float zi;
-    if constexpr (KMETA && KF::kCentre != 0.f) zi = fmaf(ks_q, sc, kmid * q2[i]);
+    if constexpr (KC) zi = sc;
+    else if constexpr (KMETA && KF::kCentre != 0.f) zi = fmaf(ks_q, sc, kmid * q2[i]);
     else if constexpr (KMETA) zi = fmaf(ks_q, sc, fmaf(-ks_q, biasq[i], g.kmn * q2[i]));
     else zi = sc;
     z[i] = (g.valid && i < G) ? zi : NEG_INF;
@@ -623,9 +702,22 @@ struct PartialLds {
   __attribute__((aligned(16))) uint16_t wzero[8];
 };
 
+// KFmt::channel at run-time indices, by compile-time selects (no table in
+// memory); used once per wave.
+template <int KB, int D>
+__device__ __forceinline__ int kf_channel_rt(int c, int e) {
+  int r = 0;
+#pragma unroll
+  for (int cc = 0; cc < D / 32; ++cc)
+#pragma unroll
+    for (int ee = 0; ee < 8; ++ee) r = (cc == c && ee == e) ? KFmt<KB, D>::channel(cc, ee) : r;
+  return r;
+}
+
 // One split of one (sequence, KV head) unit in format (KB, VB): the body of the
-// partial kernels, inlined into each of them.
-template <int KB, int VB, int D, bool M16>
+// partial kernels, inlined into each of them. KC: keys quantized per channel
+// over each page (the per-channel layout), values per token.
+template <int KB, int VB, int D, bool M16, bool KC = false>
 __device__ __forceinline__ void partial_split(const DecodeArgs& a, const int32_t* __restrict__ table,
                                               uint32_t* __restrict__ steal, float qscale, PartialLds<D>& lds) {
   using KF = KFmt<KB, D>;
@@ -709,6 +801,16 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, const int32_t
     }
   }
   __builtin_amdgcn_sched_barrier(0);  // keep the query loads ahead of the group loads
+  // per-channel keys: the lane's fragment word (chunk kc_c, word kc_v of quarter
+  // lane / 16) and the byte offsets of its two channels' metadata in a page
+  const int kc_c = (lane & 15) >> 2, kc_v = lane & 3;
+  int kc_ch0 = 0, kc_ch1 = 0;
+  if constexpr (KC) {
+    const int cw = kc_c < NCK ? kc_c : 0;
+    kc_ch0 = (lane >> 4) * (D / 4) + kf_channel_rt<KB, D>(cw, 2 * kc_v);
+    kc_ch1 = (lane >> 4) * (D / 4) + kf_channel_rt<KB, D>(cw, 2 * kc_v + 1);
+  }
+  const int kc0 = kc_ch0 * kMetaBytes, kc1 = kc_ch1 * kMetaBytes;
   constexpr int DEPTH = PrefetchDepth<KB, VB, D>::value;
   constexpr int NB = DEPTH + 1;  // group buffers
   GroupRaw<KB, VB, D> gbuf[NB];
@@ -757,7 +859,7 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, const int32_t
     for (int pp = 0; pp < 4; ++pp) blks[pp] = __builtin_amdgcn_readlane(next_tab, pp);
     resolve();
     g.gid = gid;
-    load_group<KB, VB, D, M16>(a, pool, blks, 4 * (g_lo + gid), pages, seq_len, koff, voff, lane, g);
+    load_group<KB, VB, D, M16, KC>(a, pool, blks, 4 * (g_lo + gid), pages, seq_len, koff, voff, lane, kc0, kc1, g);
   };
 #pragma unroll
   for (int j = 0; j < DEPTH; ++j) load_next(gbuf[j]);
@@ -854,6 +956,28 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, const int32_t
   }
   const uint32_t bias = vconst(0x64006400u);  // fp16 pair (1024, 1024)
 
+  // per-channel keys: the lane's q~ at its two channels, and their code scale
+  // and constant (the fragments above keep their zero rows >= group; rows 0-3
+  // are rewritten per page)
+  KcLane kl{};
+  if constexpr (KC) {
+    const int cw = kc_c < NCK ? kc_c : 0;
+    // (lanes with no word, at head_dim 64, contribute nothing)
+    const bool own = kc_c < NCK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kl.qk[i][0] = own && i < G ? qs[i][kc_ch0] * qscale : 0.f;
+      kl.qk[i][1] = own && i < G ? qs[i][kc_ch1] * qscale : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float sg = KF::sigma(cw, 2 * kc_v + j);
+      kl.isig[j] = 1.f / sg;
+      kl.bsig[j] = KF::base(cw, 2 * kc_v + j) / sg;
+    }
+    kl.word = kc_c < NCK ? (kc_c * 128 + 16 * (lane >> 4)) * 4 + kc_v : -1;
+  }
+
   __syncthreads();  // the A fragments are read by the same wave; order LDS writes before reads
 
   // ---- main loop: two groups per trip, loads of the next group in flight ----
@@ -870,7 +994,7 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, const int32_t
   // buffers, the fragments and the PV accumulators against the 256
   // architectural registers, leaving room for the rest of the loop.
   constexpr int GROUP_WORDS = 4 * KF::kWords + 16 * VRaw<VB, D>::kWords + 4;
-  constexpr bool QF_REGS = KVQ_TUNE_QF_REGS && (DEPTH + 1) * GROUP_WORDS + 8 * NCK + 4 * NCV <= 180;
+  constexpr bool QF_REGS = !KC && KVQ_TUNE_QF_REGS && (DEPTH + 1) * GROUP_WORDS + 8 * NCK + 4 * NCV <= 180;
   u32x4_t qreg[NCK][2];
   if constexpr (QF_REGS) {
 #pragma unroll
@@ -883,7 +1007,7 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, const int32_t
   }
   auto compute = [&](GroupRaw<KB, VB, D>& g) {
     if constexpr (QF_REGS) {
-      compute_group<KB, VB, D>(g, qreg, biasq, q2, inv_qsc, G, lane, bias, wt, wzero, st);
+      compute_group<KB, VB, D, KC>(g, qreg, biasq, q2, inv_qsc, G, lane, bias, wt, wzero, st, kl, qa);
     } else {
       u32x4_t qf[NCK][2];
 #pragma unroll
@@ -893,7 +1017,7 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, const int32_t
           const uint4 v = qa[c][l][lane];
           qf[c][l] = u32x4_t{v.x, v.y, v.z, v.w};
         }
-      compute_group<KB, VB, D>(g, qf, biasq, q2, inv_qsc, G, lane, bias, wt, wzero, st);
+      compute_group<KB, VB, D, KC>(g, qf, biasq, q2, inv_qsc, G, lane, bias, wt, wzero, st, kl, qa);
     }
   };
 
@@ -927,9 +1051,8 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, const int32_t
   for (int c = 0; c < NCV; ++c)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t x = f_bits(st.acc[c][i]);
-      const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-      o[c][i] = (bits_f(r[0]) + bits_f(r[1])) / VF::sigma(c) + mnsum[i];
+      // rows 0-3 (hi weights, lanes 0-15) plus rows 4-7 (lo weights, lanes 16-31)
+      o[c][i] = (st.acc[c][i] + __shfl_xor(st.acc[c][i], 16, 64)) / VF::sigma(c) + mnsum[i];
     }
   if (lane < 16) {
 #pragma unroll
@@ -970,6 +1093,26 @@ void decode_partial_kernel(DecodeArgs a, const int32_t* __restrict__ table, uint
   // cannot alias the block table, so its entries stay scalar loads)
   __shared__ PartialLds<D> lds;
   partial_split<KB, VB, D, M16>(a, table, steal, qscale, lds);
+}
+
+// Keys quantized per channel over each page, values per token: the same split,
+// work sharing and partials, with the QK A operand rebuilt per page.
+// (8-bit keys, and 8- or 16-bit values at head_dim 128 or 16-bit values at 64,
+// need more than half the register file: one wave per SIMD; checked by
+// compiling every instance and requiring zero spills)
+template <int KB, int VB, int D>
+struct KcWaves {
+  static constexpr bool wide = D == 128 ? (KB == 8 || VB == 8 || VB == 16) : VB == 16;
+  static constexpr int value = wide ? 1 : 2;
+};
+
+template <int KB, int VB, int D>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KcWaves<KB, VB, D>::value,
+                                                                    KcWaves<KB, VB, D>::value)))
+void decode_partial_kc_kernel(DecodeArgs a, const int32_t* __restrict__ table, uint32_t* __restrict__ steal,
+                              float qscale) {
+  __shared__ PartialLds<D> lds;
+  partial_split<KB, VB, D, false, true>(a, table, steal, qscale, lds);
 }
 
 // Heads of several formats in one launch (a segment whose per-head widths
@@ -1168,6 +1311,58 @@ hipError_t launch_mixed_t(const DecodeArgs& a, int n_splits, int batch, float qs
   return hipGetLastError();
 }
 
+template <int KB, int VB, int D>
+hipError_t launch_kc_partial_t(const DecodeArgs& a, int n_splits, int batch, float qscale, hipStream_t s) {
+  if (a.batch != batch || n_splits % kXcds != 0) return hipErrorInvalidValue;
+  dim3 grid(static_cast<unsigned>(n_splits) * a.n_heads * batch);
+  hipLaunchKernelGGL((decode_partial_kc_kernel<KB, VB, D>), grid, dim3(64), 0, s, a, a.table, a.steal, qscale);
+  return hipGetLastError();
+}
+
+template <int KB, int D>
+hipError_t dispatch_kc_v(const DecodeArgs& a, int vbits, int n_splits, int batch, float qs, hipStream_t s) {
+  switch (vbits) {
+    case 2: return launch_kc_partial_t<KB, 2, D>(a, n_splits, batch, qs, s);
+    case 3: return launch_kc_partial_t<KB, 3, D>(a, n_splits, batch, qs, s);
+    case 4: return launch_kc_partial_t<KB, 4, D>(a, n_splits, batch, qs, s);
+    case 8: return launch_kc_partial_t<KB, 8, D>(a, n_splits, batch, qs, s);
+    case 16: return launch_kc_partial_t<KB, 16, D>(a, n_splits, batch, qs, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int D>
+hipError_t dispatch_kc_k(const DecodeArgs& a, int kbits, int vbits, int n_splits, int batch, float qs, hipStream_t s) {
+  switch (kbits) {
+    case 2: return dispatch_kc_v<2, D>(a, vbits, n_splits, batch, qs, s);
+    case 3: return dispatch_kc_v<3, D>(a, vbits, n_splits, batch, qs, s);
+    case 4: return dispatch_kc_v<4, D>(a, vbits, n_splits, batch, qs, s);
+    case 8: return dispatch_kc_v<8, D>(a, vbits, n_splits, batch, qs, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int KB, int D>
+int kc_waves_v(int vbits) {
+  switch (vbits) {
+    case 2: return KcWaves<KB, 2, D>::value;
+    case 3: return KcWaves<KB, 3, D>::value;
+    case 4: return KcWaves<KB, 4, D>::value;
+    case 8: return KcWaves<KB, 8, D>::value;
+    default: return KcWaves<KB, 16, D>::value;
+  }
+}
+
+template <int D>
+int kc_waves_k(int kbits, int vbits) {
+  switch (kbits) {
+    case 2: return kc_waves_v<2, D>(vbits);
+    case 3: return kc_waves_v<3, D>(vbits);
+    case 4: return kc_waves_v<4, D>(vbits);
+    default: return kc_waves_v<8, D>(vbits);
+  }
+}
+
 template <int D>
 int waves_k(int kbits, int vbits) {
   switch (kbits) {
@@ -1181,7 +1376,8 @@ int waves_k(int kbits, int vbits) {
 
 }  // namespace
 
-int decode_partial_waves_per_simd(int kbits, int vbits, int d) {
+int decode_partial_waves_per_simd(int kbits, int vbits, int d, bool kc) {
+  if (kc && kbits != 16) return d == 64 ? kc_waves_k<64>(kbits, vbits) : kc_waves_k<128>(kbits, vbits);
   return d == 64 ? waves_k<64>(kbits, vbits) : waves_k<128>(kbits, vbits);
 }
 
@@ -1190,7 +1386,11 @@ hipError_t launch_decode_partial(const DecodeArgs& a, int kbits, int vbits, int 
   if (n_splits == 0 || batch == 0 || a.n_heads == 0) return hipSuccess;
   // q~ = (R q) * log2(e) / sqrt(d), with R's 1/sqrt(n) folded in.
   const float qscale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(a.had_block) * d));
-  if (a.kc && kbits != 16) return launch_decode_kc(a, kbits, vbits, d, n_splits, batch, qscale, s);
+  if (a.kc && kbits != 16) {
+    if (d == 128) return dispatch_kc_k<128>(a, kbits, vbits, n_splits, batch, qscale, s);
+    if (d == 64) return dispatch_kc_k<64>(a, kbits, vbits, n_splits, batch, qscale, s);
+    return hipErrorInvalidValue;
+  }
   if (d == 128) return dispatch_k<128>(a, kbits, vbits, n_splits, batch, qscale, s);
   if (d == 64) return dispatch_k<64>(a, kbits, vbits, n_splits, batch, qscale, s);
   return hipErrorInvalidValue;

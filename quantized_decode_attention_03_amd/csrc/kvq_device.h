@@ -116,6 +116,29 @@ __device__ __forceinline__ float dpp_zero(float v) {  // lanes with no source re
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWMASK, 0xf, true));
 }
 
+// Sums over the wave of four per-lane values at once: two exchanges (lanes
+// l ^ 32, then l ^ 16) fold them into one register (rows of 16 lanes: value 0,
+// 2, 1, 3, each summed over four lanes), a row reduction finishes, and each
+// row's last lane holds its value's sum. (Plain lane shuffles: of the two
+// results of the half-swap builtins, this compiler can return the first for
+// both.)
+__device__ __forceinline__ void wave_sum4(const float (&x)[4], float (&out)[4]) {
+  const int lane = static_cast<int>(threadIdx.x) & 63;
+  const bool h32 = (lane & 32) != 0, h16 = (lane & 16) != 0;
+  const float a = (h32 ? x[1] : x[0]) + __shfl_xor(h32 ? x[0] : x[1], 32, 64);  // lanes <32: x0, else x1
+  const float b = (h32 ? x[3] : x[2]) + __shfl_xor(h32 ? x[2] : x[3], 32, 64);  // lanes <32: x2, else x3
+  float r = (h16 ? b : a) + __shfl_xor(h16 ? a : b, 16, 64);                     // rows: x0, x2, x1, x3
+  r += dpp_zero<kDppRowShr1, 0xf>(r);
+  r += dpp_zero<kDppRowShr2, 0xf>(r);
+  r += dpp_zero<kDppRowShr4, 0xf>(r);
+  r += dpp_zero<kDppRowShr8, 0xf>(r);
+  const int ri = __builtin_bit_cast(int, r);
+  out[0] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ri, 15));
+  out[2] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ri, 31));
+  out[1] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ri, 47));
+  out[3] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ri, 63));
+}
+
 __device__ __forceinline__ float wave_sum_scalar(float x) {
   x += dpp_zero<kDppRowShr1, 0xf>(x);
   x += dpp_zero<kDppRowShr2, 0xf>(x);

@@ -179,7 +179,8 @@ SplitPlan plan_splits(const kvq_segment& s, int batch) {
     const kvq_layout& L = *s.layout;
     double simd_share = 0.0;
     for (int h = 0; h < L.num_kv_heads; ++h)
-      simd_share += 1.0 / kvq::decode_partial_waves_per_simd(L.bits_k[h], L.bits_v[h], L.head_dim);
+      simd_share += 1.0 / kvq::decode_partial_waves_per_simd(L.bits_k[h], L.bits_v[h], L.head_dim,
+                                                              L.key_per_channel != 0);
     const int cus = device_cus() > 0 ? device_cus() : 256;
     // (rounded down to whole rounds of the eight XCDs, so the round is not overfilled)
     const int64_t fit = static_cast<int64_t>(4.0 * cus / (static_cast<double>(batch) * simd_share));

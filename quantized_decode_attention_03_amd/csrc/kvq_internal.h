@@ -55,7 +55,7 @@ struct DecodeArgs {
   const void* q;       // [batch][hkv*group][d]
   int32_t q_bf16;
   int32_t meta16;      // 1: float16 {s, mn} (4 bytes per row)
-  int32_t kc;          // 1: keys quantized per channel over each block (decode_kc_kernel)
+  int32_t kc;          // 1: keys quantized per channel over each block (decode_partial_kc_kernel)
   int32_t hkv, group, had_block;
   int32_t batch;       // sequences (the grid covers batch x n_heads units)
   int32_t slot_base;   // first split slot of this segment
@@ -119,16 +119,14 @@ hipError_t launch_dequant(const DequantArgs& a, hipStream_t s);
 hipError_t launch_decode_partial(const DecodeArgs& a, int kbits, int vbits, int d, int n_splits,
                                  int batch, hipStream_t s);
 hipError_t launch_decode_merge(const MergeArgs& a, hipStream_t s);
-// Per-channel keys (a.kc, kbits < 16): called by launch_decode_partial.
-hipError_t launch_decode_kc(const DecodeArgs& a, int kbits, int vbits, int d, int n_splits, int batch, float qscale,
-                            hipStream_t s);
 hipError_t launch_zero_words(uint32_t* p, size_t n_words, hipStream_t s);
 // Zeroes out[], accumulates the squared errors, then divides by rows * d.
 hipError_t launch_quant_mse(const QuantMseArgs& a, hipStream_t s);
 hipError_t launch_requant(const RequantArgs& a, int n_seqs, hipStream_t s);
 
-// Waves per SIMD the partial kernel for (kbits, vbits, d) is compiled to hold.
-int decode_partial_waves_per_simd(int kbits, int vbits, int d);
+// Waves per SIMD the partial kernel for (kbits, vbits, d) is compiled to hold
+// (kc: keys quantized per channel).
+int decode_partial_waves_per_simd(int kbits, int vbits, int d, bool kc);
 // Whether heads of this format can share a multi-format launch (2-, 3- and
 // 4-bit keys and values, head_dim 64 or 128, per-token keys).
 bool decode_partial_mixable(int kbits, int vbits, int d);

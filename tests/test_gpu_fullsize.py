@@ -125,6 +125,28 @@ def test_bf16_32k_baseline_decode_full_size():
     run_units(L, pool, table, out, k, v, q, [(0, 1), (11, 4), (15, 7)], seed=4)
 
 
+def test_per_channel_keys_32k_decode_full_size():
+    """The 32k shape with keys quantized per channel over each 16-token block (K4) and values per token (V4)."""
+    batch, tokens, hkv, group, d = 16, 32768, 8, 4, 128
+    L = kvq.kvq_layout_init(hkv, group, d, 128, [4] * hkv, [4] * hkv, key_per_channel=True)
+    k, v, q = synth.llama_layer_torch(2002, batch, tokens, hkv, group, d, device=T.DEV)
+    pool, table, table_t = full_cache(L, batch, tokens, k, v, seed=2002)
+    out = decode_units(L, pool, table_t, batch, tokens, q)
+    assert np.all(np.isfinite(out))
+    for b, h in [(0, 0), (13, 6)]:
+        k_rows = k[b, :, h].float().cpu().numpy()
+        v_rows = v[b, :, h].float().cpu().numpy()
+        q_rows = q[b, h * group:(h + 1) * group].float().cpu().numpy()
+        lay = O.Layout(1, group, d, 128, [4], [4], key_per_channel=True)
+        ref_table = np.arange(tokens // 16, dtype=np.int32)[None]
+        ref_pool = np.zeros((tokens // 16, lay.block_bytes), np.uint8)
+        O.quantize_append(lay, ref_pool, ref_table, np.array([0]), k_rows[None, :, None, :], v_rows[None, :, None, :])
+        expect = O.decode_attention([(lay, ref_pool, ref_table, np.array([tokens]))],
+                                    q_rows[None].astype(np.float64))[0]
+        err = T.max_rel_err(out[b, h * group:(h + 1) * group], expect)
+        assert err <= T.ATTN_TOL, f"unit (b={b}, h={h}): max relative error {err:.3e}"
+
+
 def test_mixed_precision_32k_decode_full_size():
     """Batch 8, 32768 tokens, per-head bits from kvq_plan_bits (average 3, ladder {2,3,4,8})."""
     batch, tokens, hkv, group, d, layers = 8, 32768, 8, 4, 128, 32
