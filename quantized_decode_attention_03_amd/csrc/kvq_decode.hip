@@ -148,24 +148,47 @@ template <int D> struct KFmt<8, D> {
 template <int D> struct KFmt<3, D> {
   static constexpr int kWords = (3 * D / 32 + 3) / 4;  // quarter = 3D/32 bytes (12 or 6)
   static constexpr bool bf16 = false;
-  __device__ static float sigma(int, int) { return 128.f; }
   static constexpr float kCentre = 0.f;
+  // Chunk c holds code pairs 4c..4c+3 of the quarter's bit stream. A pair
+  // (k, k + 5) lies 15 bits apart: one shift of the stream puts code k at bits
+  // 7-9 of the low half (sigma 128) and code k + 5 at bits 6-8 of the high half
+  // (sigma 64), and one and-or makes both fp16 values 1024 + sigma*c. Pairs
+  // 0..kFast-1 are such pairs, in blocks of ten codes; the rest (codes 30, 31
+  // at head_dim 128; 11, 12 and 13, 14 at 64) take each code apart (sigma 128).
+  static constexpr int kFast = D == 128 ? 15 : 6;
+  __device__ static constexpr bool fast(int p) { return p < kFast; }
+  __device__ static constexpr int code_of(int p, int j) {
+    return fast(p) ? 10 * (p / 5) + p % 5 + 5 * j : (D == 128 ? 30 + j : 11 + 2 * (p - 6) + j);
+  }
+  __device__ static float sigma(int c, int e) { return fast(4 * c + e / 2) && (e & 1) ? 64.f : 128.f; }
   __device__ static float base(int, int) { return 1024.f; }
-  __device__ static int channel(int c, int e) { return 8 * c + e; }
+  __device__ static int channel(int c, int e) { return code_of(4 * c + e / 2, e & 1); }
   template <int K>
   __device__ static uint32_t code(const uint32_t (&w)[kWords]) {
     constexpr int bit = 3 * K, i = bit / 32, sh = bit % 32;
     if constexpr (sh <= 29) return (w[i] >> sh) & 7u;
     else return ((w[i] >> sh) | (w[i + 1] << (32 - sh))) & 7u;
   }
+  template <int P>
+  __device__ static uint32_t pair(const uint32_t (&w)[kWords], uint32_t b) {
+    if constexpr (fast(P)) {
+      constexpr int s = 3 * code_of(P, 0) - 7;  // stream bit that lands at bit 0
+      uint32_t x;
+      if constexpr (s < 0) {
+        x = w[0] << (-s);
+      } else {
+        constexpr int i = s / 32, sh = s % 32;
+        const uint32_t hi = i + 1 < kWords ? w[i + 1 < kWords ? i + 1 : i] : 0u;
+        x = sh ? __builtin_amdgcn_alignbit(hi, w[i], sh) : w[i];
+      }
+      return and_or(x, 0x01c00380u, b);
+    } else {
+      return (((code<code_of(P, 1)>(w) << 16) | code<code_of(P, 0)>(w)) << 7) | b;
+    }
+  }
   template <int C>
   __device__ static u32x4_t unpack_c(const uint32_t (&w)[kWords], uint32_t b) {
-    u32x4_t r;
-    r[0] = (((code<8 * C + 1>(w) << 16) | code<8 * C + 0>(w)) << 7) | b;
-    r[1] = (((code<8 * C + 3>(w) << 16) | code<8 * C + 2>(w)) << 7) | b;
-    r[2] = (((code<8 * C + 5>(w) << 16) | code<8 * C + 4>(w)) << 7) | b;
-    r[3] = (((code<8 * C + 7>(w) << 16) | code<8 * C + 6>(w)) << 7) | b;
-    return r;
+    return u32x4_t{pair<4 * C>(w, b), pair<4 * C + 1>(w, b), pair<4 * C + 2>(w, b), pair<4 * C + 3>(w, b)};
   }
   __device__ static u32x4_t unpack(const uint32_t (&w)[kWords], int c, uint32_t b) {
     if constexpr (D == 128) {
@@ -332,12 +355,28 @@ __device__ __forceinline__ u32x4_t v_operand(const uint32_t (&raw)[8][VRaw<VB, D
       out = x | bias;
       out = pk_add_h(out, VFmt<VB, D>::center_bits(0));
     } else if constexpr (VB == 3) {
+      // Both tokens' fields in one word (token a in bits 0-15, token b in
+      // 16-31, the same code at the same offset; a byte permute, shared by the
+      // chunks): one shift then puts code c at bits 7-9 of each half and one
+      // and-or makes the fp16 pair. Head_dim 128: codes 0-4 from bytes 0-1,
+      // codes 5-7 from bytes 1-2 (code 5 at bit 7).
       constexpr int bpl = 3 * D / 16;  // 24 or 12 bits per lane
-      const uint32_t sh = (bpl * n) & 7;  // the lane's first bit within the loaded byte
-      const uint32_t wa = a[0] >> sh;
-      const uint32_t wb = b[0] >> sh;
-      const uint32_t ca = (wa >> (3 * c)) & 7u, cb = (wb >> (3 * c)) & 7u;
-      out = (((cb << 16) | ca) << 7) | bias;
+      uint32_t y;
+      int sft;
+      if constexpr (D == 128) {
+        if (c < 5) {
+          y = perm_b32(b[0], a[0], 0x05040100u);
+          sft = 3 * c - 7;
+        } else {
+          y = perm_b32(b[0], a[0], 0x06050201u);
+          sft = 3 * (c - 5);
+        }
+      } else {
+        const uint32_t sh = (bpl * n) & 7;  // the lane's first bit within the loaded byte
+        y = perm_b32(b[0] >> sh, a[0] >> sh, 0x05040100u);
+        sft = 3 * c - 7;
+      }
+      out = and_or(sft < 0 ? y << (-sft) : y >> sft, 0x03800380u, bias);
       out = pk_add_h(out, VFmt<VB, D>::center_bits(0));
     } else {  // bf16 values: channel n*D/16 + c is half (c & 1) of word c/2
       const int word = c >> 1;
