@@ -367,10 +367,17 @@ kvq_status kvq_decode_workspace_init(void* ws, size_t ws_bytes, kvq_stream strea
  * ws: device workspace of at least kvq_decode_workspace_bytes bytes, zeroed
  * once by kvq_decode_workspace_init before its first use. The waves of one
  * (sequence, KV head) share its pages through counters in ws, so two calls
- * in flight at once must not share a workspace. When the call makes several
- * launches (several segments or per-head bit pairs), they run concurrently
- * on library side streams forked from and joined back to `stream` with
- * events; graph capture of the call records the same dependencies.
+ * in flight at once must not share a workspace. The heads of one segment
+ * whose key and value widths are 2, 3 or 4 bits share one launch whatever
+ * their pairs; a call with several launches (several segments, or heads with
+ * 8- or 16-bit codes beside others) runs them concurrently on library side
+ * streams forked from and joined back to `stream` with events; graph capture
+ * of the call records the same dependencies.
+ * Environment (read at each call): KVQ_DECODE_DETERMINISTIC=1 fixes the order
+ * in which a unit's waves take its pages, so results are bitwise reproducible
+ * (default: most pages go to whichever wave is free, last-bit differences
+ * between runs); KVQ_SPLIT_PAGES=n sets the pages per split instead of the
+ * planner; KVQ_MIXED_LAUNCH=0 makes one launch per width pair.
  * Errors: KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE, KVQ_ERR_DEVICE.
  */
 kvq_status kvq_decode_attn(const kvq_segment* segs, int32_t n_segs, int32_t batch,
