@@ -551,11 +551,11 @@ struct KcLane {
 };
 
 template <int KB, int VB, int D, bool KC>
-__device__ __forceinline__ void compute_group(GroupRaw<KB, VB, D>& g, const u32x4_t (&qf)[D / 32][2],
+__device__ __forceinline__ void compute_group(GroupRaw<KB, VB, D>& g, const u32x4_t (&qf)[D / 32],
                                               const float (&biasq)[4], const float (&q2)[4], float inv_qsc, int G,
                                               int lane, uint32_t bias, uint16_t (*wt)[4][64],
                                               const uint16_t* wzero, SplitState<KB, VB, D>& st,
-                                              const KcLane& kl, uint4 (*qa)[2][64]) {
+                                              const KcLane& kl, uint4 (*qa)[64]) {
   using KF = KFmt<KB, D>;
   using VF = VFmt<VB, D>;
   constexpr int NCK = D / 32, NCV = D / 16;
@@ -563,14 +563,15 @@ __device__ __forceinline__ void compute_group(GroupRaw<KB, VB, D>& g, const u32x
   constexpr float NEG_INF = -__builtin_huge_valf();
   const int row = lane & 15, g4 = lane >> 4;
 
-  // QK: one 16x16 tile per page (rows = query heads, columns = tokens). Each
-  // chunk's query fragments (hi, lo) feed all four pages.
+  // QK: one 16x16 tile per page (rows 0-3 = hi parts of the query heads, rows
+  // 4-7 = lo parts, columns = tokens). Each chunk's query fragment feeds all
+  // four pages.
   float4_t cq[4];
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp) cq[pp] = float4_t{0.f, 0.f, 0.f, 0.f};
   if constexpr (KC) {
-    // Per page: A = q~ s / sigma at a power-of-two page scale (fp16 hi/lo in the
-    // LDS fragment area, rows >= 4 kept zero), B = the codes as in the row
+    // Per page: A = q~ s / sigma at a power-of-two page scale (fp16 hi in rows
+    // 0-3 and lo in rows 4-7 of the LDS fragment area), B = the codes as in the row
     // layout; score = sum / scale + the page constant of each query row.
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) {
@@ -593,15 +594,15 @@ __device__ __forceinline__ void compute_group(GroupRaw<KB, VB, D>& g, const u32x
         psc = ldexpf(1.f, 10 - ex);
       }
       if (kl.word >= 0) {
-        uint32_t* qw = reinterpret_cast<uint32_t*>(&qa[0][0][0]);
+        uint32_t* qw = reinterpret_cast<uint32_t*>(&qa[0][0]);
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
           const float y0 = x[h][0] * psc, y1 = x[h][1] * psc;
           const _Float16 h0 = static_cast<_Float16>(y0), h1 = static_cast<_Float16>(y1);
           const _Float16 l0 = static_cast<_Float16>(y0 - static_cast<float>(h0));
           const _Float16 l1 = static_cast<_Float16>(y1 - static_cast<float>(h1));
-          qw[kl.word + 4 * h] = half_bits(h0) | (half_bits(h1) << 16);
-          qw[kl.word + 4 * h + 256] = half_bits(l0) | (half_bits(l1) << 16);
+          qw[kl.word + 4 * h] = half_bits(h0) | (half_bits(h1) << 16);        // row h: hi
+          qw[kl.word + 4 * h + 16] = half_bits(l0) | (half_bits(l1) << 16);   // row 4 + h: lo
         }
       }
       float cst[4];
@@ -610,37 +611,36 @@ __device__ __forceinline__ void compute_group(GroupRaw<KB, VB, D>& g, const u32x
       const float ipsc = 1.f / psc;
 #pragma unroll
       for (int c = 0; c < NCK; ++c) {
-        const uint4 vh = qa[c][0][lane], vl = qa[c][1][lane];
-        const u32x4_t bk = KF::unpack(g.k[pp], c, bias);
-        cq[pp] = mfma<KF::bf16>(u32x4_t{vh.x, vh.y, vh.z, vh.w}, bk, cq[pp]);
-        cq[pp] = mfma<KF::bf16>(u32x4_t{vl.x, vl.y, vl.z, vl.w}, bk, cq[pp]);
+        const uint4 vq = qa[c][lane];
+        cq[pp] = mfma<KF::bf16>(u32x4_t{vq.x, vq.y, vq.z, vq.w}, KF::unpack(g.k[pp], c, bias), cq[pp]);
       }
+      // (the hi rows, lanes 0-15, take the constant once; the lo rows are added below)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) cq[pp][i] = fmaf(cq[pp][i], ipsc, cst[i]);
+      for (int i = 0; i < 4; ++i) cq[pp][i] = lane < 16 ? fmaf(cq[pp][i], ipsc, cst[i]) : cq[pp][i] * ipsc;
       __syncthreads();  // and read before the next page writes them
     }
   } else {
 #pragma unroll
-    for (int c = 0; c < NCK; ++c) {
-      const u32x4_t ah = qf[c][0], al = qf[c][1];
+    for (int c = 0; c < NCK; ++c)
 #pragma unroll
-      for (int pp = 0; pp < 4; ++pp) {
-        const u32x4_t bk = KF::unpack(g.k[pp], c, bias);
-        cq[pp] = mfma<KF::bf16>(ah, bk, cq[pp]);
-        cq[pp] = mfma<KF::bf16>(al, bk, cq[pp]);
-      }
-    }
+      for (int pp = 0; pp < 4; ++pp) cq[pp] = mfma<KF::bf16>(qf[c], KF::unpack(g.k[pp], c, bias), cq[pp]);
   }
-  // pack the four tiles: lane = token of the group, register i = head i
+  // Pack the four tiles (hi sums in lanes 0-15, lo sums in 16-31) into lane =
+  // token of the group, register i = head i: pages 0 and 2 (1 and 3) share a
+  // register, lanes 0-31 and 32-63; hi + lo with lane l ^ 16; then lanes 16-31
+  // take page 1 and lanes 32-47 page 2.
   float z[4];
   const float ks_q = g.ks * inv_qsc;
   // centred codes: s*sum q(c - m) + (mn + m*s)*sum q, the centre term per token
   const float kmid = KF::kCentre != 0.f ? fmaf(KF::kCentre, g.ks, g.kmn) : g.kmn;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const auto r01 = __builtin_amdgcn_permlane16_swap(f_bits(cq[0][i]), f_bits(cq[1][i]), false, false);
-    const auto r23 = __builtin_amdgcn_permlane16_swap(f_bits(cq[2][i]), f_bits(cq[3][i]), false, false);
-    const auto r = __builtin_amdgcn_permlane32_swap(r01[0], r23[0], false, false);
+    const auto x02 = __builtin_amdgcn_permlane32_swap(f_bits(cq[0][i]), f_bits(cq[2][i]), false, false);
+    const auto x13 = __builtin_amdgcn_permlane32_swap(f_bits(cq[1][i]), f_bits(cq[3][i]), false, false);
+    float y02 = bits_f(x02[0]), y13 = bits_f(x13[0]);
+    y02 += __shfl_xor(y02, 16, 64);
+    y13 += __shfl_xor(y13, 16, 64);
+    const auto r = __builtin_amdgcn_permlane16_swap(f_bits(y02), f_bits(y13), false, false);
     const float sc = bits_f(r[0]);
     float zi;
     if constexpr (KC) zi = sc;
@@ -736,7 +736,7 @@ __device__ __forceinline__ void compute_group(GroupRaw<KB, VB, D>& g, const u32x
 template <int D>
 struct PartialLds {
   float qs[4][D];
-  uint4 qa[D / 32][2][64];  // QK A fragments (hi, lo) in lane order
+  uint4 qa[D / 32][64];  // QK A fragments in lane order: rows 0-3 the fp16 hi parts of q~, rows 4-7 the lo parts
   __attribute__((aligned(16))) uint16_t wt[2][4][64];
   __attribute__((aligned(16))) uint16_t wzero[8];
 };
@@ -924,15 +924,19 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, const int32_t
     __syncthreads();
   }
 
-  // ---- QK A operands: row r = lane % 16 (query head), K-slots of quarter g4 ----
+  // ---- QK A operands: row r = lane % 16, K-slots of quarter g4. Rows 0-3 hold
+  // the hi fp16 parts of query heads 0-3, rows 4-7 the lo parts, so one MFMA
+  // per chunk and page gives both sums (lanes 0-15 and 16-31 of the tile) ----
   const int row = lane & 15;
   const int g4 = lane >> 4;
+  const int qrow = row & 3;                   // the query head of this row
+  const bool qact = row < 8 && qrow < G;
   float amax = 0.f;
 #pragma unroll
   for (int c = 0; c < NCK; ++c)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float v = row < G ? qs[row][g4 * (D / 4) + KF::channel(c, e)] * qscale / KF::sigma(c, e) : 0.f;
+      const float v = qact ? qs[qrow][g4 * (D / 4) + KF::channel(c, e)] * qscale / KF::sigma(c, e) : 0.f;
       amax = fmaxf(amax, fabsf(v));
     }
   amax = wave_max_scalar(amax);
@@ -953,7 +957,7 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, const int32_t
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int e = 2 * v + half;
-        const float qt = row < G ? qs[row][g4 * (D / 4) + KF::channel(c, e)] * qscale : 0.f;
+        const float qt = qact ? qs[qrow][g4 * (D / 4) + KF::channel(c, e)] * qscale : 0.f;
         const float x = qt / KF::sigma(c, e) * qsc;
         uint32_t hb, lb;
         float hv, lv;
@@ -973,8 +977,7 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, const int32_t
         hp |= hb << (16 * half);
         lp |= lb << (16 * half);
       }
-      reinterpret_cast<uint32_t*>(&qa[c][0][lane])[v] = hp;
-      reinterpret_cast<uint32_t*>(&qa[c][1][lane])[v] = lp;
+      reinterpret_cast<uint32_t*>(&qa[c][lane])[v] = row < 4 ? hp : lp;
     }
   }
   // Sum over the four quarters (lanes row, row+16, row+32, row+48), in fp64.
@@ -982,7 +985,7 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, const int32_t
   q1 += __shfl_xor(q1, 32, 64);
   q2l += __shfl_xor(q2l, 16, 64);
   q2l += __shfl_xor(q2l, 32, 64);
-  // Per query head constants, broadcast from lane i (row i):
+  // Per query head constants, broadcast from lane i (row i, a hi row):
   //   biasq_i = sum A * (base + centre*sigma) (scaled units; 1024 * sum A for the
   //   uncentred formats, 0 for centred ones), q2_i = sum_j q~_ij (log2 units).
   float biasq[4], q2[4];
@@ -996,8 +999,8 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, const int32_t
   const uint32_t bias = vconst(0x64006400u);  // fp16 pair (1024, 1024)
 
   // per-channel keys: the lane's q~ at its two channels, and their code scale
-  // and constant (the fragments above keep their zero rows >= group; rows 0-3
-  // are rewritten per page)
+  // and constant (the fragments above keep their zero rows 8-15; rows 0-7,
+  // hi and lo, are rewritten per page, zero for heads >= group)
   KcLane kl{};
   if constexpr (KC) {
     const int cw = kc_c < NCK ? kc_c : 0;
@@ -1014,7 +1017,7 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, const int32_t
       kl.isig[j] = 1.f / sg;
       kl.bsig[j] = KF::base(cw, 2 * kc_v + j) / sg;
     }
-    kl.word = kc_c < NCK ? (kc_c * 128 + 16 * (lane >> 4)) * 4 + kc_v : -1;
+    kl.word = kc_c < NCK ? (kc_c * 64 + 16 * (lane >> 4)) * 4 + kc_v : -1;
   }
 
   __syncthreads();  // the A fragments are read by the same wave; order LDS writes before reads
@@ -1033,29 +1036,25 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, const int32_t
   // buffers, the fragments and the PV accumulators against the 256
   // architectural registers, leaving room for the rest of the loop.
   constexpr int GROUP_WORDS = 4 * KF::kWords + 16 * VRaw<VB, D>::kWords + 4;
-  constexpr bool QF_REGS = !KC && KVQ_TUNE_QF_REGS && (DEPTH + 1) * GROUP_WORDS + 8 * NCK + 4 * NCV <= 180;
-  u32x4_t qreg[NCK][2];
+  constexpr bool QF_REGS = !KC && KVQ_TUNE_QF_REGS && (DEPTH + 1) * GROUP_WORDS + 4 * NCK + 4 * NCV <= 180;
+  u32x4_t qreg[NCK];
   if constexpr (QF_REGS) {
 #pragma unroll
-    for (int c = 0; c < NCK; ++c)
-#pragma unroll
-      for (int l = 0; l < 2; ++l) {
-        const uint4 v = qa[c][l][lane];
-        qreg[c][l] = u32x4_t{v.x, v.y, v.z, v.w};
-      }
+    for (int c = 0; c < NCK; ++c) {
+      const uint4 v = qa[c][lane];
+      qreg[c] = u32x4_t{v.x, v.y, v.z, v.w};
+    }
   }
   auto compute = [&](GroupRaw<KB, VB, D>& g) {
     if constexpr (QF_REGS) {
       compute_group<KB, VB, D, KC>(g, qreg, biasq, q2, inv_qsc, G, lane, bias, wt, wzero, st, kl, qa);
     } else {
-      u32x4_t qf[NCK][2];
+      u32x4_t qf[NCK];
 #pragma unroll
-      for (int c = 0; c < NCK; ++c)
-#pragma unroll
-        for (int l = 0; l < 2; ++l) {
-          const uint4 v = qa[c][l][lane];
-          qf[c][l] = u32x4_t{v.x, v.y, v.z, v.w};
-        }
+      for (int c = 0; c < NCK; ++c) {
+        const uint4 v = qa[c][lane];
+        qf[c] = u32x4_t{v.x, v.y, v.z, v.w};
+      }
       compute_group<KB, VB, D, KC>(g, qf, biasq, q2, inv_qsc, G, lane, bias, wt, wzero, st, kl, qa);
     }
   };
