@@ -756,6 +756,29 @@ __device__ __forceinline__ int kf_channel_rt(int c, int e) {
 // One split of one (sequence, KV head) unit in format (KB, VB): the body of the
 // partial kernels, inlined into each of them. KC: keys quantized per channel
 // over each page (the per-channel layout), values per token.
+// One stage of the query rotation's butterflies: channels j and j + ST (bit ST
+// of j clear) become u + v and u - v. A lane's value k is channel
+// (lane + 64k) % D, so stride 64 pairs the lane's values k and k + 1 and
+// smaller strides pair lanes lane and lane ^ ST.
+template <int ST, int QPL>
+__device__ __forceinline__ void q_butterfly(float (&qv)[QPL], int lane) {
+  if constexpr (ST == 64) {
+#pragma unroll
+    for (int k = 0; k < QPL; k += 2) {
+      const float u = qv[k], v = qv[k + 1];
+      qv[k] = u + v;
+      qv[k + 1] = u - v;
+    }
+  } else {
+    const bool upper = (lane & ST) != 0;
+#pragma unroll
+    for (int k = 0; k < QPL; ++k) {
+      const float p = __shfl_xor(qv[k], ST, 64);
+      qv[k] = upper ? p - qv[k] : qv[k] + p;
+    }
+  }
+}
+
 template <int KB, int VB, int D, bool M16, bool KC = false>
 __device__ __forceinline__ void partial_split(const DecodeArgs& a, const int32_t* __restrict__ table,
                                               uint32_t* __restrict__ steal, float qscale, PartialLds<D>& lds) {
@@ -802,8 +825,10 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, const int32_t
   // workspace. Wave speeds differ by tens of percent (the older of two waves
   // on a SIMD is issued first; some dies run slower); fast waves take more of
   // the tail, so a group's waves finish within about a page group of each
-  // other. Eight waves per counter keep the atomics on one address few. The
-  // last wave of a group to finish resets its counters to zero. Without
+  // other. Eight waves per counter keep the atomics on one address few. Each
+  // wave's fetches end with one that finds the tail used up; the wave whose
+  // fetch is the eighth such clears the counter (of the two words kept per
+  // group the second is unused). Without
   // sharing (deterministic order) wave i takes [i*SG, (i+1)*SG) with
   // SG = ceil(NG / 8) and there is no tail.
   const int W = static_cast<int>(gridDim.x) / U;
@@ -866,7 +891,9 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, const int32_t
   uint32_t inflight = 0;                 // lane 0: the outstanding tail fetch
   bool exhausted = pool_groups == 0;     // the tail is used up: no further fetches
   int next_gid = NG;                     // group of the resolved position (>= NG: none)
-  int32_t next_tab = 0;                  // lane i < 4: table entry of its page i
+  int32_t next_tab = 0;                  // lane t0 + i: table entry of the resolved position's page i
+  int tab_lane = 0;                      // t0: 0, or 4 when the entries came with the previous position's
+  bool tab_pre = false;                  // lanes 4-7 of next_tab hold the next position's entries
   auto fetch = [&]() {
     uint32_t v = 0;
     if (lane == 0) v = atomicAdd(ctr, 1u);
@@ -878,16 +905,34 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, const int32_t
       gid = min(wx * SG + rpos, NG);
     } else if (!exhausted) {
       const uint32_t idx = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(inflight)));
-      if (idx < pool_groups) gid = pool0 + static_cast<int>(idx);
-      else exhausted = true;
+      if (idx < pool_groups) {
+        gid = pool0 + static_cast<int>(idx);
+      } else {
+        exhausted = true;
+        // Each of the group's eight waves makes exactly one fetch past the
+        // tail, and none after it; the one that gets the last of these
+        // indices is the counter's last user and clears it for the next call.
+        if (lane == 0 && idx == pool_groups + static_cast<uint32_t>(kXcds - 1)) atomicExch(ctr, 0u);
+      }
     }
     // the position after this one is a tail position: fetch its group now
     if (rpos + 1 >= SG && !exhausted) fetch();
     ++rpos;
     next_gid = __builtin_amdgcn_readfirstlane(gid);  // wave-uniform: page addresses stay scalar
-    // (unconditional, clamped into the sequence's row like the page loads)
-    const int page = 4 * (g_lo + min(next_gid, NG)) + (lane & 3);
-    next_tab = trow[max(min(page, pages - 1), 0)];
+    if (tab_pre) {  // requested with the previous position (lanes 4-7)
+      tab_lane = 4;
+      tab_pre = false;
+    } else {
+      // Lanes 0-3: this position's four entries; lanes 4-7: the next
+      // position's when it is a static one, so that of the two positions
+      // loaded back to back at the start only the first waits for the table.
+      // (unconditional, clamped into the sequence's row like the page loads)
+      const int g = ((lane & 4) != 0 && rpos < SG) ? min(wx * SG + rpos, NG) : min(next_gid, NG);
+      const int page = 4 * (g_lo + g) + (lane & 3);
+      next_tab = trow[max(min(page, pages - 1), 0)];
+      tab_lane = 0;
+      tab_pre = rpos < SG;
+    }
   };
   if (SG == 0 && !exhausted) fetch();
   resolve();
@@ -895,7 +940,7 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, const int32_t
     const int gid = next_gid;
     int32_t blks[4];
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) blks[pp] = __builtin_amdgcn_readlane(next_tab, pp);
+    for (int pp = 0; pp < 4; ++pp) blks[pp] = __builtin_amdgcn_readlane(next_tab, tab_lane + pp);
     resolve();
     g.gid = gid;
     load_group<KB, VB, D, M16, KC>(a, pool, blks, 4 * (g_lo + gid), pages, seq_len, koff, voff, lane, kc0, kc1, g);
@@ -904,25 +949,30 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, const int32_t
   for (int j = 0; j < DEPTH; ++j) load_next(gbuf[j]);
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- q' = R q for the G query heads of this KV head (LDS butterflies) ----
+  // ---- q' = R q for the G query heads of this KV head (butterflies in registers,
+  // strides 1, 2, ... below the Hadamard block) ----
+  float qv[QPL];
+#pragma unroll
+  for (int k = 0; k < QPL; ++k) qv[k] = bits_f(qhi[k] << 16 | (a.q_bf16 ? 0u : qlo[k]));
+  {
+    const int n = a.had_block;
+    if (n > 1) q_butterfly<1>(qv, lane);
+    if (n > 2) q_butterfly<2>(qv, lane);
+    if (n > 4) q_butterfly<4>(qv, lane);
+    if (n > 8) q_butterfly<8>(qv, lane);
+    if (n > 16) q_butterfly<16>(qv, lane);
+    if (n > 32) q_butterfly<32>(qv, lane);
+    if constexpr (D > 64) {
+      if (n > 64) q_butterfly<64>(qv, lane);
+    }
+  }
 #pragma unroll
   for (int k = 0; k < QPL; ++k) {
     const int e = lane + 64 * k, r = e / D;
-    const float qf = bits_f(qhi[k] << 16 | (a.q_bf16 ? 0u : qlo[k]));
-    qs[r][e % D] = r < G ? qf : 0.f;
+    qs[r][e % D] = r < G ? qv[k] : 0.f;
   }
   if (lane < 8) wzero[lane] = 0;
   __syncthreads();
-  for (int st = 1; st < a.had_block; st <<= 1) {
-    for (int pi = lane; pi < 2 * D; pi += 64) {
-      const int r = pi / (D / 2), jj = pi % (D / 2);
-      const int j = (jj / st) * 2 * st + (jj % st);
-      const float u = qs[r][j], v = qs[r][j + st];
-      qs[r][j] = u + v;
-      qs[r][j + st] = u - v;
-    }
-    __syncthreads();
-  }
 
   // ---- QK A operands: row r = lane % 16, K-slots of quarter g4. Rows 0-3 hold
   // the hi fp16 parts of query heads 0-3, rows 4-7 the lo parts, so one MFMA
@@ -936,7 +986,10 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, const int32_t
   for (int c = 0; c < NCK; ++c)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float v = qact ? qs[qrow][g4 * (D / 4) + KF::channel(c, e)] * qscale / KF::sigma(c, e) : 0.f;
+      // (read for every lane and scaled by zero in inactive rows: a read under
+      // a condition becomes a branch and a wait per value)
+      const float r = qs[qrow][g4 * (D / 4) + KF::channel(c, e)];
+      const float v = r * (qact ? qscale / KF::sigma(c, e) : 0.f);
       amax = fmaxf(amax, fabsf(v));
     }
   amax = wave_max_scalar(amax);
@@ -957,7 +1010,7 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, const int32_t
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int e = 2 * v + half;
-        const float qt = qact ? qs[qrow][g4 * (D / 4) + KF::channel(c, e)] * qscale : 0.f;
+        const float qt = qs[qrow][g4 * (D / 4) + KF::channel(c, e)] * (qact ? qscale : 0.f);
         const float x = qt / KF::sigma(c, e) * qsc;
         uint32_t hb, lb;
         float hv, lv;
@@ -1008,8 +1061,9 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, const int32_t
     const bool own = kc_c < NCK;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      kl.qk[i][0] = own && i < G ? qs[i][kc_ch0] * qscale : 0.f;
-      kl.qk[i][1] = own && i < G ? qs[i][kc_ch1] * qscale : 0.f;
+      const float f = own && i < G ? qscale : 0.f;
+      kl.qk[i][0] = qs[i][kc_ch0] * f;
+      kl.qk[i][1] = qs[i][kc_ch1] * f;
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -1109,15 +1163,6 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, const int32_t
         ml[0] = lsum[i] > 0.f ? st.m_run[i] : NEG_INF;
         ml[1] = lsum[i];
       }
-    }
-  }
-  // Every tail fetch of this wave has returned (the last one found the tail
-  // used up). The wave that completes its sharing group resets both counters.
-  if (pool_groups != 0 && lane == 0) {
-    const uint32_t done = atomicAdd(ctr + 1, 1u);
-    if (done == static_cast<uint32_t>(kXcds - 1)) {
-      atomicExch(ctr, 0u);
-      atomicExch(ctr + 1, 0u);
     }
   }
 }
