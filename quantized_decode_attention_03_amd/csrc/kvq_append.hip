@@ -166,7 +166,11 @@ __device__ __forceinline__ uint64_t pack8(const float* u) {
   }
 }
 
-template <int BITS, int D>
+// EARLY: the destination's reads go out around the row's load (the start
+// position before it, the block-table entry after it), so they overlap the
+// load and the rotation; otherwise both follow the rotation (fewer registers
+// live across it, for the instance that covers every width).
+template <int BITS, int D, bool EARLY = true>
 __device__ __forceinline__ void append_rows(const AppendArgs& a, int half, double rs_n) {
   constexpr int LPR = 4, CPR = D / LPR;  // lanes per row, channels per lane
   constexpr int RPB = kThreads / LPR;    // rows per workgroup
@@ -181,6 +185,19 @@ __device__ __forceinline__ void append_rows(const AppendArgs& a, int half, doubl
   const int r = active ? row : 0;
   const int b = r / a.n_new;
   const int i = r - b * a.n_new;
+
+  // destination: start position, then the block-table entry (clamped into the
+  // row, read by every lane)
+  int p = 0, page = 0;
+  int32_t tab = -1;
+  auto read_start = [&]() {
+    p = a.start_pos[b] + i;
+    page = p / kBlockTokens;
+  };
+  auto read_table = [&]() {
+    tab = a.table[static_cast<int64_t>(b) * a.table_stride + min(max(page, 0), a.table_stride - 1)];
+  };
+  if constexpr (EARLY) read_start();
 
   // ---- load this lane's CPR channels ----
   float x[CPR];
@@ -204,6 +221,8 @@ __device__ __forceinline__ void append_rows(const AppendArgs& a, int half, doubl
     }
   }
 
+  if constexpr (EARLY) read_table();
+
   // ---- rotate ----
   {
     double xd[CPR];
@@ -214,15 +233,13 @@ __device__ __forceinline__ void append_rows(const AppendArgs& a, int half, doubl
     for (int j = 0; j < CPR; ++j) x[j] = static_cast<float>(xd[j] * rs_n);
   }
 
-  // ---- destination; rows whose page is unmapped are skipped ----
-  const int p = a.start_pos[b] + i;
-  const int page = p / kBlockTokens;
-  bool store = active && p >= 0 && page < a.table_stride;
-  int64_t blk = -1;
-  if (store) {
-    blk = a.table[static_cast<int64_t>(b) * a.table_stride + page];
-    store = blk >= 0 && blk < a.pool_blocks;
+  if constexpr (!EARLY) {
+    read_start();
+    read_table();
   }
+  // ---- destination; rows whose page is unmapped are skipped ----
+  const int64_t blk = tab;
+  const bool store = active && p >= 0 && page < a.table_stride && blk >= 0 && blk < a.pool_blocks;
   const int slot = p - page * kBlockTokens;
   uint8_t* dst = store ? a.pool + blk * a.block_bytes + area + slot * RB + m * (CPR * BITS / 8) : nullptr;
 
@@ -337,11 +354,11 @@ void append_kernel(AppendArgs a, double rs_n) {
     const int bits = a.head_bits[half][blockIdx.y];
     if (half == 0 && bits != 16 && a.key_per_channel) return;  // keys written by append_kc_kernel
     switch (bits) {
-      case 2: append_rows<2, D>(a, half, rs_n); break;
-      case 3: append_rows<3, D>(a, half, rs_n); break;
-      case 4: append_rows<4, D>(a, half, rs_n); break;
-      case 8: append_rows<8, D>(a, half, rs_n); break;
-      default: append_rows<16, D>(a, half, rs_n); break;  // the host sends 2, 3, 4, 8 or 16
+      case 2: append_rows<2, D, false>(a, half, rs_n); break;
+      case 3: append_rows<3, D, false>(a, half, rs_n); break;
+      case 4: append_rows<4, D, false>(a, half, rs_n); break;
+      case 8: append_rows<8, D, false>(a, half, rs_n); break;
+      default: append_rows<16, D, false>(a, half, rs_n); break;  // the host sends 2, 3, 4, 8 or 16
     }
   }
 }
