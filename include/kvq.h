@@ -335,7 +335,8 @@ kvq_status kvq_dequant(const kvq_layout* L, const void* pool, int64_t pool_block
 /*
  * Host. Bytes of device workspace kvq_decode_attn needs for these segments
  * and batch size: the split-K partials (max, sum and o' per query head and
- * split) and two work-sharing counters per (segment, sequence, KV head).
+ * split) and two 32-bit work-sharing words per (segment, sequence, KV head,
+ * group of eight splits).
  */
 kvq_status kvq_decode_workspace_bytes(const kvq_segment* segs, int32_t n_segs,
                                       int32_t batch, size_t* bytes);
