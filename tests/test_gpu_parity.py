@@ -308,6 +308,18 @@ def test_decode_fp32_query_and_inputs():
     assert T.max_rel_err(out, expect) <= T.ATTN_TOL
 
 
+@pytest.mark.parametrize("d,n", [(d, n) for d in (64, 128) for n in (1, 2, 4, 8, 16, 32, 64, 128) if n <= d])
+def test_decode_every_hadamard_block_fp32_query(d, n):
+    # The query's rotation runs one butterfly stage per stride below the block
+    # size, so each block size takes its own set of stages; fp32 queries use
+    # both halves of each element.
+    lens = [70, 333]
+    L, lay, cache, ref, table, k, v = build_case(d, n, 2, [4, 3], [2, 4], lens, seed=60 + n + d, in_bf16=False)
+    q = np.random.default_rng(61 + n).standard_normal((2, 4, d)).astype(np.float32) * 2
+    out, expect = decode_both(L, lay, cache, ref, table, lens, q, q_bf16=False)
+    assert T.max_rel_err(out, expect) <= T.ATTN_TOL
+
+
 def test_decode_three_precision_segments():
     # Long-context layout: newest 128 tokens in bf16, a log-spaced subset at
     # 4 bits, the rest at 2 bits, Hadamard block 32 (scaled to 4096 tokens).
