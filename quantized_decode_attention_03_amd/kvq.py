@@ -360,6 +360,17 @@ def kvq_logquant_requant(window, mid, low, batch, moves, stream=None):
     _check(st, "kvq_logquant_requant")
 
 
+def prepare_logquant_requant(window, mid, low, batch, moves, stream=None):
+    """kvq_logquant_requant with its segments marshalled once. `moves` is read when the call runs, so
+    one prepared call serves every step whose plan is written into the same array
+    (LogQuantStates.moves)."""
+    segs = _segments([window, mid, low])
+    args = (ctypes.byref(segs[0]), ctypes.byref(segs[1]), ctypes.byref(segs[2]), int(batch), moves,
+            _stream(stream))
+    return PreparedCall(lib().kvq_logquant_requant, args, "kvq_logquant_requant", (segs, window, mid, low, moves),
+                        stream is None)
+
+
 class Segment:
     """One precision segment: layout + pool + block table + per-sequence lengths."""
 

@@ -139,11 +139,17 @@ def test_logquant_dynamic_steps_match_oracle(d, n, window, starts, steps, mid_bi
     # ---- grow token by token ----
     segs = [caches[c].segment([cap[c]] * batch) for c in range(3)]
     table_dev = caches[0].table
+    # the requant is called prepared (arguments marshalled once, moves read at each call) on even
+    # steps and directly on odd ones
+    requant = kvq.prepare_logquant_requant(segs[0], segs[1], segs[2], batch, st.moves)
     for step in range(steps):
         totals = [int(t) for t in st.field("total")]
         before_mid = [st.mid_pos[b, :st.states[b].n_mid].copy() for b in range(batch)]
         moves = st.advance()
-        kvq.kvq_logquant_requant(segs[0], segs[1], segs[2], batch, moves)
+        if step % 2 == 0:
+            requant()
+        else:
+            kvq.kvq_logquant_requant(segs[0], segs[1], segs[2], batch, moves)
         mv = st.move_array()
         new = np.stack([x[b, totals[b]] for b in range(batch)])  # [batch, 2, hkv, d]
         nt = torch.from_numpy(new).to(dev).to(torch.bfloat16)
