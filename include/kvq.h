@@ -373,12 +373,17 @@ kvq_status kvq_decode_workspace_init(void* ws, size_t ws_bytes, kvq_stream strea
  * their pairs; a call with several launches (several segments, or heads with
  * 8- or 16-bit codes beside others) runs them concurrently on library side
  * streams forked from and joined back to `stream` with events; graph capture
- * of the call records the same dependencies.
+ * of the call records the same dependencies. The splits of several segments
+ * are planned to share one resident round of waves: the segment holding the
+ * most gives up the others' share, so the small launches run beside it.
  * Environment (read at each call): KVQ_DECODE_DETERMINISTIC=1 fixes the order
  * in which a unit's waves take its pages, so results are bitwise reproducible
  * (default: most pages go to whichever wave is free, last-bit differences
  * between runs); KVQ_SPLIT_PAGES=n sets the pages per split instead of the
- * planner; KVQ_MIXED_LAUNCH=0 makes one launch per width pair.
+ * planner; KVQ_MIXED_LAUNCH=0 makes one launch per width pair;
+ * KVQ_SEGMENT_RESERVE=0 sizes every segment's launch to fill the device alone.
+ * The workspace size follows the same plan, so kvq_decode_workspace_bytes
+ * must see the same environment (a smaller workspace is KVQ_ERR_WORKSPACE).
  * Errors: KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE, KVQ_ERR_DEVICE.
  */
 kvq_status kvq_decode_attn(const kvq_segment* segs, int32_t n_segs, int32_t batch,

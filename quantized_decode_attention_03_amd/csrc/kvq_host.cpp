@@ -143,6 +143,13 @@ bool mixed_launch_enabled() {
   return !(env && env[0] == '0');
 }
 
+// KVQ_SEGMENT_RESERVE=0: every segment's launch is sized to fill the device
+// alone, as for a single segment.
+bool reserve_for_small_segments() {
+  const char* env = std::getenv("KVQ_SEGMENT_RESERVE");
+  return !(env && env[0] == '0');
+}
+
 // Split plan of one segment: nominal pages per split (a multiple of 4) and
 // the number of waves (splits) per (sequence, KV head). The kernel shares a
 // unit's pages among its waves itself; the nominal size only sets the count.
@@ -222,12 +229,42 @@ kvq_status check_segments(const kvq_segment* segs, int n_segs, int batch, const 
   return KVQ_OK;
 }
 
+// SIMDs one split of one sequence of segment s holds: a head whose format runs
+// w waves per SIMD takes 1/w of one.
+double split_simd_share(const kvq_segment& s) {
+  const kvq_layout& L = *s.layout;
+  double share = 0.0;
+  for (int h = 0; h < L.num_kv_heads; ++h)
+    share += 1.0 / kvq::decode_partial_waves_per_simd(L.bits_k[h], L.bits_v[h], L.head_dim, L.key_per_channel != 0);
+  return share;
+}
+
 int total_slots(const kvq_segment* segs, int n_segs, int batch, std::vector<SplitPlan>* plans) {
+  std::vector<SplitPlan> p(n_segs);
+  for (int i = 0; i < n_segs; ++i) p[i] = plan_splits(segs[i], batch);
+  // Several segments' launches run at once, and each was sized to fill one
+  // resident round alone. The one holding most SIMDs gives up the others'
+  // share (in whole groups of eight splits), so the small launches run beside
+  // it rather than after its waves retire.
+  if (n_segs > 1 && batch > 0 && !std::getenv("KVQ_SPLIT_PAGES") && reserve_for_small_segments()) {
+    const double round = 4.0 * (device_cus() > 0 ? device_cus() : 256);
+    int big = 0;
+    double big_share = -1.0, all = 0.0;
+    for (int i = 0; i < n_segs; ++i) {
+      const double sh = static_cast<double>(p[i].n_splits) * batch * split_simd_share(segs[i]);
+      all += sh;
+      if (sh > big_share) { big = i; big_share = sh; }
+    }
+    const double per_split = batch * split_simd_share(segs[big]);
+    if (all > round && per_split > 0.0) {
+      const int fit = static_cast<int>((round - (all - big_share)) / per_split) / 8 * 8;
+      p[big].n_splits = std::min(p[big].n_splits, std::max(fit, 8));
+    }
+  }
   int total = 0;
   for (int i = 0; i < n_segs; ++i) {
-    SplitPlan p = plan_splits(segs[i], batch);
-    if (plans) plans->push_back(p);
-    total += p.n_splits;
+    if (plans) plans->push_back(p[i]);
+    total += p[i].n_splits;
   }
   return total;
 }
