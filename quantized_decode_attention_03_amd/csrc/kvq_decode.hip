@@ -1271,21 +1271,22 @@ __global__ __launch_bounds__(64 * NW) void decode_merge_kernel(MergeArgs a, floa
       }
       __syncthreads();
       const float* pc = po + static_cast<int64_t>(s0) * D + CPL * lane;
-      int s = w;
-      for (; s + 7 * NW < n; s += 8 * NW) {
-        float v[8][CPL];
+      // batches of eight slots (w, w + NW, ...), the last one padded with the
+      // list's last slot at weight 0, so no slot waits on another's load
+      for (int s = w; s < n; s += 8 * NW) {
+        float v[8][CPL], wu[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int su = s + u * NW, sc = min(su, n - 1);
+#pragma unroll
+          for (int j = 0; j < CPL; ++j) v[u][j] = pc[static_cast<int64_t>(sc) * D + j];
+          wu[u] = su < n ? wsh[sc] : 0.f;
+        }
 #pragma unroll
         for (int u = 0; u < 8; ++u)
 #pragma unroll
-          for (int j = 0; j < CPL; ++j) v[u][j] = pc[static_cast<int64_t>(s + u * NW) * D + j];
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-#pragma unroll
-          for (int j = 0; j < CPL; ++j) x[j] = fmaf(wsh[s + u * NW], v[u][j], x[j]);
+          for (int j = 0; j < CPL; ++j) x[j] = fmaf(wu[u], v[u][j], x[j]);
       }
-      for (; s < n; s += NW)
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) x[j] = fmaf(wsh[s], pc[static_cast<int64_t>(s) * D + j], x[j]);
     }
   }
   // combine the four waves
