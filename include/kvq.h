@@ -3,18 +3,31 @@
  * fused quantized decode attention for AMD Instinct MI355X (gfx950).
  *
  * Conventions (all entry points):
- *  - Every function returns kvq_status. KVQ_OK is 0. On failure nothing is
- *    launched and nothing is written, and kvq_last_error() returns a message
- *    for the calling thread (valid until the next kvq call on that thread).
+ *  - Every function returns kvq_status. KVQ_OK is 0. An argument error
+ *    (KVQ_ERR_ARG, _UNSUPPORTED, _BUDGET, _WORKSPACE, _CAPACITY) is found
+ *    before anything is launched or written. kvq_last_error() returns a
+ *    message for the calling thread (valid until the next kvq call on that
+ *    thread).
+ *  - A call that makes several launches and gets KVQ_ERR_DEVICE from one of
+ *    them may already have queued the launches before it (they then run). A
+ *    decode call that forked work onto side streams joins them back to the
+ *    caller's stream on every return path.
  *  - No C++ exception crosses this boundary.
  *  - "device" pointers are HIP device memory owned by the caller; the library
- *    never allocates, frees or retains device memory.
+ *    never allocates, frees or retains device memory (the one exception is
+ *    kvq_decode_attn_noalloc's fixed scratch array, below).
  *  - Device work is asynchronous on the caller's hipStream_t (0 = the null
  *    stream) with no implicit synchronisation. A launch failure is reported as
  *    KVQ_ERR_DEVICE.
  *  - Host functions are synchronous and need no GPU.
- *  - Functions keep no global mutable state; concurrent calls that write
- *    different buffers are safe.
+ *  - Process-wide state, all of it created once and then only read, except
+ *    where noted: the device's compute-unit count (read once, sizes the split
+ *    plan); per device, four side streams and their fork/join events, used by
+ *    decode calls that make several partial launches (several segments, or
+ *    heads whose widths cannot share one launch). Those calls hold a mutex
+ *    while they enqueue, so such calls from different threads serialise on
+ *    the host, and their side-stream work queues behind one another on the
+ *    device. Calls that write different buffers are otherwise independent.
  *  - Inputs must be finite; results on NaN or Inf inputs are unspecified.
  *
  * Sources for what is computed (page titles as published on gist.science):
@@ -303,8 +316,11 @@ kvq_status kvq_page_alloc(const int32_t* free_list, int32_t n_free, int32_t* cur
  * For b = 16 the rotated row is stored as bf16. With key_per_channel the keys
  * of each block are quantized together, per channel over its 16 tokens (same
  * formulas along the token axis), so such appends write whole blocks: n_new
- * and every start_pos[b] must be multiples of 16 (n_new is checked; the keys
- * of a sequence whose start_pos is not are not written).
+ * and every start_pos[b] must be multiples of 16. n_new is checked here; the
+ * start positions live in device memory, which this asynchronous call does
+ * not read on the host, so for a sequence whose start_pos is not a multiple
+ * of 16 the kernel writes its values but no keys. kvq_append_check finds
+ * such a sequence on the host copy of the positions before the launch.
  * In:  k, v device [batch][n_new][Hkv][head_dim] of in_dtype; start_pos device
  *      [batch]; block_table device. Every block the new tokens touch must be
  *      mapped; a row whose block id is outside [0, pool_blocks) is skipped.
@@ -317,6 +333,18 @@ kvq_status kvq_quantize_append(const kvq_layout* L, void* pool, int64_t pool_blo
                                int32_t batch, const int32_t* start_pos, int32_t n_new,
                                const void* k, const void* v, kvq_dtype in_dtype,
                                kvq_stream stream);
+
+/*
+ * Host. Checks the start positions of a kvq_quantize_append call on their
+ * host copy, before the launch: every start_pos_host[b] >= 0, every new
+ * token's block inside the table row (start_pos_host[b] + n_new <=
+ * 16 * table_stride), and, for a layout with per-channel keys, n_new and
+ * every start_pos_host[b] multiples of 16 (whole blocks).
+ * Errors: KVQ_ERR_ARG naming the first sequence that fails (nothing else is
+ * done; a stale layout or null pointers are KVQ_ERR_ARG too).
+ */
+kvq_status kvq_append_check(const kvq_layout* L, int32_t batch, const int32_t* start_pos_host,
+                            int32_t n_new, int32_t table_stride);
 
 /*
  * Device, async. Read back n tokens [pos0, pos0 + n) of sequence `seq`:
@@ -333,10 +361,21 @@ kvq_status kvq_dequant(const kvq_layout* L, const void* pool, int64_t pool_block
                        float* k_out, float* v_out, kvq_stream stream);
 
 /*
+ * Bytes at the front of every decode workspace that hold the work-sharing
+ * counters. Their place and size are fixed (they do not follow the split
+ * plan), so one workspace may serve decode calls of any plan, geometry or
+ * batch, as long as it is large enough for each.
+ */
+#define KVQ_DECODE_COUNTER_BYTES 65536
+
+/*
  * Host. Bytes of device workspace kvq_decode_attn needs for these segments
- * and batch size: the split-K partials (max, sum and o' per query head and
- * split) and two 32-bit work-sharing words per (segment, sequence, KV head,
- * group of eight splits).
+ * and batch size: KVQ_DECODE_COUNTER_BYTES of work-sharing counters at the
+ * front, then the split-K partials (o', then max and sum, per query head and
+ * split). A call uses two 32-bit counter words per (segment, sequence, KV
+ * head, group of eight splits) from the front of the counter area; a call
+ * that would need more than the area holds runs in the fixed order
+ * (KVQ_DECODE_DETERMINISTIC) and uses none.
  */
 kvq_status kvq_decode_workspace_bytes(const kvq_segment* segs, int32_t n_segs,
                                       int32_t batch, size_t* bytes);
@@ -368,7 +407,9 @@ kvq_status kvq_decode_workspace_init(void* ws, size_t ws_bytes, kvq_stream strea
  * ws: device workspace of at least kvq_decode_workspace_bytes bytes, zeroed
  * once by kvq_decode_workspace_init before its first use. The waves of one
  * (sequence, KV head) share its pages through counters in ws, so two calls
- * in flight at once must not share a workspace. The heads of one segment
+ * in flight at once must not share a workspace. Every completed call leaves
+ * the counters zero, and the counters sit in a fixed area that partials never
+ * use, so the workspace is reused as it is by calls of any split plan. The heads of one segment
  * whose key and value widths are 2, 3 or 4 bits share one launch whatever
  * their pairs; a call with several launches (several segments, or heads with
  * 8- or 16-bit codes beside others) runs them concurrently on library side

@@ -1,6 +1,6 @@
 """Build libkvq.so in-tree with hipcc for gfx950.
 
-    python -m quantized_decode_attention_03_amd.build
+    python -m quantized_decode_attention_03_amd.build [--incremental]
 
 Every source is compiled to an object in `_build/` in parallel, then linked
 into `quantized_decode_attention_03_amd/libkvq.so`.
@@ -51,10 +51,23 @@ def _compile(src):
     return obj
 
 
-def build(verbose=True):
+def _stale(src):
+    """Whether src's object is older than src or any header (for --incremental)."""
+    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+    if not os.path.exists(obj):
+        return True
+    deps = [os.path.join(CSRC, src)] + [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")]
+    deps += [os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE)]
+    return max(os.path.getmtime(p) for p in deps) > os.path.getmtime(obj)
+
+
+def build(verbose=True, incremental=False):
+    """Compile every source (or, with incremental=True, only those whose object is out of date) and link."""
     os.makedirs(BUILD_DIR, exist_ok=True)
+    todo = [s for s in SOURCES if not incremental or _stale(s)]
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        list(ex.map(_compile, todo))
+    objs = [os.path.join(BUILD_DIR, os.path.splitext(s)[0] + ".o") for s in SOURCES]
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -67,5 +80,5 @@ def build(verbose=True):
 
 
 if __name__ == "__main__":
-    build()
+    build(incremental="--incremental" in sys.argv[1:])
     sys.exit(0)

@@ -269,18 +269,25 @@ int total_slots(const kvq_segment* segs, int n_segs, int batch, std::vector<Spli
   return total;
 }
 
-// Workspace: partial o' [batch][hq][slots][d], partial (max, sum)
-// [batch][hq][slots][2], then the work-sharing counters: for each segment
-// [batch][hkv][splits / 8][2] (uint32, zero between calls); slots is the sum
-// of the segments' splits, so the counters take slots / 8 * batch * hkv * 2
-// words in all.
+// Workspace: the work-sharing counter region (KVQ_DECODE_COUNTER_BYTES at the
+// front, zero between calls), then partial o' [batch][hq][slots][d], then
+// partial (max, sum) [batch][hq][slots][2]. A call's counters are the first
+// words of the region: per segment [batch][hkv][splits / 8][2] (uint32);
+// slots is the sum of the segments' splits, so a call takes
+// slots / 8 * batch * hkv * 2 words. The region's place and size do not depend
+// on the split plan, so no call's partials ever land on any call's counters,
+// and one workspace serves calls of any plan.
+constexpr size_t kCounterBytes = KVQ_DECODE_COUNTER_BYTES;
 size_t partials_bytes(int batch, int hq, int d, int slots) {
   if (slots == 0) slots = 1;
   return static_cast<size_t>(batch) * hq * slots * (static_cast<size_t>(d) + 2) * sizeof(float);
 }
-size_t workspace_bytes(int batch, int hq, int hkv, int d, int slots) {
-  return partials_bytes(batch, hq, d, slots) + static_cast<size_t>(slots / 8) * batch * hkv * 2 * sizeof(uint32_t);
+size_t workspace_bytes(int batch, int hq, int d, int slots) {
+  return kCounterBytes + partials_bytes(batch, hq, d, slots);
 }
+// Counter words a call with this plan uses; more than the region holds sends
+// the call to the fixed order, which uses none.
+size_t counter_words(int batch, int hkv, int slots) { return static_cast<size_t>(slots / 8) * batch * hkv * 2; }
 
 }  // namespace
 
@@ -714,6 +721,30 @@ kvq_status kvq_quantize_append(const kvq_layout* L, void* pool, int64_t pool_blo
   return ok();
 }
 
+kvq_status kvq_append_check(const kvq_layout* L, int32_t batch, const int32_t* start_pos_host, int32_t n_new,
+                            int32_t table_stride) {
+  kvq_status st = check_layout_ready(L, "kvq_append_check");
+  if (st != KVQ_OK) return st;
+  if (batch < 0 || n_new < 0 || table_stride < 1)
+    return fail(KVQ_ERR_ARG, "kvq_append_check: batch < 0, n_new < 0 or table_stride < 1");
+  if (batch > 0 && !start_pos_host) return fail(KVQ_ERR_ARG, "kvq_append_check: null start_pos_host");
+  if (L->key_per_channel && n_new % KVQ_BLOCK_TOKENS != 0)
+    return fail(KVQ_ERR_ARG, "kvq_append_check: per-channel keys are appended in whole blocks (n_new %d)", n_new);
+  const int64_t capacity = static_cast<int64_t>(table_stride) * KVQ_BLOCK_TOKENS;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t p = start_pos_host[b];
+    if (p < 0) return fail(KVQ_ERR_ARG, "kvq_append_check: sequence %d start_pos %lld < 0", b, static_cast<long long>(p));
+    if (p + n_new > capacity)
+      return fail(KVQ_ERR_ARG, "kvq_append_check: sequence %d tokens [%lld, %lld) exceed the table row (%d blocks)", b,
+                  static_cast<long long>(p), static_cast<long long>(p + n_new), table_stride);
+    if (L->key_per_channel && p % KVQ_BLOCK_TOKENS != 0)
+      return fail(KVQ_ERR_ARG,
+                  "kvq_append_check: sequence %d start_pos %lld is not a block boundary (per-channel keys)", b,
+                  static_cast<long long>(p));
+  }
+  return ok();
+}
+
 kvq_status kvq_dequant(const kvq_layout* L, const void* pool, int64_t pool_blocks, const int32_t* block_table,
                        int32_t table_stride, int32_t seq, int32_t pos0, int32_t n, int32_t rotated, float* k_out,
                        float* v_out, kvq_stream stream) {
@@ -769,8 +800,7 @@ kvq_status kvq_decode_workspace_bytes(const kvq_segment* segs, int32_t n_segs, i
   kvq_status st = check_segments(segs, n_segs, batch, "kvq_decode_workspace_bytes");
   if (st != KVQ_OK) return st;
   const kvq_layout& L = *segs[0].layout;
-  *bytes = workspace_bytes(batch, L.num_kv_heads * L.group, L.num_kv_heads, L.head_dim,
-                           total_slots(segs, n_segs, batch, nullptr));
+  *bytes = workspace_bytes(batch, L.num_kv_heads * L.group, L.head_dim, total_slots(segs, n_segs, batch, nullptr));
   return ok();
 }
 
@@ -801,13 +831,14 @@ kvq_status kvq_decode_partial(const kvq_segment* segs, int32_t n_segs, int32_t b
   const int hq = L0.num_kv_heads * L0.group;
   std::vector<SplitPlan> plans;
   const int slots = total_slots(segs, n_segs, batch, &plans);
-  const size_t need = workspace_bytes(batch, hq, L0.num_kv_heads, L0.head_dim, slots);
+  const size_t need = workspace_bytes(batch, hq, L0.head_dim, slots);
   if (ws_bytes < need)
     return fail(KVQ_ERR_WORKSPACE, "kvq_decode_partial: workspace %zu < %zu bytes", ws_bytes, need);
-  float* part_o = static_cast<float*>(ws);
+  uint32_t* steal = static_cast<uint32_t*>(ws);
+  float* part_o = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kCounterBytes);
   float* part_ml = part_o + static_cast<size_t>(batch) * hq * std::max(slots, 1) * L0.head_dim;
-  uint32_t* steal = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) +
-                                                partials_bytes(batch, hq, L0.head_dim, slots));
+  const bool share_tail =
+      !deterministic_order() && counter_words(batch, L0.num_kv_heads, slots) * sizeof(uint32_t) <= kCounterBytes;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   struct Launch {
     kvq::DecodeArgs a;
@@ -856,7 +887,7 @@ kvq_status kvq_decode_partial(const kvq_segment* segs, int32_t n_segs, int32_t b
         a.had_block = L.had_block;
         a.batch = batch;
         a.steal = steal + static_cast<size_t>(slot_base / 8) * batch * L.num_kv_heads * 2;
-        a.share_tail = deterministic_order() ? 0 : 1;
+        a.share_tail = share_tail ? 1 : 0;
         a.slot_base = slot_base;
         a.total_slots = slots;
         a.part_o = part_o;
@@ -899,17 +930,32 @@ kvq_status kvq_decode_partial(const kvq_segment* segs, int32_t n_segs, int32_t b
     return device_status(e, "kvq_decode_partial side streams (call kvq_decode_workspace_init before capturing)");
   const int n_side = std::min<int>(kSideStreams, static_cast<int>(launches.size()) - 1);
   if ((e = hipEventRecord(ss->fork, s)) != hipSuccess) return device_status(e, "kvq_decode_partial fork");
-  for (int i = 0; i < n_side; ++i)
-    if ((e = hipStreamWaitEvent(ss->s[i], ss->fork, 0)) != hipSuccess) return device_status(e, "kvq_decode_partial fork");
-  for (size_t j = 0; j < launches.size(); ++j) {
+  // Every side stream that was forked is joined back, also after a failed
+  // launch, so the caller's stream (or a capture of it) never leaves work of
+  // this call behind on a side stream.
+  int forked = 0;
+  hipError_t first = hipSuccess;
+  const char* what = "kvq_decode_partial launch";
+  for (; forked < n_side; ++forked) {
+    if ((e = hipStreamWaitEvent(ss->s[forked], ss->fork, 0)) != hipSuccess) {
+      first = e;
+      what = "kvq_decode_partial fork";
+      break;
+    }
+  }
+  for (size_t j = 0; j < launches.size() && first == hipSuccess; ++j) {
     hipStream_t st = j == 0 ? s : ss->s[(j - 1) % n_side];
-    if ((e = launch(launches[j], st)) != hipSuccess) return device_status(e, "kvq_decode_partial launch");
+    first = launch(launches[j], st);
   }
-  for (int i = 0; i < n_side; ++i) {
-    if ((e = hipEventRecord(ss->join[i], ss->s[i])) != hipSuccess) return device_status(e, "kvq_decode_partial join");
-    if ((e = hipStreamWaitEvent(s, ss->join[i], 0)) != hipSuccess) return device_status(e, "kvq_decode_partial join");
+  for (int i = 0; i < forked; ++i) {
+    hipError_t ej = hipEventRecord(ss->join[i], ss->s[i]);
+    if (ej == hipSuccess) ej = hipStreamWaitEvent(s, ss->join[i], 0);
+    if (ej != hipSuccess && first == hipSuccess) {
+      first = ej;
+      what = "kvq_decode_partial join";
+    }
   }
-  return ok();
+  return device_status(first, what);
 }
 
 kvq_status kvq_decode_merge(const kvq_segment* segs, int32_t n_segs, int32_t batch, float* out, void* ws,
@@ -921,13 +967,13 @@ kvq_status kvq_decode_merge(const kvq_segment* segs, int32_t n_segs, int32_t bat
   const kvq_layout& L0 = *segs[0].layout;
   const int hq = L0.num_kv_heads * L0.group;
   const int slots = total_slots(segs, n_segs, batch, nullptr);
-  const size_t need = workspace_bytes(batch, hq, L0.num_kv_heads, L0.head_dim, slots);
+  const size_t need = workspace_bytes(batch, hq, L0.head_dim, slots);
   if (ws_bytes < need) return fail(KVQ_ERR_WORKSPACE, "kvq_decode_merge: workspace %zu < %zu bytes", ws_bytes, need);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   // With no split at all the merge kernel still runs and writes zero rows
   // (no memset node, so the call stays safe to capture in a graph).
   kvq::MergeArgs a{};
-  a.part_o = static_cast<const float*>(ws);
+  a.part_o = reinterpret_cast<const float*>(static_cast<const uint8_t*>(ws) + kCounterBytes);
   a.part_ml = a.part_o + static_cast<size_t>(batch) * hq * std::max(slots, 1) * L0.head_dim;
   a.batch = batch;
   a.hq = hq;

@@ -27,7 +27,10 @@ EXPORTED = [
     "kvq_decode_workspace_bytes", "kvq_decode_workspace_init", "kvq_decode_attn", "kvq_decode_partial",
     "kvq_decode_merge", "kvq_fit_distortion", "kvq_amgm_ratio", "kvq_quant_mse",
     "kvq_logquant_dynamic_classes", "kvq_logquant_init", "kvq_logquant_advance", "kvq_logquant_requant",
+    "kvq_append_check",
 ]
+
+KVQ_DECODE_COUNTER_BYTES = 65536
 
 
 class KvqError(RuntimeError):
@@ -111,6 +114,7 @@ def lib():
     L.kvq_page_alloc.argtypes = [vp, i32, vp, i32, vp, vp, vp, i32]
     L.kvq_quantize_append.argtypes = [ctypes.POINTER(KvqLayout), vp, i64, vp, i32, i32, vp, i32, vp, vp,
                                       ctypes.c_int, vp]
+    L.kvq_append_check.argtypes = [ctypes.POINTER(KvqLayout), i32, vp, i32, i32]
     L.kvq_dequant.argtypes = [ctypes.POINTER(KvqLayout), vp, i64, vp, i32, i32, i32, i32, i32, vp, vp, vp]
     L.kvq_decode_workspace_bytes.argtypes = [ctypes.POINTER(KvqSegment), i32, i32, ctypes.POINTER(sz)]
     L.kvq_decode_workspace_init.argtypes = [vp, sz, vp]
@@ -312,6 +316,13 @@ def kvq_quantize_append(layout, pool, block_table, start_pos, k, v, stream=None)
         _dev_ptr(k, (torch.float32, torch.bfloat16), "k"), _dev_ptr(v, (torch.float32, torch.bfloat16), "v"),
         dt, _stream(stream))
     _check(st, "kvq_quantize_append")
+
+
+def kvq_append_check(layout, start_pos, n_new, table_stride):
+    """Host check of an append's start positions (host array-like [batch]) before the launch."""
+    start = np.ascontiguousarray(start_pos, dtype=np.int32)
+    _check(lib().kvq_append_check(ctypes.byref(layout), int(start.shape[0]), _np_ptr(start), int(n_new),
+                                  int(table_stride)), "kvq_append_check")
 
 
 def kvq_dequant(layout, pool, block_table, seq, pos0, n, rotated=True, k_out=None, v_out=None, stream=None):

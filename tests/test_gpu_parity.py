@@ -451,12 +451,51 @@ def test_decode_work_sharing_matches_fixed_order_and_oracle(monkeypatch):
     for o in outs:
         assert T.max_rel_err(o, expect) <= T.ATTN_TOL
         assert T.rel(o, fixed) < 1e-5
-    # the counters (the workspace's last words: two per sequence, KV head and
-    # group of eight splits) are zero again
-    slots = ws.numel() // (3 * 8 * 130 * 4 + 3 * 2 * 2 * 4 // 8)
-    n_cnt = (slots // 8) * 3 * 2 * 2
-    tail = ws[-4 * n_cnt:].view(torch.int32).cpu().numpy()
-    assert slots % 8 == 0 and np.all(tail == 0)
+    # the counters (the workspace's fixed front area) are zero again
+    head = ws[:kvq.KVQ_DECODE_COUNTER_BYTES].view(torch.int32).cpu().numpy()
+    assert np.all(head == 0)
+
+
+def test_workspace_reused_across_split_plans(monkeypatch):
+    """One workspace, zeroed once, serves decode calls whose split plans differ.
+
+    Widths differ per head and layer (RateQuant page, Methodology stage 3), so
+    the split plan, and with it the size of the partials, differs from call to
+    call. Layout A (every head K4/V4, two waves per SIMD) plans more splits
+    than layout B (one head with 8-bit keys, which runs one wave per SIMD);
+    the calls alternate, with the planner's split size changed in between, and
+    in the default shared-tail order. Every output must match the oracle, and
+    the counters must be zero again at the end."""
+    tokens = 32768
+    lens = [tokens]
+    LA, layA, cA, refA, tA, _, _ = build_case(128, 128, 4, [4] * 8, [4] * 8, lens, seed=61)
+    LB, layB, cB, refB, tB, _, _ = build_case(128, 128, 4, [8, 4, 4, 2, 3, 4, 4, 2], [4, 4, 2, 2, 3, 4, 3, 2],
+                                              lens, seed=62)
+    q = synth.bf16_round(np.random.default_rng(63).standard_normal((1, 32, 128)).astype(np.float32))
+    qt = torch.from_numpy(q).to(T.DEV).bfloat16()
+    segA, segB = [cA.segment(lens)], [cB.segment(lens)]
+    expect = {"A": O.decode_attention([(layA, refA, tA, np.array(lens))], q.astype(np.float64)),
+              "B": O.decode_attention([(layB, refB, tB, np.array(lens))], q.astype(np.float64))}
+    sizes = {"A": kvq.kvq_decode_workspace_bytes(segA, 1), "B": kvq.kvq_decode_workspace_bytes(segB, 1)}
+    assert sizes["A"] != sizes["B"], "the two layouts were meant to get different split plans"
+    monkeypatch.setenv("KVQ_SPLIT_PAGES", "4")
+    sizes["A4"] = kvq.kvq_decode_workspace_bytes(segA, 1)
+    sizes["B4"] = kvq.kvq_decode_workspace_bytes(segB, 1)
+    monkeypatch.delenv("KVQ_SPLIT_PAGES")
+    ws = torch.empty(max(sizes.values()), dtype=torch.uint8, device=T.DEV)
+    kvq.kvq_decode_workspace_init(ws)
+    for which, pages in (("A", None), ("B", None), ("A", None), ("B", "4"), ("A", "4"), ("B", None), ("A", None),
+                         ("B", None)):
+        if pages:
+            monkeypatch.setenv("KVQ_SPLIT_PAGES", pages)
+        else:
+            monkeypatch.delenv("KVQ_SPLIT_PAGES", raising=False)
+        seg = segA if which == "A" else segB
+        out = kvq.kvq_decode_attn(seg, qt, ws=ws).cpu().numpy()
+        err = T.max_rel_err(out, expect[which])
+        assert err <= T.ATTN_TOL, f"layout {which}, split pages {pages}: max relative error {err:.3e}"
+    head = ws[:kvq.KVQ_DECODE_COUNTER_BYTES].view(torch.int32).cpu().numpy()
+    assert np.all(head == 0)
 
 
 @pytest.mark.parametrize("deterministic", [True, False])

@@ -54,6 +54,34 @@ def test_per_channel_key_layout_rules():
     assert st == kvq.KVQ_ERR_ARG
 
 
+def test_append_check_finds_bad_start_positions():
+    """kvq_append_check: the host check of an append's start positions (the device call cannot read them)."""
+    row = kvq.kvq_layout_init(2, 4, 64, 64, [4, 4], [2, 2])
+    kc = kvq.kvq_layout_init(2, 4, 64, 64, [4, 4], [4, 4], key_per_channel=True)
+    kvq.kvq_append_check(row, [0, 5, 17], 3, 2)        # ragged starts are fine for per-token rows
+    kvq.kvq_append_check(kc, [0, 16, 32], 16, 3)       # whole blocks for per-channel keys
+    kvq.kvq_append_check(row, [], 8, 1)                # empty batch
+    bad = [
+        (row, [0, -1], 3, 2, "start_pos -1"),
+        (row, [0, 30], 3, 2, "exceed the table row"),  # 30 + 3 > 32
+        (kc, [0, 8], 16, 4, "not a block boundary"),
+        (kc, [0, 16], 20, 4, "whole blocks"),
+    ]
+    for lay, start, n_new, stride, msg in bad:
+        with pytest.raises(kvq.KvqError) as e:
+            kvq.kvq_append_check(lay, start, n_new, stride)
+        assert e.value.status == kvq.KVQ_ERR_ARG and msg in str(e.value)
+    # the first failing sequence is named
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_append_check(kc, [0, 16, 40, 7], 16, 8)
+    assert "sequence 2" in str(e.value)
+    # a stale layout is refused
+    stale = kvq.kvq_layout_init(2, 4, 64, 64, [4, 4], [2, 2])
+    stale.bits_v[1] = 4
+    with pytest.raises(kvq.KvqError):
+        kvq.kvq_append_check(stale, [0], 1, 1)
+
+
 def test_layout_rejects_bad_arguments():
     with pytest.raises(kvq.KvqError) as e:
         kvq.kvq_layout_init(4, 4, 96, 32, [4] * 4, [4] * 4)
@@ -165,9 +193,12 @@ def test_decode_argument_checks_need_no_device():
     n = ctypes.c_size_t(0)
     assert lib.kvq_decode_workspace_bytes(segs, 1, 16, ctypes.byref(n)) == kvq.KVQ_OK
     assert n.value > 16 * 32 * 130 * 4
-    # partials for every split slot, then two counters per (sequence, KV head, group of 8 splits)
-    per_slot = 16 * 32 * 130 * 4 + 16 * 8 * 2 * 4 // 8
-    assert n.value % per_slot == 0 and (n.value // per_slot) % 8 == 0
+    # the fixed counter area, then partials for every split slot (a multiple of 8 slots)
+    per_slot = 16 * 32 * 130 * 4
+    part = n.value - kvq.KVQ_DECODE_COUNTER_BYTES
+    assert part % per_slot == 0 and (part // per_slot) % 8 == 0
+    # the counters the plan uses (two words per sequence, KV head and group of 8 splits) fit the area
+    assert (part // per_slot) // 8 * 16 * 8 * 2 * 4 <= kvq.KVQ_DECODE_COUNTER_BYTES
     # workspace initialisation: null or misaligned
     assert lib.kvq_decode_workspace_init(None, 64, None) == kvq.KVQ_ERR_ARG
     assert lib.kvq_decode_workspace_init(ctypes.c_void_p(0x4002), 64, None) == kvq.KVQ_ERR_ARG
