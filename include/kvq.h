@@ -14,8 +14,7 @@
  *    caller's stream on every return path.
  *  - No C++ exception crosses this boundary.
  *  - "device" pointers are HIP device memory owned by the caller; the library
- *    never allocates, frees or retains device memory (the one exception is
- *    kvq_decode_attn_noalloc's fixed scratch array, below).
+ *    never allocates, frees or retains device memory.
  *  - Device work is asynchronous on the caller's hipStream_t (0 = the null
  *    stream) with no implicit synchronisation. A launch failure is reported as
  *    KVQ_ERR_DEVICE.
@@ -48,7 +47,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 3
+#define KVQ_ABI_VERSION 4
 #define KVQ_MAX_KV_HEADS 64
 #define KVQ_BLOCK_TOKENS 16
 
@@ -149,10 +148,35 @@ kvq_status kvq_layout_init(kvq_layout* L);
  * Errors: KVQ_ERR_ARG for bad arguments; KVQ_ERR_BUDGET if budget_bits is below
  * n*min(ladder) or above n*max(ladder) (nothing written), or if bits are left
  * over (the allocation found is still written).
+ * Limitation: the rounds only move up, so a budget that some allocation
+ * meets exactly can still end with bits left over when the only steps left
+ * are wider than the remainder: n = 2, ladder {2,3,4,8}, budget 11 ends at
+ * [4,4] with 3 bits left (KVQ_ERR_BUDGET), though [8,3] sums to 11. On
+ * {2,3,4,8} a budget of at most 4 bits per head on average is always spent
+ * exactly: while bits remain, some head is below 4, where one-bit steps
+ * remain.
  */
 kvq_status kvq_plan_bits(int32_t n, const float* w, double alpha, double beta,
                          const int32_t* ladder, int32_t n_ladder, int64_t budget_bits,
                          int32_t* bits_out, int64_t* leftover_out);
+
+/*
+ * Host. kvq_plan_bits over components that each have their own distortion
+ * curve D_i(b) = alpha[i] * beta[i]^-b, sharing one budget [RQ: Methodology 3,
+ * K/V decoupling: the keys and the values of every head are 2N separate
+ * components with their own fitted curves, so one budget decides the split
+ * between keys and values (Key results: 2.85 bits for keys, 2.15 for values
+ * at 2.5 on average)]. Rounds, ties and stopping as in kvq_plan_bits, with
+ * the drop per bit w_i (D_i(b) - D_i(b+)) / (b+ - b) of each component's own
+ * curve. With every alpha[i] and beta[i] equal it returns what kvq_plan_bits
+ * returns.
+ * In:  alpha[n] > 0, beta[n] > 1 (host), the rest as kvq_plan_bits.
+ * Out and errors: as kvq_plan_bits.
+ */
+kvq_status kvq_plan_bits_components(int32_t n, const float* w, const double* alpha,
+                                    const double* beta, const int32_t* ladder, int32_t n_ladder,
+                                    int64_t budget_bits, int32_t* bits_out,
+                                    int64_t* leftover_out);
 
 /*
  * Host. Least-squares fit of the distortion model D(b) = alpha * beta^-b to

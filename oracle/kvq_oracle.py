@@ -550,6 +550,71 @@ def plan_bits_greedy(w, alpha, beta, ladder, budget):
     return [ladder[lv] for lv in level], remaining
 
 
+def plan_bits_greedy_components(w, alpha, beta, ladder, budget):
+    """plan_bits_greedy over components that each have their own distortion
+    curve D_i(b) = alpha_i * beta_i^(-b).
+
+    RateQuant page, Methodology stage 3 ("K/V decoupling"): the keys and the
+    values of every head are separate components (2N of them), each with its
+    own fitted curve, and one budget is shared by all of them, so the split
+    between keys and values is decided by the allocation itself (the page's
+    key result finds 2.85 bits for keys and 2.15 for values at 2.5 on
+    average). The rounds are those of plan_bits_greedy: every component
+    starts at the smallest ladder width, and each round gives one more ladder
+    step to the component with the largest drop per bit,
+    w_i (D_i(b) - D_i(b+)) / (b+ - b), among steps that fit the remaining
+    budget; ties go to the lowest index; it stops when the budget is spent or
+    no step fits. alpha and beta are sequences with one value per component.
+
+    Returns (bits list, leftover bits).
+    """
+    ladder = sorted(int(b) for b in ladder)
+    w = [float(x) for x in w]
+    alpha = [float(a) for a in alpha]
+    beta = [float(b) for b in beta]
+    if not len(w) == len(alpha) == len(beta):
+        raise ValueError("one alpha and one beta per component")
+    level = [0] * len(w)
+    remaining = int(budget) - len(w) * ladder[0]
+    if remaining < 0:
+        raise ValueError("budget below the smallest allocation")
+    while remaining > 0:
+        best, best_gain = -1, -1.0
+        for i, wi in enumerate(w):
+            if level[i] + 1 >= len(ladder):
+                continue
+            b0, b1 = ladder[level[i]], ladder[level[i] + 1]
+            if b1 - b0 > remaining:
+                continue
+            gain = wi * (alpha[i] * beta[i] ** (-b0) - alpha[i] * beta[i] ** (-b1)) / (b1 - b0)
+            if gain > best_gain:
+                best, best_gain = i, gain
+        if best < 0:
+            break
+        remaining -= ladder[level[best] + 1] - ladder[level[best]]
+        level[best] += 1
+    return [ladder[lv] for lv in level], remaining
+
+
+def waterfill_bits_components(w, alpha, beta, total):
+    """Continuous optimum of sum_i w_i alpha_i beta_i^(-b_i) subject to
+    sum_i b_i = total, for components with their own curves (the relaxation
+    of plan_bits_greedy_components).
+
+    Setting the derivative of the Lagrangian to zero gives
+    w_i alpha_i ln(beta_i) beta_i^(-b_i) = lam for every i, so
+    b_i = (ln(w_i alpha_i ln beta_i) - ln lam) / ln beta_i, and the budget fixes
+    ln lam = (sum_i ln(w_i alpha_i ln beta_i) / ln beta_i - total) /
+    sum_i (1 / ln beta_i). With every alpha_i and beta_i equal this is the
+    reverse water-filling of waterfill_bits.
+    """
+    w = np.asarray(w, dtype=np.float64)
+    lb = np.log(np.asarray(beta, dtype=np.float64))
+    c = np.log(w * np.asarray(alpha, dtype=np.float64) * lb)
+    ln_lam = ((c / lb).sum() - float(total)) / (1.0 / lb).sum()
+    return (c - ln_lam) / lb
+
+
 def waterfill_bits(w, beta, b_mean):
     """Continuous optimum b*_i = b_mean + (ln w_i - ln w_bar) / ln beta, w_bar the
     geometric mean of the sensitivities (reverse water-filling)."""

@@ -328,27 +328,41 @@ kvq_status kvq_layout_init(kvq_layout* L) {
   return ok();
 }
 
-kvq_status kvq_plan_bits(int32_t n, const float* w, double alpha, double beta, const int32_t* ladder,
-                         int32_t n_ladder, int64_t budget_bits, int32_t* bits_out, int64_t* leftover_out) {
-  if (n < 1 || !w || !ladder || !bits_out) return fail(KVQ_ERR_ARG, "kvq_plan_bits: null pointer or n < 1");
-  if (n_ladder < 1 || n_ladder > 16) return fail(KVQ_ERR_ARG, "kvq_plan_bits: n_ladder %d out of [1, 16]", n_ladder);
-  if (!(alpha > 0.0) || !(beta > 1.0) || !std::isfinite(alpha) || !std::isfinite(beta))
-    return fail(KVQ_ERR_ARG, "kvq_plan_bits: need alpha > 0 and beta > 1");
+}  // extern "C"
+
+namespace {
+
+// Greedy marginal-gain allocation over components with their own curves
+// D_i(b) = alpha[i * stride] * beta[i * stride]^-b (stride 0: one curve for
+// all), shared by kvq_plan_bits and kvq_plan_bits_components.
+kvq_status plan_bits_greedy(const char* who, int32_t n, const float* w, const double* alpha, const double* beta,
+                            int stride, const int32_t* ladder, int32_t n_ladder, int64_t budget_bits,
+                            int32_t* bits_out, int64_t* leftover_out) {
+  if (n < 1 || !w || !alpha || !beta || !ladder || !bits_out) return fail(KVQ_ERR_ARG, "%s: null pointer or n < 1", who);
+  if (n_ladder < 1 || n_ladder > 16) return fail(KVQ_ERR_ARG, "%s: n_ladder %d out of [1, 16]", who, n_ladder);
+  for (int i = 0; i < (stride ? n : 1); ++i) {
+    const double a = alpha[i * stride], b = beta[i * stride];
+    if (!(a > 0.0) || !(b > 1.0) || !std::isfinite(a) || !std::isfinite(b))
+      return fail(KVQ_ERR_ARG, "%s: need alpha > 0 and beta > 1 (component %d)", who, i);
+  }
   std::vector<int> lad(ladder, ladder + n_ladder);
   std::sort(lad.begin(), lad.end());
   for (int i = 0; i < n_ladder; ++i) {
-    if (lad[i] < 1) return fail(KVQ_ERR_ARG, "kvq_plan_bits: ladder widths must be positive");
-    if (i && lad[i] == lad[i - 1]) return fail(KVQ_ERR_ARG, "kvq_plan_bits: ladder widths must be distinct");
+    if (lad[i] < 1) return fail(KVQ_ERR_ARG, "%s: ladder widths must be positive", who);
+    if (i && lad[i] == lad[i - 1]) return fail(KVQ_ERR_ARG, "%s: ladder widths must be distinct", who);
   }
   for (int i = 0; i < n; ++i)
-    if (!(w[i] > 0.f) || !std::isfinite(w[i])) return fail(KVQ_ERR_ARG, "kvq_plan_bits: w[%d] must be positive", i);
+    if (!(w[i] > 0.f) || !std::isfinite(w[i])) return fail(KVQ_ERR_ARG, "%s: w[%d] must be positive", who, i);
   const int64_t lo = static_cast<int64_t>(n) * lad.front(), hi = static_cast<int64_t>(n) * lad.back();
   if (budget_bits < lo || budget_bits > hi)
-    return fail(KVQ_ERR_BUDGET, "kvq_plan_bits: budget %lld outside [%lld, %lld]", static_cast<long long>(budget_bits),
+    return fail(KVQ_ERR_BUDGET, "%s: budget %lld outside [%lld, %lld]", who, static_cast<long long>(budget_bits),
                 static_cast<long long>(lo), static_cast<long long>(hi));
-  // D(b) at every ladder rung, in double.
-  std::vector<double> dist(n_ladder);
-  for (int k = 0; k < n_ladder; ++k) dist[k] = alpha * std::pow(beta, -static_cast<double>(lad[k]));
+  // D_i(b) at every ladder rung, in double.
+  const int n_curves = stride ? n : 1;
+  std::vector<double> dist(static_cast<size_t>(n_curves) * n_ladder);
+  for (int c = 0; c < n_curves; ++c)
+    for (int k = 0; k < n_ladder; ++k)
+      dist[static_cast<size_t>(c) * n_ladder + k] = alpha[c * stride] * std::pow(beta[c * stride], -static_cast<double>(lad[k]));
   std::vector<int> level(n, 0);
   int64_t remaining = budget_bits - lo;
   while (remaining > 0) {
@@ -359,7 +373,8 @@ kvq_status kvq_plan_bits(int32_t n, const float* w, double alpha, double beta, c
       if (lv + 1 >= n_ladder) continue;
       const int step = lad[lv + 1] - lad[lv];
       if (step > remaining) continue;
-      const double gain = static_cast<double>(w[i]) * (dist[lv] - dist[lv + 1]) / step;
+      const double* d = &dist[static_cast<size_t>(stride ? i : 0) * n_ladder];
+      const double gain = static_cast<double>(w[i]) * (d[lv] - d[lv + 1]) / step;
       if (gain > best_gain) {
         best = i;
         best_gain = gain;
@@ -372,9 +387,26 @@ kvq_status kvq_plan_bits(int32_t n, const float* w, double alpha, double beta, c
   for (int i = 0; i < n; ++i) bits_out[i] = lad[level[i]];
   if (leftover_out) *leftover_out = remaining;
   if (remaining != 0)
-    return fail(KVQ_ERR_BUDGET, "kvq_plan_bits: %lld bits could not be placed on the ladder",
+    return fail(KVQ_ERR_BUDGET, "%s: %lld bits could not be placed on the ladder", who,
                 static_cast<long long>(remaining));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_plan_bits(int32_t n, const float* w, double alpha, double beta, const int32_t* ladder,
+                         int32_t n_ladder, int64_t budget_bits, int32_t* bits_out, int64_t* leftover_out) {
+  return plan_bits_greedy("kvq_plan_bits", n, w, &alpha, &beta, 0, ladder, n_ladder, budget_bits, bits_out,
+                          leftover_out);
+}
+
+kvq_status kvq_plan_bits_components(int32_t n, const float* w, const double* alpha, const double* beta,
+                                    const int32_t* ladder, int32_t n_ladder, int64_t budget_bits, int32_t* bits_out,
+                                    int64_t* leftover_out) {
+  return plan_bits_greedy("kvq_plan_bits_components", n, w, alpha, beta, 1, ladder, n_ladder, budget_bits, bits_out,
+                          leftover_out);
 }
 
 kvq_status kvq_fit_distortion(int32_t n, const int32_t* widths, const double* mse, double* alpha_out,
@@ -820,8 +852,10 @@ kvq_status kvq_decode_workspace_init(void* ws, size_t ws_bytes, kvq_stream strea
                        "kvq_decode_workspace_init launch");
 }
 
-kvq_status kvq_decode_partial(const kvq_segment* segs, int32_t n_segs, int32_t batch, const void* q,
-                              kvq_dtype q_dtype, void* ws, size_t ws_bytes, kvq_stream stream) {
+// The partial launches of one decode call. serial: every launch goes on the
+// caller's stream, one after another (no side streams are created or used).
+static kvq_status decode_partial_impl(const kvq_segment* segs, int32_t n_segs, int32_t batch, const void* q,
+                                      kvq_dtype q_dtype, void* ws, size_t ws_bytes, kvq_stream stream, bool serial) {
   kvq_status st = check_segments(segs, n_segs, batch, "kvq_decode_partial");
   if (st != KVQ_OK) return st;
   if (q_dtype != KVQ_F32 && q_dtype != KVQ_BF16) return fail(KVQ_ERR_ARG, "kvq_decode_partial: bad q dtype");
@@ -916,6 +950,13 @@ kvq_status kvq_decode_partial(const kvq_segment* segs, int32_t n_segs, int32_t b
                    : kvq::launch_decode_partial(l.a, l.kbits, l.vbits, l.d, l.n_splits, batch, st);
   };
   if (launches.size() == 1) return device_status(launch(launches[0], s), "kvq_decode_partial launch");
+  if (serial) {
+    for (const Launch& l : launches) {
+      const hipError_t e = launch(l, s);
+      if (e != hipSuccess) return device_status(e, "kvq_decode_partial launch");
+    }
+    return ok();
+  }
   // Several launches (segments, and width groups that cannot share a launch)
   // run concurrently: the largest on the caller's stream, which starts it
   // first, the others on side streams forked from it and joined back before
@@ -956,6 +997,11 @@ kvq_status kvq_decode_partial(const kvq_segment* segs, int32_t n_segs, int32_t b
     }
   }
   return device_status(first, what);
+}
+
+kvq_status kvq_decode_partial(const kvq_segment* segs, int32_t n_segs, int32_t batch, const void* q,
+                              kvq_dtype q_dtype, void* ws, size_t ws_bytes, kvq_stream stream) {
+  return decode_partial_impl(segs, n_segs, batch, q, q_dtype, ws, ws_bytes, stream, false);
 }
 
 kvq_status kvq_decode_merge(const kvq_segment* segs, int32_t n_segs, int32_t batch, float* out, void* ws,

@@ -14,7 +14,7 @@ import numpy as np
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkvq.so")
 
-KVQ_ABI_VERSION = 3
+KVQ_ABI_VERSION = 4
 KVQ_MAX_KV_HEADS = 64
 KVQ_BLOCK_TOKENS = 16
 
@@ -27,7 +27,7 @@ EXPORTED = [
     "kvq_decode_workspace_bytes", "kvq_decode_workspace_init", "kvq_decode_attn", "kvq_decode_partial",
     "kvq_decode_merge", "kvq_fit_distortion", "kvq_amgm_ratio", "kvq_quant_mse",
     "kvq_logquant_dynamic_classes", "kvq_logquant_init", "kvq_logquant_advance", "kvq_logquant_requant",
-    "kvq_append_check",
+    "kvq_append_check", "kvq_plan_bits_components",
 ]
 
 KVQ_DECODE_COUNTER_BYTES = 65536
@@ -102,6 +102,7 @@ def lib():
     L.kvq_last_error.restype = ctypes.c_char_p
     L.kvq_layout_init.argtypes = [ctypes.POINTER(KvqLayout)]
     L.kvq_plan_bits.argtypes = [i32, vp, ctypes.c_double, ctypes.c_double, vp, i32, i64, vp, vp]
+    L.kvq_plan_bits_components.argtypes = [i32, vp, vp, vp, vp, i32, i64, vp, vp]
     L.kvq_logquant_classes.argtypes = [i32, i32, vp]
     L.kvq_fit_distortion.argtypes = [i32, vp, vp, vp, vp, vp]
     L.kvq_amgm_ratio.argtypes = [i32, vp, vp]
@@ -205,6 +206,23 @@ def kvq_plan_bits(w, alpha, beta, ladder, budget_bits, allow_leftover=False):
                              int(ladder.shape[0]), int(budget_bits), _np_ptr(out), ctypes.byref(left))
     if not (allow_leftover and st == KVQ_ERR_BUDGET and left.value != 0):
         _check(st, "kvq_plan_bits")
+    return out, left.value
+
+
+def kvq_plan_bits_components(w, alpha, beta, ladder, budget_bits, allow_leftover=False):
+    """Greedy allocation over components with their own curves alpha[i] * beta[i]^-b (e.g. the keys and
+    values of every head as 2N components sharing one budget). Returns (bits int32 array, leftover)."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    alpha = np.ascontiguousarray(np.broadcast_to(np.asarray(alpha, np.float64), w.shape))
+    beta = np.ascontiguousarray(np.broadcast_to(np.asarray(beta, np.float64), w.shape))
+    ladder = np.ascontiguousarray(ladder, dtype=np.int32)
+    out = np.zeros(w.shape[0], dtype=np.int32)
+    left = ctypes.c_int64(0)
+    st = lib().kvq_plan_bits_components(int(w.shape[0]), _np_ptr(w), _np_ptr(alpha), _np_ptr(beta),
+                                        _np_ptr(ladder), int(ladder.shape[0]), int(budget_bits), _np_ptr(out),
+                                        ctypes.byref(left))
+    if not (allow_leftover and st == KVQ_ERR_BUDGET and left.value != 0):
+        _check(st, "kvq_plan_bits_components")
     return out, left.value
 
 

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     for name in sorted(declared):
         assert hasattr(lib, name), name
     assert declared == set(kvq.EXPORTED)
-    assert kvq.kvq_abi_version() == 3
+    assert kvq.kvq_abi_version() == kvq.KVQ_ABI_VERSION == 4
     assert kvq.kvq_status_str(kvq.KVQ_ERR_BUDGET) == "KVQ_ERR_BUDGET"
 
 
@@ -118,6 +118,65 @@ def test_plan_bits_random_cases_match_oracle():
         bits, left = kvq.kvq_plan_bits(w, 0.7, beta, ladder, budget, allow_leftover=True)
         ref, ref_left = O.plan_bits_greedy(w.astype(np.float64), 0.7, beta, ladder, budget)
         assert bits.tolist() == ref and left == ref_left
+
+
+def test_plan_bits_components_matches_oracle():
+    # the mixed-precision draws as 512 components: 256 key curves (beta 3.6) and 256 value curves (beta 5.3)
+    w = np.concatenate([synth.sensitivities(32, 8, seed=3).ravel(), synth.sensitivities(32, 8, seed=33).ravel()])
+    w = w.astype(np.float32)
+    beta = np.array([3.6] * 256 + [5.3] * 256)
+    bits, left = kvq.kvq_plan_bits_components(w, 1.0, beta, [2, 3, 4, 8], 3 * 512)
+    ref, ref_left = O.plan_bits_greedy_components(w.astype(np.float64), [1.0] * 512, beta, [2, 3, 4, 8], 3 * 512)
+    assert bits.tolist() == ref and left == ref_left == 0
+    rng = np.random.default_rng(31)
+    for _ in range(50):
+        n = int(rng.integers(1, 40))
+        ladder = sorted(rng.choice(np.arange(1, 12), size=int(rng.integers(1, 5)), replace=False).tolist())
+        w = rng.lognormal(0, 1.5, size=n).astype(np.float32)
+        alpha = rng.uniform(0.3, 3.0, size=n)
+        beta = rng.uniform(1.5, 6.0, size=n)
+        budget = int(rng.integers(n * ladder[0], n * ladder[-1] + 1))
+        bits, left = kvq.kvq_plan_bits_components(w, alpha, beta, ladder, budget, allow_leftover=True)
+        ref, ref_left = O.plan_bits_greedy_components(w.astype(np.float64), alpha, beta, ladder, budget)
+        assert bits.tolist() == ref and left == ref_left
+    # one curve for every component: exactly kvq_plan_bits
+    w = synth.sensitivities(32, 8, seed=4).ravel().astype(np.float32)
+    assert (kvq.kvq_plan_bits_components(w, 1.0, 3.6, [2, 3, 4, 8], 768)[0].tolist()
+            == kvq.kvq_plan_bits(w, 1.0, 3.6, [2, 3, 4, 8], 768)[0].tolist())
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_plan_bits_components(np.ones(3, np.float32), [1.0, 1.0, 1.0], [3.6, 0.9, 5.3], [2, 3], 7)
+    assert e.value.status == kvq.KVQ_ERR_ARG
+
+
+def test_joint_key_value_budget_splits_unevenly():
+    """RateQuant page, Methodology 3 (K/V decoupling) and Key results (2.85 / 2.15 bits at 2.5): one budget
+    over the 2N key and value components of the mixed-precision draws (keys beta 3.6, values beta 5.3,
+    average 3 bits) gives the keys more bits than the values, where separate budgets give each 3."""
+    wk = synth.sensitivities(32, 8, seed=3).ravel().astype(np.float32)
+    wv = synth.sensitivities(32, 8, seed=33).ravel().astype(np.float32)
+    w = np.concatenate([wk, wv])
+    alpha = np.ones(512)
+    beta = np.array([3.6] * 256 + [5.3] * 256)
+    joint, left = kvq.kvq_plan_bits_components(w, alpha, beta, [2, 3, 4, 8], 3 * 512)
+    assert left == 0 and int(joint.sum()) == 1536
+    k_avg, v_avg = joint[:256].mean(), joint[256:].mean()
+    assert k_avg > 3.2 and v_avg < 2.8 and abs(k_avg + v_avg - 6.0) < 1e-12
+    sep_k, _ = kvq.kvq_plan_bits(wk, 1.0, 3.6, [2, 3, 4, 8], 768)
+    sep_v, _ = kvq.kvq_plan_bits(wv, 1.0, 5.3, [2, 3, 4, 8], 768)
+    obj = lambda bits: float(np.sum(w * alpha * beta ** -bits.astype(np.float64)))
+    assert obj(joint) < obj(np.concatenate([sep_k, sep_v]))
+
+
+def test_greedy_leftover_limitation_is_as_documented():
+    # n = 2, ladder {2,3,4,8}, budget 11: the rounds end at [4,4] with 3 bits left (KVQ_ERR_BUDGET),
+    # on both sides, though [8,3] would spend it
+    w = np.ones(2, np.float32)
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_plan_bits(w, 1.0, 3.6, [2, 3, 4, 8], 11)
+    assert e.value.status == kvq.KVQ_ERR_BUDGET
+    bits, left = kvq.kvq_plan_bits(w, 1.0, 3.6, [2, 3, 4, 8], 11, allow_leftover=True)
+    assert bits.tolist() == [4, 4] and left == 3
+    assert O.plan_bits_greedy([1.0, 1.0], 1.0, 3.6, [2, 3, 4, 8], 11) == ([4, 4], 3)
 
 
 def test_plan_bits_errors():

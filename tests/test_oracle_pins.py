@@ -425,6 +425,73 @@ def test_greedy_tracks_waterfilling_on_a_fine_ladder():
     assert left == 0 and np.abs(np.array(units) / 64 - star).max() <= 1 / 64 + 1e-12
 
 
+def test_greedy_components_hand_example():
+    g = GOLDEN["greedy_components"]
+    bits, left = O.plan_bits_greedy_components(g["w"], g["alpha"], g["beta"], g["ladder"], g["budget"])
+    assert bits == g["bits"] and left == g["leftover"]
+
+
+def test_greedy_components_with_equal_curves_is_the_plain_greedy():
+    rng = np.random.default_rng(21)
+    for _ in range(10):
+        n = int(rng.integers(1, 30))
+        w = rng.lognormal(0, 1, size=n)
+        ladder = [2, 3, 4, 8]
+        budget = int(rng.integers(2 * n, 8 * n + 1))
+        beta = float(rng.uniform(1.5, 6))
+        assert (O.plan_bits_greedy_components(w, [0.8] * n, [beta] * n, ladder, budget)
+                == O.plan_bits_greedy(w, 0.8, beta, ladder, budget))
+
+
+def test_greedy_components_is_optimal_on_unit_ladders_by_brute_force():
+    # Each component's drops w_i alpha_i beta_i^-b (1 - 1/beta_i) fall with b, so
+    # on unit steps the greedy is optimal; exhaustive search over every
+    # allocation of five components with different curves.
+    rng = np.random.default_rng(22)
+    ladder = [1, 2, 3, 4, 5, 6]
+    for _ in range(6):
+        w = rng.lognormal(0, 1, size=5)
+        alpha = rng.uniform(0.5, 2.0, size=5)
+        beta = rng.uniform(2.0, 6.0, size=5)
+        budget = int(rng.integers(8, 27))
+        bits, left = O.plan_bits_greedy_components(w, alpha, beta, ladder, budget)
+        obj = float(np.sum(w * alpha * beta ** -np.asarray(bits, float)))
+        best = min(float(np.sum(w * alpha * beta ** -np.asarray(c, float)))
+                   for c in itertools.product(ladder, repeat=5) if sum(c) == budget)
+        assert left == 0 and sum(bits) == budget and abs(obj - best) <= 1e-12 * best
+
+
+def test_greedy_components_tracks_the_closed_form_on_a_fine_ladder():
+    # Keys (beta 3.6) and values (beta 5.3) of 8 heads as 16 components sharing
+    # one budget of 3 bits each, on a ladder of 1/64-bit steps:
+    # D_i(u / 64) = alpha_i (beta_i^(1/64))^-u.
+    rng = np.random.default_rng(23)
+    w = rng.lognormal(0, 0.6, size=16)
+    alpha = np.ones(16)
+    beta = np.array([3.6] * 8 + [5.3] * 8)
+    star = O.waterfill_bits_components(w, alpha, beta, 3.0 * 16)
+    assert abs(star.sum() - 48.0) < 1e-9 and star.min() > 0.5 and star.max() < 7.5  # no clamping
+    units, left = O.plan_bits_greedy_components(w, alpha, beta ** (1 / 64), list(range(0, 64 * 8 + 1)), 64 * 48)
+    assert left == 0 and sum(units) == 64 * 48
+    assert np.abs(np.array(units) / 64 - star).max() <= 2 / 64
+    # keys get more bits than values (their error falls more slowly per bit)
+    assert star[:8].mean() > star[8:].mean()
+
+
+def test_components_closed_form_is_stationary_and_reduces_to_waterfilling():
+    rng = np.random.default_rng(24)
+    w = rng.lognormal(0, 1, size=12)
+    alpha = rng.uniform(0.5, 2, size=12)
+    beta = rng.uniform(2, 6, size=12)
+    star = O.waterfill_bits_components(w, alpha, beta, 40.0)
+    # equal marginal distortion drop w_i alpha_i ln(beta_i) beta_i^-b_i across components
+    marg = w * alpha * np.log(beta) * beta ** -star
+    assert abs(star.sum() - 40.0) < 1e-9 and np.ptp(marg) <= 1e-12 * marg.max()
+    # one common curve: the reverse water-filling of waterfill_bits
+    same = O.waterfill_bits_components(w, np.ones(12), np.full(12, 4.2), 3.0 * 12)
+    assert np.abs(same - O.waterfill_bits(w, 4.2, 3.0)).max() < 1e-12
+
+
 def test_waterfilling_amgm_identity():
     # sum w D(b_mean) / sum w D(b*) = AM(w) / GM(w) at the continuous optimum.
     rng = np.random.default_rng(19)
