@@ -14,7 +14,8 @@
  *    caller's stream on every return path.
  *  - No C++ exception crosses this boundary.
  *  - "device" pointers are HIP device memory owned by the caller; the library
- *    never allocates, frees or retains device memory.
+ *    never allocates, frees or retains device memory (the one exception is
+ *    kvq_decode_attn_noalloc's fixed scratch array, below).
  *  - Device work is asynchronous on the caller's hipStream_t (0 = the null
  *    stream) with no implicit synchronisation. A launch failure is reported as
  *    KVQ_ERR_DEVICE.
@@ -467,6 +468,36 @@ kvq_status kvq_decode_partial(const kvq_segment* segs, int32_t n_segs, int32_t b
                               void* ws, size_t ws_bytes, kvq_stream stream);
 kvq_status kvq_decode_merge(const kvq_segment* segs, int32_t n_segs, int32_t batch,
                             float* out, void* ws, size_t ws_bytes, kvq_stream stream);
+
+/*
+ * Size of kvq_decode_attn_noalloc's fixed scratch array, per GPU: the
+ * counter area (KVQ_DECODE_COUNTER_BYTES) and the split-K partials.
+ */
+#define KVQ_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * Device, async. kvq_decode_attn without a caller workspace, for callers that
+ * cannot allocate device memory or hand one in: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. Computes exactly what
+ * kvq_decode_attn computes (same kernels), with the workspace in a fixed
+ * device array of KVQ_NOALLOC_SCRATCH_BYTES that the library holds per GPU
+ * until the process ends. No hipMalloc, hipFree, stream creation or other
+ * allocating call is made: the first call on a device looks up the array's
+ * address and clears its counter area with a kernel on `stream`. All of a
+ * call's partial launches go on `stream`, one after another (no side
+ * streams).
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (on different streams without ordering, or from several threads) race
+ * and give wrong results. Each completed call leaves the counters zero for
+ * the next; after a call that failed on the device the counters may not be
+ * zero, and the array cannot be reset.
+ * In/Out: as kvq_decode_attn.
+ * Errors: as kvq_decode_attn; KVQ_ERR_WORKSPACE when the call's workspace
+ * (kvq_decode_workspace_bytes) exceeds KVQ_NOALLOC_SCRATCH_BYTES.
+ */
+kvq_status kvq_decode_attn_noalloc(const kvq_segment* segs, int32_t n_segs, int32_t batch,
+                                   const void* q, kvq_dtype q_dtype, float* out,
+                                   kvq_stream stream);
 
 #ifdef __cplusplus
 }

@@ -1038,3 +1038,68 @@ kvq_status kvq_decode_attn(const kvq_segment* segs, int32_t n_segs, int32_t batc
 }
 
 }  // extern "C"
+
+namespace {
+
+// Scratch memory of kvq_decode_attn_noalloc: the decode workspace (counter
+// area, then partials) in a fixed device array, one copy per GPU the library
+// runs on, held until the process ends. Host code never uses the array's name
+// as an address (on the host it is only a stand-in): the device address comes
+// from hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kNoallocScratchBytes = KVQ_NOALLOC_SCRATCH_BYTES;
+static_assert(kNoallocScratchBytes % 256 == 0 && kNoallocScratchBytes > kCounterBytes, "scratch size");
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address; on the first call for a device its
+// counter area is cleared on `s` (a kernel, not a memset node), which every
+// later call on that device's streams follows in stream order or by the
+// caller's synchronisation.
+hipError_t noalloc_scratch(void** out, hipStream_t s) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if ((e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    if ((e = kvq::launch_zero_words(static_cast<uint32_t*>(ptr), kCounterBytes / 4, s)) != hipSuccess) return e;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_decode_attn_noalloc(const kvq_segment* segs, int32_t n_segs, int32_t batch, const void* q,
+                                   kvq_dtype q_dtype, float* out, kvq_stream stream) {
+  const char* who = "kvq_decode_attn_noalloc";
+  kvq_status st = check_segments(segs, n_segs, batch, who);
+  if (st != KVQ_OK) return st;
+  if (q_dtype != KVQ_F32 && q_dtype != KVQ_BF16) return fail(KVQ_ERR_ARG, "%s: bad q dtype", who);
+  if (batch == 0) return ok();
+  if (!q || !out) return fail(KVQ_ERR_ARG, "%s: null q or output", who);
+  const kvq_layout& L0 = *segs[0].layout;
+  const size_t need =
+      workspace_bytes(batch, L0.num_kv_heads * L0.group, L0.head_dim, total_slots(segs, n_segs, batch, nullptr));
+  if (need > kNoallocScratchBytes)
+    return fail(KVQ_ERR_WORKSPACE, "%s: this call needs %zu bytes of scratch, more than the fixed %zu", who, need,
+                kNoallocScratchBytes);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  const hipError_t e = noalloc_scratch(&ws, s);
+  if (e != hipSuccess) return device_status(e, "kvq_decode_attn_noalloc scratch");
+  st = decode_partial_impl(segs, n_segs, batch, q, q_dtype, ws, kNoallocScratchBytes, stream, true);
+  if (st != KVQ_OK) return st;
+  return kvq_decode_merge(segs, n_segs, batch, out, ws, kNoallocScratchBytes, stream);
+}
+
+}  // extern "C"

@@ -27,10 +27,11 @@ EXPORTED = [
     "kvq_decode_workspace_bytes", "kvq_decode_workspace_init", "kvq_decode_attn", "kvq_decode_partial",
     "kvq_decode_merge", "kvq_fit_distortion", "kvq_amgm_ratio", "kvq_quant_mse",
     "kvq_logquant_dynamic_classes", "kvq_logquant_init", "kvq_logquant_advance", "kvq_logquant_requant",
-    "kvq_append_check", "kvq_plan_bits_components",
+    "kvq_append_check", "kvq_decode_attn_noalloc", "kvq_plan_bits_components",
 ]
 
 KVQ_DECODE_COUNTER_BYTES = 65536
+KVQ_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class KvqError(RuntimeError):
@@ -122,6 +123,7 @@ def lib():
     L.kvq_decode_attn.argtypes = [ctypes.POINTER(KvqSegment), i32, i32, vp, ctypes.c_int, vp, vp, sz, vp]
     L.kvq_decode_partial.argtypes = [ctypes.POINTER(KvqSegment), i32, i32, vp, ctypes.c_int, vp, sz, vp]
     L.kvq_decode_merge.argtypes = [ctypes.POINTER(KvqSegment), i32, i32, vp, vp, sz, vp]
+    L.kvq_decode_attn_noalloc.argtypes = [ctypes.POINTER(KvqSegment), i32, i32, vp, ctypes.c_int, vp, vp]
     for name in EXPORTED:
         if name not in ("kvq_abi_version", "kvq_status_str", "kvq_last_error"):
             getattr(L, name).restype = ctypes.c_int
@@ -459,6 +461,18 @@ def kvq_decode_attn(segments, q, out=None, ws=None, stream=None):
                                _dev_ptr(out, (torch.float32,), "out"), _dev_ptr(ws, (torch.uint8,), "ws"),
                                ws.numel(), _stream(stream))
     _check(st, "kvq_decode_attn")
+    return out
+
+
+def kvq_decode_attn_noalloc(segments, q, out, stream=None):
+    """kvq_decode_attn with the library's fixed per-GPU scratch array instead of a workspace; `out`
+    (fp32 [batch, Hq, d]) is written in place."""
+    import torch
+    dt = KVQ_BF16 if q.dtype == torch.bfloat16 else KVQ_F32
+    st = lib().kvq_decode_attn_noalloc(_segments(segments), len(segments), int(q.shape[0]),
+                                       _dev_ptr(q, (torch.float32, torch.bfloat16), "q"), dt,
+                                       _dev_ptr(out, (torch.float32,), "out"), _stream(stream))
+    _check(st, "kvq_decode_attn_noalloc")
     return out
 
 
