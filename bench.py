@@ -136,8 +136,30 @@ def bytes_per_layer():
     return cache + table + q
 
 
-def cpu_baseline(units, seed=77):
-    """Time the CPU oracle on `units` (sequence, KV head, layer) units of one step."""
+def host_cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_workers():
+    """Worker processes for the oracle: the host cores this process may use, at most 16 (one GPU's
+    share of a shared box)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _oracle_worker(units, barrier, out_q):
+    """One host process: build its units' caches (untimed), wait for every worker, then time the
+    append of one token + decode over T tokens for each of its units."""
     from threadpoolctl import threadpool_limits
 
     from oracle import kvq_oracle as O
@@ -146,22 +168,51 @@ def cpu_baseline(units, seed=77):
     lay = O.Layout(1, G, D, HAD, [BITS_K], [BITS_V])
     nb = T // 16
     table = np.arange(nb, dtype=np.int32)[None]
-    elapsed = 0.0
     with threadpool_limits(limits=1):
-        for u in range(units):
-            k, v, q = synth.llama_layer_np(seed=seed + u, batch=1, tokens=T, hkv=1)
+        work = []
+        for u in units:
+            k, v, q = synth.llama_layer_np(seed=77 + u, batch=1, tokens=T, hkv=1)
             pool = np.zeros((nb, lay.block_bytes), np.uint8)
             O.quantize_append(lay, pool, table, np.array([0]), k[:, :T - 1], v[:, :T - 1])  # prefill, untimed
-            t0 = time.perf_counter()
-            O.quantize_append(lay, pool, table, np.array([T - 1]), k[:, T - 1:], v[:, T - 1:])
-            O.decode_attention([(lay, pool, table, np.array([T]))], q[:, :G].astype(np.float64))
-            elapsed += time.perf_counter() - t0
-    per_unit = elapsed / units
-    step_s = per_unit * B * HKV * LAYERS
-    return {"value": B / step_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{units} (sequence, kv head, layer) units of the step (append 1 token + decode over "
-                      f"{T} tokens each, {elapsed:.1f} s on 1 host thread), scaled x{B * HKV * LAYERS // units} "
-                      f"to the full step ({B * HKV * LAYERS} units)"}
+            work.append((pool, k[:, T - 1:], v[:, T - 1:], q[:, :G].astype(np.float64)))
+        barrier.wait()
+        t0 = time.time()
+        for pool, nk, nv, q in work:
+            O.quantize_append(lay, pool, table, np.array([T - 1]), nk, nv)
+            O.decode_attention([(lay, pool, table, np.array([T]))], q)
+        t1 = time.time()
+    out_q.put((t0, t1, len(units)))
+
+
+def cpu_baseline(units_per_worker):
+    """Time the CPU oracle on a sample of (sequence, KV head, layer) units of one step, on every host core
+    this process may use (one process per core, one thread each), and scale it to the full step.
+
+    Runs before the GPU is touched; the workers are fresh interpreters (spawn) that load only numpy and
+    the oracle."""
+    import multiprocessing as mp
+
+    workers = host_workers()
+    ctx = mp.get_context("spawn")
+    barrier = ctx.Barrier(workers)
+    out_q = ctx.Queue()
+    procs = [ctx.Process(target=_oracle_worker,
+                         args=(list(range(w * units_per_worker, (w + 1) * units_per_worker)), barrier, out_q))
+             for w in range(workers)]
+    for p in procs:
+        p.start()
+    res = [out_q.get() for _ in procs]
+    for p in procs:
+        p.join()
+    wall = max(r[1] for r in res) - min(r[0] for r in res)
+    units = sum(r[2] for r in res)
+    step_units = B * HKV * LAYERS
+    step_s = wall / units * step_units
+    return {"value": B / step_s, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "cpu_model": host_cpu_model(),
+            "sample": f"{units} (sequence, kv head, layer) units of the step (append 1 token + decode over {T} "
+                      f"tokens each) on {workers} host processes of one thread, {wall:.1f} s wall, scaled "
+                      f"x{step_units / units:.1f} to the full step ({step_units} units)"}
 
 
 def decode_bytes(batch, tokens, bits_k, bits_v, d=D, meta=8):
@@ -352,6 +403,7 @@ def run_decode(args, torch, dev, kvq):
 
     part_ms = [a.elapsed_time(b) for a, b in zip(ev_a, ev_b)]
     part_us = 1e3 * float(np.mean(part_ms))
+    p10, p50, p90 = (1e3 * float(x) for x in np.percentile(part_ms, [10, 50, 90]))
     ms_per_step = 1e3 * elapsed / args.steps
     achieved = layer_bytes / (part_us * 1e-6) / 1e9
     extra = {}
@@ -369,7 +421,9 @@ def run_decode(args, torch, dev, kvq):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic() if args.workload == "llama32k" else None,
-                     "kernel": kernel, "avg_us": round(part_us, 3), "bytes_per_launch": int(layer_bytes)},
+                     "kernel": kernel, "avg_us": round(part_us, 3), "median_us": round(p50, 3),
+                     "p10_us": round(p10, 3), "p90_us": round(p90, 3), "launches": len(part_ms),
+                     "bytes_per_launch": int(layer_bytes)},
         "step_hbm_gbs": round(layer_bytes * args.layers / (ms_per_step * 1e-3) / 1e9, 1),
     }
 
@@ -645,7 +699,8 @@ def main():
                     help="decode workloads: after the eager timed steps (which give the partial kernel's "
                          "per-launch times), capture the same steps as one HIP graph and take the step rate "
                          "from its replay (default on)")
-    ap.add_argument("--cpu-units", type=int, default=48, help="oracle units timed for cpu_baseline (0: skip)")
+    ap.add_argument("--cpu-units", type=int, default=6,
+                    help="oracle units per host worker timed for cpu_baseline (0: skip)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run one 1 GiB device copy (for scaling HBM counters)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -664,6 +719,11 @@ def main():
               "(this build runs on a single MI355X)", file=sys.stderr)
         sys.exit(2)
 
+    # the oracle's CPU baseline first, before anything touches the GPU (its workers are spawned processes)
+    cpu = None
+    if args.cpu_units > 0 and args.workload == "llama32k":
+        cpu = cpu_baseline(args.cpu_units)
+
     import torch
 
     from quantized_decode_attention_03_amd import kvq
@@ -681,15 +741,27 @@ def main():
     else:
         res = run_decode(args, torch, dev, kvq)
 
+    # streaming ceiling on this machine: a 1 GiB device-to-device copy (1 GiB read + 1 GiB written), the median
+    # of 10 timed copies; --copy-calib adds one untimed copy that the counter passes scale HBM bytes by
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
     if args.copy_calib:
-        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
-
-    cpu = None
-    if args.cpu_units > 0 and args.workload == "llama32k":
-        cpu = cpu_baseline(args.cpu_units)
+    copy_ms = []
+    for _ in range(10):
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        dst.copy_(src)
+        c1.record()
+        torch.cuda.synchronize()
+        copy_ms.append(c0.elapsed_time(c1))
+    copy_gbs = 2 * COPY_BYTES / (float(np.median(copy_ms)) * 1e-3) / 1e9
+    del src, dst
+    res.setdefault("roofline", {})["measured_copy_gbs"] = round(copy_gbs, 1)
+    res["roofline"]["frac_of_copy"] = round(res["roofline"].get("achieved", 0.0) / copy_gbs, 4)
 
     line = {
         "metric": res.pop("metric", "quantized-KV decode attention: tokens/s and HBM GB/s (% of peak) at 32k ctx"),
@@ -703,6 +775,10 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": res.pop("dtype", "f16"),
+        "dtype_detail": res.pop("dtype_detail", "int4 K/V codes with fp32 {scale, min} per row, bf16 queries and new "
+                                                "rows; scores and PV on fp16 MFMA operands (codes exact, query and "
+                                                "weights as fp16 hi+lo pairs, ~22 bits), fp32 accumulation and "
+                                                "softmax"),
         "data": "synthetic",
         "config": res.pop("config"),
         "roofline": res.pop("roofline"),

@@ -82,8 +82,11 @@ def decode_units(L, pool, table_t, batch, tokens, q):
     return kvq.kvq_decode_attn([kvq.Segment(L, pool, table_t, lens, tokens)], q).cpu().numpy()
 
 
-def run_units(L, pool, table, out, k, v, q, units, seed):
-    """Oracle comparison for the sampled units; returns the code statistics."""
+def run_units(L, pool, table, out, k, v, q, units, seed, all_rows=()):
+    """Oracle comparison for the sampled units; returns the code statistics.
+
+    Units listed in all_rows have every stored row compared, the others a
+    sample of ROW_SAMPLE rows."""
     g, n = L.group, L.had_block
     rng = np.random.default_rng(seed)
     stats = T.CodeStats()
@@ -97,21 +100,32 @@ def run_units(L, pool, table, out, k, v, q, units, seed):
                                     q_rows[None].astype(np.float64))[0]
         err = T.max_rel_err(out[b, h * g:(h + 1) * g], expect)
         assert err <= T.ATTN_TOL, f"unit (b={b}, h={h}): max relative error {err:.3e}"
-        positions = np.sort(rng.choice(tokens, size=min(ROW_SAMPLE, tokens), replace=False))
+        if (b, h) in all_rows:
+            positions = np.arange(tokens)
+        else:
+            positions = np.sort(rng.choice(tokens, size=min(ROW_SAMPLE, tokens), replace=False))
         check_unit_rows(L, pool, table, b, h, lay, ref_pool, ref_table, k_rows, v_rows, positions, stats)
     assert stats.rate <= TIE_RATE
     return stats
 
 
 def test_llama_32k_decode_full_size():
-    """Batch 16, 32768 tokens, 8 KV heads x 4, head_dim 128, K4/V4, Hadamard 128 (one layer)."""
+    """Batch 16, 32768 tokens, 8 KV heads x 4, head_dim 128, K4/V4, Hadamard 128 (one layer).
+
+    Compared against the oracle: all 8 KV heads of sequences 0 and 11, and one
+    head of every other sequence (a different head each, so every head index
+    and every sequence is covered: 30 of the 128 units, over all XCDs and
+    sharing groups of the launch). Units of sequence 0 have every stored row
+    compared."""
     batch, tokens, hkv, group, d = 16, 32768, 8, 4, 128
     L = kvq.kvq_layout_init(hkv, group, d, 128, [4] * hkv, [4] * hkv)
     k, v, q = synth.llama_layer_torch(2000, batch, tokens, hkv, group, d, device=T.DEV)
     pool, table, table_t = full_cache(L, batch, tokens, k, v, seed=2000)
     out = decode_units(L, pool, table_t, batch, tokens, q)
     assert np.all(np.isfinite(out))
-    run_units(L, pool, table, out, k, v, q, [(0, 0), (7, 3), (15, 7), (9, 5)], seed=1)
+    units = [(0, h) for h in range(hkv)] + [(11, h) for h in range(hkv)]
+    units += [(b, (3 * b + 1) % hkv) for b in range(batch) if b not in (0, 11)]
+    run_units(L, pool, table, out, k, v, q, units, seed=1, all_rows={(0, h) for h in range(hkv)})
 
 
 def test_bf16_32k_baseline_decode_full_size():
@@ -148,7 +162,14 @@ def test_per_channel_keys_32k_decode_full_size():
 
 
 def test_mixed_precision_32k_decode_full_size():
-    """Batch 8, 32768 tokens, per-head bits from kvq_plan_bits (average 3, ladder {2,3,4,8})."""
+    """Batch 8, 32768 tokens, per-head bits from kvq_plan_bits (average 3, ladder {2,3,4,8}).
+
+    As the benchmark runs it: several layers decoded one after another through
+    one workspace sized for the largest of them, so layers with different
+    split plans (those with an 8-bit head plan fewer splits) reuse the
+    workspace. Layers decoded: every layer with an 8-bit head, the layer with
+    the most distinct (K, V) pairs, and the layers next to them; one unit per
+    distinct pair of each is compared against the oracle."""
     batch, tokens, hkv, group, d, layers = 8, 32768, 8, 4, 128, 32
     ladder = [2, 3, 4, 8]
     w_k = synth.sensitivities(layers, hkv, seed=3).ravel()
@@ -158,26 +179,40 @@ def test_mixed_precision_32k_decode_full_size():
     bits_v = kvq.kvq_plan_bits(w_v, 1.0, 5.3, ladder, budget)[0].reshape(layers, hkv)
     ref_k, left_k = O.plan_bits_greedy(w_k.astype(np.float32), 1.0, 3.6, ladder, budget)
     assert left_k == 0 and np.array_equal(bits_k.ravel(), np.asarray(ref_k))
-    # the layer with the most distinct (K, V) bit pairs
+    wide = [l for l in range(layers) if (bits_k[l] == 8).any() or (bits_v[l] == 8).any()]
     pairs = [len({(int(a), int(c)) for a, c in zip(bits_k[l], bits_v[l])}) for l in range(layers)]
-    layer = int(np.argmax(pairs))
-    bk, bv = [int(x) for x in bits_k[layer]], [int(x) for x in bits_v[layer]]
-    L = kvq.kvq_layout_init(hkv, group, d, 128, bk, bv)
-    k, v, q = synth.llama_layer_torch(3000 + layer, batch, tokens, hkv, group, d, device=T.DEV)
-    pool, table, table_t = full_cache(L, batch, tokens, k, v, seed=3000 + layer)
-    out = decode_units(L, pool, table_t, batch, tokens, q)
-    assert np.all(np.isfinite(out))
-    # one unit per distinct bit pair, spread over the batch
-    seen, units = set(), []
-    for h in range(hkv):
-        if (bk[h], bv[h]) not in seen:
-            seen.add((bk[h], bv[h]))
-            units.append((len(units) % batch, h))
-    run_units(L, pool, table, out, k, v, q, units, seed=2)
+    most = int(np.argmax(pairs))
+    chosen = sorted({most, *wide, *(l + 1 for l in wide if l + 1 < layers), (most + 1) % layers})
+    assert wide, "the planner was expected to give some head 8 bits"
+    built = []
+    for layer in chosen:
+        bk, bv = [int(x) for x in bits_k[layer]], [int(x) for x in bits_v[layer]]
+        L = kvq.kvq_layout_init(hkv, group, d, 128, bk, bv)
+        k, v, q = synth.llama_layer_torch(3000 + layer, batch, tokens, hkv, group, d, device=T.DEV)
+        pool, table, table_t = full_cache(L, batch, tokens, k, v, seed=3000 + layer)
+        lens = torch.full((batch,), tokens, dtype=torch.int32, device=T.DEV)
+        built.append((layer, L, pool, table, [kvq.Segment(L, pool, table_t, lens, tokens)], k, v, q))
+    sizes = [kvq.kvq_decode_workspace_bytes(seg, batch) for (_, _, _, _, seg, _, _, _) in built]
+    assert len(set(sizes)) > 1, "the chosen layers were expected to have different split plans"
+    ws = torch.empty(max(sizes), dtype=torch.uint8, device=T.DEV)
+    kvq.kvq_decode_workspace_init(ws)
+    outs = [kvq.kvq_decode_attn(seg, q, ws=ws).cpu().numpy() for (_, _, _, _, seg, _, _, q) in built]
+    for (layer, L, pool, table, _, k, v, q), out in zip(built, outs):
+        assert np.all(np.isfinite(out))
+        bk, bv = list(L.bits_k[:hkv]), list(L.bits_v[:hkv])
+        seen, units = set(), []
+        for h in range(hkv):
+            if (bk[h], bv[h]) not in seen:
+                seen.add((bk[h], bv[h]))
+                units.append(((layer + len(units)) % batch, h))
+        run_units(L, pool, table, out, k, v, q, units, seed=2 + layer)
+    head = ws[:kvq.KVQ_DECODE_COUNTER_BYTES].view(torch.int32).cpu().numpy()
+    assert np.all(head == 0)
 
 
 def test_long_context_131k_three_segments_full_size():
-    """Batch 1, 131072 tokens, Hadamard 32: bf16 window of 128, log-spaced 4-bit subset, 2-bit rest."""
+    """Batch 1, 131072 tokens, Hadamard 32: bf16 window of 128, log-spaced 4-bit subset, 2-bit rest.
+    Every KV head is compared against the oracle."""
     tokens, window, hkv, group, d = 131072, 128, 8, 4, 128
     cls = kvq.kvq_logquant_classes(tokens, window)
     assert np.array_equal(cls.astype(np.int32), O.logquant_precision_map(tokens, window))
@@ -196,7 +231,7 @@ def test_long_context_131k_three_segments_full_size():
         keep.append((L, pool, table, kk, vv))
     out = kvq.kvq_decode_attn(segs, q).cpu().numpy()
     assert np.all(np.isfinite(out))
-    for h in (0, 5):
+    for h in range(hkv):
         q_rows = q[0, h * group:(h + 1) * group].float().cpu().numpy()
         ref_segs = []
         stats = T.CodeStats()
@@ -223,3 +258,25 @@ def test_bulk_append_16k_then_decode_full_size():
     out = decode_units(L, pool, table_t, batch, tokens, q)
     assert np.all(np.isfinite(out))
     run_units(L, pool, table, out, k, v, q, [(0, 0), (3, 6), (1, 3)], seed=3)
+
+
+def test_long_context_three_segments_equal_one_merged_segment():
+    """The union over segments is the attention over their tokens in any order (LogQuant page,
+    Methodology 4, A.V = A_P.V_P): the 131072 tokens at one width (2 bits) as one segment, and the same
+    tokens split by the long-context classes into three segments of that width, decode to the same
+    output (up to the order of the fp32 sums)."""
+    tokens, window, hkv, group, d = 131072, 128, 8, 4, 128
+    cls = kvq.kvq_logquant_classes(tokens, window)
+    k, v, q = synth.llama_layer_torch(44, 1, tokens, hkv, group, d, device=T.DEV)
+    L = kvq.kvq_layout_init(hkv, group, d, 32, [2] * hkv, [2] * hkv)
+    pool, _, table_t = full_cache(L, 1, tokens, k, v, seed=45)
+    one = kvq.kvq_decode_attn([kvq.Segment(L, pool, table_t, torch.full((1,), tokens, dtype=torch.int32,
+                                                                         device=T.DEV), tokens)], q)
+    segs = []
+    for c in range(3):
+        idx = torch.from_numpy(np.flatnonzero(cls == c)).to(T.DEV)
+        n = int(idx.numel())
+        p, _, t = full_cache(L, 1, n, k[:, idx].contiguous(), v[:, idx].contiguous(), seed=46 + c)
+        segs.append(kvq.Segment(L, p, t, torch.full((1,), n, dtype=torch.int32, device=T.DEV), n))
+    three = kvq.kvq_decode_attn(segs, q)
+    assert T.max_rel_err(three.cpu().numpy(), one.cpu().numpy()) < 1e-5
