@@ -427,7 +427,7 @@ kvq_status kvq_decode_workspace_init(void* ws, size_t ws_bytes, kvq_stream strea
  * o = R^T o' (one inverse rotation per output row) [SAW: section 3]. Split-K
  * over pages with an online-softmax merge; fp32 accumulation.
  * A sequence with no tokens in any segment gets a zero output row.
- * In:  q device [batch][Hkv*G][head_dim] of q_dtype.
+ * In:  q device [batch][Hkv*G][head_dim] of q_dtype, 16-byte aligned.
  * Out: out device float [batch][Hkv*G][head_dim].
  * ws: device workspace of at least kvq_decode_workspace_bytes bytes, zeroed
  * once by kvq_decode_workspace_init before its first use. The waves of one
@@ -468,6 +468,31 @@ kvq_status kvq_decode_partial(const kvq_segment* segs, int32_t n_segs, int32_t b
                               void* ws, size_t ws_bytes, kvq_stream stream);
 kvq_status kvq_decode_merge(const kvq_segment* segs, int32_t n_segs, int32_t batch,
                             float* out, void* ws, size_t ws_bytes, kvq_stream stream);
+
+/*
+ * Measurement helpers, not part of the decode path: two read-only kernels that
+ * give the read bandwidth the decode kernel is measured against on the device
+ * it runs on (its roofline in practice, beside the HBM specification).
+ *
+ * kvq_measure_read_stream: 2048 waves read `bytes` (a multiple of 8192,
+ * 16-byte aligned) once, the waves sweeping adjacent 8 KiB chunks, and each
+ * wave writes one word to sink (device, sink_words >= 2048).
+ *
+ * kvq_measure_read_paged: the partial decode kernel's load pattern over one
+ * segment with no compute: one wave per (sequence, KV head, split) in the
+ * decode's grid order, each split a contiguous range of four-page groups of
+ * max_len tokens, reading per page the head's K area and V area through the
+ * block table (two groups in flight while one is folded). splits = 0 takes
+ * the decode planner's split count for this segment and batch; sink (device)
+ * receives one word per wave (splits * num_kv_heads * batch words).
+ * Covers areas of up to 2 KiB per head (all widths up to 8 bits at head_dim
+ * 128); 16-bit rows give KVQ_ERR_UNSUPPORTED.
+ * Errors: KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_DEVICE.
+ */
+kvq_status kvq_measure_read_stream(const void* buf, size_t bytes, uint32_t* sink, int32_t sink_words,
+                                   kvq_stream stream);
+kvq_status kvq_measure_read_paged(const kvq_segment* seg, int32_t batch, int32_t splits, uint32_t* sink,
+                                  int32_t sink_words, kvq_stream stream);
 
 /*
  * Size of kvq_decode_attn_noalloc's fixed scratch array, per GPU: the

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkvq.so")
 
-SOURCES = ["kvq_host.cpp", "kvq_append.hip", "kvq_decode.hip"]
+SOURCES = ["kvq_host.cpp", "kvq_append.hip", "kvq_decode.hip", "kvq_measure.hip"]
 
 # The decode kernel's work-sharing fetch is one lane's atomic whose result is
 # read a whole page group later; the compiler's atomic rewrite (a wave

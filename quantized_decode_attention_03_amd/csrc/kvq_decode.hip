@@ -758,22 +758,25 @@ __device__ __forceinline__ int kf_channel_rt(int c, int e) {
 // over each page (the per-channel layout), values per token.
 // One stage of the query rotation's butterflies: channels j and j + ST (bit ST
 // of j clear) become u + v and u - v. A lane's value k is channel
-// (lane + 64k) % D, so stride 64 pairs the lane's values k and k + 1 and
-// smaller strides pair lanes lane and lane ^ ST.
+// (lane % 16) * QPL + k of query row lane / 16, so strides below QPL pair
+// values of one lane and the others pair lanes lane and lane ^ (ST / QPL),
+// inside a row of 16 lanes (DPP moves, no LDS).
 template <int ST, int QPL>
 __device__ __forceinline__ void q_butterfly(float (&qv)[QPL], int lane) {
-  if constexpr (ST == 64) {
-#pragma unroll
-    for (int k = 0; k < QPL; k += 2) {
-      const float u = qv[k], v = qv[k + 1];
-      qv[k] = u + v;
-      qv[k + 1] = u - v;
-    }
-  } else {
-    const bool upper = (lane & ST) != 0;
+  if constexpr (ST < QPL) {
 #pragma unroll
     for (int k = 0; k < QPL; ++k) {
-      const float p = __shfl_xor(qv[k], ST, 64);
+      if (k & ST) continue;
+      const float u = qv[k], v = qv[k + ST];
+      qv[k] = u + v;
+      qv[k + ST] = u - v;
+    }
+  } else {
+    constexpr int X = ST / QPL;
+    const bool upper = (lane & X) != 0;
+#pragma unroll
+    for (int k = 0; k < QPL; ++k) {
+      const float p = xor_lanes16<X>(qv[k], lane);
       qv[k] = upper ? p - qv[k] : qv[k] + p;
     }
   }
@@ -836,35 +839,20 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, const int32_t
   const int wx = split % kXcds, wr = split / kXcds;
   const int sgrp = ((wr - wx) % S + S) % S;
   const int NGU = (pages + 3) / 4;
-  const int g_lo = static_cast<int>((static_cast<int64_t>(NGU) * sgrp) / S);
-  const int NG = static_cast<int>((static_cast<int64_t>(NGU) * (sgrp + 1)) / S) - g_lo;
+  // (32-bit products below 2^31, the common case, avoid the 64-bit division sequence)
+  const bool narrow = NGU < (1 << 20) && S <= 1024;
+  const int g_lo = narrow ? static_cast<int>(static_cast<uint32_t>(NGU * sgrp) / static_cast<uint32_t>(S))
+                          : static_cast<int>((static_cast<int64_t>(NGU) * sgrp) / S);
+  const int g_hi = narrow ? static_cast<int>(static_cast<uint32_t>(NGU * (sgrp + 1)) / static_cast<uint32_t>(S))
+                          : static_cast<int>((static_cast<int64_t>(NGU) * (sgrp + 1)) / S);
+  const int NG = g_hi - g_lo;
   const int SG = a.share_tail ? (NG * kStaticEighths / 8) / kXcds : (NG + kXcds - 1) / kXcds;
   const int pool0 = min(SG * kXcds, NG);
   const uint32_t pool_groups = static_cast<uint32_t>(NG - pool0);
   uint32_t* const ctr = steal + 2 * ((static_cast<int64_t>(b) * a.hkv + h) * S + sgrp);
   const uint8_t* pool = a.pool;
   const int32_t* trow = table + static_cast<int64_t>(b) * a.table_stride;
-  // The query loads go out first (straight-line, no lane-dependent branch),
-  // then the first two groups' loads, so that preparing the query waits only
-  // for the query.
-  constexpr int QPL = 4 * D / 64;  // query values per lane (4 head rows)
-  // Both element types are read as 16-bit halves (upper half at byte esz - 2,
-  // lower half at byte 0; for bf16 both read the element itself), so the loads
-  // are the same instructions whatever the type.
-  uint32_t qhi[QPL], qlo[QPL];
-  {
-    const int64_t qrow0 = static_cast<int64_t>(b) * hq + h * G;
-    const int esz = a.q_bf16 ? 2 : 4;
-    const uint8_t* qp = static_cast<const uint8_t*>(a.q);
-#pragma unroll
-    for (int k = 0; k < QPL; ++k) {
-      const int e = lane + 64 * k, r = min(e / D, G - 1);
-      const uint8_t* el = qp + ((qrow0 + r) * D + e % D) * esz;
-      qhi[k] = *reinterpret_cast<const uint16_t*>(el + esz - 2);
-      qlo[k] = *reinterpret_cast<const uint16_t*>(el);
-    }
-  }
-  __builtin_amdgcn_sched_barrier(0);  // keep the query loads ahead of the group loads
+  constexpr int QPL = 4 * D / 64;  // query values per lane: QPL contiguous channels of one query row
   // per-channel keys: the lane's fragment word (chunk kc_c, word kc_v of quarter
   // lane / 16) and the byte offsets of its two channels' metadata in a page
   const int kc_c = (lane & 15) >> 2, kc_v = lane & 3;
@@ -936,6 +924,33 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, const int32_t
   };
   if (SG == 0 && !exhausted) fetch();
   resolve();
+  // The first positions' block-table entries are requested first; the query
+  // loads follow them, so the first page loads wait only for the table (the
+  // loads complete in order), and preparing the query overlaps those pages.
+  // Lane l reads channels [c0, c0 + QPL) of query row l / 16 (rows past the
+  // group repeat the last row and are zeroed after the rotation): QPL
+  // elements as two loads of QPL * 2 bytes, the second at the same address for
+  // bf16, so the instructions are the same whatever the type.
+  __builtin_amdgcn_sched_barrier(0);
+  uint32_t qw[QPL];
+  {
+    const int r = min(lane >> 4, G - 1);
+    const int c0 = (lane & 15) * QPL;
+    const int64_t qrow = static_cast<int64_t>(b) * hq + h * G + r;
+    const uint8_t* qp = static_cast<const uint8_t*>(a.q) + (qrow * D + c0) * (a.q_bf16 ? 2 : 4);
+    const int second = a.q_bf16 ? 0 : QPL * 2;
+    if constexpr (QPL == 8) {
+      const uint4 w0 = *reinterpret_cast<const uint4*>(qp);
+      const uint4 w1 = *reinterpret_cast<const uint4*>(qp + second);
+      qw[0] = w0.x; qw[1] = w0.y; qw[2] = w0.z; qw[3] = w0.w;
+      qw[4] = w1.x; qw[5] = w1.y; qw[6] = w1.z; qw[7] = w1.w;
+    } else {
+      const uint2 w0 = *reinterpret_cast<const uint2*>(qp);
+      const uint2 w1 = *reinterpret_cast<const uint2*>(qp + second);
+      qw[0] = w0.x; qw[1] = w0.y; qw[2] = w1.x; qw[3] = w1.y;
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
   auto load_next = [&](GroupRaw<KB, VB, D>& g) {
     const int gid = next_gid;
     int32_t blks[4];
@@ -953,7 +968,10 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, const int32_t
   // strides 1, 2, ... below the Hadamard block) ----
   float qv[QPL];
 #pragma unroll
-  for (int k = 0; k < QPL; ++k) qv[k] = bits_f(qhi[k] << 16 | (a.q_bf16 ? 0u : qlo[k]));
+  for (int k = 0; k < QPL; ++k) {
+    const uint32_t hb = (k & 1) ? (qw[k / 2] & 0xffff0000u) : (qw[k / 2] << 16);
+    qv[k] = bits_f(a.q_bf16 ? hb : qw[k]);
+  }
   {
     const int n = a.had_block;
     if (n > 1) q_butterfly<1>(qv, lane);
@@ -966,10 +984,12 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, const int32_t
       if (n > 64) q_butterfly<64>(qv, lane);
     }
   }
+  {
+    const int r = lane >> 4;
+    float4* dst = reinterpret_cast<float4*>(&qs[r][(lane & 15) * QPL]);
 #pragma unroll
-  for (int k = 0; k < QPL; ++k) {
-    const int e = lane + 64 * k, r = e / D;
-    qs[r][e % D] = r < G ? qv[k] : 0.f;
+    for (int j = 0; j < QPL / 4; ++j)
+      dst[j] = r < G ? make_float4(qv[4 * j], qv[4 * j + 1], qv[4 * j + 2], qv[4 * j + 3]) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   if (lane < 8) wzero[lane] = 0;
   __syncthreads();

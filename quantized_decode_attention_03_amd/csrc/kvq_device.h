@@ -149,6 +149,28 @@ __device__ __forceinline__ float wave_sum_scalar(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
 }
 
+// The value of lane lane ^ X (X = 1, 2, 4 or 8: a partner in the same row of
+// 16 lanes) by DPP: quad permutations for 1 and 2, a rotation of the row by 8
+// for 8, and for 4 a shift up or down by 4 picked by the lane's bit 2.
+constexpr int kDppQuadXor1 = 0xB1, kDppQuadXor2 = 0x4E, kDppRowShl4 = 0x104,
+              kDppRowRor8 = 0x128;
+template <int X>
+__device__ __forceinline__ float xor_lanes16(float v, int lane) {
+  const int i = __builtin_bit_cast(int, v);
+  if constexpr (X == 1) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, i, kDppQuadXor1, 0xf, 0xf, false));
+  } else if constexpr (X == 2) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, i, kDppQuadXor2, 0xf, 0xf, false));
+  } else if constexpr (X == 4) {
+    const int up = __builtin_amdgcn_update_dpp(0, i, kDppRowShl4, 0xf, 0xf, false);  // lane + 4
+    const int dn = __builtin_amdgcn_update_dpp(0, i, kDppRowShr4, 0xf, 0xf, false);  // lane - 4
+    return __builtin_bit_cast(float, (lane & 4) ? dn : up);
+  } else {
+    static_assert(X == 8, "partners inside a row of 16 lanes");
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, i, kDppRowRor8, 0xf, 0xf, false));
+  }
+}
+
 // A constant materialised in a VGPR: lets v_and_or_b32 / v_perm_b32 take it
 // as their vector operand (gfx9 VOP3 encodings take no literal constants and
 // at most one scalar operand).

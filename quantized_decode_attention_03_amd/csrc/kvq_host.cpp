@@ -861,6 +861,7 @@ static kvq_status decode_partial_impl(const kvq_segment* segs, int32_t n_segs, i
   if (q_dtype != KVQ_F32 && q_dtype != KVQ_BF16) return fail(KVQ_ERR_ARG, "kvq_decode_partial: bad q dtype");
   if (batch == 0) return ok();
   if (!q || !ws) return fail(KVQ_ERR_ARG, "kvq_decode_partial: null q or workspace");
+  if (reinterpret_cast<uintptr_t>(q) % 16 != 0) return fail(KVQ_ERR_ARG, "kvq_decode_partial: q not 16-byte aligned");
   const kvq_layout& L0 = *segs[0].layout;
   const int hq = L0.num_kv_heads * L0.group;
   std::vector<SplitPlan> plans;
@@ -1002,6 +1003,35 @@ static kvq_status decode_partial_impl(const kvq_segment* segs, int32_t n_segs, i
 kvq_status kvq_decode_partial(const kvq_segment* segs, int32_t n_segs, int32_t batch, const void* q,
                               kvq_dtype q_dtype, void* ws, size_t ws_bytes, kvq_stream stream) {
   return decode_partial_impl(segs, n_segs, batch, q, q_dtype, ws, ws_bytes, stream, false);
+}
+
+kvq_status kvq_measure_read_stream(const void* buf, size_t bytes, uint32_t* sink, int32_t sink_words,
+                                   kvq_stream stream) {
+  constexpr int kWaves = 2048;
+  if (!buf || !sink) return fail(KVQ_ERR_ARG, "kvq_measure_read_stream: null pointer");
+  if (bytes < 8192 || bytes % 8192 != 0 || reinterpret_cast<uintptr_t>(buf) % 16 != 0)
+    return fail(KVQ_ERR_ARG, "kvq_measure_read_stream: bytes must be a positive multiple of 8192, buf 16-byte aligned");
+  if (sink_words < kWaves) return fail(KVQ_ERR_ARG, "kvq_measure_read_stream: sink_words %d < %d", sink_words, kWaves);
+  return device_status(kvq::launch_measure_stream(buf, bytes, sink, kWaves, reinterpret_cast<hipStream_t>(stream)),
+                       "kvq_measure_read_stream");
+}
+
+kvq_status kvq_measure_read_paged(const kvq_segment* seg, int32_t batch, int32_t splits, uint32_t* sink,
+                                  int32_t sink_words, kvq_stream stream) {
+  const char* who = "kvq_measure_read_paged";
+  kvq_status st = check_segments(seg, 1, batch, who);
+  if (st != KVQ_OK) return st;
+  if (batch < 1 || seg->max_len < 1) return fail(KVQ_ERR_ARG, "%s: need batch >= 1 and max_len >= 1", who);
+  if (!sink) return fail(KVQ_ERR_ARG, "%s: null sink", who);
+  if (splits == 0) splits = plan_splits(*seg, batch).n_splits;
+  if (splits < 8 || splits % 8 != 0) return fail(KVQ_ERR_ARG, "%s: splits %d not a positive multiple of 8", who, splits);
+  const int64_t waves = static_cast<int64_t>(splits) * seg->layout->num_kv_heads * batch;
+  if (sink_words < waves) return fail(KVQ_ERR_ARG, "%s: sink_words %d < %lld waves", who, sink_words,
+                                      static_cast<long long>(waves));
+  const hipError_t e = kvq::launch_measure_paged(*seg, batch, splits, sink, reinterpret_cast<hipStream_t>(stream));
+  if (e == hipErrorInvalidValue)
+    return fail(KVQ_ERR_UNSUPPORTED, "%s: areas of more than 2 KiB per head (16-bit rows) are not covered", who);
+  return device_status(e, who);
 }
 
 kvq_status kvq_decode_merge(const kvq_segment* segs, int32_t n_segs, int32_t batch, float* out, void* ws,

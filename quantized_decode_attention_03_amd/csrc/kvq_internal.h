@@ -134,4 +134,11 @@ bool decode_partial_mixable(int kbits, int vbits, int d);
 // every pair mixable. Same grid, partials and counters as launch_decode_partial.
 hipError_t launch_decode_partial_mixed(const DecodeArgs& a, int d, int n_splits, int batch, hipStream_t s);
 
+// Read-bandwidth references (measurement only): a streaming read of `bytes`
+// by `waves` waves, and the partial decode kernel's load pattern over one
+// segment with no compute (areas up to 2 KiB per head). Each wave writes one
+// word to sink.
+hipError_t launch_measure_stream(const void* buf, size_t bytes, uint32_t* sink, int waves, hipStream_t s);
+hipError_t launch_measure_paged(const kvq_segment& seg, int batch, int splits, uint32_t* sink, hipStream_t s);
+
 }  // namespace kvq

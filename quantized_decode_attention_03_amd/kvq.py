@@ -27,7 +27,8 @@ EXPORTED = [
     "kvq_decode_workspace_bytes", "kvq_decode_workspace_init", "kvq_decode_attn", "kvq_decode_partial",
     "kvq_decode_merge", "kvq_fit_distortion", "kvq_amgm_ratio", "kvq_quant_mse",
     "kvq_logquant_dynamic_classes", "kvq_logquant_init", "kvq_logquant_advance", "kvq_logquant_requant",
-    "kvq_append_check", "kvq_decode_attn_noalloc", "kvq_plan_bits_components",
+    "kvq_append_check", "kvq_decode_attn_noalloc", "kvq_plan_bits_components", "kvq_measure_read_stream",
+    "kvq_measure_read_paged",
 ]
 
 KVQ_DECODE_COUNTER_BYTES = 65536
@@ -123,6 +124,8 @@ def lib():
     L.kvq_decode_attn.argtypes = [ctypes.POINTER(KvqSegment), i32, i32, vp, ctypes.c_int, vp, vp, sz, vp]
     L.kvq_decode_partial.argtypes = [ctypes.POINTER(KvqSegment), i32, i32, vp, ctypes.c_int, vp, sz, vp]
     L.kvq_decode_merge.argtypes = [ctypes.POINTER(KvqSegment), i32, i32, vp, vp, sz, vp]
+    L.kvq_measure_read_stream.argtypes = [vp, sz, vp, i32, vp]
+    L.kvq_measure_read_paged.argtypes = [ctypes.POINTER(KvqSegment), i32, i32, vp, i32, vp]
     L.kvq_decode_attn_noalloc.argtypes = [ctypes.POINTER(KvqSegment), i32, i32, vp, ctypes.c_int, vp, vp]
     for name in EXPORTED:
         if name not in ("kvq_abi_version", "kvq_status_str", "kvq_last_error"):
@@ -462,6 +465,22 @@ def kvq_decode_attn(segments, q, out=None, ws=None, stream=None):
                                ws.numel(), _stream(stream))
     _check(st, "kvq_decode_attn")
     return out
+
+
+def kvq_measure_read_stream(buf, sink, stream=None):
+    """Streaming read of the uint8 device tensor buf (measurement only); sink: int32 device tensor >= 2048."""
+    import torch
+    _check(lib().kvq_measure_read_stream(_dev_ptr(buf, (torch.uint8,), "buf"), buf.numel(),
+                                         _dev_ptr(sink, (torch.int32,), "sink"), sink.numel(), _stream(stream)),
+           "kvq_measure_read_stream")
+
+
+def kvq_measure_read_paged(segment, batch, sink, splits=0, stream=None):
+    """The partial decode kernel's load pattern over one segment with no compute (measurement only)."""
+    import torch
+    segs = _segments([segment])
+    _check(lib().kvq_measure_read_paged(segs, int(batch), int(splits), _dev_ptr(sink, (torch.int32,), "sink"),
+                                        sink.numel(), _stream(stream)), "kvq_measure_read_paged")
 
 
 def kvq_decode_attn_noalloc(segments, q, out, stream=None):

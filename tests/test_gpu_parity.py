@@ -498,6 +498,20 @@ def test_workspace_reused_across_split_plans(monkeypatch):
     assert np.all(head == 0)
 
 
+def test_measurement_reads_run_over_a_cache():
+    """The two read references of the benchmark run over a real cache and buffer (they only read)."""
+    lens = [3000, 37]
+    L, lay, cache, ref, table, k, v = build_case(128, 128, 4, [4, 4], [4, 2], lens, seed=81)
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device=T.DEV)
+    before = cache.pool.clone()
+    kvq.kvq_measure_read_paged(cache.segment(lens), 2, sink)
+    kvq.kvq_measure_read_paged(cache.segment(lens), 2, sink, splits=8)
+    buf = torch.ones(1 << 20, dtype=torch.uint8, device=T.DEV)
+    kvq.kvq_measure_read_stream(buf, sink)
+    torch.cuda.synchronize()
+    assert torch.equal(before, cache.pool)
+
+
 @pytest.mark.parametrize("deterministic", [True, False])
 def test_decode_step_in_hip_graph_matches_eager(monkeypatch, deterministic):
     # append one token + partial + merge captured as one graph, over two

@@ -282,6 +282,23 @@ def test_decode_argument_checks_need_no_device():
     assert "kvq_layout_init" in kvq.kvq_last_error()
 
 
+def test_measurement_helpers_argument_checks_need_no_device():
+    lib = kvq.lib()
+    p = ctypes.c_void_p(0x1000)
+    assert lib.kvq_measure_read_stream(None, 8192, p, 4096, None) == kvq.KVQ_ERR_ARG
+    assert lib.kvq_measure_read_stream(p, 8000, p, 4096, None) == kvq.KVQ_ERR_ARG     # not a multiple of 8192
+    assert lib.kvq_measure_read_stream(ctypes.c_void_p(0x1004), 8192, p, 4096, None) == kvq.KVQ_ERR_ARG
+    assert lib.kvq_measure_read_stream(p, 8192, p, 100, None) == kvq.KVQ_ERR_ARG      # sink too small
+    L = kvq.kvq_layout_init(8, 4, 128, 128, [4] * 8, [4] * 8)
+    seg = (kvq.KvqSegment * 1)(_fake_segment(L, 32768, 2048))
+    assert lib.kvq_measure_read_paged(seg, 16, 12, p, 1 << 20, None) == kvq.KVQ_ERR_ARG  # splits not a multiple of 8
+    assert lib.kvq_measure_read_paged(seg, 16, 16, p, 100, None) == kvq.KVQ_ERR_ARG      # sink below one word per wave
+    assert lib.kvq_measure_read_paged(seg, 16, 16, None, 1 << 20, None) == kvq.KVQ_ERR_ARG
+    bf = kvq.kvq_layout_init(8, 4, 128, 128, [16] * 8, [16] * 8)
+    seg16 = (kvq.KvqSegment * 1)(_fake_segment(bf, 32768, 2048))
+    assert lib.kvq_measure_read_paged(seg16, 16, 16, p, 1 << 20, None) == kvq.KVQ_ERR_UNSUPPORTED
+
+
 def test_append_and_dequant_argument_checks_need_no_device():
     lib = kvq.lib()
     L = kvq.kvq_layout_init(4, 4, 64, 64, [4] * 4, [2] * 4)
