@@ -425,7 +425,7 @@ constexpr int kXcds = 8;  // accelerator dies of the chip; workgroups go round-r
 constexpr int kStaticEighths = KVQ_TUNE_STATIC_EIGHTHS;
 
 template <int KB, int VB, int D, bool M16, bool KC>
-__device__ __forceinline__ void load_group(const DecodeArgs& a, const uint8_t* pool, const int32_t (&blks)[4],
+__device__ __forceinline__ void load_group(const DecodeSeg& a, const uint8_t* pool, const int32_t (&blks)[4],
                                            int grp, int p1, int seq_len, int64_t koff, int64_t voff, int lane,
                                            int kc0, int kc1, GroupRaw<KB, VB, D>& g) {
   constexpr int RBK = D * KB / 8, RBV = D * VB / 8, QBYTES = RBK / 4;
@@ -783,7 +783,7 @@ __device__ __forceinline__ void q_butterfly(float (&qv)[QPL], int lane) {
 }
 
 template <int KB, int VB, int D, bool M16, bool KC = false>
-__device__ __forceinline__ void partial_split(const DecodeArgs& a, const int32_t* __restrict__ table,
+__device__ __forceinline__ void partial_split(const DecodeArgs& a, int si, int L, const int32_t* __restrict__ table,
                                               uint32_t* __restrict__ steal, float qscale, PartialLds<D>& lds) {
   using KF = KFmt<KB, D>;
   using VF = VFmt<VB, D>;
@@ -797,25 +797,28 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, const int32_t
   auto& wzero = lds.wzero;
 
   const int lane = threadIdx.x;
-  // One-dimensional grid of U units x W splits (W a multiple of the XCD
-  // count). Workgroup L runs on XCD x = L % 8 as that XCD's m-th workgroup,
-  // m = L / 8, and serves unit m % U as its split x + 8 * (m / U). So every
-  // unit has waves on all eight XCDs and from early and late in each XCD's
-  // dispatch order (of two waves on a SIMD the first dispatched is issued
-  // first); sharing the tail then evens the units out.
-  const int U = a.n_heads * a.batch;
-  const int m = static_cast<int>(blockIdx.x) / kXcds;
+  const DecodeSeg& sg = a.seg[si];
+  // One-dimensional grid of U units x W splits per segment (W a multiple of
+  // the XCD count, each segment's range starting at a multiple of 8).
+  // Workgroup L of the segment runs on XCD x = L % 8 as that XCD's m-th
+  // workgroup of it, m = L / 8, and serves unit m % U as its split
+  // x + 8 * (m / U). So every unit has waves on all eight XCDs and from early
+  // and late in each XCD's dispatch order (of two waves on a SIMD the first
+  // dispatched is issued first); sharing the tail then evens the units out.
+  const int U = sg.n_heads * a.batch;
+  const int m = L / kXcds;
   const int unit = m % U;
-  const int split = static_cast<int>(blockIdx.x) % kXcds + kXcds * (m / U);
-  const int hidx = unit % a.n_heads;
-  const int b = unit / a.n_heads;
-  const int h = a.heads[hidx];
+  const int split = L % kXcds + kXcds * (m / U);
+  const int hidx = unit % sg.n_heads;
+  const int b = unit / sg.n_heads;
+  const int he = sg.head_base + hidx;
+  const int h = a.heads[he];
   const int G = a.group;
   const int hq = a.hkv * G;
-  const int64_t koff = a.k_off[hidx], voff = a.v_off[hidx];
-  const int seq_len = a.seq_lens[b];
-  const int pages = min((seq_len + kBlockTokens - 1) / kBlockTokens, a.table_stride);
-  const int slot = a.slot_base + split;
+  const int64_t koff = a.k_off[he], voff = a.v_off[he];
+  const int seq_len = sg.seq_lens[b];
+  const int pages = min((seq_len + kBlockTokens - 1) / kBlockTokens, sg.table_stride);
+  const int slot = sg.slot_base + split;
 
   // Work sharing inside the unit (sequence b, KV head h), whose W waves each
   // write one partial. The unit's page groups (four pages each) are divided
@@ -834,7 +837,7 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, const int32_t
   // group the second is unused). Without
   // sharing (deterministic order) wave i takes [i*SG, (i+1)*SG) with
   // SG = ceil(NG / 8) and there is no tail.
-  const int W = static_cast<int>(gridDim.x) / U;
+  const int W = sg.n_splits;
   const int S = W / kXcds;
   const int wx = split % kXcds, wr = split / kXcds;
   const int sgrp = ((wr - wx) % S + S) % S;
@@ -850,8 +853,8 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, const int32_t
   const int pool0 = min(SG * kXcds, NG);
   const uint32_t pool_groups = static_cast<uint32_t>(NG - pool0);
   uint32_t* const ctr = steal + 2 * ((static_cast<int64_t>(b) * a.hkv + h) * S + sgrp);
-  const uint8_t* pool = a.pool;
-  const int32_t* trow = table + static_cast<int64_t>(b) * a.table_stride;
+  const uint8_t* pool = sg.pool;
+  const int32_t* trow = table + static_cast<int64_t>(b) * sg.table_stride;
   constexpr int QPL = 4 * D / 64;  // query values per lane: QPL contiguous channels of one query row
   // per-channel keys: the lane's fragment word (chunk kc_c, word kc_v of quarter
   // lane / 16) and the byte offsets of its two channels' metadata in a page
@@ -958,7 +961,7 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, const int32_t
     for (int pp = 0; pp < 4; ++pp) blks[pp] = __builtin_amdgcn_readlane(next_tab, tab_lane + pp);
     resolve();
     g.gid = gid;
-    load_group<KB, VB, D, M16, KC>(a, pool, blks, 4 * (g_lo + gid), pages, seq_len, koff, voff, lane, kc0, kc1, g);
+    load_group<KB, VB, D, M16, KC>(sg, pool, blks, 4 * (g_lo + gid), pages, seq_len, koff, voff, lane, kc0, kc1, g);
   };
 #pragma unroll
   for (int j = 0; j < DEPTH; ++j) load_next(gbuf[j]);
@@ -990,6 +993,14 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, const int32_t
 #pragma unroll
     for (int j = 0; j < QPL / 4; ++j)
       dst[j] = r < G ? make_float4(qv[4 * j], qv[4 * j + 1], qv[4 * j + 2], qv[4 * j + 3]) : make_float4(0.f, 0.f, 0.f, 0.f);
+    // q~ = q' * qscale of this unit's query heads, for the short bf16 segment
+    // the merge kernel attends to itself (one wave per unit writes it)
+    if (sg.write_q && split == 0 && r < G) {
+      float4* qd = reinterpret_cast<float4*>(a.qrot + ((static_cast<int64_t>(b) * hq + h * G + r) * D + (lane & 15) * QPL));
+#pragma unroll
+      for (int j = 0; j < QPL / 4; ++j)
+        qd[j] = make_float4(qv[4 * j] * qscale, qv[4 * j + 1] * qscale, qv[4 * j + 2] * qscale, qv[4 * j + 3] * qscale);
+    }
   }
   if (lane < 8) wzero[lane] = 0;
   __syncthreads();
@@ -1195,7 +1206,7 @@ void decode_partial_kernel(DecodeArgs a, const int32_t* __restrict__ table, uint
   // (table and counters as separate restrict arguments: the counters' atomics
   // cannot alias the block table, so its entries stay scalar loads)
   __shared__ PartialLds<D> lds;
-  partial_split<KB, VB, D, M16>(a, table, steal, qscale, lds);
+  partial_split<KB, VB, D, M16>(a, 0, static_cast<int>(blockIdx.x), table, steal, qscale, lds);
 }
 
 // Keys quantized per channel over each page, values per token: the same split,
@@ -1215,31 +1226,39 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KcWaves<KB, 
 void decode_partial_kc_kernel(DecodeArgs a, const int32_t* __restrict__ table, uint32_t* __restrict__ steal,
                               float qscale) {
   __shared__ PartialLds<D> lds;
-  partial_split<KB, VB, D, false, true>(a, table, steal, qscale, lds);
+  partial_split<KB, VB, D, false, true>(a, 0, static_cast<int>(blockIdx.x), table, steal, qscale, lds);
 }
 
-// Heads of several formats in one launch (a segment whose per-head widths
-// differ): each wave runs the body of its head's (key, value) width pair.
-// Covers the pairs of 2-, 3- and 4-bit codes, which all run two waves per
-// SIMD. One launch fills the device in one dispatch; launches per format on
+// Heads of several formats, and of several segments, in one launch: each wave
+// finds its segment (the last whose grid range starts at or before its
+// workgroup) and runs the body of its head's (key, value) width pair. Covers
+// the pairs of 2-, 3- and 4-bit codes, which all run two waves per SIMD. One
+// launch fills the device in one dispatch; launches per format or segment on
 // concurrent streams start one after another, tens of microseconds apart.
 template <int D, bool M16>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void decode_partial_mixed_kernel(DecodeArgs a, const int32_t* __restrict__ table, uint32_t* __restrict__ steal,
-                                 float qscale) {
+void decode_partial_multi_kernel(DecodeArgs a, float qscale) {
   __shared__ PartialLds<D> lds;
-  const int unit = (static_cast<int>(blockIdx.x) / kXcds) % (a.n_heads * a.batch);
-  const int pair = __builtin_amdgcn_readfirstlane(a.pair[unit % a.n_heads]);
+  const int blk = static_cast<int>(blockIdx.x);
+  int si = 0;
+  for (int s = 1; s < a.n_segs; ++s)
+    if (blk >= a.seg[s].grid_start) si = s;
+  const DecodeSeg& sg = a.seg[si];
+  const int L = blk - sg.grid_start;
+  const int unit = (L / kXcds) % (sg.n_heads * a.batch);
+  const int pair = __builtin_amdgcn_readfirstlane(a.pair[sg.head_base + unit % sg.n_heads]);
+  const int32_t* table = sg.table;
+  uint32_t* steal = sg.steal;
   switch (pair) {
-    case 0x22: partial_split<2, 2, D, M16>(a, table, steal, qscale, lds); break;
-    case 0x23: partial_split<2, 3, D, M16>(a, table, steal, qscale, lds); break;
-    case 0x24: partial_split<2, 4, D, M16>(a, table, steal, qscale, lds); break;
-    case 0x32: partial_split<3, 2, D, M16>(a, table, steal, qscale, lds); break;
-    case 0x33: partial_split<3, 3, D, M16>(a, table, steal, qscale, lds); break;
-    case 0x34: partial_split<3, 4, D, M16>(a, table, steal, qscale, lds); break;
-    case 0x42: partial_split<4, 2, D, M16>(a, table, steal, qscale, lds); break;
-    case 0x43: partial_split<4, 3, D, M16>(a, table, steal, qscale, lds); break;
-    case 0x44: partial_split<4, 4, D, M16>(a, table, steal, qscale, lds); break;
+    case 0x22: partial_split<2, 2, D, M16>(a, si, L, table, steal, qscale, lds); break;
+    case 0x23: partial_split<2, 3, D, M16>(a, si, L, table, steal, qscale, lds); break;
+    case 0x24: partial_split<2, 4, D, M16>(a, si, L, table, steal, qscale, lds); break;
+    case 0x32: partial_split<3, 2, D, M16>(a, si, L, table, steal, qscale, lds); break;
+    case 0x33: partial_split<3, 3, D, M16>(a, si, L, table, steal, qscale, lds); break;
+    case 0x34: partial_split<3, 4, D, M16>(a, si, L, table, steal, qscale, lds); break;
+    case 0x42: partial_split<4, 2, D, M16>(a, si, L, table, steal, qscale, lds); break;
+    case 0x43: partial_split<4, 3, D, M16>(a, si, L, table, steal, qscale, lds); break;
+    case 0x44: partial_split<4, 4, D, M16>(a, si, L, table, steal, qscale, lds); break;
     default: break;  // the host sends only these pairs
   }
 }
@@ -1251,6 +1270,12 @@ void decode_partial_mixed_kernel(DecodeArgs a, const int32_t* __restrict__ table
 // split slots (wave w takes slots s = w mod NW), so a long list of slots
 // (batch 1 at long context has hundreds) is read with NW waves' loads in
 // flight; each wave's loop is bound by load latency, not bandwidth.
+//
+// A short bf16 segment (a.win.pool set: every head 16-bit keys and values, at
+// most kMergeWindowMax tokens) is attended to here rather than by a partial
+// launch: its scores z_t = q~ . k'_t (q~ written by the partial launch, k'_t
+// the stored rotated row, log2 units as in the partials), then its weights
+// 2^(z_t - M) and weighted rows enter the same sums as the split partials'.
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) void decode_merge_kernel(MergeArgs a, float rs_n) {
   constexpr int CPL = D / 64;  // channels per lane: [CPL*lane, CPL*lane + CPL)
@@ -1259,15 +1284,66 @@ __global__ __launch_bounds__(64 * NW) void decode_merge_kernel(MergeArgs a, floa
   __shared__ float wsh[CHUNK];   // split weights 2^(m_s - M) of the current chunk
   __shared__ float red[NW][D];   // per-wave channel sums
   __shared__ float scal[NW][2];  // per-wave max, then per-wave sum of weights * l
+  __shared__ float wq[D];        // window segment: q~ of this query head
+  __shared__ float wz[kMergeWindowMax];  // window segment: scores, then weights
+  __shared__ int32_t wrow[kMergeWindowMax];  // window segment: block of each token (0 when unmapped)
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t bg = blockIdx.x;
   const int S = a.total_slots;
   const float* ml = a.part_ml + bg * S * 2;
   const float* po = a.part_o + bg * S * D;
+  const MergeWindow& win = a.win;
+  const int b = static_cast<int>(bg / a.hq);
+  const int h = static_cast<int>(bg % a.hq) / a.group;
+  const int nwin = win.pool ? min(win.seq_lens[b], win.max_len) : 0;
+  const uint32_t wblocks = win.pool_blocks > 0x7fffffff ? 0x80000000u : static_cast<uint32_t>(win.pool_blocks);
+  // the window row of token t (block 0 for an unmapped page; its weight is 0)
+  auto win_row = [&](int t, int64_t off, bool& ok) {
+    const int32_t blk = win.table[static_cast<int64_t>(b) * win.table_stride + t / kBlockTokens];
+    ok = static_cast<uint32_t>(blk) < wblocks;
+    return win.pool + (ok ? blk : 0) * win.block_bytes + off + (t % kBlockTokens) * (D * 2);
+  };
+  if (nwin > 0) {
+    if (tid < D) wq[tid] = a.qrot[bg * D + tid];
+    __syncthreads();
+  }
 
-  // global max over splits
+  // global max over splits and window tokens; a window token's score is
+  // summed by eight lanes, D / 8 channels each, then over the eight lanes
   float mx = NEG_INF;
   for (int s = tid; s < S; s += 64 * NW) mx = fmaxf(mx, ml[2 * s]);
+  {
+    constexpr int CH = D / 8;  // channels per lane of a token
+    const int part = lane & 7;
+    for (int t0 = tid >> 3; t0 < ((nwin + 7) & ~7); t0 += 8 * NW) {
+      const int t = min(t0, nwin - 1);  // lanes past the last token repeat it (not stored)
+      bool ok;
+      const uint4* row = reinterpret_cast<const uint4*>(win_row(t, win.k_off[h], ok)) + part * (CH / 8);
+      float z = 0.f;
+#pragma unroll
+      for (int c = 0; c < CH / 8; ++c) {
+        const uint4 v = row[c];
+        const float* qq = &wq[part * CH + 8 * c];
+        z = fmaf(qq[0], bf16lo_to_f(v.x), z);
+        z = fmaf(qq[1], bf16hi_to_f(v.x), z);
+        z = fmaf(qq[2], bf16lo_to_f(v.y), z);
+        z = fmaf(qq[3], bf16hi_to_f(v.y), z);
+        z = fmaf(qq[4], bf16lo_to_f(v.z), z);
+        z = fmaf(qq[5], bf16hi_to_f(v.z), z);
+        z = fmaf(qq[6], bf16lo_to_f(v.w), z);
+        z = fmaf(qq[7], bf16hi_to_f(v.w), z);
+      }
+      z += xor_lanes16<1>(z, lane);
+      z += xor_lanes16<2>(z, lane);
+      z += xor_lanes16<4>(z, lane);
+      z = ok ? z : NEG_INF;
+      if (part == 0 && t0 < nwin) {
+        wz[t] = z;
+        wrow[t] = ok ? win.table[static_cast<int64_t>(b) * win.table_stride + t / kBlockTokens] : 0;
+      }
+      if (t0 < nwin) mx = fmaxf(mx, z);
+    }
+  }
   mx = wave_max_scalar(mx);
   if (lane == 0) scal[w][0] = mx;
   __syncthreads();
@@ -1308,8 +1384,40 @@ __global__ __launch_bounds__(64 * NW) void decode_merge_kernel(MergeArgs a, floa
           for (int j = 0; j < CPL; ++j) x[j] = fmaf(wu[u], v[u][j], x[j]);
       }
     }
+    if (nwin > 0) {
+      // window weights 2^(z_t - M) (each thread its own tokens), then each
+      // wave adds tokens t = w mod NW of the value rows, CPL channels a lane
+      __syncthreads();  // every token's score is stored
+      for (int t = tid; t < nwin; t += 64 * NW) {
+        const float p = __builtin_amdgcn_exp2f(wz[t] - mx);  // masked: exp2(-inf) = 0
+        wz[t] = p;
+        lpart += p;
+      }
+      __syncthreads();
+      // tokens t = w, w + NW, ... in batches of eight (the last padded with
+      // the last token at weight 0), each token's row read by its CPL-channel
+      // lane slices, so a batch's loads are all in flight together
+      const uint8_t* vbase = win.pool + win.v_off[h] + (CPL == 2 ? 4 : 2) * lane;
+      for (int t = w; t < nwin; t += 8 * NW) {
+        uint32_t raw[8];
+        float pw[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int tu = t + u * NW, tc = min(tu, nwin - 1);
+          const uint8_t* row = vbase + wrow[tc] * win.block_bytes + (tc % kBlockTokens) * (D * 2);
+          if constexpr (CPL == 2) raw[u] = *reinterpret_cast<const uint32_t*>(row);
+          else raw[u] = *reinterpret_cast<const uint16_t*>(row);
+          pw[u] = tu < nwin ? wz[tc] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          x[0] = fmaf(pw[u], bf16lo_to_f(raw[u]), x[0]);
+          if constexpr (CPL == 2) x[1] = fmaf(pw[u], bf16hi_to_f(raw[u]), x[1]);
+        }
+      }
+    }
   }
-  // combine the four waves
+  // combine the waves
   lpart = wave_sum_scalar(lpart);
   if (lane == 0) scal[w][1] = lpart;
 #pragma unroll
@@ -1355,43 +1463,51 @@ __global__ __launch_bounds__(64 * NW) void decode_merge_kernel(MergeArgs a, floa
   }
 }
 
+// Workgroups of a single-segment launch (0 if its split count is not a multiple of the XCD count).
+unsigned single_grid(const DecodeArgs& a) {
+  const DecodeSeg& sg = a.seg[0];
+  if (a.n_segs != 1 || sg.n_splits % kXcds != 0 || sg.grid_start != 0) return 0;
+  return static_cast<unsigned>(sg.n_splits) * sg.n_heads * a.batch;
+}
+
 template <int KB, int VB, int D, bool M16>
-hipError_t launch_partial_t(const DecodeArgs& a, int n_splits, int batch, float qscale, hipStream_t s) {
-  if (a.batch != batch || n_splits % kXcds != 0) return hipErrorInvalidValue;
-  dim3 grid(static_cast<unsigned>(n_splits) * a.n_heads * batch);
-  hipLaunchKernelGGL((decode_partial_kernel<KB, VB, D, M16>), grid, dim3(64), 0, s, a, a.table, a.steal, qscale);
+hipError_t launch_partial_t(const DecodeArgs& a, float qscale, hipStream_t s) {
+  const unsigned grid = single_grid(a);
+  if (grid == 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((decode_partial_kernel<KB, VB, D, M16>), dim3(grid), dim3(64), 0, s, a, a.seg[0].table,
+                     a.seg[0].steal, qscale);
   return hipGetLastError();
 }
 
 // Formats whose rows carry metadata get a float16-metadata instance too.
 template <int KB, int VB, int D>
-hipError_t launch_partial_m(const DecodeArgs& a, int n_splits, int batch, float qs, hipStream_t s) {
+hipError_t launch_partial_m(const DecodeArgs& a, float qs, hipStream_t s) {
   if constexpr (KB != 16 || VB != 16) {
-    if (a.meta16) return launch_partial_t<KB, VB, D, true>(a, n_splits, batch, qs, s);
+    if (a.meta16) return launch_partial_t<KB, VB, D, true>(a, qs, s);
   }
-  return launch_partial_t<KB, VB, D, false>(a, n_splits, batch, qs, s);
+  return launch_partial_t<KB, VB, D, false>(a, qs, s);
 }
 
 template <int KB, int D>
-hipError_t dispatch_v(const DecodeArgs& a, int vbits, int n_splits, int batch, float qs, hipStream_t s) {
+hipError_t dispatch_v(const DecodeArgs& a, int vbits, float qs, hipStream_t s) {
   switch (vbits) {
-    case 2: return launch_partial_m<KB, 2, D>(a, n_splits, batch, qs, s);
-    case 3: return launch_partial_m<KB, 3, D>(a, n_splits, batch, qs, s);
-    case 4: return launch_partial_m<KB, 4, D>(a, n_splits, batch, qs, s);
-    case 8: return launch_partial_m<KB, 8, D>(a, n_splits, batch, qs, s);
-    case 16: return launch_partial_m<KB, 16, D>(a, n_splits, batch, qs, s);
+    case 2: return launch_partial_m<KB, 2, D>(a, qs, s);
+    case 3: return launch_partial_m<KB, 3, D>(a, qs, s);
+    case 4: return launch_partial_m<KB, 4, D>(a, qs, s);
+    case 8: return launch_partial_m<KB, 8, D>(a, qs, s);
+    case 16: return launch_partial_m<KB, 16, D>(a, qs, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int D>
-hipError_t dispatch_k(const DecodeArgs& a, int kbits, int vbits, int n_splits, int batch, float qs, hipStream_t s) {
+hipError_t dispatch_k(const DecodeArgs& a, int kbits, int vbits, float qs, hipStream_t s) {
   switch (kbits) {
-    case 2: return dispatch_v<2, D>(a, vbits, n_splits, batch, qs, s);
-    case 3: return dispatch_v<3, D>(a, vbits, n_splits, batch, qs, s);
-    case 4: return dispatch_v<4, D>(a, vbits, n_splits, batch, qs, s);
-    case 8: return dispatch_v<8, D>(a, vbits, n_splits, batch, qs, s);
-    case 16: return dispatch_v<16, D>(a, vbits, n_splits, batch, qs, s);
+    case 2: return dispatch_v<2, D>(a, vbits, qs, s);
+    case 3: return dispatch_v<3, D>(a, vbits, qs, s);
+    case 4: return dispatch_v<4, D>(a, vbits, qs, s);
+    case 8: return dispatch_v<8, D>(a, vbits, qs, s);
+    case 16: return dispatch_v<16, D>(a, vbits, qs, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1408,40 +1524,46 @@ int waves_v(int vbits) {
 }
 
 template <int D, bool M16>
-hipError_t launch_mixed_t(const DecodeArgs& a, int n_splits, int batch, float qscale, hipStream_t s) {
-  if (a.batch != batch || n_splits % kXcds != 0) return hipErrorInvalidValue;
-  dim3 grid(static_cast<unsigned>(n_splits) * a.n_heads * batch);
-  hipLaunchKernelGGL((decode_partial_mixed_kernel<D, M16>), grid, dim3(64), 0, s, a, a.table, a.steal, qscale);
+hipError_t launch_multi_t(const DecodeArgs& a, float qscale, hipStream_t s) {
+  unsigned grid = 0;
+  for (int i = 0; i < a.n_segs; ++i) {
+    const DecodeSeg& sg = a.seg[i];
+    if (sg.n_splits % kXcds != 0 || sg.grid_start != static_cast<int>(grid)) return hipErrorInvalidValue;
+    grid += static_cast<unsigned>(sg.n_splits) * sg.n_heads * a.batch;
+  }
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL((decode_partial_multi_kernel<D, M16>), dim3(grid), dim3(64), 0, s, a, qscale);
   return hipGetLastError();
 }
 
 template <int KB, int VB, int D>
-hipError_t launch_kc_partial_t(const DecodeArgs& a, int n_splits, int batch, float qscale, hipStream_t s) {
-  if (a.batch != batch || n_splits % kXcds != 0) return hipErrorInvalidValue;
-  dim3 grid(static_cast<unsigned>(n_splits) * a.n_heads * batch);
-  hipLaunchKernelGGL((decode_partial_kc_kernel<KB, VB, D>), grid, dim3(64), 0, s, a, a.table, a.steal, qscale);
+hipError_t launch_kc_partial_t(const DecodeArgs& a, float qscale, hipStream_t s) {
+  const unsigned grid = single_grid(a);
+  if (grid == 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((decode_partial_kc_kernel<KB, VB, D>), dim3(grid), dim3(64), 0, s, a, a.seg[0].table,
+                     a.seg[0].steal, qscale);
   return hipGetLastError();
 }
 
 template <int KB, int D>
-hipError_t dispatch_kc_v(const DecodeArgs& a, int vbits, int n_splits, int batch, float qs, hipStream_t s) {
+hipError_t dispatch_kc_v(const DecodeArgs& a, int vbits, float qs, hipStream_t s) {
   switch (vbits) {
-    case 2: return launch_kc_partial_t<KB, 2, D>(a, n_splits, batch, qs, s);
-    case 3: return launch_kc_partial_t<KB, 3, D>(a, n_splits, batch, qs, s);
-    case 4: return launch_kc_partial_t<KB, 4, D>(a, n_splits, batch, qs, s);
-    case 8: return launch_kc_partial_t<KB, 8, D>(a, n_splits, batch, qs, s);
-    case 16: return launch_kc_partial_t<KB, 16, D>(a, n_splits, batch, qs, s);
+    case 2: return launch_kc_partial_t<KB, 2, D>(a, qs, s);
+    case 3: return launch_kc_partial_t<KB, 3, D>(a, qs, s);
+    case 4: return launch_kc_partial_t<KB, 4, D>(a, qs, s);
+    case 8: return launch_kc_partial_t<KB, 8, D>(a, qs, s);
+    case 16: return launch_kc_partial_t<KB, 16, D>(a, qs, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int D>
-hipError_t dispatch_kc_k(const DecodeArgs& a, int kbits, int vbits, int n_splits, int batch, float qs, hipStream_t s) {
+hipError_t dispatch_kc_k(const DecodeArgs& a, int kbits, int vbits, float qs, hipStream_t s) {
   switch (kbits) {
-    case 2: return dispatch_kc_v<2, D>(a, vbits, n_splits, batch, qs, s);
-    case 3: return dispatch_kc_v<3, D>(a, vbits, n_splits, batch, qs, s);
-    case 4: return dispatch_kc_v<4, D>(a, vbits, n_splits, batch, qs, s);
-    case 8: return dispatch_kc_v<8, D>(a, vbits, n_splits, batch, qs, s);
+    case 2: return dispatch_kc_v<2, D>(a, vbits, qs, s);
+    case 3: return dispatch_kc_v<3, D>(a, vbits, qs, s);
+    case 4: return dispatch_kc_v<4, D>(a, vbits, qs, s);
+    case 8: return dispatch_kc_v<8, D>(a, vbits, qs, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1485,18 +1607,17 @@ int decode_partial_waves_per_simd(int kbits, int vbits, int d, bool kc) {
   return d == 64 ? waves_k<64>(kbits, vbits) : waves_k<128>(kbits, vbits);
 }
 
-hipError_t launch_decode_partial(const DecodeArgs& a, int kbits, int vbits, int d, int n_splits,
-                                 int batch, hipStream_t s) {
-  if (n_splits == 0 || batch == 0 || a.n_heads == 0) return hipSuccess;
+hipError_t launch_decode_partial(const DecodeArgs& a, int kbits, int vbits, int d, hipStream_t s) {
+  if (a.n_segs != 1 || a.seg[0].n_splits == 0 || a.batch == 0 || a.seg[0].n_heads == 0) return hipSuccess;
   // q~ = (R q) * log2(e) / sqrt(d), with R's 1/sqrt(n) folded in.
   const float qscale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(a.had_block) * d));
   if (a.kc && kbits != 16) {
-    if (d == 128) return dispatch_kc_k<128>(a, kbits, vbits, n_splits, batch, qscale, s);
-    if (d == 64) return dispatch_kc_k<64>(a, kbits, vbits, n_splits, batch, qscale, s);
+    if (d == 128) return dispatch_kc_k<128>(a, kbits, vbits, qscale, s);
+    if (d == 64) return dispatch_kc_k<64>(a, kbits, vbits, qscale, s);
     return hipErrorInvalidValue;
   }
-  if (d == 128) return dispatch_k<128>(a, kbits, vbits, n_splits, batch, qscale, s);
-  if (d == 64) return dispatch_k<64>(a, kbits, vbits, n_splits, batch, qscale, s);
+  if (d == 128) return dispatch_k<128>(a, kbits, vbits, qscale, s);
+  if (d == 64) return dispatch_k<64>(a, kbits, vbits, qscale, s);
   return hipErrorInvalidValue;
 }
 
@@ -1504,16 +1625,19 @@ bool decode_partial_mixable(int kbits, int vbits, int d) {
   return (d == 64 || d == 128) && kbits >= 2 && kbits <= 4 && vbits >= 2 && vbits <= 4;
 }
 
-hipError_t launch_decode_partial_mixed(const DecodeArgs& a, int d, int n_splits, int batch, hipStream_t s) {
-  if (n_splits == 0 || batch == 0 || a.n_heads == 0) return hipSuccess;
-  if (a.kc) return hipErrorInvalidValue;
-  for (int i = 0; i < a.n_heads; ++i)
-    if (!decode_partial_mixable(a.pair[i] >> 4, a.pair[i] & 15, d)) return hipErrorInvalidValue;
+hipError_t launch_decode_partial_multi(const DecodeArgs& a, int d, hipStream_t s) {
+  if (a.batch == 0 || a.n_segs == 0) return hipSuccess;
+  if (a.kc || a.n_segs > kMaxLaunchSegs) return hipErrorInvalidValue;
+  for (int i = 0; i < a.n_segs; ++i)
+    for (int j = 0; j < a.seg[i].n_heads; ++j) {
+      const int e = a.seg[i].head_base + j;
+      if (e < 0 || e >= KVQ_MAX_KV_HEADS || !decode_partial_mixable(a.pair[e] >> 4, a.pair[e] & 15, d))
+        return hipErrorInvalidValue;
+    }
   const float qscale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(a.had_block) * d));
-  if (d == 128) return a.meta16 ? launch_mixed_t<128, true>(a, n_splits, batch, qscale, s)
-                                : launch_mixed_t<128, false>(a, n_splits, batch, qscale, s);
-  return a.meta16 ? launch_mixed_t<64, true>(a, n_splits, batch, qscale, s)
-                  : launch_mixed_t<64, false>(a, n_splits, batch, qscale, s);
+  if (d == 128) return a.meta16 ? launch_multi_t<128, true>(a, qscale, s) : launch_multi_t<128, false>(a, qscale, s);
+  if (d == 64) return a.meta16 ? launch_multi_t<64, true>(a, qscale, s) : launch_multi_t<64, false>(a, qscale, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode_merge(const MergeArgs& a, hipStream_t s) {

@@ -239,9 +239,51 @@ double split_simd_share(const kvq_segment& s) {
   return share;
 }
 
-int total_slots(const kvq_segment* segs, int n_segs, int batch, std::vector<SplitPlan>* plans) {
-  std::vector<SplitPlan> p(n_segs);
-  for (int i = 0; i < n_segs; ++i) p[i] = plan_splits(segs[i], batch);
+// KVQ_WINDOW_IN_MERGE=0: a short bf16 segment gets a partial launch of its
+// own instead of being attended to by the merge kernel.
+bool window_in_merge_enabled() {
+  const char* env = std::getenv("KVQ_WINDOW_IN_MERGE");
+  return !(env && env[0] == '0');
+}
+
+// A segment the merge kernel can attend to itself: 16-bit keys and values in
+// every head, at most kMergeWindowMax tokens.
+bool window_candidate(const kvq_segment& s) {
+  const kvq_layout& L = *s.layout;
+  if (L.key_per_channel || s.max_len < 1 || s.max_len > kvq::kMergeWindowMax) return false;
+  for (int h = 0; h < L.num_kv_heads; ++h)
+    if (L.bits_k[h] != 16 || L.bits_v[h] != 16) return false;
+  return true;
+}
+
+// The plan of one decode call, shared by the partial and merge calls (and the
+// workspace size): the splits of every segment, the segment the merge
+// attends to itself, and the segment whose split-0 waves leave q~ for it.
+struct CallPlan {
+  std::vector<SplitPlan> split;
+  int slots = 0;
+  int window = -1;
+  int q_writer = -1;
+};
+
+CallPlan plan_call(const kvq_segment* segs, int n_segs, int batch) {
+  CallPlan c;
+  c.split.resize(n_segs);
+  for (int i = 0; i < n_segs; ++i) c.split[i] = plan_splits(segs[i], batch);
+  // A short bf16 segment beside others: the merge kernel computes its
+  // attention from the rotated query one of the other launches leaves, so it
+  // needs no partial launch (its waves would need a whole SIMD each and wait
+  // for the low-precision waves to retire).
+  if (batch > 0 && n_segs > 1 && window_in_merge_enabled()) {
+    for (int i = 0; i < n_segs && c.window < 0; ++i)
+      if (window_candidate(segs[i])) c.window = i;
+    if (c.window >= 0) {
+      for (int i = 0; i < n_segs && c.q_writer < 0; ++i)
+        if (i != c.window && c.split[i].n_splits > 0) c.q_writer = i;
+      if (c.q_writer < 0) c.window = -1;
+      else c.split[c.window].n_splits = 0;
+    }
+  }
   // Several segments' launches run at once, and each was sized to fill one
   // resident round alone. The one holding most SIMDs gives up the others'
   // share (in whole groups of eight splits), so the small launches run beside
@@ -251,39 +293,40 @@ int total_slots(const kvq_segment* segs, int n_segs, int batch, std::vector<Spli
     int big = 0;
     double big_share = -1.0, all = 0.0;
     for (int i = 0; i < n_segs; ++i) {
-      const double sh = static_cast<double>(p[i].n_splits) * batch * split_simd_share(segs[i]);
+      const double sh = static_cast<double>(c.split[i].n_splits) * batch * split_simd_share(segs[i]);
       all += sh;
       if (sh > big_share) { big = i; big_share = sh; }
     }
     const double per_split = batch * split_simd_share(segs[big]);
     if (all > round && per_split > 0.0) {
       const int fit = static_cast<int>((round - (all - big_share)) / per_split) / 8 * 8;
-      p[big].n_splits = std::min(p[big].n_splits, std::max(fit, 8));
+      c.split[big].n_splits = std::min(c.split[big].n_splits, std::max(fit, 8));
     }
   }
-  int total = 0;
-  for (int i = 0; i < n_segs; ++i) {
-    if (plans) plans->push_back(p[i]);
-    total += p[i].n_splits;
-  }
-  return total;
+  for (int i = 0; i < n_segs; ++i) c.slots += c.split[i].n_splits;
+  return c;
 }
 
 // Workspace: the work-sharing counter region (KVQ_DECODE_COUNTER_BYTES at the
-// front, zero between calls), then partial o' [batch][hq][slots][d], then
-// partial (max, sum) [batch][hq][slots][2]. A call's counters are the first
-// words of the region: per segment [batch][hkv][splits / 8][2] (uint32);
-// slots is the sum of the segments' splits, so a call takes
-// slots / 8 * batch * hkv * 2 words. The region's place and size do not depend
-// on the split plan, so no call's partials ever land on any call's counters,
-// and one workspace serves calls of any plan.
+// front, zero between calls), then partial o' [batch][hq][slots][d], partial
+// (max, sum) [batch][hq][slots][2], and q~ [batch][hq][d] for a window
+// segment. A call's counters are the first words of the region: per segment
+// [batch][hkv][splits / 8][2] (uint32); slots is the sum of the segments'
+// splits, so a call takes slots / 8 * batch * hkv * 2 words. The region's
+// place and size do not depend on the split plan, so no call's partials ever
+// land on any call's counters, and one workspace serves calls of any plan.
 constexpr size_t kCounterBytes = KVQ_DECODE_COUNTER_BYTES;
-size_t partials_bytes(int batch, int hq, int d, int slots) {
-  if (slots == 0) slots = 1;
-  return static_cast<size_t>(batch) * hq * slots * (static_cast<size_t>(d) + 2) * sizeof(float);
-}
-size_t workspace_bytes(int batch, int hq, int d, int slots) {
-  return kCounterBytes + partials_bytes(batch, hq, d, slots);
+struct WsLayout {
+  size_t part_o, part_ml, qrot, total;
+};
+WsLayout ws_layout(int batch, int hq, int d, int slots) {
+  const size_t rows = static_cast<size_t>(batch) * hq, s1 = static_cast<size_t>(std::max(slots, 1));
+  WsLayout w;
+  w.part_o = kCounterBytes;
+  w.part_ml = w.part_o + rows * s1 * d * sizeof(float);
+  w.qrot = w.part_ml + rows * s1 * 2 * sizeof(float);
+  w.total = w.qrot + rows * d * sizeof(float);
+  return w;
 }
 // Counter words a call with this plan uses; more than the region holds sends
 // the call to the fixed order, which uses none.
@@ -832,7 +875,7 @@ kvq_status kvq_decode_workspace_bytes(const kvq_segment* segs, int32_t n_segs, i
   kvq_status st = check_segments(segs, n_segs, batch, "kvq_decode_workspace_bytes");
   if (st != KVQ_OK) return st;
   const kvq_layout& L = *segs[0].layout;
-  *bytes = workspace_bytes(batch, L.num_kv_heads * L.group, L.head_dim, total_slots(segs, n_segs, batch, nullptr));
+  *bytes = ws_layout(batch, L.num_kv_heads * L.group, L.head_dim, plan_call(segs, n_segs, batch).slots).total;
   return ok();
 }
 
@@ -864,92 +907,141 @@ static kvq_status decode_partial_impl(const kvq_segment* segs, int32_t n_segs, i
   if (reinterpret_cast<uintptr_t>(q) % 16 != 0) return fail(KVQ_ERR_ARG, "kvq_decode_partial: q not 16-byte aligned");
   const kvq_layout& L0 = *segs[0].layout;
   const int hq = L0.num_kv_heads * L0.group;
-  std::vector<SplitPlan> plans;
-  const int slots = total_slots(segs, n_segs, batch, &plans);
-  const size_t need = workspace_bytes(batch, hq, L0.head_dim, slots);
-  if (ws_bytes < need)
-    return fail(KVQ_ERR_WORKSPACE, "kvq_decode_partial: workspace %zu < %zu bytes", ws_bytes, need);
+  const int d = L0.head_dim;
+  const CallPlan plan = plan_call(segs, n_segs, batch);
+  const WsLayout wl = ws_layout(batch, hq, d, plan.slots);
+  if (ws_bytes < wl.total)
+    return fail(KVQ_ERR_WORKSPACE, "kvq_decode_partial: workspace %zu < %zu bytes", ws_bytes, wl.total);
   uint32_t* steal = static_cast<uint32_t*>(ws);
-  float* part_o = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kCounterBytes);
-  float* part_ml = part_o + static_cast<size_t>(batch) * hq * std::max(slots, 1) * L0.head_dim;
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
   const bool share_tail =
-      !deterministic_order() && counter_words(batch, L0.num_kv_heads, slots) * sizeof(uint32_t) <= kCounterBytes;
+      !deterministic_order() && counter_words(batch, L0.num_kv_heads, plan.slots) * sizeof(uint32_t) <= kCounterBytes;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+  kvq::DecodeArgs base{};
+  base.q = q;
+  base.q_bf16 = q_dtype == KVQ_BF16;
+  base.hkv = L0.num_kv_heads;
+  base.group = L0.group;
+  base.had_block = L0.had_block;
+  base.batch = batch;
+  base.total_slots = plan.slots;
+  base.share_tail = share_tail ? 1 : 0;
+  base.part_o = reinterpret_cast<float*>(wsb + wl.part_o);
+  base.part_ml = reinterpret_cast<float*>(wsb + wl.part_ml);
+  base.qrot = reinterpret_cast<float*>(wsb + wl.qrot);
+
+  std::vector<int> slot_base(n_segs, 0);
+  for (int i = 1; i < n_segs; ++i) slot_base[i] = slot_base[i - 1] + plan.split[i - 1].n_splits;
+  // segment i's part of a launch, over head entries [head_base, head_base + n_heads)
+  auto seg_desc = [&](int i, int head_base, int n_heads, int grid_start) {
+    const kvq_segment& sg = segs[i];
+    kvq::DecodeSeg ds{};
+    ds.pool = static_cast<const uint8_t*>(sg.pool);
+    ds.pool_blocks = sg.pool_blocks;
+    ds.block_bytes = sg.layout->block_bytes;
+    ds.table = sg.block_table;
+    ds.table_stride = sg.table_stride;
+    ds.seq_lens = sg.seq_lens;
+    ds.steal = steal + static_cast<size_t>(slot_base[i] / 8) * batch * L0.num_kv_heads * 2;
+    ds.slot_base = slot_base[i];
+    ds.n_splits = plan.split[i].n_splits;
+    ds.grid_start = grid_start;
+    ds.n_heads = n_heads;
+    ds.head_base = head_base;
+    ds.write_q = i == plan.q_writer && plan.window >= 0;
+    return ds;
+  };
   struct Launch {
     kvq::DecodeArgs a;
-    int kbits, vbits, d, n_splits;
-    bool mixed;
+    int kbits, vbits;
+    bool multi;
     int64_t bytes;  // code bytes the launch reads per sequence (orders the launches)
   };
   std::vector<Launch> launches;
-  int slot_base = 0;
+  auto add_head = [&](kvq::DecodeArgs& a, const kvq_layout& L, int h, int e) {
+    a.heads[e] = h;
+    a.k_off[e] = L.k_off[h];
+    a.v_off[e] = L.v_off[h];
+    a.pair[e] = static_cast<uint8_t>(L.bits_k[h] << 4 | L.bits_v[h]);
+  };
   const bool allow_mixed = mixed_launch_enabled();
-  for (int i = 0; i < n_segs; ++i) {
-    const kvq_segment& sg = segs[i];
-    const kvq_layout& L = *sg.layout;
-    const SplitPlan& p = plans[i];
-    if (p.n_splits > 0) {
-      bool done[KVQ_MAX_KV_HEADS] = {};
-      // Heads of two or more mixable formats go into one multi-format launch;
-      // the rest get one launch per format.
-      bool mixable[KVQ_MAX_KV_HEADS] = {};
-      int first_pair = -1;
-      bool several = false;
+  auto mixable = [&](const kvq_layout& L, int h) {
+    return allow_mixed && !L.key_per_channel && kvq::decode_partial_mixable(L.bits_k[h], L.bits_v[h], d);
+  };
+  // Heads of 2-, 3- and 4-bit pairs, over every segment (of one metadata
+  // width), share one multi-format launch when they make more than one
+  // (segment, pair) group; the rest get one launch per (segment, pair).
+  int meta16_multi = -1;  // the metadata width whose heads go into the multi launch
+  {
+    int groups = 0, segs_in = 0, entries = 0, first_meta = -1;
+    for (int i = 0; i < n_segs; ++i) {
+      const kvq_layout& L = *segs[i].layout;
+      if (plan.split[i].n_splits == 0) continue;
+      if (first_meta < 0) first_meta = L.meta_fp16;
+      if (L.meta_fp16 != first_meta) continue;
+      int pairs[KVQ_MAX_KV_HEADS], np = 0, here = 0;
       for (int h = 0; h < L.num_kv_heads; ++h) {
-        mixable[h] = allow_mixed && !L.key_per_channel &&
-                     kvq::decode_partial_mixable(L.bits_k[h], L.bits_v[h], L.head_dim);
-        if (!mixable[h]) continue;
+        if (!mixable(L, h)) continue;
+        ++here;
         const int pr = L.bits_k[h] << 4 | L.bits_v[h];
-        if (first_pair < 0) first_pair = pr;
-        else if (pr != first_pair) several = true;
+        bool seen = false;
+        for (int k = 0; k < np; ++k) seen = seen || pairs[k] == pr;
+        if (!seen) pairs[np++] = pr;
       }
-      for (int h0 = 0; h0 < L.num_kv_heads; ++h0) {
-        if (done[h0]) continue;
-        const bool mixed = several && mixable[h0];
-        kvq::DecodeArgs a{};
-        a.pool = static_cast<const uint8_t*>(sg.pool);
-        a.pool_blocks = sg.pool_blocks;
-        a.block_bytes = L.block_bytes;
-        a.table = sg.block_table;
-        a.table_stride = sg.table_stride;
-        a.seq_lens = sg.seq_lens;
-        a.q = q;
-        a.q_bf16 = q_dtype == KVQ_BF16;
-        a.meta16 = L.meta_fp16;
-        a.kc = L.key_per_channel;
-        a.hkv = L.num_kv_heads;
-        a.group = L.group;
-        a.had_block = L.had_block;
-        a.batch = batch;
-        a.steal = steal + static_cast<size_t>(slot_base / 8) * batch * L.num_kv_heads * 2;
-        a.share_tail = share_tail ? 1 : 0;
-        a.slot_base = slot_base;
-        a.total_slots = slots;
-        a.part_o = part_o;
-        a.part_ml = part_ml;
-        for (int h = h0; h < L.num_kv_heads; ++h) {
-          const bool same = mixed ? mixable[h] : L.bits_k[h] == L.bits_k[h0] && L.bits_v[h] == L.bits_v[h0];
-          if (!done[h] && same) {
-            a.heads[a.n_heads] = h;
-            a.k_off[a.n_heads] = L.k_off[h];
-            a.v_off[a.n_heads] = L.v_off[h];
-            a.pair[a.n_heads] = static_cast<uint8_t>(L.bits_k[h] << 4 | L.bits_v[h]);
-            ++a.n_heads;
-            done[h] = true;
-          }
-        }
-        int64_t row_bits = 0;
-        for (int j = 0; j < a.n_heads; ++j) row_bits += L.bits_k[a.heads[j]] + L.bits_v[a.heads[j]];
-        launches.push_back({a, L.bits_k[h0], L.bits_v[h0], L.head_dim, p.n_splits, mixed,
-                            row_bits * L.head_dim / 8 * std::max(sg.max_len, 0)});
-      }
+      if (here) ++segs_in;
+      groups += np;
+      entries += here;
     }
-    slot_base += p.n_splits;
+    if (groups >= 2 && segs_in <= kvq::kMaxLaunchSegs && entries <= KVQ_MAX_KV_HEADS) meta16_multi = first_meta;
+  }
+  if (meta16_multi >= 0) {
+    Launch l{base, 0, 0, true, 0};
+    int e = 0, grid = 0;
+    for (int i = 0; i < n_segs; ++i) {
+      const kvq_layout& L = *segs[i].layout;
+      if (plan.split[i].n_splits == 0 || L.meta_fp16 != meta16_multi) continue;
+      const int e0 = e;
+      for (int h = 0; h < L.num_kv_heads; ++h)
+        if (mixable(L, h)) {
+          add_head(l.a, L, h, e++);
+          l.bytes += static_cast<int64_t>(L.bits_k[h] + L.bits_v[h]) * d / 8 * std::max(segs[i].max_len, 0);
+        }
+      if (e == e0) continue;
+      l.a.seg[l.a.n_segs++] = seg_desc(i, e0, e - e0, grid);
+      grid += plan.split[i].n_splits * (e - e0) * batch;
+    }
+    l.a.meta16 = meta16_multi;
+    launches.push_back(l);
+  }
+  for (int i = 0; i < n_segs; ++i) {
+    const kvq_layout& L = *segs[i].layout;
+    if (plan.split[i].n_splits == 0) continue;
+    const bool in_multi = meta16_multi >= 0 && L.meta_fp16 == meta16_multi;
+    bool done[KVQ_MAX_KV_HEADS] = {};
+    for (int h0 = 0; h0 < L.num_kv_heads; ++h0) {
+      if (done[h0] || (in_multi && mixable(L, h0))) continue;
+      Launch l{base, L.bits_k[h0], L.bits_v[h0], false, 0};
+      l.a.meta16 = L.meta_fp16;
+      l.a.kc = L.key_per_channel;
+      int e = 0;
+      for (int h = h0; h < L.num_kv_heads; ++h) {
+        if (!done[h] && L.bits_k[h] == L.bits_k[h0] && L.bits_v[h] == L.bits_v[h0] && !(in_multi && mixable(L, h))) {
+          add_head(l.a, L, h, e++);
+          done[h] = true;
+        }
+      }
+      l.a.seg[0] = seg_desc(i, 0, e, 0);
+      l.a.n_segs = 1;
+      l.bytes = static_cast<int64_t>(e) * (L.bits_k[h0] + L.bits_v[h0]) * d / 8 * std::max(segs[i].max_len, 0);
+      launches.push_back(l);
+    }
   }
   auto launch = [&](const Launch& l, hipStream_t st) {
-    return l.mixed ? kvq::launch_decode_partial_mixed(l.a, l.d, l.n_splits, batch, st)
-                   : kvq::launch_decode_partial(l.a, l.kbits, l.vbits, l.d, l.n_splits, batch, st);
+    return l.multi ? kvq::launch_decode_partial_multi(l.a, d, st)
+                   : kvq::launch_decode_partial(l.a, l.kbits, l.vbits, d, st);
   };
+  if (launches.empty()) return ok();
   if (launches.size() == 1) return device_status(launch(launches[0], s), "kvq_decode_partial launch");
   if (serial) {
     for (const Launch& l : launches) {
@@ -958,11 +1050,11 @@ static kvq_status decode_partial_impl(const kvq_segment* segs, int32_t n_segs, i
     }
     return ok();
   }
-  // Several launches (segments, and width groups that cannot share a launch)
-  // run concurrently: the largest on the caller's stream, which starts it
-  // first, the others on side streams forked from it and joined back before
-  // the call returns. (One after another on one stream is slower: the small
-  // launches of a short segment are latency-bound and then add up.)
+  // Several launches (width groups that cannot share a launch) run
+  // concurrently: the largest on the caller's stream, which starts it first,
+  // the others on side streams forked from it and joined back before the call
+  // returns. (One after another on one stream is slower: small launches are
+  // latency-bound and then add up.)
   std::stable_sort(launches.begin(), launches.end(),
                    [](const Launch& x, const Launch& y) { return x.bytes > y.bytes; });
   std::lock_guard<std::mutex> lock(g_side_mutex);
@@ -1042,21 +1134,39 @@ kvq_status kvq_decode_merge(const kvq_segment* segs, int32_t n_segs, int32_t bat
   if (!out || !ws) return fail(KVQ_ERR_ARG, "kvq_decode_merge: null output or workspace");
   const kvq_layout& L0 = *segs[0].layout;
   const int hq = L0.num_kv_heads * L0.group;
-  const int slots = total_slots(segs, n_segs, batch, nullptr);
-  const size_t need = workspace_bytes(batch, hq, L0.head_dim, slots);
-  if (ws_bytes < need) return fail(KVQ_ERR_WORKSPACE, "kvq_decode_merge: workspace %zu < %zu bytes", ws_bytes, need);
+  const CallPlan plan = plan_call(segs, n_segs, batch);
+  const WsLayout wl = ws_layout(batch, hq, L0.head_dim, plan.slots);
+  if (ws_bytes < wl.total)
+    return fail(KVQ_ERR_WORKSPACE, "kvq_decode_merge: workspace %zu < %zu bytes", ws_bytes, wl.total);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   // With no split at all the merge kernel still runs and writes zero rows
   // (no memset node, so the call stays safe to capture in a graph).
+  const uint8_t* wsb = static_cast<const uint8_t*>(ws);
   kvq::MergeArgs a{};
-  a.part_o = reinterpret_cast<const float*>(static_cast<const uint8_t*>(ws) + kCounterBytes);
-  a.part_ml = a.part_o + static_cast<size_t>(batch) * hq * std::max(slots, 1) * L0.head_dim;
+  a.part_o = reinterpret_cast<const float*>(wsb + wl.part_o);
+  a.part_ml = reinterpret_cast<const float*>(wsb + wl.part_ml);
+  a.qrot = reinterpret_cast<const float*>(wsb + wl.qrot);
   a.batch = batch;
   a.hq = hq;
   a.d = L0.head_dim;
   a.had_block = L0.had_block;
-  a.total_slots = slots;
+  a.total_slots = plan.slots;
+  a.group = L0.group;
   a.out = out;
+  if (plan.window >= 0) {
+    const kvq_segment& w = segs[plan.window];
+    a.win.pool = static_cast<const uint8_t*>(w.pool);
+    a.win.pool_blocks = w.pool_blocks;
+    a.win.block_bytes = w.layout->block_bytes;
+    a.win.table = w.block_table;
+    a.win.table_stride = w.table_stride;
+    a.win.seq_lens = w.seq_lens;
+    a.win.max_len = w.max_len;
+    for (int h = 0; h < w.layout->num_kv_heads; ++h) {
+      a.win.k_off[h] = w.layout->k_off[h];
+      a.win.v_off[h] = w.layout->v_off[h];
+    }
+  }
   return device_status(kvq::launch_decode_merge(a, s), "kvq_decode_merge launch");
 }
 
@@ -1118,8 +1228,7 @@ kvq_status kvq_decode_attn_noalloc(const kvq_segment* segs, int32_t n_segs, int3
   if (batch == 0) return ok();
   if (!q || !out) return fail(KVQ_ERR_ARG, "%s: null q or output", who);
   const kvq_layout& L0 = *segs[0].layout;
-  const size_t need =
-      workspace_bytes(batch, L0.num_kv_heads * L0.group, L0.head_dim, total_slots(segs, n_segs, batch, nullptr));
+  const size_t need = ws_layout(batch, L0.num_kv_heads * L0.group, L0.head_dim, plan_call(segs, n_segs, batch).slots).total;
   if (need > kNoallocScratchBytes)
     return fail(KVQ_ERR_WORKSPACE, "%s: this call needs %zu bytes of scratch, more than the fixed %zu", who, need,
                 kNoallocScratchBytes);

@@ -43,32 +43,49 @@ struct DequantArgs {
   float* out;  // [n][hkv][d]
 };
 
-// One partial-decode launch: one segment, the heads of that segment whose
-// (K bits, V bits) pair is (kbits, vbits).
-struct DecodeArgs {
+// One segment's share of a partial-decode launch: its pool, table and
+// lengths, the heads of it the launch covers (entries head_base ..
+// head_base + n_heads - 1 of DecodeArgs' head arrays), its splits, and where
+// its workgroups start in the launch's one-dimensional grid.
+constexpr int kMaxLaunchSegs = 4;
+struct DecodeSeg {
   const uint8_t* pool;
   int64_t pool_blocks;
   int64_t block_bytes;
   const int32_t* table;
   int32_t table_stride;
   const int32_t* seq_lens;
+  uint32_t* steal;     // [batch][hkv][splits / 8][2] work-sharing counters of this segment (zero between calls)
+  int32_t slot_base;   // first split slot of this segment
+  int32_t n_splits;    // splits per (sequence, KV head), a multiple of 8
+  int32_t grid_start;  // first workgroup of this segment (a multiple of 8)
+  int32_t n_heads;
+  int32_t head_base;
+  int32_t write_q;     // 1: the waves of split 0 write their unit's q~ to qrot
+};
+
+// One partial-decode launch over the listed heads of one or more segments.
+// A single-format launch has one segment whose heads all share (kbits, vbits);
+// the multi-format launch takes heads of 2-, 3- and 4-bit pairs from several
+// segments (pair[i] names head entry i's widths).
+struct DecodeArgs {
   const void* q;       // [batch][hkv*group][d]
   int32_t q_bf16;
   int32_t meta16;      // 1: float16 {s, mn} (4 bytes per row)
   int32_t kc;          // 1: keys quantized per channel over each block (decode_partial_kc_kernel)
   int32_t hkv, group, had_block;
-  int32_t batch;       // sequences (the grid covers batch x n_heads units)
-  int32_t slot_base;   // first split slot of this segment
-  int32_t total_slots; // split slots over all segments
-  uint32_t* steal;     // [batch][hkv][2] work-sharing counters of this segment (zero between calls)
+  int32_t batch;
+  int32_t total_slots; // split slots over all segments of the call
   int32_t share_tail;  // 1: most of each unit's groups go to whichever wave is free; 0: fixed order
-  int32_t n_heads;
+  int32_t n_segs;
+  DecodeSeg seg[kMaxLaunchSegs];
   int32_t heads[KVQ_MAX_KV_HEADS];
   int64_t k_off[KVQ_MAX_KV_HEADS];
   int64_t v_off[KVQ_MAX_KV_HEADS];
-  uint8_t pair[KVQ_MAX_KV_HEADS];  // (key bits << 4) | value bits per listed head (multi-format launch)
+  uint8_t pair[KVQ_MAX_KV_HEADS];  // (key bits << 4) | value bits per head entry
   float* part_o;       // [batch][hq][total_slots][d]
   float* part_ml;      // [batch][hq][total_slots][2]  (running max in log2 units, sum)
+  float* qrot;         // [batch][hq][d]: q~ = (R q) log2(e) / sqrt(d), for a window segment the merge computes
 };
 
 // Distortion calibration: rows [rows][d] of fp32 or bf16, rotated and
@@ -104,11 +121,27 @@ struct RequantArgs {
   int32_t moves[kRequantMaxSeqs][4];   // win_slot, mid_slot, demote_slot, low_slot
 };
 
+// A short bf16 segment whose attention the merge kernel computes itself
+// (every head 16-bit keys and values), from the q~ the partial launch left.
+struct MergeWindow {
+  const uint8_t* pool;     // null: no such segment
+  int64_t pool_blocks;
+  int64_t block_bytes;
+  const int32_t* table;
+  int32_t table_stride;
+  const int32_t* seq_lens;
+  int32_t max_len;
+  int64_t k_off[KVQ_MAX_KV_HEADS];
+  int64_t v_off[KVQ_MAX_KV_HEADS];
+};
+
 struct MergeArgs {
   const float* part_o;
   const float* part_ml;
-  int32_t batch, hq, d, had_block, total_slots;
+  const float* qrot;
+  int32_t batch, hq, d, had_block, total_slots, group;
   float* out;  // [batch][hq][d]
+  MergeWindow win;
 };
 
 // Launchers return hipSuccess or the launch error; they never synchronise.
@@ -116,8 +149,8 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 // Per-channel keys of whole blocks (a.bits[0] < 16, n_new a multiple of 16).
 hipError_t launch_append_kc(const AppendArgs& a, hipStream_t s);
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t s);
-hipError_t launch_decode_partial(const DecodeArgs& a, int kbits, int vbits, int d, int n_splits,
-                                 int batch, hipStream_t s);
+// One segment (a.seg[0], a.n_segs = 1) whose heads all have widths (kbits, vbits).
+hipError_t launch_decode_partial(const DecodeArgs& a, int kbits, int vbits, int d, hipStream_t s);
 hipError_t launch_decode_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_zero_words(uint32_t* p, size_t n_words, hipStream_t s);
 // Zeroes out[], accumulates the squared errors, then divides by rows * d.
@@ -130,9 +163,12 @@ int decode_partial_waves_per_simd(int kbits, int vbits, int d, bool kc);
 // Whether heads of this format can share a multi-format launch (2-, 3- and
 // 4-bit keys and values, head_dim 64 or 128, per-token keys).
 bool decode_partial_mixable(int kbits, int vbits, int d);
-// One launch over heads of several formats: a.pair[i] names head i's widths,
-// every pair mixable. Same grid, partials and counters as launch_decode_partial.
-hipError_t launch_decode_partial_mixed(const DecodeArgs& a, int d, int n_splits, int batch, hipStream_t s);
+// One launch over heads of several formats and segments: a.pair[i] names
+// head entry i's widths, every pair mixable; each segment's workgroups are
+// a.seg[s].n_splits * n_heads * batch, from a.seg[s].grid_start.
+hipError_t launch_decode_partial_multi(const DecodeArgs& a, int d, hipStream_t s);
+// Window segments the merge can take: up to this many tokens.
+constexpr int kMergeWindowMax = 512;
 
 // Read-bandwidth references (measurement only): a streaming read of `bytes`
 // by `waves` waves, and the partial decode kernel's load pattern over one

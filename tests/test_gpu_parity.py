@@ -498,6 +498,39 @@ def test_workspace_reused_across_split_plans(monkeypatch):
     assert np.all(head == 0)
 
 
+@pytest.mark.parametrize("mid_bits", [(4, 4), (3, 2)])
+def test_window_segment_attended_in_the_merge(monkeypatch, mid_bits):
+    """A short bf16 segment beside quantized ones is attended to by the merge kernel (from the rotated
+    query the partial launch leaves), and the quantized segments share one launch. Ragged lengths, an
+    empty window for one sequence and an empty quantized segment for another; against the oracle, and
+    against a partial launch of the window's own (KVQ_WINDOW_IN_MERGE=0)."""
+    lens_w, lens_a, lens_b = [128, 0, 37], [1500, 700, 90], [3000, 16, 0]
+    Lw, layw, cw, rw, tw, _, _ = build_case(128, 32, 4, [16, 16], [16, 16], lens_w, seed=91)
+    La, laya, ca, ra, ta, _, _ = build_case(128, 32, 4, [mid_bits[0]] * 2, [mid_bits[1]] * 2, lens_a, seed=92)
+    Lb, layb, cb, rb, tb, _, _ = build_case(128, 32, 4, [2, 2], [2, 2], lens_b, seed=93)
+    q = synth.bf16_round(np.random.default_rng(94).standard_normal((3, 8, 128)).astype(np.float32))
+    qt = torch.from_numpy(q).to(T.DEV).bfloat16()
+    expect = O.decode_attention([(layw, rw, tw, np.array(lens_w)), (laya, ra, ta, np.array(lens_a)),
+                                 (layb, rb, tb, np.array(lens_b))], q.astype(np.float64))
+    for order in ((0, 1, 2), (2, 0, 1)):
+        segs = [[cw.segment(lens_w), ca.segment(lens_a), cb.segment(lens_b)][i] for i in order]
+        monkeypatch.delenv("KVQ_WINDOW_IN_MERGE", raising=False)
+        folded = kvq.kvq_decode_attn(segs, qt).cpu().numpy()
+        assert T.max_rel_err(folded, expect) <= T.ATTN_TOL
+        monkeypatch.setenv("KVQ_WINDOW_IN_MERGE", "0")
+        launched = kvq.kvq_decode_attn(segs, qt).cpu().numpy()
+        assert T.max_rel_err(launched, expect) <= T.ATTN_TOL
+        assert T.rel(folded, launched) < 1e-5
+    # a window longer than the merge takes (513 tokens) keeps its own launch
+    monkeypatch.delenv("KVQ_WINDOW_IN_MERGE", raising=False)
+    lens_l = [513, 200, 1]
+    Ll, layl, cl, rl, tl, _, _ = build_case(128, 32, 4, [16, 16], [16, 16], lens_l, seed=95)
+    out = kvq.kvq_decode_attn([cl.segment(lens_l), ca.segment(lens_a)], qt).cpu().numpy()
+    ref = O.decode_attention([(layl, rl, tl, np.array(lens_l)), (laya, ra, ta, np.array(lens_a))],
+                             q.astype(np.float64))
+    assert T.max_rel_err(out, ref) <= T.ATTN_TOL
+
+
 def test_measurement_reads_run_over_a_cache():
     """The two read references of the benchmark run over a real cache and buffer (they only read)."""
     lens = [3000, 37]

@@ -252,9 +252,10 @@ def test_decode_argument_checks_need_no_device():
     n = ctypes.c_size_t(0)
     assert lib.kvq_decode_workspace_bytes(segs, 1, 16, ctypes.byref(n)) == kvq.KVQ_OK
     assert n.value > 16 * 32 * 130 * 4
-    # the fixed counter area, then partials for every split slot (a multiple of 8 slots)
+    # the fixed counter area, then partials for every split slot (a multiple of 8 slots), then one
+    # rotated query row per query head
     per_slot = 16 * 32 * 130 * 4
-    part = n.value - kvq.KVQ_DECODE_COUNTER_BYTES
+    part = n.value - kvq.KVQ_DECODE_COUNTER_BYTES - 16 * 32 * 128 * 4
     assert part % per_slot == 0 and (part // per_slot) % 8 == 0
     # the counters the plan uses (two words per sequence, KV head and group of 8 splits) fit the area
     assert (part // per_slot) // 8 * 16 * 8 * 2 * 4 <= kvq.KVQ_DECODE_COUNTER_BYTES
