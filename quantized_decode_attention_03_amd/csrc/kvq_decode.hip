@@ -1156,6 +1156,14 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, int si, int L
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         load_next(gbuf[(j + DEPTH) % NB]);
+        // Of two waves on a SIMD the older is issued first, so one runs up to
+        // twice the other's pace, and when the shared tail runs dry the slow
+        // wave still has its prefetched groups to finish. Raising each wave's
+        // issue priority on every other group (waves out of step by their
+        // split) lets the two take turns, which narrows both the spread of
+        // groups per wave and of the waves' end times.
+        if ((rpos + split) & 1) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
         if (gbuf[j].gid < NG) compute(gbuf[j]);
       }
       if (gbuf[0].gid >= NG) break;
