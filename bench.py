@@ -127,6 +127,29 @@ def summarize_trace(trace_csv):
     return "\n".join(out) + "\n"
 
 
+def summarize_counters(csv_paths, match):
+    """Mean per dispatch of every counter in rocprofv3 --pmc CSVs, for kernels whose name contains `match`."""
+    vals, names = {}, set()
+    for path in csv_paths:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if match not in r["Kernel_Name"]:
+                    continue
+                m = re.search(r"(\w+_kernel(<[^>]*>)?)", r["Kernel_Name"])
+                short = m.group(1) if m else r["Kernel_Name"]
+                key = (short, int(r["Grid_Size"]))
+                vals.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+                names.add(r["Counter_Name"])
+    names = sorted(names)
+    out = ["| kernel | grid threads | dispatches | " + " | ".join(names) + " |",
+           "|---|---|---|" + "---|" * len(names)]
+    for (short, grid), cnt in sorted(vals.items()):
+        n = max(len(v) for v in cnt.values())
+        out.append(f"| {short} | {grid} | {n} | " +
+                   " | ".join(f"{np.mean(cnt[c]):.4g}" if c in cnt else "-" for c in names) + " |")
+    return "\n".join(out) + "\n"
+
+
 def bytes_per_layer():
     """Algorithmic HBM bytes of the partial decode kernel for one layer."""
     row = D * BITS_K // 8 + D * BITS_V // 8 + 16   # codes K + V + fp32 {s, mn} x 2 per token-head
@@ -233,6 +256,18 @@ def make_pool(kvq, torch, dev, L, batch, tokens, seed):
             torch.from_numpy(table_np).to(dev))
 
 
+def window_in_merge():
+    """Whether the library attends to a short bf16 segment inside the merge kernel (its default)."""
+    return os.environ.get("KVQ_WINDOW_IN_MERGE", "1") != "0"
+
+
+def long_kernel_label():
+    if window_in_merge():
+        return ("decode_partial_multi_kernel<128> (the 4-bit and 2-bit segments, one launch; the bf16 window "
+                "is read by decode_merge_kernel and its bytes are not counted here)")
+    return "decode_partial_multi_kernel<128> (4-bit and 2-bit segments) + decode_partial_kernel<16,16,128>"
+
+
 def synth_mod():
     from quantized_decode_attention_03_amd import synth
     return synth
@@ -267,7 +302,9 @@ def build_decode_layers(args, kvq, torch, dev):
                               "head_dim 128, per-head K/V bits from kvq_plan_bits (ladder {2,3,4,8}, average 3, "
                               "beta_K 3.6, beta_V 5.3), hadamard 128",
                   "layers": args.layers, "batch": batch, "ctx": tokens}
-        return layers, config, batch, total_bytes / args.layers, "decode_partial_kernel (per (K,V) bit pair)"
+        return layers, config, batch, total_bytes / args.layers, (
+            "decode_partial_multi_kernel<128> (the 2/3/4-bit heads of a layer, one launch) + "
+            "decode_partial_kernel<8,*,128> beside it for the layers with an 8-bit head")
     if args.workload == "long131k":
         batch, tokens, window = 1, 131072, 128
         cls = kvq.kvq_logquant_classes(tokens, window)
@@ -284,7 +321,8 @@ def build_decode_layers(args, kvq, torch, dev):
                                         k[:, idx_all[c]].contiguous(), v[:, idx_all[c]].contiguous())
                 segs.append((L, pool, table, torch.full((batch,), counts[c], dtype=torch.int32, device=dev),
                              counts[c]))
-                total_bytes += decode_bytes(batch, counts[c], [bits] * HKV, [bits] * HKV)
+                if bits != 16 or not window_in_merge():
+                    total_bytes += decode_bytes(batch, counts[c], [bits] * HKV, [bits] * HKV)
             # the new token goes into the bf16 window (its last slot is rewritten each step)
             layers.append({"segs": segs, "q": q, "app": 0, "new_k": k[:, -1:].contiguous(),
                            "new_v": v[:, -1:].contiguous(), "pos": counts[0] - 1})
@@ -293,7 +331,7 @@ def build_decode_layers(args, kvq, torch, dev):
                               "hadamard 32; segments: bf16 window 128, log-spaced 4-bit subset 1280, 2-bit 129664; "
                               "layers back to back (each layer's cache evicted from the MALL by the others)",
                   "layers": args.layers, "batch": batch, "ctx": tokens}
-        return layers, config, batch, total_bytes / args.layers, "decode_partial_kernel (3 segments)"
+        return layers, config, batch, total_bytes / args.layers, long_kernel_label()
     # default: Llama-3-8B-shaped 32k decode (bf16_32k: the same shape with 16-bit rows, the unquantized
     # baseline the 4-bit cache is compared with)
     batch, tokens = B, T
@@ -588,7 +626,8 @@ def run_long_dynamic(args, torch, dev, kvq):
             kvq.kvq_quantize_append(L, pool, table, torch.zeros(batch, dtype=torch.int32, device=dev),
                                     k[:, idx_all[c]].contiguous(), v[:, idx_all[c]].contiguous())
             segs.append(kvq.Segment(L, pool, table, lens[c], caps[c]))
-            total_bytes += decode_bytes(batch, counts[c], [bits] * HKV, [bits] * HKV)
+            if bits != 16 or not window_in_merge():
+                total_bytes += decode_bytes(batch, counts[c], [bits] * HKV, [bits] * HKV)
         layers.append({"segs": segs, "q": q, "new_k": k[:, tokens:].contiguous(), "new_v": v[:, tokens:].contiguous()})
         del k, v
     st = kvq.LogQuantStates(batch, window, cap_mid=caps[1])
@@ -653,7 +692,7 @@ def run_long_dynamic(args, torch, dev, kvq):
                    "layers": args.layers, "batch": batch, "ctx": tokens},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "decode_partial_kernel (3 segments)", "avg_us": round(part_us, 3),
+                     "kernel": long_kernel_label(), "avg_us": round(part_us, 3),
                      "bytes_per_launch": int(layer_bytes)},
         "update_us_per_layer": round(upd_us, 3),
         "final_state": {"total": int(st.states[0].total), "n_mid": int(st.states[0].n_mid),
@@ -732,12 +771,19 @@ def main():
                     help="print the traffic summary of two counter passes and exit")
     ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
                     help="print per-kernel durations from a rocprofv3 kernel trace and exit")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="COUNTER_CSV",
+                    help="print per-dispatch means of the counters in rocprofv3 --pmc CSVs (kernels matching "
+                         "--match) and exit")
+    ap.add_argument("--match", default="kvq::", help="kernel-name filter for --summarize-counters")
     args = ap.parse_args()
     if args.summarize_pmc:
         sys.stdout.write(summarize_pmc(*args.summarize_pmc))
         return
     if args.summarize_trace:
         sys.stdout.write(summarize_trace(args.summarize_trace))
+        return
+    if args.summarize_counters:
+        sys.stdout.write(summarize_counters(args.summarize_counters, args.match))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
