@@ -443,23 +443,28 @@ def run_decode(args, torch, dev, kvq):
     # plan), over the layers in turn so no layer's pages are still in the 256 MB cache in front of HBM
     pattern_gbs = None
     try:
-        seg0 = seg_objs[0][0]
+        def seg_bytes_of(sg):
+            if sg.layout.key_per_channel:
+                return layer_bytes - batch * HKV * G * D * 2
+            return decode_bytes(batch, sg.max_len, list(sg.layout.bits_k[:HKV]), list(sg.layout.bits_v[:HKV]),
+                                meta=4 if sg.layout.meta_fp16 else 8)
+        # the segment holding most of a layer's bytes (the 2-bit one at long context)
+        si = max(range(len(seg_objs[0])), key=lambda i: seg_bytes_of(seg_objs[0][i]))
+        seg0 = seg_objs[0][si]
         sink = torch.empty(1 << 20, dtype=torch.int32, device=dev)
-        kvq.kvq_measure_read_paged(seg0, batch, sink)
+        per_layer = [segs[si] for segs in seg_objs]
+        kvq.kvq_measure_read_paged(per_layer, batch, sink)
+        # one library call launches the layers' reads back to back, so the two events span GPU work only
+        # (timed one launch at a time, the host's enqueue of each call falls inside the interval)
         pat_ms = []
-        for r in range(2 * len(seg_objs)):
-            sg = seg_objs[r % len(seg_objs)][0]
+        for _ in range(3):
             p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             p0.record()
-            kvq.kvq_measure_read_paged(sg, batch, sink)
+            kvq.kvq_measure_read_paged(per_layer, batch, sink)
             p1.record()
             torch.cuda.synchronize()
-            pat_ms.append(p0.elapsed_time(p1))
-        seg_bytes = decode_bytes(batch, seg0.max_len, list(seg0.layout.bits_k[:HKV]), list(seg0.layout.bits_v[:HKV]),
-                                 meta=4 if seg0.layout.meta_fp16 else 8)
-        if seg0.layout.key_per_channel:
-            seg_bytes = layer_bytes - batch * HKV * G * D * 2
-        pattern_gbs = seg_bytes / (float(np.median(pat_ms)) * 1e-3) / 1e9
+            pat_ms.append(p0.elapsed_time(p1) / len(per_layer))
+        pattern_gbs = seg_bytes_of(seg0) / (float(np.median(pat_ms)) * 1e-3) / 1e9
     except kvq.KvqError:  # a layout outside what the probe covers (16-bit rows, 8-bit codes at head_dim 128)
         pass
     part_ms = [a.elapsed_time(b) for a, b in zip(ev_a, ev_b)]

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 4
+#define KVQ_ABI_VERSION 5
 #define KVQ_MAX_KV_HEADS 64
 #define KVQ_BLOCK_TOKENS 16
 
@@ -478,21 +478,26 @@ kvq_status kvq_decode_merge(const kvq_segment* segs, int32_t n_segs, int32_t bat
  * 16-byte aligned) once, the waves sweeping adjacent 8 KiB chunks, and each
  * wave writes one word to sink (device, sink_words >= 2048).
  *
- * kvq_measure_read_paged: the partial decode kernel's load pattern over one
- * segment with no compute: one wave per (sequence, KV head, split) in the
- * decode's grid order, each split a contiguous range of four-page groups of
- * max_len tokens, reading per page the head's K area and V area through the
- * block table (two groups in flight while one is folded). splits = 0 takes
- * the decode planner's split count for this segment and batch; sink (device)
- * receives one word per wave (splits * num_kv_heads * batch words).
- * Covers areas of up to 2 KiB per head (all widths up to 8 bits at head_dim
- * 128); 16-bit rows give KVQ_ERR_UNSUPPORTED.
+ * kvq_measure_read_paged: the partial decode kernel's load pattern with no
+ * compute, over each of n_segs segments in turn (one launch per segment,
+ * back to back on the stream, so a caller can time many launches between two
+ * events, e.g. one segment per layer so that no layer's pages are still
+ * cached): one wave per (sequence, KV head, split) in the decode's grid
+ * order, each split a contiguous range of four-page groups of max_len tokens,
+ * reading per page the head's K area and V area through the block table (two
+ * groups in flight while one is folded). The segments must share head count,
+ * group and head_dim. splits = 0 takes the decode planner's split count for
+ * each segment alone and batch; sink (device) receives one word per wave of
+ * each launch (sink_words >= the largest launch's splits * num_kv_heads *
+ * batch; the launches overwrite each other's words). Covers areas of up to
+ * 2 KiB per head (all widths up to 8 bits at head_dim 128); 16-bit rows give
+ * KVQ_ERR_UNSUPPORTED. Every segment is checked before the first launch.
  * Errors: KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_DEVICE.
  */
 kvq_status kvq_measure_read_stream(const void* buf, size_t bytes, uint32_t* sink, int32_t sink_words,
                                    kvq_stream stream);
-kvq_status kvq_measure_read_paged(const kvq_segment* seg, int32_t batch, int32_t splits, uint32_t* sink,
-                                  int32_t sink_words, kvq_stream stream);
+kvq_status kvq_measure_read_paged(const kvq_segment* segs, int32_t n_segs, int32_t batch, int32_t splits,
+                                  uint32_t* sink, int32_t sink_words, kvq_stream stream);
 
 /*
  * Size of kvq_decode_attn_noalloc's fixed scratch array, per GPU: the

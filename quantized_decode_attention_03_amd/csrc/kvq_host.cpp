@@ -1108,22 +1108,33 @@ kvq_status kvq_measure_read_stream(const void* buf, size_t bytes, uint32_t* sink
                        "kvq_measure_read_stream");
 }
 
-kvq_status kvq_measure_read_paged(const kvq_segment* seg, int32_t batch, int32_t splits, uint32_t* sink,
-                                  int32_t sink_words, kvq_stream stream) {
+kvq_status kvq_measure_read_paged(const kvq_segment* segs, int32_t n_segs, int32_t batch, int32_t splits,
+                                  uint32_t* sink, int32_t sink_words, kvq_stream stream) {
   const char* who = "kvq_measure_read_paged";
-  kvq_status st = check_segments(seg, 1, batch, who);
+  kvq_status st = check_segments(segs, n_segs, batch, who);
   if (st != KVQ_OK) return st;
-  if (batch < 1 || seg->max_len < 1) return fail(KVQ_ERR_ARG, "%s: need batch >= 1 and max_len >= 1", who);
+  if (batch < 1) return fail(KVQ_ERR_ARG, "%s: need batch >= 1", who);
   if (!sink) return fail(KVQ_ERR_ARG, "%s: null sink", who);
-  if (splits == 0) splits = plan_splits(*seg, batch).n_splits;
-  if (splits < 8 || splits % 8 != 0) return fail(KVQ_ERR_ARG, "%s: splits %d not a positive multiple of 8", who, splits);
-  const int64_t waves = static_cast<int64_t>(splits) * seg->layout->num_kv_heads * batch;
-  if (sink_words < waves) return fail(KVQ_ERR_ARG, "%s: sink_words %d < %lld waves", who, sink_words,
-                                      static_cast<long long>(waves));
-  const hipError_t e = kvq::launch_measure_paged(*seg, batch, splits, sink, reinterpret_cast<hipStream_t>(stream));
-  if (e == hipErrorInvalidValue)
-    return fail(KVQ_ERR_UNSUPPORTED, "%s: areas of more than 2 KiB per head (16-bit rows) are not covered", who);
-  return device_status(e, who);
+  if (splits != 0 && (splits < 8 || splits % 8 != 0))
+    return fail(KVQ_ERR_ARG, "%s: splits %d not a positive multiple of 8", who, splits);
+  std::vector<int> plan(n_segs);
+  for (int i = 0; i < n_segs; ++i) {
+    const kvq_segment& sg = segs[i];
+    if (sg.max_len < 1) return fail(KVQ_ERR_ARG, "%s: segment %d: max_len %d < 1", who, i, sg.max_len);
+    if (!kvq::measure_paged_covers(*sg.layout))
+      return fail(KVQ_ERR_UNSUPPORTED, "%s: segment %d: areas of more than 2 KiB per head (16-bit rows) are not "
+                  "covered", who, i);
+    plan[i] = splits != 0 ? splits : plan_splits(sg, batch).n_splits;
+    const int64_t waves = static_cast<int64_t>(plan[i]) * sg.layout->num_kv_heads * batch;
+    if (sink_words < waves)
+      return fail(KVQ_ERR_ARG, "%s: segment %d: sink_words %d < %lld waves", who, i, sink_words,
+                  static_cast<long long>(waves));
+  }
+  for (int i = 0; i < n_segs; ++i) {
+    const hipError_t e = kvq::launch_measure_paged(segs[i], batch, plan[i], sink, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return device_status(e, who);
+  }
+  return ok();
 }
 
 kvq_status kvq_decode_merge(const kvq_segment* segs, int32_t n_segs, int32_t batch, float* out, void* ws,

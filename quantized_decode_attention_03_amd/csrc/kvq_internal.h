@@ -175,6 +175,9 @@ constexpr int kMergeWindowMax = 512;
 // segment with no compute (areas up to 2 KiB per head). Each wave writes one
 // word to sink.
 hipError_t launch_measure_stream(const void* buf, size_t bytes, uint32_t* sink, int waves, hipStream_t s);
+// Whether measure_paged covers the layout: every head's K and V areas 16-byte
+// multiples of 16 B to 2 KiB.
+bool measure_paged_covers(const kvq_layout& L);
 hipError_t launch_measure_paged(const kvq_segment& seg, int batch, int splits, uint32_t* sink, hipStream_t s);
 
 }  // namespace kvq

@@ -48,8 +48,10 @@ struct PagedArgs {
 };
 
 // A head's K and V areas of one page are read as 16-byte chunks, lane l taking
-// chunks l and l + 64 (clamped to the area's last chunk: areas of up to 2 KiB,
-// every width up to 8 bits at head_dim 128); a group is four pages.
+// chunk l and, for areas of more than 1 KiB, chunk l + 64 (clamped to the
+// area's last chunk: areas of up to 2 KiB, every width up to 8 bits at
+// head_dim 128); an area of at most 1 KiB takes one load. A group is four
+// pages.
 struct PagedBuf {
   uint4 v[4][2][2];
 };
@@ -78,7 +80,8 @@ __device__ __forceinline__ void paged_load(const PagedArgs& a, const GroupTab& t
       const uint4* base = reinterpret_cast<const uint4*>(a.pool + bo + a.area_off[half][h]);
       const int last = a.last16[half][h];
       r.v[pp][half][0] = base[min(lane, last)];
-      r.v[pp][half][1] = base[min(lane + 64, last)];
+      // (the area's size is the same in every lane: a uniform branch)
+      r.v[pp][half][1] = last >= 64 ? base[min(lane + 64, last)] : make_uint4(0u, 0u, 0u, 0u);
     }
   }
 }
@@ -144,6 +147,22 @@ hipError_t launch_measure_stream(const void* buf, size_t bytes, uint32_t* sink, 
   return hipGetLastError();
 }
 
+namespace {
+int64_t area_bytes(const kvq_layout& L, int half, int h) {
+  if (half == 0) return (h + 1 < L.num_kv_heads ? L.k_off[h + 1] : L.v_off[0]) - L.k_off[h];
+  return (h + 1 < L.num_kv_heads ? L.v_off[h + 1] : L.block_bytes) - L.v_off[h];
+}
+}  // namespace
+
+bool measure_paged_covers(const kvq_layout& L) {
+  for (int h = 0; h < L.num_kv_heads; ++h)
+    for (int half = 0; half < 2; ++half) {
+      const int64_t n = area_bytes(L, half, h);
+      if (n % 16 != 0 || n < 16 || n > 2048) return false;
+    }
+  return true;
+}
+
 hipError_t launch_measure_paged(const kvq_segment& seg, int batch, int splits, uint32_t* sink, hipStream_t s) {
   const kvq_layout& L = *seg.layout;
   PagedArgs a{};
@@ -156,15 +175,13 @@ hipError_t launch_measure_paged(const kvq_segment& seg, int batch, int splits, u
   a.n_heads = L.num_kv_heads;
   a.splits = splits;
   a.pages = (seg.max_len + KVQ_BLOCK_TOKENS - 1) / KVQ_BLOCK_TOKENS;
-  if (a.pages == 0 || batch == 0 || splits < 8 || splits % 8 != 0) return hipErrorInvalidValue;
+  if (a.pages == 0 || batch == 0 || splits < 8 || splits % 8 != 0 || !measure_paged_covers(L))
+    return hipErrorInvalidValue;
   for (int h = 0; h < L.num_kv_heads; ++h) {
-    const int64_t kb = (h + 1 < L.num_kv_heads ? L.k_off[h + 1] : L.v_off[0]) - L.k_off[h];
-    const int64_t vb = (h + 1 < L.num_kv_heads ? L.v_off[h + 1] : L.block_bytes) - L.v_off[h];
-    if (kb % 16 != 0 || vb % 16 != 0 || kb > 2048 || vb > 2048 || kb < 16 || vb < 16) return hipErrorInvalidValue;
     a.area_off[0][h] = L.k_off[h];
     a.area_off[1][h] = L.v_off[h];
-    a.last16[0][h] = static_cast<int32_t>(kb / 16 - 1);
-    a.last16[1][h] = static_cast<int32_t>(vb / 16 - 1);
+    a.last16[0][h] = static_cast<int32_t>(area_bytes(L, 0, h) / 16 - 1);
+    a.last16[1][h] = static_cast<int32_t>(area_bytes(L, 1, h) / 16 - 1);
   }
   a.sink = sink;
   hipLaunchKernelGGL(measure_paged_kernel, dim3(static_cast<unsigned>(splits) * a.n_heads * batch), dim3(64), 0, s, a);

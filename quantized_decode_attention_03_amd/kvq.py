@@ -14,7 +14,7 @@ import numpy as np
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkvq.so")
 
-KVQ_ABI_VERSION = 4
+KVQ_ABI_VERSION = 5
 KVQ_MAX_KV_HEADS = 64
 KVQ_BLOCK_TOKENS = 16
 
@@ -125,7 +125,7 @@ def lib():
     L.kvq_decode_partial.argtypes = [ctypes.POINTER(KvqSegment), i32, i32, vp, ctypes.c_int, vp, sz, vp]
     L.kvq_decode_merge.argtypes = [ctypes.POINTER(KvqSegment), i32, i32, vp, vp, sz, vp]
     L.kvq_measure_read_stream.argtypes = [vp, sz, vp, i32, vp]
-    L.kvq_measure_read_paged.argtypes = [ctypes.POINTER(KvqSegment), i32, i32, vp, i32, vp]
+    L.kvq_measure_read_paged.argtypes = [ctypes.POINTER(KvqSegment), i32, i32, i32, vp, i32, vp]
     L.kvq_decode_attn_noalloc.argtypes = [ctypes.POINTER(KvqSegment), i32, i32, vp, ctypes.c_int, vp, vp]
     for name in EXPORTED:
         if name not in ("kvq_abi_version", "kvq_status_str", "kvq_last_error"):
@@ -475,12 +475,15 @@ def kvq_measure_read_stream(buf, sink, stream=None):
            "kvq_measure_read_stream")
 
 
-def kvq_measure_read_paged(segment, batch, sink, splits=0, stream=None):
-    """The partial decode kernel's load pattern over one segment with no compute (measurement only)."""
+def kvq_measure_read_paged(segments, batch, sink, splits=0, stream=None):
+    """The partial decode kernel's load pattern with no compute over each segment in turn (one launch per
+    segment, back to back; measurement only). `segments` is a Segment or a list of them."""
     import torch
-    segs = _segments([segment])
-    _check(lib().kvq_measure_read_paged(segs, int(batch), int(splits), _dev_ptr(sink, (torch.int32,), "sink"),
-                                        sink.numel(), _stream(stream)), "kvq_measure_read_paged")
+    if isinstance(segments, Segment):
+        segments = [segments]
+    _check(lib().kvq_measure_read_paged(_segments(segments), len(segments), int(batch), int(splits),
+                                        _dev_ptr(sink, (torch.int32,), "sink"), sink.numel(), _stream(stream)),
+           "kvq_measure_read_paged")
 
 
 def kvq_decode_attn_noalloc(segments, q, out, stream=None):

@@ -539,6 +539,7 @@ def test_measurement_reads_run_over_a_cache():
     before = cache.pool.clone()
     kvq.kvq_measure_read_paged(cache.segment(lens), 2, sink)
     kvq.kvq_measure_read_paged(cache.segment(lens), 2, sink, splits=8)
+    kvq.kvq_measure_read_paged([cache.segment(lens), cache.segment(lens)], 2, sink)
     buf = torch.ones(1 << 20, dtype=torch.uint8, device=T.DEV)
     kvq.kvq_measure_read_stream(buf, sink)
     torch.cuda.synchronize()

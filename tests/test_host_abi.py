@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     for name in sorted(declared):
         assert hasattr(lib, name), name
     assert declared == set(kvq.EXPORTED)
-    assert kvq.kvq_abi_version() == kvq.KVQ_ABI_VERSION == 4
+    assert kvq.kvq_abi_version() == kvq.KVQ_ABI_VERSION == 5
     assert kvq.kvq_status_str(kvq.KVQ_ERR_BUDGET) == "KVQ_ERR_BUDGET"
 
 
@@ -292,12 +292,21 @@ def test_measurement_helpers_argument_checks_need_no_device():
     assert lib.kvq_measure_read_stream(p, 8192, p, 100, None) == kvq.KVQ_ERR_ARG      # sink too small
     L = kvq.kvq_layout_init(8, 4, 128, 128, [4] * 8, [4] * 8)
     seg = (kvq.KvqSegment * 1)(_fake_segment(L, 32768, 2048))
-    assert lib.kvq_measure_read_paged(seg, 16, 12, p, 1 << 20, None) == kvq.KVQ_ERR_ARG  # splits not a multiple of 8
-    assert lib.kvq_measure_read_paged(seg, 16, 16, p, 100, None) == kvq.KVQ_ERR_ARG      # sink below one word per wave
-    assert lib.kvq_measure_read_paged(seg, 16, 16, None, 1 << 20, None) == kvq.KVQ_ERR_ARG
+    assert lib.kvq_measure_read_paged(seg, 1, 16, 12, p, 1 << 20, None) == kvq.KVQ_ERR_ARG  # splits not a multiple of 8
+    assert lib.kvq_measure_read_paged(seg, 1, 16, 16, p, 100, None) == kvq.KVQ_ERR_ARG      # sink below one word per wave
+    assert lib.kvq_measure_read_paged(seg, 1, 16, 16, None, 1 << 20, None) == kvq.KVQ_ERR_ARG
+    assert lib.kvq_measure_read_paged(seg, 0, 16, 16, p, 1 << 20, None) == kvq.KVQ_ERR_ARG   # no segment
     bf = kvq.kvq_layout_init(8, 4, 128, 128, [16] * 8, [16] * 8)
     seg16 = (kvq.KvqSegment * 1)(_fake_segment(bf, 32768, 2048))
-    assert lib.kvq_measure_read_paged(seg16, 16, 16, p, 1 << 20, None) == kvq.KVQ_ERR_UNSUPPORTED
+    assert lib.kvq_measure_read_paged(seg16, 1, 16, 16, p, 1 << 20, None) == kvq.KVQ_ERR_UNSUPPORTED
+    # several segments: every one is checked before the first launch (here a 16-bit one second, so the
+    # call fails with nothing launched, which needs no device)
+    two = (kvq.KvqSegment * 2)(_fake_segment(L, 32768, 2048), _fake_segment(bf, 32768, 2048))
+    assert lib.kvq_measure_read_paged(two, 2, 16, 16, p, 1 << 20, None) == kvq.KVQ_ERR_UNSUPPORTED
+    assert "segment 1" in kvq.kvq_last_error()
+    short = (kvq.KvqSegment * 2)(_fake_segment(L, 32768, 2048), _fake_segment(L, 32768, 2048))
+    short[1].max_len = 0
+    assert lib.kvq_measure_read_paged(short, 2, 16, 16, p, 1 << 20, None) == kvq.KVQ_ERR_ARG
 
 
 def test_append_and_dequant_argument_checks_need_no_device():
