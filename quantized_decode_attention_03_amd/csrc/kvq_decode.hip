@@ -1311,26 +1311,67 @@ __global__ __launch_bounds__(64 * NW) void decode_merge_kernel(MergeArgs a, floa
     ok = static_cast<uint32_t>(blk) < wblocks;
     return win.pool + (ok ? blk : 0) * win.block_bytes + off + (t % kBlockTokens) * (D * 2);
   };
+  // This wave's first batch of split slots (w, w + NW, ... of the first chunk,
+  // padded with the chunk's last slot) and of window value rows (tokens w,
+  // w + NW, ...), loaded before the max is known: the values do not depend
+  // on it, so their round trips overlap the max pass and the window scores.
+  const int n0 = min(CHUNK, S);
+  float v0[8][CPL];
+  if (w < n0) {
+    const float* pc = po + CPL * lane;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int sc = min(w + u * NW, n0 - 1);
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) v0[u][j] = pc[static_cast<int64_t>(sc) * D + j];
+    }
+  }
+  const uint8_t* vbase = win.pool ? win.pool + win.v_off[h] + (CPL == 2 ? 4 : 2) * lane : nullptr;
+  uint32_t wraw0[8];
+  if (w < nwin) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int tc = min(w + u * NW, nwin - 1);
+      const int32_t blk = win.table[static_cast<int64_t>(b) * win.table_stride + tc / kBlockTokens];
+      const uint8_t* row = vbase + (static_cast<uint32_t>(blk) < wblocks ? blk : 0) * win.block_bytes +
+                           (tc % kBlockTokens) * (D * 2);
+      if constexpr (CPL == 2) wraw0[u] = *reinterpret_cast<const uint32_t*>(row);
+      else wraw0[u] = *reinterpret_cast<const uint16_t*>(row);
+    }
+  }
+  // global max over splits and window tokens (the splits' maxima read before
+  // q~ arrives); a window token's score is summed by eight lanes, D / 8
+  // channels each, then over the eight lanes. This thread's first window key
+  // row is also read before q~ arrives.
+  float mx = NEG_INF;
+  for (int s = tid; s < S; s += 64 * NW) mx = fmaxf(mx, ml[2 * s]);
+  constexpr int CH = D / 8;  // channels per lane of a token
+  const int part = lane & 7;
+  const int t00 = tid >> 3, tend = (nwin + 7) & ~7;
+  uint4 k0[CH / 8];
+  int32_t blk0 = 0;
+  if (t00 < tend) {
+    const int t = min(t00, nwin - 1);
+    bool ok;
+    const uint4* row = reinterpret_cast<const uint4*>(win_row(t, win.k_off[h], ok)) + part * (CH / 8);
+#pragma unroll
+    for (int c = 0; c < CH / 8; ++c) k0[c] = row[c];
+    blk0 = ok ? win.table[static_cast<int64_t>(b) * win.table_stride + t / kBlockTokens] : -1;
+  }
   if (nwin > 0) {
     if (tid < D) wq[tid] = a.qrot[bg * D + tid];
     __syncthreads();
   }
-
-  // global max over splits and window tokens; a window token's score is
-  // summed by eight lanes, D / 8 channels each, then over the eight lanes
-  float mx = NEG_INF;
-  for (int s = tid; s < S; s += 64 * NW) mx = fmaxf(mx, ml[2 * s]);
   {
-    constexpr int CH = D / 8;  // channels per lane of a token
-    const int part = lane & 7;
-    for (int t0 = tid >> 3; t0 < ((nwin + 7) & ~7); t0 += 8 * NW) {
+    for (int t0 = t00; t0 < tend; t0 += 8 * NW) {
       const int t = min(t0, nwin - 1);  // lanes past the last token repeat it (not stored)
-      bool ok;
-      const uint4* row = reinterpret_cast<const uint4*>(win_row(t, win.k_off[h], ok)) + part * (CH / 8);
+      const bool first = t0 == t00;     // the row read before q~ arrived
+      bool ok = blk0 >= 0;
+      const uint4* row = first ? nullptr : reinterpret_cast<const uint4*>(win_row(t, win.k_off[h], ok)) + part * (CH / 8);
       float z = 0.f;
 #pragma unroll
       for (int c = 0; c < CH / 8; ++c) {
-        const uint4 v = row[c];
+        const uint4 v = first ? k0[c] : row[c];
         const float* qq = &wq[part * CH + 8 * c];
         z = fmaf(qq[0], bf16lo_to_f(v.x), z);
         z = fmaf(qq[1], bf16hi_to_f(v.x), z);
@@ -1347,7 +1388,7 @@ __global__ __launch_bounds__(64 * NW) void decode_merge_kernel(MergeArgs a, floa
       z = ok ? z : NEG_INF;
       if (part == 0 && t0 < nwin) {
         wz[t] = z;
-        wrow[t] = ok ? win.table[static_cast<int64_t>(b) * win.table_stride + t / kBlockTokens] : 0;
+        wrow[t] = !ok ? 0 : first ? blk0 : win.table[static_cast<int64_t>(b) * win.table_stride + t / kBlockTokens];
       }
       if (t0 < nwin) mx = fmaxf(mx, z);
     }
@@ -1379,11 +1420,12 @@ __global__ __launch_bounds__(64 * NW) void decode_merge_kernel(MergeArgs a, floa
       // list's last slot at weight 0, so no slot waits on another's load
       for (int s = w; s < n; s += 8 * NW) {
         float v[8][CPL], wu[8];
+        const bool first = s0 == 0 && s == w;  // the batch loaded at the start
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int su = s + u * NW, sc = min(su, n - 1);
 #pragma unroll
-          for (int j = 0; j < CPL; ++j) v[u][j] = pc[static_cast<int64_t>(sc) * D + j];
+          for (int j = 0; j < CPL; ++j) v[u][j] = first ? v0[u][j] : pc[static_cast<int64_t>(sc) * D + j];
           wu[u] = su < n ? wsh[sc] : 0.f;
         }
 #pragma unroll
@@ -1405,16 +1447,19 @@ __global__ __launch_bounds__(64 * NW) void decode_merge_kernel(MergeArgs a, floa
       // tokens t = w, w + NW, ... in batches of eight (the last padded with
       // the last token at weight 0), each token's row read by its CPL-channel
       // lane slices, so a batch's loads are all in flight together
-      const uint8_t* vbase = win.pool + win.v_off[h] + (CPL == 2 ? 4 : 2) * lane;
       for (int t = w; t < nwin; t += 8 * NW) {
         uint32_t raw[8];
         float pw[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int tu = t + u * NW, tc = min(tu, nwin - 1);
-          const uint8_t* row = vbase + wrow[tc] * win.block_bytes + (tc % kBlockTokens) * (D * 2);
-          if constexpr (CPL == 2) raw[u] = *reinterpret_cast<const uint32_t*>(row);
-          else raw[u] = *reinterpret_cast<const uint16_t*>(row);
+          if (t == w) {
+            raw[u] = wraw0[u];  // loaded at the start
+          } else {
+            const uint8_t* row = vbase + wrow[tc] * win.block_bytes + (tc % kBlockTokens) * (D * 2);
+            if constexpr (CPL == 2) raw[u] = *reinterpret_cast<const uint32_t*>(row);
+            else raw[u] = *reinterpret_cast<const uint16_t*>(row);
+          }
           pw[u] = tu < nwin ? wz[tc] : 0.f;
         }
 #pragma unroll
