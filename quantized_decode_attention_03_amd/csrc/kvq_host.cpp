@@ -956,9 +956,21 @@ static kvq_status decode_partial_impl(const kvq_segment* segs, int32_t n_segs, i
     kvq::DecodeArgs a;
     int kbits, vbits;
     bool multi;
-    int64_t bytes;  // code bytes the launch reads per sequence (orders the launches)
+    // a wave's share of the launch: pages per split times the bytes of a
+    // page of its heaviest head (orders the launches: the longest first)
+    int64_t bytes;
   };
   std::vector<Launch> launches;
+  // bytes one wave reads for head h of segment i: its pages per split times
+  // the head's K and V codes and metadata per page
+  auto wave_bytes = [&](int i, int h) {
+    const kvq_layout& L = *segs[i].layout;
+    const int64_t page = static_cast<int64_t>(KVQ_BLOCK_TOKENS) * (L.bits_k[h] + L.bits_v[h]) * d / 8 +
+                         2 * KVQ_BLOCK_TOKENS * (L.meta_fp16 ? 4 : 8);
+    const int pages = (std::max(segs[i].max_len, 0) + KVQ_BLOCK_TOKENS - 1) / KVQ_BLOCK_TOKENS;
+    const int splits = std::max(plan.split[i].n_splits, 1);
+    return page * ((pages + splits - 1) / splits);
+  };
   auto add_head = [&](kvq::DecodeArgs& a, const kvq_layout& L, int h, int e) {
     a.heads[e] = h;
     a.k_off[e] = L.k_off[h];
@@ -1005,7 +1017,7 @@ static kvq_status decode_partial_impl(const kvq_segment* segs, int32_t n_segs, i
       for (int h = 0; h < L.num_kv_heads; ++h)
         if (mixable(L, h)) {
           add_head(l.a, L, h, e++);
-          l.bytes += static_cast<int64_t>(L.bits_k[h] + L.bits_v[h]) * d / 8 * std::max(segs[i].max_len, 0);
+          l.bytes = std::max(l.bytes, wave_bytes(i, h));
         }
       if (e == e0) continue;
       l.a.seg[l.a.n_segs++] = seg_desc(i, e0, e - e0, grid);
@@ -1033,7 +1045,7 @@ static kvq_status decode_partial_impl(const kvq_segment* segs, int32_t n_segs, i
       }
       l.a.seg[0] = seg_desc(i, 0, e, 0);
       l.a.n_segs = 1;
-      l.bytes = static_cast<int64_t>(e) * (L.bits_k[h0] + L.bits_v[h0]) * d / 8 * std::max(segs[i].max_len, 0);
+      l.bytes = wave_bytes(i, h0);
       launches.push_back(l);
     }
   }
@@ -1051,10 +1063,11 @@ static kvq_status decode_partial_impl(const kvq_segment* segs, int32_t n_segs, i
     return ok();
   }
   // Several launches (width groups that cannot share a launch) run
-  // concurrently: the largest on the caller's stream, which starts it first,
-  // the others on side streams forked from it and joined back before the call
-  // returns. (One after another on one stream is slower: small launches are
-  // latency-bound and then add up.)
+  // concurrently: the one whose waves have most to read on the caller's
+  // stream, which starts it first (side-stream launches start 10-25 us
+  // later), the others on side streams forked from it and joined back before
+  // the call returns. (One after another on one stream is slower: small
+  // launches are latency-bound and then add up.)
   std::stable_sort(launches.begin(), launches.end(),
                    [](const Launch& x, const Launch& y) { return x.bytes > y.bytes; });
   std::lock_guard<std::mutex> lock(g_side_mutex);
