@@ -383,7 +383,9 @@ def build_decode_layers(args, kvq, torch, dev):
 
 
 def run_decode(args, torch, dev, kvq):
-    """One step = per layer: append the new token, partial decode, merge."""
+    """One step = per layer: append the new token and decode. By default one library call per layer does
+    both (kvq_append_decode_partial, then kvq_append_decode_merge, which quantizes, stores and attends to
+    the new token); --separate-append makes the append a launch of its own (kvq_quantize_append)."""
     layers, config, batch, layer_bytes, kernel = build_decode_layers(args, kvq, torch, dev)
     torch.cuda.synchronize()
     seg_objs = [[kvq.Segment(L, pool, table, lens, n) for (L, pool, table, lens, n) in ly["segs"]] for ly in layers]
@@ -393,12 +395,22 @@ def run_decode(args, torch, dev, kvq):
     kvq.kvq_decode_workspace_init(ws)
     out = torch.empty((batch, HKV * G, D), dtype=torch.float32, device=dev)
     calls = []
+    fused_any = False
     for ly, segs in zip(layers, seg_objs):
         L, pool, table, _, _ = ly["segs"][ly["app"]]
         start = torch.full((batch,), ly["pos"], dtype=torch.int32, device=dev)
-        calls.append((kvq.prepare_quantize_append(L, pool, table, start, ly["new_k"], ly["new_v"]),
-                      kvq.prepare_decode_partial(segs, ly["q"], ws),
-                      kvq.prepare_decode_merge(segs, batch, out, ws)))
+        if not args.separate_append and not L.key_per_channel and ly["new_k"].shape[1] == 1:
+            fused_any = True
+            nk, nv = ly["new_k"][:, 0].contiguous(), ly["new_v"][:, 0].contiguous()
+            calls.append((None, kvq.prepare_append_decode_partial(segs, ly["app"], start, nk, nv, ly["q"], ws),
+                          kvq.prepare_append_decode_merge(segs, ly["app"], start, batch, out, ws)))
+        else:
+            calls.append((kvq.prepare_quantize_append(L, pool, table, start, ly["new_k"], ly["new_v"]),
+                          kvq.prepare_decode_partial(segs, ly["q"], ws),
+                          kvq.prepare_decode_merge(segs, batch, out, ws)))
+    config = dict(config, step=("per layer one call: the new token's append fused into the decode "
+                                "(kvq_append_decode_partial + kvq_append_decode_merge)") if fused_any else
+                  "per layer: kvq_quantize_append, kvq_decode_partial, kvq_decode_merge")
 
     n_ev = args.layers * args.steps
     ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
@@ -406,7 +418,8 @@ def run_decode(args, torch, dev, kvq):
 
     def step(record=None):
         for i, (app, part, merge) in enumerate(calls):
-            app()
+            if app is not None:
+                app()
             if record is not None:
                 ev_a[record + i].record()
             part()
@@ -639,20 +652,29 @@ def run_long_dynamic(args, torch, dev, kvq):
     st.init(0, tokens)
     ws = kvq.decode_workspace(layers[0]["segs"], batch, dev)
     out = torch.empty((batch, HKV * G, D), dtype=torch.float32, device=dev)
-    prepared = [(kvq.prepare_decode_partial(ly["segs"], ly["q"], ws), kvq.prepare_decode_merge(ly["segs"], batch, out, ws))
+    start = torch.zeros((batch,), dtype=torch.int32, device=dev)
+    fused = not args.separate_append
+    prepared = [(None if fused else kvq.prepare_decode_partial(ly["segs"], ly["q"], ws),
+                 kvq.prepare_append_decode_merge(ly["segs"], 0, start, batch, out, ws) if fused else
+                 kvq.prepare_decode_merge(ly["segs"], batch, out, ws))
                 for ly in layers]
     n_ev = args.layers * args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(3)]
 
     # Calls marshalled once: the requant reads the planner's move array when it runs, and each
-    # step's append has its own prepared call (its token's rows) writing at the start position
-    # filled in per step.
-    start = torch.zeros((batch,), dtype=torch.int32, device=dev)
+    # step's append (fused into the merge, or a launch of its own) has its own prepared call (its
+    # token's rows) writing at the start position filled in per step.
     requants = [kvq.prepare_logquant_requant(ly["segs"][0], ly["segs"][1], ly["segs"][2], batch, st.moves)
                 for ly in layers]
-    appends = [[kvq.prepare_quantize_append(ly["segs"][0].layout, ly["segs"][0].pool, ly["segs"][0].block_table,
-                                            start, ly["new_k"][:, i:i + 1], ly["new_v"][:, i:i + 1])
-                for i in range(args.warmup + args.steps)] for ly in layers]
+    if fused:
+        appends = [[kvq.prepare_append_decode_partial(ly["segs"], 0, start, ly["new_k"][:, i].contiguous(),
+                                                      ly["new_v"][:, i].contiguous(), ly["q"], ws)
+                    for i in range(args.warmup + args.steps)] for ly in layers]
+    else:
+        appends = [[kvq.prepare_quantize_append(ly["segs"][0].layout, ly["segs"][0].pool,
+                                                ly["segs"][0].block_table, start, ly["new_k"][:, i:i + 1],
+                                                ly["new_v"][:, i:i + 1])
+                    for i in range(args.warmup + args.steps)] for ly in layers]
 
     def step(i, record=None):
         st.advance()
@@ -665,10 +687,14 @@ def run_long_dynamic(args, torch, dev, kvq):
             if record is not None:
                 ev[0][record + li].record()
             requants[li]()
-            appends[li][i]()
+            if not fused:
+                appends[li][i]()
             if record is not None:
                 ev[1][record + li].record()
-            part()
+            if fused:
+                appends[li][i]()  # the partials, this step's token appended by their split-0 waves
+            else:
+                part()
             if record is not None:
                 ev[2][record + li].record()
             merge()
@@ -693,7 +719,8 @@ def run_long_dynamic(args, torch, dev, kvq):
         "config": {"workload": "long-context decode with LogQuant's dynamic adjustment: batch 1, ctx 131072 "
                                "growing one token per step, 8 kv heads x 4 q heads, head_dim 128, hadamard 32; "
                                "segments: bf16 window ring 128, log-spaced 4-bit subset, 2-bit rest; per layer "
-                               "per step: requant of the moved rows, append, partials, merge (eager)",
+                               "per step: requant of the moved rows, then the partials and the merge with the new "
+                               "token's append fused into it (--separate-append: its own launch) (eager)",
                    "layers": args.layers, "batch": batch, "ctx": tokens},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
@@ -780,6 +807,9 @@ def main():
                     help="print per-dispatch means of the counters in rocprofv3 --pmc CSVs (kernels matching "
                          "--match) and exit")
     ap.add_argument("--match", default="kvq::", help="kernel-name filter for --summarize-counters")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="decode steps append the new token with a launch of its own (kvq_quantize_append) "
+                         "instead of fusing it into the decode call")
     args = ap.parse_args()
     if args.summarize_pmc:
         sys.stdout.write(summarize_pmc(*args.summarize_pmc))

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 5
+#define KVQ_ABI_VERSION 6
 #define KVQ_MAX_KV_HEADS 64
 #define KVQ_BLOCK_TOKENS 16
 
@@ -468,6 +468,61 @@ kvq_status kvq_decode_partial(const kvq_segment* segs, int32_t n_segs, int32_t b
                               void* ws, size_t ws_bytes, kvq_stream stream);
 kvq_status kvq_decode_merge(const kvq_segment* segs, int32_t n_segs, int32_t batch,
                             float* out, void* ws, size_t ws_bytes, kvq_stream stream);
+
+/*
+ * Device, async. One decode step in one call: the quantize-on-append of one
+ * new token per sequence into segment append_seg, then decode attention over
+ * every segment, the new token included [SAW: section 3 (rotation and
+ * quantization fused with the cache write; attention read straight from the
+ * quantized cache); LQ: Methodology 2 (new tokens enter the full-precision
+ * window)]. Equals kvq_quantize_append(segs[append_seg], start_pos, n_new = 1,
+ * k_new, v_new) followed by kvq_decode_attn(segs, q): the stored rows and
+ * metadata are bit-identical to the append's, and the output equals the two
+ * calls' up to the order of fp32 sums. The new token is not read back from the
+ * cache: the partial launch masks its slot, its split-0 wave of each
+ * (sequence, KV head) quantizes and stores the token and leaves its
+ * dequantized rows in ws, and the merge kernel attends to it from those rows,
+ * so the step makes no append launch.
+ * In:  segs, n_segs, batch, q, q_dtype, ws, ws_bytes: as kvq_decode_attn.
+ *      append_seg: index of the segment that receives the token (a row
+ *      layout: per-channel keys append whole blocks through
+ *      kvq_quantize_append). Its pool is written (the segment's pool pointer
+ *      must be writable device memory).
+ *      start_pos device int32 [batch]: the token's slot in that segment
+ *      (negative: no token for that sequence). Its page must be mapped for the
+ *      row to be stored; it is attended to when also below the segment's
+ *      min(seq_lens[b], max_len), so seq_lens counts the new token.
+ *      k_new, v_new device [batch][Hkv][head_dim] of in_dtype (KVQ_BF16 or
+ *      KVQ_F32), 16-byte aligned.
+ * Out: out as kvq_decode_attn; the new rows in the append segment's pool.
+ * Errors: as kvq_decode_attn; KVQ_ERR_ARG (append_seg out of range, null
+ * start_pos / k_new / v_new, misaligned rows, bad in_dtype),
+ * KVQ_ERR_UNSUPPORTED (per-channel keys in the append segment).
+ */
+kvq_status kvq_append_decode_attn(const kvq_segment* segs, int32_t n_segs, int32_t batch,
+                                  int32_t append_seg, const int32_t* start_pos,
+                                  const void* k_new, const void* v_new, kvq_dtype in_dtype,
+                                  const void* q, kvq_dtype q_dtype, float* out,
+                                  void* ws, size_t ws_bytes, kvq_stream stream);
+
+/*
+ * The two halves of kvq_append_decode_attn, exported so a profiler or caller
+ * can time them apart (as kvq_decode_partial and kvq_decode_merge): the
+ * partial launch, whose split-0 wave of each (sequence, KV head) quantizes
+ * and stores the new token and leaves its dequantized rows in ws (every wave
+ * masks its slot), then the merge, which attends to the token from those rows.
+ * Same arguments and errors as kvq_append_decode_attn (the merge half takes
+ * no rows); calling them in this order on one stream with one workspace
+ * equals one kvq_append_decode_attn call.
+ */
+kvq_status kvq_append_decode_partial(const kvq_segment* segs, int32_t n_segs, int32_t batch,
+                                     int32_t append_seg, const int32_t* start_pos,
+                                     const void* k_new, const void* v_new, kvq_dtype in_dtype,
+                                     const void* q, kvq_dtype q_dtype,
+                                     void* ws, size_t ws_bytes, kvq_stream stream);
+kvq_status kvq_append_decode_merge(const kvq_segment* segs, int32_t n_segs, int32_t batch,
+                                   int32_t append_seg, const int32_t* start_pos,
+                                   float* out, void* ws, size_t ws_bytes, kvq_stream stream);
 
 /*
  * Measurement helpers, not part of the decode path: two read-only kernels that

@@ -13,6 +13,7 @@
 // shuffles.
 #include "kvq_device.h"
 #include "kvq_internal.h"
+#include "kvq_rowq.h"
 
 #include <cmath>
 
@@ -67,104 +68,6 @@ __device__ __forceinline__ void fwht8(float (&x)[8], int lane_in_row, int n) {
 // exact in fp64, so scaling by 1/sqrt(n) and rounding to fp32 reproduces the
 // rotation's value (an exact matrix product, one rounding).
 // ---------------------------------------------------------------------------
-
-constexpr int kDppXor1 = 0xb1;  // quad_perm [1, 0, 3, 2]
-constexpr int kDppXor2 = 0x4e;  // quad_perm [2, 3, 0, 1]
-
-template <int CTRL>
-__device__ __forceinline__ double dpp_f64(double x) {
-  const uint64_t u = __builtin_bit_cast(uint64_t, x);
-  const int lo = __builtin_amdgcn_mov_dpp(static_cast<int>(u), CTRL, 0xf, 0xf, false);
-  const int hi = __builtin_amdgcn_mov_dpp(static_cast<int>(u >> 32), CTRL, 0xf, 0xf, false);
-  return __builtin_bit_cast(double, (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) |
-                                        static_cast<uint32_t>(lo));
-}
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
-}
-
-template <int CPR, int MAXST>
-__device__ __forceinline__ void butterflies_in_lane(double (&x)[CPR]) {
-#pragma unroll
-  for (int st = 1; st < MAXST; st <<= 1) {
-#pragma unroll
-    for (int j = 0; j < CPR; ++j) {
-      if (!(j & st)) {
-        const double u = x[j], v = x[j | st];
-        x[j] = u + v;
-        x[j | st] = u - v;
-      }
-    }
-  }
-}
-
-template <int CPR>
-__device__ __forceinline__ void fwht_row_f64(double (&x)[CPR], int m, int n) {
-  // blocks at least a lane wide (the common case) take every in-lane stride
-  if (n >= CPR) {
-    butterflies_in_lane<CPR, CPR>(x);
-  } else {
-#pragma unroll
-    for (int st = 1; st < CPR; st <<= 1) {
-      if (st < n) {
-#pragma unroll
-        for (int j = 0; j < CPR; ++j) {
-          if (!(j & st)) {
-            const double u = x[j], v = x[j | st];
-            x[j] = u + v;
-            x[j | st] = u - v;
-          }
-        }
-      }
-    }
-  }
-  // lower lane of a pair keeps x + y, upper keeps y - x: fma(+-1, x, y) rounds
-  // once, exactly like the add or subtract
-  if (CPR < n) {
-    const double sgn = (m & 1) ? -1.0 : 1.0;
-#pragma unroll
-    for (int j = 0; j < CPR; ++j) x[j] = fma(sgn, x[j], dpp_f64<kDppXor1>(x[j]));
-  }
-  if (2 * CPR < n) {
-    const double sgn = (m & 2) ? -1.0 : 1.0;
-#pragma unroll
-    for (int j = 0; j < CPR; ++j) x[j] = fma(sgn, x[j], dpp_f64<kDppXor2>(x[j]));
-  }
-}
-
-// Codes of 8 consecutive values (already scaled to code units u) packed
-// little-endian: BITS=4 -> one word, 2 -> 16 bits, 8 -> two words, 3 -> 24 bits.
-// v_cvt_pk_u8_f32 rounds half to even and saturates to [0, 255]; u lies in
-// [0, 2^b - 1 + 2^-22 (2^b - 1)], so every code is already in range.
-template <int BITS>
-__device__ __forceinline__ uint64_t pack8(const float* u) {
-  if constexpr (BITS == 8) {
-    uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      w0 = __builtin_amdgcn_cvt_pk_u8_f32(u[j], j, w0);
-      w1 = __builtin_amdgcn_cvt_pk_u8_f32(u[4 + j], j, w1);
-    }
-    return w0 | (static_cast<uint64_t>(w1) << 32);
-  } else if constexpr (BITS == 4 || BITS == 2) {
-    uint32_t ev = 0, od = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      ev = __builtin_amdgcn_cvt_pk_u8_f32(u[2 * j], j, ev);
-      od = __builtin_amdgcn_cvt_pk_u8_f32(u[2 * j + 1], j, od);
-    }
-    if constexpr (BITS == 4) return ev | (od << 4);
-    const uint32_t t = ev | (od << 2);              // byte k: c[2k] | c[2k+1] << 2
-    const uint32_t v = (t | (t >> 4)) & 0x00ff00ffu; // byte 0: c0..c3, byte 2: c4..c7
-    return (v & 0xffu) | ((v >> 8) & 0xff00u);
-  } else {  // BITS == 3
-    uint32_t w = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) w |= static_cast<uint32_t>(__builtin_rintf(u[j])) << (3 * j);
-    return w;
-  }
-}
 
 // EARLY: the destination's reads go out around the row's load (the start
 // position before it, the block-table entry after it), so they overlap the
@@ -224,14 +127,7 @@ __device__ __forceinline__ void append_rows(const AppendArgs& a, int half, doubl
   if constexpr (EARLY) read_table();
 
   // ---- rotate ----
-  {
-    double xd[CPR];
-#pragma unroll
-    for (int j = 0; j < CPR; ++j) xd[j] = static_cast<double>(x[j]);
-    fwht_row_f64<CPR>(xd, m, a.had_block);
-#pragma unroll
-    for (int j = 0; j < CPR; ++j) x[j] = static_cast<float>(xd[j] * rs_n);
-  }
+  rotate_row<CPR>(x, m, a.had_block, rs_n);
 
   if constexpr (!EARLY) {
     read_start();
@@ -244,93 +140,14 @@ __device__ __forceinline__ void append_rows(const AppendArgs& a, int half, doubl
   uint8_t* dst = store ? a.pool + blk * a.block_bytes + area + slot * RB + m * (CPR * BITS / 8) : nullptr;
 
   if constexpr (BITS == 16) {
-    if (store) {
-#pragma unroll
-      for (int k = 0; k < CPR / 8; ++k) {
-        uint4 w;
-        w.x = f_to_bf16_rne(x[8 * k + 0]) | (f_to_bf16_rne(x[8 * k + 1]) << 16);
-        w.y = f_to_bf16_rne(x[8 * k + 2]) | (f_to_bf16_rne(x[8 * k + 3]) << 16);
-        w.z = f_to_bf16_rne(x[8 * k + 4]) | (f_to_bf16_rne(x[8 * k + 5]) << 16);
-        w.w = f_to_bf16_rne(x[8 * k + 6]) | (f_to_bf16_rne(x[8 * k + 7]) << 16);
-        reinterpret_cast<uint4*>(dst)[k] = w;
-      }
-    }
+    if (store) store_row_bf16<CPR>(x, dst);
   } else {
-    // ---- row min / max: this lane's values, then the row's four lanes ----
-    float mn = x[0], mx = x[0];
-#pragma unroll
-    for (int j = 1; j < CPR; ++j) { mn = fminf(mn, x[j]); mx = fmaxf(mx, x[j]); }
-    mn = fminf(mn, dpp_f32<kDppXor1>(mn));
-    mx = fmaxf(mx, dpp_f32<kDppXor1>(mx));
-    mn = fminf(mn, dpp_f32<kDppXor2>(mn));
-    mx = fmaxf(mx, dpp_f32<kDppXor2>(mx));
-    const float qmax = static_cast<float>((1 << BITS) - 1);
-    float s = 0.f, inv = 0.f;
-    uint32_t meta_h = 0;  // float16 pair (s low, mn high)
-    if (a.meta16) {
-      // float16 metadata: the minimum rounded down and the scale up, so the
-      // pair still bounds the row; the codes are taken against them
-      const uint32_t mnh = f16_down(mn);
-      mn = f16_to_f(mnh);
-      const float rng = mx - mn;
-      uint32_t sh = 0;
-      if (rng > 0.f) {
-        sh = f16_up(rng / qmax);
-        s = f16_to_f(sh);
-        inv = 1.f / s;
-      }
-      meta_h = sh | (mnh << 16);
-    } else {
-      const float rng = mx - mn;
-      if (rng > 0.f) {
-        s = rng / qmax;  // IEEE division (correctly rounded)
-        inv = qmax / rng;
-      }
-    }
-    // ---- quantize and pack this lane's CPR codes ----
-    float u[CPR];
-#pragma unroll
-    for (int j = 0; j < CPR; ++j) u[j] = (x[j] - mn) * inv;
-    uint64_t g[CPR / 8];
-#pragma unroll
-    for (int k = 0; k < CPR / 8; ++k) g[k] = pack8<BITS>(u + 8 * k);
+    // ---- row min / max over the quad, the metadata, then the codes ----
+    RowQ<CPR> q;
+    quantize_row<BITS, CPR>(x, a.meta16 != 0, q);
     if (store) {
-      if constexpr (BITS == 4) {
-        if constexpr (CPR == 32)
-          *reinterpret_cast<uint4*>(dst) = make_uint4(static_cast<uint32_t>(g[0]), static_cast<uint32_t>(g[1]),
-                                                      static_cast<uint32_t>(g[2]), static_cast<uint32_t>(g[3]));
-        else
-          *reinterpret_cast<uint2*>(dst) = make_uint2(static_cast<uint32_t>(g[0]), static_cast<uint32_t>(g[1]));
-      } else if constexpr (BITS == 2) {
-        if constexpr (CPR == 32)
-          *reinterpret_cast<uint2*>(dst) = make_uint2(static_cast<uint32_t>(g[0] | (g[1] << 16)),
-                                                      static_cast<uint32_t>(g[2] | (g[3] << 16)));
-        else
-          *reinterpret_cast<uint32_t*>(dst) = static_cast<uint32_t>(g[0] | (g[1] << 16));
-      } else if constexpr (BITS == 8) {
-#pragma unroll
-        for (int k = 0; k < CPR / 16; ++k)
-          reinterpret_cast<uint4*>(dst)[k] =
-              make_uint4(static_cast<uint32_t>(g[2 * k]), static_cast<uint32_t>(g[2 * k] >> 32),
-                         static_cast<uint32_t>(g[2 * k + 1]), static_cast<uint32_t>(g[2 * k + 1] >> 32));
-      } else {  // BITS == 3: 24 bits per group of 8
-        if constexpr (CPR == 32) {  // 12 bytes at a 4-byte aligned offset
-          uint32_t* w = reinterpret_cast<uint32_t*>(dst);
-          w[0] = static_cast<uint32_t>(g[0] | (g[1] << 24));
-          w[1] = static_cast<uint32_t>((g[1] >> 8) | (g[2] << 16));
-          w[2] = static_cast<uint32_t>((g[2] >> 16) | (g[3] << 8));
-        } else {  // 6 bytes at a 2-byte aligned offset
-          uint16_t* w = reinterpret_cast<uint16_t*>(dst);
-          w[0] = static_cast<uint16_t>(g[0]);
-          w[1] = static_cast<uint16_t>((g[0] >> 16) | (g[1] << 8));
-          w[2] = static_cast<uint16_t>(g[1] >> 8);
-        }
-      }
-      if (m == 0) {
-        uint8_t* meta = a.pool + blk * a.block_bytes + area + kBlockTokens * RB;
-        if (a.meta16) *reinterpret_cast<uint32_t*>(meta + slot * 4) = meta_h;
-        else *reinterpret_cast<float2*>(meta + slot * kMetaBytes) = make_float2(s, mn);
-      }
+      uint8_t* meta = a.pool + blk * a.block_bytes + area + kBlockTokens * RB + slot * (a.meta16 ? 4 : kMetaBytes);
+      store_row<BITS, CPR>(q, dst, meta, m, a.meta16 != 0);
     }
   }
 }
@@ -495,21 +312,14 @@ __global__ __launch_bounds__(kThreads) void quant_mse_kernel(QuantMseArgs a, dou
         x[4 * k + 0] = w.x; x[4 * k + 1] = w.y; x[4 * k + 2] = w.z; x[4 * k + 3] = w.w;
       }
     }
-    {
-      double xd[CPR];
-#pragma unroll
-      for (int j = 0; j < CPR; ++j) xd[j] = static_cast<double>(x[j]);
-      fwht_row_f64<CPR>(xd, m, a.had_block);
-#pragma unroll
-      for (int j = 0; j < CPR; ++j) x[j] = static_cast<float>(xd[j] * rs_n);
-    }
+    rotate_row<CPR>(x, m, a.had_block, rs_n);
     float mn = x[0], mx = x[0];
 #pragma unroll
     for (int j = 1; j < CPR; ++j) { mn = fminf(mn, x[j]); mx = fmaxf(mx, x[j]); }
-    mn = fminf(mn, dpp_f32<kDppXor1>(mn));
-    mx = fmaxf(mx, dpp_f32<kDppXor1>(mx));
-    mn = fminf(mn, dpp_f32<kDppXor2>(mn));
-    mx = fmaxf(mx, dpp_f32<kDppXor2>(mx));
+    mn = fminf(mn, dpp_f32<kDppQuadXor1>(mn));
+    mx = fmaxf(mx, dpp_f32<kDppQuadXor1>(mx));
+    mn = fminf(mn, dpp_f32<kDppQuadXor2>(mn));
+    mx = fmaxf(mx, dpp_f32<kDppQuadXor2>(mx));
     const float rng = mx - mn;
     if (!active) continue;
 #pragma unroll

@@ -36,6 +36,7 @@
 // kernel merges the splits of all segments and applies R^T.
 #include "kvq_device.h"
 #include "kvq_internal.h"
+#include "kvq_rowq.h"
 
 #include <algorithm>
 #include <cmath>
@@ -426,8 +427,8 @@ constexpr int kStaticEighths = KVQ_TUNE_STATIC_EIGHTHS;
 
 template <int KB, int VB, int D, bool M16, bool KC>
 __device__ __forceinline__ void load_group(const DecodeSeg& a, const uint8_t* pool, const int32_t (&blks)[4],
-                                           int grp, int p1, int seq_len, int64_t koff, int64_t voff, int lane,
-                                           int kc0, int kc1, GroupRaw<KB, VB, D>& g) {
+                                           int grp, int p1, int seq_len, int skip, int64_t koff, int64_t voff,
+                                           int lane, int kc0, int kc1, GroupRaw<KB, VB, D>& g) {
   constexpr int RBK = D * KB / 8, RBV = D * VB / 8, QBYTES = RBK / 4;
   const int tslot = lane & 15, g4 = lane >> 4;
   int64_t boff[4];
@@ -449,7 +450,8 @@ __device__ __forceinline__ void load_group(const DecodeSeg& a, const uint8_t* po
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp) load_kquarter<KB, D>(pool + boff[pp] + koff + kl, g.k[pp]);
   // token layout: lane = (page g4, slot tslot); each page's metadata by its 16 lanes
-  g.valid = ((pv >> g4) & 1u) && (grp + g4) * kBlockTokens + tslot < seq_len;
+  const int tpos = (grp + g4) * kBlockTokens + tslot;
+  g.valid = ((pv >> g4) & 1u) && tpos < seq_len && tpos != skip;
   // (all lanes active: a load under a divergent branch would make the compiler
   // wait for every outstanding load, including the prefetch)
   const int64_t my_boff = (g4 & 2) ? ((g4 & 1) ? boff[3] : boff[2]) : ((g4 & 1) ? boff[1] : boff[0]);
@@ -494,7 +496,8 @@ __device__ __forceinline__ void load_group(const DecodeSeg& a, const uint8_t* po
     for (int e = 0; e < 8; ++e) {
       const int pg = 2 * pp2 + (e >> 2);
       load_vtoken<VB, D>(pool + boff[pg] + voff + 4 * (e & 3) * RBV + vl, g.v[pp2][e]);
-      const bool ok = ((pv >> pg) & 1u) && (grp + pg) * kBlockTokens + 4 * (e & 3) + g4 < seq_len;
+      const int vpos = (grp + pg) * kBlockTokens + 4 * (e & 3) + g4;
+      const bool ok = ((pv >> pg) & 1u) && vpos < seq_len && vpos != skip;
       g.vmask |= static_cast<uint32_t>(ok) << (8 * pp2 + e);
     }
   }
@@ -517,14 +520,14 @@ struct PrefetchDepth {
 };
 
 // The wide formats (8- and 16-bit keys, bf16 values, and the 8-bit values
-// beside 4-bit keys at head_dim 128; 16-bit keys beside 3- or 16-bit values and
-// 8-bit keys beside bf16 values at head_dim 64) need more than half the
-// register file: one wave per SIMD. The choice is checked by compiling every
-// instance and requiring zero spills.
+// beside 3- or 4-bit keys at head_dim 128; 16-bit keys beside 3- or 16-bit
+// values and 8-bit keys beside bf16 values at head_dim 64) need more than half
+// the register file: one wave per SIMD. The choice is checked by compiling
+// every instance and requiring zero spills.
 template <int KB, int VB, int D>
 struct PartialWaves {
   static constexpr bool wide =
-      D == 128 ? (VB == 16 || KB == 16 || KB == 8 || (KB == 4 && VB == 8))
+      D == 128 ? (VB == 16 || KB == 16 || KB == 8 || ((KB == 4 || KB == 3) && VB == 8))
                : ((KB == 16 && (VB == 3 || VB == 16)) || (KB == 8 && VB == 16));
   static constexpr int value = wide ? 1 : (D == 128 ? KVQ_TUNE_WAVES128 : 2);
 };
@@ -817,6 +820,9 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, int si, int L
   const int hq = a.hkv * G;
   const int64_t koff = a.k_off[he], voff = a.v_off[he];
   const int seq_len = sg.seq_lens[b];
+  // the slot a fused append fills in this call: masked here (its old bytes
+  // are read), attended to by the merge kernel from the new values
+  const int skip = sg.skip_pos ? sg.skip_pos[b] : -1;
   const int pages = min((seq_len + kBlockTokens - 1) / kBlockTokens, sg.table_stride);
   const int slot = sg.slot_base + split;
 
@@ -961,7 +967,8 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, int si, int L
     for (int pp = 0; pp < 4; ++pp) blks[pp] = __builtin_amdgcn_readlane(next_tab, tab_lane + pp);
     resolve();
     g.gid = gid;
-    load_group<KB, VB, D, M16, KC>(sg, pool, blks, 4 * (g_lo + gid), pages, seq_len, koff, voff, lane, kc0, kc1, g);
+    load_group<KB, VB, D, M16, KC>(sg, pool, blks, 4 * (g_lo + gid), pages, seq_len, skip, koff, voff, lane, kc0,
+                                     kc1, g);
   };
 #pragma unroll
   for (int j = 0; j < DEPTH; ++j) load_next(gbuf[j]);
@@ -1206,6 +1213,102 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, int si, int L
   }
 }
 
+// Fused append: a group of LPR lanes per row (lanes [0, LPR): the K row,
+// [LPR, 2 LPR): the V row; 16 channels a lane, so 8 lanes per row at head_dim
+// 128) quantizes the new token's row of head h as the append kernel does (the
+// same rotation, metadata and codes: the shared row routines; any lane split
+// of the exact rotation gives the same values), stores it at slot `slot` of
+// `page` (null: not stored) and leaves its dequantized rotated values
+// x_hat = c * s + mn (a rounded product, then a rounded sum; bf16 rows: the
+// rounded value) in `rows` (global memory).
+template <int D>
+struct AppendLanes {
+  static constexpr int CPR = 16, LPR = D / CPR;
+};
+
+template <int BITS, int D>
+__device__ __forceinline__ void token_append_quant(const TokenAppend& ap, float (&x)[AppendLanes<D>::CPR], int m,
+                                                   uint8_t* page, int64_t off, int slot, float* row) {
+  constexpr int CPR = AppendLanes<D>::CPR, LPR = AppendLanes<D>::LPR, RB = D * BITS / 8;
+  if constexpr (BITS == 16) {
+    if (page) store_row_bf16<CPR>(x, page + off + slot * RB + m * (CPR * 2));
+#pragma unroll
+    for (int j = 0; j < CPR; ++j) row[m * CPR + j] = bf16lo_to_f(f_to_bf16_rne(x[j]));
+  } else {
+    RowQ<CPR> q;
+    quantize_row<BITS, CPR, LPR>(x, ap.meta16 != 0, q);
+    if (page)
+      store_row<BITS, CPR>(q, page + off + slot * RB + m * (CPR * BITS / 8),
+                           page + off + kBlockTokens * RB + slot * (ap.meta16 ? 4 : kMetaBytes), m, ap.meta16 != 0);
+#pragma unroll
+    for (int j = 0; j < CPR; ++j) row[m * CPR + j] = __fadd_rn(__fmul_rn(__builtin_rintf(q.u[j]), q.s), q.mn);
+  }
+}
+
+// lane: 0 .. 2 * LPR - 1
+template <int D>
+__device__ __forceinline__ void token_append_row(const TokenAppend& ap, int had_block, int b, int h, int hkv,
+                                                 int lane, uint8_t* page, int slot, float (*rows)[D]) {
+  constexpr int CPR = AppendLanes<D>::CPR, LPR = AppendLanes<D>::LPR;
+  const int m = lane % LPR, half = lane / LPR;
+  float x[CPR];
+  const size_t elem = (static_cast<size_t>(b) * hkv + h) * D + m * CPR;
+  const void* src = half ? ap.v_new : ap.k_new;
+  if (ap.src_bf16) {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + elem);
+#pragma unroll
+    for (int k = 0; k < CPR / 8; ++k) {
+      const uint4 w = p[k];
+      x[8 * k + 0] = bf16lo_to_f(w.x); x[8 * k + 1] = bf16hi_to_f(w.x);
+      x[8 * k + 2] = bf16lo_to_f(w.y); x[8 * k + 3] = bf16hi_to_f(w.y);
+      x[8 * k + 4] = bf16lo_to_f(w.z); x[8 * k + 5] = bf16hi_to_f(w.z);
+      x[8 * k + 6] = bf16lo_to_f(w.w); x[8 * k + 7] = bf16hi_to_f(w.w);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(src) + elem);
+#pragma unroll
+    for (int k = 0; k < CPR / 4; ++k) {
+      const float4 w = p[k];
+      x[4 * k + 0] = w.x; x[4 * k + 1] = w.y; x[4 * k + 2] = w.z; x[4 * k + 3] = w.w;
+    }
+  }
+  rotate_row<CPR, LPR>(x, m, had_block, ap.rs_n);
+  const int64_t off = half ? ap.v_off[h] : ap.k_off[h];
+  float* row = rows[half];
+  switch (half ? ap.bits_v[h] : ap.bits_k[h]) {
+    case 2: token_append_quant<2, D>(ap, x, m, page, off, slot, row); break;
+    case 3: token_append_quant<3, D>(ap, x, m, page, off, slot, row); break;
+    case 4: token_append_quant<4, D>(ap, x, m, page, off, slot, row); break;
+    case 8: token_append_quant<8, D>(ap, x, m, page, off, slot, row); break;
+    default: token_append_quant<16, D>(ap, x, m, page, off, slot, row); break;  // the host sends 2, 3, 4, 8, 16
+  }
+}
+
+// The split-0 wave of each (sequence, KV head) of the segment that writes q~
+// also appends the call's new token of that head (a fused append), before its
+// own pages: one wave per (sequence, KV head) stores it, and the merge reads
+// its dequantized rows from the workspace. (Other waves may read the slot's
+// old bytes meanwhile; the slot is masked for all of them.)
+template <int D>
+__device__ __forceinline__ void partial_append_job(const DecodeArgs& a, int si, int L) {
+  const DecodeSeg& sg = a.seg[si];
+  const TokenAppend& ap = a.ap;
+  if (!ap.pool || !sg.write_q) return;
+  const int U = sg.n_heads * a.batch;
+  if (L % kXcds != 0 || L / kXcds >= U) return;  // not split 0
+  const int unit = L / kXcds, b = unit / sg.n_heads;
+  const int h = a.heads[sg.head_base + unit % sg.n_heads];
+  const int pos = ap.start_pos[b];
+  if (pos < 0) return;
+  const int pg = pos / kBlockTokens;
+  const int32_t blk = pg < ap.table_stride ? ap.table[static_cast<int64_t>(b) * ap.table_stride + pg] : -1;
+  uint8_t* page = blk >= 0 && blk < ap.pool_blocks ? ap.pool + blk * ap.block_bytes : nullptr;
+  const int lane = threadIdx.x;
+  if (lane < 2 * AppendLanes<D>::LPR)
+    token_append_row<D>(ap, a.had_block, b, h, a.hkv, lane, page, pos % kBlockTokens,
+                        reinterpret_cast<float (*)[D]>(a.anew + (static_cast<int64_t>(b) * a.hkv + h) * 2 * D));
+}
+
 template <int KB, int VB, int D, bool M16>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PartialWaves<KB, VB, D>::value,
                                                                     PartialWaves<KB, VB, D>::value)))
@@ -1214,6 +1317,7 @@ void decode_partial_kernel(DecodeArgs a, const int32_t* __restrict__ table, uint
   // (table and counters as separate restrict arguments: the counters' atomics
   // cannot alias the block table, so its entries stay scalar loads)
   __shared__ PartialLds<D> lds;
+  partial_append_job<D>(a, 0, static_cast<int>(blockIdx.x));
   partial_split<KB, VB, D, M16>(a, 0, static_cast<int>(blockIdx.x), table, steal, qscale, lds);
 }
 
@@ -1234,6 +1338,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KcWaves<KB, 
 void decode_partial_kc_kernel(DecodeArgs a, const int32_t* __restrict__ table, uint32_t* __restrict__ steal,
                               float qscale) {
   __shared__ PartialLds<D> lds;
+  partial_append_job<D>(a, 0, static_cast<int>(blockIdx.x));
   partial_split<KB, VB, D, false, true>(a, 0, static_cast<int>(blockIdx.x), table, steal, qscale, lds);
 }
 
@@ -1257,6 +1362,7 @@ void decode_partial_multi_kernel(DecodeArgs a, float qscale) {
   const int pair = __builtin_amdgcn_readfirstlane(a.pair[sg.head_base + unit % sg.n_heads]);
   const int32_t* table = sg.table;
   uint32_t* steal = sg.steal;
+  partial_append_job<D>(a, si, L);
   switch (pair) {
     case 0x22: partial_split<2, 2, D, M16>(a, si, L, table, steal, qscale, lds); break;
     case 0x23: partial_split<2, 3, D, M16>(a, si, L, table, steal, qscale, lds); break;
@@ -1284,6 +1390,8 @@ void decode_partial_multi_kernel(DecodeArgs a, float qscale) {
 // launch: its scores z_t = q~ . k'_t (q~ written by the partial launch, k'_t
 // the stored rotated row, log2 units as in the partials), then its weights
 // 2^(z_t - M) and weighted rows enter the same sums as the split partials'.
+__device__ __forceinline__ bool ap_pool(const MergeArgs& a) { return a.ap.pool != nullptr; }
+
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) void decode_merge_kernel(MergeArgs a, float rs_n) {
   constexpr int CPL = D / 64;  // channels per lane: [CPL*lane, CPL*lane + CPL)
@@ -1311,6 +1419,33 @@ __global__ __launch_bounds__(64 * NW) void decode_merge_kernel(MergeArgs a, floa
     ok = static_cast<uint32_t>(blk) < wblocks;
     return win.pool + (ok ? blk : 0) * win.block_bytes + off + (t % kBlockTokens) * (D * 2);
   };
+  const int wskip = win.pool && win.skip_pos ? win.skip_pos[b] : -1;  // the window slot a fused append fills
+  // q~ of this query head (written by the partial launch), read first: its
+  // round trip overlaps the preloads
+  const bool need_q = nwin > 0 || ap_pool(a);
+  const float qv = need_q && tid < D ? a.qrot[bg * D + tid] : 0.f;
+  // Fused append: the partial launch quantized and stored the new token and
+  // left its dequantized rows in anew; it is attended to below when its slot
+  // is mapped and inside the segment's length.
+  const TokenAppend& ap = a.ap;
+  bool attend_new = false;
+  float anew_k[CPL], anew_v[CPL];  // (wave 0) the new token's rows, CPL channels a lane
+  if (ap.pool) {
+    const int pos = ap.start_pos[b];
+    if (pos >= 0) {
+      const int pg = pos / kBlockTokens;
+      const int32_t blk = pg < ap.table_stride ? ap.table[static_cast<int64_t>(b) * ap.table_stride + pg] : -1;
+      attend_new = blk >= 0 && blk < ap.pool_blocks && pos < min(ap.seq_lens[b], ap.max_len);
+    }
+    if (attend_new && w == 0) {
+      const float* rows = a.anew + (static_cast<int64_t>(b) * (a.hq / a.group) + h) * 2 * D + CPL * lane;
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        anew_k[j] = rows[j];
+        anew_v[j] = rows[D + j];
+      }
+    }
+  }
   // This wave's first batch of split slots (w, w + NW, ... of the first chunk,
   // padded with the chunk's last slot) and of window value rows (tokens w,
   // w + NW, ...), loaded before the max is known: the values do not depend
@@ -1337,6 +1472,7 @@ __global__ __launch_bounds__(64 * NW) void decode_merge_kernel(MergeArgs a, floa
                            (tc % kBlockTokens) * (D * 2);
       if constexpr (CPL == 2) wraw0[u] = *reinterpret_cast<const uint32_t*>(row);
       else wraw0[u] = *reinterpret_cast<const uint16_t*>(row);
+      if (tc == wskip) wraw0[u] = 0u;  // (the slot's old bytes may not be a number)
     }
   }
   // global max over splits and window tokens (the splits' maxima read before
@@ -1358,8 +1494,8 @@ __global__ __launch_bounds__(64 * NW) void decode_merge_kernel(MergeArgs a, floa
     for (int c = 0; c < CH / 8; ++c) k0[c] = row[c];
     blk0 = ok ? win.table[static_cast<int64_t>(b) * win.table_stride + t / kBlockTokens] : -1;
   }
-  if (nwin > 0) {
-    if (tid < D) wq[tid] = a.qrot[bg * D + tid];
+  if (need_q) {
+    if (tid < D) wq[tid] = qv;
     __syncthreads();
   }
   {
@@ -1385,13 +1521,22 @@ __global__ __launch_bounds__(64 * NW) void decode_merge_kernel(MergeArgs a, floa
       z += xor_lanes16<1>(z, lane);
       z += xor_lanes16<2>(z, lane);
       z += xor_lanes16<4>(z, lane);
-      z = ok ? z : NEG_INF;
+      z = ok && t != wskip ? z : NEG_INF;
       if (part == 0 && t0 < nwin) {
         wz[t] = z;
         wrow[t] = !ok ? 0 : first ? blk0 : win.table[static_cast<int64_t>(b) * win.table_stride + t / kBlockTokens];
       }
       if (t0 < nwin) mx = fmaxf(mx, z);
     }
+  }
+  // the fused append's token: its score from q~ (in LDS) and its K row
+  float z_new = NEG_INF;
+  if (attend_new && w == 0) {
+    float t = 0.f;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) t = fmaf(wq[CPL * lane + j], anew_k[j], t);
+    z_new = wave_sum_scalar(t);
+    mx = fmaxf(mx, z_new);
   }
   mx = wave_max_scalar(mx);
   if (lane == 0) scal[w][0] = mx;
@@ -1459,6 +1604,7 @@ __global__ __launch_bounds__(64 * NW) void decode_merge_kernel(MergeArgs a, floa
             const uint8_t* row = vbase + wrow[tc] * win.block_bytes + (tc % kBlockTokens) * (D * 2);
             if constexpr (CPL == 2) raw[u] = *reinterpret_cast<const uint32_t*>(row);
             else raw[u] = *reinterpret_cast<const uint16_t*>(row);
+            if (tc == wskip) raw[u] = 0u;  // (the slot's old bytes may not be a number)
           }
           pw[u] = tu < nwin ? wz[tc] : 0.f;
         }
@@ -1468,6 +1614,12 @@ __global__ __launch_bounds__(64 * NW) void decode_merge_kernel(MergeArgs a, floa
           if constexpr (CPL == 2) x[1] = fmaf(pw[u], bf16hi_to_f(raw[u]), x[1]);
         }
       }
+    }
+    if (attend_new && w == 0) {
+      const float p = __builtin_amdgcn_exp2f(z_new - mx);
+      if (lane == 0) lpart += p;
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) x[j] = fmaf(p, anew_v[j], x[j]);
     }
   }
   // combine the waves

@@ -266,7 +266,9 @@ struct CallPlan {
   int q_writer = -1;
 };
 
-CallPlan plan_call(const kvq_segment* segs, int n_segs, int batch) {
+// need_q: the merge needs q~ (a fused append's token is attended to there),
+// so some segment's split-0 waves write it even without a window.
+CallPlan plan_call(const kvq_segment* segs, int n_segs, int batch, bool need_q = false) {
   CallPlan c;
   c.split.resize(n_segs);
   for (int i = 0; i < n_segs; ++i) c.split[i] = plan_splits(segs[i], batch);
@@ -303,29 +305,70 @@ CallPlan plan_call(const kvq_segment* segs, int n_segs, int batch) {
       c.split[big].n_splits = std::min(c.split[big].n_splits, std::max(fit, 8));
     }
   }
+  if (need_q && c.q_writer < 0)
+    for (int i = 0; i < n_segs && c.q_writer < 0; ++i)
+      if (c.split[i].n_splits > 0) c.q_writer = i;
   for (int i = 0; i < n_segs; ++i) c.slots += c.split[i].n_splits;
   return c;
 }
 
+// A fused append (kvq_append_decode_attn): one token per sequence into
+// segment `seg` at slot start_pos[b]; the partial launch masks that slot and
+// the merge kernel quantizes, stores and attends to the token.
+struct FusedAppend {
+  int seg;
+  const int32_t* start_pos;
+  const void* k_new;
+  const void* v_new;
+  kvq_dtype dtype;
+};
+
+// The kernels' description of a fused append.
+void fill_token_append(const kvq_segment* segs, const FusedAppend& fa, kvq::TokenAppend& ap) {
+  const kvq_segment& g = segs[fa.seg];
+  const kvq_layout& L = *g.layout;
+  // (the segment's pool is const for decoding; a fused append writes the new rows into it)
+  ap.pool = static_cast<uint8_t*>(const_cast<void*>(g.pool));
+  ap.pool_blocks = g.pool_blocks;
+  ap.block_bytes = L.block_bytes;
+  ap.table = g.block_table;
+  ap.table_stride = g.table_stride;
+  ap.seq_lens = g.seq_lens;
+  ap.start_pos = fa.start_pos;
+  ap.k_new = fa.k_new;
+  ap.v_new = fa.v_new;
+  ap.src_bf16 = fa.dtype == KVQ_BF16;
+  ap.meta16 = L.meta_fp16;
+  ap.max_len = g.max_len;
+  ap.rs_n = 1.0 / std::sqrt(static_cast<double>(L.had_block));  // (as the append kernel's)
+  for (int h = 0; h < L.num_kv_heads; ++h) {
+    ap.k_off[h] = static_cast<int32_t>(L.k_off[h]);
+    ap.v_off[h] = static_cast<int32_t>(L.v_off[h]);
+    ap.bits_k[h] = static_cast<uint8_t>(L.bits_k[h]);
+    ap.bits_v[h] = static_cast<uint8_t>(L.bits_v[h]);
+  }
+}
+
 // Workspace: the work-sharing counter region (KVQ_DECODE_COUNTER_BYTES at the
 // front, zero between calls), then partial o' [batch][hq][slots][d], partial
-// (max, sum) [batch][hq][slots][2], and q~ [batch][hq][d] for a window
-// segment. A call's counters are the first words of the region: per segment
+// (max, sum) [batch][hq][slots][2], q~ [batch][hq][d] for a window segment or a
+// fused append, and a fused append's dequantized rows [batch][hkv][2][d]. A call's counters are the first words of the region: per segment
 // [batch][hkv][splits / 8][2] (uint32); slots is the sum of the segments'
 // splits, so a call takes slots / 8 * batch * hkv * 2 words. The region's
 // place and size do not depend on the split plan, so no call's partials ever
 // land on any call's counters, and one workspace serves calls of any plan.
 constexpr size_t kCounterBytes = KVQ_DECODE_COUNTER_BYTES;
 struct WsLayout {
-  size_t part_o, part_ml, qrot, total;
+  size_t part_o, part_ml, qrot, anew, total;
 };
-WsLayout ws_layout(int batch, int hq, int d, int slots) {
-  const size_t rows = static_cast<size_t>(batch) * hq, s1 = static_cast<size_t>(std::max(slots, 1));
+WsLayout ws_layout(int batch, int hkv, int group, int d, int slots) {
+  const size_t rows = static_cast<size_t>(batch) * hkv * group, s1 = static_cast<size_t>(std::max(slots, 1));
   WsLayout w;
   w.part_o = kCounterBytes;
   w.part_ml = w.part_o + rows * s1 * d * sizeof(float);
   w.qrot = w.part_ml + rows * s1 * 2 * sizeof(float);
-  w.total = w.qrot + rows * d * sizeof(float);
+  w.anew = w.qrot + rows * d * sizeof(float);
+  w.total = w.anew + static_cast<size_t>(batch) * hkv * 2 * d * sizeof(float);
   return w;
 }
 // Counter words a call with this plan uses; more than the region holds sends
@@ -875,7 +918,7 @@ kvq_status kvq_decode_workspace_bytes(const kvq_segment* segs, int32_t n_segs, i
   kvq_status st = check_segments(segs, n_segs, batch, "kvq_decode_workspace_bytes");
   if (st != KVQ_OK) return st;
   const kvq_layout& L = *segs[0].layout;
-  *bytes = ws_layout(batch, L.num_kv_heads * L.group, L.head_dim, plan_call(segs, n_segs, batch).slots).total;
+  *bytes = ws_layout(batch, L.num_kv_heads, L.group, L.head_dim, plan_call(segs, n_segs, batch).slots).total;
   return ok();
 }
 
@@ -898,7 +941,8 @@ kvq_status kvq_decode_workspace_init(void* ws, size_t ws_bytes, kvq_stream strea
 // The partial launches of one decode call. serial: every launch goes on the
 // caller's stream, one after another (no side streams are created or used).
 static kvq_status decode_partial_impl(const kvq_segment* segs, int32_t n_segs, int32_t batch, const void* q,
-                                      kvq_dtype q_dtype, void* ws, size_t ws_bytes, kvq_stream stream, bool serial) {
+                                      kvq_dtype q_dtype, void* ws, size_t ws_bytes, kvq_stream stream, bool serial,
+                                      const FusedAppend* fa = nullptr) {
   kvq_status st = check_segments(segs, n_segs, batch, "kvq_decode_partial");
   if (st != KVQ_OK) return st;
   if (q_dtype != KVQ_F32 && q_dtype != KVQ_BF16) return fail(KVQ_ERR_ARG, "kvq_decode_partial: bad q dtype");
@@ -908,8 +952,8 @@ static kvq_status decode_partial_impl(const kvq_segment* segs, int32_t n_segs, i
   const kvq_layout& L0 = *segs[0].layout;
   const int hq = L0.num_kv_heads * L0.group;
   const int d = L0.head_dim;
-  const CallPlan plan = plan_call(segs, n_segs, batch);
-  const WsLayout wl = ws_layout(batch, hq, d, plan.slots);
+  const CallPlan plan = plan_call(segs, n_segs, batch, fa != nullptr);
+  const WsLayout wl = ws_layout(batch, L0.num_kv_heads, L0.group, d, plan.slots);
   if (ws_bytes < wl.total)
     return fail(KVQ_ERR_WORKSPACE, "kvq_decode_partial: workspace %zu < %zu bytes", ws_bytes, wl.total);
   uint32_t* steal = static_cast<uint32_t*>(ws);
@@ -930,6 +974,10 @@ static kvq_status decode_partial_impl(const kvq_segment* segs, int32_t n_segs, i
   base.part_o = reinterpret_cast<float*>(wsb + wl.part_o);
   base.part_ml = reinterpret_cast<float*>(wsb + wl.part_ml);
   base.qrot = reinterpret_cast<float*>(wsb + wl.qrot);
+  if (fa) {
+    fill_token_append(segs, *fa, base.ap);
+    base.anew = reinterpret_cast<float*>(wsb + wl.anew);
+  }
 
   std::vector<int> slot_base(n_segs, 0);
   for (int i = 1; i < n_segs; ++i) slot_base[i] = slot_base[i - 1] + plan.split[i - 1].n_splits;
@@ -949,7 +997,8 @@ static kvq_status decode_partial_impl(const kvq_segment* segs, int32_t n_segs, i
     ds.grid_start = grid_start;
     ds.n_heads = n_heads;
     ds.head_base = head_base;
-    ds.write_q = i == plan.q_writer && plan.window >= 0;
+    ds.write_q = i == plan.q_writer;
+    ds.skip_pos = fa && i == fa->seg ? fa->start_pos : nullptr;
     return ds;
   };
   struct Launch {
@@ -1150,16 +1199,18 @@ kvq_status kvq_measure_read_paged(const kvq_segment* segs, int32_t n_segs, int32
   return ok();
 }
 
-kvq_status kvq_decode_merge(const kvq_segment* segs, int32_t n_segs, int32_t batch, float* out, void* ws,
-                            size_t ws_bytes, kvq_stream stream) {
+}  // extern "C"
+
+static kvq_status decode_merge_impl(const kvq_segment* segs, int32_t n_segs, int32_t batch, float* out, void* ws,
+                                    size_t ws_bytes, kvq_stream stream, const FusedAppend* fa) {
   kvq_status st = check_segments(segs, n_segs, batch, "kvq_decode_merge");
   if (st != KVQ_OK) return st;
   if (batch == 0) return ok();
   if (!out || !ws) return fail(KVQ_ERR_ARG, "kvq_decode_merge: null output or workspace");
   const kvq_layout& L0 = *segs[0].layout;
   const int hq = L0.num_kv_heads * L0.group;
-  const CallPlan plan = plan_call(segs, n_segs, batch);
-  const WsLayout wl = ws_layout(batch, hq, L0.head_dim, plan.slots);
+  const CallPlan plan = plan_call(segs, n_segs, batch, fa != nullptr);
+  const WsLayout wl = ws_layout(batch, L0.num_kv_heads, L0.group, L0.head_dim, plan.slots);
   if (ws_bytes < wl.total)
     return fail(KVQ_ERR_WORKSPACE, "kvq_decode_merge: workspace %zu < %zu bytes", ws_bytes, wl.total);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -1185,13 +1236,25 @@ kvq_status kvq_decode_merge(const kvq_segment* segs, int32_t n_segs, int32_t bat
     a.win.table = w.block_table;
     a.win.table_stride = w.table_stride;
     a.win.seq_lens = w.seq_lens;
+    a.win.skip_pos = fa && fa->seg == plan.window ? fa->start_pos : nullptr;
     a.win.max_len = w.max_len;
     for (int h = 0; h < w.layout->num_kv_heads; ++h) {
       a.win.k_off[h] = w.layout->k_off[h];
       a.win.v_off[h] = w.layout->v_off[h];
     }
   }
+  if (fa) {
+    fill_token_append(segs, *fa, a.ap);
+    a.anew = reinterpret_cast<const float*>(wsb + wl.anew);
+  }
   return device_status(kvq::launch_decode_merge(a, s), "kvq_decode_merge launch");
+}
+
+extern "C" {
+
+kvq_status kvq_decode_merge(const kvq_segment* segs, int32_t n_segs, int32_t batch, float* out, void* ws,
+                            size_t ws_bytes, kvq_stream stream) {
+  return decode_merge_impl(segs, n_segs, batch, out, ws, ws_bytes, stream, nullptr);
 }
 
 kvq_status kvq_decode_attn(const kvq_segment* segs, int32_t n_segs, int32_t batch, const void* q, kvq_dtype q_dtype,
@@ -1199,6 +1262,72 @@ kvq_status kvq_decode_attn(const kvq_segment* segs, int32_t n_segs, int32_t batc
   kvq_status st = kvq_decode_partial(segs, n_segs, batch, q, q_dtype, ws, ws_bytes, stream);
   if (st != KVQ_OK) return st;
   return kvq_decode_merge(segs, n_segs, batch, out, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+// The fused append's own argument checks (before any launch); the segments
+// are checked by the partial and merge calls.
+static kvq_status check_fused(const kvq_segment* segs, int32_t n_segs, int32_t batch, int32_t append_seg,
+                              const int32_t* start_pos, const void* k_new, const void* v_new, kvq_dtype in_dtype,
+                              bool rows, const char* who) {
+  kvq_status st = check_segments(segs, n_segs, batch, who);
+  if (st != KVQ_OK) return st;
+  if (append_seg < 0 || append_seg >= n_segs)
+    return fail(KVQ_ERR_ARG, "%s: append_seg %d outside [0, %d)", who, append_seg, n_segs);
+  const kvq_segment& g = segs[append_seg];
+  if (g.layout->key_per_channel)
+    return fail(KVQ_ERR_UNSUPPORTED, "%s: per-channel keys are appended in whole blocks (kvq_quantize_append)", who);
+  if (batch == 0) return ok();
+  if (!start_pos) return fail(KVQ_ERR_ARG, "%s: null start_pos", who);
+  if (!rows) return ok();
+  if (in_dtype != KVQ_F32 && in_dtype != KVQ_BF16) return fail(KVQ_ERR_ARG, "%s: bad input dtype", who);
+  if (!k_new || !v_new) return fail(KVQ_ERR_ARG, "%s: null k_new or v_new", who);
+  if (reinterpret_cast<uintptr_t>(k_new) % 16 != 0 || reinterpret_cast<uintptr_t>(v_new) % 16 != 0)
+    return fail(KVQ_ERR_ARG, "%s: k_new and v_new must be 16-byte aligned", who);
+  if (!g.pool || !g.block_table || !g.seq_lens) return fail(KVQ_ERR_ARG, "%s: null pool, table or lengths", who);
+  return ok();
+}
+
+extern "C" {
+
+// The partial half quantizes and stores the new token (its split-0 waves) and
+// needs the new rows; the merge half reads the token's dequantized rows from
+// the workspace and needs only where the token went.
+kvq_status kvq_append_decode_partial(const kvq_segment* segs, int32_t n_segs, int32_t batch, int32_t append_seg,
+                                     const int32_t* start_pos, const void* k_new, const void* v_new,
+                                     kvq_dtype in_dtype, const void* q, kvq_dtype q_dtype, void* ws,
+                                     size_t ws_bytes, kvq_stream stream) {
+  kvq_status st = check_fused(segs, n_segs, batch, append_seg, start_pos, k_new, v_new, in_dtype, true,
+                              "kvq_append_decode_partial");
+  if (st != KVQ_OK || batch == 0) return st;
+  const FusedAppend fa{append_seg, start_pos, k_new, v_new, in_dtype};
+  return decode_partial_impl(segs, n_segs, batch, q, q_dtype, ws, ws_bytes, stream, false, &fa);
+}
+
+kvq_status kvq_append_decode_merge(const kvq_segment* segs, int32_t n_segs, int32_t batch, int32_t append_seg,
+                                   const int32_t* start_pos, float* out, void* ws, size_t ws_bytes,
+                                   kvq_stream stream) {
+  kvq_status st = check_fused(segs, n_segs, batch, append_seg, start_pos, nullptr, nullptr, KVQ_BF16, false,
+                              "kvq_append_decode_merge");
+  if (st != KVQ_OK || batch == 0) return st;
+  // (the merge kernel reads no new row: only the slot, its page and the lengths)
+  const FusedAppend fa{append_seg, start_pos, nullptr, nullptr, KVQ_BF16};
+  return decode_merge_impl(segs, n_segs, batch, out, ws, ws_bytes, stream, &fa);
+}
+
+kvq_status kvq_append_decode_attn(const kvq_segment* segs, int32_t n_segs, int32_t batch, int32_t append_seg,
+                                  const int32_t* start_pos, const void* k_new, const void* v_new, kvq_dtype in_dtype,
+                                  const void* q, kvq_dtype q_dtype, float* out, void* ws, size_t ws_bytes,
+                                  kvq_stream stream) {
+  // (every argument checked before the first launch)
+  kvq_status st = check_fused(segs, n_segs, batch, append_seg, start_pos, k_new, v_new, in_dtype, true,
+                              "kvq_append_decode_attn");
+  if (st != KVQ_OK || batch == 0) return st;
+  st = kvq_append_decode_partial(segs, n_segs, batch, append_seg, start_pos, k_new, v_new, in_dtype, q, q_dtype,
+                                 ws, ws_bytes, stream);
+  if (st != KVQ_OK) return st;
+  return kvq_append_decode_merge(segs, n_segs, batch, append_seg, start_pos, out, ws, ws_bytes, stream);
 }
 
 }  // extern "C"
@@ -1252,7 +1381,8 @@ kvq_status kvq_decode_attn_noalloc(const kvq_segment* segs, int32_t n_segs, int3
   if (batch == 0) return ok();
   if (!q || !out) return fail(KVQ_ERR_ARG, "%s: null q or output", who);
   const kvq_layout& L0 = *segs[0].layout;
-  const size_t need = ws_layout(batch, L0.num_kv_heads * L0.group, L0.head_dim, plan_call(segs, n_segs, batch).slots).total;
+  const size_t need =
+      ws_layout(batch, L0.num_kv_heads, L0.group, L0.head_dim, plan_call(segs, n_segs, batch).slots).total;
   if (need > kNoallocScratchBytes)
     return fail(KVQ_ERR_WORKSPACE, "%s: this call needs %zu bytes of scratch, more than the fixed %zu", who, need,
                 kNoallocScratchBytes);

@@ -55,6 +55,7 @@ struct DecodeSeg {
   const int32_t* table;
   int32_t table_stride;
   const int32_t* seq_lens;
+  const int32_t* skip_pos;  // [batch] slot to mask (the token a fused append adds; the merge attends to it), or null
   uint32_t* steal;     // [batch][hkv][splits / 8][2] work-sharing counters of this segment (zero between calls)
   int32_t slot_base;   // first split slot of this segment
   int32_t n_splits;    // splits per (sequence, KV head), a multiple of 8
@@ -62,6 +63,32 @@ struct DecodeSeg {
   int32_t n_heads;
   int32_t head_base;
   int32_t write_q;     // 1: the waves of split 0 write their unit's q~ to qrot
+};
+
+// The one token per sequence a fused append adds (kvq_append_decode_attn):
+// row b of k_new and v_new is quantized into the segment's pool at slot
+// start_pos[b] exactly as the append kernel would, by the partial launch's
+// split-0 wave of each (sequence, KV head) (the wave that writes q~), which
+// also leaves the token's dequantized rotated K and V rows in the workspace
+// (anew); the merge kernel attends to the token from those rows when its slot
+// is mapped and below the segment's min(seq_lens[b], max_len). The partial
+// launch or the window scan masks that slot.
+struct TokenAppend {
+  uint8_t* pool;  // null: no fused append
+  int64_t pool_blocks;
+  int64_t block_bytes;
+  const int32_t* table;
+  int32_t table_stride;
+  const int32_t* seq_lens;
+  const int32_t* start_pos;
+  const void* k_new;  // [batch][hkv][d], bf16 or fp32
+  const void* v_new;
+  int32_t src_bf16, meta16, max_len;
+  double rs_n;  // 1 / sqrt(had_block)
+  int32_t k_off[KVQ_MAX_KV_HEADS];
+  int32_t v_off[KVQ_MAX_KV_HEADS];
+  uint8_t bits_k[KVQ_MAX_KV_HEADS];
+  uint8_t bits_v[KVQ_MAX_KV_HEADS];
 };
 
 // One partial-decode launch over the listed heads of one or more segments.
@@ -86,6 +113,8 @@ struct DecodeArgs {
   float* part_o;       // [batch][hq][total_slots][d]
   float* part_ml;      // [batch][hq][total_slots][2]  (running max in log2 units, sum)
   float* qrot;         // [batch][hq][d]: q~ = (R q) log2(e) / sqrt(d), for a window segment the merge computes
+  TokenAppend ap;      // a fused append (ap.pool set): done by the split-0 waves of the write_q segment
+  float* anew;         // [batch][hkv][2][d]: the appended token's dequantized rotated K and V rows
 };
 
 // Distortion calibration: rows [rows][d] of fp32 or bf16, rotated and
@@ -130,6 +159,7 @@ struct MergeWindow {
   const int32_t* table;
   int32_t table_stride;
   const int32_t* seq_lens;
+  const int32_t* skip_pos;  // [batch] slot a fused append fills (masked in the scan), or null
   int32_t max_len;
   int64_t k_off[KVQ_MAX_KV_HEADS];
   int64_t v_off[KVQ_MAX_KV_HEADS];
@@ -142,6 +172,8 @@ struct MergeArgs {
   int32_t batch, hq, d, had_block, total_slots, group;
   float* out;  // [batch][hq][d]
   MergeWindow win;
+  TokenAppend ap;     // a fused append (ap.pool set): the token is attended to from anew
+  const float* anew;  // [batch][hkv][2][d]
 };
 
 // Launchers return hipSuccess or the launch error; they never synchronise.

@@ -14,7 +14,7 @@ import numpy as np
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkvq.so")
 
-KVQ_ABI_VERSION = 5
+KVQ_ABI_VERSION = 6
 KVQ_MAX_KV_HEADS = 64
 KVQ_BLOCK_TOKENS = 16
 
@@ -28,7 +28,7 @@ EXPORTED = [
     "kvq_decode_merge", "kvq_fit_distortion", "kvq_amgm_ratio", "kvq_quant_mse",
     "kvq_logquant_dynamic_classes", "kvq_logquant_init", "kvq_logquant_advance", "kvq_logquant_requant",
     "kvq_append_check", "kvq_decode_attn_noalloc", "kvq_plan_bits_components", "kvq_measure_read_stream",
-    "kvq_measure_read_paged",
+    "kvq_measure_read_paged", "kvq_append_decode_attn", "kvq_append_decode_partial", "kvq_append_decode_merge",
 ]
 
 KVQ_DECODE_COUNTER_BYTES = 65536
@@ -127,6 +127,11 @@ def lib():
     L.kvq_measure_read_stream.argtypes = [vp, sz, vp, i32, vp]
     L.kvq_measure_read_paged.argtypes = [ctypes.POINTER(KvqSegment), i32, i32, i32, vp, i32, vp]
     L.kvq_decode_attn_noalloc.argtypes = [ctypes.POINTER(KvqSegment), i32, i32, vp, ctypes.c_int, vp, vp]
+    L.kvq_append_decode_attn.argtypes = [ctypes.POINTER(KvqSegment), i32, i32, i32, vp, vp, vp, ctypes.c_int, vp,
+                                         ctypes.c_int, vp, vp, sz, vp]
+    L.kvq_append_decode_partial.argtypes = [ctypes.POINTER(KvqSegment), i32, i32, i32, vp, vp, vp, ctypes.c_int,
+                                            vp, ctypes.c_int, vp, sz, vp]
+    L.kvq_append_decode_merge.argtypes = [ctypes.POINTER(KvqSegment), i32, i32, i32, vp, vp, vp, sz, vp]
     for name in EXPORTED:
         if name not in ("kvq_abi_version", "kvq_status_str", "kvq_last_error"):
             getattr(L, name).restype = ctypes.c_int
@@ -465,6 +470,63 @@ def kvq_decode_attn(segments, q, out=None, ws=None, stream=None):
                                ws.numel(), _stream(stream))
     _check(st, "kvq_decode_attn")
     return out
+
+
+def kvq_append_decode_attn(segments, append_seg, start_pos, k_new, v_new, q, out=None, ws=None, stream=None):
+    """One decode step: append one token per sequence (k_new, v_new [batch, Hkv, d], fp32 or bf16, at slot
+    start_pos [batch] of segments[append_seg]) and decode q over every segment; returns fp32 [batch, Hq, d]."""
+    import torch
+    batch, ws = _decode_common(segments, q, ws)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    _check(lib().kvq_append_decode_attn(*_append_decode_args(segments, append_seg, start_pos, k_new, v_new, q, out,
+                                                             ws, stream)), "kvq_append_decode_attn")
+    return out
+
+
+def _append_decode_args(segments, append_seg, start_pos, k_new, v_new, q, out, ws, stream):
+    import torch
+    if k_new.dtype != v_new.dtype or k_new.shape != v_new.shape or k_new.dim() != 3 or k_new.shape[0] != q.shape[0]:
+        raise ValueError("k_new and v_new must be [batch, Hkv, d] of one dtype")
+    return (_segments(segments), len(segments), int(q.shape[0]), int(append_seg),
+            _dev_ptr(start_pos, (torch.int32,), "start_pos"), _dev_ptr(k_new, (torch.float32, torch.bfloat16), "k_new"),
+            _dev_ptr(v_new, (torch.float32, torch.bfloat16), "v_new"),
+            KVQ_BF16 if k_new.dtype == torch.bfloat16 else KVQ_F32,
+            _dev_ptr(q, (torch.float32, torch.bfloat16), "q"), KVQ_BF16 if q.dtype == torch.bfloat16 else KVQ_F32,
+            _dev_ptr(out, (torch.float32,), "out"), _dev_ptr(ws, (torch.uint8,), "ws"), ws.numel(), _stream(stream))
+
+
+def prepare_append_decode_attn(segments, append_seg, start_pos, k_new, v_new, q, out, ws, stream=None):
+    args = _append_decode_args(segments, append_seg, start_pos, k_new, v_new, q, out, ws, stream)
+    return PreparedCall(lib().kvq_append_decode_attn, args, "kvq_append_decode_attn",
+                        (segments, start_pos, k_new, v_new, q, out, ws), stream is None)
+
+
+def prepare_append_decode_partial(segments, append_seg, start_pos, k_new, v_new, q, ws, stream=None):
+    """The partial half of kvq_append_decode_attn (its split-0 waves append the token; every wave masks
+    its slot), marshalled once."""
+    import torch
+    if k_new.dtype != v_new.dtype or k_new.shape != v_new.shape or k_new.dim() != 3 or k_new.shape[0] != q.shape[0]:
+        raise ValueError("k_new and v_new must be [batch, Hkv, d] of one dtype")
+    args = (_segments(segments), len(segments), int(q.shape[0]), int(append_seg),
+            _dev_ptr(start_pos, (torch.int32,), "start_pos"), _dev_ptr(k_new, (torch.float32, torch.bfloat16), "k_new"),
+            _dev_ptr(v_new, (torch.float32, torch.bfloat16), "v_new"),
+            KVQ_BF16 if k_new.dtype == torch.bfloat16 else KVQ_F32,
+            _dev_ptr(q, (torch.float32, torch.bfloat16), "q"), KVQ_BF16 if q.dtype == torch.bfloat16 else KVQ_F32,
+            _dev_ptr(ws, (torch.uint8,), "ws"), ws.numel(), _stream(stream))
+    return PreparedCall(lib().kvq_append_decode_partial, args, "kvq_append_decode_partial",
+                        (segments, start_pos, k_new, v_new, q, ws), stream is None)
+
+
+def prepare_append_decode_merge(segments, append_seg, start_pos, batch, out, ws, stream=None):
+    """The merge half of kvq_append_decode_attn (the new token attended to from the rows the partial half
+    left in ws), marshalled once."""
+    import torch
+    args = (_segments(segments), len(segments), int(batch), int(append_seg),
+            _dev_ptr(start_pos, (torch.int32,), "start_pos"), _dev_ptr(out, (torch.float32,), "out"),
+            _dev_ptr(ws, (torch.uint8,), "ws"), ws.numel(), _stream(stream))
+    return PreparedCall(lib().kvq_append_decode_merge, args, "kvq_append_decode_merge",
+                        (segments, start_pos, out, ws), stream is None)
 
 
 def kvq_measure_read_stream(buf, sink, stream=None):

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     for name in sorted(declared):
         assert hasattr(lib, name), name
     assert declared == set(kvq.EXPORTED)
-    assert kvq.kvq_abi_version() == kvq.KVQ_ABI_VERSION == 5
+    assert kvq.kvq_abi_version() == kvq.KVQ_ABI_VERSION == 6
     assert kvq.kvq_status_str(kvq.KVQ_ERR_BUDGET) == "KVQ_ERR_BUDGET"
 
 
@@ -253,9 +253,9 @@ def test_decode_argument_checks_need_no_device():
     assert lib.kvq_decode_workspace_bytes(segs, 1, 16, ctypes.byref(n)) == kvq.KVQ_OK
     assert n.value > 16 * 32 * 130 * 4
     # the fixed counter area, then partials for every split slot (a multiple of 8 slots), then one
-    # rotated query row per query head
+    # rotated query row per query head and a fused append's K and V rows per KV head
     per_slot = 16 * 32 * 130 * 4
-    part = n.value - kvq.KVQ_DECODE_COUNTER_BYTES - 16 * 32 * 128 * 4
+    part = n.value - kvq.KVQ_DECODE_COUNTER_BYTES - 16 * 32 * 128 * 4 - 16 * 8 * 2 * 128 * 4
     assert part % per_slot == 0 and (part // per_slot) % 8 == 0
     # the counters the plan uses (two words per sequence, KV head and group of 8 splits) fit the area
     assert (part // per_slot) // 8 * 16 * 8 * 2 * 4 <= kvq.KVQ_DECODE_COUNTER_BYTES
@@ -281,6 +281,31 @@ def test_decode_argument_checks_need_no_device():
     stale = (kvq.KvqSegment * 1)(_fake_segment(L3, 64, 4))
     assert lib.kvq_decode_workspace_bytes(stale, 1, 1, ctypes.byref(n)) == kvq.KVQ_ERR_ARG
     assert "kvq_layout_init" in kvq.kvq_last_error()
+
+
+def test_append_decode_argument_checks_need_no_device():
+    """kvq_append_decode_attn's own checks, all before any launch."""
+    lib = kvq.lib()
+    L = kvq.kvq_layout_init(8, 4, 128, 128, [4] * 8, [4] * 8)
+    segs = (kvq.KvqSegment * 1)(_fake_segment(L, 32768, 2048))
+    p = ctypes.c_void_p
+    q, out, ws, sp, kv = p(0x4000), p(0x5000), p(0x6000), p(0x7000), p(0x8000)
+
+    def call(seg_arr, n, append_seg, start=sp, k=kv, v=kv, in_dt=kvq.KVQ_BF16, ws_bytes=1 << 30):
+        return lib.kvq_append_decode_attn(seg_arr, n, 16, append_seg, start, k, v, in_dt, q, kvq.KVQ_BF16, out, ws,
+                                          ws_bytes, None)
+
+    assert call(segs, 1, 1) == kvq.KVQ_ERR_ARG             # append_seg out of range
+    assert call(segs, 1, -1) == kvq.KVQ_ERR_ARG
+    assert call(segs, 1, 0, start=None) == kvq.KVQ_ERR_ARG
+    assert call(segs, 1, 0, k=None) == kvq.KVQ_ERR_ARG
+    assert call(segs, 1, 0, v=p(0x8004)) == kvq.KVQ_ERR_ARG  # rows not 16-byte aligned
+    assert call(segs, 1, 0, in_dt=7) == kvq.KVQ_ERR_ARG
+    assert call(segs, 1, 0, ws_bytes=16) == kvq.KVQ_ERR_WORKSPACE
+    kc = kvq.kvq_layout_init(8, 4, 128, 128, [4] * 8, [4] * 8, key_per_channel=True)
+    kcs = (kvq.KvqSegment * 1)(_fake_segment(kc, 32768, 2048))
+    assert call(kcs, 1, 0) == kvq.KVQ_ERR_UNSUPPORTED
+    assert "per-channel" in kvq.kvq_last_error()
 
 
 def test_measurement_helpers_argument_checks_need_no_device():
