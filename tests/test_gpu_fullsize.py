@@ -12,6 +12,8 @@ head's bits) and computes their attention. Compared:
   rate of at most 1e-5).
 """
 
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -24,6 +26,7 @@ pytestmark = pytest.mark.gpu
 
 TIE_RATE = 1e-5
 ROW_SAMPLE = 512
+ORACLE_THREADS = 8  # oracle units computed side by side (numpy releases the GIL in its array work)
 
 
 def device_rows(pool, block_bytes, table_np, seq, positions, area_off, d, bits):
@@ -109,23 +112,66 @@ def run_units(L, pool, table, out, k, v, q, units, seed, all_rows=()):
     return stats
 
 
-def test_llama_32k_decode_full_size():
-    """Batch 16, 32768 tokens, 8 KV heads x 4, head_dim 128, K4/V4, Hadamard 128 (one layer).
+def run_units_threaded(L, pool, table, out, k, v, q, units, seed, all_rows=(), row_sample=ROW_SAMPLE):
+    """run_units with the oracle's per-unit work on ORACLE_THREADS threads.
 
-    Compared against the oracle: all 8 KV heads of sequences 0 and 11, and one
-    head of every other sequence (a different head each, so every head index
-    and every sequence is covered: 30 of the 128 units, over all XCDs and
-    sharing groups of the launch). Units of sequence 0 have every stored row
-    compared."""
+    Inputs are copied to the host and the GPU rows gathered in the calling
+    thread; the threads run only the oracle (numpy)."""
+    g, n = L.group, L.had_block
+    tokens = k.shape[1]
+    inputs = [(k[b, :, h].float().cpu().numpy(), v[b, :, h].float().cpu().numpy(),
+               q[b, h * g:(h + 1) * g].float().cpu().numpy()) for b, h in units]
+
+    def oracle(i):
+        (b, h), (k_rows, v_rows, q_rows) = units[i], inputs[i]
+        lay, ref_pool, ref_table = oracle_unit(k_rows, v_rows, q_rows, L.bits_k[h], L.bits_v[h], n)
+        expect = O.decode_attention([(lay, ref_pool, ref_table, np.array([tokens]))],
+                                    q_rows[None].astype(np.float64))[0]
+        return lay, ref_pool, ref_table, expect
+
+    rng = np.random.default_rng(seed)
+    stats = T.CodeStats()
+    with ThreadPoolExecutor(ORACLE_THREADS) as ex:
+        for i, (lay, ref_pool, ref_table, expect) in enumerate(ex.map(oracle, range(len(units)))):
+            b, h = units[i]
+            err = T.max_rel_err(out[b, h * g:(h + 1) * g], expect)
+            assert err <= T.ATTN_TOL, f"unit (b={b}, h={h}): max relative error {err:.3e}"
+            if (b, h) in all_rows:
+                positions = np.arange(tokens)
+            else:
+                positions = np.sort(rng.choice(tokens, size=min(row_sample, tokens), replace=False))
+            k_rows, v_rows, _ = inputs[i]
+            check_unit_rows(L, pool, table, b, h, lay, ref_pool, ref_table, k_rows, v_rows, positions, stats)
+            inputs[i] = None
+    assert stats.rate <= TIE_RATE
+    return stats
+
+
+@pytest.fixture(scope="module")
+def llama32k():
+    """One layer of the 32k workload, filled and decoded as the benchmark runs it."""
     batch, tokens, hkv, group, d = 16, 32768, 8, 4, 128
     L = kvq.kvq_layout_init(hkv, group, d, 128, [4] * hkv, [4] * hkv)
     k, v, q = synth.llama_layer_torch(2000, batch, tokens, hkv, group, d, device=T.DEV)
     pool, table, table_t = full_cache(L, batch, tokens, k, v, seed=2000)
     out = decode_units(L, pool, table_t, batch, tokens, q)
+    yield L, pool, table, out, k, v, q
+    del k, v, q, pool, table_t
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("part", range(4))
+def test_llama_32k_decode_full_size(llama32k, part):
+    """Batch 16, 32768 tokens, 8 KV heads x 4, head_dim 128, K4/V4, Hadamard 128 (one layer).
+
+    Every one of the 128 (sequence, KV head) units is compared against the
+    oracle, 32 per part (sequences 4*part to 4*part + 3). Units of sequence 0
+    have every stored row compared, the others 128 sampled rows."""
+    L, pool, table, out, k, v, q = llama32k
     assert np.all(np.isfinite(out))
-    units = [(0, h) for h in range(hkv)] + [(11, h) for h in range(hkv)]
-    units += [(b, (3 * b + 1) % hkv) for b in range(batch) if b not in (0, 11)]
-    run_units(L, pool, table, out, k, v, q, units, seed=1, all_rows={(0, h) for h in range(hkv)})
+    units = [(b, h) for b in range(4 * part, 4 * part + 4) for h in range(L.num_kv_heads)]
+    run_units_threaded(L, pool, table, out, k, v, q, units, seed=1 + part,
+                       all_rows={(0, h) for h in range(L.num_kv_heads)}, row_sample=128)
 
 
 def test_bf16_32k_baseline_decode_full_size():
@@ -250,14 +296,17 @@ def test_long_context_131k_three_segments_full_size():
 
 
 def test_bulk_append_16k_then_decode_full_size():
-    """Batch 4, 16384 new tokens in one append, K4/V2, Hadamard 128, then one decode over them."""
+    """Batch 4, 16384 new tokens in one append, K4/V2, Hadamard 128, then one decode over them.
+    Every (sequence, KV head) unit is compared against the oracle."""
     batch, tokens, hkv, group, d = 4, 16384, 8, 4, 128
     L = kvq.kvq_layout_init(hkv, group, d, 128, [4] * hkv, [2] * hkv)
     k, v, q = synth.llama_layer_torch(5, batch, tokens, hkv, group, d, device=T.DEV)
     pool, table, table_t = full_cache(L, batch, tokens, k, v, seed=5)
     out = decode_units(L, pool, table_t, batch, tokens, q)
     assert np.all(np.isfinite(out))
-    run_units(L, pool, table, out, k, v, q, [(0, 0), (3, 6), (1, 3)], seed=3)
+    # all 32 units' outputs; sampled stored rows of each
+    units = [(b, h) for b in range(batch) for h in range(hkv)]
+    run_units_threaded(L, pool, table, out, k, v, q, units, seed=3, row_sample=256)
 
 
 def test_long_context_three_segments_equal_one_merged_segment():
