@@ -1420,9 +1420,15 @@ __global__ __launch_bounds__(64 * NW) void decode_merge_kernel(MergeArgs a, floa
     return win.pool + (ok ? blk : 0) * win.block_bytes + off + (t % kBlockTokens) * (D * 2);
   };
   const int wskip = win.pool && win.skip_pos ? win.skip_pos[b] : -1;  // the window slot a fused append fills
-  // q~ of this query head (written by the partial launch), read first: its
-  // round trip overlaps the preloads
+  // Read first: the table entry of this thread's first window key row (token
+  // tid / 8, eight lanes a token), so that the row's load further down waits
+  // for none of the preloads issued in between (loads complete in order), and
+  // q~ of this query head (written by the partial launch), whose round trip
+  // overlaps the preloads.
   const bool need_q = nwin > 0 || ap_pool(a);
+  const int t00 = tid >> 3, tend = (nwin + 7) & ~7;
+  int32_t tab0 = 0;
+  if (t00 < tend) tab0 = win.table[static_cast<int64_t>(b) * win.table_stride + min(t00, nwin - 1) / kBlockTokens];
   const float qv = need_q && tid < D ? a.qrot[bg * D + tid] : 0.f;
   // Fused append: the partial launch quantized and stored the new token and
   // left its dequantized rows in anew; it is attended to below when its slot
@@ -1483,16 +1489,16 @@ __global__ __launch_bounds__(64 * NW) void decode_merge_kernel(MergeArgs a, floa
   for (int s = tid; s < S; s += 64 * NW) mx = fmaxf(mx, ml[2 * s]);
   constexpr int CH = D / 8;  // channels per lane of a token
   const int part = lane & 7;
-  const int t00 = tid >> 3, tend = (nwin + 7) & ~7;
   uint4 k0[CH / 8];
   int32_t blk0 = 0;
   if (t00 < tend) {
     const int t = min(t00, nwin - 1);
-    bool ok;
-    const uint4* row = reinterpret_cast<const uint4*>(win_row(t, win.k_off[h], ok)) + part * (CH / 8);
+    const bool ok = static_cast<uint32_t>(tab0) < wblocks;
+    const uint4* row = reinterpret_cast<const uint4*>(win.pool + (ok ? tab0 : 0) * win.block_bytes + win.k_off[h] +
+                                                      (t % kBlockTokens) * (D * 2)) + part * (CH / 8);
 #pragma unroll
     for (int c = 0; c < CH / 8; ++c) k0[c] = row[c];
-    blk0 = ok ? win.table[static_cast<int64_t>(b) * win.table_stride + t / kBlockTokens] : -1;
+    blk0 = ok ? tab0 : -1;
   }
   if (need_q) {
     if (tid < D) wq[tid] = qv;
