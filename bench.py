@@ -280,6 +280,11 @@ def build_decode_layers(args, kvq, torch, dev):
     layers = []
     if args.workload == "mixed32k":
         batch, tokens = 8, 32768
+        args.dtype_detail = ("2/3/4/8-bit K/V codes with fp32 {scale, min} per row, bf16 queries and new rows; "
+                             "scores on int8 MFMA for 2-, 4- and 8-bit keys (the query as three signed-byte digits "
+                             "of a 24-bit fixed-point number per head, exact int32 sums) and on fp16 MFMA (hi+lo "
+                             "pairs) for 3-bit keys; PV on fp16 MFMA (weights as hi+lo pairs, ~22 bits); fp32 "
+                             "softmax and accumulation")
         w_k = synth.sensitivities(LAYERS, HKV, seed=3).ravel()
         w_v = synth.sensitivities(LAYERS, HKV, seed=33).ravel()
         budget = 3 * LAYERS * HKV
@@ -306,6 +311,10 @@ def build_decode_layers(args, kvq, torch, dev):
             "decode_partial_multi_kernel<128> (the 2/3/4-bit heads of a layer, one launch) + "
             "decode_partial_kernel<8,*,128> beside it for the layers with an 8-bit head")
     if args.workload == "long131k":
+        args.dtype_detail = ("2- and 4-bit K/V codes with fp32 {scale, min} per row and a bf16 window, bf16 queries "
+                             "and new rows; scores of the coded tokens on int8 MFMA (the query as three signed-byte "
+                             "digits of a 24-bit fixed-point number per head, exact int32 sums), PV on fp16 MFMA "
+                             "(weights as hi+lo pairs); the window scored and weighted in fp32 by the merge kernel")
         batch, tokens, window = 1, 131072, 128
         cls = kvq.kvq_logquant_classes(tokens, window)
         idx_all = [torch.from_numpy(np.flatnonzero(cls == c)).to(dev) for c in range(3)]
@@ -362,6 +371,10 @@ def build_decode_layers(args, kvq, torch, dev):
                   "layers": args.layers, "batch": B, "ctx": T, "kv_heads": HKV, "q_per_kv": G, "head_dim": D,
                   "bits_k": BITS_K, "bits_v": BITS_V, "had_block": HAD, "keys": "per channel"}
         per_tok = D * BITS_K // 8 + D * 8 // 16 + D * BITS_V // 8 + 8
+        args.dtype = "f16"
+        args.dtype_detail = ("int4 codes (keys with fp32 {scale, min} per channel and block, values per row), bf16 "
+                             "queries; scores and PV on fp16 MFMA (codes exact, query and weights as fp16 hi+lo "
+                             "pairs, ~22 bits), fp32 softmax and accumulation")
         return (layers, config, batch, B * HKV * T * per_tok + B * (T // 16) * 4 + B * HKV * G * D * 2,
                 "decode_partial_kc_kernel<4,4,128>")
     if m16:
@@ -372,6 +385,8 @@ def build_decode_layers(args, kvq, torch, dev):
                 "decode_partial_kernel<4,4,128,fp16 meta>")
     if args.workload == "bf16_32k":
         args.dtype = "bf16"
+        args.dtype_detail = ("bf16 K/V rows (rotated), bf16 queries; scores and PV on bf16 MFMA (the query and the "
+                             "weights as bf16 hi+lo pairs), fp32 softmax and accumulation")
         config = {"workload": "bf16 paged decode baseline: " + WORKLOAD.replace("K4/V4 token-wise INT4", "bf16 K/V rows (rotated, no metadata)"),
                   "layers": args.layers, "batch": B, "ctx": T, "kv_heads": HKV, "q_per_kv": G, "head_dim": D,
                   "bits_k": 16, "bits_v": 16, "had_block": HAD}
@@ -491,6 +506,8 @@ def run_decode(args, torch, dev, kvq):
         extra["eager_tokens_per_s"] = round(batch * args.steps / eager_elapsed, 2)
     if getattr(args, "dtype", None):
         extra["dtype"] = args.dtype
+    if getattr(args, "dtype_detail", None):
+        extra["dtype_detail"] = args.dtype_detail
     return {**extra,
         "value": round(batch * args.steps / elapsed, 2),
         "unit": "tokens/s",
@@ -895,11 +912,12 @@ def main():
         "higher_is_better": res.pop("higher_is_better"),
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": res.pop("dtype", "f16"),
+        "dtype": res.pop("dtype", "i8+f16"),
         "dtype_detail": res.pop("dtype_detail", "int4 K/V codes with fp32 {scale, min} per row, bf16 queries and new "
-                                                "rows; scores and PV on fp16 MFMA operands (codes exact, query and "
-                                                "weights as fp16 hi+lo pairs, ~22 bits), fp32 accumulation and "
-                                                "softmax"),
+                                                "rows; scores on int8 MFMA (codes exact as bytes, the query as three "
+                                                "signed-byte digits of a 24-bit fixed-point number per head, exact "
+                                                "int32 sums), PV on fp16 MFMA (centred codes exact, weights as fp16 "
+                                                "hi+lo pairs, ~22 bits), fp32 softmax and accumulation"),
         "data": "synthetic",
         "config": res.pop("config"),
         "roofline": res.pop("roofline"),

@@ -12,12 +12,15 @@
 //
 // Work decomposition (split-K / flash-decoding): one wave per (sequence, KV
 // head, split of pages). A split walks its pages four at a time (64 tokens):
-//  * QK on the matrix cores: v_mfma_f32_16x16x32_f16 with A = the G query rows
-//    of this KV head (hi and lo fp16 halves of q', each its own MFMA, so the
-//    product carries ~22 bits of q) and B = the page's key codes, which the
-//    lanes turn into exact fp16 numbers 1024 + sigma*c with one v_and_or_b32
-//    per pair; 4-bit keys are centred to sigma*(c - 8) by one packed add, for
-//    the other widths the constant 1024*sum(q) is removed afterwards.
+//  * QK on the matrix cores. 2-, 4- and 8-bit keys: v_mfma_i32_16x16x64_i8
+//    with A = the G query rows of this KV head, each as three signed-byte
+//    digits of a 24-bit fixed-point number (rows 4h..4h+2), and B = the
+//    page's key codes as bytes (a mask and a shift per four codes); the int32
+//    sums are exact. 3-bit keys, bf16 keys and keys per channel:
+//    v_mfma_f32_16x16x32_f16 with A = hi and lo fp16 halves of q' (rows 0-3
+//    and 4-7, so the product carries ~22 bits of q) and B = exact fp16 numbers
+//    1024 + sigma*c made by one v_and_or_b32 per pair, the constant removed
+//    afterwards.
 //  * The four pages' score tiles are packed into one dense set of four
 //    registers (lane = token, register = query head) with
 //    v_permlane16_swap / v_permlane32_swap.
@@ -53,6 +56,12 @@ __device__ __forceinline__ float4_t mfma_f16(u32x4_t a, u32x4_t b, float4_t c) {
 __device__ __forceinline__ float4_t mfma_bf16(u32x4_t a, u32x4_t b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+// 16x16 tile, 64 products per element: A and B 16 signed bytes a lane, exact int32 sums
+__device__ __forceinline__ i32x4_t mfma_i8(u32x4_t a, u32x4_t b, i32x4_t c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4_t, a), __builtin_bit_cast(i32x4_t, b), c,
+                                               0, 0, 0);
 }
 template <bool BF16>
 __device__ __forceinline__ float4_t mfma(u32x4_t a, u32x4_t b, float4_t c) {
@@ -215,6 +224,51 @@ template <int D> struct KFmt<16, D> {
   __device__ static u32x4_t unpack(const uint32_t (&w)[kWords], int c, uint32_t) {
     u32x4_t r;
     r[0] = w[4 * c]; r[1] = w[4 * c + 1]; r[2] = w[4 * c + 2]; r[3] = w[4 * c + 3];
+    return r;
+  }
+};
+
+// Integer scores for 2-, 4- and 8-bit keys: the codes become bytes (one mask,
+// and a shift for all but the first field of a word) and meet the query, held
+// as three signed-byte digits of a 24-bit fixed-point number, in the int8
+// matrix core, whose int32 sums are exact. Against the fp16 path this halves
+// the QK matrix instructions (64 channels per step) and the unpacking, and
+// needs no centring: no large offset enters a rounded sum. The score is then
+// s * sum(q~ c) + mn * sum(q~), as for the other formats without centring
+// (8-bit codes, above the signed byte range, enter as c - 128: kOff = 128).
+// channel(s, p) is the channel (relative to the lane's quarter) in byte p of
+// step s; A and B take the same order, which the sums do not depend on.
+#ifndef KVQ_TUNE_KI8
+#define KVQ_TUNE_KI8 1
+#endif
+template <int KB, int D>
+struct KI8 {
+  static constexpr bool on = KVQ_TUNE_KI8 && (KB == 2 || KB == 4 || KB == 8);
+  static constexpr int kSteps = D / 64;  // 16 channels of the quarter per step
+  static constexpr float kOff = KB == 8 ? 128.f : 0.f;
+  __device__ static constexpr int channel(int s, int p) {
+    const int d = p >> 2, q = p & 3;
+    if constexpr (KB == 2) return 16 * s + 4 * q + d;                     // word s, field 4q + d
+    else if constexpr (KB == 4) return 8 * (2 * s + (d >> 1)) + 2 * q + (d & 1);  // word 2s + d/2, nibble 2q + d%2
+    else return 16 * s + 4 * d + q;                                       // word 4s + d, byte q
+  }
+  __device__ static u32x4_t bytes(const uint32_t (&w)[KFmt<KB, D>::kWords], int s) {
+    u32x4_t r;
+    if constexpr (KB == 2) {
+      const uint32_t x = w[s];
+      r[0] = x & 0x03030303u;
+      r[1] = (x >> 2) & 0x03030303u;
+      r[2] = (x >> 4) & 0x03030303u;
+      r[3] = (x >> 6) & 0x03030303u;
+    } else if constexpr (KB == 4) {
+      r[0] = w[2 * s] & 0x0f0f0f0fu;
+      r[1] = (w[2 * s] >> 4) & 0x0f0f0f0fu;
+      r[2] = w[2 * s + 1] & 0x0f0f0f0fu;
+      r[3] = (w[2 * s + 1] >> 4) & 0x0f0f0f0fu;
+    } else {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) r[d] = w[4 * s + d] ^ 0x80808080u;
+    }
     return r;
   }
 };
@@ -555,7 +609,7 @@ struct KcLane {
 
 template <int KB, int VB, int D, bool KC>
 __device__ __forceinline__ void compute_group(GroupRaw<KB, VB, D>& g, const u32x4_t (&qf)[D / 32],
-                                              const float (&biasq)[4], const float (&q2)[4], float inv_qsc, int G,
+                                              const u32x4_t (&qi)[D / 64], float inv_ql, const float (&biasq)[4], const float (&q2)[4], float inv_qsc, int G,
                                               int lane, uint32_t bias, uint16_t (*wt)[4][64],
                                               const uint16_t* wzero, SplitState<KB, VB, D>& st,
                                               const KcLane& kl, uint4 (*qa)[64]) {
@@ -566,13 +620,26 @@ __device__ __forceinline__ void compute_group(GroupRaw<KB, VB, D>& g, const u32x
   constexpr float NEG_INF = -__builtin_huge_valf();
   const int row = lane & 15, g4 = lane >> 4;
 
-  // QK: one 16x16 tile per page (rows 0-3 = hi parts of the query heads, rows
-  // 4-7 = lo parts, columns = tokens). Each chunk's query fragment feeds all
-  // four pages.
+  // QK: one 16x16 tile per page, columns = tokens (fp16 path: rows 0-3 = hi
+  // parts of the query heads, rows 4-7 = lo parts; each chunk's query fragment
+  // feeds all four pages).
+  constexpr bool QI8 = KI8<KB, D>::on && !KC;
   float4_t cq[4];
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp) cq[pp] = float4_t{0.f, 0.f, 0.f, 0.f};
-  if constexpr (KC) {
+  float zs[4];  // (QI8) per page: sum q~ c of head g4 at token row of the page
+  if constexpr (QI8) {
+    // one integer tile per page: rows 4h + j = digit j of head h, so lane
+    // group g4 holds head g4's three digit sums for token `row` of the page
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      i32x4_t acc = i32x4_t{0, 0, 0, 0};
+#pragma unroll
+      for (int st = 0; st < D / 64; ++st) acc = mfma_i8(qi[st], KI8<KB, D>::bytes(g.k[pp], st), acc);
+      zs[pp] = fmaf(static_cast<float>(acc[0]), 65536.f * inv_ql,
+                    fmaf(static_cast<float>(acc[1]), 256.f * inv_ql, static_cast<float>(acc[2]) * inv_ql));
+    }
+  } else if constexpr (KC) {
     // Per page: A = q~ s / sigma at a power-of-two page scale (fp16 hi in rows
     // 0-3 and lo in rows 4-7 of the LDS fragment area), B = the codes as in the row
     // layout; score = sum / scale + the page constant of each query row.
@@ -633,24 +700,37 @@ __device__ __forceinline__ void compute_group(GroupRaw<KB, VB, D>& g, const u32x
   // register, lanes 0-31 and 32-63; hi + lo with lane l ^ 16; then lanes 16-31
   // take page 1 and lanes 32-47 page 2.
   float z[4];
-  const float ks_q = g.ks * inv_qsc;
-  // centred codes: s*sum q(c - m) + (mn + m*s)*sum q, the centre term per token
-  const float kmid = KF::kCentre != 0.f ? fmaf(KF::kCentre, g.ks, g.kmn) : g.kmn;
+  if constexpr (QI8) {
+    // (lane group = head, register = page) to (lane group = page, register =
+    // head): a transpose of 16-lane blocks in two swap stages
+    const auto t02 = __builtin_amdgcn_permlane32_swap(f_bits(zs[0]), f_bits(zs[2]), false, false);
+    const auto t13 = __builtin_amdgcn_permlane32_swap(f_bits(zs[1]), f_bits(zs[3]), false, false);
+    const auto u01 = __builtin_amdgcn_permlane16_swap(t02[0], t13[0], false, false);
+    const auto u23 = __builtin_amdgcn_permlane16_swap(t02[1], t13[1], false, false);
+    const float sc[4] = {bits_f(u01[0]), bits_f(u01[1]), bits_f(u23[0]), bits_f(u23[1])};
+    const float kmid = fmaf(KI8<KB, D>::kOff, g.ks, g.kmn);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const auto x02 = __builtin_amdgcn_permlane32_swap(f_bits(cq[0][i]), f_bits(cq[2][i]), false, false);
-    const auto x13 = __builtin_amdgcn_permlane32_swap(f_bits(cq[1][i]), f_bits(cq[3][i]), false, false);
-    float y02 = bits_f(x02[0]), y13 = bits_f(x13[0]);
-    y02 += __shfl_xor(y02, 16, 64);
-    y13 += __shfl_xor(y13, 16, 64);
-    const auto r = __builtin_amdgcn_permlane16_swap(f_bits(y02), f_bits(y13), false, false);
-    const float sc = bits_f(r[0]);
-    float zi;
-    if constexpr (KC) zi = sc;
-    else if constexpr (KMETA && KF::kCentre != 0.f) zi = fmaf(ks_q, sc, kmid * q2[i]);
-    else if constexpr (KMETA) zi = fmaf(ks_q, sc, fmaf(-ks_q, biasq[i], g.kmn * q2[i]));
-    else zi = sc;
-    z[i] = (g.valid && i < G) ? zi : NEG_INF;
+    for (int i = 0; i < 4; ++i) z[i] = (g.valid && i < G) ? fmaf(g.ks, sc[i], kmid * q2[i]) : NEG_INF;
+  } else {
+    const float ks_q = g.ks * inv_qsc;
+    // centred codes: s*sum q(c - m) + (mn + m*s)*sum q, the centre term per token
+    const float kmid = KF::kCentre != 0.f ? fmaf(KF::kCentre, g.ks, g.kmn) : g.kmn;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const auto x02 = __builtin_amdgcn_permlane32_swap(f_bits(cq[0][i]), f_bits(cq[2][i]), false, false);
+      const auto x13 = __builtin_amdgcn_permlane32_swap(f_bits(cq[1][i]), f_bits(cq[3][i]), false, false);
+      float y02 = bits_f(x02[0]), y13 = bits_f(x13[0]);
+      y02 += __shfl_xor(y02, 16, 64);
+      y13 += __shfl_xor(y13, 16, 64);
+      const auto r = __builtin_amdgcn_permlane16_swap(f_bits(y02), f_bits(y13), false, false);
+      const float sc = bits_f(r[0]);
+      float zi;
+      if constexpr (KC) zi = sc;
+      else if constexpr (KMETA && KF::kCentre != 0.f) zi = fmaf(ks_q, sc, kmid * q2[i]);
+      else if constexpr (KMETA) zi = fmaf(ks_q, sc, fmaf(-ks_q, biasq[i], g.kmn * q2[i]));
+      else zi = sc;
+      z[i] = (g.valid && i < G) ? zi : NEG_INF;
+    }
   }
 
   // online softmax (log2 units): the reference max is raised (and the
@@ -1012,80 +1092,141 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, int si, int L
   if (lane < 8) wzero[lane] = 0;
   __syncthreads();
 
-  // ---- QK A operands: row r = lane % 16, K-slots of quarter g4. Rows 0-3 hold
-  // the hi fp16 parts of query heads 0-3, rows 4-7 the lo parts, so one MFMA
-  // per chunk and page gives both sums (lanes 0-15 and 16-31 of the tile) ----
   const int row = lane & 15;
   const int g4 = lane >> 4;
-  const int qrow = row & 3;                   // the query head of this row
-  const bool qact = row < 8 && qrow < G;
-  float amax = 0.f;
-#pragma unroll
-  for (int c = 0; c < NCK; ++c)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      // (read for every lane and scaled by zero in inactive rows: a read under
-      // a condition becomes a branch and a wait per value)
-      const float r = qs[qrow][g4 * (D / 4) + KF::channel(c, e)];
-      const float v = r * (qact ? qscale / KF::sigma(c, e) : 0.f);
-      amax = fmaxf(amax, fabsf(v));
-    }
-  amax = wave_max_scalar(amax);
-  // Power-of-two scale keeping the fp16 halves away from subnormals.
-  float qsc = 1.f;
-  if (!KF::bf16 && amax > 0.f) {
-    int ex;
-    frexpf(amax, &ex);
-    qsc = ldexpf(1.f, 10 - ex);
-  }
-  double q1 = 0.0;  // this lane's share of sum A * (base + centre*sigma): the offset to remove
-  double q2l = 0.0; // and of sum_j q~_j (the min term)
-#pragma unroll
-  for (int c = 0; c < NCK; ++c) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      uint32_t hp = 0, lp = 0;
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int e = 2 * v + half;
-        const float qt = qs[qrow][g4 * (D / 4) + KF::channel(c, e)] * (qact ? qscale : 0.f);
-        const float x = qt / KF::sigma(c, e) * qsc;
-        uint32_t hb, lb;
-        float hv, lv;
-        if constexpr (KF::bf16) {
-          hb = f_to_bf16_rne(x); hv = bf16lo_to_f(hb);
-          lb = f_to_bf16_rne(x - hv); lv = bf16lo_to_f(lb);
-        } else {
-          const _Float16 hh = static_cast<_Float16>(x);
-          hv = static_cast<float>(hh);
-          const _Float16 ll = static_cast<_Float16>(x - hv);
-          lv = static_cast<float>(ll);
-          hb = half_bits(hh); lb = half_bits(ll);
-        }
-        q1 += (static_cast<double>(hv) + static_cast<double>(lv)) *
-              static_cast<double>(KF::base(c, e) + KF::kCentre * KF::sigma(c, e));
-        q2l += static_cast<double>(qt);
-        hp |= hb << (16 * half);
-        lp |= lb << (16 * half);
-      }
-      reinterpret_cast<uint32_t*>(&qa[c][lane])[v] = row < 4 ? hp : lp;
-    }
-  }
-  // Sum over the four quarters (lanes row, row+16, row+32, row+48), in fp64.
-  q1 += __shfl_xor(q1, 16, 64);
-  q1 += __shfl_xor(q1, 32, 64);
-  q2l += __shfl_xor(q2l, 16, 64);
-  q2l += __shfl_xor(q2l, 32, 64);
-  // Per query head constants, broadcast from lane i (row i, a hi row):
-  //   biasq_i = sum A * (base + centre*sigma) (scaled units; 1024 * sum A for the
-  //   uncentred formats, 0 for centred ones), q2_i = sum_j q~_ij (log2 units).
   float biasq[4], q2[4];
-  const float inv_qsc = 1.f / qsc;
+  float inv_qsc = 1.f;
+  constexpr bool QI8 = KI8<KB, D>::on && !KC;
+  constexpr int KS = D / 64;
+  u32x4_t qi[KS];   // integer QK A operands (QI8)
+  float inv_ql = 0.f;  // (QI8) 1 / fixed-point scale of query head g4, whose sums this lane's tile rows hold
+  if constexpr (QI8) {
+    // ---- QK A operands, integer: row r = lane % 16 holds digit r % 4 (the
+    // 2^16, 2^8 and 1 digits; the fourth row zero) of query head r / 4, at the
+    // channels of quarter g4 in KI8 order. x = rint(q~ * 2^(22 - e)), e the
+    // exponent of the head's largest |q~|, so |x| < 2^22 and
+    // x = d0 * 2^16 + d1 * 2^8 + d2 with each digit a signed byte. ----
+    const int qh = row >> 2, dig = row & 3;
+    const float f = qh < G ? qscale : 0.f;
+    float amax = 0.f;
+    double q2l = 0.0;  // this lane's share of sum_j q~_hj
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float q1i = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, static_cast<float>(q1)), i));
-    biasq[i] = q1i;
-    q2[i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, static_cast<float>(q2l)), i));
+    for (int st = 0; st < KS; ++st)
+#pragma unroll
+      for (int pb = 0; pb < 16; ++pb) {
+        const float qt = qs[qh][g4 * (D / 4) + KI8<KB, D>::channel(st, pb)] * f;
+        amax = fmaxf(amax, fabsf(qt));
+        q2l += static_cast<double>(qt);
+      }
+    // over the four quarters (lanes row, row+16, row+32, row+48)
+    amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+    q2l += __shfl_xor(q2l, 16, 64);
+    q2l += __shfl_xor(q2l, 32, 64);
+    float qsc = 1.f;
+    if (amax > 0.f) {
+      int ex;
+      frexpf(amax, &ex);
+      qsc = ldexpf(1.f, 22 - ex);
+    }
+#pragma unroll
+    for (int st = 0; st < KS; ++st)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float qt = qs[qh][g4 * (D / 4) + KI8<KB, D>::channel(st, 4 * d + q)] * f;
+          const int x = static_cast<int>(rintf(qt * qsc));
+          const int d2 = (x << 24) >> 24;
+          const int x1 = (x - d2) >> 8;
+          const int d1 = (x1 << 24) >> 24;
+          const int d0 = (x1 - d1) >> 8;
+          const int v = dig == 0 ? d0 : dig == 1 ? d1 : dig == 2 ? d2 : 0;
+          word |= (static_cast<uint32_t>(v) & 0xffu) << (8 * q);
+        }
+        qi[st][d] = word;
+      }
+    // head g4's scale from lane 4 * g4 (row 4 g4: head g4)
+    inv_ql = 1.f / __shfl(qsc, 4 * g4, 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      biasq[i] = 0.f;
+      q2[i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, static_cast<float>(q2l)), 4 * i));
+    }
+  } else {
+    // ---- QK A operands: row r = lane % 16, K-slots of quarter g4. Rows 0-3 hold
+    // the hi fp16 parts of query heads 0-3, rows 4-7 the lo parts, so one MFMA
+    // per chunk and page gives both sums (lanes 0-15 and 16-31 of the tile) ----
+    const int qrow = row & 3;                   // the query head of this row
+    const bool qact = row < 8 && qrow < G;
+    float amax = 0.f;
+#pragma unroll
+    for (int c = 0; c < NCK; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        // (read for every lane and scaled by zero in inactive rows: a read under
+        // a condition becomes a branch and a wait per value)
+        const float r = qs[qrow][g4 * (D / 4) + KF::channel(c, e)];
+        const float v = r * (qact ? qscale / KF::sigma(c, e) : 0.f);
+        amax = fmaxf(amax, fabsf(v));
+      }
+    amax = wave_max_scalar(amax);
+    // Power-of-two scale keeping the fp16 halves away from subnormals.
+    float qsc = 1.f;
+    if (!KF::bf16 && amax > 0.f) {
+      int ex;
+      frexpf(amax, &ex);
+      qsc = ldexpf(1.f, 10 - ex);
+    }
+    double q1 = 0.0;  // this lane's share of sum A * (base + centre*sigma): the offset to remove
+    double q2l = 0.0; // and of sum_j q~_j (the min term)
+#pragma unroll
+    for (int c = 0; c < NCK; ++c) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        uint32_t hp = 0, lp = 0;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int e = 2 * v + half;
+          const float qt = qs[qrow][g4 * (D / 4) + KF::channel(c, e)] * (qact ? qscale : 0.f);
+          const float x = qt / KF::sigma(c, e) * qsc;
+          uint32_t hb, lb;
+          float hv, lv;
+          if constexpr (KF::bf16) {
+            hb = f_to_bf16_rne(x); hv = bf16lo_to_f(hb);
+            lb = f_to_bf16_rne(x - hv); lv = bf16lo_to_f(lb);
+          } else {
+            const _Float16 hh = static_cast<_Float16>(x);
+            hv = static_cast<float>(hh);
+            const _Float16 ll = static_cast<_Float16>(x - hv);
+            lv = static_cast<float>(ll);
+            hb = half_bits(hh); lb = half_bits(ll);
+          }
+          q1 += (static_cast<double>(hv) + static_cast<double>(lv)) *
+                static_cast<double>(KF::base(c, e) + KF::kCentre * KF::sigma(c, e));
+          q2l += static_cast<double>(qt);
+          hp |= hb << (16 * half);
+          lp |= lb << (16 * half);
+        }
+        reinterpret_cast<uint32_t*>(&qa[c][lane])[v] = row < 4 ? hp : lp;
+      }
+    }
+    // Sum over the four quarters (lanes row, row+16, row+32, row+48), in fp64.
+    q1 += __shfl_xor(q1, 16, 64);
+    q1 += __shfl_xor(q1, 32, 64);
+    q2l += __shfl_xor(q2l, 16, 64);
+    q2l += __shfl_xor(q2l, 32, 64);
+    // Per query head constants, broadcast from lane i (row i, a hi row):
+    //   biasq_i = sum A * (base + centre*sigma) (scaled units; 1024 * sum A for the
+    //   uncentred formats, 0 for centred ones), q2_i = sum_j q~_ij (log2 units).
+    inv_qsc = 1.f / qsc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float q1i = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, static_cast<float>(q1)), i));
+      biasq[i] = q1i;
+      q2[i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, static_cast<float>(q2l)), i));
+    }
   }
   const uint32_t bias = vconst(0x64006400u);  // fp16 pair (1024, 1024)
 
@@ -1128,7 +1269,7 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, int si, int L
   // buffers, the fragments and the PV accumulators against the 256
   // architectural registers, leaving room for the rest of the loop.
   constexpr int GROUP_WORDS = 4 * KF::kWords + 16 * VRaw<VB, D>::kWords + 4;
-  constexpr bool QF_REGS = !KC && KVQ_TUNE_QF_REGS && (DEPTH + 1) * GROUP_WORDS + 4 * NCK + 4 * NCV <= 180;
+  constexpr bool QF_REGS = !KC && !QI8 && KVQ_TUNE_QF_REGS && (DEPTH + 1) * GROUP_WORDS + 4 * NCK + 4 * NCV <= 180;
   u32x4_t qreg[NCK];
   if constexpr (QF_REGS) {
 #pragma unroll
@@ -1138,8 +1279,8 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, int si, int L
     }
   }
   auto compute = [&](GroupRaw<KB, VB, D>& g) {
-    if constexpr (QF_REGS) {
-      compute_group<KB, VB, D, KC>(g, qreg, biasq, q2, inv_qsc, G, lane, bias, wt, wzero, st, kl, qa);
+    if constexpr (QF_REGS || QI8) {
+      compute_group<KB, VB, D, KC>(g, qreg, qi, inv_ql, biasq, q2, inv_qsc, G, lane, bias, wt, wzero, st, kl, qa);
     } else {
       u32x4_t qf[NCK];
 #pragma unroll
@@ -1147,7 +1288,7 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, int si, int L
         const uint4 v = qa[c][lane];
         qf[c] = u32x4_t{v.x, v.y, v.z, v.w};
       }
-      compute_group<KB, VB, D, KC>(g, qf, biasq, q2, inv_qsc, G, lane, bias, wt, wzero, st, kl, qa);
+      compute_group<KB, VB, D, KC>(g, qf, qi, inv_ql, biasq, q2, inv_qsc, G, lane, bias, wt, wzero, st, kl, qa);
     }
   };
 
