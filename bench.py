@@ -574,6 +574,9 @@ def run_bulk_append(args, torch, dev, kvq):
     achieved = app_bytes / (app_us * 1e-6) / 1e9
     return {
         "metric": "quantized-KV bulk append: GB/s (bf16 read + packed write), then one decode step",
+        "dtype": "f64",
+        "dtype_detail": "bf16 rows rotated in fp64 (exact sums), rounded to fp32; fp32 min/max, scale and "
+                        "round-half-even codes; 4-bit K and 2-bit V codes with fp32 {scale, min} written",
         "value": round(achieved, 1),
         "unit": "GB/s",
         "ms_per_step": round(app_us * args.layers / 1e3, 4),
