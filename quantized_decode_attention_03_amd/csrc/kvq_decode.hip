@@ -282,17 +282,16 @@ __device__ __forceinline__ void load_kquarter(const uint8_t* p, uint32_t (&w)[KF
     w[0] = s[0] | (static_cast<uint32_t>(s[1]) << 16);
     w[1] = s[2];
   } else if constexpr (kW == 1) {
-    w[0] = *reinterpret_cast<const uint32_t*>(p);
+    w[0] = ld_cache_u1(p);
   } else if constexpr (kW == 2) {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    const uint2 v = ld_cache_u2(p);
     w[0] = v.x; w[1] = v.y;
   } else if constexpr (kW == 3) {
-    const uint32_t* s = reinterpret_cast<const uint32_t*>(p);
-    w[0] = s[0]; w[1] = s[1]; w[2] = s[2];
+    w[0] = ld_cache_u1(p); w[1] = ld_cache_u1(p + 4); w[2] = ld_cache_u1(p + 8);
   } else {
 #pragma unroll
     for (int j = 0; j < kW; j += 4) {
-      const uint4 v = *reinterpret_cast<const uint4*>(p + 4 * j);
+      const uint4 v = ld_cache_u4(p + 4 * j);
       w[j] = v.x; w[j + 1] = v.y; w[j + 2] = v.z; w[j + 3] = v.w;
     }
   }
@@ -329,12 +328,12 @@ __device__ __forceinline__ void load_vtoken(const uint8_t* p, uint32_t* w) {
     // byte belongs to the next lane or row, still inside the area
     __builtin_memcpy(&w[0], p, 4);
   } else if constexpr (kW == 1) {
-    w[0] = *reinterpret_cast<const uint32_t*>(p);
+    w[0] = ld_cache_u1(p);
   } else if constexpr (kW == 2) {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    const uint2 v = ld_cache_u2(p);
     w[0] = v.x; w[1] = v.y;
   } else {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    const uint4 v = ld_cache_u4(p);
     w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
   }
 }
@@ -518,24 +517,24 @@ __device__ __forceinline__ void load_group(const DecodeSeg& a, const uint8_t* po
 #pragma unroll
       for (int pp = 0; pp < 4; ++pp) {
         const uint8_t* km = pool + boff[pp] + koff + kBlockTokens * RBK;
-        const float2 m0 = *reinterpret_cast<const float2*>(km + kc0);
-        const float2 m1 = *reinterpret_cast<const float2*>(km + kc1);
+        const float2 m0 = ld_cache_f2(km + kc0);
+        const float2 m1 = ld_cache_f2(km + kc1);
         g.kcm[pp] = make_float4(m0.x, m0.y, m1.x, m1.y);
       }
     } else if constexpr (M16) {
-      const uint32_t mk = *reinterpret_cast<const uint32_t*>(mbase + koff + kBlockTokens * RBK);
+      const uint32_t mk = ld_cache_u1(mbase + koff + kBlockTokens * RBK);
       g.ks = f16_to_f(mk & 0xffffu); g.kmn = f16_to_f(mk >> 16);
     } else {
-      const float2 mk = *reinterpret_cast<const float2*>(mbase + koff + kBlockTokens * RBK);
+      const float2 mk = ld_cache_f2(mbase + koff + kBlockTokens * RBK);
       g.ks = mk.x; g.kmn = mk.y;
     }
   }
   if constexpr (VB != 16) {
     if constexpr (M16) {
-      const uint32_t mv = *reinterpret_cast<const uint32_t*>(mbase + voff + kBlockTokens * RBV);
+      const uint32_t mv = ld_cache_u1(mbase + voff + kBlockTokens * RBV);
       g.vs = f16_to_f(mv & 0xffffu); g.vmn = f16_to_f(mv >> 16);
     } else {
-      const float2 mv = *reinterpret_cast<const float2*>(mbase + voff + kBlockTokens * RBV);
+      const float2 mv = ld_cache_f2(mbase + voff + kBlockTokens * RBV);
       g.vs = mv.x; g.vmn = mv.y;
     }
   }

@@ -27,7 +27,7 @@ __global__ __launch_bounds__(64) void measure_stream_kernel(const uint8_t* buf, 
     const uint8_t* p = buf + c * kStreamChunk + lane * 16;
     uint4 v[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = *reinterpret_cast<const uint4*>(p + i * 1024);
+    for (int i = 0; i < 8; ++i) v[i] = ld_cache_u4(p + i * 1024);
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
   }
@@ -79,9 +79,9 @@ __device__ __forceinline__ void paged_load(const PagedArgs& a, const GroupTab& t
     for (int half = 0; half < 2; ++half) {
       const uint4* base = reinterpret_cast<const uint4*>(a.pool + bo + a.area_off[half][h]);
       const int last = a.last16[half][h];
-      r.v[pp][half][0] = base[min(lane, last)];
+      r.v[pp][half][0] = ld_cache_u4(base + min(lane, last));
       // (the area's size is the same in every lane: a uniform branch)
-      r.v[pp][half][1] = last >= 64 ? base[min(lane + 64, last)] : make_uint4(0u, 0u, 0u, 0u);
+      r.v[pp][half][1] = last >= 64 ? ld_cache_u4(base + min(lane + 64, last)) : make_uint4(0u, 0u, 0u, 0u);
     }
   }
 }
