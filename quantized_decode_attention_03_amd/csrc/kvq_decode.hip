@@ -472,10 +472,11 @@ constexpr float kRescaleSlack = 4.f;
 // wave-uniform and the per-lane part is a loop-invariant offset.
 constexpr int kXcds = 8;  // accelerator dies of the chip; workgroups go round-robin over them
 #ifndef KVQ_TUNE_STATIC_EIGHTHS
-#define KVQ_TUNE_STATIC_EIGHTHS 2
+#define KVQ_TUNE_STATIC_EIGHTHS 5
 #endif
 // Share of a unit's groups dealt out in fixed order before the shared tail
-// (measured: 2/8 beats 0, 4/8 and 6/8 at the 32k Llama-shaped decode).
+// (measured with non-temporal cache loads at the 32k Llama-shaped decode, one
+// box: 5/8 110.0 us, 4/8 and 6/8 110.4-110.8, 3/8 111.8, 2/8 113.0, 0 115.6).
 constexpr int kStaticEighths = KVQ_TUNE_STATIC_EIGHTHS;
 
 template <int KB, int VB, int D, bool M16, bool KC>
@@ -911,7 +912,7 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, int si, int L
   // split = x + 8r (x its XCD, r its dispatch round) joins group (r - x) mod
   // (W/8), so a group mixes all eight XCDs and early and late waves. In its
   // group's range of NG groups a wave first takes the SG groups
-  // [i*SG, (i+1)*SG) (a quarter of the range, in order; i = x), then groups of
+  // [i*SG, (i+1)*SG) (together kStaticEighths/8 of the range, in order; i = x), then groups of
   // the shared tail [8*SG, NG), one at a time, from the group's counter in the
   // workspace. Wave speeds differ by tens of percent (the older of two waves
   // on a SIMD is issued first; some dies run slower); fast waves take more of
