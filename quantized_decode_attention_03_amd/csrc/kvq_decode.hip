@@ -1108,17 +1108,23 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, int si, int L
     // x = d0 * 2^16 + d1 * 2^8 + d2 with each digit a signed byte. ----
     const int qh = row >> 2, dig = row & 3;
     const float f = qh < G ? qscale : 0.f;
+    // The head's largest |q~| and sum_j q~_j: the four digit rows of a head
+    // (lanes 4*qh .. 4*qh+3, a DPP quad) each take D/16 of the quarter's
+    // channels, then the quad and the four quarters (lanes row, row+16,
+    // row+32, row+48) are combined.
+    constexpr int CD = D / 16;
     float amax = 0.f;
-    double q2l = 0.0;  // this lane's share of sum_j q~_hj
+    double q2l = 0.0;  // sum_j q~_hj, this lane's share
 #pragma unroll
-    for (int st = 0; st < KS; ++st)
-#pragma unroll
-      for (int pb = 0; pb < 16; ++pb) {
-        const float qt = qs[qh][g4 * (D / 4) + KI8<KB, D>::channel(st, pb)] * f;
-        amax = fmaxf(amax, fabsf(qt));
-        q2l += static_cast<double>(qt);
-      }
-    // over the four quarters (lanes row, row+16, row+32, row+48)
+    for (int j = 0; j < CD; ++j) {
+      const float qt = qs[qh][g4 * (D / 4) + dig * CD + j] * f;
+      amax = fmaxf(amax, fabsf(qt));
+      q2l += static_cast<double>(qt);
+    }
+    amax = fmaxf(amax, dpp_f32<kDppQuadXor1>(amax));
+    amax = fmaxf(amax, dpp_f32<kDppQuadXor2>(amax));
+    q2l += dpp_f64<kDppQuadXor1>(q2l);
+    q2l += dpp_f64<kDppQuadXor2>(q2l);
     amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
     amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
     q2l += __shfl_xor(q2l, 16, 64);
@@ -1129,23 +1135,25 @@ __device__ __forceinline__ void partial_split(const DecodeArgs& a, int si, int L
       frexpf(amax, &ex);
       qsc = ldexpf(1.f, 22 - ex);
     }
+    // Digits: with y = x + 0x808080, byte k of y is digit k + 128 (balanced
+    // base-256 digits, no carries since |x| <= 2^22), so this row's signed
+    // digit is byte 2 - dig of y with its top bit flipped. v_perm gathers that
+    // byte of four values into one word; the fourth row of a head stays zero.
+    const uint32_t bsel = static_cast<uint32_t>(2 - dig);
+    const uint32_t sel_lo = dig == 3 ? 0x0c0c0c0cu : (0x0c0c0000u | ((4u + bsel) << 8) | bsel);
+    const uint32_t sel_hi = dig == 3 ? 0x0c0c0c0cu : (((4u + bsel) << 24) | (bsel << 16) | 0x0c0cu);
+    const uint32_t flip = dig == 3 ? 0u : 0x80808080u;
 #pragma unroll
     for (int st = 0; st < KS; ++st)
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        uint32_t word = 0;
+        uint32_t y[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float qt = qs[qh][g4 * (D / 4) + KI8<KB, D>::channel(st, 4 * d + q)] * f;
-          const int x = static_cast<int>(rintf(qt * qsc));
-          const int d2 = (x << 24) >> 24;
-          const int x1 = (x - d2) >> 8;
-          const int d1 = (x1 << 24) >> 24;
-          const int d0 = (x1 - d1) >> 8;
-          const int v = dig == 0 ? d0 : dig == 1 ? d1 : dig == 2 ? d2 : 0;
-          word |= (static_cast<uint32_t>(v) & 0xffu) << (8 * q);
+          y[q] = static_cast<uint32_t>(static_cast<int>(rintf(qt * qsc))) + 0x808080u;
         }
-        qi[st][d] = word;
+        qi[st][d] = (perm_b32(y[1], y[0], sel_lo) | perm_b32(y[3], y[2], sel_hi)) ^ flip;
       }
     // head g4's scale from lane 4 * g4 (row 4 g4: head g4)
     inv_ql = 1.f / __shfl(qsc, 4 * g4, 64);
