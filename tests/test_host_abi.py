@@ -487,3 +487,25 @@ def test_logquant_init_and_advance_capacity_and_consistency_errors():
         st2.advance()
     assert e.value.status == kvq.KVQ_ERR_ARG
     assert st2.states[0].total == 8
+
+
+def test_query_digit_bytes_are_the_balanced_decomposition():
+    """The integer-score prologue of the decode kernel splits each fixed-point
+    query value x (|x| <= 2^22) into signed-byte digits x = d0*2^16 + d1*2^8 + d2
+    by reading the bytes of x + 0x808080 with their top bit flipped. Checked
+    here for every such x against the sign-extend-and-subtract decomposition."""
+    x = np.arange(-(1 << 22), (1 << 22) + 1, dtype=np.int64)
+
+    def sext8(v):
+        return ((v & 0xff) ^ 0x80) - 0x80
+
+    d2 = sext8(x)
+    x1 = (x - d2) >> 8
+    d1 = sext8(x1)
+    d0 = (x1 - d1) >> 8
+    assert np.array_equal(d0 * 65536 + d1 * 256 + d2, x)
+    assert d0.min() >= -128 and d0.max() <= 127
+    y = (x + 0x808080) & 0xffffffff
+    for k, d in ((0, d2), (1, d1), (2, d0)):
+        assert np.array_equal(((y >> (8 * k)) & 0xff) ^ 0x80, d & 0xff), k
+    assert np.all((y >> 24) == 0)  # no carry out of the three bytes
