@@ -86,8 +86,14 @@ __device__ __forceinline__ void append_rows(const AppendArgs& a, int half, doubl
   const int total = a.batch * a.n_new;
   const bool active = row < total;
   const int r = active ? row : 0;
-  const int b = r / a.n_new;
-  const int i = r - b * a.n_new;
+  // b = r / n_new by the invariant-divisor multiply: the estimate is the
+  // quotient or one less (r < 2^31), so one correction makes it exact
+  int b = static_cast<int>(__umulhi(static_cast<uint32_t>(r), a.n_new_magic) >> a.n_new_shift);
+  int i = r - b * a.n_new;
+  if (i >= a.n_new) {
+    ++b;
+    i -= a.n_new;
+  }
 
   // destination: start position, then the block-table entry (clamped into the
   // row, read by every lane)
@@ -645,8 +651,13 @@ hipError_t launch_append_k(const AppendArgs& a, double rs, hipStream_t s) {
 #undef KVQ_APPEND_CALL
 }
 
-hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
-  if (a.batch * a.n_new == 0 || a.n_heads == 0) return hipSuccess;
+hipError_t launch_append(const AppendArgs& args, hipStream_t s) {
+  if (args.batch * args.n_new == 0 || args.n_heads == 0) return hipSuccess;
+  AppendArgs a = args;
+  int l = 0;
+  while ((int64_t{2} << l) <= a.n_new) ++l;  // floor(log2 n_new)
+  a.n_new_shift = l;
+  a.n_new_magic = static_cast<uint32_t>(((uint64_t{1} << (32 + l)) - 1) / static_cast<uint64_t>(a.n_new));
   bool uniform = true;
   for (int half = 0; half < 2; ++half)
     for (int i = 0; i < a.n_heads; ++i) {

@@ -22,6 +22,12 @@ struct AppendArgs {
   int32_t meta16;       // 1: float16 {s, mn} (4 bytes per row)
   int32_t key_per_channel;  // 1: keys are written per block by append_kc_kernel, not per row
   int32_t batch, n_new, hkv, d, had_block;
+  // row r of the launch is new token r % n_new of sequence r / n_new; the
+  // quotient is floor(r * n_new_magic / 2^(32 + n_new_shift)) plus at most one
+  // for r < 2^31 (filled by launch_append: n_new_shift = floor(log2 n_new),
+  // n_new_magic = floor((2^(32 + n_new_shift) - 1) / n_new), below 2^32)
+  uint32_t n_new_magic;
+  int32_t n_new_shift;
   int32_t n_heads;      // heads in this launch
   int32_t bits[2];      // append_kc_kernel: the key bits of the listed heads
   int32_t heads[KVQ_MAX_KV_HEADS];
